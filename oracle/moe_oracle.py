@@ -1,0 +1,454 @@
+"""CPU oracle for the single-device Mixture-of-Experts layer (test infrastructure).
+
+Plain, slow, obviously correct: NumPy float64 arithmetic with an explicit
+rounding to float32 (and then to bfloat16 or e4m3) at each point where the GPU
+path holds float32 and stores a narrower type. Only tests, the smoke check and
+the CPU-baseline leg of the benchmark use this module; the product path never
+imports it, and it shares no code with the HIP library.
+
+Every function cites the passage of the pages it follows:
+  [TE-MoE]   Transformer Engine user guide, "Mixture of Experts"
+  [TE-MIX]   Transformer Engine example te_mixtral.py (TEMixtralSparseMoeBlock)
+  [TT-1269]  torchtitan pull request 1269 (Llama4 MoE: GroupedExperts, MoE.forward)
+  [AO-2600]  pytorch/ao pull request 2600, "MoE refactor to use grouped_mm and
+             scaled_grouped_mm"
+  [HF-48201] transformers pull request 48201 (Qwen3MoeSparseMoeBlock benchmark)
+
+Readings taken where the pages are silent are marked READING in the docstrings.
+
+Pinned by tests/test_oracle_*.py against brute force, closed forms, library
+routines and finite differences; no function here is "parity unpinned".
+
+``exact=True`` switches every rounding off (pure float64), which the
+finite-difference and dense-reference pins use.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID = 0, 1, 2
+E4M3_MAX = 448.0
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 values (exact: bf16 is the top half of fp32)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bits, round to nearest, ties to even (NaN -> quiet NaN)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> 16) & 1
+    r = (u + 0x7FFF + keep_lsb) >> 16
+    r = np.where(np.isnan(a), ((u >> 16) & 0x8000) | 0x7FC0, r)
+    return r.astype(np.uint16)
+
+
+def as_values(a) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 values; any float array -> float64."""
+    a = np.asarray(a)
+    return bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def to_f32(x, exact=False):
+    """One rounding of a float64 result to float32 (the GPU's accumulator type)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x if exact else x.astype(np.float32).astype(np.float64)
+
+
+def to_bf16(x, exact=False):
+    """float64 -> float32 -> bfloat16, returned as float64 values.
+
+    The GPU path holds float32 and stores bfloat16, so the oracle rounds twice,
+    in that order, at the same points.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if exact:
+        return x
+    return bf16_bits_to_f64(f32_to_bf16_bits(x.astype(np.float32)))
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 (the 'fn' variant: no infinities, S.1111.111 is NaN) -> float64.
+
+    Layout: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits. Exponent field 0
+    holds subnormals m/8 * 2^-6. Largest finite value 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return s * val
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """float32 values -> E4M3 codes, round to nearest-even, saturating to +-448.
+
+    Exact for every float32 input: the scaling by powers of two is exact in float64
+    and ``np.rint`` rounds half to even.
+    """
+    v = np.asarray(v, dtype=np.float32).astype(np.float64)
+    assert not np.isnan(v).any(), "NaN input to e4m3_encode"
+    sign = np.where(np.signbit(v), 0x80, 0x00)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # subnormal grid: multiples of 2^-9; q == 8 lands exactly on the smallest normal (code 8)
+    code = np.where(sub, np.rint(a * 2.0 ** 9).astype(np.int64), code)
+    mant, ex = np.frexp(np.where(sub, 1.0, a))          # a = mant * 2^ex, mant in [0.5, 1)
+    e_unb = ex - 1                                        # a = (2*mant) * 2^e_unb
+    q = np.rint((2.0 * mant - 1.0) * 8.0).astype(np.int64)  # 3-bit mantissa, may round up to 8
+    e_unb = np.where(q == 8, e_unb + 1, e_unb)
+    q = np.where(q == 8, 0, q)
+    normal_code = ((e_unb + 7) << 3) | q
+    code = np.where(sub, code, normal_code)
+    return (code | sign).astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# router  [TE-MoE "Router"; TE-MIX TEMixtralSparseMoeBlock.forward]
+# ---------------------------------------------------------------------------
+
+
+def topk_select(logits: np.ndarray, k: int) -> np.ndarray:
+    """Top-k expert ids per token, in descending order of the logit.
+
+    [TE-MoE "Router"]: the router picks the top-k experts per token.
+    READING: selection is on the logits themselves (softmax and sigmoid are strictly
+    increasing, so the chosen set is the same real-number choice), ties go to the
+    lower expert index, and the ids are listed best first.
+    Built as k rounds of arg-max (np.argmax returns the first, i.e. lowest, index of
+    a tie), each round removing the chosen expert.
+    """
+    l = np.asarray(logits, dtype=np.float32)
+    assert np.isfinite(l).all(), "non-finite logits are not supported"
+    T, E = l.shape
+    assert 1 <= k <= E
+    avail = np.ones((T, E), dtype=bool)
+    idx = np.empty((T, k), dtype=np.int32)
+    rows = np.arange(T)
+    for j in range(k):
+        cand = np.where(avail, l.astype(np.float64), -np.inf)
+        e = np.argmax(cand, axis=1)
+        idx[:, j] = e
+        avail[rows, e] = False
+    return idx
+
+
+def topk_probs(logits: np.ndarray, idx: np.ndarray, score: int, exact=False) -> np.ndarray:
+    """Routing weights of the selected experts, computed in float64, rounded once to fp32.
+
+    SOFTMAX_PRE_RENORM [TE-MIX forward: softmax in fp32 over all experts, topk, then
+      divide by the row sum of the kept weights; AO-2600 mixtral model does the same]:
+      p_e = exp(l_e - m) / sum_e' exp(l_e' - m),  q_j = p_idx_j / sum_j' p_idx_j'.
+    SOFTMAX_POST [TE-MoE "Router": use_pre_softmax=False applies the softmax after
+      the top-k]: q_j = exp(l_idx_j) / sum_j' exp(l_idx_j').
+    SIGMOID [TE-MoE "Router" score functions; "Token combine": sigmoid top-1 weights
+      are not one and must be applied]: q_j = 1 / (1 + exp(-l_idx_j)).
+      READING: no renormalisation of sigmoid weights.
+    """
+    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    T = l.shape[0]
+    sel = np.take_along_axis(l, idx.astype(np.int64), axis=1)
+    if score == SOFTMAX_PRE_RENORM:
+        m = l.max(axis=1, keepdims=True)
+        p = np.exp(l - m)
+        p = p / p.sum(axis=1, keepdims=True)
+        ps = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+        q = ps / ps.sum(axis=1, keepdims=True)
+    elif score == SOFTMAX_POST:
+        m = sel.max(axis=1, keepdims=True)
+        z = np.exp(sel - m)
+        q = z / z.sum(axis=1, keepdims=True)
+    elif score == SIGMOID:
+        q = 1.0 / (1.0 + np.exp(-sel))
+    else:
+        raise ValueError(f"unknown score function {score}")
+    assert q.shape == (T, idx.shape[1])
+    return to_f32(q, exact)
+
+
+def router_topk(logits: np.ndarray, k: int, score: int, exact=False):
+    """Fused score function + top-k [TE-MoE "Router"].
+
+    Returns topk_idx [T,k] int32, topk_prob [T,k], counts [E] int32,
+    routing_map [T,E] uint8 (1 at the selected experts), probs_dense [T,E] (the
+    weights at the selected experts, 0 elsewhere).
+    counts = tokens routed to each expert [TE-MoE "Load balancing": routing_map.sum(0)].
+    """
+    T, E = logits.shape
+    idx = topk_select(logits, k)
+    q = topk_probs(logits, idx, score, exact)
+    rmap = np.zeros((T, E), dtype=np.uint8)
+    dense = np.zeros((T, E), dtype=np.float64)
+    rows = np.arange(T)[:, None]
+    rmap[rows, idx] = 1
+    dense[rows, idx] = q
+    counts = rmap.sum(axis=0).astype(np.int32)
+    return idx, q, counts, rmap, dense
+
+
+# ---------------------------------------------------------------------------
+# dispatch  [TE-MoE "Token dispatch"]
+# ---------------------------------------------------------------------------
+
+
+def dispatch_meta(idx: np.ndarray, E: int):
+    """Expert-contiguous row layout for dropless routing [TE-MoE "Token dispatch";
+    "Example: MoE layer on a single device": num_out_tokens = num_tokens * top_k].
+
+    offsets[e] = number of routed rows of experts < e (cumulative per-expert counts);
+    block e holds the (token, slot) pairs routed to e.
+    READING: inside a block, rows follow ascending token index (a token never picks
+    an expert twice). row_of[t, j] is the row of token t's j-th choice; src_of[r] is
+    the token that fills row r.
+    """
+    T, k = idx.shape
+    flat = idx.reshape(-1).astype(np.int64)
+    counts = np.array([(flat == e).sum() for e in range(E)], dtype=np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    row_of = np.full(T * k, -1, dtype=np.int64)
+    src_of = np.full(T * k, -1, dtype=np.int64)
+    for e in range(E):
+        entries = np.nonzero(flat == e)[0]               # ascending flat index = ascending token
+        rows = offsets[e] + np.arange(entries.size)
+        row_of[entries] = rows
+        src_of[rows] = entries // k
+    return offsets.astype(np.int32), row_of.reshape(T, k).astype(np.int32), src_of.astype(np.int32)
+
+
+def permute(x_bits: np.ndarray, src_of: np.ndarray) -> np.ndarray:
+    """Token dispatch gather: row r of the permuted buffer is token src_of[r]
+    [TE-MoE "Token dispatch"]. A bit copy."""
+    return np.asarray(x_bits)[np.asarray(src_of, dtype=np.int64)]
+
+
+def quantize_rows_e4m3(vals: np.ndarray):
+    """Dynamic per-row e4m3 quantisation [TE-MoE "Grouped GEMM": inputs are quantised
+    and the expert GEMMs run in the recipe's precision; AO-2600: fp8 dynamic
+    activation quantisation with scaled_grouped_mm].
+
+    READING: s_r = amax_r / 448 (float32 divide), s_r = 1 when the row is all zero;
+    q = e4m3(x / s_r) with a float32 divide, nearest-even, saturating.
+    vals: float64 array holding float32-representable values (bf16 here), [R, C].
+    """
+    v = np.asarray(vals, dtype=np.float64).astype(np.float32)
+    amax = np.abs(v).max(axis=1) if v.shape[1] else np.zeros(v.shape[0], np.float32)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+    q = e4m3_encode((v / s[:, None]).astype(np.float32))
+    return q, s
+
+
+def quantize_cols_e4m3(w_vals: np.ndarray):
+    """Per-output-channel e4m3 quantisation of expert weights [.., K, N]: one scale per
+    (expert, column) over the K (reduction) dimension. Same rounding rule as
+    ``quantize_rows_e4m3`` applied to the transposed matrix."""
+    w = np.asarray(w_vals, dtype=np.float64)
+    lead = w.shape[:-2]
+    K, N = w.shape[-2:]
+    wt = np.swapaxes(w.reshape(-1, K, N), 1, 2).reshape(-1, K)     # rows = (batch, column)
+    q, s = quantize_rows_e4m3(wt)
+    q = np.swapaxes(q.reshape(-1, N, K), 1, 2).reshape(*lead, K, N)
+    return q, s.reshape(*lead, N)
+
+
+# ---------------------------------------------------------------------------
+# grouped expert MLP  [TE-MoE "Grouped GEMM", "Grouped MLP"; TE-MIX _expert_ffn;
+#                      TT-1269 GroupedExperts]
+# ---------------------------------------------------------------------------
+
+
+def silu(g):
+    """SiLU, x * sigmoid(x) = x / (1 + e^-x), float64."""
+    return g / (1.0 + np.exp(-g))
+
+
+def grouped_gemm(a_vals, b_vals, offsets, exact=False, a_scale=None, b_scale=None):
+    """Y_e = A_e B_e for every expert block e of the rows of A [TE-MoE "Grouped GEMM":
+    Y_i = X_i W_i (the pages write the weight transposed), one result block per expert,
+    identical to a loop of one product per expert].
+
+    a_vals [N, K] (expert-contiguous rows), b_vals [E, K, Ncol], offsets [E+1].
+    Accumulation in float64, then one rounding to fp32. With scales (fp8 recipe):
+    Y = fp32((sum_k qa qb) * s_a[row] * s_b[e, col]).
+    Returns float64 values of the fp32 results, [N, Ncol].
+    """
+    a = np.asarray(a_vals, dtype=np.float64)
+    b = np.asarray(b_vals, dtype=np.float64)
+    E = b.shape[0]
+    out = np.zeros((a.shape[0], b.shape[2]), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        y = a[r0:r1] @ b[e]
+        if a_scale is not None:
+            y = y * np.asarray(a_scale, np.float64)[r0:r1, None] * np.asarray(b_scale, np.float64)[e][None, :]
+        out[r0:r1] = to_f32(y, exact)
+    return out
+
+
+def swiglu_from_gu(g, u, exact=False):
+    """h = silu(g) * u from float32 g, u, then fp32 -> bf16 [TT-1269 GroupedExperts:
+    silu(x w1) * (x w3); TE-MIX _expert_ffn: silu(gate) * up]."""
+    return to_bf16(silu(g) * u, exact)
+
+
+def expert_mlp(xp_vals, w_gu_vals, w_down_vals, offsets, I, exact=False, fp8=False):
+    """Grouped expert SwiGLU MLP on expert-contiguous rows.
+
+    [TE-MIX __init__ / _expert_ffn]: fused gate/up weight with 2I outputs split in
+    two halves, gate first. READING: w_gu [E, H, 2I] in the x @ W orientation with
+    gate = columns [0, I), up = columns [I, 2I); no biases.
+    [TE-MoE "Grouped MLP"]: FC1 with the activation, then FC2 reading the bf16
+    intermediate h.
+    fp8 [TE-MoE "Grouped GEMM" low precision; AO-2600 fp8dq]: x rows quantised per
+    row, weights per output column; h is re-quantised per row from its bf16 value.
+    Returns dict with g, u (fp32 values), h (bf16 values), out (bf16 values).
+    """
+    if fp8:
+        qx, sx = quantize_rows_e4m3(xp_vals)
+        qw, sw = quantize_cols_e4m3(w_gu_vals)
+        gu = grouped_gemm(e4m3_decode(qx), e4m3_decode(qw), offsets, exact, sx, sw)
+    else:
+        gu = grouped_gemm(xp_vals, w_gu_vals, offsets, exact)
+    g, u = gu[:, :I], gu[:, I:]
+    h = swiglu_from_gu(g, u, exact)
+    if fp8:
+        qh, sh = quantize_rows_e4m3(h)
+        qd, sd = quantize_cols_e4m3(w_down_vals)
+        out = grouped_gemm(e4m3_decode(qh), e4m3_decode(qd), offsets, exact, sh, sd)
+    else:
+        out = grouped_gemm(h, w_down_vals, offsets, exact)
+    return {"g": g, "u": u, "h": h, "out": to_bf16(out, exact)}
+
+
+def dense_mlp(x_vals, w_gu_vals, w_down_vals, I, exact=False):
+    """Shared expert: the same SwiGLU MLP on every token, unweighted
+    [TT-1269 MoE.forward: shared_expert(x) is the base the routed outputs are added to;
+    TE-MoE "Expert parallelism": shared experts are a regular dense MLP]."""
+    T = x_vals.shape[0]
+    offs = np.array([0, T])
+    r = expert_mlp(x_vals, w_gu_vals[None], w_down_vals[None], offs, I, exact)
+    return r["out"]
+
+
+# ---------------------------------------------------------------------------
+# combine  [TE-MoE "Token combine", "Token probabilities"]
+# ---------------------------------------------------------------------------
+
+
+def combine(out_vals, row_of, prob=None, shared_vals=None, exact=False):
+    """y[t] = sum_j q[t,j] * out[row_of[t,j]] (+ shared[t]), summed in float64, one
+    rounding to fp32 then bf16 [TE-MoE "Token combine": weighted sum of the per-expert
+    contributions in the same pass; "Token probabilities": weights applied once].
+    prob=None: unweighted sum (the dispatch backward uses this form).
+    """
+    o = np.asarray(out_vals, dtype=np.float64)
+    T, k = row_of.shape
+    acc = np.zeros((T, o.shape[1]), dtype=np.float64)
+    for j in range(k):
+        rows = o[np.asarray(row_of[:, j], dtype=np.int64)]
+        if prob is not None:
+            rows = rows * np.asarray(prob, np.float64)[:, j:j + 1]
+        acc += rows
+    if shared_vals is not None:
+        acc += np.asarray(shared_vals, dtype=np.float64)
+    return to_bf16(acc, exact)
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+
+
+def moe_forward(x_bits, logits, w_gu_bits, w_down_bits, k, score, I,
+                shared_gu_bits=None, shared_down_bits=None, fp8=False, exact=False):
+    """Route -> dispatch -> grouped MLP -> combine [TE-MoE "Introduction", the four
+    stages; "Example: MoE layer on a single device"]. x and the weights are bf16 bit
+    patterns (or float64 values, for the exact-arithmetic pins); logits are float32.
+    Returns a dict of every intermediate."""
+    x = as_values(x_bits)
+    E = logits.shape[1]
+    idx, q, counts, rmap, dense = router_topk(logits, k, score, exact)
+    offsets, row_of, src_of = dispatch_meta(idx, E)
+    xp = x[src_of.astype(np.int64)]
+    mlp = expert_mlp(xp, as_values(w_gu_bits), as_values(w_down_bits), offsets, I, exact, fp8)
+    shared = None
+    if shared_gu_bits is not None:
+        Is = shared_down_bits.shape[0]
+        shared = dense_mlp(x, as_values(shared_gu_bits), as_values(shared_down_bits), Is, exact)
+    y = combine(mlp["out"], row_of, q, shared, exact)
+    res = dict(topk_idx=idx, topk_prob=q, counts=counts, routing_map=rmap, probs_dense=dense,
+               offsets=offsets, row_of=row_of, src_of=src_of, xp=xp, shared=shared, y=y)
+    res.update(mlp)
+    return res
+
+
+def swiglu_backward(dh, g, u, exact=False):
+    """Gradient of h = silu(g) * u: with s = sigmoid(g),
+    dg = dh * u * s * (1 + g (1 - s)),  du = dh * g * s.  Returns bf16 values."""
+    s = 1.0 / (1.0 + np.exp(-g))
+    dg = dh * u * s * (1.0 + g * (1.0 - s))
+    du = dh * g * s
+    return to_bf16(dg, exact), to_bf16(du, exact)
+
+
+def grouped_gemm_dw(a_vals, b_vals, offsets, exact=False):
+    """dW_e = A_e^T B_e over the rows of each expert block (reduction over that expert's
+    routed rows) [TE-MoE "Example": every stage is differentiable]. An expert with no
+    rows gets a zero gradient. Returns fp32 values [E, Ka, Kb]."""
+    a = np.asarray(a_vals, dtype=np.float64)
+    b = np.asarray(b_vals, dtype=np.float64)
+    E = len(offsets) - 1
+    out = np.zeros((E, a.shape[1], b.shape[1]), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            out[e] = to_f32(a[r0:r1].T @ b[r0:r1], exact)
+    return out
+
+
+def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False):
+    """Backward of the expert path for an upstream gradient dy [T, H]
+    [TE-MoE "Example: MoE layer on a single device": all stages differentiable;
+    HF-48201 "Numbers": the block is timed forward + backward].
+
+    READING: logits are an input, so no gradient flows to the router; dx goes
+    through the expert path only. dW are rounded to bf16.
+      d_out[row_of[t,j]] = bf16(q[t,j] * dy[t])                 (combine backward)
+      dh    = fp32(d_out_e @ W_down[e]^T);  dGU = SwiGLU'(dh; saved bf16 g, u)
+      dW_down[e] = bf16(h_e^T @ d_out_e)
+      dxp   = bf16(dGU_e @ W_gu[e]^T);      dW_gu[e] = bf16(xp_e^T @ dGU_e)
+      dx[t] = bf16(sum_j dxp[row_of[t,j]])                      (dispatch backward)
+    """
+    dy = as_values(dy_bits)
+    row_of, q, offsets = fwd["row_of"], fwd["topk_prob"], fwd["offsets"]
+    T, k = row_of.shape
+    N = T * k
+    H = dy.shape[1]
+    w_gu = as_values(w_gu_bits)
+    w_d = as_values(w_down_bits)
+    d_out = np.zeros((N, H), dtype=np.float64)
+    for j in range(k):
+        d_out[row_of[:, j].astype(np.int64)] = to_bf16(dy * q[:, j:j + 1], exact)
+    # GEMM2 backward: dh = d_out W_d^T (per expert), then the SwiGLU backward
+    dh = grouped_gemm(d_out, np.swapaxes(w_d, 1, 2), offsets, exact)
+    g_saved, u_saved = to_bf16(fwd["g"], exact), to_bf16(fwd["u"], exact)
+    dg, du = swiglu_backward(dh, g_saved, u_saved, exact)
+    dgu = np.concatenate([dg, du], axis=1)
+    dw_down = to_bf16(grouped_gemm_dw(fwd["h"], d_out, offsets, exact), exact)
+    # GEMM1 backward
+    dxp = to_bf16(grouped_gemm(dgu, np.swapaxes(w_gu, 1, 2), offsets, exact), exact)
+    dw_gu = to_bf16(grouped_gemm_dw(fwd["xp"], dgu, offsets, exact), exact)
+    dx = combine(dxp, row_of, None, None, exact)
+    return dict(d_out=d_out, dh=dh, dgu=dgu, dxp=dxp, dx=dx, dw_gu=dw_gu, dw_down=dw_down)
