@@ -1,0 +1,233 @@
+/*
+ * moe_amd.h -- C ABI of the single-device Mixture-of-Experts layer hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The path follows the four stages of an MoE layer described in the Transformer
+ * Engine user guide "Mixture of Experts" (section "Introduction"): the router
+ * scores the experts and keeps the top-k per token, token dispatch lays the tokens
+ * out expert-contiguously, the grouped expert MLP runs over all expert blocks, and
+ * token combine merges the per-expert outputs back in token order.
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers, row-major, densely packed, owned by
+ *    the caller. The library never allocates, frees or synchronises inside these
+ *    calls, never reads device data on the host, and enqueues work only on
+ *    `stream` (a hipStream_t passed as void*; NULL is the default stream).
+ *  - bf16 tensors are passed as void* (IEEE bfloat16 bit patterns); e4m3 tensors
+ *    as uint8 codes of the OCP FP8 E4M3 ("fn") format; scales as float32.
+ *  - Token counts per expert stay on the device (Transformer Engine guide,
+ *    "Grouped GEMM": device-side counts avoid a host synchronisation), so every
+ *    call can be captured in a HIP graph.
+ *  - Routing is dropless: routed row buffers always hold T*k rows (guide, "Example:
+ *    MoE layer on a single device": num_out_tokens = num_tokens * top_k).
+ *  - Errors: host-side argument checks return MOE_ERR_INVALID_ARG (bad pointer,
+ *    negative size, k out of range) or MOE_ERR_UNSUPPORTED (a size the kernels do
+ *    not handle); a failed kernel launch returns MOE_ERR_HIP; a workspace smaller
+ *    than required returns MOE_ERR_WORKSPACE. Nothing is enqueued when a check
+ *    fails. T == 0 is a valid no-op. Out-of-range expert ids in topk_idx are the
+ *    caller's error and are not checked on the device.
+ *  - Supported sizes: 1 <= k <= min(E, 32), E <= 256, H % 64 == 0, I % 64 == 0,
+ *    every pointer 16-byte aligned.
+ */
+#ifndef MOE_AMD_H
+#define MOE_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status_t;
+
+typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3 = 1, MOE_FP32 = 2 } moe_dtype_t;
+
+/* Score functions (guide, "Router": softmax before or after the top-k, sigmoid).
+ * MOE_SOFTMAX_PRE_RENORM: softmax over all experts, keep the top-k, divide by their
+ *   sum (te_mixtral.py, TEMixtralSparseMoeBlock.forward).
+ * MOE_SOFTMAX_POST: softmax over the k kept logits (guide, use_pre_softmax=False).
+ * MOE_SIGMOID: sigmoid of each kept logit, not renormalised (guide, "Token
+ *   combine": sigmoid top-1 weights are not one and must be applied).
+ * Selection is on the logits, descending, ties to the lower expert index. */
+typedef enum {
+  MOE_SOFTMAX_PRE_RENORM = 0,
+  MOE_SOFTMAX_POST = 1,
+  MOE_SIGMOID = 2
+} moe_score_t;
+
+/* Layouts of the grouped GEMM (guide, "Grouped GEMM": Y_i = X_i W_i per expert
+ * block, the same result as one product per expert). "rows" is the number of rows
+ * of the expert-contiguous buffers; group g owns rows [offsets[g], offsets[g+1]).
+ *  MOE_GEMM_NN:    C[rows,N]  = A[rows,K] . B[g][K,N]
+ *  MOE_GEMM_NT:    C[rows,N]  = A[rows,K] . B[g][N,K]^T
+ *  MOE_GEMM_TN_DW: C[g][M,N]  = A_g[rows_g,M]^T . B_g[rows_g,N]  (weight gradient;
+ *                  a group with no rows gets C[g] = 0) */
+typedef enum { MOE_GEMM_NN = 0, MOE_GEMM_NT = 1, MOE_GEMM_TN_DW = 2 } moe_gemm_mode_t;
+
+const char* moe_status_str(moe_status_t s);
+
+/* Router: fused score function + top-k (guide, "Router"; all math in fp32).
+ *  logits      [T,E] float32 in.
+ *  topk_idx    [T,k] int32 out: expert ids, best first.
+ *  topk_prob   [T,k] float32 out: routing weights of those experts.
+ *  counts      [E]   int32 out: tokens routed to each expert (overwritten).
+ *  routing_map [T,E] uint8 out, nullable: 1 at the selected experts, else 0.
+ *  probs_dense [T,E] float32 out, nullable: weights at the selected experts, else 0. */
+moe_status_t moe_router_topk(const float* logits, int T, int E, int k, int score,
+                             int32_t* topk_idx, float* topk_prob, int32_t* counts,
+                             uint8_t* routing_map, float* probs_dense, void* stream);
+
+/* Scratch bytes moe_permute needs for (T, E, k). */
+size_t moe_permute_workspace_bytes(int T, int E, int k);
+
+/* Token dispatch (guide, "Token dispatch"): expert-contiguous copy of the tokens.
+ *  x        [T,H] bf16 in.       topk_idx [T,k] int32 in (ids in [0,E)).
+ *  out_dtype MOE_BF16: xp [T*k,H] bf16 is a bit copy of the token rows.
+ *            MOE_FP8_E4M3: xp [T*k,H] e4m3 codes, xp_scale [T*k] float32: each token
+ *            quantised per row, scale = amax/448 (1 for an all-zero row).
+ *  offsets  [E+1] int32 out: offsets[e] = rows of experts < e; offsets[E] = T*k.
+ *  row_of   [T,k] int32 out: row of token t's j-th choice. Inside a block rows
+ *            follow ascending token index.
+ *  src_of   [T*k] int32 out: token that fills each row.
+ *  ws/ws_bytes: scratch of at least moe_permute_workspace_bytes(T,E,k) bytes. */
+moe_status_t moe_permute(const void* x, const int32_t* topk_idx, int T, int H, int E, int k,
+                         int out_dtype, void* xp, float* xp_scale, int32_t* offsets,
+                         int32_t* row_of, int32_t* src_of, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Grouped GEMM1 with the SwiGLU epilogue (guide, "Grouped MLP": FC1 with the
+ * activation fused, FC2 separate; te_mixtral.py _expert_ffn: gate/up fused weight,
+ * silu(gate) * up).
+ *  xp      [rows,H] bf16 (dtype MOE_BF16) or e4m3 codes (MOE_FP8_E4M3) in.
+ *  xp_scale [rows] float32 per-row scales (fp8 only, else NULL).
+ *  w_gu    bf16: [G,H,2I], gate = columns [0,I), up = columns [I,2I).
+ *          fp8:  [G,2I,H] e4m3 codes (output-channel major, as written by
+ *                moe_quantize_fp8_weights), w_scale [G,2I] float32.
+ *  offsets [G+1] int32 device group boundaries.
+ *  h       [rows,I] bf16 out: silu(g) * u, g and u held in fp32.
+ *  gu_saved [rows,2I] bf16 out, nullable: g and u rounded to bf16 (for backward). */
+moe_status_t moe_grouped_gemm_swiglu(const void* xp, const float* xp_scale, const void* w_gu,
+                                     const float* w_scale, const int32_t* offsets, int G,
+                                     int rows, int H, int I, int dtype, void* h, void* gu_saved,
+                                     void* stream);
+
+/* Grouped GEMM (guide, "Grouped GEMM"); see moe_gemm_mode_t for the layouts.
+ *  dtype MOE_BF16: A, B bf16.  MOE_FP8_E4M3 (mode NT only): A e4m3 [rows,K] with
+ *  a_scale [rows], B e4m3 [G][N,K] with b_scale [G,N]; C = acc * a_scale * b_scale.
+ *  c_dtype MOE_BF16 or MOE_FP32 (fp32 accumulation in every case). M is used by
+ *  MOE_GEMM_TN_DW only, K by NN/NT only. */
+moe_status_t moe_grouped_gemm(int mode, const void* A, const float* a_scale, const void* B,
+                              const float* b_scale, const int32_t* offsets, int G, int rows,
+                              int M, int N, int K, int dtype, void* C, int c_dtype, void* stream);
+
+/* Backward of GEMM2 + SwiGLU: dh = d_out[rows,H] . W_down[g][I,H]^T (layout NT), then
+ *  with the saved bf16 g,u and s = sigmoid(g): dg = dh*u*s*(1+g*(1-s)), du = dh*g*s,
+ *  written as dgu [rows,2I] bf16 (dg in [0,I), du in [I,2I)). */
+moe_status_t moe_grouped_gemm_swiglu_bwd(const void* d_out, const void* w_down,
+                                         const int32_t* offsets, const void* gu_saved, int G,
+                                         int rows, int H, int I, void* dgu, void* stream);
+
+/* Token combine (guide, "Token combine"): y[t] = sum_j p[t,j] * y_perm[row_of[t,j]]
+ * (+ shared_out[t]), summed in fp32, one rounding to bf16.
+ *  y_perm [T*k,H] bf16, row_of [T,k], topk_prob [T,k] float32 or NULL (unweighted
+ *  sum: the dispatch backward), shared_out [T,H] bf16 or NULL, y [T,H] bf16 out. */
+moe_status_t moe_unpermute_combine(const void* y_perm, const int32_t* row_of,
+                                   const float* topk_prob, const void* shared_out, int T,
+                                   int H, int k, void* y, void* stream);
+
+/* Backward of the weighted combine: d_out[row_of[t,j]] = bf16(p[t,j] * dy[t]). */
+moe_status_t moe_combine_backward(const void* dy, const int32_t* row_of, const float* topk_prob,
+                                  int T, int H, int k, void* d_out, void* stream);
+
+/* Per-row e4m3 quantisation of a bf16 matrix x [R,C]: scale[r] = amax_r/448 (1 for a
+ * zero row), q = e4m3(x/scale), nearest-even, saturating. */
+moe_status_t moe_quantize_fp8_rows(const void* x, int R, int C, uint8_t* q, float* scale,
+                                   void* stream);
+
+/* Offline weight preparation for the fp8 recipe: per-output-channel e4m3
+ * quantisation of w [G,K,N] bf16, one scale per (g, n) over K. Writes the codes
+ * output-channel major, q [G,N,K], and scale [G,N]. */
+moe_status_t moe_quantize_fp8_weights(const void* w, int G, int K, int N, uint8_t* q,
+                                      float* scale, void* stream);
+
+/* ---- whole layer ------------------------------------------------------------ */
+
+typedef struct {
+  int T, H, E, k, I;
+  int shared_I;  /* 0: no shared expert; else a dense SwiGLU MLP of width shared_I,
+                    unweighted, added in combine (torchtitan pull request 1269,
+                    MoE.forward) */
+  int score;     /* moe_score_t */
+  int dtype;     /* expert GEMMs: MOE_BF16 or MOE_FP8_E4M3 */
+  int training;  /* 1: keep what moe_backward needs in the workspace */
+} moe_problem_t;
+
+typedef struct {
+  const void* x;              /* [T,H] bf16 */
+  const float* logits;        /* [T,E] */
+  const void* w_gu;           /* bf16 [E,H,2I]  | fp8 [E,2I,H] codes */
+  const float* w_gu_scale;    /* fp8: [E,2I] */
+  const void* w_down;         /* bf16 [E,I,H]   | fp8 [E,H,I] codes */
+  const float* w_down_scale;  /* fp8: [E,H] */
+  const void* shared_gu;      /* bf16 [H,2*shared_I] or NULL */
+  const void* shared_down;    /* bf16 [shared_I,H] or NULL */
+  void* y;                    /* [T,H] bf16 out */
+} moe_tensors_t;
+
+/* Device pointers into a forward workspace (all inside ws). */
+typedef struct {
+  int32_t* topk_idx;   /* [T,k] */
+  float* topk_prob;    /* [T,k] */
+  int32_t* counts;     /* [E] */
+  int32_t* offsets;    /* [E+1] */
+  int32_t* row_of;     /* [T,k] */
+  int32_t* src_of;     /* [T*k] */
+  void* xp;            /* [T*k,H] bf16 (or e4m3) */
+  float* xp_scale;     /* [T*k] (fp8) */
+  void* gu;            /* [T*k,2I] bf16 (training) */
+  void* h;             /* [T*k,I] bf16 */
+  uint8_t* hq;         /* [T*k,I] e4m3 (fp8) */
+  float* h_scale;      /* [T*k] (fp8) */
+  void* out;           /* [T*k,H] bf16 */
+  void* shared_h;      /* [T,shared_I] bf16 */
+  void* shared_out;    /* [T,H] bf16 */
+  int32_t* shared_offsets; /* [2] = {0, T} */
+  void* d_out;         /* [T*k,H] bf16 (training) */
+  void* dgu;           /* [T*k,2I] bf16 (training) */
+  void* dxp;           /* [T*k,H] bf16 (training) */
+  void* scratch;       /* moe_permute scratch */
+  size_t scratch_bytes;
+} moe_views_t;
+
+/* Bytes of workspace moe_forward (and, when training, moe_backward) needs. */
+size_t moe_workspace_bytes(const moe_problem_t* p);
+
+/* Fill `v` with the pointers of every intermediate inside workspace `ws`. */
+moe_status_t moe_workspace_views(const moe_problem_t* p, void* ws, size_t ws_bytes,
+                                 moe_views_t* v);
+
+/* Whole forward: router -> dispatch -> grouped SwiGLU MLP -> combine, enqueued on
+ * `stream` with no host synchronisation. All intermediates live in `ws`, which
+ * moe_backward later reads: keep it untouched between the two calls. */
+moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Backward of the expert path for upstream gradient dy [T,H] bf16 (bf16 MLP,
+ * training=1 forward only): dx [T,H] bf16, dw_gu [E,H,2I] bf16, dw_down [E,I,H]
+ * bf16. Logits are an input of the layer, so no gradient flows to the router. */
+moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const void* dy,
+                          void* dx, void* dw_gu, void* dw_down, void* ws, size_t ws_bytes,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_AMD_H */

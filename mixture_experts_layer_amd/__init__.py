@@ -1,0 +1,298 @@
+"""Python binding of libmoe_amd.so, the MI355X (gfx950) MoE layer hot path.
+
+Argument marshalling only: every function here checks tensor dtypes, shapes and
+devices, then calls the C entry point of the same name declared in
+include/moe_amd.h. All arithmetic runs in the HIP kernels. PyTorch supplies device
+memory and the current stream. The library must have been built
+(``python -m mixture_experts_layer_amd._build``); importing without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime the library then shares)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_amd.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_BF16, MOE_FP8_E4M3, MOE_FP32 = 0, 1, 2
+MOE_SOFTMAX_PRE_RENORM, MOE_SOFTMAX_POST, MOE_SIGMOID = 0, 1, 2
+MOE_GEMM_NN, MOE_GEMM_NT, MOE_GEMM_TN_DW = 0, 1, 2
+
+EXPORTS = [
+    "moe_status_str", "moe_router_topk", "moe_permute_workspace_bytes", "moe_permute",
+    "moe_grouped_gemm_swiglu", "moe_grouped_gemm", "moe_grouped_gemm_swiglu_bwd",
+    "moe_unpermute_combine", "moe_combine_backward", "moe_quantize_fp8_rows",
+    "moe_quantize_fp8_weights", "moe_workspace_bytes", "moe_workspace_views", "moe_forward",
+    "moe_backward",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} returned {_status_name(status)} ({status})")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int), ("H", ctypes.c_int), ("E", ctypes.c_int),
+                ("k", ctypes.c_int), ("I", ctypes.c_int), ("shared_I", ctypes.c_int),
+                ("score", ctypes.c_int), ("dtype", ctypes.c_int), ("training", ctypes.c_int)]
+
+
+class Tensors(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("x", "logits", "w_gu", "w_gu_scale", "w_down", "w_down_scale",
+                 "shared_gu", "shared_down", "y")]
+
+
+class Views(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_idx", "topk_prob", "counts", "offsets", "row_of", "src_of", "xp",
+                 "xp_scale", "gu", "h", "hq", "h_scale", "out", "shared_h", "shared_out",
+                 "shared_offsets", "d_out", "dgu", "dxp", "scratch")] + \
+               [("scratch_bytes", ctypes.c_size_t)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m mixture_experts_layer_amd._build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    sig = {
+        "moe_status_str": ([i], ctypes.c_char_p),
+        "moe_router_topk": ([vp, i, i, i, i, vp, vp, vp, vp, vp, vp], i),
+        "moe_permute_workspace_bytes": ([i, i, i], sz),
+        "moe_permute": ([vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp, sz, vp], i),
+        "moe_grouped_gemm_swiglu": ([vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp], i),
+        "moe_grouped_gemm": ([i, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp], i),
+        "moe_grouped_gemm_swiglu_bwd": ([vp, vp, vp, vp, i, i, i, i, vp, vp], i),
+        "moe_unpermute_combine": ([vp, vp, vp, vp, i, i, i, vp, vp], i),
+        "moe_combine_backward": ([vp, vp, vp, i, i, i, vp, vp], i),
+        "moe_quantize_fp8_rows": ([vp, i, i, vp, vp, vp], i),
+        "moe_quantize_fp8_weights": ([vp, i, i, i, vp, vp, vp], i),
+        "moe_workspace_bytes": ([ctypes.POINTER(Problem)], sz),
+        "moe_workspace_views": ([ctypes.POINTER(Problem), vp, sz, ctypes.POINTER(Views)], i),
+        "moe_forward": ([ctypes.POINTER(Problem), ctypes.POINTER(Tensors), vp, sz, vp], i),
+        "moe_backward": ([ctypes.POINTER(Problem), ctypes.POINTER(Tensors), vp, vp, vp, vp, vp,
+                          sz, vp], i),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes, f.restype = args, res
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _status_name(st):
+    return _lib.moe_status_str(st).decode()
+
+
+def _check(fn, st):
+    if st != MOE_OK:
+        raise MoeError(fn, st)
+
+
+def _p(t):
+    """Device pointer of a tensor (or None)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _want(t, dtype, shape, name):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+_SCORE = {"softmax_pre_renorm": MOE_SOFTMAX_PRE_RENORM, "softmax_post": MOE_SOFTMAX_POST,
+          "sigmoid": MOE_SIGMOID}
+
+
+def _score(s):
+    return _SCORE[s] if isinstance(s, str) else int(s)
+
+
+# ---- stage calls ---------------------------------------------------------------------
+
+def moe_router_topk(logits, k, score, topk_idx, topk_prob, counts, routing_map=None,
+                    probs_dense=None, stream=None):
+    T, E = logits.shape
+    _want(logits, torch.float32, (T, E), "logits")
+    _want(topk_idx, torch.int32, (T, k), "topk_idx")
+    _want(topk_prob, torch.float32, (T, k), "topk_prob")
+    _want(counts, torch.int32, (E,), "counts")
+    if routing_map is not None:
+        _want(routing_map, torch.uint8, (T, E), "routing_map")
+    if probs_dense is not None:
+        _want(probs_dense, torch.float32, (T, E), "probs_dense")
+    _check("moe_router_topk", _lib.moe_router_topk(
+        _p(logits), T, E, k, _score(score), _p(topk_idx), _p(topk_prob), _p(counts),
+        _p(routing_map), _p(probs_dense), _stream(stream)))
+
+
+def moe_permute_workspace_bytes(T, E, k):
+    return int(_lib.moe_permute_workspace_bytes(T, E, k))
+
+
+def moe_permute(x, topk_idx, E, xp, offsets, row_of, src_of, ws, out_dtype=MOE_BF16,
+                xp_scale=None, stream=None):
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    _want(x, torch.bfloat16, (T, H), "x")
+    _want(topk_idx, torch.int32, (T, k), "topk_idx")
+    _want(xp, torch.bfloat16 if out_dtype == MOE_BF16 else torch.uint8, (T * k, H), "xp")
+    _want(offsets, torch.int32, (E + 1,), "offsets")
+    _want(row_of, torch.int32, (T, k), "row_of")
+    _want(src_of, torch.int32, (T * k,), "src_of")
+    _check("moe_permute", _lib.moe_permute(
+        _p(x), _p(topk_idx), T, H, E, k, out_dtype, _p(xp), _p(xp_scale), _p(offsets),
+        _p(row_of), _p(src_of), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_grouped_gemm_swiglu(xp, w_gu, offsets, h, gu_saved=None, dtype=MOE_BF16, xp_scale=None,
+                            w_scale=None, stream=None):
+    rows, H = xp.shape
+    G = offsets.numel() - 1
+    I = h.shape[1]
+    _want(h, torch.bfloat16, (rows, I), "h")
+    if dtype == MOE_BF16:
+        _want(w_gu, torch.bfloat16, (G, H, 2 * I), "w_gu")
+    else:
+        _want(w_gu, torch.uint8, (G, 2 * I, H), "w_gu")
+    if gu_saved is not None:
+        _want(gu_saved, torch.bfloat16, (rows, 2 * I), "gu_saved")
+    _check("moe_grouped_gemm_swiglu", _lib.moe_grouped_gemm_swiglu(
+        _p(xp), _p(xp_scale), _p(w_gu), _p(w_scale), _p(offsets), G, rows, H, I, dtype, _p(h),
+        _p(gu_saved), _stream(stream)))
+
+
+def moe_grouped_gemm(mode, A, B, offsets, C, dtype=MOE_BF16, a_scale=None, b_scale=None,
+                     stream=None):
+    G = offsets.numel() - 1
+    rows = A.shape[0]
+    c_dtype = MOE_FP32 if C.dtype == torch.float32 else MOE_BF16
+    if mode == MOE_GEMM_TN_DW:
+        M, N, K = A.shape[1], B.shape[1], 0
+        _want(C, C.dtype, (G, M, N), "C")
+    else:
+        K = A.shape[1]
+        N = B.shape[2] if mode == MOE_GEMM_NN else B.shape[1]
+        M = 0
+        _want(C, C.dtype, (rows, N), "C")
+    _check("moe_grouped_gemm", _lib.moe_grouped_gemm(
+        mode, _p(A), _p(a_scale), _p(B), _p(b_scale), _p(offsets), G, rows, M, N, K, dtype,
+        _p(C), c_dtype, _stream(stream)))
+
+
+def moe_grouped_gemm_swiglu_bwd(d_out, w_down, offsets, gu_saved, dgu, stream=None):
+    rows, H = d_out.shape
+    G, I, _ = w_down.shape
+    _want(gu_saved, torch.bfloat16, (rows, 2 * I), "gu_saved")
+    _want(dgu, torch.bfloat16, (rows, 2 * I), "dgu")
+    _check("moe_grouped_gemm_swiglu_bwd", _lib.moe_grouped_gemm_swiglu_bwd(
+        _p(d_out), _p(w_down), _p(offsets), _p(gu_saved), G, rows, H, I, _p(dgu),
+        _stream(stream)))
+
+
+def moe_unpermute_combine(y_perm, row_of, topk_prob, y, shared_out=None, stream=None):
+    T, k = row_of.shape
+    H = y.shape[1]
+    _want(y_perm, torch.bfloat16, (y_perm.shape[0], H), "y_perm")
+    _want(y, torch.bfloat16, (T, H), "y")
+    _check("moe_unpermute_combine", _lib.moe_unpermute_combine(
+        _p(y_perm), _p(row_of), _p(topk_prob), _p(shared_out), T, H, k, _p(y), _stream(stream)))
+
+
+def moe_combine_backward(dy, row_of, topk_prob, d_out, stream=None):
+    T, k = row_of.shape
+    H = dy.shape[1]
+    _want(d_out, torch.bfloat16, (T * k, H), "d_out")
+    _check("moe_combine_backward", _lib.moe_combine_backward(
+        _p(dy), _p(row_of), _p(topk_prob), T, H, k, _p(d_out), _stream(stream)))
+
+
+def moe_quantize_fp8_rows(x, q, scale, stream=None):
+    R, C = x.shape
+    _want(q, torch.uint8, (R, C), "q")
+    _want(scale, torch.float32, (R,), "scale")
+    _check("moe_quantize_fp8_rows", _lib.moe_quantize_fp8_rows(
+        _p(x), R, C, _p(q), _p(scale), _stream(stream)))
+
+
+def moe_quantize_fp8_weights(w, q, scale, stream=None):
+    G, K, N = w.shape
+    _want(q, torch.uint8, (G, N, K), "q")
+    _want(scale, torch.float32, (G, N), "scale")
+    _check("moe_quantize_fp8_weights", _lib.moe_quantize_fp8_weights(
+        _p(w), G, K, N, _p(q), _p(scale), _stream(stream)))
+
+
+# ---- whole layer -----------------------------------------------------------------------
+
+def problem(T, H, E, k, I, score, shared_I=0, dtype=MOE_BF16, training=False):
+    return Problem(T, H, E, k, I, shared_I, _score(score), dtype, int(bool(training)))
+
+
+def moe_workspace_bytes(prob: Problem):
+    n = int(_lib.moe_workspace_bytes(ctypes.byref(prob)))
+    if n == 0:
+        raise MoeError("moe_workspace_bytes", MOE_ERR_INVALID_ARG)
+    return n
+
+
+def moe_workspace_views(prob: Problem, ws):
+    v = Views()
+    _check("moe_workspace_views", _lib.moe_workspace_views(
+        ctypes.byref(prob), _p(ws), ws.numel() * ws.element_size(), ctypes.byref(v)))
+    return v
+
+
+def tensors(x, logits, w_gu, w_down, y, w_gu_scale=None, w_down_scale=None, shared_gu=None,
+            shared_down=None):
+    return Tensors(_p(x), _p(logits), _p(w_gu), _p(w_gu_scale), _p(w_down), _p(w_down_scale),
+                   _p(shared_gu), _p(shared_down), _p(y))
+
+
+def moe_forward(prob: Problem, tens: Tensors, ws, stream=None):
+    _check("moe_forward", _lib.moe_forward(
+        ctypes.byref(prob), ctypes.byref(tens), _p(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def moe_backward(prob: Problem, tens: Tensors, dy, dx, dw_gu, dw_down, ws, stream=None):
+    _check("moe_backward", _lib.moe_backward(
+        ctypes.byref(prob), ctypes.byref(tens), _p(dy), _p(dx), _p(dw_gu), _p(dw_down), _p(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def view_tensor(ptr, shape, dtype, like):
+    """A torch tensor aliasing device memory at ``ptr`` inside a workspace tensor ``like``."""
+    base = like.data_ptr()
+    nbytes = int(torch.tensor([], dtype=dtype).element_size())
+    off = int(ptr) - base
+    count = 1
+    for s in shape:
+        count *= s
+    if off < 0 or off + count * nbytes > like.numel() * like.element_size():
+        raise ValueError("view outside the workspace")
+    flat = like.view(torch.uint8)[off: off + count * nbytes]
+    return flat.view(dtype).view(*shape)

@@ -1,0 +1,96 @@
+// Device helpers shared by the MoE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_amd.h"
+
+#define MOE_DEV __device__ __forceinline__
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+// ---- bf16 <-> fp32 --------------------------------------------------------
+MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+MOE_DEV float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+MOE_DEV float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN -> quiet NaN of the same sign.
+MOE_DEV uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+MOE_DEV uint32_t pack_bf16x2(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
+
+// ---- OCP FP8 E4M3 ("fn": no infinities, max 448) ---------------------------
+// Round to nearest even, saturating to +-448. Works on the fp32 bit pattern:
+// normal range |v| >= 2^-6 keeps 3 mantissa bits, below that a fixed 2^-9 grid.
+MOE_DEV uint32_t f32_to_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fminf(fabsf(v), 448.0f);
+  uint32_t au = __float_as_uint(a);
+  uint32_t code;
+  if (a < 0.015625f) {                      // 2^-6: subnormal grid of 2^-9
+    // a * 2^9 is exact; rint rounds half to even
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    uint32_t exp = (au >> 23) - 127 + 7;    // biased e4m3 exponent, 1..15
+    uint32_t mant = au & 0x7fffffu;
+    uint32_t keep = mant >> 20;             // top 3 mantissa bits
+    uint32_t rest = mant & 0xfffffu;        // dropped 20 bits
+    uint32_t half = 0x80000u;
+    if (rest > half || (rest == half && (keep & 1u))) keep += 1;
+    code = (exp << 3) + keep;               // a carry out of the mantissa bumps the exponent
+  }
+  return sign | code;
+}
+
+MOE_DEV float e4m3_to_f32(uint32_t c) {
+  uint32_t e = (c >> 3) & 0xf, m = c & 7;
+  float v = e == 0 ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -v : v;
+}
+
+// ---- wave reductions -------------------------------------------------------
+MOE_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+MOE_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+MOE_DEV uint64_t lanemask_lt() {
+  int l = __lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+}  // namespace moe
+
+// ---- host-side helpers (internal; not exported) ---------------------------
+#define MOE_CHECK_LAUNCH()                                      \
+  do {                                                          \
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;    \
+  } while (0)
+
+#define MOE_REQUIRE(cond, err) \
+  do {                         \
+    if (!(cond)) return (err); \
+  } while (0)
+
+static inline bool moe_aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }

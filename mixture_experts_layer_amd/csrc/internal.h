@@ -1,0 +1,52 @@
+// Internal launchers (host side) shared by the C-ABI layer. Not exported.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// router.hip
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int score,
+                              int32_t* topk_idx, float* topk_prob, int32_t* counts,
+                              uint8_t* routing_map, float* probs_dense, hipStream_t s);
+
+// permute.hip
+constexpr int kPermChunk = 1024;  // flattened (token, slot) entries per dispatch chunk
+size_t permute_scratch_bytes(int T, int E, int k);
+hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, int32_t* offsets,
+                                int32_t* row_of, int32_t* src_of, void* scratch, hipStream_t s);
+hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, const float* prob, int T,
+                               int H, int k, void* xp, hipStream_t s);
+hipError_t launch_scatter_rows_fp8(const void* x, const int32_t* row_of, int T, int H, int k,
+                                   uint8_t* xq, float* xscale, hipStream_t s);
+hipError_t launch_combine(const void* y_perm, const int32_t* row_of, const float* prob,
+                          const void* shared, int T, int H, int k, void* y, hipStream_t s);
+hipError_t launch_quantize_rows(const void* x, int R, int C, uint8_t* q, float* scale,
+                                hipStream_t s);
+hipError_t launch_quantize_weights(const void* w, int G, int K, int N, uint8_t* q, float* scale,
+                                   hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+
+// gemm.hip
+enum GemmEpi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2 };
+
+struct GemmParams {
+  int mode;              // moe_gemm_mode_t
+  int epi;               // GemmEpi
+  int fp8;               // operands e4m3 (NT only) instead of bf16
+  const void* A;
+  const void* B;
+  const float* a_scale;  // fp8: [rows]
+  const float* b_scale;  // fp8: [G, Ncols]
+  const int32_t* offsets;
+  int G, rows;
+  int M, N, K;           // NN/NT: C[rows,N] = A[rows,K] B_g ; DW: C[g][M,N], K ragged
+  void* C;
+  int c_fp32;
+  int I;                 // SwiGLU width (EPI_SWIGLU: N = 2I; EPI_SWIGLU_BWD: N = I)
+  void* gu_out;          // EPI_SWIGLU: optional saved g,u [rows,2I]
+  const void* gu_in;     // EPI_SWIGLU_BWD: saved g,u [rows,2I]
+};
+hipError_t launch_grouped_gemm(const GemmParams& p, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,503 @@
+// extern "C" entry points declared in include/moe_amd.h: argument checks, workspace
+// layout, and the enqueue order of the whole-layer forward and backward.
+#include "internal.h"
+
+using namespace moe;
+
+namespace {
+
+inline hipStream_t S(void* s) { return (hipStream_t)s; }
+inline moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                           \
+  do {                                          \
+    hipError_t _e = (expr);                     \
+    if (_e != hipSuccess) return MOE_ERR_HIP;   \
+  } while (0)
+
+bool ok_ptr(const void* p) { return p != nullptr && moe_aligned16(p); }
+bool opt_ptr(const void* p) { return p == nullptr || moe_aligned16(p); }
+
+moe_status_t check_shape(int T, int H, int E, int k) {
+  if (T < 0 || H <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
+  if (k > E) return MOE_ERR_INVALID_ARG;
+  if (k > 32 || E > 256) return MOE_ERR_UNSUPPORTED;
+  if (H % 64) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * k * (long long)(H > 0 ? H : 1) > (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace layout of moe_forward / moe_backward. Every region is 256-byte aligned.
+struct Layout {
+  size_t topk_idx, topk_prob, counts, offsets, row_of, src_of, shared_offsets;
+  size_t xp, xp_scale, gu, h, hq, h_scale, out, shared_h, shared_out;
+  size_t d_out, dgu, dxp, scratch, scratch_bytes, total;
+};
+
+Layout make_layout(const moe_problem_t& p) {
+  Layout L{};
+  const size_t N = (size_t)p.T * p.k;
+  const bool fp8 = p.dtype == MOE_FP8_E4M3;
+  const size_t act = fp8 ? 1 : 2;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  L.topk_idx = take(N * 4);
+  L.topk_prob = take(N * 4);
+  L.counts = take((size_t)p.E * 4);
+  L.offsets = take(((size_t)p.E + 1) * 4);
+  L.row_of = take(N * 4);
+  L.src_of = take(N * 4);
+  L.shared_offsets = take(2 * 4);
+  L.xp = take(N * p.H * act);
+  L.xp_scale = take(fp8 ? N * 4 : 0);
+  L.gu = take(p.training ? N * 2 * p.I * 2 : 0);
+  L.h = take(N * p.I * 2);
+  L.hq = take(fp8 ? N * p.I : 0);
+  L.h_scale = take(fp8 ? N * 4 : 0);
+  L.out = take(N * p.H * 2);
+  L.shared_h = take(p.shared_I ? (size_t)p.T * p.shared_I * 2 : 0);
+  L.shared_out = take(p.shared_I ? (size_t)p.T * p.H * 2 : 0);
+  L.d_out = take(p.training ? N * p.H * 2 : 0);
+  L.dgu = take(p.training ? N * 2 * p.I * 2 : 0);
+  L.dxp = take(p.training ? N * p.H * 2 : 0);
+  L.scratch_bytes = permute_scratch_bytes(p.T, p.E, p.k);
+  L.scratch = take(L.scratch_bytes);
+  L.total = o;
+  return L;
+}
+
+moe_status_t check_problem(const moe_problem_t* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  moe_status_t st = check_shape(p->T, p->H, p->E, p->k);
+  if (st != MOE_OK) return st;
+  if (p->I <= 0 || p->shared_I < 0) return MOE_ERR_INVALID_ARG;
+  if (p->I % 64 || p->shared_I % 64) return MOE_ERR_UNSUPPORTED;
+  if (p->score < MOE_SOFTMAX_PRE_RENORM || p->score > MOE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (p->dtype == MOE_FP8_E4M3) {
+    if (p->H % 128 || p->I % 128) return MOE_ERR_UNSUPPORTED;
+    if (p->training || p->shared_I) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+moe_status_t moe_router_topk(const float* logits, int T, int E, int k, int score,
+                             int32_t* topk_idx, float* topk_prob, int32_t* counts,
+                             uint8_t* routing_map, float* probs_dense, void* stream) {
+  moe_status_t st = check_shape(T, 64, E, k);
+  if (st != MOE_OK) return st;
+  if (score < MOE_SOFTMAX_PRE_RENORM || score > MOE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (!ok_ptr(counts)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!ok_ptr(logits) || !ok_ptr(topk_idx) || !ok_ptr(topk_prob)))
+    return MOE_ERR_INVALID_ARG;
+  if (!opt_ptr(routing_map) || !opt_ptr(probs_dense)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_router_topk(logits, T, E, k, score, topk_idx, topk_prob, counts,
+                                       routing_map, probs_dense, S(stream)));
+}
+
+size_t moe_permute_workspace_bytes(int T, int E, int k) {
+  if (T < 0 || E <= 0 || k <= 0) return 0;
+  return permute_scratch_bytes(T, E, k);
+}
+
+moe_status_t moe_permute(const void* x, const int32_t* topk_idx, int T, int H, int E, int k,
+                         int out_dtype, void* xp, float* xp_scale, int32_t* offsets,
+                         int32_t* row_of, int32_t* src_of, void* ws, size_t ws_bytes,
+                         void* stream) {
+  moe_status_t st = check_shape(T, H, E, k);
+  if (st != MOE_OK) return st;
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (!ok_ptr(offsets)) return MOE_ERR_INVALID_ARG;
+  if (T > 0) {
+    if (!ok_ptr(x) || !ok_ptr(topk_idx) || !ok_ptr(xp) || !ok_ptr(row_of) || !ok_ptr(src_of))
+      return MOE_ERR_INVALID_ARG;
+    if (out_dtype == MOE_FP8_E4M3 && !ok_ptr(xp_scale)) return MOE_ERR_INVALID_ARG;
+    if (!ok_ptr(ws)) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < permute_scratch_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
+  }
+  hipStream_t s = S(stream);
+  MOE_TRY(launch_dispatch_meta(topk_idx, T, E, k, offsets, row_of, src_of, ws, s));
+  if (out_dtype == MOE_BF16) MOE_TRY(launch_scatter_rows(x, row_of, nullptr, T, H, k, xp, s));
+  else MOE_TRY(launch_scatter_rows_fp8(x, row_of, T, H, k, (uint8_t*)xp, xp_scale, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_grouped_gemm_swiglu(const void* xp, const float* xp_scale, const void* w_gu,
+                                     const float* w_scale, const int32_t* offsets, int G,
+                                     int rows, int H, int I, int dtype, void* h, void* gu_saved,
+                                     void* stream) {
+  if (G <= 0 || rows < 0 || H <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 64 || I % 64 || G > 256) return MOE_ERR_UNSUPPORTED;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = dtype == MOE_FP8_E4M3;
+  if (fp8 && (H % 128)) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!ok_ptr(xp) || !ok_ptr(w_gu) || !ok_ptr(offsets) || !ok_ptr(h) || !opt_ptr(gu_saved))
+    return MOE_ERR_INVALID_ARG;
+  if (fp8 && (!ok_ptr(xp_scale) || !ok_ptr(w_scale))) return MOE_ERR_INVALID_ARG;
+  GemmParams p{};
+  p.mode = fp8 ? MOE_GEMM_NT : MOE_GEMM_NN;
+  p.epi = EPI_SWIGLU;
+  p.fp8 = fp8;
+  p.A = xp;
+  p.B = w_gu;
+  p.a_scale = xp_scale;
+  p.b_scale = w_scale;
+  p.offsets = offsets;
+  p.G = G;
+  p.rows = rows;
+  p.N = 2 * I;
+  p.K = H;
+  p.C = h;
+  p.I = I;
+  p.gu_out = gu_saved;
+  return hip_status(launch_grouped_gemm(p, S(stream)));
+}
+
+moe_status_t moe_grouped_gemm(int mode, const void* A, const float* a_scale, const void* B,
+                              const float* b_scale, const int32_t* offsets, int G, int rows,
+                              int M, int N, int K, int dtype, void* C, int c_dtype, void* stream) {
+  if (G <= 0 || rows < 0 || N <= 0) return MOE_ERR_INVALID_ARG;
+  if (G > 256) return MOE_ERR_UNSUPPORTED;
+  if (mode != MOE_GEMM_NN && mode != MOE_GEMM_NT && mode != MOE_GEMM_TN_DW)
+    return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (c_dtype != MOE_BF16 && c_dtype != MOE_FP32) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = dtype == MOE_FP8_E4M3;
+  if (fp8 && mode != MOE_GEMM_NT) return MOE_ERR_UNSUPPORTED;
+  if (N % 64) return MOE_ERR_UNSUPPORTED;
+  if (mode == MOE_GEMM_TN_DW) {
+    if (M <= 0) return MOE_ERR_INVALID_ARG;
+    if (M % 64) return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (K <= 0) return MOE_ERR_INVALID_ARG;
+    if (K % (fp8 ? 128 : 64)) return MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+  }
+  if (!ok_ptr(A) || !ok_ptr(B) || !ok_ptr(offsets) || !ok_ptr(C)) return MOE_ERR_INVALID_ARG;
+  if (fp8 && (!ok_ptr(a_scale) || !ok_ptr(b_scale))) return MOE_ERR_INVALID_ARG;
+  GemmParams p{};
+  p.mode = mode;
+  p.epi = EPI_STORE;
+  p.fp8 = fp8;
+  p.A = A;
+  p.B = B;
+  p.a_scale = a_scale;
+  p.b_scale = b_scale;
+  p.offsets = offsets;
+  p.G = G;
+  p.rows = rows;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.C = C;
+  p.c_fp32 = c_dtype == MOE_FP32;
+  return hip_status(launch_grouped_gemm(p, S(stream)));
+}
+
+moe_status_t moe_grouped_gemm_swiglu_bwd(const void* d_out, const void* w_down,
+                                         const int32_t* offsets, const void* gu_saved, int G,
+                                         int rows, int H, int I, void* dgu, void* stream) {
+  if (G <= 0 || rows < 0 || H <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 64 || I % 64 || G > 256) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!ok_ptr(d_out) || !ok_ptr(w_down) || !ok_ptr(offsets) || !ok_ptr(gu_saved) || !ok_ptr(dgu))
+    return MOE_ERR_INVALID_ARG;
+  GemmParams p{};
+  p.mode = MOE_GEMM_NT;
+  p.epi = EPI_SWIGLU_BWD;
+  p.A = d_out;
+  p.B = w_down;
+  p.offsets = offsets;
+  p.G = G;
+  p.rows = rows;
+  p.N = I;
+  p.K = H;
+  p.C = dgu;
+  p.I = I;
+  p.gu_in = gu_saved;
+  return hip_status(launch_grouped_gemm(p, S(stream)));
+}
+
+moe_status_t moe_unpermute_combine(const void* y_perm, const int32_t* row_of,
+                                   const float* topk_prob, const void* shared_out, int T,
+                                   int H, int k, void* y, void* stream) {
+  if (T < 0 || H <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
+  if (k > 32) return MOE_ERR_UNSUPPORTED;
+  if (H % 64) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(y_perm) || !ok_ptr(row_of) || !ok_ptr(y) || !opt_ptr(topk_prob) ||
+      !opt_ptr(shared_out))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(y_perm, row_of, topk_prob, shared_out, T, H, k, y, S(stream)));
+}
+
+moe_status_t moe_combine_backward(const void* dy, const int32_t* row_of, const float* topk_prob,
+                                  int T, int H, int k, void* d_out, void* stream) {
+  if (T < 0 || H <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
+  if (k > 32) return MOE_ERR_UNSUPPORTED;
+  if (H % 64) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(dy) || !ok_ptr(row_of) || !ok_ptr(topk_prob) || !ok_ptr(d_out))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_scatter_rows(dy, row_of, topk_prob, T, H, k, d_out, S(stream)));
+}
+
+moe_status_t moe_quantize_fp8_rows(const void* x, int R, int C, uint8_t* q, float* scale,
+                                   void* stream) {
+  if (R < 0 || C <= 0) return MOE_ERR_INVALID_ARG;
+  if (C % 64) return MOE_ERR_UNSUPPORTED;
+  if (R == 0) return MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(q) || !ok_ptr(scale)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_rows(x, R, C, q, scale, S(stream)));
+}
+
+moe_status_t moe_quantize_fp8_weights(const void* w, int G, int K, int N, uint8_t* q,
+                                      float* scale, void* stream) {
+  if (G <= 0 || K <= 0 || N <= 0) return MOE_ERR_INVALID_ARG;
+  if (!ok_ptr(w) || !ok_ptr(q) || !ok_ptr(scale)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_weights(w, G, K, N, q, scale, S(stream)));
+}
+
+size_t moe_workspace_bytes(const moe_problem_t* p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return make_layout(*p).total;
+}
+
+moe_status_t moe_workspace_views(const moe_problem_t* p, void* ws, size_t ws_bytes,
+                                 moe_views_t* v) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!v || !ok_ptr(ws)) return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(*p);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  uint8_t* b = (uint8_t*)ws;
+  const bool fp8 = p->dtype == MOE_FP8_E4M3;
+  v->topk_idx = (int32_t*)(b + L.topk_idx);
+  v->topk_prob = (float*)(b + L.topk_prob);
+  v->counts = (int32_t*)(b + L.counts);
+  v->offsets = (int32_t*)(b + L.offsets);
+  v->row_of = (int32_t*)(b + L.row_of);
+  v->src_of = (int32_t*)(b + L.src_of);
+  v->xp = b + L.xp;
+  v->xp_scale = fp8 ? (float*)(b + L.xp_scale) : nullptr;
+  v->gu = p->training ? b + L.gu : nullptr;
+  v->h = b + L.h;
+  v->hq = fp8 ? b + L.hq : nullptr;
+  v->h_scale = fp8 ? (float*)(b + L.h_scale) : nullptr;
+  v->out = b + L.out;
+  v->shared_h = p->shared_I ? b + L.shared_h : nullptr;
+  v->shared_out = p->shared_I ? b + L.shared_out : nullptr;
+  v->shared_offsets = (int32_t*)(b + L.shared_offsets);
+  v->d_out = p->training ? b + L.d_out : nullptr;
+  v->dgu = p->training ? b + L.dgu : nullptr;
+  v->dxp = p->training ? b + L.dxp : nullptr;
+  v->scratch = b + L.scratch;
+  v->scratch_bytes = L.scratch_bytes;
+  return MOE_OK;
+}
+
+moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* ws,
+                         size_t ws_bytes, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!t) return MOE_ERR_INVALID_ARG;
+  if (p->T == 0) return MOE_OK;
+  const bool fp8 = p->dtype == MOE_FP8_E4M3;
+  if (!ok_ptr(t->x) || !ok_ptr(t->logits) || !ok_ptr(t->w_gu) || !ok_ptr(t->w_down) ||
+      !ok_ptr(t->y))
+    return MOE_ERR_INVALID_ARG;
+  if (fp8 && (!ok_ptr(t->w_gu_scale) || !ok_ptr(t->w_down_scale))) return MOE_ERR_INVALID_ARG;
+  if (p->shared_I && (!ok_ptr(t->shared_gu) || !ok_ptr(t->shared_down)))
+    return MOE_ERR_INVALID_ARG;
+  moe_views_t v;
+  st = moe_workspace_views(p, ws, ws_bytes, &v);
+  if (st != MOE_OK) return st;
+  hipStream_t s = S(stream);
+  const int T = p->T, H = p->H, E = p->E, k = p->k, I = p->I;
+  const int N = T * k;
+
+  // 1. router
+  MOE_TRY(launch_router_topk(t->logits, T, E, k, p->score, v.topk_idx, v.topk_prob, v.counts,
+                             nullptr, nullptr, s));
+  // 2. dispatch
+  MOE_TRY(launch_dispatch_meta(v.topk_idx, T, E, k, v.offsets, v.row_of, v.src_of, v.scratch, s));
+  if (fp8) MOE_TRY(launch_scatter_rows_fp8(t->x, v.row_of, T, H, k, (uint8_t*)v.xp, v.xp_scale, s));
+  else MOE_TRY(launch_scatter_rows(t->x, v.row_of, nullptr, T, H, k, v.xp, s));
+  // 3. grouped MLP
+  GemmParams g1{};
+  g1.mode = fp8 ? MOE_GEMM_NT : MOE_GEMM_NN;
+  g1.epi = EPI_SWIGLU;
+  g1.fp8 = fp8;
+  g1.A = v.xp;
+  g1.a_scale = v.xp_scale;
+  g1.B = t->w_gu;
+  g1.b_scale = t->w_gu_scale;
+  g1.offsets = v.offsets;
+  g1.G = E;
+  g1.rows = N;
+  g1.N = 2 * I;
+  g1.K = H;
+  g1.C = v.h;
+  g1.I = I;
+  g1.gu_out = p->training ? v.gu : nullptr;
+  MOE_TRY(launch_grouped_gemm(g1, s));
+  GemmParams g2{};
+  g2.mode = fp8 ? MOE_GEMM_NT : MOE_GEMM_NN;
+  g2.epi = EPI_STORE;
+  g2.fp8 = fp8;
+  if (fp8) {
+    MOE_TRY(launch_quantize_rows(v.h, N, I, v.hq, v.h_scale, s));
+    g2.A = v.hq;
+    g2.a_scale = v.h_scale;
+  } else {
+    g2.A = v.h;
+  }
+  g2.B = t->w_down;
+  g2.b_scale = t->w_down_scale;
+  g2.offsets = v.offsets;
+  g2.G = E;
+  g2.rows = N;
+  g2.N = H;
+  g2.K = I;
+  g2.C = v.out;
+  MOE_TRY(launch_grouped_gemm(g2, s));
+  // shared expert: one dense group over all T tokens, read straight from x
+  if (p->shared_I) {
+    MOE_TRY(launch_fill_i32(v.shared_offsets, 1, 0, s));
+    MOE_TRY(launch_fill_i32(v.shared_offsets + 1, 1, T, s));
+    GemmParams s1{};
+    s1.mode = MOE_GEMM_NN;
+    s1.epi = EPI_SWIGLU;
+    s1.A = t->x;
+    s1.B = t->shared_gu;
+    s1.offsets = v.shared_offsets;
+    s1.G = 1;
+    s1.rows = T;
+    s1.N = 2 * p->shared_I;
+    s1.K = H;
+    s1.C = v.shared_h;
+    s1.I = p->shared_I;
+    MOE_TRY(launch_grouped_gemm(s1, s));
+    GemmParams s2{};
+    s2.mode = MOE_GEMM_NN;
+    s2.epi = EPI_STORE;
+    s2.A = v.shared_h;
+    s2.B = t->shared_down;
+    s2.offsets = v.shared_offsets;
+    s2.G = 1;
+    s2.rows = T;
+    s2.N = H;
+    s2.K = p->shared_I;
+    s2.C = v.shared_out;
+    MOE_TRY(launch_grouped_gemm(s2, s));
+  }
+  // 4. combine
+  MOE_TRY(launch_combine(v.out, v.row_of, v.topk_prob, p->shared_I ? v.shared_out : nullptr, T, H,
+                         k, t->y, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const void* dy,
+                          void* dx, void* dw_gu, void* dw_down, void* ws, size_t ws_bytes,
+                          void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!t || !p->training || p->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p->shared_I) return MOE_ERR_UNSUPPORTED;
+  if (!ok_ptr(t->w_gu) || !ok_ptr(t->w_down) || !ok_ptr(dw_gu) || !ok_ptr(dw_down))
+    return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!ok_ptr(dy) || !ok_ptr(dx))) return MOE_ERR_INVALID_ARG;
+  moe_views_t v;
+  st = moe_workspace_views(p, ws, ws_bytes, &v);
+  if (st != MOE_OK) return st;
+  hipStream_t s = S(stream);
+  const int T = p->T, H = p->H, E = p->E, k = p->k, I = p->I;
+  const int N = T * k;
+  if (T == 0) {
+    // no routed rows: the weight gradients are zero (the dW GEMMs see empty groups)
+    MOE_TRY(launch_fill_i32(v.offsets, E + 1, 0, s));
+  } else {
+    // combine backward: d_out[row_of[t,j]] = bf16(p[t,j] * dy[t])
+    MOE_TRY(launch_scatter_rows(dy, v.row_of, v.topk_prob, T, H, k, v.d_out, s));
+  }
+  // GEMM2 backward: dgu = SwiGLU'(d_out . W_down^T), dW_down = h^T . d_out
+  GemmParams a{};
+  a.mode = MOE_GEMM_NT;
+  a.epi = EPI_SWIGLU_BWD;
+  a.A = v.d_out;
+  a.B = t->w_down;
+  a.offsets = v.offsets;
+  a.G = E;
+  a.rows = N;
+  a.N = I;
+  a.K = H;
+  a.C = v.dgu;
+  a.I = I;
+  a.gu_in = v.gu;
+  if (N > 0) MOE_TRY(launch_grouped_gemm(a, s));
+  GemmParams b{};
+  b.mode = MOE_GEMM_TN_DW;
+  b.epi = EPI_STORE;
+  b.A = v.h;
+  b.B = v.d_out;
+  b.offsets = v.offsets;
+  b.G = E;
+  b.rows = N;
+  b.M = I;
+  b.N = H;
+  b.C = dw_down;
+  MOE_TRY(launch_grouped_gemm(b, s));
+  // GEMM1 backward: dxp = dgu . W_gu^T, dW_gu = xp^T . dgu
+  GemmParams c{};
+  c.mode = MOE_GEMM_NT;
+  c.epi = EPI_STORE;
+  c.A = v.dgu;
+  c.B = t->w_gu;
+  c.offsets = v.offsets;
+  c.G = E;
+  c.rows = N;
+  c.N = H;
+  c.K = 2 * I;
+  c.C = v.dxp;
+  if (N > 0) MOE_TRY(launch_grouped_gemm(c, s));
+  GemmParams d{};
+  d.mode = MOE_GEMM_TN_DW;
+  d.epi = EPI_STORE;
+  d.A = v.xp;
+  d.B = v.dgu;
+  d.offsets = v.offsets;
+  d.G = E;
+  d.rows = N;
+  d.M = H;
+  d.N = 2 * I;
+  d.C = dw_gu;
+  MOE_TRY(launch_grouped_gemm(d, s));
+  // dispatch backward: dx[t] = sum_j dxp[row_of[t,j]]
+  MOE_TRY(launch_combine(v.dxp, v.row_of, nullptr, nullptr, T, H, k, dx, s));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,334 @@
+// Token dispatch and combine (HBM-bound side of the path).
+//
+// Transformer Engine guide "Mixture of Experts", sections "Token dispatch" and "Token
+// combine": dispatch lays the routed (token, choice) pairs out expert-contiguously,
+// combine returns the expert outputs to token order and merges a token's k
+// contributions with the routing weights in the same pass.
+//
+// Dispatch metadata is a stable counting sort of the flattened [T,k] choices by expert:
+//   1. dispatch_hist  : per chunk of 1024 entries, a histogram over experts (LDS atomics);
+//   2. dispatch_scan  : one block; offsets[e] = exclusive scan of the totals, and each
+//                       chunk's starting row per expert;
+//   3. dispatch_rank  : one wave per chunk walks its entries in order; lanes that chose
+//                       the same expert find each other with 9 ballots (one per bit of the
+//                       id), so a row is chunk_base + rank among the earlier lanes.
+// No atomics decide any order, so the layout is deterministic and matches a stable sort.
+// Row copies read each token row once and write its k destination rows with 16-byte
+// vector accesses (scatter form: x is read exactly once).
+#include "internal.h"
+
+namespace moe {
+
+size_t permute_scratch_bytes(int T, int E, int k) {
+  size_t n = (size_t)T * k;
+  size_t chunks = (n + kPermChunk - 1) / kPermChunk;
+  return 2 * chunks * (size_t)E * sizeof(int32_t);
+}
+
+__global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ idx, int n,
+                                                            int E, int32_t* __restrict__ partial) {
+  __shared__ int h[256];
+  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kPermChunk;
+  for (int i = threadIdx.x; i < kPermChunk; i += 256) {
+    int f = base + i;
+    if (f < n) atomicAdd(&h[idx[f]], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) partial[(size_t)blockIdx.x * E + e] = h[e];
+}
+
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __restrict__ partial,
+                                                            int nchunks, int E,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ chunk_base) {
+  __shared__ int s[256];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E)
+    for (int c = 0; c < nchunks; ++c) total += partial[(size_t)c * E + e];
+  s[e] = total;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scan
+    int add = e >= o ? s[e - o] : 0;
+    __syncthreads();
+    s[e] += add;
+    __syncthreads();
+  }
+  int run = s[e] - total;
+  if (e < E) {
+    offsets[e] = run;
+    for (int c = 0; c < nchunks; ++c) {
+      chunk_base[(size_t)c * E + e] = run;
+      run += partial[(size_t)c * E + e];
+    }
+  }
+  if (e == 255) offsets[E] = s[255];
+}
+
+__global__ __launch_bounds__(64) void dispatch_rank_kernel(const int32_t* __restrict__ idx, int n,
+                                                           int k, int E,
+                                                           const int32_t* __restrict__ chunk_base,
+                                                           int32_t* __restrict__ row_of,
+                                                           int32_t* __restrict__ src_of) {
+  __shared__ int base[256];
+  const int lane = threadIdx.x;
+  const int c = blockIdx.x;
+  for (int e = lane; e < E; e += 64) base[e] = chunk_base[(size_t)c * E + e];
+  __syncthreads();
+  const uint64_t lt = lanemask_lt();
+  for (int it = 0; it < kPermChunk / 64; ++it) {
+    const int f = c * kPermChunk + it * 64 + lane;
+    const bool valid = f < n;
+    const int e = valid ? idx[f] : 0x1ff;  // 9-bit sentinel never equals a real id (< 256)
+    uint64_t peers = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(peers & lt);
+    if (valid) {
+      const int r = base[e] + rank;
+      row_of[f] = r;
+      src_of[r] = f / k;
+    }
+    __syncthreads();
+    if (valid && (peers >> lane) == 1ull) base[e] += __popcll(peers);  // last lane of the group
+    __syncthreads();
+  }
+}
+
+hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, int32_t* offsets,
+                                int32_t* row_of, int32_t* src_of, void* scratch, hipStream_t s) {
+  const int n = T * k;
+  const int nchunks = (n + kPermChunk - 1) / kPermChunk;
+  int32_t* partial = (int32_t*)scratch;
+  int32_t* chunk_base = partial + (size_t)nchunks * E;
+  if (n == 0) return launch_fill_i32(offsets, E + 1, 0, s);
+  dispatch_hist_kernel<<<nchunks, 256, 0, s>>>(topk_idx, n, E, partial);
+  dispatch_scan_kernel<<<1, 256, 0, s>>>(partial, nchunks, E, offsets, chunk_base);
+  dispatch_rank_kernel<<<nchunks, 64, 0, s>>>(topk_idx, n, k, E, chunk_base, row_of, src_of);
+  return hipGetLastError();
+}
+
+// ---- row movement ----------------------------------------------------------
+
+// xp[row_of[t,j]] = x[t] (prob == NULL), or bf16(prob[t,j] * x[t]) (combine backward).
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4_t* __restrict__ x,
+                                                           const int32_t* __restrict__ row_of,
+                                                           const float* __restrict__ prob, int H8,
+                                                           int k, u32x4_t* __restrict__ xp) {
+  __shared__ int rows[32];
+  __shared__ float p[32];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    rows[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
+    p[threadIdx.x] = prob ? prob[(size_t)t * k + threadIdx.x] : 1.f;
+  }
+  __syncthreads();
+  for (int v = threadIdx.x; v < H8; v += blockDim.x) {
+    const u32x4_t val = x[(size_t)t * H8 + v];
+    for (int j = 0; j < k; ++j) {
+      u32x4_t o = val;
+      if (prob) {
+        const float q = p[j];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(q * bf16lo(val[d]), q * bf16hi(val[d]));
+      }
+      __builtin_nontemporal_store(o, &xp[(size_t)rows[j] * H8 + v]);
+    }
+  }
+}
+
+hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, const float* prob, int T,
+                               int H, int k, void* xp, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  scatter_rows_kernel<<<T, 256, 0, s>>>((const u32x4_t*)x, row_of, prob, H / 8, k, (u32x4_t*)xp);
+  return hipGetLastError();
+}
+
+MOE_DEV float block_max_256(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+// Row-wise e4m3 quantisation helper: 8 bf16 values -> 8 codes (two u32 words).
+MOE_DEV u32x2_t quant8(const u32x4_t val, float s) {
+  u32x2_t o;
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    uint32_t c0 = f32_to_e4m3(bf16lo(val[2 * d]) / s);
+    uint32_t c1 = f32_to_e4m3(bf16hi(val[2 * d]) / s);
+    uint32_t c2 = f32_to_e4m3(bf16lo(val[2 * d + 1]) / s);
+    uint32_t c3 = f32_to_e4m3(bf16hi(val[2 * d + 1]) / s);
+    o[d] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  }
+  return o;
+}
+
+MOE_DEV float amax8(const u32x4_t val) {
+  float a = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) a = fmaxf(a, fmaxf(fabsf(bf16lo(val[d])), fabsf(bf16hi(val[d]))));
+  return a;
+}
+
+// Dispatch with dynamic per-token e4m3 quantisation: scale = amax/448 (1 for a zero row).
+__global__ __launch_bounds__(256) void scatter_rows_fp8_kernel(const u32x4_t* __restrict__ x,
+                                                               const int32_t* __restrict__ row_of,
+                                                               int H8, int k,
+                                                               u32x2_t* __restrict__ xq,
+                                                               float* __restrict__ xscale) {
+  __shared__ int rows[32];
+  __shared__ float red[8];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) rows[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
+  float a = 0.f;
+  for (int v = threadIdx.x; v < H8; v += blockDim.x) a = fmaxf(a, amax8(x[(size_t)t * H8 + v]));
+  a = block_max_256(a, red);
+  const float sc = a == 0.f ? 1.f : a / 448.0f;
+  for (int v = threadIdx.x; v < H8; v += blockDim.x) {
+    const u32x2_t q = quant8(x[(size_t)t * H8 + v], sc);
+    for (int j = 0; j < k; ++j) xq[(size_t)rows[j] * H8 + v] = q;
+  }
+  if (threadIdx.x < k) xscale[rows[threadIdx.x]] = sc;
+}
+
+hipError_t launch_scatter_rows_fp8(const void* x, const int32_t* row_of, int T, int H, int k,
+                                   uint8_t* xq, float* xscale, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  scatter_rows_fp8_kernel<<<T, 256, 0, s>>>((const u32x4_t*)x, row_of, H / 8, k, (u32x2_t*)xq,
+                                            xscale);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const u32x4_t* __restrict__ x, int C8,
+                                                            u32x2_t* __restrict__ q,
+                                                            float* __restrict__ scale) {
+  __shared__ float red[8];
+  const size_t r = blockIdx.x;
+  float a = 0.f;
+  for (int v = threadIdx.x; v < C8; v += blockDim.x) a = fmaxf(a, amax8(x[r * C8 + v]));
+  a = block_max_256(a, red);
+  const float sc = a == 0.f ? 1.f : a / 448.0f;
+  for (int v = threadIdx.x; v < C8; v += blockDim.x) q[r * C8 + v] = quant8(x[r * C8 + v], sc);
+  if (threadIdx.x == 0) scale[r] = sc;
+}
+
+hipError_t launch_quantize_rows(const void* x, int R, int C, uint8_t* q, float* scale,
+                                hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  quantize_rows_kernel<<<R, 256, 0, s>>>((const u32x4_t*)x, C / 8, (u32x2_t*)q, scale);
+  return hipGetLastError();
+}
+
+// Per-output-channel weight quantisation w[g][K][N] -> q[g][N][K], scale[g][N].
+// One block per (g, 64 columns): a column-amax pass, then 64x64 tiles transposed
+// through LDS so both the reads and the code writes are coalesced.
+__global__ __launch_bounds__(256) void quantize_weights_kernel(const uint16_t* __restrict__ w, int K,
+                                                               int N, uint8_t* __restrict__ q,
+                                                               float* __restrict__ scale) {
+  __shared__ float part[4][64];
+  __shared__ float sc[64];
+  __shared__ float tile[64][65];
+  const int g = blockIdx.y;
+  const int n0 = blockIdx.x * 64;
+  const uint16_t* wg = w + (size_t)g * K * N;
+  const int c = threadIdx.x & 63, r4 = threadIdx.x >> 6;
+  float a = 0.f;
+  if (n0 + c < N)
+    for (int kk = r4; kk < K; kk += 4) a = fmaxf(a, fabsf(bf16_to_f32(wg[(size_t)kk * N + n0 + c])));
+  part[r4][c] = a;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    float m = fmaxf(fmaxf(part[0][c], part[1][c]), fmaxf(part[2][c], part[3][c]));
+    float s = m == 0.f ? 1.f : m / 448.0f;
+    sc[c] = s;
+    if (n0 + c < N) scale[(size_t)g * N + n0 + c] = s;
+  }
+  __syncthreads();
+  uint8_t* qg = q + (size_t)g * N * K;
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      int kk = i / 64, cc = i % 64;
+      tile[kk][cc] = (k0 + kk < K && n0 + cc < N) ? bf16_to_f32(wg[(size_t)(k0 + kk) * N + n0 + cc]) : 0.f;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      int cc = i / 64, kk = i % 64;
+      if (k0 + kk < K && n0 + cc < N)
+        qg[(size_t)(n0 + cc) * K + k0 + kk] = (uint8_t)f32_to_e4m3(tile[kk][cc] / sc[cc]);
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_quantize_weights(const void* w, int G, int K, int N, uint8_t* q, float* scale,
+                                   hipStream_t s) {
+  if (G == 0 || N == 0) return hipSuccess;
+  dim3 grid((N + 63) / 64, G);
+  quantize_weights_kernel<<<grid, 256, 0, s>>>((const uint16_t*)w, K, N, q, scale);
+  return hipGetLastError();
+}
+
+// y[t] = sum_j p[t,j] * y_perm[row_of[t,j]] (+ shared[t]); fp32 sum in slot order, one
+// rounding to bf16. prob == NULL gives the unweighted sum used by the dispatch backward.
+__global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict__ yp,
+                                                      const int32_t* __restrict__ row_of,
+                                                      const float* __restrict__ prob,
+                                                      const u32x4_t* __restrict__ shared, int H8,
+                                                      int k, u32x4_t* __restrict__ y) {
+  __shared__ int rows[32];
+  __shared__ float p[32];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    rows[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
+    p[threadIdx.x] = prob ? prob[(size_t)t * k + threadIdx.x] : 1.f;
+  }
+  __syncthreads();
+  for (int v = threadIdx.x; v < H8; v += blockDim.x) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const u32x4_t val = __builtin_nontemporal_load(&yp[(size_t)rows[j] * H8 + v]);
+      const float q = p[j];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc[2 * d] = fmaf(q, bf16lo(val[d]), acc[2 * d]);
+        acc[2 * d + 1] = fmaf(q, bf16hi(val[d]), acc[2 * d + 1]);
+      }
+    }
+    if (shared) {
+      const u32x4_t sv = shared[(size_t)t * H8 + v];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc[2 * d] += bf16lo(sv[d]);
+        acc[2 * d + 1] += bf16hi(sv[d]);
+      }
+    }
+    u32x4_t o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(acc[2 * d], acc[2 * d + 1]);
+    y[(size_t)t * H8 + v] = o;
+  }
+}
+
+hipError_t launch_combine(const void* y_perm, const int32_t* row_of, const float* prob,
+                          const void* shared, int T, int H, int k, void* y, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  combine_kernel<<<T, 256, 0, s>>>((const u32x4_t*)y_perm, row_of, prob, (const u32x4_t*)shared,
+                                   H / 8, k, (u32x4_t*)y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,134 @@
+// Router: fused score function + top-k, one wavefront per token.
+//
+// Transformer Engine guide "Mixture of Experts", section "Router": the score function
+// and the top-k run in one kernel with fp32 math; outputs are the selected expert ids,
+// their routing weights, and optionally the [T,E] mask and dense weights.
+//
+// Selection works on the logits (softmax and sigmoid are strictly increasing, so they
+// select the same experts): k rounds of a wave-wide arg-max with the lower expert id
+// winning a tie, each lane holding up to four experts (E <= 256) in registers.
+// Weights: for softmax (before or after the top-k) q_j = exp(l_j - l_max) / sum over
+// the k kept logits -- the full-softmax denominator cancels in the renormalisation --
+// and sigmoid(l_j) without renormalisation for the sigmoid score.
+#include "internal.h"
+
+namespace moe {
+
+__global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_i32_kernel<<<(n + 255) / 256, 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+template <int EPL>  // experts per lane: ceil(E / 64)
+__global__ __launch_bounds__(256) void router_topk_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int score, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_prob, int32_t* __restrict__ counts, uint8_t* __restrict__ routing_map,
+    float* __restrict__ probs_dense) {
+  __shared__ int hist[256];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int waves = blockDim.x >> 6;
+  for (int t = blockIdx.x * waves + (threadIdx.x >> 6); t < T; t += gridDim.x * waves) {
+    const float* row = logits + (size_t)t * E;
+    float v[EPL];
+    bool taken[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      int e = lane + 64 * i;
+      taken[i] = e >= E;
+      v[i] = taken[i] ? 0.f : row[e];
+    }
+    int my_e = 0;
+    float my_v = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float bv = 0.f;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {  // ascending id: strict > keeps the lower id on a tie
+        if (!taken[i] && (be == 0x7fffffff || v[i] > bv)) {
+          bv = v[i];
+          be = lane + 64 * i;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        float ov = __shfl_xor(bv, o, 64);
+        int oe = __shfl_xor(be, o, 64);
+        bool other = (be == 0x7fffffff) ||
+                     (oe != 0x7fffffff && (ov > bv || (ov == bv && oe < be)));
+        if (other) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if (lane == j) {
+        my_e = be;
+        my_v = bv;
+      }
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (be == lane + 64 * i) taken[i] = true;
+    }
+    float q;
+    if (score == MOE_SIGMOID) {
+      q = 1.0f / (1.0f + expf(-my_v));
+    } else {
+      float m = __shfl(my_v, 0, 64);  // the best logit is the first choice
+      float z = lane < k ? expf(my_v - m) : 0.f;
+      q = z / wave_sum(z);
+    }
+    if (lane < k) {
+      topk_idx[(size_t)t * k + lane] = my_e;
+      topk_prob[(size_t)t * k + lane] = q;
+      atomicAdd(&hist[my_e], 1);
+    }
+    if (routing_map || probs_dense) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        int e = lane + 64 * i;
+        if (e < E) {
+          if (routing_map) routing_map[(size_t)t * E + e] = taken[i] ? 1 : 0;
+          if (probs_dense && !taken[i]) probs_dense[(size_t)t * E + e] = 0.f;
+        }
+      }
+      if (probs_dense && lane < k) probs_dense[(size_t)t * E + my_e] = q;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    if (hist[e]) atomicAdd(&counts[e], hist[e]);
+}
+
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int score,
+                              int32_t* topk_idx, float* topk_prob, int32_t* counts,
+                              uint8_t* routing_map, float* probs_dense, hipStream_t s) {
+  hipError_t err = launch_fill_i32(counts, E, 0, s);
+  if (err != hipSuccess || T == 0) return err;
+  int blocks = (T + 3) / 4;
+  if (blocks > 2048) blocks = 2048;
+  int epl = (E + 63) / 64;
+#define MOE_ROUTER_CASE(n)                                                                    \
+  case n:                                                                                     \
+    router_topk_kernel<n><<<blocks, 256, 0, s>>>(logits, T, E, k, score, topk_idx, topk_prob, \
+                                                 counts, routing_map, probs_dense);           \
+    break;
+  switch (epl) {
+    MOE_ROUTER_CASE(1)
+    MOE_ROUTER_CASE(2)
+    MOE_ROUTER_CASE(3)
+    MOE_ROUTER_CASE(4)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MOE_ROUTER_CASE
+  return hipGetLastError();
+}
+
+}  // namespace moe

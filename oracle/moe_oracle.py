@@ -272,27 +272,33 @@ def silu(g):
     return g / (1.0 + np.exp(-g))
 
 
-def grouped_gemm(a_vals, b_vals, offsets, exact=False, a_scale=None, b_scale=None):
+def grouped_gemm(a_vals, b, offsets, exact=False, a_scale=None, b_scale=None, quantize_b=False):
     """Y_e = A_e B_e for every expert block e of the rows of A [TE-MoE "Grouped GEMM":
     Y_i = X_i W_i (the pages write the weight transposed), one result block per expert,
     identical to a loop of one product per expert].
 
-    a_vals [N, K] (expert-contiguous rows), b_vals [E, K, Ncol], offsets [E+1].
-    Accumulation in float64, then one rounding to fp32. With scales (fp8 recipe):
-    Y = fp32((sum_k qa qb) * s_a[row] * s_b[e, col]).
+    a_vals [N, K] (expert-contiguous rows); b [E, K, Ncol] as values or bf16 bits
+    (converted one expert at a time); offsets [E+1]. Accumulation in float64, then one
+    rounding to fp32. Scaled (fp8 recipe): Y = fp32((sum_k qa qb) * s_a[row] * s_b[e, col]),
+    with b holding decoded codes and b_scale the column scales, or with quantize_b=True
+    each expert's weight is quantised per output column here.
     Returns float64 values of the fp32 results, [N, Ncol].
     """
     a = np.asarray(a_vals, dtype=np.float64)
-    b = np.asarray(b_vals, dtype=np.float64)
     E = b.shape[0]
     out = np.zeros((a.shape[0], b.shape[2]), dtype=np.float64)
     for e in range(E):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 == r0:
             continue
-        y = a[r0:r1] @ b[e]
+        be = as_values(b[e])
+        col_scale = None if b_scale is None else np.asarray(b_scale, np.float64)[e]
+        if quantize_b:
+            qb, sb = quantize_cols_e4m3(be)
+            be, col_scale = e4m3_decode(qb), sb.astype(np.float64)
+        y = a[r0:r1] @ be
         if a_scale is not None:
-            y = y * np.asarray(a_scale, np.float64)[r0:r1, None] * np.asarray(b_scale, np.float64)[e][None, :]
+            y = y * np.asarray(a_scale, np.float64)[r0:r1, None] * col_scale[None, :]
         out[r0:r1] = to_f32(y, exact)
     return out
 
@@ -317,16 +323,14 @@ def expert_mlp(xp_vals, w_gu_vals, w_down_vals, offsets, I, exact=False, fp8=Fal
     """
     if fp8:
         qx, sx = quantize_rows_e4m3(xp_vals)
-        qw, sw = quantize_cols_e4m3(w_gu_vals)
-        gu = grouped_gemm(e4m3_decode(qx), e4m3_decode(qw), offsets, exact, sx, sw)
+        gu = grouped_gemm(e4m3_decode(qx), w_gu_vals, offsets, exact, sx, quantize_b=True)
     else:
         gu = grouped_gemm(xp_vals, w_gu_vals, offsets, exact)
     g, u = gu[:, :I], gu[:, I:]
     h = swiglu_from_gu(g, u, exact)
     if fp8:
         qh, sh = quantize_rows_e4m3(h)
-        qd, sd = quantize_cols_e4m3(w_down_vals)
-        out = grouped_gemm(e4m3_decode(qh), e4m3_decode(qd), offsets, exact, sh, sd)
+        out = grouped_gemm(e4m3_decode(qh), w_down_vals, offsets, exact, sh, quantize_b=True)
     else:
         out = grouped_gemm(h, w_down_vals, offsets, exact)
     return {"g": g, "u": u, "h": h, "out": to_bf16(out, exact)}
@@ -338,7 +342,7 @@ def dense_mlp(x_vals, w_gu_vals, w_down_vals, I, exact=False):
     TE-MoE "Expert parallelism": shared experts are a regular dense MLP]."""
     T = x_vals.shape[0]
     offs = np.array([0, T])
-    r = expert_mlp(x_vals, w_gu_vals[None], w_down_vals[None], offs, I, exact)
+    r = expert_mlp(x_vals, np.asarray(w_gu_vals)[None], np.asarray(w_down_vals)[None], offs, I, exact)
     return r["out"]
 
 
@@ -382,11 +386,11 @@ def moe_forward(x_bits, logits, w_gu_bits, w_down_bits, k, score, I,
     idx, q, counts, rmap, dense = router_topk(logits, k, score, exact)
     offsets, row_of, src_of = dispatch_meta(idx, E)
     xp = x[src_of.astype(np.int64)]
-    mlp = expert_mlp(xp, as_values(w_gu_bits), as_values(w_down_bits), offsets, I, exact, fp8)
+    mlp = expert_mlp(xp, w_gu_bits, w_down_bits, offsets, I, exact, fp8)
     shared = None
     if shared_gu_bits is not None:
         Is = shared_down_bits.shape[0]
-        shared = dense_mlp(x, as_values(shared_gu_bits), as_values(shared_down_bits), Is, exact)
+        shared = dense_mlp(x, shared_gu_bits, shared_down_bits, Is, exact)
     y = combine(mlp["out"], row_of, q, shared, exact)
     res = dict(topk_idx=idx, topk_prob=q, counts=counts, routing_map=rmap, probs_dense=dense,
                offsets=offsets, row_of=row_of, src_of=src_of, xp=xp, shared=shared, y=y)
@@ -436,8 +440,8 @@ def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False):
     T, k = row_of.shape
     N = T * k
     H = dy.shape[1]
-    w_gu = as_values(w_gu_bits)
-    w_d = as_values(w_down_bits)
+    w_gu = np.asarray(w_gu_bits)     # converted one expert at a time inside the GEMMs
+    w_d = np.asarray(w_down_bits)
     d_out = np.zeros((N, H), dtype=np.float64)
     for j in range(k):
         d_out[row_of[:, j].astype(np.int64)] = to_bf16(dy * q[:, j:j + 1], exact)

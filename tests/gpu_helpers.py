@@ -1,0 +1,131 @@
+"""Helpers of the GPU parity tests: upload/download and the tolerance rules.
+
+Float tolerances (bf16 outputs, fp32 accumulation): rel-L2 <= 1e-2 and max-abs <= 2e-2;
+an element whose error exceeds 2e-2 is still accepted when it is within one bf16 ulp of
+the reference (two correct fp32 accumulation orders can straddle one bf16 rounding
+boundary, and one bf16 ulp exceeds 2e-2 from magnitude 4 on). fp8 outputs: rel-L2 <= 5e-2
+against the quantised oracle. Integer outputs: bit-exact.
+"""
+import numpy as np
+import torch
+
+import mixture_experts_layer_amd as M
+import oracle as O
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_vals(t):
+    """bf16 / fp32 device tensor -> float64 numpy values."""
+    if t.dtype == torch.bfloat16:
+        return O.bf16_bits_to_f64(host_bits(t))
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def bf16_ulp(ref):
+    a = np.maximum(np.abs(ref), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def check_bf16(got, ref, name, max_abs=2e-2, rel_l2=1e-2):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(got - ref) / max(nref, 1e-30)
+    diff = np.abs(got - ref)
+    bad = (diff > max_abs) & (diff > bf16_ulp(ref) * (1 + 1e-9))
+    excused = int(((diff > max_abs) & ~bad).sum())
+    info = f"{name}: rel_l2={rel:.3e} max_abs={diff.max() if diff.size else 0:.3e} excused={excused} bad={int(bad.sum())}"
+    print(info)
+    assert rel <= rel_l2, info
+    assert not bad.any(), info
+    return rel
+
+
+def check_fp8(got, ref, name, rel_l2=5e-2):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    print(f"{name}: rel_l2={rel:.3e}")
+    assert rel <= rel_l2, f"{name}: rel_l2={rel:.3e}"
+    return rel
+
+
+class GpuMoE:
+    """Uploads one workload's inputs and runs moe_forward / moe_backward through the C ABI."""
+
+    def __init__(self, w, d, training=None, canary=True):
+        self.w, self.d = w, d
+        T = d["T"]
+        self.T = T
+        self.training = w.training if training is None else training
+        self.dtype = M.MOE_FP8_E4M3 if w.fp8 else M.MOE_BF16
+        self.prob = M.problem(T, w.H, w.E, w.k, w.I, w.score, w.shared_I, self.dtype, self.training)
+        self.x = dev_bf16(d["x"])
+        self.logits = dev(d["logits"])
+        self.w_gu = dev_bf16(d["w_gu"])
+        self.w_down = dev_bf16(d["w_down"])
+        self.shared_gu = dev_bf16(d["shared_gu"]) if w.shared_I else None
+        self.shared_down = dev_bf16(d["shared_down"]) if w.shared_I else None
+        self.w_gu_scale = self.w_down_scale = None
+        if w.fp8:
+            E, H, I = w.E, w.H, w.I
+            self.w_gu_q = torch.empty((E, 2 * I, H), dtype=torch.uint8, device="cuda")
+            self.w_gu_scale = torch.empty((E, 2 * I), dtype=torch.float32, device="cuda")
+            self.w_down_q = torch.empty((E, H, I), dtype=torch.uint8, device="cuda")
+            self.w_down_scale = torch.empty((E, H), dtype=torch.float32, device="cuda")
+            M.moe_quantize_fp8_weights(self.w_gu, self.w_gu_q, self.w_gu_scale)
+            M.moe_quantize_fp8_weights(self.w_down, self.w_down_q, self.w_down_scale)
+        self.y = torch.empty((T, w.H), dtype=torch.bfloat16, device="cuda")
+        nbytes = M.moe_workspace_bytes(self.prob)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        if canary:  # NaN bit patterns everywhere: an unwritten output shows up as NaN
+            self.ws.fill_(0xFF)
+            self.y.view(torch.int16).fill_(0x7FC0)
+        self.views = M.moe_workspace_views(self.prob, self.ws)
+        self.tens = M.tensors(self.x, self.logits, self.w_gu_q if w.fp8 else self.w_gu,
+                              self.w_down_q if w.fp8 else self.w_down, self.y,
+                              self.w_gu_scale, self.w_down_scale, self.shared_gu, self.shared_down)
+
+    def forward(self):
+        M.moe_forward(self.prob, self.tens, self.ws)
+        torch.cuda.synchronize()
+        return self.y
+
+    def backward(self, dy_bits):
+        w = self.w
+        self.dy = dev_bf16(dy_bits)
+        self.dx = torch.empty((self.T, w.H), dtype=torch.bfloat16, device="cuda")
+        self.dw_gu = torch.empty((w.E, w.H, 2 * w.I), dtype=torch.bfloat16, device="cuda")
+        self.dw_down = torch.empty((w.E, w.I, w.H), dtype=torch.bfloat16, device="cuda")
+        for t in (self.dx, self.dw_gu, self.dw_down):
+            t.view(torch.int16).fill_(0x7FC0)
+        M.moe_backward(self.prob, self.tens, self.dy, self.dx, self.dw_gu, self.dw_down, self.ws)
+        torch.cuda.synchronize()
+
+    def view(self, name, shape, dtype):
+        return M.view_tensor(getattr(self.views, name), shape, dtype, self.ws)
+
+    def ints(self):
+        w, T = self.w, self.T
+        return dict(
+            topk_idx=self.view("topk_idx", (T, w.k), torch.int32).cpu().numpy(),
+            topk_prob=self.view("topk_prob", (T, w.k), torch.float32).cpu().numpy(),
+            counts=self.view("counts", (w.E,), torch.int32).cpu().numpy(),
+            offsets=self.view("offsets", (w.E + 1,), torch.int32).cpu().numpy(),
+            row_of=self.view("row_of", (T, w.k), torch.int32).cpu().numpy(),
+            src_of=self.view("src_of", (T * w.k,), torch.int32).cpu().numpy(),
+        )
