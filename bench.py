@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer hot path on one MI355X.
+
+Default workload: the Qwen3-30B-A3B-shaped MoE block, forward + backward
+(T=4096 tokens, hidden 2048, 128 experts, top-8, expert width 768, bf16), synthetic
+seeded inputs resident in HBM. One step = moe_forward + moe_backward through the C ABI
+(router, dispatch, grouped SwiGLU MLP, combine, and the expert-path backward).
+
+Prints one JSON line: whole-layer tokens/s, grouped-GEMM TFLOP/s, a roofline entry for
+the dominant kernel (timed with HIP events on the launch stream), and the CPU oracle
+timed on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # dense matrix-core peaks
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stage_costs(w, training):
+    """Algorithmic FLOPs and HBM bytes of each GEMM launch (read every input once,
+    write every output once)."""
+    N, H, I, E = w.T * w.k, w.H, w.I, w.E
+    act = 1 if w.fp8 else 2
+    c = {
+        "gemm1_swiglu": (2.0 * N * H * 2 * I,
+                         N * H * act + E * H * 2 * I * act + N * I * 2 + (N * 2 * I * 2 if training else 0)),
+        "gemm2": (2.0 * N * I * H, N * I * act + E * I * H * act + N * H * 2),
+    }
+    if training:
+        c.update({
+            "gemm2_bwd_swiglu": (2.0 * N * H * I, N * H * 2 + E * I * H * 2 + 2 * N * 2 * I * 2),
+            "dw_down": (2.0 * N * I * H, N * I * 2 + N * H * 2 + E * I * H * 2),
+            "gemm1_bwd_dx": (2.0 * N * 2 * I * H, N * 2 * I * 2 + E * H * 2 * I * 2 + N * H * 2),
+            "dw_gu": (2.0 * N * H * 2 * I, N * H * 2 + N * 2 * I * 2 + E * H * 2 * I * 2),
+        })
+    return c
+
+
+def row_costs(w, training):
+    """Algorithmic bytes of the row-movement launches."""
+    T, N, H, k = w.T, w.T * w.k, w.H, w.k
+    act = 1 if w.fp8 else 2
+    c = {
+        "permute_scatter": T * H * 2 + N * H * act + T * k * 4,
+        "combine": N * H * 2 + T * k * 8 + T * H * 2,
+    }
+    if training:
+        c["combine_bwd"] = T * H * 2 + T * k * 8 + N * H * 2
+        c["dispatch_bwd"] = N * H * 2 + T * k * 4 + T * H * 2
+    return c
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3",
+                    help="qwen3 (default, forward+backward) | mixtral | llama4 | skewed_fp8 | tiny")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the MoE path here is single-device "
+              f"(no expert parallelism); got --gpus {args.gpus}, WORLD_SIZE={world}.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_amd as M
+    import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    training = w.training
+    _log(f"bench: workload {w.name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} "
+         f"fp8={w.fp8} training={training}")
+    d = W.make_inputs(w.name)
+    dev = torch.device("cuda:0")
+    bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    x, w_gu, w_down = bf(d["x"]), bf(d["w_gu"]), bf(d["w_down"])
+    logits = torch.from_numpy(d["logits"]).to(dev)
+    shared_gu = bf(d["shared_gu"]) if w.shared_I else None
+    shared_down = bf(d["shared_down"]) if w.shared_I else None
+    dtype = M.MOE_FP8_E4M3 if w.fp8 else M.MOE_BF16
+    w_gu_s = w_down_s = None
+    if w.fp8:  # offline weight preparation, outside the timed region
+        wq = torch.empty((w.E, 2 * w.I, w.H), dtype=torch.uint8, device=dev)
+        w_gu_s = torch.empty((w.E, 2 * w.I), dtype=torch.float32, device=dev)
+        M.moe_quantize_fp8_weights(w_gu, wq, w_gu_s)
+        dq = torch.empty((w.E, w.H, w.I), dtype=torch.uint8, device=dev)
+        w_down_s = torch.empty((w.E, w.H), dtype=torch.float32, device=dev)
+        M.moe_quantize_fp8_weights(w_down, dq, w_down_s)
+        w_gu, w_down = wq, dq
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+    prob = M.problem(w.T, w.H, w.E, w.k, w.I, w.score, w.shared_I, dtype, training)
+    ws = torch.zeros(M.moe_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+    tens = M.tensors(x, logits, w_gu, w_down, y, w_gu_s, w_down_s, shared_gu, shared_down)
+    if training:
+        dy = bf(d["dy"])
+        dx = torch.empty_like(x)
+        dw_gu = torch.empty((w.E, w.H, 2 * w.I), dtype=torch.bfloat16, device=dev)
+        dw_down = torch.empty((w.E, w.I, w.H), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        M.moe_forward(prob, tens, ws)
+        if training:
+            M.moe_backward(prob, tens, dy, dx, dw_gu, dw_down, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _log(f"bench: warmup done ({args.warmup} steps)")
+
+    # ---- timed region: whole layer --------------------------------------------------
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    tokens_per_s = w.T / (ms / 1e3)
+    _log(f"bench: {args.steps} steps, {ms:.3f} ms/step, {tokens_per_s:,.0f} tokens/s")
+
+    # ---- per-kernel durations with HIP events on the launch stream -----------------
+    stream = torch.cuda.current_stream()
+    v = M.moe_workspace_views(prob, ws)
+    N, H, I, E, k, T = w.T * w.k, w.H, w.I, w.E, w.k, w.T
+    vt = lambda name, shape, dt: M.view_tensor(getattr(v, name), shape, dt, ws)
+    offs = vt("offsets", (E + 1,), torch.int32)
+    row_of = vt("row_of", (T, k), torch.int32)
+    topk_prob = vt("topk_prob", (T, k), torch.float32)
+    act_dt = torch.uint8 if w.fp8 else torch.bfloat16
+    xp = vt("xp", (N, H), act_dt)
+    h = vt("h", (N, I), torch.bfloat16)
+    out = vt("out", (N, H), torch.bfloat16)
+    gu = vt("gu", (N, 2 * I), torch.bfloat16) if training else None
+    xp_scale = vt("xp_scale", (N,), torch.float32) if w.fp8 else None
+    hq = vt("hq", (N, I), torch.uint8) if w.fp8 else None
+    h_scale = vt("h_scale", (N,), torch.float32) if w.fp8 else None
+    shared_out = vt("shared_out", (T, H), torch.bfloat16) if w.shared_I else None
+    scratch = M.view_tensor(v.scratch, (max(v.scratch_bytes, 16),), torch.uint8, ws)
+    idx_t = vt("topk_idx", (T, k), torch.int32)
+    src_of = vt("src_of", (N,), torch.int32)
+    counts = vt("counts", (E,), torch.int32)
+
+    launches = {
+        "router": lambda: M.moe_router_topk(logits, k, w.score, idx_t, topk_prob, counts),
+        "permute": lambda: M.moe_permute(x, idx_t, E, xp, offs, row_of, src_of, scratch,
+                                         dtype, xp_scale),
+        "gemm1_swiglu": lambda: M.moe_grouped_gemm_swiglu(xp, w_gu, offs, h, gu, dtype,
+                                                          xp_scale, w_gu_s),
+        "gemm2": (lambda: M.moe_grouped_gemm(M.MOE_GEMM_NT, hq, w_down, offs, out, dtype,
+                                             h_scale, w_down_s)) if w.fp8 else
+                 (lambda: M.moe_grouped_gemm(M.MOE_GEMM_NN, h, w_down, offs, out)),
+        "combine": lambda: M.moe_unpermute_combine(out, row_of, topk_prob, y, shared_out),
+    }
+    if w.fp8:
+        launches["quantize_h"] = lambda: M.moe_quantize_fp8_rows(h, hq, h_scale)
+    if training:
+        d_out = vt("d_out", (N, H), torch.bfloat16)
+        dgu = vt("dgu", (N, 2 * I), torch.bfloat16)
+        dxp = vt("dxp", (N, H), torch.bfloat16)
+        launches.update({
+            "combine_bwd": lambda: M.moe_combine_backward(dy, row_of, topk_prob, d_out),
+            "gemm2_bwd_swiglu": lambda: M.moe_grouped_gemm_swiglu_bwd(d_out, w_down, offs, gu, dgu),
+            "dw_down": lambda: M.moe_grouped_gemm(M.MOE_GEMM_TN_DW, h, d_out, offs, dw_down),
+            "gemm1_bwd_dx": lambda: M.moe_grouped_gemm(M.MOE_GEMM_NT, dgu, w_gu, offs, dxp),
+            "dw_gu": lambda: M.moe_grouped_gemm(M.MOE_GEMM_TN_DW, xp, dgu, offs, dw_gu),
+            "dispatch_bwd": lambda: M.moe_unpermute_combine(dxp, row_of, None, dx),
+        })
+    kernel_us = {}
+    for name, fn in launches.items():
+        fn()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.kernel_reps):
+            fn()
+        ev1.record(stream)
+        ev1.synchronize()
+        kernel_us[name] = ev0.elapsed_time(ev1) * 1e3 / args.kernel_reps
+    step()  # leave the workspace as one full step wrote it
+    torch.cuda.synchronize()
+    _log("bench: per-launch us " + json.dumps({k_: round(v_, 2) for k_, v_ in kernel_us.items()}))
+
+    costs = stage_costs(w, training)
+    peak_tf = MFMA_PEAK_TFLOPS["fp8" if w.fp8 else "bf16"]
+    gemm = {}
+    for name, (fl, by) in costs.items():
+        t = kernel_us[name] * 1e-6
+        gemm[name] = {"us": round(kernel_us[name], 2), "tflops": round(fl / t / 1e12, 1),
+                      "mfma_frac": round(fl / t / 1e12 / peak_tf, 4),
+                      "gbs": round(by / t / 1e9, 1), "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+    gemm_flops = sum(fl for fl, _ in costs.values())
+    gemm_time = sum(kernel_us[n] for n in costs) * 1e-6
+    rows = {}
+    for name, by in row_costs(w, training).items():
+        key = "permute" if name == "permute_scatter" else name
+        t = kernel_us[key] * 1e-6
+        rows[name] = {"us": round(kernel_us[key], 2), "gbs": round(by / t / 1e9, 1),
+                      "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+    # dominant kernel: the GEMM launch with the longest duration
+    dom = max(costs, key=lambda n: kernel_us[n])
+    fl, by = costs[dom]
+    t_dom = kernel_us[dom] * 1e-6
+    t_at_mfma, t_at_hbm = fl / (peak_tf * 1e12), by / (HBM_PEAK_GBS * 1e9)
+    if t_at_mfma >= t_at_hbm:
+        roof = {"bound": "mfma", "achieved": round(fl / t_dom / 1e12, 2), "peak": peak_tf,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(by / t_dom / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["launch_us"] = round(kernel_us[dom], 2)
+
+    # ---- CPU oracle on a bounded sample -----------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        from threadpoolctl import threadpool_info
+        S = min(args.cpu_sample_tokens, w.T)
+        _log(f"bench: timing the CPU oracle on {S} tokens")
+        tc0 = time.perf_counter()
+        r = O.moe_forward(d["x"][:S], d["logits"][:S], d["w_gu"], d["w_down"], w.k, w.score,
+                          w.I, d.get("shared_gu"), d.get("shared_down"), fp8=w.fp8)
+        if training:
+            O.moe_backward(r, d["dy"][:S], d["w_gu"], d["w_down"], w.I)
+        tc = time.perf_counter() - tc0
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+        cpu = {"value": round(S / tc, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"first {S} of the {w.T} tokens, full weights, "
+                         f"{'forward+backward' if training else 'forward'}; {tc:.1f} s"}
+        _log(f"bench: oracle {S} tokens in {tc:.1f} s")
+
+    res = {
+        "metric": "MoE layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), Qwen3-30B-A3B block",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if w.fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}-shaped MoE block " + ("forward+backward" if training else "forward"),
+                   "T": w.T, "H": w.H, "E": w.E, "top_k": w.k, "I": w.I, "shared_I": w.shared_I,
+                   "score": ["softmax_pre_renorm", "softmax_post", "sigmoid"][w.score],
+                   "parallelism": "single GPU"},
+        "grouped_gemm_tflops": round(gemm_flops / gemm_time / 1e12, 1),
+        "grouped_gemm_mfma_frac": round(gemm_flops / gemm_time / 1e12 / peak_tf, 4),
+        "gemm": gemm,
+        "rows": rows,
+        "kernel_us": {k_: round(v_, 2) for k_, v_ in kernel_us.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -40,13 +40,18 @@ def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
-    """float32 -> bfloat16 bits, round to nearest, ties to even (NaN -> quiet NaN)."""
+    """float32 -> bfloat16 bits, round to nearest, ties to even (NaN -> quiet NaN).
+
+    Adds 0x7FFF plus the lowest kept bit to the fp32 pattern and keeps the top half;
+    for every non-NaN input the sum fits in 32 bits.
+    """
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    keep_lsb = (u >> 16) & 1
-    r = (u + 0x7FFF + keep_lsb) >> 16
-    r = np.where(np.isnan(a), ((u >> 16) & 0x8000) | 0x7FC0, r)
-    return r.astype(np.uint16)
+    u = a.view(np.uint32)
+    r = ((u + (np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1)))) >> 16).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        r[nan] = ((u[nan] >> 16) & 0x8000) | 0x7FC0
+    return r
 
 
 def as_values(a) -> np.ndarray:
@@ -407,10 +412,11 @@ def swiglu_backward(dh, g, u, exact=False):
     return to_bf16(dg, exact), to_bf16(du, exact)
 
 
-def grouped_gemm_dw(a_vals, b_vals, offsets, exact=False):
+def grouped_gemm_dw(a_vals, b_vals, offsets, exact=False, out_bf16=False):
     """dW_e = A_e^T B_e over the rows of each expert block (reduction over that expert's
     routed rows) [TE-MoE "Example": every stage is differentiable]. An expert with no
-    rows gets a zero gradient. Returns fp32 values [E, Ka, Kb]."""
+    rows gets a zero gradient. Returns fp32 values [E, Ka, Kb] (bf16 values when
+    out_bf16: fp32 then bf16, one expert at a time)."""
     a = np.asarray(a_vals, dtype=np.float64)
     b = np.asarray(b_vals, dtype=np.float64)
     E = len(offsets) - 1
@@ -418,7 +424,8 @@ def grouped_gemm_dw(a_vals, b_vals, offsets, exact=False):
     for e in range(E):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 > r0:
-            out[e] = to_f32(a[r0:r1].T @ b[r0:r1], exact)
+            y = to_f32(a[r0:r1].T @ b[r0:r1], exact)
+            out[e] = to_bf16(y, exact) if out_bf16 else y
     return out
 
 
@@ -450,9 +457,9 @@ def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False):
     g_saved, u_saved = to_bf16(fwd["g"], exact), to_bf16(fwd["u"], exact)
     dg, du = swiglu_backward(dh, g_saved, u_saved, exact)
     dgu = np.concatenate([dg, du], axis=1)
-    dw_down = to_bf16(grouped_gemm_dw(fwd["h"], d_out, offsets, exact), exact)
+    dw_down = grouped_gemm_dw(fwd["h"], d_out, offsets, exact, out_bf16=True)
     # GEMM1 backward
     dxp = to_bf16(grouped_gemm(dgu, np.swapaxes(w_gu, 1, 2), offsets, exact), exact)
-    dw_gu = to_bf16(grouped_gemm_dw(fwd["xp"], dgu, offsets, exact), exact)
+    dw_gu = grouped_gemm_dw(fwd["xp"], dgu, offsets, exact, out_bf16=True)
     dx = combine(dxp, row_of, None, None, exact)
     return dict(d_out=d_out, dh=dh, dgu=dgu, dxp=dxp, dx=dx, dw_gu=dw_gu, dw_down=dw_down)

@@ -9,7 +9,8 @@ import torch
 import mixture_experts_layer_amd as M
 import oracle as O
 import workloads as W
-from gpu_helpers import GpuMoE, check_bf16, check_fp8, dev, dev_bf16, host_bits, host_vals
+from gpu_helpers import (GpuMoE, check_bf16, check_fp8, combine_slack, dev, dev_bf16, host_bits,
+                         host_vals)
 
 pytestmark = pytest.mark.gpu
 
@@ -330,7 +331,8 @@ def test_forward_parity_small(name):
     if w.fp8:
         check_fp8(host_vals(y), ref["y"], f"{name} y")
     else:
-        check_bf16(host_vals(y), ref["y"], f"{name} y")
+        slack = combine_slack(ref["out"], ref["row_of"], ref["topk_prob"], ref["shared"])
+        check_bf16(host_vals(y), ref["y"], f"{name} y", slack=slack)
         N = w.T * w.k
         check_bf16(host_vals(g.view("h", (N, w.I), torch.bfloat16)), ref["h"], f"{name} h")
 
@@ -345,7 +347,7 @@ def test_backward_parity_small(name):
     g.backward(d["dy"])
     ref = O.moe_forward(d["x"], d["logits"], d["w_gu"], d["w_down"], w.k, w.score, w.I)
     rb = O.moe_backward(ref, d["dy"], d["w_gu"], d["w_down"], w.I)
-    check_bf16(host_vals(g.dx), rb["dx"], f"{name} dx")
+    check_bf16(host_vals(g.dx), rb["dx"], f"{name} dx", slack=combine_slack(rb["dxp"], ref["row_of"]))
     check_bf16(host_vals(g.dw_gu), rb["dw_gu"], f"{name} dw_gu")
     check_bf16(host_vals(g.dw_down), rb["dw_down"], f"{name} dw_down")
 
