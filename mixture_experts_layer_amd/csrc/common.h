@@ -24,14 +24,20 @@ MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 
 MOE_DEV float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 MOE_DEV float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16, round to nearest even; NaN -> quiet NaN of the same sign.
-MOE_DEV uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// fp32 -> bf16, round to nearest even (the hardware convert, v_cvt_pk_bf16_f32).
+MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
-MOE_DEV uint32_t pack_bf16x2(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
+MOE_DEV uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
+
+// Logistic function from the hardware 2^x and reciprocal (about 1 ulp each):
+// 1 / (1 + 2^(-x log2 e)). Saturates to 0 / 1 for large |x|.
+MOE_DEV float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
 
 // ---- OCP FP8 E4M3 ("fn": no infinities, max 448) ---------------------------
 // Round to nearest even, saturating to +-448. Works on the fp32 bit pattern:

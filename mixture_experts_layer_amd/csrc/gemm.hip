@@ -7,88 +7,149 @@
 // on a fused gate/up weight) and FC2 is a separate grouped GEMM.
 //
 // Design (gfx950, wave64):
-//  * 128x128 output tile per 256-thread block, four waves in a 2x2 grid, each wave a
-//    64x64 sub-tile of four 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16, or
-//    v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales for e4m3).
-//  * K is staged 128 bytes at a time (64 bf16 or 128 e4m3) through two LDS buffers
-//    (double buffering: the next tile's global loads are in flight while the MFMAs
-//    consume the current one). Rows are padded to 144 bytes so the 16-byte fragment
-//    reads of 16 consecutive rows hit distinct banks.
-//  * Both operands are stored K-contiguous in LDS. Operands that are contiguous along
-//    M or N in memory (the weight of the NN forward, both operands of the weight
-//    gradient) are loaded as 8x8 bf16 blocks and transposed in registers before the
-//    LDS write.
+//  * Block tile BM x BN, WM x WN waves; each wave owns (BM/WM) x (BN/WN) outputs as
+//    32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16, or v_mfma_scale_f32_32x32x64_f8f6f4
+//    with unit scales for e4m3). A wave's M blocks are interleaved (wave wm takes
+//    blocks wm, wm+WM, ...) so the blocks past a group's last row, which are skipped,
+//    are spread over the waves.
+//  * K advances 128 bytes per stage (64 bf16 or 128 e4m3). Operands go from global
+//    memory straight into an LDS ring of STAGES buffers with 16-byte
+//    global_load_lds (no staging registers, no VALU copies); the loads for stage
+//    kt+STAGES-1 are in flight while stage kt is multiplied.
+//  * LDS layouts. K-contiguous operands: rows of 128 bytes, the 16-byte chunk index
+//    XORed with (row/2)%8, so the fragment reads of 16 consecutive rows hit distinct
+//    banks. M- or N-contiguous operands (the bf16 weight of the NN forward, both
+//    operands of the weight gradient): rows of k, the 64-byte segment index XORed with
+//    k%4, read with ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one
+//    column (two reads form the 8-element MFMA operand). The swizzles are applied on
+//    the global side because global_load_lds places lane l's 16 bytes at base + 16*l.
+//  * Rows past a group's end and columns past N load from a zero block; the weight
+//    gradient's ragged reduction is zero-padded the same way.
+//  * Epilogue through LDS: accumulators (converted, or consumed by SwiGLU / SwiGLU
+//    backward) are staged row-major and written with 16-byte stores.
 //  * Tile schedule on the device: every block rebuilds the prefix of per-group M-tile
 //    counts from offsets[] in LDS, so any row split works with no host sync and no
 //    padding. Tiles are ordered (group, N-tile, M-tile) so the M-tiles that share one
 //    weight panel are neighbours, and block ids are remapped so that neighbours land
 //    on the same XCD (blocks are dispatched round-robin over the 8 XCDs, each with
 //    its own L2).
+#include <type_traits>
+
 #include "internal.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int BM = 128, BN = 128;
-constexpr int BKB = 128;                    // K bytes per stage
-constexpr int PITCH = BKB + 16;             // padded LDS row pitch, bytes
-constexpr int REGION_A = BM * PITCH;
-constexpr int STAGE = (BM + BN) * PITCH;    // 36864 bytes
-constexpr int NT = 256;
+constexpr int BKB = 128;  // K bytes per stage
 
-MOE_DEV uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-MOE_DEV uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+__device__ __attribute__((aligned(256))) uint8_t g_zero_block[4096];  // stays zero
 
-// 8x8 bf16 transpose: in[i] holds columns 0..7 of row i; out[j] holds rows 0..7 of column j.
-MOE_DEV void transpose8x8(const u32x4_t in[8], u32x4_t out[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t a = in[2 * d][j >> 1], b = in[2 * d + 1][j >> 1];
-      out[j][d] = (j & 1) ? hi_pair(a, b) : lo_pair(a, b);
-    }
-  }
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Workgroup barrier for the LDS ring. The memory clobbers keep the compiler from moving
+// LDS accesses across it without emitting any wait: the producers' completion is
+// established by the explicit vmcnt wait before it (global_load_lds) and by the
+// consumers' own lgkmcnt waits (their fragments feed MFMAs issued before it).
+MOE_DEV void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+MOE_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 16 bytes per lane from global memory straight into LDS at M0 + 16*lane.
+// Issued from inline asm so the compiler does not track it as an LDS write (its
+// conservative tracking would wait for every DMA in flight before any LDS read); the
+// instruction has no result registers, and its address and M0 are read at issue. The
+// kernel orders these writes itself with explicit vmcnt waits and barriers.
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+MOE_DEV void load_lds16(const void* g, uint8_t* lds) {
+  const unsigned m0 = (unsigned)(uintptr_t)((lds_u8_t*)lds);
+  // one wait state between the M0 write and the LDS-DMA that reads it
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+struct Cfg {
+  static constexpr int NW = WM * WN;
+  static constexpr int NT = NW * 64;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int MB = TM / 32, NB = TN / 32;
+  static constexpr int A_BYTES = BM * BKB, B_BYTES = BN * BKB;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int SMEM = STAGE * STAGES;
+  static constexpr int A_LOADS = BM / 8 / NW, B_LOADS = BN / 8 / NW;  // 1 KB chunks per wave
+  static constexpr int LOADS = A_LOADS + B_LOADS;
+  static_assert(MB >= 1 && NB >= 1, "wave tile");
+  static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "load split");
+};
 
 struct Tile {
   int g;
-  int m0;          // first row (NN/NT: absolute row of the buffer; DW: first M index)
+  int m0;          // NN/NT: first buffer row of the tile; DW: first M index
   int n0;          // first output column (SWIGLU: first h column)
-  int rows_valid;  // NN/NT: rows of this tile inside the group
+  int rows_valid;  // NN/NT: rows of this tile inside the group; DW: BM
   int kcount;      // DW: rows of the group (the reduction length)
   int kbase;       // DW: first row of the group
 };
 
-template <int MODE, int EPI>
-MOE_DEV int n_tiles(const GemmParams& p) {
-  if (EPI == EPI_SWIGLU) return p.I / (BN / 2);
-  return (p.N + BN - 1) / BN;
+// Global source of one 1 KB chunk-load of a K-contiguous operand tile.
+// Lane l fills LDS row (chunk*8 + l/8), physical 16-byte slot l%8; the logical
+// chunk held there is slot ^ ((row >> 1) & 7).
+MOE_DEV int kc_row(int chunk, int lane) { return chunk * 8 + (lane >> 3); }
+MOE_DEV int kc_logical(int row, int lane) { return (lane & 7) ^ ((row >> 1) & 7); }
+
+// M/N-contiguous operand tile: 64 k-rows of W bytes (W = 2*cols). Lane l of chunk c
+// fills row (c*1024 + 16*l) / W at physical offset (16*l) % W; the physical 64-byte
+// segment is the logical one XOR (k & 3).
+template <int COLS>
+MOE_DEV void mn_slot(int chunk, int lane, int& k, int& logical_byte) {
+  constexpr int W = COLS * 2;
+  const int byte = chunk * 1024 + lane * 16;
+  k = byte / W;
+  const int phys = byte % W;
+  logical_byte = (((phys >> 6) ^ (k & 3)) << 6) | (phys & 63);
 }
 
-// Column of the B operand held by LDS row c of this tile.
-template <int EPI>
-MOE_DEV int bcol(const GemmParams& p, int n0, int c) {
-  if (EPI == EPI_SWIGLU) return c < BN / 2 ? n0 + c : p.I + n0 + c - BN / 2;
-  return n0 + c;
+// LDS byte offset of element (k, col) in an M/N-contiguous tile.
+template <int COLS>
+MOE_DEV int mn_offset(int k, int col) {
+  const int byte = col * 2;
+  return k * (COLS * 2) + ((((byte >> 6) ^ (k & 3)) << 6) | (byte & 63));
 }
 
 }  // namespace
 
-template <int MODE, int EPI, bool FP8>
-__global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(const GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const GemmParams p) {
+  using C = Cfg<BM, BN, WM, WN, STAGES>;
+  static_assert(STAGES == 3, "the ring below is written for three stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[C::STAGE];
   __shared__ int s_pref[264];
+  static_assert(EPI != EPI_SWIGLU || C::NB == 2, "SwiGLU wave tile: one gate + one up block");
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int ntn = n_tiles<MODE, EPI>(p);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases stay scalar
+  const int wm = wave / WN, wn = wave % WN;
+  constexpr bool DW = MODE == MOE_GEMM_TN_DW;
+  constexpr bool B_MN = (MODE == MOE_GEMM_NN) || DW;  // B tile M/N-contiguous in memory
+  constexpr int HB = BN / 2;                           // SwiGLU: h columns per tile
+  const int ntn = EPI == EPI_SWIGLU ? p.I / HB : (p.N + BN - 1) / BN;
 
   // ---- tile schedule ------------------------------------------------------------
   int total;
-  if (MODE != MOE_GEMM_TN_DW) {
+  if (!DW) {
     if (wave == 0) {
       const int per = (p.G + 63) / 64;
       int loc[5];
@@ -97,10 +158,7 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(const GemmParams p)
       for (int i = 0; i < 5; ++i) {
         const int g = lane * per + i;
         int mt = 0;
-        if (i < per && g < p.G) {
-          const int cnt = p.offsets[g + 1] - p.offsets[g];
-          mt = (cnt + BM - 1) / BM;
-        }
+        if (i < per && g < p.G) mt = (p.offsets[g + 1] - p.offsets[g] + BM - 1) / BM;
         sum += mt;
         loc[i] = sum;
       }
@@ -131,7 +189,7 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(const GemmParams p)
     tile = xcd * base + (xcd < rem ? xcd : rem) + i;
   }
   Tile t;
-  if (MODE != MOE_GEMM_TN_DW) {
+  if (!DW) {
     int lo = 0, hi = p.G;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -146,7 +204,7 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(const GemmParams p)
     t.g = g;
     t.m0 = gbeg + mtile * BM;
     t.rows_valid = min(BM, cnt - mtile * BM);
-    t.n0 = ntile * (EPI == EPI_SWIGLU ? BN / 2 : BN);
+    t.n0 = ntile * (EPI == EPI_SWIGLU ? HB : BN);
     t.kcount = p.K;
     t.kbase = 0;
   } else {
@@ -160,288 +218,481 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(const GemmParams p)
     t.kcount = p.offsets[g + 1] - t.kbase;
   }
 
-  // ---- operand addressing ---------------------------------------------------------
-  // Each thread stages eight 16-byte global loads per K step.
-  //  NT: all threads: rows (i*32 + tid/8) of A (i < 4) and of B (i >= 4), chunk tid%8.
-  //  NN: threads 0..127 load one 8(k) x 8(n) block of B_g[K,N] (k block tid%8, column
-  //      block tid/8) and transpose it; threads 128..255 load eight K-contiguous
-  //      chunks of A, rows (tid-128)/8 + 16*i, chunk (tid-128)%8.
-  //  DW: threads 0..127 transpose an 8x8 block of A[rows,M], threads 128..255 one of
-  //      B[rows,N] (the reduction runs over the group's rows).
-  const int q = tid & 127;
-  const bool lower = tid < 128;
-  const int kb = q & 7, nb = q >> 3;          // 8x8 block coordinates
+  t.g = __builtin_amdgcn_readfirstlane(t.g);
+  t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+  t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+  t.rows_valid = __builtin_amdgcn_readfirstlane(t.rows_valid);
+  t.kcount = __builtin_amdgcn_readfirstlane(t.kcount);
+  t.kbase = __builtin_amdgcn_readfirstlane(t.kbase);
+
+  // ---- load descriptors: a global pointer per 1 KB chunk-load, advanced per stage ----
   const int esz = FP8 ? 1 : 2;
-  const uint8_t* src[8];                      // K-contiguous row pointers
-  const uint16_t* blk = nullptr;              // 8x8 block source (row kb*8 of the tile)
-  int blk_ld = 0;                             // its leading dimension, elements
-  bool blk_ok = true;
+  const uint8_t* zero = g_zero_block;
+  const uint8_t* a_src[C::A_LOADS];
+  const uint8_t* b_src[C::B_LOADS];
+  size_t a_step, b_step;      // bytes per stage
+  int a_krow[C::A_LOADS], b_krow[C::B_LOADS];  // DW: k row of the chunk lane (zero past kcount)
   int nk;
-  if (MODE != MOE_GEMM_TN_DW) {
+  if (!DW) {
     const size_t lda = (size_t)p.K * esz;
-    const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.N * lda;
-    if (MODE == MOE_GEMM_NT) {
+    nk = (int)(lda / BKB);
+    a_step = BKB;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = min(i * 32 + (tid >> 3), t.rows_valid - 1);
-        src[i] = (const uint8_t*)p.A + (size_t)(t.m0 + r) * lda + (tid & 7) * 16;
-        const int c = min(bcol<EPI>(p, t.n0, i * 32 + (tid >> 3)), p.N - 1);
-        src[4 + i] = bg + (size_t)c * lda + (tid & 7) * 16;
+    for (int i = 0; i < C::A_LOADS; ++i) {
+      const int chunk = wave + C::NW * i;
+      const int row = kc_row(chunk, lane);
+      a_src[i] = row < t.rows_valid
+                     ? (const uint8_t*)p.A + (size_t)(t.m0 + row) * lda + kc_logical(row, lane) * 16
+                     : zero;
+      a_krow[i] = 0;
+    }
+    if (!B_MN) {  // NT: B_g is [N, K]
+      b_step = BKB;
+      const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.N * lda;
+#pragma unroll
+      for (int i = 0; i < C::B_LOADS; ++i) {
+        const int chunk = wave + C::NW * i;
+        const int row = kc_row(chunk, lane);
+        int col = row;
+        if (EPI == EPI_SWIGLU) col = row < HB ? t.n0 + row : p.I + t.n0 + row - HB;
+        else col = t.n0 + row;
+        b_src[i] = col < p.N ? bg + (size_t)col * lda + kc_logical(row, lane) * 16 : zero;
+        b_krow[i] = 0;
       }
-    } else if (lower) {  // NN, B block
-      const int c = bcol<EPI>(p, t.n0, nb * 8);
-      blk_ok = c < p.N;
-      blk_ld = p.N;
-      blk = (const uint16_t*)p.B + (size_t)t.g * p.K * p.N + (size_t)(kb * 8) * p.N + (blk_ok ? c : 0);
-    } else {             // NN, A chunks
+    } else {      // NN: B_g is [K, N]
+      b_step = (size_t)64 * p.N * 2;
+      const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.K * p.N * 2;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = min((q >> 3) + 16 * i, t.rows_valid - 1);
-        src[i] = (const uint8_t*)p.A + (size_t)(t.m0 + r) * lda + (q & 7) * 16;
+      for (int i = 0; i < C::B_LOADS; ++i) {
+        const int chunk = wave + C::NW * i;
+        int k, lb;
+        mn_slot<BN>(chunk, lane, k, lb);
+        const int c = lb / 2;  // column within the tile
+        int col;
+        if (EPI == EPI_SWIGLU) col = c < HB ? t.n0 + c : p.I + t.n0 + c - HB;
+        else col = t.n0 + c;
+        b_src[i] = col < p.N ? bg + ((size_t)k * p.N + col) * 2 : zero;
+        b_krow[i] = 0;
       }
     }
-    nk = (int)(lda / BKB);
   } else {
-    const int ld = lower ? p.M : p.N;
-    const int c = (lower ? t.m0 : t.n0) + nb * 8;
-    blk_ok = c < ld;
-    blk_ld = ld;
-    blk = (const uint16_t*)(lower ? p.A : p.B) + (size_t)(t.kbase + kb * 8) * ld + (blk_ok ? c : 0);
     nk = (t.kcount + 63) / 64;
+    a_step = (size_t)64 * p.M * 2;
+    b_step = (size_t)64 * p.N * 2;
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i) {
+      const int chunk = wave + C::NW * i;
+      int k, lb;
+      mn_slot<BM>(chunk, lane, k, lb);
+      const int col = t.m0 + lb / 2;
+      a_krow[i] = col < p.M ? k : 0x40000000;  // never valid when the column is out of range
+      a_src[i] = (const uint8_t*)p.A + ((size_t)(t.kbase + k) * p.M + (col < p.M ? col : 0)) * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_LOADS; ++i) {
+      const int chunk = wave + C::NW * i;
+      int k, lb;
+      mn_slot<BN>(chunk, lane, k, lb);
+      const int col = t.n0 + lb / 2;
+      b_krow[i] = col < p.N ? k : 0x40000000;
+      b_src[i] = (const uint8_t*)p.B + ((size_t)(t.kbase + k) * p.N + (col < p.N ? col : 0)) * 2;
+    }
   }
 
-  u32x4_t st[8];
-
-  auto load_stage = [&](int kt) {
-    const bool is_blk = (MODE == MOE_GEMM_TN_DW) || (MODE == MOE_GEMM_NN && lower);
-    if (!is_blk) {
-      const size_t kbyte = (size_t)kt * BKB;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) st[i] = *(const u32x4_t*)(src[i] + kbyte);
+  // Load slot i < LOADS of stage kt: A chunk-loads first, then B.
+  auto issue_one = [&](int kt, uint8_t* sa, int i) __attribute__((always_inline)) {
+    if (i < C::A_LOADS) {
+      const uint8_t* src;
+      if (DW) src = (kt * 64 + a_krow[i] < t.kcount) ? a_src[i] + (size_t)kt * a_step : zero;
+      else src = a_src[i] == zero ? zero : a_src[i] + (size_t)kt * a_step;
+      load_lds16(src, sa + (wave + C::NW * i) * 1024);
     } else {
-      const uint16_t* s0 = blk + (size_t)kt * 64 * blk_ld;
-      const int krow = kt * 64 + kb * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool in = blk_ok && (MODE != MOE_GEMM_TN_DW || krow + i < t.kcount);
-        st[i] = in ? *(const u32x4_t*)(s0 + (size_t)i * blk_ld) : u32x4_t{0, 0, 0, 0};
-      }
+      const int j = i - C::A_LOADS;
+      const uint8_t* src;
+      if (DW) src = (kt * 64 + b_krow[j] < t.kcount) ? b_src[j] + (size_t)kt * b_step : zero;
+      else src = b_src[j] == zero ? zero : b_src[j] + (size_t)kt * b_step;
+      load_lds16(src, sa + C::A_BYTES + (wave + C::NW * j) * 1024);
     }
   };
-
-  auto store_stage = [&](int buf) {
-    uint8_t* sa = smem + buf * STAGE;
-    uint8_t* sb = sa + REGION_A;
-    if (MODE == MOE_GEMM_NT) {
+  auto issue_stage = [&](int kt, uint8_t* sa) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *(u32x4_t*)(sa + (i * 32 + (tid >> 3)) * PITCH + (tid & 7) * 16) = st[i];
-        *(u32x4_t*)(sb + (i * 32 + (tid >> 3)) * PITCH + (tid & 7) * 16) = st[4 + i];
-      }
-    } else if (MODE == MOE_GEMM_NN && !lower) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *(u32x4_t*)(sa + ((q >> 3) + 16 * i) * PITCH + (q & 7) * 16) = st[i];
-    } else {
-      uint8_t* dst = (MODE == MOE_GEMM_NN || !lower) ? sb : sa;
-      u32x4_t tr[8];
-      transpose8x8(st, tr);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) *(u32x4_t*)(dst + (nb * 8 + j) * PITCH + kb * 16) = tr[j];
-    }
+    for (int i = 0; i < C::LOADS; ++i) issue_one(kt, sa, i);
   };
 
-  f32x16_t acc[2][2];
+  // ---- fragments --------------------------------------------------------------------
+  f32x16_t acc[C::MB][C::NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < C::NB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // LDS rows of this lane's fragments
-  const int arow0 = wm * 64 + (lane & 31);
-  int brow[2];
-  if (EPI == EPI_SWIGLU) {
-    brow[0] = wn * 32 + (lane & 31);            // gate columns
-    brow[1] = BN / 2 + wn * 32 + (lane & 31);   // up columns
-  } else {
-    brow[0] = wn * 64 + (lane & 31);
-    brow[1] = wn * 64 + 32 + (lane & 31);
-  }
-  const int khalf = lane >> 5;
+  // M blocks of this wave that hold at least one valid row (wave-uniform)
+  int mb_live = 0;
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i)
+    if ((wm + WM * i) * 32 < t.rows_valid) mb_live = i + 1;
+  mb_live = __builtin_amdgcn_readfirstlane(mb_live);
+  nk = __builtin_amdgcn_readfirstlane(nk);
 
-  auto compute_stage = [&](int buf) {
-    const uint8_t* sa = smem + buf * STAGE;
-    const uint8_t* sb = sa + REGION_A;
-    if (!FP8) {
+  // B block column (within the tile) of N block j of this wave
+  auto bcol0 = [&](int j) __attribute__((always_inline)) {
+    if (EPI == EPI_SWIGLU) return j == 0 ? wn * 32 : HB + wn * 32;
+    return (wn * C::NB + j) * 32;
+  };
+
+  const int l32 = lane & 31, khalf = lane >> 5;
+  // tr16 address pattern: row (k) and column offset of this lane's 4-element source
+  const int tr_k = khalf * 8 + ((lane & 15) >> 2);
+  const int tr_c = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+
+  auto kc_frag = [&](const uint8_t* base, int row, int chunk) __attribute__((always_inline)) -> u32x4_t {
+    return *(const u32x4_t*)(base + row * BKB + ((chunk ^ ((row >> 1) & 7)) << 4));
+  };
+  // Fragment loads of k sub-step ks into registers.
+  auto load_frags = [&](auto MBL_c, const uint8_t* sa, int ks, auto& af, auto& bfr) __attribute__((always_inline)) {
+    constexpr int MBL = decltype(MBL_c)::value;
+    const uint8_t* sb = sa + C::A_BYTES;
+    if constexpr (!FP8) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        bf16x8_t af[2], bfr[2];
+      for (int i = 0; i < MBL; ++i) {
+        const int r0 = (wm + WM * i) * 32;
+        if constexpr (!DW) {
+          af[i] = __builtin_bit_cast(bf16x8_t, kc_frag(sa, r0 + l32, ks * 2 + khalf));
+        } else {
+          const int k = ks * 16 + tr_k;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(sa + mn_offset<BM>(k, r0 + tr_c)));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(sa + mn_offset<BM>(k + 4, r0 + tr_c)));
+          af[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      }
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-          af[mi] = *(const bf16x8_t*)(sa + (arow0 + mi * 32) * PITCH + ks * 32 + khalf * 16);
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          bfr[ni] = *(const bf16x8_t*)(sb + brow[ni] * PITCH + ks * 32 + khalf * 16);
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 2; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+      for (int j = 0; j < C::NB; ++j) {
+        const int c0 = bcol0(j);
+        if constexpr (!B_MN) {
+          bfr[j] = __builtin_bit_cast(bf16x8_t, kc_frag(sb, c0 + l32, ks * 2 + khalf));
+        } else {
+          const int k = ks * 16 + tr_k;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(sb + mn_offset<BN>(k, c0 + tr_c)));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(sb + mn_offset<BN>(k + 4, c0 + tr_c)));
+          bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
       }
     } else {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        i32x8_t af[2], bfr[2];
+      for (int i = 0; i < MBL; ++i) {
+        const int r = (wm + WM * i) * 32 + l32;
+        const u32x4_t x0 = kc_frag(sa, r, ks * 4 + khalf * 2);
+        const u32x4_t x1 = kc_frag(sa, r, ks * 4 + khalf * 2 + 1);
+        af[i] = i32x8_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                        (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      }
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          const uint8_t* src = sa + (arow0 + mi * 32) * PITCH + ks * 64 + khalf * 32;
-          const u32x4_t x0 = *(const u32x4_t*)src, x1 = *(const u32x4_t*)(src + 16);
-          af[mi] = i32x8_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                           (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-        }
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const uint8_t* src = sb + brow[ni] * PITCH + ks * 64 + khalf * 32;
-          const u32x4_t x0 = *(const u32x4_t*)src, x1 = *(const u32x4_t*)(src + 16);
-          bfr[ni] = i32x8_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                            (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-        }
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 2; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[mi], bfr[ni], acc[mi][ni], 0, 0, 0, 127, 0, 127);
+      for (int j = 0; j < C::NB; ++j) {
+        const int r = bcol0(j) + l32;
+        const u32x4_t x0 = kc_frag(sb, r, ks * 4 + khalf * 2);
+        const u32x4_t x1 = kc_frag(sb, r, ks * 4 + khalf * 2 + 1);
+        bfr[j] = i32x8_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                         (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
       }
     }
   };
-
-  // ---- main loop: double-buffered LDS ---------------------------------------------
-  if (nk > 0) {
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt + 1 < nk;
-      if (more) load_stage(kt + 1);
-      compute_stage(kt & 1);
-      if (more) store_stage((kt + 1) & 1);
-      __syncthreads();
+  auto mfmas = [&](auto MBL_c, const auto& af, const auto& bfr) __attribute__((always_inline)) {
+    constexpr int MBL = decltype(MBL_c)::value;
+#pragma unroll
+    for (int i = 0; i < MBL; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j) {
+        if constexpr (!FP8)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], acc[i][j],
+                                                                       0, 0, 0, 127, 0, 127);
+      }
+  };
+  // One ring stage: KS k sub-steps; while sub-step ks multiplies, the fragments of ks+1
+  // are read and a slice of the loads of stage kt+2 (into `nxt`) is issued.
+  auto compute_stage = [&](auto MBL_c, const uint8_t* sa, int kt_next, uint8_t* nxt) __attribute__((always_inline)) {
+    constexpr int KS = FP8 ? 2 : 4;
+    constexpr int PER = (C::LOADS + KS - 1) / KS;
+    using frag_t = typename std::conditional<FP8, i32x8_t, bf16x8_t>::type;
+    frag_t af[2][C::MB], bfr[2][C::NB];
+    load_frags(MBL_c, sa, 0, af[0], bfr[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) load_frags(MBL_c, sa, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+      if (kt_next >= 0) {
+#pragma unroll
+        for (int q = ks * PER; q < (ks + 1) * PER && q < C::LOADS; ++q) issue_one(kt_next, nxt, q);
+      }
+      mfmas(MBL_c, af[ks & 1], bfr[ks & 1]);
     }
-  }
+  };
 
-  // ---- epilogue -------------------------------------------------------------------
-  // 32x32 accumulator layout: lane l, element v -> column l%32,
-  // row 8*(v/4) + 4*(l/32) + v%4.
-  const int lcol = lane & 31;
-  const int rbase = 4 * (lane >> 5);
+  // ---- main loop: ring of three LDS buffers, unrolled so each buffer is static ------
+  // step(kt): stage kt is complete in `cur` once this wave's loads for it have landed
+  // (at most the next stage's loads still in flight) and every wave passed the barrier;
+  // the loads for stage kt+2 go to `nxt`, which held stage kt-1, spread over the
+  // sub-steps of this stage's multiply.
+  auto main_loop = [&](auto MBL_c) __attribute__((always_inline)) {
+    auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+      if (kt + 1 < nk) wait_vmcnt<C::LOADS>();
+      else wait_vmcnt<0>();
+      ring_barrier();
+      compute_stage(MBL_c, cur, kt + 2 < nk ? kt + 2 : -1, nxt);
+    };
+    if (nk > 0) issue_stage(0, ring0);
+    if (nk > 1) issue_stage(1, ring1);
+    for (int kt = 0; kt < nk; kt += 3) {
+      step(kt, ring0, ring2);
+      if (kt + 1 < nk) step(kt + 1, ring1, ring0);
+      if (kt + 2 < nk) step(kt + 2, ring2, ring1);
+    }
+  };
+  static_assert(C::MB <= 4, "live-block dispatch below covers up to four M blocks per wave");
+  // Every wave runs the loop: it issues its share of each stage's loads and takes part
+  // in every barrier even when none of its M blocks holds a valid row (MBL = 0).
+  switch (mb_live) {
+    case 0: main_loop(std::integral_constant<int, 0>{}); break;
+    case 1: main_loop(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (C::MB >= 2) main_loop(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (C::MB >= 3) main_loop(std::integral_constant<int, 3>{}); break;
+    default: if constexpr (C::MB >= 4) main_loop(std::integral_constant<int, 4>{}); break;
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // ---- epilogue: stage row slices of the tile in LDS, then 16-byte stores ----------
+  // 32x32 accumulator layout: lane l, element v -> column l%32, row 8*(v/4) + 4*(l/32) + v%4.
+  // A slice of PR rows holds the M blocks (wm + WM*i) whose rows fall inside it.
+  const int rb = 4 * khalf;
   if (EPI == EPI_SWIGLU) {
-    const int hcol = t.n0 + wn * 32 + lcol;
-    uint16_t* h = (uint16_t*)p.C;
-    uint16_t* gu = (uint16_t*)p.gu_out;
+    // h slice [PR][HB] bf16 in ring0, g,u slice [PR][BN] bf16 in ring1
+    constexpr int HP = HB * 2 + 16, GP = BN * 2 + 16;
+    constexpr int PR = (C::STAGE / GP) >= BM ? BM : 128;
+    static_assert(PR * GP <= C::STAGE && PR * HP <= C::STAGE && PR % 32 == 0, "slice");
+    uint8_t* sh = ring0;
+    uint8_t* sgu = ring1;
+    const int hc = wn * 32 + l32;   // h column within the tile
     const size_t twoI = 2 * (size_t)p.I;
     float sg = 1.f, su = 1.f;
     if (FP8) {
-      sg = p.b_scale[(size_t)t.g * twoI + hcol];
-      su = p.b_scale[(size_t)t.g * twoI + p.I + hcol];
+      sg = p.b_scale[(size_t)t.g * twoI + t.n0 + hc];
+      su = p.b_scale[(size_t)t.g * twoI + p.I + t.n0 + hc];
     }
+    for (int r0 = 0; r0 < t.rows_valid; r0 += PR) {
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
+      for (int i = 0; i < C::MB; ++i) {
+        const int blk = (wm + WM * i) * 32;
+        if (i >= mb_live || blk < r0 || blk >= r0 + PR) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * 64 + mi * 32 + 8 * (v >> 2) + rbase + (v & 3);
-        if (r < t.rows_valid) {
-          const size_t row = (size_t)t.m0 + r;
-          float g = acc[mi][0][v], u = acc[mi][1][v];
+        for (int v = 0; v < 16; v += 2) {  // rows r and r+1 share one packed convert
+          const int r = blk + 8 * (v >> 2) + rb + (v & 3);
+          float g0 = acc[i][0][v], u0 = acc[i][1][v], g1 = acc[i][0][v + 1], u1 = acc[i][1][v + 1];
           if (FP8) {
-            const float sa = p.a_scale[row];
-            g = g * sa * sg;
-            u = u * sa * su;
+            const float sa0 = r < t.rows_valid ? p.a_scale[t.m0 + r] : 0.f;
+            const float sa1 = r + 1 < t.rows_valid ? p.a_scale[t.m0 + r + 1] : 0.f;
+            g0 *= sa0 * sg;
+            u0 *= sa0 * su;
+            g1 *= sa1 * sg;
+            u1 *= sa1 * su;
           }
-          const float hv = g / (1.0f + expf(-g)) * u;
-          h[row * p.I + hcol] = (uint16_t)f32_to_bf16(hv);
-          if (gu) {
-            gu[row * twoI + hcol] = (uint16_t)f32_to_bf16(g);
-            gu[row * twoI + p.I + hcol] = (uint16_t)f32_to_bf16(u);
+          const uint32_t hv = pack_bf16x2(g0 * sigmoid_fast(g0) * u0, g1 * sigmoid_fast(g1) * u1);
+          uint8_t* hrow = sh + (r - r0) * HP + hc * 2;
+          *(uint16_t*)hrow = (uint16_t)hv;
+          *(uint16_t*)(hrow + HP) = (uint16_t)(hv >> 16);
+          if (p.gu_out) {
+            const uint32_t gv = pack_bf16x2(g0, g1), uv = pack_bf16x2(u0, u1);
+            uint8_t* grow = sgu + (r - r0) * GP + hc * 2;
+            *(uint16_t*)grow = (uint16_t)gv;
+            *(uint16_t*)(grow + GP) = (uint16_t)(gv >> 16);
+            *(uint16_t*)(grow + HB * 2) = (uint16_t)uv;
+            *(uint16_t*)(grow + GP + HB * 2) = (uint16_t)(uv >> 16);
           }
         }
       }
+      __syncthreads();
+      constexpr int HV = HB / 8;  // 16-byte vectors per h row
+      for (int idx = tid; idx < PR * HV; idx += C::NT) {
+        const int r = idx / HV, c = idx % HV;
+        if (r0 + r < t.rows_valid) {
+          const u32x4_t v = *(const u32x4_t*)(sh + r * HP + c * 16);
+          *(u32x4_t*)((uint16_t*)p.C + (size_t)(t.m0 + r0 + r) * p.I + t.n0 + c * 8) = v;
+        }
+      }
+      if (p.gu_out) {
+        constexpr int GV = BN / 8;
+        for (int idx = tid; idx < PR * GV; idx += C::NT) {
+          const int r = idx / GV, c = idx % GV;
+          if (r0 + r < t.rows_valid) {
+            const u32x4_t v = *(const u32x4_t*)(sgu + r * GP + c * 16);
+            const int col = c < HV ? t.n0 + c * 8 : p.I + t.n0 + (c - HV) * 8;
+            *(u32x4_t*)((uint16_t*)p.gu_out + (size_t)(t.m0 + r0 + r) * twoI + col) = v;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  } else if (EPI == EPI_SWIGLU_BWD || p.c_fp32) {
+    // fp32 slice [PR][BN] in ring0
+    constexpr int FP = BN * 4 + 16;
+    constexpr int PR = (C::STAGE / FP) >= 128 ? 128 : (C::STAGE / FP) >= 64 ? 64 : 32;
+    static_assert(PR * FP <= C::STAGE, "slice");
+    uint8_t* sf = ring0;
+    for (int r0 = 0; r0 < t.rows_valid; r0 += PR) {
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i) {
+        const int blk = (wm + WM * i) * 32;
+        if (i >= mb_live || blk < r0 || blk >= r0 + PR) continue;
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j) {
+          const int c = bcol0(j) + l32;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = blk + 8 * (v >> 2) + rb + (v & 3);
+            *(float*)(sf + (r - r0) * FP + c * 4) = acc[i][j][v];
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int V8 = BN / 8;  // 8-column groups per row
+      for (int idx = tid; idx < PR * V8; idx += C::NT) {
+        const int r = idx / V8, c8 = idx % V8;
+        const int col = t.n0 + c8 * 8;
+        const int rr = r0 + r;
+        if (rr >= t.rows_valid || col >= p.N) continue;
+        if (DW && t.m0 + rr >= p.M) continue;
+        const f32x4_t x0 = *(const f32x4_t*)(sf + r * FP + c8 * 32);
+        const f32x4_t x1 = *(const f32x4_t*)(sf + r * FP + c8 * 32 + 16);
+        float val[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        if (EPI == EPI_SWIGLU_BWD) {
+          const size_t twoI = 2 * (size_t)p.I;
+          const size_t row = (size_t)t.m0 + rr;
+          const u32x4_t gv = *(const u32x4_t*)((const uint16_t*)p.gu_in + row * twoI + col);
+          const u32x4_t uv = *(const u32x4_t*)((const uint16_t*)p.gu_in + row * twoI + p.I + col);
+          u32x4_t dg, du;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            float o[4];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const float g = h2 ? bf16hi(gv[d]) : bf16lo(gv[d]);
+              const float u = h2 ? bf16hi(uv[d]) : bf16lo(uv[d]);
+              const float dh = val[2 * d + h2];
+              const float sgm = sigmoid_fast(g);
+              o[h2] = dh * u * sgm * (1.0f + g * (1.0f - sgm));
+              o[2 + h2] = dh * g * sgm;
+            }
+            dg[d] = pack_bf16x2(o[0], o[1]);
+            du[d] = pack_bf16x2(o[2], o[3]);
+          }
+          *(u32x4_t*)((uint16_t*)p.C + row * twoI + col) = dg;
+          *(u32x4_t*)((uint16_t*)p.C + row * twoI + p.I + col) = du;
+        } else {
+          const size_t o = DW ? (size_t)t.g * p.M * p.N + (size_t)(t.m0 + rr) * p.N + col
+                              : (size_t)(t.m0 + rr) * p.N + col;
+          if (FP8) {
+            const float sa = p.a_scale[t.m0 + rr];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) val[e] *= sa * p.b_scale[(size_t)t.g * p.N + col + e];
+          }
+          *(f32x4_t*)((float*)p.C + o) = f32x4_t{val[0], val[1], val[2], val[3]};
+          *(f32x4_t*)((float*)p.C + o + 4) = f32x4_t{val[4], val[5], val[6], val[7]};
+        }
+      }
+      __syncthreads();
     }
   } else {
+    // bf16 slice [PR][BN] in ring0
+    constexpr int CP = BN * 2 + 16;
+    constexpr int PR = (C::STAGE / CP) >= BM ? BM : 128;
+    static_assert(PR * CP <= C::STAGE, "slice");
+    uint8_t* sc = ring0;
+    for (int r0 = 0; r0 < t.rows_valid; r0 += PR) {
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int col = t.n0 + wn * 64 + ni * 32 + lcol;
-      if (col >= p.N) continue;
-      float sb = 1.f;
-      if (FP8) sb = p.b_scale[(size_t)t.g * p.N + col];
+      for (int i = 0; i < C::MB; ++i) {
+        const int blk = (wm + WM * i) * 32;
+        if (i >= mb_live || blk < r0 || blk >= r0 + PR) continue;
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
+        for (int j = 0; j < C::NB; ++j) {
+          const int c = bcol0(j) + l32;
+          float sb = 1.f;
+          if (FP8) sb = (t.n0 + c < p.N) ? p.b_scale[(size_t)t.g * p.N + t.n0 + c] : 0.f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * 64 + mi * 32 + 8 * (v >> 2) + rbase + (v & 3);
-          float val = acc[mi][ni][v];
-          if (MODE == MOE_GEMM_TN_DW) {
-            const int m = t.m0 + r;
-            if (m >= p.M) continue;
-            const size_t o = (size_t)t.g * p.M * p.N + (size_t)m * p.N + col;
-            if (p.c_fp32) ((float*)p.C)[o] = val;
-            else ((uint16_t*)p.C)[o] = (uint16_t)f32_to_bf16(val);
-          } else {
-            if (r >= t.rows_valid) continue;
-            const size_t row = (size_t)t.m0 + r;
-            if (FP8) val = val * p.a_scale[row] * sb;
-            if (EPI == EPI_SWIGLU_BWD) {
-              // val = dh[row, col], col < I; saved g, u are bf16
-              const uint16_t* gu = (const uint16_t*)p.gu_in;
-              const size_t twoI = 2 * (size_t)p.I;
-              const float g = bf16_to_f32(gu[row * twoI + col]);
-              const float u = bf16_to_f32(gu[row * twoI + p.I + col]);
-              const float s = 1.0f / (1.0f + expf(-g));
-              const float dg = val * u * s * (1.0f + g * (1.0f - s));
-              const float du = val * g * s;
-              uint16_t* dgu = (uint16_t*)p.C;
-              dgu[row * twoI + col] = (uint16_t)f32_to_bf16(dg);
-              dgu[row * twoI + p.I + col] = (uint16_t)f32_to_bf16(du);
-            } else {
-              const size_t o = row * p.N + col;
-              if (p.c_fp32) ((float*)p.C)[o] = val;
-              else ((uint16_t*)p.C)[o] = (uint16_t)f32_to_bf16(val);
+          for (int v = 0; v < 16; v += 2) {  // rows r and r+1 share one packed convert
+            const int r = blk + 8 * (v >> 2) + rb + (v & 3);
+            float v0 = acc[i][j][v], v1 = acc[i][j][v + 1];
+            if (FP8) {
+              v0 = r < t.rows_valid ? v0 * p.a_scale[t.m0 + r] * sb : 0.f;
+              v1 = r + 1 < t.rows_valid ? v1 * p.a_scale[t.m0 + r + 1] * sb : 0.f;
             }
+            const uint32_t pk = pack_bf16x2(v0, v1);
+            uint8_t* crow = sc + (r - r0) * CP + c * 2;
+            *(uint16_t*)crow = (uint16_t)pk;
+            *(uint16_t*)(crow + CP) = (uint16_t)(pk >> 16);
           }
         }
       }
+      __syncthreads();
+      constexpr int V8 = BN / 8;
+      for (int idx = tid; idx < PR * V8; idx += C::NT) {
+        const int r = idx / V8, c8 = idx % V8;
+        const int col = t.n0 + c8 * 8;
+        const int rr = r0 + r;
+        if (rr >= t.rows_valid || col >= p.N) continue;
+        if (DW && t.m0 + rr >= p.M) continue;
+        const size_t o = DW ? (size_t)t.g * p.M * p.N + (size_t)(t.m0 + rr) * p.N + col
+                            : (size_t)(t.m0 + rr) * p.N + col;
+        *(u32x4_t*)((uint16_t*)p.C + o) = *(const u32x4_t*)(sc + r * CP + c8 * 16);
+      }
+      __syncthreads();
     }
   }
 }
 
-hipError_t launch_grouped_gemm(const GemmParams& p, hipStream_t s) {
-  if (p.G <= 0) return hipSuccess;
-  // Upper bound of the tile count; the surplus blocks exit at once (the real count
-  // lives on the device).
+namespace {
+
+template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
+hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
+  using C = Cfg<BM, BN, WM, WN, STAGES>;
+  auto kern = grouped_gemm_kernel<MODE, EPI, FP8, BM, BN, WM, WN, STAGES>;
+  static_assert(C::SMEM + 264 * 4 <= 160 * 1024, "LDS budget");
+  const int ntn = EPI == EPI_SWIGLU ? p.I / (BN / 2) : (p.N + BN - 1) / BN;
   long long blocks;
-  int ntn = p.epi == EPI_SWIGLU ? p.I / (BN / 2) : (p.N + BN - 1) / BN;
-  if (p.mode == MOE_GEMM_TN_DW) blocks = (long long)p.G * ((p.M + BM - 1) / BM) * ntn;
+  if (MODE == MOE_GEMM_TN_DW) blocks = (long long)p.G * ((p.M + BM - 1) / BM) * ntn;
   else blocks = ((long long)(p.rows + BM - 1) / BM + p.G) * ntn;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  dim3 grid((unsigned)blocks), block(NT);
-#define MOE_GG(MODE, EPI, F8) grouped_gemm_kernel<MODE, EPI, F8><<<grid, block, 0, s>>>(p)
+  kern<<<dim3((unsigned)blocks), dim3(C::NT), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm(const GemmParams& p, hipStream_t s) {
+  if (p.G <= 0) return hipSuccess;
+  // 256x128 tiles, 4 waves of 128x64, 3-stage ring (144 KB of LDS)
+#define MOE_GG(MODE, EPI, F8) return launch_cfg<MODE, EPI, F8, 256, 128, 2, 2, 3>(p, s)
   if (p.fp8) {
     if (p.mode != MOE_GEMM_NT) return hipErrorInvalidValue;
     if (p.epi == EPI_SWIGLU) MOE_GG(MOE_GEMM_NT, EPI_SWIGLU, true);
-    else MOE_GG(MOE_GEMM_NT, EPI_STORE, true);
-  } else if (p.mode == MOE_GEMM_NN) {
-    if (p.epi == EPI_SWIGLU) MOE_GG(MOE_GEMM_NN, EPI_SWIGLU, false);
-    else MOE_GG(MOE_GEMM_NN, EPI_STORE, false);
-  } else if (p.mode == MOE_GEMM_NT) {
-    if (p.epi == EPI_SWIGLU_BWD) MOE_GG(MOE_GEMM_NT, EPI_SWIGLU_BWD, false);
-    else MOE_GG(MOE_GEMM_NT, EPI_STORE, false);
-  } else {
-    MOE_GG(MOE_GEMM_TN_DW, EPI_STORE, false);
+    MOE_GG(MOE_GEMM_NT, EPI_STORE, true);
   }
+  if (p.mode == MOE_GEMM_NN) {
+    if (p.epi == EPI_SWIGLU) MOE_GG(MOE_GEMM_NN, EPI_SWIGLU, false);
+    MOE_GG(MOE_GEMM_NN, EPI_STORE, false);
+  }
+  if (p.mode == MOE_GEMM_NT) {
+    if (p.epi == EPI_SWIGLU_BWD) MOE_GG(MOE_GEMM_NT, EPI_SWIGLU_BWD, false);
+    MOE_GG(MOE_GEMM_NT, EPI_STORE, false);
+  }
+  MOE_GG(MOE_GEMM_TN_DW, EPI_STORE, false);
 #undef MOE_GG
-  return hipGetLastError();
 }
 
 }  // namespace moe
