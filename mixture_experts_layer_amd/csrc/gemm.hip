@@ -92,6 +92,11 @@ struct Cfg {
   static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "load split");
 };
 
+// Rows of an epilogue slice: the tallest of BM, 128, 64, 32 whose staging fits `cap` bytes.
+constexpr int slice_rows(int bm, int row_bytes, int cap) {
+  return bm * row_bytes <= cap ? bm : 128 * row_bytes <= cap ? 128 : 64 * row_bytes <= cap ? 64 : 32;
+}
+
 struct Tile {
   int g;
   int m0;          // NN/NT: first buffer row of the tile; DW: first M index
@@ -131,12 +136,12 @@ MOE_DEV int mn_offset(int k, int col) {
 template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const GemmParams p) {
   using C = Cfg<BM, BN, WM, WN, STAGES>;
-  static_assert(STAGES == 3, "the ring below is written for three stages");
+  static_assert(STAGES == 2 || STAGES == 3, "the ring below is written for two or three stages");
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[STAGES > 2 ? C::STAGE : 1024];
   __shared__ int s_pref[264];
-  static_assert(EPI != EPI_SWIGLU || C::NB == 2, "SwiGLU wave tile: one gate + one up block");
+  static_assert(EPI != EPI_SWIGLU || C::NB % 2 == 0, "SwiGLU wave tile: gate blocks + as many up blocks");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   constexpr bool DW = MODE == MOE_GEMM_TN_DW;
   constexpr bool B_MN = (MODE == MOE_GEMM_NN) || DW;  // B tile M/N-contiguous in memory
   constexpr int HB = BN / 2;                           // SwiGLU: h columns per tile
-  const int ntn = EPI == EPI_SWIGLU ? p.I / HB : (p.N + BN - 1) / BN;
+  const int ntn = EPI == EPI_SWIGLU ? (p.I + HB - 1) / HB : (p.N + BN - 1) / BN;
 
   // ---- tile schedule ------------------------------------------------------------
   int total;
@@ -254,9 +259,16 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
         const int chunk = wave + C::NW * i;
         const int row = kc_row(chunk, lane);
         int col = row;
-        if (EPI == EPI_SWIGLU) col = row < HB ? t.n0 + row : p.I + t.n0 + row - HB;
-        else col = t.n0 + row;
-        b_src[i] = col < p.N ? bg + (size_t)col * lda + kc_logical(row, lane) * 16 : zero;
+        bool ok;
+        if (EPI == EPI_SWIGLU) {
+          const int hcol = t.n0 + (row < HB ? row : row - HB);
+          col = row < HB ? hcol : p.I + hcol;
+          ok = hcol < p.I;
+        } else {
+          col = t.n0 + row;
+          ok = col < p.N;
+        }
+        b_src[i] = ok ? bg + (size_t)col * lda + kc_logical(row, lane) * 16 : zero;
         b_krow[i] = 0;
       }
     } else {      // NN: B_g is [K, N]
@@ -269,9 +281,16 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
         mn_slot<BN>(chunk, lane, k, lb);
         const int c = lb / 2;  // column within the tile
         int col;
-        if (EPI == EPI_SWIGLU) col = c < HB ? t.n0 + c : p.I + t.n0 + c - HB;
-        else col = t.n0 + c;
-        b_src[i] = col < p.N ? bg + ((size_t)k * p.N + col) * 2 : zero;
+        bool ok;
+        if (EPI == EPI_SWIGLU) {
+          const int hcol = t.n0 + (c < HB ? c : c - HB);
+          col = c < HB ? hcol : p.I + hcol;
+          ok = hcol < p.I;
+        } else {
+          col = t.n0 + c;
+          ok = col < p.N;
+        }
+        b_src[i] = ok ? bg + ((size_t)k * p.N + col) * 2 : zero;
         b_krow[i] = 0;
       }
     }
@@ -336,9 +355,13 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   mb_live = __builtin_amdgcn_readfirstlane(mb_live);
   nk = __builtin_amdgcn_readfirstlane(nk);
 
-  // B block column (within the tile) of N block j of this wave
+  // B block column (within the tile) of N block j of this wave. SwiGLU: the first NB/2
+  // blocks are gate columns, the last NB/2 the matching up columns (offset HB).
   auto bcol0 = [&](int j) __attribute__((always_inline)) {
-    if (EPI == EPI_SWIGLU) return j == 0 ? wn * 32 : HB + wn * 32;
+    if (EPI == EPI_SWIGLU) {
+      constexpr int NH = C::NB / 2;
+      return j < NH ? (wn * NH + j) * 32 : HB + (wn * NH + j - NH) * 32;
+    }
     return (wn * C::NB + j) * 32;
   };
 
@@ -440,18 +463,32 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   // the loads for stage kt+2 go to `nxt`, which held stage kt-1, spread over the
   // sub-steps of this stage's multiply.
   auto main_loop = [&](auto MBL_c) __attribute__((always_inline)) {
-    auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
-      if (kt + 1 < nk) wait_vmcnt<C::LOADS>();
-      else wait_vmcnt<0>();
-      ring_barrier();
-      compute_stage(MBL_c, cur, kt + 2 < nk ? kt + 2 : -1, nxt);
-    };
-    if (nk > 0) issue_stage(0, ring0);
-    if (nk > 1) issue_stage(1, ring1);
-    for (int kt = 0; kt < nk; kt += 3) {
-      step(kt, ring0, ring2);
-      if (kt + 1 < nk) step(kt + 1, ring1, ring0);
-      if (kt + 2 < nk) step(kt + 2, ring2, ring1);
+    if constexpr (STAGES == 3) {
+      auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+        if (kt + 1 < nk) wait_vmcnt<C::LOADS>();
+        else wait_vmcnt<0>();
+        ring_barrier();
+        compute_stage(MBL_c, cur, kt + 2 < nk ? kt + 2 : -1, nxt);
+      };
+      if (nk > 0) issue_stage(0, ring0);
+      if (nk > 1) issue_stage(1, ring1);
+      for (int kt = 0; kt < nk; kt += 3) {
+        step(kt, ring0, ring2);
+        if (kt + 1 < nk) step(kt + 1, ring1, ring0);
+        if (kt + 2 < nk) step(kt + 2, ring2, ring1);
+      }
+    } else {
+      // two stages: the loads of stage kt+1 go to the other buffer during stage kt
+      auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+        wait_vmcnt<0>();
+        ring_barrier();
+        compute_stage(MBL_c, cur, kt + 1 < nk ? kt + 1 : -1, nxt);
+      };
+      if (nk > 0) issue_stage(0, ring0);
+      for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, ring0, ring1);
+        if (kt + 1 < nk) step(kt + 1, ring1, ring0);
+      }
     }
   };
   static_assert(C::MB <= 4, "live-block dispatch below covers up to four M blocks per wave");
@@ -474,45 +511,50 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   if (EPI == EPI_SWIGLU) {
     // h slice [PR][HB] bf16 in ring0, g,u slice [PR][BN] bf16 in ring1
     constexpr int HP = HB * 2 + 16, GP = BN * 2 + 16;
-    constexpr int PR = (C::STAGE / GP) >= BM ? BM : 128;
-    static_assert(PR * GP <= C::STAGE && PR * HP <= C::STAGE && PR % 32 == 0, "slice");
+    constexpr int PR = slice_rows(BM, GP, C::STAGE);
+    static_assert(PR * GP <= C::STAGE && PR * HP <= C::STAGE, "slice");
     uint8_t* sh = ring0;
     uint8_t* sgu = ring1;
-    const int hc = wn * 32 + l32;   // h column within the tile
+    constexpr int NH = C::NB / 2;
     const size_t twoI = 2 * (size_t)p.I;
-    float sg = 1.f, su = 1.f;
-    if (FP8) {
-      sg = p.b_scale[(size_t)t.g * twoI + t.n0 + hc];
-      su = p.b_scale[(size_t)t.g * twoI + p.I + t.n0 + hc];
-    }
     for (int r0 = 0; r0 < t.rows_valid; r0 += PR) {
 #pragma unroll
-      for (int i = 0; i < C::MB; ++i) {
-        const int blk = (wm + WM * i) * 32;
-        if (i >= mb_live || blk < r0 || blk >= r0 + PR) continue;
+      for (int jg = 0; jg < NH; ++jg) {
+        const int hc = (wn * NH + jg) * 32 + l32;   // h column within the tile
+        float sg = 1.f, su = 1.f;
+        if (FP8 && t.n0 + hc < p.I) {
+          sg = p.b_scale[(size_t)t.g * twoI + t.n0 + hc];
+          su = p.b_scale[(size_t)t.g * twoI + p.I + t.n0 + hc];
+        }
 #pragma unroll
-        for (int v = 0; v < 16; v += 2) {  // rows r and r+1 share one packed convert
-          const int r = blk + 8 * (v >> 2) + rb + (v & 3);
-          float g0 = acc[i][0][v], u0 = acc[i][1][v], g1 = acc[i][0][v + 1], u1 = acc[i][1][v + 1];
-          if (FP8) {
-            const float sa0 = r < t.rows_valid ? p.a_scale[t.m0 + r] : 0.f;
-            const float sa1 = r + 1 < t.rows_valid ? p.a_scale[t.m0 + r + 1] : 0.f;
-            g0 *= sa0 * sg;
-            u0 *= sa0 * su;
-            g1 *= sa1 * sg;
-            u1 *= sa1 * su;
-          }
-          const uint32_t hv = pack_bf16x2(g0 * sigmoid_fast(g0) * u0, g1 * sigmoid_fast(g1) * u1);
-          uint8_t* hrow = sh + (r - r0) * HP + hc * 2;
-          *(uint16_t*)hrow = (uint16_t)hv;
-          *(uint16_t*)(hrow + HP) = (uint16_t)(hv >> 16);
-          if (p.gu_out) {
-            const uint32_t gv = pack_bf16x2(g0, g1), uv = pack_bf16x2(u0, u1);
-            uint8_t* grow = sgu + (r - r0) * GP + hc * 2;
-            *(uint16_t*)grow = (uint16_t)gv;
-            *(uint16_t*)(grow + GP) = (uint16_t)(gv >> 16);
-            *(uint16_t*)(grow + HB * 2) = (uint16_t)uv;
-            *(uint16_t*)(grow + GP + HB * 2) = (uint16_t)(uv >> 16);
+        for (int i = 0; i < C::MB; ++i) {
+          const int blk = (wm + WM * i) * 32;
+          if (i >= mb_live || blk < r0 || blk >= r0 + PR) continue;
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {  // rows r and r+1 share one packed convert
+            const int r = blk + 8 * (v >> 2) + rb + (v & 3);
+            float g0 = acc[i][jg][v], u0 = acc[i][jg + NH][v];
+            float g1 = acc[i][jg][v + 1], u1 = acc[i][jg + NH][v + 1];
+            if (FP8) {
+              const float sa0 = r < t.rows_valid ? p.a_scale[t.m0 + r] : 0.f;
+              const float sa1 = r + 1 < t.rows_valid ? p.a_scale[t.m0 + r + 1] : 0.f;
+              g0 *= sa0 * sg;
+              u0 *= sa0 * su;
+              g1 *= sa1 * sg;
+              u1 *= sa1 * su;
+            }
+            const uint32_t hv = pack_bf16x2(g0 * sigmoid_fast(g0) * u0, g1 * sigmoid_fast(g1) * u1);
+            uint8_t* hrow = sh + (r - r0) * HP + hc * 2;
+            *(uint16_t*)hrow = (uint16_t)hv;
+            *(uint16_t*)(hrow + HP) = (uint16_t)(hv >> 16);
+            if (p.gu_out) {
+              const uint32_t gv = pack_bf16x2(g0, g1), uv = pack_bf16x2(u0, u1);
+              uint8_t* grow = sgu + (r - r0) * GP + hc * 2;
+              *(uint16_t*)grow = (uint16_t)gv;
+              *(uint16_t*)(grow + GP) = (uint16_t)(gv >> 16);
+              *(uint16_t*)(grow + HB * 2) = (uint16_t)uv;
+              *(uint16_t*)(grow + GP + HB * 2) = (uint16_t)(uv >> 16);
+            }
           }
         }
       }
@@ -520,7 +562,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       constexpr int HV = HB / 8;  // 16-byte vectors per h row
       for (int idx = tid; idx < PR * HV; idx += C::NT) {
         const int r = idx / HV, c = idx % HV;
-        if (r0 + r < t.rows_valid) {
+        if (r0 + r < t.rows_valid && t.n0 + c * 8 < p.I) {
           const u32x4_t v = *(const u32x4_t*)(sh + r * HP + c * 16);
           *(u32x4_t*)((uint16_t*)p.C + (size_t)(t.m0 + r0 + r) * p.I + t.n0 + c * 8) = v;
         }
@@ -529,9 +571,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
         constexpr int GV = BN / 8;
         for (int idx = tid; idx < PR * GV; idx += C::NT) {
           const int r = idx / GV, c = idx % GV;
-          if (r0 + r < t.rows_valid) {
+          const int hcol = t.n0 + (c < HV ? c : c - HV) * 8;
+          if (r0 + r < t.rows_valid && hcol < p.I) {
             const u32x4_t v = *(const u32x4_t*)(sgu + r * GP + c * 16);
-            const int col = c < HV ? t.n0 + c * 8 : p.I + t.n0 + (c - HV) * 8;
+            const int col = c < HV ? hcol : p.I + hcol;
             *(u32x4_t*)((uint16_t*)p.gu_out + (size_t)(t.m0 + r0 + r) * twoI + col) = v;
           }
         }
@@ -541,7 +584,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   } else if (EPI == EPI_SWIGLU_BWD || p.c_fp32) {
     // fp32 slice [PR][BN] in ring0
     constexpr int FP = BN * 4 + 16;
-    constexpr int PR = (C::STAGE / FP) >= 128 ? 128 : (C::STAGE / FP) >= 64 ? 64 : 32;
+    constexpr int PR = slice_rows(BM, FP, C::STAGE);
     static_assert(PR * FP <= C::STAGE, "slice");
     uint8_t* sf = ring0;
     for (int r0 = 0; r0 < t.rows_valid; r0 += PR) {
@@ -610,7 +653,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   } else {
     // bf16 slice [PR][BN] in ring0
     constexpr int CP = BN * 2 + 16;
-    constexpr int PR = (C::STAGE / CP) >= BM ? BM : 128;
+    constexpr int PR = slice_rows(BM, CP, C::STAGE);
     static_assert(PR * CP <= C::STAGE, "slice");
     uint8_t* sc = ring0;
     for (int r0 = 0; r0 < t.rows_valid; r0 += PR) {
@@ -662,7 +705,7 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   using C = Cfg<BM, BN, WM, WN, STAGES>;
   auto kern = grouped_gemm_kernel<MODE, EPI, FP8, BM, BN, WM, WN, STAGES>;
   static_assert(C::SMEM + 264 * 4 <= 160 * 1024, "LDS budget");
-  const int ntn = EPI == EPI_SWIGLU ? p.I / (BN / 2) : (p.N + BN - 1) / BN;
+  const int ntn = EPI == EPI_SWIGLU ? (p.I + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   long long blocks;
   if (MODE == MOE_GEMM_TN_DW) blocks = (long long)p.G * ((p.M + BM - 1) / BM) * ntn;
   else blocks = ((long long)(p.rows + BM - 1) / BM + p.G) * ntn;
@@ -674,10 +717,27 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
+// Tile configurations (BM, BN, WM, WN, STAGES), chosen by measurement on the Qwen3- and
+// Mixtral-shaped expert GEMMs: bf16 uses 256x256 tiles with eight waves (two per SIMD,
+// 128x64 each) and a two-stage ring; e4m3 uses 256x128 tiles with four waves and a
+// three-stage ring (its eight-wave build does not fit the register file).
+#ifndef MOE_GEMM_TILE_BF16
+#define MOE_GEMM_TILE_BF16 256, 256, 2, 4, 2
+#endif
+#ifndef MOE_GEMM_TILE_FP8
+#define MOE_GEMM_TILE_FP8 256, 128, 2, 2, 3
+#endif
+namespace {
+template <int MODE, int EPI, bool F8>
+hipError_t launch_sel(const GemmParams& p, hipStream_t s) {
+  if constexpr (F8) return launch_cfg<MODE, EPI, true, MOE_GEMM_TILE_FP8>(p, s);
+  else return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16>(p, s);
+}
+}  // namespace
+
 hipError_t launch_grouped_gemm(const GemmParams& p, hipStream_t s) {
   if (p.G <= 0) return hipSuccess;
-  // 256x128 tiles, 4 waves of 128x64, 3-stage ring (144 KB of LDS)
-#define MOE_GG(MODE, EPI, F8) return launch_cfg<MODE, EPI, F8, 256, 128, 2, 2, 3>(p, s)
+#define MOE_GG(MODE, EPI, F8) return launch_sel<MODE, EPI, F8>(p, s)
   if (p.fp8) {
     if (p.mode != MOE_GEMM_NT) return hipErrorInvalidValue;
     if (p.epi == EPI_SWIGLU) MOE_GG(MOE_GEMM_NT, EPI_SWIGLU, true);
