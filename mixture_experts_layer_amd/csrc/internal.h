@@ -9,10 +9,19 @@ namespace moe {
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int score,
                               int32_t* topk_idx, float* topk_prob, int32_t* counts,
                               uint8_t* routing_map, float* probs_dense, hipStream_t s);
+// Router that also writes the per-expert histogram of each chunk of `chunk_tokens`
+// tokens to partial[chunk][E] (input of launch_dispatch_from_hist).
+hipError_t launch_router_hist(const float* logits, int T, int E, int k, int score,
+                              int32_t* topk_idx, float* topk_prob, int32_t* partial,
+                              int chunk_tokens, hipStream_t s);
 
 // permute.hip
 constexpr int kPermChunk = 1024;  // flattened (token, slot) entries per dispatch chunk
 size_t permute_scratch_bytes(int T, int E, int k);
+int router_chunk_tokens(int T);
+hipError_t launch_dispatch_from_hist(const int32_t* topk_idx, int T, int E, int k, int chunk_tokens,
+                                     int32_t* partial, int32_t* counts, int32_t* offsets,
+                                     int32_t* row_of, int32_t* src_of, hipStream_t s);
 hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, int32_t* offsets,
                                 int32_t* row_of, int32_t* src_of, void* scratch, hipStream_t s);
 hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, const float* prob, int T,

@@ -339,11 +339,13 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   const int T = p->T, H = p->H, E = p->E, k = p->k, I = p->I;
   const int N = T * k;
 
-  // 1. router
-  MOE_TRY(launch_router_topk(t->logits, T, E, k, p->score, v.topk_idx, v.topk_prob, v.counts,
-                             nullptr, nullptr, s));
-  // 2. dispatch
-  MOE_TRY(launch_dispatch_meta(v.topk_idx, T, E, k, v.offsets, v.row_of, v.src_of, v.scratch, s));
+  // 1. router, writing per-chunk expert histograms (no atomics)
+  const int chunk_tokens = router_chunk_tokens(T);
+  MOE_TRY(launch_router_hist(t->logits, T, E, k, p->score, v.topk_idx, v.topk_prob,
+                             (int32_t*)v.scratch, chunk_tokens, s));
+  // 2. dispatch: counts, offsets, row maps from the histograms, then the row copies
+  MOE_TRY(launch_dispatch_from_hist(v.topk_idx, T, E, k, chunk_tokens, (int32_t*)v.scratch,
+                                    v.counts, v.offsets, v.row_of, v.src_of, s));
   if (fp8) MOE_TRY(launch_scatter_rows_fp8(t->x, v.row_of, T, H, k, (uint8_t*)v.xp, v.xp_scale, s));
   else MOE_TRY(launch_scatter_rows(t->x, v.row_of, nullptr, T, H, k, v.xp, s));
   // 3. grouped MLP

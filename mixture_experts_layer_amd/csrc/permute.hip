@@ -6,9 +6,11 @@
 // contributions with the routing weights in the same pass.
 //
 // Dispatch metadata is a stable counting sort of the flattened [T,k] choices by expert:
-//   1. dispatch_hist  : per chunk of 1024 entries, a histogram over experts (LDS atomics);
-//   2. dispatch_scan  : one block; offsets[e] = exclusive scan of the totals, and each
-//                       chunk's starting row per expert;
+//   1. per-chunk histograms over experts: dispatch_hist (chunks of 1024 entries, LDS
+//      atomics) for a given topk_idx, or written by the router itself inside the layer
+//      (chunks of whole tokens, see router.hip);
+//   2. dispatch_scan  : one block; per-expert totals (the counts), offsets[e] = their
+//                       exclusive scan, and each chunk's starting row per expert;
 //   3. dispatch_rank  : one wave per chunk walks its entries in order; lanes that chose
 //                       the same expert find each other with 9 ballots (one per bit of the
 //                       id), so a row is chunk_base + rank among the earlier lanes.
@@ -19,10 +21,19 @@
 
 namespace moe {
 
+int router_chunk_tokens(int T) {
+  // whole-token chunks for the fused router histogram: at most 512 chunks, 8 tokens or more
+  int c = (T + 511) / 512;
+  c = (c + 3) / 4 * 4;
+  return c < 8 ? 8 : c;
+}
+
 size_t permute_scratch_bytes(int T, int E, int k) {
-  size_t n = (size_t)T * k;
-  size_t chunks = (n + kPermChunk - 1) / kPermChunk;
-  return 2 * chunks * (size_t)E * sizeof(int32_t);
+  const size_t n = (size_t)T * k;
+  const size_t a = (n + kPermChunk - 1) / kPermChunk;
+  const int ct = router_chunk_tokens(T);
+  const size_t b = ((size_t)T + ct - 1) / ct;
+  return 2 * (a > b ? a : b) * (size_t)E * sizeof(int32_t);
 }
 
 __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ idx, int n,
@@ -39,36 +50,51 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
   for (int e = threadIdx.x; e < E; e += 256) partial[(size_t)blockIdx.x * E + e] = h[e];
 }
 
-__global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __restrict__ partial,
-                                                            int nchunks, int E,
-                                                            int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ chunk_base) {
+// One block of 1024 threads: thread (part, e) with part = tid/256 sums a quarter of the
+// chunks of expert e; totals -> counts and offsets (exclusive scan over e), then each
+// part writes the running row base of its chunks.
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ partial,
+                                                             int nchunks, int E,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ chunk_base) {
+  __shared__ int psum[4][256];
   __shared__ int s[256];
-  const int e = threadIdx.x;
-  int total = 0;
+  const int e = threadIdx.x & 255, part = threadIdx.x >> 8;
+  const int L = (nchunks + 3) / 4;
+  const int c0 = part * L, c1 = min(nchunks, c0 + L);
+  int sum = 0;
   if (e < E)
-    for (int c = 0; c < nchunks; ++c) total += partial[(size_t)c * E + e];
-  s[e] = total;
+    for (int c = c0; c < c1; ++c) sum += partial[(size_t)c * E + e];
+  psum[part][e] = sum;
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scan
-    int add = e >= o ? s[e - o] : 0;
+  const int tot = psum[0][e] + psum[1][e] + psum[2][e] + psum[3][e];
+  if (part == 0) s[e] = tot;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scan over the 256 totals
+    const int add = (part == 0 && e >= o) ? s[e - o] : 0;
     __syncthreads();
-    s[e] += add;
+    if (part == 0) s[e] += add;
     __syncthreads();
   }
-  int run = s[e] - total;
+  const int excl = s[e] - tot;
+  if (part == 0 && e < E) {
+    offsets[e] = excl;
+    if (counts) counts[e] = tot;
+  }
+  if (threadIdx.x == 255) offsets[E] = s[255];
   if (e < E) {
-    offsets[e] = run;
-    for (int c = 0; c < nchunks; ++c) {
+    int run = excl;
+    for (int q = 0; q < part; ++q) run += psum[q][e];
+    for (int c = c0; c < c1; ++c) {
       chunk_base[(size_t)c * E + e] = run;
       run += partial[(size_t)c * E + e];
     }
   }
-  if (e == 255) offsets[E] = s[255];
 }
 
 __global__ __launch_bounds__(64) void dispatch_rank_kernel(const int32_t* __restrict__ idx, int n,
-                                                           int k, int E,
+                                                           int k, int E, int chunk_entries,
                                                            const int32_t* __restrict__ chunk_base,
                                                            int32_t* __restrict__ row_of,
                                                            int32_t* __restrict__ src_of) {
@@ -78,9 +104,11 @@ __global__ __launch_bounds__(64) void dispatch_rank_kernel(const int32_t* __rest
   for (int e = lane; e < E; e += 64) base[e] = chunk_base[(size_t)c * E + e];
   __syncthreads();
   const uint64_t lt = lanemask_lt();
-  for (int it = 0; it < kPermChunk / 64; ++it) {
-    const int f = c * kPermChunk + it * 64 + lane;
-    const bool valid = f < n;
+  const int iters = (chunk_entries + 63) / 64;
+  for (int it = 0; it < iters; ++it) {
+    const int off = it * 64 + lane;
+    const int f = c * chunk_entries + off;
+    const bool valid = off < chunk_entries && f < n;
     const int e = valid ? idx[f] : 0x1ff;  // 9-bit sentinel never equals a real id (< 256)
     uint64_t peers = ~0ull;
 #pragma unroll
@@ -109,8 +137,22 @@ hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, in
   int32_t* chunk_base = partial + (size_t)nchunks * E;
   if (n == 0) return launch_fill_i32(offsets, E + 1, 0, s);
   dispatch_hist_kernel<<<nchunks, 256, 0, s>>>(topk_idx, n, E, partial);
-  dispatch_scan_kernel<<<1, 256, 0, s>>>(partial, nchunks, E, offsets, chunk_base);
-  dispatch_rank_kernel<<<nchunks, 64, 0, s>>>(topk_idx, n, k, E, chunk_base, row_of, src_of);
+  dispatch_scan_kernel<<<1, 1024, 0, s>>>(partial, nchunks, E, nullptr, offsets, chunk_base);
+  dispatch_rank_kernel<<<nchunks, 64, 0, s>>>(topk_idx, n, k, E, kPermChunk, chunk_base, row_of,
+                                              src_of);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_from_hist(const int32_t* topk_idx, int T, int E, int k, int chunk_tokens,
+                                     int32_t* partial, int32_t* counts, int32_t* offsets,
+                                     int32_t* row_of, int32_t* src_of, hipStream_t s) {
+  const int n = T * k;
+  if (n == 0) return launch_fill_i32(offsets, E + 1, 0, s);
+  const int nchunks = (T + chunk_tokens - 1) / chunk_tokens;
+  int32_t* chunk_base = partial + (size_t)nchunks * E;
+  dispatch_scan_kernel<<<1, 1024, 0, s>>>(partial, nchunks, E, counts, offsets, chunk_base);
+  dispatch_rank_kernel<<<nchunks, 64, 0, s>>>(topk_idx, n, k, E, chunk_tokens * k, chunk_base,
+                                              row_of, src_of);
   return hipGetLastError();
 }
 

@@ -25,17 +25,32 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPL>  // experts per lane: ceil(E / 64)
+// HIST = false: a grid-stride loop over tokens; per-expert counts are summed in LDS and
+//   added to `counts` with one atomic per (block, expert).
+// HIST = true: block c owns the chunk of `chunk_tokens` tokens starting at c*chunk_tokens
+//   and writes that chunk's per-expert histogram to partial[c][0..E) (no atomics); the
+//   dispatch scan turns these rows into counts, offsets and per-chunk row bases.
+template <int EPL, bool HIST>  // experts per lane: ceil(E / 64)
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int score, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_prob, int32_t* __restrict__ counts, uint8_t* __restrict__ routing_map,
-    float* __restrict__ probs_dense) {
+    float* __restrict__ probs_dense, int chunk_tokens) {
   __shared__ int hist[256];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int waves = blockDim.x >> 6;
-  for (int t = blockIdx.x * waves + (threadIdx.x >> 6); t < T; t += gridDim.x * waves) {
+  int t0, t_end, t_step;
+  if (HIST) {
+    t0 = blockIdx.x * chunk_tokens + (threadIdx.x >> 6);
+    t_end = min(T, (blockIdx.x + 1) * chunk_tokens);
+    t_step = waves;
+  } else {
+    t0 = blockIdx.x * waves + (threadIdx.x >> 6);
+    t_end = T;
+    t_step = gridDim.x * waves;
+  }
+  for (int t = t0; t < t_end; t += t_step) {
     const float* row = logits + (size_t)t * E;
     float v[EPL];
     bool taken[EPL];
@@ -102,8 +117,12 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    if (hist[e]) atomicAdd(&counts[e], hist[e]);
+  if (HIST) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) counts[(size_t)blockIdx.x * E + e] = hist[e];
+  } else {
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+      if (hist[e]) atomicAdd(&counts[e], hist[e]);
+  }
 }
 
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int score,
@@ -116,8 +135,33 @@ hipError_t launch_router_topk(const float* logits, int T, int E, int k, int scor
   int epl = (E + 63) / 64;
 #define MOE_ROUTER_CASE(n)                                                                    \
   case n:                                                                                     \
-    router_topk_kernel<n><<<blocks, 256, 0, s>>>(logits, T, E, k, score, topk_idx, topk_prob, \
-                                                 counts, routing_map, probs_dense);           \
+    router_topk_kernel<n, false><<<blocks, 256, 0, s>>>(logits, T, E, k, score, topk_idx,      \
+                                                        topk_prob, counts, routing_map,        \
+                                                        probs_dense, 0);                       \
+    break;
+  switch (epl) {
+    MOE_ROUTER_CASE(1)
+    MOE_ROUTER_CASE(2)
+    MOE_ROUTER_CASE(3)
+    MOE_ROUTER_CASE(4)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MOE_ROUTER_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_router_hist(const float* logits, int T, int E, int k, int score,
+                              int32_t* topk_idx, float* topk_prob, int32_t* partial,
+                              int chunk_tokens, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int blocks = (T + chunk_tokens - 1) / chunk_tokens;
+  int epl = (E + 63) / 64;
+#define MOE_ROUTER_CASE(n)                                                                     \
+  case n:                                                                                      \
+    router_topk_kernel<n, true><<<blocks, 256, 0, s>>>(logits, T, E, k, score, topk_idx,        \
+                                                       topk_prob, partial, nullptr, nullptr,    \
+                                                       chunk_tokens);                          \
     break;
   switch (epl) {
     MOE_ROUTER_CASE(1)
