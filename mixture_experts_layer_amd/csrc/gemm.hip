@@ -41,8 +41,6 @@ namespace moe {
 
 namespace {
 
-constexpr int BKB = 128;  // K bytes per stage
-
 __device__ __attribute__((aligned(256))) uint8_t g_zero_block[4096];  // stays zero
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
@@ -77,8 +75,10 @@ MOE_DEV void load_lds16(const void* g, uint8_t* lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int STAGES, int BKB_>
 struct Cfg {
+  static constexpr int BKB = BKB_;      // K bytes per stage: 64 or 128
+  static constexpr int KR = BKB / 2;    // bf16 k rows of an M/N-contiguous stage tile
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
@@ -86,10 +86,11 @@ struct Cfg {
   static constexpr int A_BYTES = BM * BKB, B_BYTES = BN * BKB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int SMEM = STAGE * STAGES;
-  static constexpr int A_LOADS = BM / 8 / NW, B_LOADS = BN / 8 / NW;  // 1 KB chunks per wave
+  static constexpr int A_LOADS = A_BYTES / 1024 / NW, B_LOADS = B_BYTES / 1024 / NW;  // per wave
   static constexpr int LOADS = A_LOADS + B_LOADS;
+  static_assert(BKB == 64 || BKB == 128, "stage depth");
   static_assert(MB >= 1 && NB >= 1, "wave tile");
-  static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "load split");
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "load split");
 };
 
 // Rows of an epilogue slice: the tallest of BM, 128, 64, 32 whose staging fits `cap` bytes.
@@ -106,40 +107,55 @@ struct Tile {
   int kbase;       // DW: first row of the group
 };
 
-// Global source of one 1 KB chunk-load of a K-contiguous operand tile.
-// Lane l fills LDS row (chunk*8 + l/8), physical 16-byte slot l%8; the logical
-// chunk held there is slot ^ ((row >> 1) & 7).
-MOE_DEV int kc_row(int chunk, int lane) { return chunk * 8 + (lane >> 3); }
-MOE_DEV int kc_logical(int row, int lane) { return (lane & 7) ^ ((row >> 1) & 7); }
+// K-contiguous operand tile: rows of BKB bytes, the 16-byte chunk index XORed with a
+// function of the row so the fragment reads of 16 consecutive rows hit distinct banks:
+// BKB = 128: 8 chunks, XOR (row/2)%8; BKB = 64: 4 chunks, XOR (row/4)%4.
+template <int BKB>
+MOE_DEV int kc_swz(int row) { return BKB == 128 ? (row >> 1) & 7 : (row >> 2) & 3; }
+// One 1 KB chunk-load: lane l fills LDS row (chunk*rows + l/slots), physical 16-byte slot
+// l%slots; the logical chunk it must hold is slot ^ swz(row).
+template <int BKB>
+MOE_DEV int kc_row(int chunk, int lane) { return chunk * (1024 / BKB) + lane / (BKB / 16); }
+template <int BKB>
+MOE_DEV int kc_logical(int row, int lane) { return (lane & (BKB / 16 - 1)) ^ kc_swz<BKB>(row); }
 
-// M/N-contiguous operand tile: 64 k-rows of W bytes (W = 2*cols). Lane l of chunk c
-// fills row (c*1024 + 16*l) / W at physical offset (16*l) % W; the physical 64-byte
-// segment is the logical one XOR (k & 3).
+// M/N-contiguous operand tile: KR k-rows of W bytes (W = 2*cols), made of 64-byte
+// segments. The physical segment of (k, logical segment s) is s ^ mn_swz(k), chosen so
+// the ds_read_b64_tr_b16 pattern (rows k..k+3 and k+8..k+11, one segment each) spreads
+// over the four 16-bank groups: W >= 256: s ^ (k & 3); W = 128 (two segments per row,
+// row k starting at bank group 2k mod 4): s ^ ((k >> 1) & 1).
+template <int COLS>
+MOE_DEV int mn_swz(int k) {
+  static_assert(COLS * 2 >= 128, "rows of at least two 64-byte segments");
+  return COLS * 2 >= 256 ? (k & 3) : ((k >> 1) & 1);
+}
+// Lane l of chunk c fills row (c*1024 + 16*l) / W at physical offset (16*l) % W.
 template <int COLS>
 MOE_DEV void mn_slot(int chunk, int lane, int& k, int& logical_byte) {
   constexpr int W = COLS * 2;
   const int byte = chunk * 1024 + lane * 16;
   k = byte / W;
   const int phys = byte % W;
-  logical_byte = (((phys >> 6) ^ (k & 3)) << 6) | (phys & 63);
+  logical_byte = (((phys >> 6) ^ mn_swz<COLS>(k)) << 6) | (phys & 63);
 }
 
 // LDS byte offset of element (k, col) in an M/N-contiguous tile.
 template <int COLS>
 MOE_DEV int mn_offset(int k, int col) {
   const int byte = col * 2;
-  return k * (COLS * 2) + ((((byte >> 6) ^ (k & 3)) << 6) | (byte & 63));
+  return k * (COLS * 2) + ((((byte >> 6) ^ mn_swz<COLS>(k)) << 6) | (byte & 63));
 }
 
 }  // namespace
 
-template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
+template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int BKB_>
 __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const GemmParams p) {
-  using C = Cfg<BM, BN, WM, WN, STAGES>;
-  static_assert(STAGES == 2 || STAGES == 3, "the ring below is written for two or three stages");
-  __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring2[STAGES > 2 ? C::STAGE : 1024];
+  using C = Cfg<BM, BN, WM, WN, STAGES, BKB_>;
+  constexpr int BKB = C::BKB, KR = C::KR;
+  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+  // The LDS ring: stage kt lives in buffer kt % STAGES. The DMA writes are issued from
+  // inline asm, so the compiler's own LDS-DMA tracking never serialises reads behind them.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
   __shared__ int s_pref[264];
   static_assert(EPI != EPI_SWIGLU || C::NB % 2 == 0, "SwiGLU wave tile: gate blocks + as many up blocks");
 
@@ -238,26 +254,26 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   size_t a_step, b_step;      // bytes per stage
   int a_krow[C::A_LOADS], b_krow[C::B_LOADS];  // DW: k row of the chunk lane (zero past kcount)
   int nk;
-  if (!DW) {
+  if constexpr (!DW) {
     const size_t lda = (size_t)p.K * esz;
     nk = (int)(lda / BKB);
     a_step = BKB;
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
       const int chunk = wave + C::NW * i;
-      const int row = kc_row(chunk, lane);
+      const int row = kc_row<BKB>(chunk, lane);
       a_src[i] = row < t.rows_valid
-                     ? (const uint8_t*)p.A + (size_t)(t.m0 + row) * lda + kc_logical(row, lane) * 16
+                     ? (const uint8_t*)p.A + (size_t)(t.m0 + row) * lda + kc_logical<BKB>(row, lane) * 16
                      : zero;
       a_krow[i] = 0;
     }
-    if (!B_MN) {  // NT: B_g is [N, K]
+    if constexpr (!B_MN) {  // NT: B_g is [N, K]
       b_step = BKB;
       const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.N * lda;
 #pragma unroll
       for (int i = 0; i < C::B_LOADS; ++i) {
         const int chunk = wave + C::NW * i;
-        const int row = kc_row(chunk, lane);
+        const int row = kc_row<BKB>(chunk, lane);
         int col = row;
         bool ok;
         if (EPI == EPI_SWIGLU) {
@@ -268,11 +284,11 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
           col = t.n0 + row;
           ok = col < p.N;
         }
-        b_src[i] = ok ? bg + (size_t)col * lda + kc_logical(row, lane) * 16 : zero;
+        b_src[i] = ok ? bg + (size_t)col * lda + kc_logical<BKB>(row, lane) * 16 : zero;
         b_krow[i] = 0;
       }
     } else {      // NN: B_g is [K, N]
-      b_step = (size_t)64 * p.N * 2;
+      b_step = (size_t)KR * p.N * 2;
       const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.K * p.N * 2;
 #pragma unroll
       for (int i = 0; i < C::B_LOADS; ++i) {
@@ -295,9 +311,9 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       }
     }
   } else {
-    nk = (t.kcount + 63) / 64;
-    a_step = (size_t)64 * p.M * 2;
-    b_step = (size_t)64 * p.N * 2;
+    nk = (t.kcount + KR - 1) / KR;
+    a_step = (size_t)KR * p.M * 2;
+    b_step = (size_t)KR * p.N * 2;
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
       const int chunk = wave + C::NW * i;
@@ -322,13 +338,13 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   auto issue_one = [&](int kt, uint8_t* sa, int i) __attribute__((always_inline)) {
     if (i < C::A_LOADS) {
       const uint8_t* src;
-      if (DW) src = (kt * 64 + a_krow[i] < t.kcount) ? a_src[i] + (size_t)kt * a_step : zero;
+      if (DW) src = (kt * KR + a_krow[i] < t.kcount) ? a_src[i] + (size_t)kt * a_step : zero;
       else src = a_src[i] == zero ? zero : a_src[i] + (size_t)kt * a_step;
       load_lds16(src, sa + (wave + C::NW * i) * 1024);
     } else {
       const int j = i - C::A_LOADS;
       const uint8_t* src;
-      if (DW) src = (kt * 64 + b_krow[j] < t.kcount) ? b_src[j] + (size_t)kt * b_step : zero;
+      if (DW) src = (kt * KR + b_krow[j] < t.kcount) ? b_src[j] + (size_t)kt * b_step : zero;
       else src = b_src[j] == zero ? zero : b_src[j] + (size_t)kt * b_step;
       load_lds16(src, sa + C::A_BYTES + (wave + C::NW * j) * 1024);
     }
@@ -371,7 +387,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   const int tr_c = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
   auto kc_frag = [&](const uint8_t* base, int row, int chunk) __attribute__((always_inline)) -> u32x4_t {
-    return *(const u32x4_t*)(base + row * BKB + ((chunk ^ ((row >> 1) & 7)) << 4));
+    return *(const u32x4_t*)(base + row * BKB + ((chunk ^ kc_swz<BKB>(row)) << 4));
   };
   // Fragment loads of k sub-step ks into registers.
   auto load_frags = [&](auto MBL_c, const uint8_t* sa, int ks, auto& af, auto& bfr) __attribute__((always_inline)) {
@@ -441,7 +457,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   // One ring stage: KS k sub-steps; while sub-step ks multiplies, the fragments of ks+1
   // are read and a slice of the loads of stage kt+2 (into `nxt`) is issued.
   auto compute_stage = [&](auto MBL_c, const uint8_t* sa, int kt_next, uint8_t* nxt) __attribute__((always_inline)) {
-    constexpr int KS = FP8 ? 2 : 4;
+    constexpr int KS = FP8 ? BKB / 64 : BKB / 32;
     constexpr int PER = (C::LOADS + KS - 1) / KS;
     using frag_t = typename std::conditional<FP8, i32x8_t, bf16x8_t>::type;
     frag_t af[2][C::MB], bfr[2][C::NB];
@@ -462,33 +478,20 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   // (at most the next stage's loads still in flight) and every wave passed the barrier;
   // the loads for stage kt+2 go to `nxt`, which held stage kt-1, spread over the
   // sub-steps of this stage's multiply.
+  auto buf = [&](int kt) __attribute__((always_inline)) { return smem + (kt % STAGES) * C::STAGE; };
   auto main_loop = [&](auto MBL_c) __attribute__((always_inline)) {
-    if constexpr (STAGES == 3) {
-      auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
-        if (kt + 1 < nk) wait_vmcnt<C::LOADS>();
-        else wait_vmcnt<0>();
-        ring_barrier();
-        compute_stage(MBL_c, cur, kt + 2 < nk ? kt + 2 : -1, nxt);
-      };
-      if (nk > 0) issue_stage(0, ring0);
-      if (nk > 1) issue_stage(1, ring1);
-      for (int kt = 0; kt < nk; kt += 3) {
-        step(kt, ring0, ring2);
-        if (kt + 1 < nk) step(kt + 1, ring1, ring0);
-        if (kt + 2 < nk) step(kt + 2, ring2, ring1);
-      }
-    } else {
-      // two stages: the loads of stage kt+1 go to the other buffer during stage kt
-      auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
-        wait_vmcnt<0>();
-        ring_barrier();
-        compute_stage(MBL_c, cur, kt + 1 < nk ? kt + 1 : -1, nxt);
-      };
-      if (nk > 0) issue_stage(0, ring0);
-      for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, ring0, ring1);
-        if (kt + 1 < nk) step(kt + 1, ring1, ring0);
-      }
+    constexpr int LEAD = STAGES - 1;  // stages in flight ahead of the one being multiplied
+#pragma unroll
+    for (int s0 = 0; s0 < LEAD; ++s0)
+      if (s0 < nk) issue_stage(s0, buf(s0));
+    for (int kt = 0; kt < nk; ++kt) {
+      // stage kt has landed once at most the later issued stages are still in flight
+      const int later = min(LEAD - 1, nk - 1 - kt);
+      if (LEAD - 1 >= 2 && later >= 2) wait_vmcnt<(LEAD >= 3 ? 2 : 0) * C::LOADS>();
+      else if (LEAD - 1 >= 1 && later >= 1) wait_vmcnt<C::LOADS>();
+      else wait_vmcnt<0>();
+      ring_barrier();  // every wave's loads for stage kt landed; stage kt-1 fully read
+      compute_stage(MBL_c, buf(kt), kt + LEAD < nk ? kt + LEAD : -1, buf(kt + LEAD));
     }
   };
   static_assert(C::MB <= 4, "live-block dispatch below covers up to four M blocks per wave");
@@ -509,12 +512,12 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   // A slice of PR rows holds the M blocks (wm + WM*i) whose rows fall inside it.
   const int rb = 4 * khalf;
   if (EPI == EPI_SWIGLU) {
-    // h slice [PR][HB] bf16 in ring0, g,u slice [PR][BN] bf16 in ring1
+    // h slice [PR][HB] bf16 in the first half of the ring, g,u slice [PR][BN] in the second
     constexpr int HP = HB * 2 + 16, GP = BN * 2 + 16;
-    constexpr int PR = slice_rows(BM, GP, C::STAGE);
-    static_assert(PR * GP <= C::STAGE && PR * HP <= C::STAGE, "slice");
-    uint8_t* sh = ring0;
-    uint8_t* sgu = ring1;
+    constexpr int PR = slice_rows(BM, GP, C::SMEM / 2);
+    static_assert(PR * GP <= C::SMEM / 2 && PR * HP <= C::SMEM / 2, "slice");
+    uint8_t* sh = smem;
+    uint8_t* sgu = smem + C::SMEM / 2;
     constexpr int NH = C::NB / 2;
     const size_t twoI = 2 * (size_t)p.I;
     for (int r0 = 0; r0 < t.rows_valid; r0 += PR) {
@@ -582,11 +585,11 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       __syncthreads();
     }
   } else if (EPI == EPI_SWIGLU_BWD || p.c_fp32) {
-    // fp32 slice [PR][BN] in ring0
+    // fp32 slice [PR][BN] in the ring
     constexpr int FP = BN * 4 + 16;
-    constexpr int PR = slice_rows(BM, FP, C::STAGE);
-    static_assert(PR * FP <= C::STAGE, "slice");
-    uint8_t* sf = ring0;
+    constexpr int PR = slice_rows(BM, FP, C::SMEM);
+    static_assert(PR * FP <= C::SMEM, "slice");
+    uint8_t* sf = smem;
     for (int r0 = 0; r0 < t.rows_valid; r0 += PR) {
 #pragma unroll
       for (int i = 0; i < C::MB; ++i) {
@@ -651,11 +654,11 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       __syncthreads();
     }
   } else {
-    // bf16 slice [PR][BN] in ring0
+    // bf16 slice [PR][BN] in the ring
     constexpr int CP = BN * 2 + 16;
-    constexpr int PR = slice_rows(BM, CP, C::STAGE);
-    static_assert(PR * CP <= C::STAGE, "slice");
-    uint8_t* sc = ring0;
+    constexpr int PR = slice_rows(BM, CP, C::SMEM);
+    static_assert(PR * CP <= C::SMEM, "slice");
+    uint8_t* sc = smem;
     for (int r0 = 0; r0 < t.rows_valid; r0 += PR) {
 #pragma unroll
       for (int i = 0; i < C::MB; ++i) {
@@ -700,10 +703,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
 
 namespace {
 
-template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
+template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int BKB>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
-  using C = Cfg<BM, BN, WM, WN, STAGES>;
-  auto kern = grouped_gemm_kernel<MODE, EPI, FP8, BM, BN, WM, WN, STAGES>;
+  using C = Cfg<BM, BN, WM, WN, STAGES, BKB>;
+  auto kern = grouped_gemm_kernel<MODE, EPI, FP8, BM, BN, WM, WN, STAGES, BKB>;
   static_assert(C::SMEM + 264 * 4 <= 160 * 1024, "LDS budget");
   const int ntn = EPI == EPI_SWIGLU ? (p.I + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   long long blocks;
@@ -717,21 +720,37 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
-// Tile configurations (BM, BN, WM, WN, STAGES), chosen by measurement on the Qwen3- and
-// Mixtral-shaped expert GEMMs: bf16 uses 256x256 tiles with eight waves (two per SIMD,
-// 128x64 each) and a two-stage ring; e4m3 uses 256x128 tiles with four waves and a
-// three-stage ring (its eight-wave build does not fit the register file).
+// Tile configurations (BM, BN, WM, WN, STAGES, K bytes per stage), chosen by
+// measurement on the Qwen3- and Mixtral-shaped expert GEMMs: bf16 uses 256x256 tiles with
+// eight waves (two per SIMD, 128x64 each) and a four-stage ring of 64-byte K steps (three
+// stages of loads in flight); e4m3 uses 256x128 tiles with four waves and a three-stage
+// ring of 128-byte steps (its eight-wave build does not fit the register file).
 #ifndef MOE_GEMM_TILE_BF16
-#define MOE_GEMM_TILE_BF16 256, 256, 2, 4, 2
+#define MOE_GEMM_TILE_BF16 256, 256, 2, 4, 4, 64
 #endif
 #ifndef MOE_GEMM_TILE_FP8
-#define MOE_GEMM_TILE_FP8 256, 128, 2, 2, 3
+#define MOE_GEMM_TILE_FP8 256, 128, 2, 2, 3, 128
+#endif
+// Small-M tiles (decode: a handful of rows per expert): 32-row tiles, 64 output columns
+// per block (one wave), a four-stage ring of 64-byte K steps; many blocks per CU so that
+// enough waves stream the weights.
+#ifndef MOE_GEMM_TILE_SMALL_M
+#define MOE_GEMM_TILE_SMALL_M 32, 64, 1, 1, 4, 64
 #endif
 namespace {
 template <int MODE, int EPI, bool F8>
 hipError_t launch_sel(const GemmParams& p, hipStream_t s) {
-  if constexpr (F8) return launch_cfg<MODE, EPI, true, MOE_GEMM_TILE_FP8>(p, s);
-  else return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16>(p, s);
+  if constexpr (F8) {
+    return launch_cfg<MODE, EPI, true, MOE_GEMM_TILE_FP8>(p, s);
+  } else {
+    // every group fits one 32-row tile when the whole buffer has at most 32 rows per group
+    // on average and at most 256 rows: the decode case
+    if constexpr (MODE != MOE_GEMM_TN_DW) {
+      if (p.rows <= 256 && p.rows <= 32 * p.G)
+        return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_SMALL_M>(p, s);
+    }
+    return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16>(p, s);
+  }
 }
 }  // namespace
 
