@@ -64,6 +64,86 @@ def row_costs(w, training):
     return c
 
 
+GEMM_STAGES = ["gemm1_swiglu", "gemm2", "gemm2_bwd_swiglu", "dw_down", "gemm1_bwd_dx", "dw_gu"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_hbm_traffic_qwen3.md")
+GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_amd", "csrc", "gemm.hip")
+CALIB_BYTES = 256 << 20
+
+
+def _source_hash():
+    import hashlib
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _pmc_rows(folder, counter):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def pmc_summary(fetch_dir, write_dir, workload):
+    """HBM bytes per launch of each GEMM stage of one --pmc-pass run: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) scaled by what each counter reads for a plain copy of
+    CALIB_BYTES (read CALIB_BYTES, write CALIB_BYTES)."""
+    out = {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(folder, counter)
+        gemm = [r for r in rows if "grouped_gemm_kernel" in r[1]]
+        assert len(gemm) >= len(GEMM_STAGES), f"{counter}: {len(gemm)} GEMM dispatches"
+        # the calibration copy (an fp32 negation, CALIB_BYTES in and out) is the last dispatch
+        assert "elementwise" in rows[-1][1], rows[-1][1]
+        factor = CALIB_BYTES / (rows[-1][2] * 1024.0)
+        # the pass launches each stage once, in GEMM_STAGES order, after one warm step
+        stage_rows = gemm[-len(GEMM_STAGES):]
+        out[counter] = {"factor": factor, "stages": {n: r[2] * 1024.0 * factor
+                                                     for n, r in zip(GEMM_STAGES, stage_rows)},
+                        "kernels": {n: r[1] for n, r in zip(GEMM_STAGES, stage_rows)}}
+    data = {"workload": workload, "gemm_source_sha256_16": _source_hash(),
+            "fetch_factor": round(out["FETCH_SIZE"]["factor"], 4),
+            "write_factor": round(out["WRITE_SIZE"]["factor"], 4),
+            "bytes_per_launch": {n: round(out["FETCH_SIZE"]["stages"][n] + out["WRITE_SIZE"]["stages"][n])
+                                 for n in GEMM_STAGES},
+            "fetch_bytes_per_launch": {n: round(out["FETCH_SIZE"]["stages"][n]) for n in GEMM_STAGES},
+            "write_bytes_per_launch": {n: round(out["WRITE_SIZE"]["stages"][n]) for n in GEMM_STAGES}}
+    lines = ["# HBM traffic of the grouped-GEMM launches: Qwen3-30B-A3B-shaped block", "",
+             "Commands (repository root; rocprofv3 run from /tmp):", "", "```",
+             "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --pmc-pass --no-cpu-baseline",
+             "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o run -- python3 bench.py --pmc-pass --no-cpu-baseline",
+             "python3 bench.py --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write", "```", "",
+             f"Calibration: a plain copy of {CALIB_BYTES >> 20} MiB reads FETCH_SIZE x {data['fetch_factor']} "
+             f"and WRITE_SIZE x {data['write_factor']} of its true byte counts; the factors scale the "
+             "GEMM readings below. The data block is read by bench.py while the GEMM source hash matches.", "",
+             "| stage | kernel | HBM read MB | HBM write MB | total MB |", "|---|---|---:|---:|---:|"]
+    for n in GEMM_STAGES:
+        k = out["FETCH_SIZE"]["kernels"][n]
+        k = k[k.find("grouped_gemm_kernel"):][:60]
+        lines.append(f"| {n} | `{k}` | {data['fetch_bytes_per_launch'][n] / 1e6:.1f} | "
+                     f"{data['write_bytes_per_launch'][n] / 1e6:.1f} | {data['bytes_per_launch'][n] / 1e6:.1f} |")
+    lines += ["", "```json", json.dumps(data), "```", ""]
+    return "\n".join(lines)
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of `stage` from the committed counter summary, or None when the
+    summary is missing or the GEMM source changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        data = json.loads(blob)
+    except (OSError, IndexError, ValueError):
+        return None
+    if data.get("gemm_source_sha256_16") != _source_hash():
+        return None
+    return data["bytes_per_launch"].get(stage)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -74,7 +154,14 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--cpu-sample-tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="launch each stage once plus a 256 MiB calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the HBM-traffic summary from two rocprofv3 --pmc output folders")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(pmc_summary(*args.pmc_summary, args.workload))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -119,6 +206,9 @@ def main():
         dx = torch.empty_like(x)
         dw_gu = torch.empty((w.E, w.H, 2 * w.I), dtype=torch.bfloat16, device=dev)
         dw_down = torch.empty((w.E, w.I, w.H), dtype=torch.bfloat16, device=dev)
+
+    if args.pmc_pass:  # counters: one warm step, then each GEMM stage once
+        args.warmup, args.steps = 1, 1
 
     def step():
         M.moe_forward(prob, tens, ws)
@@ -188,6 +278,19 @@ def main():
             "dw_gu": lambda: M.moe_grouped_gemm(M.MOE_GEMM_TN_DW, xp, dgu, offs, dw_gu),
             "dispatch_bwd": lambda: M.moe_unpermute_combine(dxp, row_of, None, dx),
         })
+    if args.pmc_pass:
+        for name in GEMM_STAGES:
+            if name in launches:
+                launches[name]()
+                torch.cuda.synchronize()
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_pass": [n for n in GEMM_STAGES if n in launches]}), flush=True)
+        return
+
     kernel_us = {}
     for name, fn in launches.items():
         fn()
@@ -232,7 +335,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(by / t_dom / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom)
     roof["kernel"] = dom
     roof["launch_us"] = round(kernel_us[dom], 2)
 
