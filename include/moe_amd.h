@@ -134,6 +134,14 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const void* d_out, const void* w_down,
                                          const int32_t* offsets, const void* gu_saved, int G,
                                          int rows, int H, int I, void* dgu, void* stream);
 
+/* Cap on the persistent grid of every grouped-GEMM launch (the entry points above and
+ * the ones inside moe_forward / moe_backward). Each launch runs min(tiles, resident)
+ * blocks, resident = compute units x blocks per unit, and every block walks its share of
+ * the tiles. max_blocks > 0 lowers the cap to that many blocks (leaving compute units to
+ * concurrent work, or forcing many tiles per block); 0 restores the default. Process-wide
+ * host setting, read at launch time. MOE_ERR_INVALID_ARG for max_blocks < 0. */
+moe_status_t moe_set_gemm_max_blocks(int max_blocks);
+
 /* Token combine (guide, "Token combine"): y[t] = sum_j p[t,j] * y_perm[row_of[t,j]]
  * (+ shared_out[t]), summed in fp32, one rounding to bf16.
  *  y_perm [T*k,H] bf16, row_of [T,k], topk_prob [T,k] float32 or NULL (unweighted

@@ -24,7 +24,7 @@ MOE_GEMM_NN, MOE_GEMM_NT, MOE_GEMM_TN_DW = 0, 1, 2
 EXPORTS = [
     "moe_status_str", "moe_router_topk", "moe_permute_workspace_bytes", "moe_permute",
     "moe_grouped_gemm_swiglu", "moe_grouped_gemm", "moe_grouped_gemm_swiglu_bwd",
-    "moe_unpermute_combine", "moe_combine_backward", "moe_quantize_fp8_rows",
+    "moe_set_gemm_max_blocks", "moe_unpermute_combine", "moe_combine_backward", "moe_quantize_fp8_rows",
     "moe_quantize_fp8_weights", "moe_workspace_bytes", "moe_workspace_views", "moe_forward",
     "moe_backward",
 ]
@@ -70,6 +70,7 @@ def _load():
         "moe_grouped_gemm_swiglu": ([vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp], i),
         "moe_grouped_gemm": ([i, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp], i),
         "moe_grouped_gemm_swiglu_bwd": ([vp, vp, vp, vp, i, i, i, i, vp, vp], i),
+        "moe_set_gemm_max_blocks": ([i], i),
         "moe_unpermute_combine": ([vp, vp, vp, vp, i, i, i, vp, vp], i),
         "moe_combine_backward": ([vp, vp, vp, i, i, i, vp, vp], i),
         "moe_quantize_fp8_rows": ([vp, i, i, vp, vp, vp], i),
@@ -132,6 +133,11 @@ def _score(s):
 
 
 # ---- stage calls ---------------------------------------------------------------------
+
+def moe_status_str(status):
+    """Name of a moe_status_t value."""
+    return _lib.moe_status_str(int(status)).decode()
+
 
 def moe_router_topk(logits, k, score, topk_idx, topk_prob, counts, routing_map=None,
                     probs_dense=None, stream=None):
@@ -211,6 +217,11 @@ def moe_grouped_gemm_swiglu_bwd(d_out, w_down, offsets, gu_saved, dgu, stream=No
     _check("moe_grouped_gemm_swiglu_bwd", _lib.moe_grouped_gemm_swiglu_bwd(
         _p(d_out), _p(w_down), _p(offsets), _p(gu_saved), G, rows, H, I, _p(dgu),
         _stream(stream)))
+
+
+def moe_set_gemm_max_blocks(max_blocks):
+    """Cap the persistent grid of the grouped-GEMM launches (0: every resident block)."""
+    _check("moe_set_gemm_max_blocks", _lib.moe_set_gemm_max_blocks(int(max_blocks)))
 
 
 def moe_unpermute_combine(y_perm, row_of, topk_prob, y, shared_out=None, stream=None):

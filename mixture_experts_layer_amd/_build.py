@@ -18,6 +18,9 @@ FLAGS = [
     "-mcode-object-version=5",
     # packed fp32 VALU ops stay off: ordinary float code must not become v_pk_*_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # atomics stay as written: the wave-level atomic rewrite would read a tile ticket back
+    # (and wait for every load in flight) right where it is issued
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 
@@ -41,7 +44,8 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
         logs = list(ex.map(compile_one, range(len(SOURCES))))
     tmp = LIB + ".tmp"
-    logs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]))
+    # -z defs: a symbol missing from the objects fails the link instead of the first load
+    logs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]))
     os.replace(tmp, LIB)
     log = "\n".join(l for l in logs if l)
     if verbose and log:

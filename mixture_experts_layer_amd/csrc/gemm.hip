@@ -33,6 +33,7 @@
 //    weight panel are neighbours, and block ids are remapped so that neighbours land
 //    on the same XCD (blocks are dispatched round-robin over the 8 XCDs, each with
 //    its own L2).
+#include <atomic>
 #include <type_traits>
 
 #include "internal.h"
@@ -42,6 +43,14 @@ namespace moe {
 namespace {
 
 __device__ __attribute__((aligned(256))) uint8_t g_zero_block[4096];  // stays zero
+
+// Tile counters of the persistent launches: slot s holds one counter per XCD ([0..8)) and
+// the count of finished blocks ([8]). The last block of a launch to finish puts the slot
+// back to zero, so the next launch that takes the slot starts from zero. Launches take the
+// slots in turn (kSchedSlots of them), so launches in flight at the same time on one device
+// use different slots as long as fewer than kSchedSlots overlap.
+constexpr int kSchedSlots = 64;
+__device__ int g_sched[kSchedSlots][16];
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -93,11 +102,6 @@ struct Cfg {
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "load split");
 };
 
-// Rows of an epilogue slice: the tallest of BM, 128, 64, 32 whose staging fits `cap` bytes.
-constexpr int slice_rows(int bm, int row_bytes, int cap) {
-  return bm * row_bytes <= cap ? bm : 128 * row_bytes <= cap ? 128 : 64 * row_bytes <= cap ? 64 : 32;
-}
-
 struct Tile {
   int g;
   int m0;          // NN/NT: first buffer row of the tile; DW: first M index
@@ -148,15 +152,59 @@ MOE_DEV int mn_offset(int k, int col) {
 
 }  // namespace
 
+namespace {
+
+// Buffer resource over one output tile: stores whose byte offset is kOutOfRange (at or past
+// the record count) are dropped by the hardware range check, so masked lanes still issue
+// their store and every wave issues the same number of stores per epilogue.
+constexpr int kOutOfRange = 0x7fffffff;
+MOE_DEV __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kOutOfRange, 0x00020000);
+}
+
+// s_waitcnt vmcnt for "stage landed": `pend` later stages (LOADS each) and, with allow > 0,
+// one epilogue's stores (S1 or S2 instructions) were issued after the stage's loads. The
+// counter drains in issue order, so any allowance not above the younger operations is safe.
+template <int LOADS, int S1, int S2>
+MOE_DEV void wait_stage(int pend, int allow) {
+  constexpr int A = S1 < 63 ? S1 : 63, B = S2 < 63 ? S2 : 63;
+  constexpr int A1 = LOADS + S1 < 63 ? LOADS + S1 : 63, B1 = LOADS + S2 < 63 ? LOADS + S2 : 63;
+  constexpr int A2 = 2 * LOADS + S1 < 63 ? 2 * LOADS + S1 : 63;
+  constexpr int B2 = 2 * LOADS + S2 < 63 ? 2 * LOADS + S2 : 63;
+  if (allow == 0) {
+    if (pend >= 2) wait_vmcnt<2 * LOADS>();
+    else if (pend == 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+  } else if (allow == 1) {
+    if (pend >= 2) wait_vmcnt<A2>();
+    else if (pend == 1) wait_vmcnt<A1>();
+    else wait_vmcnt<A>();
+  } else {
+    if (pend >= 2) wait_vmcnt<B2>();
+    else if (pend == 1) wait_vmcnt<B1>();
+    else wait_vmcnt<B>();
+  }
+}
+
+}  // namespace
+
 template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int BKB_>
 __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const GemmParams p) {
   using C = Cfg<BM, BN, WM, WN, STAGES, BKB_>;
   constexpr int BKB = C::BKB, KR = C::KR;
+  constexpr int LEAD = STAGES - 1;  // stages in flight ahead of the one being multiplied
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
-  // The LDS ring: stage kt lives in buffer kt % STAGES. The DMA writes are issued from
+  // The LDS ring: stream stage s lives in buffer s % STAGES. The DMA writes are issued from
   // inline asm, so the compiler's own LDS-DMA tracking never serialises reads behind them.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
-  __shared__ int s_pref[264];
+  __shared__ int s_pref[264];  // NN/NT: prefix of the per-group M-tile counts
+  __shared__ int s_off[264];   // offsets[0..G]
+  // per-wave epilogue staging: 32 rows of SB bytes (128 when it fits the LDS budget)
+  constexpr int SB = C::SMEM + 2 * 264 * 4 + 64 + C::NW * 4096 <= 160 * 1024 &&
+                             (EPI == EPI_SWIGLU ? (C::NB / 2) % 2 == 0 : C::NB % 2 == 0)
+                         ? 128 : 64;
+  __shared__ __attribute__((aligned(16))) uint8_t s_epi[C::NW * 32 * SB];
+  __shared__ int s_tk[8];      // published tile tickets
   static_assert(EPI != EPI_SWIGLU || C::NB % 2 == 0, "SwiGLU wave tile: gate blocks + as many up blocks");
 
   const int tid = threadIdx.x;
@@ -168,9 +216,11 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   constexpr int HB = BN / 2;                           // SwiGLU: h columns per tile
   const int ntn = EPI == EPI_SWIGLU ? (p.I + HB - 1) / HB : (p.N + BN - 1) / BN;
 
-  // ---- tile schedule ------------------------------------------------------------
+  // ---- group offsets and tile count ----------------------------------------------
+  for (int g = tid; g <= p.G; g += C::NT) s_off[g] = p.offsets[g];
+  __syncthreads();
   int total;
-  if (!DW) {
+  if constexpr (!DW) {
     if (wave == 0) {
       const int per = (p.G + 63) / 64;
       int loc[5];
@@ -179,7 +229,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       for (int i = 0; i < 5; ++i) {
         const int g = lane * per + i;
         int mt = 0;
-        if (i < per && g < p.G) mt = (p.offsets[g + 1] - p.offsets[g] + BM - 1) / BM;
+        if (i < per && g < p.G) mt = (s_off[g + 1] - s_off[g] + BM - 1) / BM;
         sum += mt;
         loc[i] = sum;
       }
@@ -202,174 +252,267 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   } else {
     total = p.G * ((p.M + BM - 1) / BM) * ntn;
   }
-  const int b = blockIdx.x;
-  if (b >= total) return;
-  int tile;
-  {
-    const int xcd = b & 7, i = b >> 3, base = total >> 3, rem = total & 7;
-    tile = xcd * base + (xcd < rem ? xcd : rem) + i;
-  }
-  Tile t;
-  if (!DW) {
-    int lo = 0, hi = p.G;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pref[mid] * ntn <= tile) lo = mid;
-      else hi = mid - 1;
-    }
-    const int g = lo;
-    const int mt = s_pref[g + 1] - s_pref[g];
-    const int local = tile - s_pref[g] * ntn;
-    const int ntile = local / mt, mtile = local % mt;
-    const int gbeg = p.offsets[g], cnt = p.offsets[g + 1] - gbeg;
-    t.g = g;
-    t.m0 = gbeg + mtile * BM;
-    t.rows_valid = min(BM, cnt - mtile * BM);
-    t.n0 = ntile * (EPI == EPI_SWIGLU ? HB : BN);
-    t.kcount = p.K;
-    t.kbase = 0;
-  } else {
-    const int mtn = (p.M + BM - 1) / BM;
-    const int g = tile / (mtn * ntn), rem = tile % (mtn * ntn);
-    t.g = g;
-    t.m0 = (rem / ntn) * BM;
-    t.n0 = (rem % ntn) * BN;
-    t.rows_valid = BM;
-    t.kbase = p.offsets[g];
-    t.kcount = p.offsets[g + 1] - t.kbase;
-  }
+  total = __builtin_amdgcn_readfirstlane(total);
 
-  t.g = __builtin_amdgcn_readfirstlane(t.g);
-  t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
-  t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
-  t.rows_valid = __builtin_amdgcn_readfirstlane(t.rows_valid);
-  t.kcount = __builtin_amdgcn_readfirstlane(t.kcount);
-  t.kbase = __builtin_amdgcn_readfirstlane(t.kbase);
+  // ---- this block's tiles ------------------------------------------------------------
+  // The grid is persistent. Tiles are ordered (group, N-tile, M-tile); blocks are handed
+  // out round-robin over the 8 XCDs, so XCD x serves the x-th eighth of the tile range and
+  // neighbours that share weight panels run at the same time on one XCD (one L2).
+  // NN/NT (ragged rows, uneven tile costs): each XCD's blocks take tickets from its own
+  // counter as they free up. A block holds three tickets at start; at the end of each
+  // epilogue wave 0 publishes the ticket requested one tile earlier (so the atomic's
+  // latency is never waited for) and requests the next.
+  // Weight gradients (equal tiles): a fixed stride through the XCD's eighth.
+  constexpr bool DYN = !DW;
+  const int nx = (gridDim.x & 7) == 0 ? 8 : 1;
+  const int xcd = nx == 8 ? (int)(blockIdx.x & 7) : 0;
+  int r_start, r_end;
+  {
+    const int base = total / nx, rem = total % nx;
+    r_start = xcd * base + (xcd < rem ? xcd : rem);
+    r_end = r_start + base + (xcd < rem ? 1 : 0);
+  }
+  const int seq_first = r_start + (int)(blockIdx.x / nx), seq_stride = (int)gridDim.x / nx;
+  int* const ctr = &g_sched[p.sched_slot][xcd];
+  int n_pub = 0x40000000;     // tickets published in s_tk (a ring of 8); unbounded when static
+  bool sched_open = false;    // later tickets may still hold tiles
+  int pend_tk = 0;            // wave 0 holds a requested, unpublished ticket
+  int tk = 0;                 // wave 0, lane 0: that ticket
+  if constexpr (DYN) {
+    if (tid == 0) {
+      const int t0 = atomicAdd(ctr, 3);
+      s_tk[0] = t0;
+      s_tk[1] = t0 + 1;
+      s_tk[2] = t0 + 2;
+    }
+    __syncthreads();
+    n_pub = 3;
+    sched_open = s_tk[2] + r_start < r_end;
+  }
+  auto tile_of = [&](int j) __attribute__((always_inline)) -> int {  // DYN: j < n_pub
+    int t;
+    if constexpr (DYN) {
+      // The first 3*BX tickets of an XCD (three per block, taken at start) are spread so
+      // that blocks start on consecutive tiles: ticket 3i+k -> tile i + BX*k. Later tickets
+      // map to themselves.
+      const int BX = (int)gridDim.x / nx;
+      t = s_tk[j & 7];
+      if (t < 3 * BX && r_end - r_start >= 3 * BX) t = t / 3 + BX * (t % 3);
+      t += r_start;
+      t = t < r_end ? t : -1;
+    } else {
+      t = seq_first + j * seq_stride;
+      t = t < r_end ? t : -1;
+    }
+    return __builtin_amdgcn_readfirstlane(t);
+  };
+  // Tile fields from the tile index (LDS reads only: no global loads while DMAs fly).
+  auto decode = [&](int tile) __attribute__((always_inline)) -> Tile {
+    Tile t;
+    if constexpr (!DW) {
+      int lo = 0, hi = p.G;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pref[mid] * ntn <= tile) lo = mid;
+        else hi = mid - 1;
+      }
+      const int g = lo;
+      const int mt = s_pref[g + 1] - s_pref[g];
+      const int local = tile - s_pref[g] * ntn;
+      const int ntile = local / mt, mtile = local % mt;
+      const int gbeg = s_off[g], cnt = s_off[g + 1] - gbeg;
+      t.g = g;
+      t.m0 = gbeg + mtile * BM;
+      t.rows_valid = min(BM, cnt - mtile * BM);
+      t.n0 = ntile * (EPI == EPI_SWIGLU ? HB : BN);
+      t.kcount = p.K;
+      t.kbase = 0;
+    } else {
+      const int mtn = (p.M + BM - 1) / BM;
+      const int g = tile / (mtn * ntn), rem = tile % (mtn * ntn);
+      t.g = g;
+      t.m0 = (rem / ntn) * BM;
+      t.n0 = (rem % ntn) * BN;
+      t.rows_valid = BM;
+      t.kbase = s_off[g];
+      t.kcount = s_off[g + 1] - t.kbase;
+    }
+    t.g = __builtin_amdgcn_readfirstlane(t.g);
+    t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+    t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+    t.rows_valid = __builtin_amdgcn_readfirstlane(t.rows_valid);
+    t.kcount = __builtin_amdgcn_readfirstlane(t.kcount);
+    t.kbase = __builtin_amdgcn_readfirstlane(t.kbase);
+    return t;
+  };
 
   // ---- load descriptors: a global pointer per 1 KB chunk-load, advanced per stage ----
   const int esz = FP8 ? 1 : 2;
   const uint8_t* zero = g_zero_block;
+  const size_t lda = (size_t)p.K * esz;
+  const int nk_fixed = DW ? 0 : (int)(lda / BKB);
+  size_t a_step, b_step;  // bytes per stage
+  if constexpr (!DW) {
+    a_step = BKB;
+    b_step = B_MN ? (size_t)KR * p.N * 2 : (size_t)BKB;
+  } else {
+    a_step = (size_t)KR * p.M * 2;
+    b_step = (size_t)KR * p.N * 2;
+  }
+  auto stages_of = [&](const Tile& t) __attribute__((always_inline)) {
+    return DW ? (t.kcount + KR - 1) / KR : nk_fixed;
+  };
+  // NN/NT: a_src/b_src point at the cursor's next stage and advance by a_inc/b_inc per
+  // stage (0 for lanes that read the zero block). A chunks wholly past the tile's last row
+  // (tail tiles) are issued by one lane only: the instruction still counts towards vmcnt,
+  // but the dead rows cost no bandwidth. DW: base pointers plus the stage index.
   const uint8_t* a_src[C::A_LOADS];
   const uint8_t* b_src[C::B_LOADS];
-  size_t a_step, b_step;      // bytes per stage
+  uint32_t a_inc[C::A_LOADS], b_inc[C::B_LOADS];
   int a_krow[C::A_LOADS], b_krow[C::B_LOADS];  // DW: k row of the chunk lane (zero past kcount)
-  int nk;
-  if constexpr (!DW) {
-    const size_t lda = (size_t)p.K * esz;
-    nk = (int)(lda / BKB);
-    a_step = BKB;
+  int a_dead = 0;                              // NN/NT: bit i set: A chunk i holds no valid row
+  auto setup_loads = [&](const Tile& t) __attribute__((always_inline)) {
+    if constexpr (!DW) {
+      a_dead = 0;
 #pragma unroll
-    for (int i = 0; i < C::A_LOADS; ++i) {
-      const int chunk = wave + C::NW * i;
-      const int row = kc_row<BKB>(chunk, lane);
-      a_src[i] = row < t.rows_valid
-                     ? (const uint8_t*)p.A + (size_t)(t.m0 + row) * lda + kc_logical<BKB>(row, lane) * 16
-                     : zero;
-      a_krow[i] = 0;
-    }
-    if constexpr (!B_MN) {  // NT: B_g is [N, K]
-      b_step = BKB;
-      const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.N * lda;
-#pragma unroll
-      for (int i = 0; i < C::B_LOADS; ++i) {
+      for (int i = 0; i < C::A_LOADS; ++i) {
         const int chunk = wave + C::NW * i;
         const int row = kc_row<BKB>(chunk, lane);
-        int col = row;
-        bool ok;
-        if (EPI == EPI_SWIGLU) {
-          const int hcol = t.n0 + (row < HB ? row : row - HB);
-          col = row < HB ? hcol : p.I + hcol;
-          ok = hcol < p.I;
-        } else {
-          col = t.n0 + row;
-          ok = col < p.N;
-        }
-        b_src[i] = ok ? bg + (size_t)col * lda + kc_logical<BKB>(row, lane) * 16 : zero;
-        b_krow[i] = 0;
+        const bool ok = row < t.rows_valid;
+        a_src[i] = ok ? (const uint8_t*)p.A + (size_t)(t.m0 + row) * lda + kc_logical<BKB>(row, lane) * 16
+                      : zero;
+        a_inc[i] = ok ? (uint32_t)a_step : 0u;
+        if (chunk * (1024 / BKB) >= t.rows_valid) a_dead |= 1 << i;
+        a_krow[i] = 0;
       }
-    } else {      // NN: B_g is [K, N]
-      b_step = (size_t)KR * p.N * 2;
-      const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.K * p.N * 2;
+      a_dead = __builtin_amdgcn_readfirstlane(a_dead);
+      if constexpr (!B_MN) {  // NT: B_g is [N, K]
+        const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.N * lda;
+#pragma unroll
+        for (int i = 0; i < C::B_LOADS; ++i) {
+          const int chunk = wave + C::NW * i;
+          const int row = kc_row<BKB>(chunk, lane);
+          int col;
+          bool ok;
+          if (EPI == EPI_SWIGLU) {
+            const int hcol = t.n0 + (row < HB ? row : row - HB);
+            col = row < HB ? hcol : p.I + hcol;
+            ok = hcol < p.I;
+          } else {
+            col = t.n0 + row;
+            ok = col < p.N;
+          }
+          b_src[i] = ok ? bg + (size_t)col * lda + kc_logical<BKB>(row, lane) * 16 : zero;
+          b_inc[i] = ok ? (uint32_t)b_step : 0u;
+          b_krow[i] = 0;
+        }
+      } else {  // NN: B_g is [K, N]
+        const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.K * p.N * 2;
+#pragma unroll
+        for (int i = 0; i < C::B_LOADS; ++i) {
+          const int chunk = wave + C::NW * i;
+          int k, lb;
+          mn_slot<BN>(chunk, lane, k, lb);
+          const int c = lb / 2;  // column within the tile
+          int col;
+          bool ok;
+          if (EPI == EPI_SWIGLU) {
+            const int hcol = t.n0 + (c < HB ? c : c - HB);
+            col = c < HB ? hcol : p.I + hcol;
+            ok = hcol < p.I;
+          } else {
+            col = t.n0 + c;
+            ok = col < p.N;
+          }
+          b_src[i] = ok ? bg + ((size_t)k * p.N + col) * 2 : zero;
+          b_inc[i] = ok ? (uint32_t)b_step : 0u;
+          b_krow[i] = 0;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::A_LOADS; ++i) {
+        const int chunk = wave + C::NW * i;
+        int k, lb;
+        mn_slot<BM>(chunk, lane, k, lb);
+        const int col = t.m0 + lb / 2;
+        a_krow[i] = col < p.M ? k : 0x40000000;  // never valid when the column is out of range
+        a_src[i] = (const uint8_t*)p.A + ((size_t)(t.kbase + k) * p.M + (col < p.M ? col : 0)) * 2;
+      }
 #pragma unroll
       for (int i = 0; i < C::B_LOADS; ++i) {
         const int chunk = wave + C::NW * i;
         int k, lb;
         mn_slot<BN>(chunk, lane, k, lb);
-        const int c = lb / 2;  // column within the tile
-        int col;
-        bool ok;
-        if (EPI == EPI_SWIGLU) {
-          const int hcol = t.n0 + (c < HB ? c : c - HB);
-          col = c < HB ? hcol : p.I + hcol;
-          ok = hcol < p.I;
-        } else {
-          col = t.n0 + c;
-          ok = col < p.N;
-        }
-        b_src[i] = ok ? bg + ((size_t)k * p.N + col) * 2 : zero;
-        b_krow[i] = 0;
+        const int col = t.n0 + lb / 2;
+        b_krow[i] = col < p.N ? k : 0x40000000;
+        b_src[i] = (const uint8_t*)p.B + ((size_t)(t.kbase + k) * p.N + (col < p.N ? col : 0)) * 2;
       }
     }
-  } else {
-    nk = (t.kcount + KR - 1) / KR;
-    a_step = (size_t)KR * p.M * 2;
-    b_step = (size_t)KR * p.N * 2;
-#pragma unroll
-    for (int i = 0; i < C::A_LOADS; ++i) {
-      const int chunk = wave + C::NW * i;
-      int k, lb;
-      mn_slot<BM>(chunk, lane, k, lb);
-      const int col = t.m0 + lb / 2;
-      a_krow[i] = col < p.M ? k : 0x40000000;  // never valid when the column is out of range
-      a_src[i] = (const uint8_t*)p.A + ((size_t)(t.kbase + k) * p.M + (col < p.M ? col : 0)) * 2;
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_LOADS; ++i) {
-      const int chunk = wave + C::NW * i;
-      int k, lb;
-      mn_slot<BN>(chunk, lane, k, lb);
-      const int col = t.n0 + lb / 2;
-      b_krow[i] = col < p.N ? k : 0x40000000;
-      b_src[i] = (const uint8_t*)p.B + ((size_t)(t.kbase + k) * p.N + (col < p.N ? col : 0)) * 2;
-    }
-  }
+  };
 
-  // Load slot i < LOADS of stage kt: A chunk-loads first, then B.
-  auto issue_one = [&](int kt, uint8_t* sa, int i) __attribute__((always_inline)) {
+  // ---- load cursor: walks this block's tiles ahead of the multiply ---------------------
+  Tile lt;              // tile whose stages are being loaded
+  int lj = -1;          // its index in this block's sequence
+  int lk = 0, lnk = 0;  // next stage to load, stages of the tile
+  // Cursor state, one variable (separate flags end up in scratch memory once the compiler
+  // merges their stores): a stage is available to load, the next tile's ticket is not
+  // published yet, or the block's tiles are all loaded.
+  enum { L_END = 0, L_LIVE = 1, L_BLOCKED = 2 };
+  int l_state = L_END;
+  auto cursor_advance = [&]() __attribute__((always_inline)) {
+    int st = L_END;
+    for (;;) {
+      if (lj + 1 >= n_pub) {
+        st = L_BLOCKED;
+        break;
+      }
+      ++lj;
+      const int tl = tile_of(lj);
+      if (tl < 0) break;
+      lt = decode(tl);
+      lnk = stages_of(lt);
+      lk = 0;
+      if (lnk > 0) {
+        setup_loads(lt);
+        st = L_LIVE;
+        break;
+      }
+    }
+    l_state = __builtin_amdgcn_readfirstlane(st);
+  };
+  // Load slot i < LOADS of the cursor's stage lk: A chunk-loads first, then B.
+  auto issue_one = [&](uint8_t* sa, int i) __attribute__((always_inline)) {
     if (i < C::A_LOADS) {
-      const uint8_t* src;
-      if (DW) src = (kt * KR + a_krow[i] < t.kcount) ? a_src[i] + (size_t)kt * a_step : zero;
-      else src = a_src[i] == zero ? zero : a_src[i] + (size_t)kt * a_step;
-      load_lds16(src, sa + (wave + C::NW * i) * 1024);
+      uint8_t* dst = sa + (wave + C::NW * i) * 1024;
+      if constexpr (DW) {
+        load_lds16((lk * KR + a_krow[i] < lt.kcount) ? a_src[i] + (size_t)lk * a_step : zero, dst);
+      } else {
+        if (a_dead & (1 << i)) {
+          if (lane == 0) load_lds16(zero, dst);
+        } else {
+          load_lds16(a_src[i], dst);
+        }
+        a_src[i] += a_inc[i];
+      }
     } else {
       const int j = i - C::A_LOADS;
-      const uint8_t* src;
-      if (DW) src = (kt * KR + b_krow[j] < t.kcount) ? b_src[j] + (size_t)kt * b_step : zero;
-      else src = b_src[j] == zero ? zero : b_src[j] + (size_t)kt * b_step;
-      load_lds16(src, sa + C::A_BYTES + (wave + C::NW * j) * 1024);
+      uint8_t* dst = sa + C::A_BYTES + (wave + C::NW * j) * 1024;
+      if constexpr (DW) {
+        load_lds16((lk * KR + b_krow[j] < lt.kcount) ? b_src[j] + (size_t)lk * b_step : zero, dst);
+      } else {
+        load_lds16(b_src[j], dst);
+        b_src[j] += b_inc[j];
+      }
     }
   };
-  auto issue_stage = [&](int kt, uint8_t* sa) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) issue_one(kt, sa, i);
-  };
 
-  // ---- fragments --------------------------------------------------------------------
+  // ---- fragments ----------------------------------------------------------------------
+  // The MFMA takes the B fragment as its first operand, so each accumulator block holds
+  // C^T: lane l, element v -> output row l%32 of the block, output column
+  // 8*(v/4) + 4*(l/32) + v%4. Each lane thus owns runs of 4 consecutive output columns,
+  // which the epilogue writes straight from registers.
   f32x16_t acc[C::MB][C::NB];
-#pragma unroll
-  for (int i = 0; i < C::MB; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NB; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  // M blocks of this wave that hold at least one valid row (wave-uniform)
-  int mb_live = 0;
-#pragma unroll
-  for (int i = 0; i < C::MB; ++i)
-    if ((wm + WM * i) * 32 < t.rows_valid) mb_live = i + 1;
-  mb_live = __builtin_amdgcn_readfirstlane(mb_live);
-  nk = __builtin_amdgcn_readfirstlane(nk);
 
   // B block column (within the tile) of N block j of this wave. SwiGLU: the first NB/2
   // blocks are gate columns, the last NB/2 the matching up columns (offset HB).
@@ -448,15 +591,15 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
 #pragma unroll
       for (int j = 0; j < C::NB; ++j) {
         if constexpr (!FP8)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
         else
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], acc[i][j],
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j],
                                                                        0, 0, 0, 127, 0, 127);
       }
   };
   // One ring stage: KS k sub-steps; while sub-step ks multiplies, the fragments of ks+1
-  // are read and a slice of the loads of stage kt+2 (into `nxt`) is issued.
-  auto compute_stage = [&](auto MBL_c, const uint8_t* sa, int kt_next, uint8_t* nxt) __attribute__((always_inline)) {
+  // are read and a slice of the cursor's next stage (into `nxt`) is issued.
+  auto compute_stage = [&](auto MBL_c, const uint8_t* sa, bool iss, uint8_t* nxt) __attribute__((always_inline)) {
     constexpr int KS = FP8 ? BKB / 64 : BKB / 32;
     constexpr int PER = (C::LOADS + KS - 1) / KS;
     using frag_t = typename std::conditional<FP8, i32x8_t, bf16x8_t>::type;
@@ -465,268 +608,407 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 1 < KS) load_frags(MBL_c, sa, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
-      if (kt_next >= 0) {
+      if (iss) {
 #pragma unroll
-        for (int q = ks * PER; q < (ks + 1) * PER && q < C::LOADS; ++q) issue_one(kt_next, nxt, q);
+        for (int q = ks * PER; q < (ks + 1) * PER && q < C::LOADS; ++q) issue_one(nxt, q);
       }
       mfmas(MBL_c, af[ks & 1], bfr[ks & 1]);
     }
   };
 
-  // ---- main loop: ring of three LDS buffers, unrolled so each buffer is static ------
-  // step(kt): stage kt is complete in `cur` once this wave's loads for it have landed
-  // (at most the next stage's loads still in flight) and every wave passed the barrier;
-  // the loads for stage kt+2 go to `nxt`, which held stage kt-1, spread over the
-  // sub-steps of this stage's multiply.
-  auto buf = [&](int kt) __attribute__((always_inline)) { return smem + (kt % STAGES) * C::STAGE; };
-  auto main_loop = [&](auto MBL_c) __attribute__((always_inline)) {
-    constexpr int LEAD = STAGES - 1;  // stages in flight ahead of the one being multiplied
+  // ---- epilogue: per-wave staging, 16-byte row stores -------------------------------
+  // Each wave owns an LDS area outside the ring of 32 rows x SB bytes (SB = 128 when the
+  // budget allows: two 32-column bf16 blocks side by side, so every store covers whole
+  // 128-byte lines; else 64). Values go in as 8- or 16-byte pieces from the C^T layout, the
+  // 16-byte chunk index XORed with a row function so both the writes and the row reads are
+  // conflict-free, and come back as 16 consecutive bytes of one row per lane. Only this
+  // wave touches its area and LDS accesses of a wave complete in order: no barrier needed.
+  uint8_t* stg = s_epi + wave * (32 * SB);
+  constexpr int LPR = SB / 16, RPI = 64 / LPR, NRI = 32 / RPI;  // lanes/row, rows/read, reads
+  constexpr int PB = SB / 64;                                   // bf16 blocks per group
+  auto stg_addr = [&](int r, int chunk) __attribute__((always_inline)) -> uint8_t* {
+    const int sw = SB == 128 ? (r >> 1) & 7 : (r >> 2) & 3;
+    return stg + r * SB + ((chunk ^ sw) << 4);
+  };
+  // Store instructions per wave and epilogue (bf16 output; SwiGLU without / with g,u),
+  // the same for every tile: masked lanes store out of range instead of branching.
+  constexpr int NH_ = EPI == EPI_SWIGLU ? C::NB / 2 : 1;
+  constexpr int S_STORE = C::MB * (C::NB / PB) * NRI;
+  constexpr int S_SWIGLU = C::MB * (NH_ / PB) * NRI;
+  constexpr int S_SWIGLU_GU = 3 * S_SWIGLU;
+  constexpr int S1 = EPI == EPI_SWIGLU ? S_SWIGLU : S_STORE;
+  constexpr int S2 = EPI == EPI_SWIGLU ? S_SWIGLU_GU : S_STORE;
+  static_assert((EPI == EPI_SWIGLU ? NH_ : C::NB) % PB == 0, "staging groups");
+  auto epilogue = [&](const Tile& t) __attribute__((always_inline)) {
+    // Lane-derived row and column parts, made opaque so the address arithmetic below is
+    // not hoisted out of the tile loop (where it would sit in registers the whole time).
+    int l32 = lane & 31, kh = lane >> 5, rr = lane / LPR, cc = lane % LPR;
+    asm volatile("" : "+v"(l32), "+v"(kh), "+v"(rr), "+v"(cc));
+    // Stage a group of PB bf16 blocks (`val(b, q)`: the packed values of block b, 4-column
+    // run q) and store its 32 rows of PB*32 columns.
+    auto group_bf16 = [&](auto val, auto row_ok, auto col_ok, auto offset, const __amdgpu_buffer_rsrc_t& rs)
+        __attribute__((always_inline)) {
 #pragma unroll
-    for (int s0 = 0; s0 < LEAD; ++s0)
-      if (s0 < nk) issue_stage(s0, buf(s0));
-    for (int kt = 0; kt < nk; ++kt) {
-      // stage kt has landed once at most the later issued stages are still in flight
-      const int later = min(LEAD - 1, nk - 1 - kt);
-      if (LEAD - 1 >= 2 && later >= 2) wait_vmcnt<(LEAD >= 3 ? 2 : 0) * C::LOADS>();
-      else if (LEAD - 1 >= 1 && later >= 1) wait_vmcnt<C::LOADS>();
-      else wait_vmcnt<0>();
-      ring_barrier();  // every wave's loads for stage kt landed; stage kt-1 fully read
-      compute_stage(MBL_c, buf(kt), kt + LEAD < nk ? kt + LEAD : -1, buf(kt + LEAD));
+      for (int b = 0; b < PB; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int piece = 8 * b + 2 * q + kh;  // 8-byte piece of the staged row
+          *(u32x2_t*)(stg_addr(l32, piece >> 1) + (piece & 1) * 8) = val(b, q);
+        }
+#pragma unroll
+      for (int h = 0; h < NRI; ++h) {
+        const int r = rr + RPI * h;
+        const u32x4_t v = *(const u32x4_t*)stg_addr(r, cc);
+        const bool ok = row_ok(r) && col_ok(8 * cc);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, ok ? offset(r, 8 * cc) : kOutOfRange, 0, 0);
+      }
+    };
+    // Stage one fp32 block in 128 / SB passes of SB/4 columns; `use(r, c, v)` gets row r,
+    // first column c and the 4 values of each lane's 16-byte piece.
+    auto block_f32 = [&](const f32x16_t& a, auto use) __attribute__((always_inline)) {
+      constexpr int NP = 128 / SB, QP = 4 / NP;  // passes, 4-column runs per pass
+#pragma unroll
+      for (int ps = 0; ps < NP; ++ps) {
+#pragma unroll
+        for (int q = ps * QP; q < ps * QP + QP; ++q)
+          *(u32x4_t*)stg_addr(l32, 2 * (q - ps * QP) + kh) =
+              u32x4_t{__float_as_uint(a[4 * q]), __float_as_uint(a[4 * q + 1]),
+                      __float_as_uint(a[4 * q + 2]), __float_as_uint(a[4 * q + 3])};
+#pragma unroll
+        for (int h = 0; h < NRI; ++h) {
+          const int r = rr + RPI * h;
+          use(ps * NRI + h, r, ps * (SB / 4) + 4 * cc, *(const u32x4_t*)stg_addr(r, cc));
+        }
+      }
+    };
+    if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int NH = C::NB / 2;
+      const int twoI = 2 * p.I;
+      const auto hr = tile_rsrc((const uint16_t*)p.C + (size_t)t.m0 * p.I + t.n0);
+      const auto gr = tile_rsrc(p.gu_out ? (const uint16_t*)p.gu_out + (size_t)t.m0 * twoI + t.n0
+                                         : (const uint16_t*)p.C);
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i) {
+        const int r0 = (wm + WM * i) * 32;
+        float sa = 1.f;
+        if (FP8) sa = p.a_scale[t.m0 + (r0 + l32 < t.rows_valid ? r0 + l32 : 0)];
+        auto row_ok = [&](int r) { return r0 + r < t.rows_valid; };
+#pragma unroll
+        for (int jg0 = 0; jg0 < NH; jg0 += PB) {
+          const int hb = (wn * NH + jg0) * 32;  // first h column of the group within the tile
+          auto col_ok = [&](int c) { return t.n0 + hb + c < p.I; };
+          float g[PB][16], u[PB][16];
+#pragma unroll
+          for (int b = 0; b < PB; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              g[b][v] = acc[i][jg0 + b][v];
+              u[b][v] = acc[i][jg0 + b + NH][v];
+            }
+          if (FP8) {
+            const float* bs = p.b_scale + (size_t)t.g * twoI;
+#pragma unroll
+            for (int b = 0; b < PB; ++b)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int c = t.n0 + hb + 32 * b + 8 * q + 4 * kh;
+                const int cs = c < p.I ? c : 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  g[b][4 * q + r] *= sa * bs[cs + r];
+                  u[b][4 * q + r] *= sa * bs[p.I + cs + r];
+                }
+              }
+          }
+          group_bf16([&](int b, int q) {
+                       float hv[4];
+#pragma unroll
+                       for (int r = 0; r < 4; ++r) {
+                         const float gg = g[b][4 * q + r];
+                         hv[r] = gg * sigmoid_fast(gg) * u[b][4 * q + r];
+                       }
+                       return u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+                     },
+                     row_ok, col_ok, [&](int r, int c) { return ((r0 + r) * p.I + hb + c) * 2; }, hr);
+          if (p.gu_out) {
+            group_bf16([&](int b, int q) {
+                         return u32x2_t{pack_bf16x2(g[b][4 * q], g[b][4 * q + 1]),
+                                        pack_bf16x2(g[b][4 * q + 2], g[b][4 * q + 3])};
+                       },
+                       row_ok, col_ok, [&](int r, int c) { return ((r0 + r) * twoI + hb + c) * 2; }, gr);
+            group_bf16([&](int b, int q) {
+                         return u32x2_t{pack_bf16x2(u[b][4 * q], u[b][4 * q + 1]),
+                                        pack_bf16x2(u[b][4 * q + 2], u[b][4 * q + 3])};
+                       },
+                       row_ok, col_ok, [&](int r, int c) { return ((r0 + r) * twoI + p.I + hb + c) * 2; }, gr);
+          }
+        }
+      }
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+      // acc = dh[m, hcol] (fp32); with s = sigmoid(g): dgu[m] = [dh u s (1 + g (1 - s)), dh g s]
+      const int twoI = 2 * p.I;
+      const size_t org = (size_t)t.m0 * twoI + t.n0;
+      const auto dr = tile_rsrc((const uint16_t*)p.C + org);
+      const auto gi = tile_rsrc((const uint16_t*)p.gu_in + org);
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i) {
+        const int r0 = (wm + WM * i) * 32;
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j) {
+          const int c0 = bcol0(j);
+          // the saved g,u of the block's lanes, loaded up front (latency paid once per block)
+          constexpr int NPIECE = (128 / SB) * NRI;
+          int go[NPIECE], uo[NPIECE];
+          u32x2_t gv[NPIECE], uv[NPIECE];
+#pragma unroll
+          for (int x = 0; x < NPIECE; ++x) {
+            const int r = rr + RPI * (x % NRI);
+            const int c = (x / NRI) * (SB / 4) + 4 * cc;
+            const bool ok = r0 + r < t.rows_valid && t.n0 + c0 + c < p.N;
+            go[x] = ok ? ((r0 + r) * twoI + c0 + c) * 2 : kOutOfRange;
+            uo[x] = ok ? go[x] + p.I * 2 : kOutOfRange;
+            gv[x] = __builtin_amdgcn_raw_buffer_load_b64(gi, go[x], 0, 0);
+            uv[x] = __builtin_amdgcn_raw_buffer_load_b64(gi, uo[x], 0, 0);
+          }
+          block_f32(acc[i][j], [&](int x, int r, int c, u32x4_t dv) {
+            float dg[4], du[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t gw = gv[x][e >> 1], uw = uv[x][e >> 1];
+              const float gg = (e & 1) ? bf16hi(gw) : bf16lo(gw);
+              const float uu = (e & 1) ? bf16hi(uw) : bf16lo(uw);
+              const float dh = __uint_as_float(dv[e]);
+              const float sg = sigmoid_fast(gg);
+              dg[e] = dh * uu * sg * (1.0f + gg * (1.0f - sg));
+              du[e] = dh * gg * sg;
+            }
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])},
+                                                  dr, go[x], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])},
+                                                  dr, uo[x], 0, 0);
+          });
+        }
+      }
+    } else {
+      const int mlim = DW ? p.M - t.m0 : t.rows_valid;
+      const size_t org = DW ? (size_t)t.g * p.M * p.N + (size_t)t.m0 * p.N + t.n0
+                            : (size_t)t.m0 * p.N + t.n0;
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i) {
+        const int r0 = (wm + WM * i) * 32;
+        float sa = 1.f;
+        if (FP8) sa = p.a_scale[t.m0 + (r0 + l32 < mlim ? r0 + l32 : 0)];
+        auto row_ok = [&](int r) { return r0 + r < mlim; };
+        float v[C::NB][16];
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) v[j][e] = acc[i][j][e];
+          if (FP8) {
+            const int c0 = bcol0(j);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c = t.n0 + c0 + 8 * q + 4 * kh;
+              const float* bs = p.b_scale + (size_t)t.g * p.N + (c < p.N ? c : 0);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v[j][4 * q + r] *= sa * bs[r];
+            }
+          }
+        }
+        if (p.c_fp32) {
+          const auto cr = tile_rsrc((const float*)p.C + org);
+#pragma unroll
+          for (int j = 0; j < C::NB; ++j) {
+            const int c0 = bcol0(j);
+            f32x16_t a;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) a[e] = v[j][e];
+            block_f32(a, [&](int, int r, int c, u32x4_t x) {
+              const bool ok = row_ok(r) && t.n0 + c0 + c < p.N;
+              __builtin_amdgcn_raw_buffer_store_b128(x, cr, ok ? ((r0 + r) * p.N + c0 + c) * 4 : kOutOfRange, 0, 0);
+            });
+          }
+        } else {
+          const auto cr = tile_rsrc((const uint16_t*)p.C + org);
+#pragma unroll
+          for (int j0 = 0; j0 < C::NB; j0 += PB) {
+            const int c0 = bcol0(j0);
+            auto col_ok = [&](int c) { return t.n0 + c0 + c < p.N; };
+            group_bf16([&](int b, int q) {
+                         return u32x2_t{pack_bf16x2(v[j0 + b][4 * q], v[j0 + b][4 * q + 1]),
+                                        pack_bf16x2(v[j0 + b][4 * q + 2], v[j0 + b][4 * q + 3])};
+                       },
+                       row_ok, col_ok, [&](int r, int c) { return ((r0 + r) * p.N + c0 + c) * 2; }, cr);
+          }
+        }
+      }
+    }
+  };
+
+  // ---- the stage stream -----------------------------------------------------------------
+  // Stream stages are numbered over all of this block's tiles: gs is the next stage to
+  // multiply, gl the next to load, gl - gs <= LEAD. With `cross`, the cursor runs into the
+  // next tile while the current one finishes, so the next tile's first stages are in flight
+  // during the epilogue (whose stores then sit between those loads and their wait). Without
+  // it (epilogues that read global memory, fp32 output) each tile starts with its own
+  // prologue after the previous epilogue.
+  constexpr bool CROSS = !FP8 && EPI != EPI_SWIGLU_BWD;
+  const bool cross = CROSS && !p.c_fp32;
+  const int s_allow = (EPI == EPI_SWIGLU && p.gu_out) ? 2 : 1;
+  auto buf = [&](int s) __attribute__((always_inline)) { return smem + (s % STAGES) * C::STAGE; };
+  int gs = 0, gl = 0;
+  int epi1 = -1, epi2 = -1;  // gl at the last two epilogues: stages below were loaded before their stores
+  int cj = 0;
+  auto run_tile = [&](auto MBL_c, int cnk) __attribute__((always_inline)) {
+    for (int kt = 0; kt < cnk; ++kt) {
+      const int pend = gl - gs - 1;  // stages loaded after this one
+      const int allow = gs < epi2 ? 0 : (gs < epi1 ? s_allow : 0);
+      wait_stage<C::LOADS, S1, S2>(pend, allow);
+      ring_barrier();  // every wave's loads for stage gs landed; stage gs-1 fully read
+      const bool iss = l_state == L_LIVE && (cross || lj == cj);
+      compute_stage(MBL_c, buf(gs), iss, buf(gl));
+      if (iss) {
+        ++gl;
+        if (++lk == lnk) cursor_advance();
+      }
+      ++gs;
     }
   };
   static_assert(C::MB <= 4, "live-block dispatch below covers up to four M blocks per wave");
-  // Every wave runs the loop: it issues its share of each stage's loads and takes part
-  // in every barrier even when none of its M blocks holds a valid row (MBL = 0).
-  switch (mb_live) {
-    case 0: main_loop(std::integral_constant<int, 0>{}); break;
-    case 1: main_loop(std::integral_constant<int, 1>{}); break;
-    case 2: if constexpr (C::MB >= 2) main_loop(std::integral_constant<int, 2>{}); break;
-    case 3: if constexpr (C::MB >= 3) main_loop(std::integral_constant<int, 3>{}); break;
-    default: if constexpr (C::MB >= 4) main_loop(std::integral_constant<int, 4>{}); break;
-  }
-  wait_vmcnt<0>();
-  __syncthreads();
 
-  // ---- epilogue: stage row slices of the tile in LDS, then 16-byte stores ----------
-  // 32x32 accumulator layout: lane l, element v -> column l%32, row 8*(v/4) + 4*(l/32) + v%4.
-  // A slice of PR rows holds the M blocks (wm + WM*i) whose rows fall inside it.
-  const int rb = 4 * khalf;
-  if (EPI == EPI_SWIGLU) {
-    // h slice [PR][HB] bf16 in the first half of the ring, g,u slice [PR][BN] in the second
-    constexpr int HP = HB * 2 + 16, GP = BN * 2 + 16;
-    constexpr int PR = slice_rows(BM, GP, C::SMEM / 2);
-    static_assert(PR * GP <= C::SMEM / 2 && PR * HP <= C::SMEM / 2, "slice");
-    uint8_t* sh = smem;
-    uint8_t* sgu = smem + C::SMEM / 2;
-    constexpr int NH = C::NB / 2;
-    const size_t twoI = 2 * (size_t)p.I;
-    for (int r0 = 0; r0 < t.rows_valid; r0 += PR) {
+  cursor_advance();
+  for (;; ++cj) {
+    const int tc = tile_of(cj);
+    if (tc < 0) break;
+    const Tile ct = decode(tc);
+    const int cnk = stages_of(ct);
+    // prologue: fill the ring up to LEAD stages ahead (a no-op while the stream is primed)
+    while (l_state == L_LIVE && (cross || lj == cj) && gl < gs + LEAD) {
 #pragma unroll
-      for (int jg = 0; jg < NH; ++jg) {
-        const int hc = (wn * NH + jg) * 32 + l32;   // h column within the tile
-        float sg = 1.f, su = 1.f;
-        if (FP8 && t.n0 + hc < p.I) {
-          sg = p.b_scale[(size_t)t.g * twoI + t.n0 + hc];
-          su = p.b_scale[(size_t)t.g * twoI + p.I + t.n0 + hc];
-        }
-#pragma unroll
-        for (int i = 0; i < C::MB; ++i) {
-          const int blk = (wm + WM * i) * 32;
-          if (i >= mb_live || blk < r0 || blk >= r0 + PR) continue;
-#pragma unroll
-          for (int v = 0; v < 16; v += 2) {  // rows r and r+1 share one packed convert
-            const int r = blk + 8 * (v >> 2) + rb + (v & 3);
-            float g0 = acc[i][jg][v], u0 = acc[i][jg + NH][v];
-            float g1 = acc[i][jg][v + 1], u1 = acc[i][jg + NH][v + 1];
-            if (FP8) {
-              const float sa0 = r < t.rows_valid ? p.a_scale[t.m0 + r] : 0.f;
-              const float sa1 = r + 1 < t.rows_valid ? p.a_scale[t.m0 + r + 1] : 0.f;
-              g0 *= sa0 * sg;
-              u0 *= sa0 * su;
-              g1 *= sa1 * sg;
-              u1 *= sa1 * su;
-            }
-            const uint32_t hv = pack_bf16x2(g0 * sigmoid_fast(g0) * u0, g1 * sigmoid_fast(g1) * u1);
-            uint8_t* hrow = sh + (r - r0) * HP + hc * 2;
-            *(uint16_t*)hrow = (uint16_t)hv;
-            *(uint16_t*)(hrow + HP) = (uint16_t)(hv >> 16);
-            if (p.gu_out) {
-              const uint32_t gv = pack_bf16x2(g0, g1), uv = pack_bf16x2(u0, u1);
-              uint8_t* grow = sgu + (r - r0) * GP + hc * 2;
-              *(uint16_t*)grow = (uint16_t)gv;
-              *(uint16_t*)(grow + GP) = (uint16_t)(gv >> 16);
-              *(uint16_t*)(grow + HB * 2) = (uint16_t)uv;
-              *(uint16_t*)(grow + GP + HB * 2) = (uint16_t)(uv >> 16);
-            }
-          }
-        }
-      }
-      __syncthreads();
-      constexpr int HV = HB / 8;  // 16-byte vectors per h row
-      for (int idx = tid; idx < PR * HV; idx += C::NT) {
-        const int r = idx / HV, c = idx % HV;
-        if (r0 + r < t.rows_valid && t.n0 + c * 8 < p.I) {
-          const u32x4_t v = *(const u32x4_t*)(sh + r * HP + c * 16);
-          *(u32x4_t*)((uint16_t*)p.C + (size_t)(t.m0 + r0 + r) * p.I + t.n0 + c * 8) = v;
-        }
-      }
-      if (p.gu_out) {
-        constexpr int GV = BN / 8;
-        for (int idx = tid; idx < PR * GV; idx += C::NT) {
-          const int r = idx / GV, c = idx % GV;
-          const int hcol = t.n0 + (c < HV ? c : c - HV) * 8;
-          if (r0 + r < t.rows_valid && hcol < p.I) {
-            const u32x4_t v = *(const u32x4_t*)(sgu + r * GP + c * 16);
-            const int col = c < HV ? hcol : p.I + hcol;
-            *(u32x4_t*)((uint16_t*)p.gu_out + (size_t)(t.m0 + r0 + r) * twoI + col) = v;
-          }
-        }
-      }
-      __syncthreads();
+      for (int i = 0; i < C::LOADS; ++i) issue_one(buf(gl), i);
+      ++gl;
+      if (++lk == lnk) cursor_advance();
     }
-  } else if (EPI == EPI_SWIGLU_BWD || p.c_fp32) {
-    // fp32 slice [PR][BN] in the ring
-    constexpr int FP = BN * 4 + 16;
-    constexpr int PR = slice_rows(BM, FP, C::SMEM);
-    static_assert(PR * FP <= C::SMEM, "slice");
-    uint8_t* sf = smem;
-    for (int r0 = 0; r0 < t.rows_valid; r0 += PR) {
 #pragma unroll
-      for (int i = 0; i < C::MB; ++i) {
-        const int blk = (wm + WM * i) * 32;
-        if (i >= mb_live || blk < r0 || blk >= r0 + PR) continue;
+    for (int i = 0; i < C::MB; ++i)
 #pragma unroll
-        for (int j = 0; j < C::NB; ++j) {
-          const int c = bcol0(j) + l32;
+      for (int j = 0; j < C::NB; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = blk + 8 * (v >> 2) + rb + (v & 3);
-            *(float*)(sf + (r - r0) * FP + c * 4) = acc[i][j][v];
-          }
-        }
-      }
-      __syncthreads();
-      constexpr int V8 = BN / 8;  // 8-column groups per row
-      for (int idx = tid; idx < PR * V8; idx += C::NT) {
-        const int r = idx / V8, c8 = idx % V8;
-        const int col = t.n0 + c8 * 8;
-        const int rr = r0 + r;
-        if (rr >= t.rows_valid || col >= p.N) continue;
-        if (DW && t.m0 + rr >= p.M) continue;
-        const f32x4_t x0 = *(const f32x4_t*)(sf + r * FP + c8 * 32);
-        const f32x4_t x1 = *(const f32x4_t*)(sf + r * FP + c8 * 32 + 16);
-        float val[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        if (EPI == EPI_SWIGLU_BWD) {
-          const size_t twoI = 2 * (size_t)p.I;
-          const size_t row = (size_t)t.m0 + rr;
-          const u32x4_t gv = *(const u32x4_t*)((const uint16_t*)p.gu_in + row * twoI + col);
-          const u32x4_t uv = *(const u32x4_t*)((const uint16_t*)p.gu_in + row * twoI + p.I + col);
-          u32x4_t dg, du;
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    // M blocks of this wave that hold at least one valid row (wave-uniform)
+    int mb_live = 0;
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            float o[4];
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              const float g = h2 ? bf16hi(gv[d]) : bf16lo(gv[d]);
-              const float u = h2 ? bf16hi(uv[d]) : bf16lo(uv[d]);
-              const float dh = val[2 * d + h2];
-              const float sgm = sigmoid_fast(g);
-              o[h2] = dh * u * sgm * (1.0f + g * (1.0f - sgm));
-              o[2 + h2] = dh * g * sgm;
-            }
-            dg[d] = pack_bf16x2(o[0], o[1]);
-            du[d] = pack_bf16x2(o[2], o[3]);
-          }
-          *(u32x4_t*)((uint16_t*)p.C + row * twoI + col) = dg;
-          *(u32x4_t*)((uint16_t*)p.C + row * twoI + p.I + col) = du;
-        } else {
-          const size_t o = DW ? (size_t)t.g * p.M * p.N + (size_t)(t.m0 + rr) * p.N + col
-                              : (size_t)(t.m0 + rr) * p.N + col;
-          if (FP8) {
-            const float sa = p.a_scale[t.m0 + rr];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) val[e] *= sa * p.b_scale[(size_t)t.g * p.N + col + e];
-          }
-          *(f32x4_t*)((float*)p.C + o) = f32x4_t{val[0], val[1], val[2], val[3]};
-          *(f32x4_t*)((float*)p.C + o + 4) = f32x4_t{val[4], val[5], val[6], val[7]};
-        }
-      }
-      __syncthreads();
+    for (int i = 0; i < C::MB; ++i)
+      if ((wm + WM * i) * 32 < ct.rows_valid) mb_live = i + 1;
+    mb_live = __builtin_amdgcn_readfirstlane(mb_live);
+    // Every wave runs the stages: it issues its share of each stage's loads and takes part
+    // in every barrier even when none of its M blocks holds a valid row (MBL = 0).
+    switch (mb_live) {
+      case 0: run_tile(std::integral_constant<int, 0>{}, cnk); break;
+      case 1: run_tile(std::integral_constant<int, 1>{}, cnk); break;
+      case 2: if constexpr (C::MB >= 2) run_tile(std::integral_constant<int, 2>{}, cnk); break;
+      case 3: if constexpr (C::MB >= 3) run_tile(std::integral_constant<int, 3>{}, cnk); break;
+      default: if constexpr (C::MB >= 4) run_tile(std::integral_constant<int, 4>{}, cnk); break;
     }
-  } else {
-    // bf16 slice [PR][BN] in the ring
-    constexpr int CP = BN * 2 + 16;
-    constexpr int PR = slice_rows(BM, CP, C::SMEM);
-    static_assert(PR * CP <= C::SMEM, "slice");
-    uint8_t* sc = smem;
-    for (int r0 = 0; r0 < t.rows_valid; r0 += PR) {
-#pragma unroll
-      for (int i = 0; i < C::MB; ++i) {
-        const int blk = (wm + WM * i) * 32;
-        if (i >= mb_live || blk < r0 || blk >= r0 + PR) continue;
-#pragma unroll
-        for (int j = 0; j < C::NB; ++j) {
-          const int c = bcol0(j) + l32;
-          float sb = 1.f;
-          if (FP8) sb = (t.n0 + c < p.N) ? p.b_scale[(size_t)t.g * p.N + t.n0 + c] : 0.f;
-#pragma unroll
-          for (int v = 0; v < 16; v += 2) {  // rows r and r+1 share one packed convert
-            const int r = blk + 8 * (v >> 2) + rb + (v & 3);
-            float v0 = acc[i][j][v], v1 = acc[i][j][v + 1];
-            if (FP8) {
-              v0 = r < t.rows_valid ? v0 * p.a_scale[t.m0 + r] * sb : 0.f;
-              v1 = r + 1 < t.rows_valid ? v1 * p.a_scale[t.m0 + r + 1] * sb : 0.f;
-            }
-            const uint32_t pk = pack_bf16x2(v0, v1);
-            uint8_t* crow = sc + (r - r0) * CP + c * 2;
-            *(uint16_t*)crow = (uint16_t)pk;
-            *(uint16_t*)(crow + CP) = (uint16_t)(pk >> 16);
-          }
+    epilogue(ct);
+    epi2 = epi1;
+    epi1 = gl;
+    if constexpr (DYN) {
+      if (wave == 0) {
+        // this wave's stores and the ticket requested one epilogue ago have landed
+        wait_vmcnt<0>();
+        if (lane == 0) {
+          if (pend_tk) s_tk[n_pub & 7] = tk;
+          if (sched_open) tk = atomicAdd(ctr, 1);
         }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the ticket is in LDS before the barrier
       }
-      __syncthreads();
-      constexpr int V8 = BN / 8;
-      for (int idx = tid; idx < PR * V8; idx += C::NT) {
-        const int r = idx / V8, c8 = idx % V8;
-        const int col = t.n0 + c8 * 8;
-        const int rr = r0 + r;
-        if (rr >= t.rows_valid || col >= p.N) continue;
-        if (DW && t.m0 + rr >= p.M) continue;
-        const size_t o = DW ? (size_t)t.g * p.M * p.N + (size_t)(t.m0 + rr) * p.N + col
-                            : (size_t)(t.m0 + rr) * p.N + col;
-        *(u32x4_t*)((uint16_t*)p.C + o) = *(const u32x4_t*)(sc + r * CP + c8 * 16);
+      if (pend_tk) ++n_pub;
+      pend_tk = sched_open ? 1 : 0;
+      ring_barrier();
+      if (sched_open) sched_open = s_tk[(n_pub - 1) & 7] + r_start < r_end;
+      if (l_state == L_BLOCKED) cursor_advance();
+    }
+  }
+  // the last block to finish resets the launch's counters for the next user of the slot
+  if constexpr (DYN) {
+    if (tid == 0) {
+      wait_vmcnt<0>();
+      __threadfence();
+      if (atomicAdd(&g_sched[p.sched_slot][8], 1) == (int)gridDim.x - 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g_sched[p.sched_slot][i] = 0;
+        g_sched[p.sched_slot][8] = 0;
+        __threadfence();
       }
-      __syncthreads();
     }
   }
 }
 
 namespace {
 
+// Resident blocks of one kernel on the current device (compute units x blocks per CU),
+// queried once per device and instantiation.
+template <typename K>
+int persistent_blocks(K kern, int threads) {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0) != hipSuccess) return 0;
+    cache[dev] = cus * (occ > 0 ? occ : 1);
+  }
+  return cache[dev];
+}
+
+int g_max_blocks = 0;  // grid cap set through moe_set_gemm_max_blocks (0: none)
+std::atomic<unsigned> g_launch_seq{0};  // picks the tile-counter slot of each launch
+
 template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int BKB>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   using C = Cfg<BM, BN, WM, WN, STAGES, BKB>;
   auto kern = grouped_gemm_kernel<MODE, EPI, FP8, BM, BN, WM, WN, STAGES, BKB>;
-  static_assert(C::SMEM + 264 * 4 <= 160 * 1024, "LDS budget");
+  static_assert(C::SMEM + 2 * 264 * 4 + 64 + C::NW * 2048 <= 160 * 1024, "LDS budget");
   const int ntn = EPI == EPI_SWIGLU ? (p.I + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
-  long long blocks;
-  if (MODE == MOE_GEMM_TN_DW) blocks = (long long)p.G * ((p.M + BM - 1) / BM) * ntn;
-  else blocks = ((long long)(p.rows + BM - 1) / BM + p.G) * ntn;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  kern<<<dim3((unsigned)blocks), dim3(C::NT), 0, s>>>(p);
+  // upper bound of the tile count (the exact count depends on offsets[], read on the device)
+  long long tiles;
+  if (MODE == MOE_GEMM_TN_DW) tiles = (long long)p.G * ((p.M + BM - 1) / BM) * ntn;
+  else tiles = ((long long)(p.rows + BM - 1) / BM + p.G) * ntn;
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  // epilogue offsets are 32-bit byte offsets from a tile's first output element
+  const long long row_bytes = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD) ? 4LL * p.I
+                                                                          : (long long)p.N * (p.c_fp32 ? 4 : 2);
+  if ((long long)BM * row_bytes >= kOutOfRange) return hipErrorInvalidValue;
+  const int resident = persistent_blocks(kern, C::NT);
+  if (resident <= 0) return hipErrorInvalidValue;
+  long long grid = tiles < resident ? tiles : resident;
+  if (g_max_blocks > 0 && grid > g_max_blocks) grid = g_max_blocks;
+  GemmParams q = p;
+  q.sched_slot = (int)(g_launch_seq.fetch_add(1, std::memory_order_relaxed) % kSchedSlots);
+  kern<<<dim3((unsigned)grid), dim3(C::NT), 0, s>>>(q);
   return hipGetLastError();
 }
 
 }  // namespace
 
 // Tile configurations (BM, BN, WM, WN, STAGES, K bytes per stage), chosen by
-// measurement on the Qwen3- and Mixtral-shaped expert GEMMs: bf16 uses 256x256 tiles with
-// eight waves (two per SIMD, 128x64 each) and a four-stage ring of 64-byte K steps (three
-// stages of loads in flight); e4m3 uses 256x128 tiles with four waves and a three-stage
+// measurement on the Qwen3- and Mixtral-shaped expert GEMMs. bf16: 256x256 tiles with eight
+// waves (two per SIMD, 128x64 each; the SwiGLU forward 64x128 each, so that a wave's h, g
+// and u rows are 64 columns wide) and a three-stage ring of 64-byte K steps; the SwiGLU
+// backward (whose epilogue reads the saved g,u) 256x128 tiles with four waves and a
+// three-stage ring of 128-byte steps. e4m3: 256x128 tiles with four waves and a three-stage
 // ring of 128-byte steps (its eight-wave build does not fit the register file).
 #ifndef MOE_GEMM_TILE_BF16
-#define MOE_GEMM_TILE_BF16 256, 256, 2, 4, 4, 64
+#define MOE_GEMM_TILE_BF16 256, 256, 2, 4, 3, 64
+#endif
+#ifndef MOE_GEMM_TILE_BF16_SWIGLU
+#define MOE_GEMM_TILE_BF16_SWIGLU 256, 256, 4, 2, 3, 64
+#endif
+#ifndef MOE_GEMM_TILE_BF16_SWIGLU_BWD
+#define MOE_GEMM_TILE_BF16_SWIGLU_BWD 256, 128, 2, 2, 3, 128
 #endif
 #ifndef MOE_GEMM_TILE_FP8
 #define MOE_GEMM_TILE_FP8 256, 128, 2, 2, 3, 128
@@ -749,10 +1031,14 @@ hipError_t launch_sel(const GemmParams& p, hipStream_t s) {
       if (p.rows <= 256 && p.rows <= 32 * p.G)
         return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_SMALL_M>(p, s);
     }
-    return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16>(p, s);
+    if constexpr (EPI == EPI_SWIGLU_BWD) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU_BWD>(p, s);
+    else if constexpr (EPI == EPI_SWIGLU) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU>(p, s);
+    else return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16>(p, s);
   }
 }
 }  // namespace
+
+void set_gemm_max_blocks(int n) { g_max_blocks = n; }
 
 hipError_t launch_grouped_gemm(const GemmParams& p, hipStream_t s) {
   if (p.G <= 0) return hipSuccess;

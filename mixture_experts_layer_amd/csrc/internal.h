@@ -55,7 +55,10 @@ struct GemmParams {
   int I;                 // SwiGLU width (EPI_SWIGLU: N = 2I; EPI_SWIGLU_BWD: N = I)
   void* gu_out;          // EPI_SWIGLU: optional saved g,u [rows,2I]
   const void* gu_in;     // EPI_SWIGLU_BWD: saved g,u [rows,2I]
+  int sched_slot;        // tile-counter slot of the launch (set by the launcher)
 };
 hipError_t launch_grouped_gemm(const GemmParams& p, hipStream_t s);
+// Grid cap of the persistent grouped-GEMM launches (0: every resident block).
+void set_gemm_max_blocks(int n);
 
 }  // namespace moe

@@ -103,6 +103,12 @@ const char* moe_status_str(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
+moe_status_t moe_set_gemm_max_blocks(int max_blocks) {
+  MOE_REQUIRE(max_blocks >= 0, MOE_ERR_INVALID_ARG);
+  moe::set_gemm_max_blocks(max_blocks);
+  return MOE_OK;
+}
+
 moe_status_t moe_router_topk(const float* logits, int T, int E, int k, int score,
                              int32_t* topk_idx, float* topk_prob, int32_t* counts,
                              uint8_t* routing_map, float* probs_dense, void* stream) {

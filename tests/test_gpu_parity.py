@@ -263,6 +263,124 @@ def test_grouped_gemm_swiglu_bwd():
     check_bf16(host_vals(dgu), np.concatenate([dg, du], 1), "dgu")
 
 
+# ---- persistent grid: many tiles per block -------------------------------------------------
+# With the grid capped, every block walks a long run of tiles: bf16 epilogues overlap the
+# next tile's loads (their stores counted in the wait), fp32 / SwiGLU-backward / fp8
+# epilogues drain between tiles, and weight-gradient tiles of empty experts have no stages.
+
+STREAM_COUNTS = [300, 0, 257, 1, 511, 0, 0, 64, 700, 33, 0, 256, 255, 129, 0, 400]
+
+
+@pytest.fixture
+def grid_cap():
+    yield M.moe_set_gemm_max_blocks
+    M.moe_set_gemm_max_blocks(0)
+
+
+@pytest.mark.parametrize("cap", [1, 3, 16])
+def test_gemm_many_tiles_per_block(cap, grid_cap):
+    grid_cap(cap)
+    counts = STREAM_COUNTS
+    offs = _groups(counts)
+    rows, G = int(offs[-1]), len(counts)
+    K, N, I = 192, 320, 192
+    _say("stream", cap)
+    rng = np.random.default_rng(20 + cap)
+    a = W.to_bf16_bits(rng.standard_normal((rows, K)).astype(np.float32))
+    av = O.bf16_bits_to_f64(a)
+    b = W.to_bf16_bits(rng.standard_normal((G, K, N)).astype(np.float32) * 0.05)
+    ref = O.grouped_gemm(av, b, offs)
+    for mode in (M.MOE_GEMM_NN, M.MOE_GEMM_NT):
+        bdev = dev_bf16(b) if mode == M.MOE_GEMM_NN else dev_bf16(np.ascontiguousarray(np.swapaxes(b, 1, 2)))
+        for out_dt in (torch.bfloat16, torch.float32):
+            c = torch.full((rows, N), float("nan"), dtype=out_dt, device="cuda")
+            M.moe_grouped_gemm(mode, dev_bf16(a), bdev, dev(offs), c)
+            torch.cuda.synchronize()
+            r = O.to_bf16(ref) if out_dt == torch.bfloat16 else ref
+            check_bf16(host_vals(c), r, f"stream cap={cap} mode={mode} {out_dt}",
+                       max_abs=2e-2 if out_dt == torch.bfloat16 else 1e-3)
+
+    # SwiGLU with and without the saved g,u (two epilogue store counts)
+    wgu = W.to_bf16_bits(rng.standard_normal((G, K, 2 * I)).astype(np.float32) * 0.05)
+    h1 = torch.full((rows, I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gu = torch.full((rows, 2 * I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    h2 = torch.full((rows, I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.moe_grouped_gemm_swiglu(dev_bf16(a), dev_bf16(wgu), dev(offs), h1, gu)
+    M.moe_grouped_gemm_swiglu(dev_bf16(a), dev_bf16(wgu), dev(offs), h2, None)
+    torch.cuda.synchronize()
+    r = O.expert_mlp(av, wgu, np.zeros((G, I, 8)), offs, I)
+    check_bf16(host_vals(h1), r["h"], f"stream cap={cap} swiglu h")
+    check_bf16(host_vals(gu), np.concatenate([r["g"], r["u"]], 1), f"stream cap={cap} swiglu gu")
+    assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))
+
+    # SwiGLU backward: dh = d_out W_down^T, then the gate/up gradients
+    d_out = W.to_bf16_bits(rng.standard_normal((rows, K)).astype(np.float32))
+    wd = W.to_bf16_bits(rng.standard_normal((G, I, K)).astype(np.float32) * 0.05)
+    gub = host_bits(gu)
+    dgu = torch.full((rows, 2 * I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.moe_grouped_gemm_swiglu_bwd(dev_bf16(d_out), dev_bf16(wd), dev(offs), dev_bf16(gub), dgu)
+    torch.cuda.synchronize()
+    dh = O.grouped_gemm(O.bf16_bits_to_f64(d_out), np.swapaxes(wd, 1, 2), offs)
+    dg, du = O.swiglu_backward(dh, O.bf16_bits_to_f64(gub[:, :I]), O.bf16_bits_to_f64(gub[:, I:]))
+    check_bf16(host_vals(dgu), np.concatenate([dg, du], 1), f"stream cap={cap} swiglu bwd")
+
+    # weight gradient, bf16 and fp32 output; empty experts get zero tiles
+    Md, Nd = 192, 256
+    wa = W.to_bf16_bits(rng.standard_normal((rows, Md)).astype(np.float32))
+    wb = W.to_bf16_bits(rng.standard_normal((rows, Nd)).astype(np.float32) * 0.1)
+    dref = O.grouped_gemm_dw(O.bf16_bits_to_f64(wa), O.bf16_bits_to_f64(wb), offs)
+    for out_dt in (torch.bfloat16, torch.float32):
+        c = torch.full((G, Md, Nd), float("nan"), dtype=out_dt, device="cuda")
+        M.moe_grouped_gemm(M.MOE_GEMM_TN_DW, dev_bf16(wa), dev_bf16(wb), dev(offs), c)
+        torch.cuda.synchronize()
+        r = O.to_bf16(dref) if out_dt == torch.bfloat16 else dref
+        check_bf16(host_vals(c), r, f"stream cap={cap} dw {out_dt}",
+                   max_abs=2e-2 if out_dt == torch.bfloat16 else 1e-3)
+        for g in range(G):
+            if counts[g] == 0:
+                assert not host_vals(c[g]).any()
+
+
+@pytest.mark.parametrize("cap", [1, 5])
+def test_gemm_fp8_and_small_m_many_tiles(cap, grid_cap):
+    grid_cap(cap)
+    _say("stream fp8/small-M", cap)
+    rng = np.random.default_rng(40 + cap)
+    counts = STREAM_COUNTS
+    offs = _groups(counts)
+    rows, G = int(offs[-1]), len(counts)
+    K, N = 256, 384
+    a_bits = W.to_bf16_bits(rng.standard_normal((rows, K)).astype(np.float32))
+    b_bits = W.to_bf16_bits(rng.standard_normal((G, K, N)).astype(np.float32) * 0.02)
+    aq = torch.empty((rows, K), dtype=torch.uint8, device="cuda")
+    as_ = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8_rows(dev_bf16(a_bits), aq, as_)
+    bq = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    bs = torch.empty((G, N), dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8_weights(dev_bf16(b_bits), bq, bs)
+    c = torch.full((rows, N), float("nan"), dtype=torch.float32, device="cuda")
+    M.moe_grouped_gemm(M.MOE_GEMM_NT, aq, bq, dev(offs), c, M.MOE_FP8_E4M3, as_, bs)
+    torch.cuda.synchronize()
+    qa, sa = O.quantize_rows_e4m3(O.bf16_bits_to_f64(a_bits))
+    ref = O.grouped_gemm(O.e4m3_decode(qa), b_bits, offs, False, sa, quantize_b=True)
+    check_bf16(host_vals(c), ref, f"stream cap={cap} fp8", max_abs=1e-3, rel_l2=1e-4)
+
+    # decode shape: a few rows per expert take the small-M tiles
+    dcounts = [3, 0, 1, 8, 2, 0, 5, 1, 0, 4, 2, 6]
+    doffs = _groups(dcounts)
+    drows, dG = int(doffs[-1]), len(dcounts)
+    Hd, Id = 256, 320
+    x = W.to_bf16_bits(rng.standard_normal((drows, Hd)).astype(np.float32))
+    wgu = W.to_bf16_bits(rng.standard_normal((dG, Hd, 2 * Id)).astype(np.float32) * 0.05)
+    h = torch.full((drows, Id), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gu = torch.full((drows, 2 * Id), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.moe_grouped_gemm_swiglu(dev_bf16(x), dev_bf16(wgu), dev(doffs), h, gu)
+    torch.cuda.synchronize()
+    r = O.expert_mlp(O.bf16_bits_to_f64(x), wgu, np.zeros((dG, Id, 8)), doffs, Id)
+    check_bf16(host_vals(h), r["h"], f"stream cap={cap} small-M swiglu h")
+    check_bf16(host_vals(gu), np.concatenate([r["g"], r["u"]], 1), f"stream cap={cap} small-M gu")
+
+
 def test_quantize_weights_bit_exact():
     rng = np.random.default_rng(9)
     G, K, N = 3, 320, 192
