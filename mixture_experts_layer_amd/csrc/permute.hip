@@ -22,10 +22,10 @@
 namespace moe {
 
 int router_chunk_tokens(int T) {
-  // whole-token chunks for the fused router histogram: at most 512 chunks, 8 tokens or more
+  // whole-token chunks for the fused router histogram: at most 512 chunks, a multiple of
+  // 32 tokens (one router block step)
   int c = (T + 511) / 512;
-  c = (c + 3) / 4 * 4;
-  return c < 8 ? 8 : c;
+  return (c + 31) / 32 * 32;
 }
 
 size_t permute_scratch_bytes(int T, int E, int k) {
@@ -50,28 +50,45 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
   for (int e = threadIdx.x; e < E; e += 256) partial[(size_t)blockIdx.x * E + e] = h[e];
 }
 
-// One block of 1024 threads: thread (part, e) with part = tid/256 sums a quarter of the
-// chunks of expert e; totals -> counts and offsets (exclusive scan over e), then each
-// part writes the running row base of its chunks.
+// One block of 1024 threads: thread (part, e), e < EP (E rounded up to 64, 128 or 256),
+// part < 1024/EP, owns a contiguous run of the chunks of expert e. It loads its run in
+// batches of SCAN_BATCH independent loads (kept in registers when the run fits one batch),
+// sums them; totals -> counts and offsets (exclusive scan over e); then each thread writes
+// the running row base of its chunks.
+constexpr int SCAN_BATCH = 64;
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ partial,
                                                              int nchunks, int E,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ chunk_base) {
-  __shared__ int psum[4][256];
+  __shared__ int psum[1024];
   __shared__ int s[256];
-  const int e = threadIdx.x & 255, part = threadIdx.x >> 8;
-  const int L = (nchunks + 3) / 4;
+  const int EP = E <= 64 ? 64 : (E <= 128 ? 128 : 256);
+  const int P = 1024 / EP;
+  const int e = threadIdx.x % EP, part = threadIdx.x / EP;
+  const int L = (nchunks + P - 1) / P;
   const int c0 = part * L, c1 = min(nchunks, c0 + L);
+  int v[SCAN_BATCH];
   int sum = 0;
-  if (e < E)
-    for (int c = c0; c < c1; ++c) sum += partial[(size_t)c * E + e];
-  psum[part][e] = sum;
+  if (e < E) {
+    for (int b = c0; b < c1; b += SCAN_BATCH) {
+#pragma unroll
+      for (int i = 0; i < SCAN_BATCH; ++i) v[i] = b + i < c1 ? partial[(size_t)(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < SCAN_BATCH; ++i) sum += v[i];
+    }
+  }
+  psum[threadIdx.x] = sum;
   __syncthreads();
-  const int tot = psum[0][e] + psum[1][e] + psum[2][e] + psum[3][e];
-  if (part == 0) s[e] = tot;
+  int tot = 0, before = 0;
+  for (int q = 0; q < P; ++q) {
+    const int x = psum[q * EP + e];
+    tot += x;
+    if (q < part) before += x;
+  }
+  if (part == 0) s[e] = e < E ? tot : 0;
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scan over the 256 totals
+  for (int o = 1; o < EP; o <<= 1) {  // inclusive Hillis-Steele scan over the totals
     const int add = (part == 0 && e >= o) ? s[e - o] : 0;
     __syncthreads();
     if (part == 0) s[e] += add;
@@ -82,13 +99,21 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
     offsets[e] = excl;
     if (counts) counts[e] = tot;
   }
-  if (threadIdx.x == 255) offsets[E] = s[255];
+  if (threadIdx.x == EP - 1) offsets[E] = s[EP - 1];
   if (e < E) {
-    int run = excl;
-    for (int q = 0; q < part; ++q) run += psum[q][e];
-    for (int c = c0; c < c1; ++c) {
-      chunk_base[(size_t)c * E + e] = run;
-      run += partial[(size_t)c * E + e];
+    int run = excl + before;
+    if (c1 - c0 <= SCAN_BATCH) {  // the run is still in registers
+#pragma unroll
+      for (int i = 0; i < SCAN_BATCH; ++i)
+        if (c0 + i < c1) {
+          chunk_base[(size_t)(c0 + i) * E + e] = run;
+          run += v[i];
+        }
+    } else {
+      for (int c = c0; c < c1; ++c) {
+        chunk_base[(size_t)c * E + e] = run;
+        run += partial[(size_t)c * E + e];
+      }
     }
   }
 }

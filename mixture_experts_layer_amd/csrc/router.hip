@@ -125,11 +125,147 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   }
 }
 
+// Router for k <= 16: one token per 16-lane row (four tokens per wave), each lane holding
+// the logits of experts r, r+16, ... (EPR of them). A round's arg-max is a local pass over
+// the lane's untaken experts and four DPP row rotations (8, 4, 2, 1 lanes) combining
+// (value, id) pairs under "larger value, then lower id" -- a total order, so every lane of
+// the row ends with the same winner. Blocks of 512 threads take 32 tokens per step. HIST as
+// in router_topk_kernel (tokens_per_block tokens per block, a multiple of 32).
+MOE_DEV int dpp_ror(int v, int ctrl_sel) {
+  switch (ctrl_sel) {  // row_ror:N is DPP control 0x120 + N
+    case 8: return __builtin_amdgcn_update_dpp(v, v, 0x128, 0xf, 0xf, false);
+    case 4: return __builtin_amdgcn_update_dpp(v, v, 0x124, 0xf, 0xf, false);
+    case 2: return __builtin_amdgcn_update_dpp(v, v, 0x122, 0xf, 0xf, false);
+    default: return __builtin_amdgcn_update_dpp(v, v, 0x121, 0xf, 0xf, false);
+  }
+}
+
+template <int EPR, bool HIST>  // experts per lane: ceil(E / 16)
+__global__ __launch_bounds__(512) void router_row_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int score, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_prob, int32_t* __restrict__ counts, uint8_t* __restrict__ routing_map,
+    float* __restrict__ probs_dense, int tokens_per_block) {
+  __shared__ int hist[256];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int r = threadIdx.x & 15;            // lane within the token's row
+  const int row = threadIdx.x >> 4;          // 32 rows per block
+  int t_begin, t_end, t_step;
+  if (HIST) {
+    t_begin = blockIdx.x * tokens_per_block;
+    t_end = min(T, t_begin + tokens_per_block);
+    t_step = 32;
+  } else {
+    t_begin = blockIdx.x * 32;
+    t_end = T;
+    t_step = gridDim.x * 32;
+  }
+  for (int t0 = t_begin; t0 < t_end; t0 += t_step) {
+    const int t = t0 + row;
+    const bool live = t < t_end;
+    const float* lrow = logits + (size_t)(live ? t : t0) * E;
+    float v[EPR];
+    int avail = 0;  // bit i: expert r + 16 i exists and is not taken
+#pragma unroll
+    for (int i = 0; i < EPR; ++i) {
+      const int e = r + 16 * i;
+      v[i] = e < E ? lrow[e] : 0.f;
+      if (e < E) avail |= 1 << i;
+    }
+    int my_e = 0;
+    float my_v = 0.f, top_v = 0.f;
+    for (int j = 0; j < k; ++j) {
+      // branch-free: a lane with no candidate holds (-inf, INT_MAX), which every finite
+      // logit beats and which keeps ties among empty lanes harmless
+      float bv = -__builtin_inff();
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < EPR; ++i) {  // ascending id: strict > keeps the lower id on a tie
+        const bool take = ((avail >> i) & 1) & (v[i] > bv);
+        bv = take ? v[i] : bv;
+        be = take ? r + 16 * i : be;
+      }
+#pragma unroll
+      for (int sh = 8; sh > 0; sh >>= 1) {
+        const float ov = __int_as_float(dpp_ror(__float_as_int(bv), sh));
+        const int oe = dpp_ror(be, sh);
+        const bool other = (ov > bv) | ((ov == bv) & (oe < be));
+        bv = other ? ov : bv;
+        be = other ? oe : be;
+      }
+      if (j == 0) top_v = bv;
+      if (r == j) {
+        my_e = be;
+        my_v = bv;
+      }
+      if ((be & 15) == r) avail &= ~(1 << (be >> 4));
+    }
+    float q;
+    if (score == MOE_SIGMOID) {
+      q = 1.0f / (1.0f + expf(-my_v));
+    } else {
+      const float z = r < k ? expf(my_v - top_v) : 0.f;  // the best logit is the first choice
+      float sum = z;
+#pragma unroll
+      for (int sh = 8; sh > 0; sh >>= 1) sum += __int_as_float(dpp_ror(__float_as_int(sum), sh));
+      q = z / sum;
+    }
+    if (live) {
+      if (r < k) {
+        topk_idx[(size_t)t * k + r] = my_e;
+        topk_prob[(size_t)t * k + r] = q;
+        atomicAdd(&hist[my_e], 1);
+      }
+      if (routing_map || probs_dense) {
+#pragma unroll
+        for (int i = 0; i < EPR; ++i) {
+          const int e = r + 16 * i;
+          if (e < E) {
+            const bool taken = !(avail >> i & 1);
+            if (routing_map) routing_map[(size_t)t * E + e] = taken ? 1 : 0;
+            if (probs_dense && !taken) probs_dense[(size_t)t * E + e] = 0.f;
+          }
+        }
+      }
+    }
+    // kept experts were not zeroed above, so no ordering is needed
+    if (live && probs_dense && r < k) probs_dense[(size_t)t * E + my_e] = q;
+  }
+  __syncthreads();
+  if (HIST) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) counts[(size_t)blockIdx.x * E + e] = hist[e];
+  } else {
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+      if (hist[e]) atomicAdd(&counts[e], hist[e]);
+  }
+}
+
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int score,
                               int32_t* topk_idx, float* topk_prob, int32_t* counts,
                               uint8_t* routing_map, float* probs_dense, hipStream_t s) {
   hipError_t err = launch_fill_i32(counts, E, 0, s);
   if (err != hipSuccess || T == 0) return err;
+  if (k <= 16) {
+    int blocks = (T + 31) / 32;
+    if (blocks > 2048) blocks = 2048;
+    const int epr = (E + 15) / 16;
+#define MOE_ROUTER_ROW(n)                                                                       \
+  case n:                                                                                       \
+    router_row_kernel<n, false><<<blocks, 512, 0, s>>>(logits, T, E, k, score, topk_idx,         \
+                                                       topk_prob, counts, routing_map,           \
+                                                       probs_dense, 0);                          \
+    break;
+    switch ((epr + 3) / 4 * 4) {
+      MOE_ROUTER_ROW(4)
+      MOE_ROUTER_ROW(8)
+      MOE_ROUTER_ROW(12)
+      MOE_ROUTER_ROW(16)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef MOE_ROUTER_ROW
+    return hipGetLastError();
+  }
   int blocks = (T + 3) / 4;
   if (blocks > 2048) blocks = 2048;
   int epl = (E + 63) / 64;
@@ -156,6 +292,25 @@ hipError_t launch_router_hist(const float* logits, int T, int E, int k, int scor
                               int chunk_tokens, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int blocks = (T + chunk_tokens - 1) / chunk_tokens;
+  if (k <= 16 && chunk_tokens % 32 == 0) {
+    const int epr = (E + 15) / 16;
+#define MOE_ROUTER_ROW(n)                                                                       \
+  case n:                                                                                       \
+    router_row_kernel<n, true><<<blocks, 512, 0, s>>>(logits, T, E, k, score, topk_idx,          \
+                                                      topk_prob, partial, nullptr, nullptr,      \
+                                                      chunk_tokens);                             \
+    break;
+    switch ((epr + 3) / 4 * 4) {
+      MOE_ROUTER_ROW(4)
+      MOE_ROUTER_ROW(8)
+      MOE_ROUTER_ROW(12)
+      MOE_ROUTER_ROW(16)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef MOE_ROUTER_ROW
+    return hipGetLastError();
+  }
   int epl = (E + 63) / 64;
 #define MOE_ROUTER_CASE(n)                                                                     \
   case n:                                                                                      \

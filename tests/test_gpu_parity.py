@@ -47,7 +47,8 @@ def test_router_full_size(name):
 
 def test_router_ties_and_k_limits():
     rng = np.random.default_rng(0)
-    for (T, E, k, score) in [(100, 32, 32, 0), (77, 256, 8, 1), (5, 3, 3, 2), (64, 200, 17, 0)]:
+    for (T, E, k, score) in [(100, 32, 32, 0), (77, 256, 8, 1), (5, 3, 3, 2), (64, 200, 17, 0),
+                             (50, 64, 16, 0), (33, 16, 1, 2), (19, 129, 16, 1)]:
         l = rng.integers(-3, 3, (T, E)).astype(np.float32)   # many exact ties
         ti = torch.empty((T, k), dtype=torch.int32, device="cuda")
         tp = torch.empty((T, k), dtype=torch.float32, device="cuda")
