@@ -263,7 +263,11 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   // epilogue wave 0 publishes the ticket requested one tile earlier (so the atomic's
   // latency is never waited for) and requests the next.
   // Weight gradients (equal tiles): a fixed stride through the XCD's eighth.
+#ifdef MOE_GEMM_STATIC_SCHED
+  constexpr bool DYN = false;
+#else
   constexpr bool DYN = !DW;
+#endif
   const int nx = (gridDim.x & 7) == 0 ? 8 : 1;
   const int xcd = nx == 8 ? (int)(blockIdx.x & 7) : 0;
   int r_start, r_end;
@@ -284,20 +288,28 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       s_tk[0] = t0;
       s_tk[1] = t0 + 1;
       s_tk[2] = t0 + 2;
+#pragma unroll
+      for (int i = 3; i < 8; ++i) s_tk[i] = 0x40000000;  // never a tile
     }
     __syncthreads();
     n_pub = 3;
-    sched_open = s_tk[2] + r_start < r_end;
+    // tickets past the first 3 BX map to themselves: more grabs pay off while they can
+    // still land inside the range
+    sched_open = 3 * ((int)gridDim.x / nx) < r_end - r_start;
   }
-  auto tile_of = [&](int j) __attribute__((always_inline)) -> int {  // DYN: j < n_pub
+  // The sequence ends at the first index without a tile; past the published tickets there
+  // is none (a block whose last published ticket is valid stops there).
+  auto tile_of = [&](int j) __attribute__((always_inline)) -> int {
     int t;
     if constexpr (DYN) {
+      if (j >= n_pub) return -1;
       // The first 3*BX tickets of an XCD (three per block, taken at start) are spread so
-      // that blocks start on consecutive tiles: ticket 3i+k -> tile i + BX*k. Later tickets
-      // map to themselves.
+      // that blocks start on consecutive tiles, and a range shorter than 3 BX still gives
+      // every block its share: ticket 3i+k -> tile i + BX*k. Later tickets map to
+      // themselves.
       const int BX = (int)gridDim.x / nx;
       t = s_tk[j & 7];
-      if (t < 3 * BX && r_end - r_start >= 3 * BX) t = t / 3 + BX * (t % 3);
+      if (t < 3 * BX) t = t / 3 + BX * (t % 3);  // a bijection of [0, 3 BX)
       t += r_start;
       t = t < r_end ? t : -1;
     } else {
@@ -926,7 +938,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       if (pend_tk) ++n_pub;
       pend_tk = sched_open ? 1 : 0;
       ring_barrier();
-      if (sched_open) sched_open = s_tk[(n_pub - 1) & 7] + r_start < r_end;
+      if (sched_open) sched_open = s_tk[(n_pub - 1) & 7] + 1 < r_end - r_start;
       if (l_state == L_BLOCKED) cursor_advance();
     }
   }
@@ -948,10 +960,9 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
 namespace {
 
 // Resident blocks of one kernel on the current device (compute units x blocks per CU),
-// queried once per device and instantiation.
+// queried once per device and kernel: `cache` belongs to the caller's instantiation.
 template <typename K>
-int persistent_blocks(K kern, int threads) {
-  static int cache[64];
+int persistent_blocks(K kern, int threads, int (&cache)[64]) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   if (cache[dev] == 0) {
@@ -982,9 +993,14 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   const long long row_bytes = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD) ? 4LL * p.I
                                                                           : (long long)p.N * (p.c_fp32 ? 4 : 2);
   if ((long long)BM * row_bytes >= kOutOfRange) return hipErrorInvalidValue;
-  const int resident = persistent_blocks(kern, C::NT);
+  static int resident_cache[64];  // one per instantiation of launch_cfg
+  const int resident = persistent_blocks(kern, C::NT, resident_cache);
   if (resident <= 0) return hipErrorInvalidValue;
+#ifdef MOE_GEMM_ONE_TILE_PER_BLOCK
+  long long grid = tiles;
+#else
   long long grid = tiles < resident ? tiles : resident;
+#endif
   if (g_max_blocks > 0 && grid > g_max_blocks) grid = g_max_blocks;
   GemmParams q = p;
   q.sched_slot = (int)(g_launch_seq.fetch_add(1, std::memory_order_relaxed) % kSchedSlots);
