@@ -263,11 +263,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   // epilogue wave 0 publishes the ticket requested one tile earlier (so the atomic's
   // latency is never waited for) and requests the next.
   // Weight gradients (equal tiles): a fixed stride through the XCD's eighth.
-#ifdef MOE_GEMM_STATIC_SCHED
-  constexpr bool DYN = false;
-#else
   constexpr bool DYN = !DW;
-#endif
   const int nx = (gridDim.x & 7) == 0 ? 8 : 1;
   const int xcd = nx == 8 ? (int)(blockIdx.x & 7) : 0;
   int r_start, r_end;
@@ -996,11 +992,7 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   static int resident_cache[64];  // one per instantiation of launch_cfg
   const int resident = persistent_blocks(kern, C::NT, resident_cache);
   if (resident <= 0) return hipErrorInvalidValue;
-#ifdef MOE_GEMM_ONE_TILE_PER_BLOCK
-  long long grid = tiles;
-#else
   long long grid = tiles < resident ? tiles : resident;
-#endif
   if (g_max_blocks > 0 && grid > g_max_blocks) grid = g_max_blocks;
   GemmParams q = p;
   q.sched_slot = (int)(g_launch_seq.fetch_add(1, std::memory_order_relaxed) % kSchedSlots);
