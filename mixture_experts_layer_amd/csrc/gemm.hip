@@ -259,9 +259,9 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   // out round-robin over the 8 XCDs, so XCD x serves the x-th eighth of the tile range and
   // neighbours that share weight panels run at the same time on one XCD (one L2).
   // NN/NT (ragged rows, uneven tile costs): each XCD's blocks take tickets from its own
-  // counter as they free up. A block holds three tickets at start; at the end of each
-  // epilogue wave 0 publishes the ticket requested one tile earlier (so the atomic's
-  // latency is never waited for) and requests the next.
+  // counter as they free up. A block holds three tickets at start (from its index); at the
+  // end of each epilogue wave 0 publishes the ticket requested one tile earlier (so the
+  // atomic's latency is never waited for) and requests the next.
   // Weight gradients (equal tiles): a fixed stride through the XCD's eighth.
   constexpr bool DYN = !DW;
   const int nx = (gridDim.x & 7) == 0 ? 8 : 1;
@@ -279,8 +279,11 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   int pend_tk = 0;            // wave 0 holds a requested, unpublished ticket
   int tk = 0;                 // wave 0, lane 0: that ticket
   if constexpr (DYN) {
+    // The three starting tickets follow the block index (blocks are spread over the CUs in
+    // index order, so the first tiles are too); later tickets come from the counter, past
+    // the 3 BX starting ones.
     if (tid == 0) {
-      const int t0 = atomicAdd(ctr, 3);
+      const int t0 = 3 * (int)(blockIdx.x / nx);
       s_tk[0] = t0;
       s_tk[1] = t0 + 1;
       s_tk[2] = t0 + 2;
@@ -371,17 +374,13 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
     return DW ? (t.kcount + KR - 1) / KR : nk_fixed;
   };
   // NN/NT: a_src/b_src point at the cursor's next stage and advance by a_inc/b_inc per
-  // stage (0 for lanes that read the zero block). A chunks wholly past the tile's last row
-  // (tail tiles) are issued by one lane only: the instruction still counts towards vmcnt,
-  // but the dead rows cost no bandwidth. DW: base pointers plus the stage index.
+  // stage (0 for lanes that read the zero block). DW: base pointers plus the stage index.
   const uint8_t* a_src[C::A_LOADS];
   const uint8_t* b_src[C::B_LOADS];
   uint32_t a_inc[C::A_LOADS], b_inc[C::B_LOADS];
   int a_krow[C::A_LOADS], b_krow[C::B_LOADS];  // DW: k row of the chunk lane (zero past kcount)
-  int a_dead = 0;                              // NN/NT: bit i set: A chunk i holds no valid row
   auto setup_loads = [&](const Tile& t) __attribute__((always_inline)) {
     if constexpr (!DW) {
-      a_dead = 0;
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i) {
         const int chunk = wave + C::NW * i;
@@ -390,10 +389,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
         a_src[i] = ok ? (const uint8_t*)p.A + (size_t)(t.m0 + row) * lda + kc_logical<BKB>(row, lane) * 16
                       : zero;
         a_inc[i] = ok ? (uint32_t)a_step : 0u;
-        if (chunk * (1024 / BKB) >= t.rows_valid) a_dead |= 1 << i;
         a_krow[i] = 0;
       }
-      a_dead = __builtin_amdgcn_readfirstlane(a_dead);
       if constexpr (!B_MN) {  // NT: B_g is [N, K]
         const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.N * lda;
 #pragma unroll
@@ -496,11 +493,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       if constexpr (DW) {
         load_lds16((lk * KR + a_krow[i] < lt.kcount) ? a_src[i] + (size_t)lk * a_step : zero, dst);
       } else {
-        if (a_dead & (1 << i)) {
-          if (lane == 0) load_lds16(zero, dst);
-        } else {
-          load_lds16(a_src[i], dst);
-        }
+        load_lds16(a_src[i], dst);
         a_src[i] += a_inc[i];
       }
     } else {
@@ -927,7 +920,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
         wait_vmcnt<0>();
         if (lane == 0) {
           if (pend_tk) s_tk[n_pub & 7] = tk;
-          if (sched_open) tk = atomicAdd(ctr, 1);
+          if (sched_open) tk = 3 * ((int)gridDim.x / nx) + atomicAdd(ctr, 1);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the ticket is in LDS before the barrier
       }
