@@ -30,10 +30,12 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def stage_costs(w, training):
+def stage_costs(w, training, active=None):
     """Algorithmic FLOPs and HBM bytes of each GEMM launch (read every input once,
-    write every output once)."""
-    N, H, I, E = w.T * w.k, w.H, w.I, w.E
+    write every output once). Weights are counted for the `active` experts (those that
+    received rows; all E by default): an expert with no rows has no tiles."""
+    N, H, I = w.T * w.k, w.H, w.I
+    E = w.E if active is None else active
     act = 1 if w.fp8 else 2
     c = {
         "gemm1_swiglu": (2.0 * N * H * 2 * I,
@@ -306,7 +308,8 @@ def main():
     torch.cuda.synchronize()
     _log("bench: per-launch us " + json.dumps({k_: round(v_, 2) for k_, v_ in kernel_us.items()}))
 
-    costs = stage_costs(w, training)
+    active = int((counts > 0).sum().item())  # experts that received rows in this step
+    costs = stage_costs(w, training, active)
     peak_tf = MFMA_PEAK_TFLOPS["fp8" if w.fp8 else "bf16"]
     gemm = {}
     for name, (fl, by) in costs.items():
@@ -375,7 +378,7 @@ def main():
         "config": {"workload": f"{w.name}-shaped MoE block " + ("forward+backward" if training else "forward"),
                    "T": w.T, "H": w.H, "E": w.E, "top_k": w.k, "I": w.I, "shared_I": w.shared_I,
                    "score": ["softmax_pre_renorm", "softmax_post", "sigmoid"][w.score],
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "active_experts": active},
         "grouped_gemm_tflops": round(gemm_flops / gemm_time / 1e12, 1),
         "grouped_gemm_mfma_frac": round(gemm_flops / gemm_time / 1e12 / peak_tf, 4),
         "gemm": gemm,
