@@ -27,7 +27,8 @@
  *    fails. T == 0 is a valid no-op. Out-of-range expert ids in topk_idx are the
  *    caller's error and are not checked on the device.
  *  - Supported sizes: 1 <= k <= min(E, 32), E <= 256, H % 64 == 0, I % 64 == 0,
- *    every pointer 16-byte aligned.
+ *    one expert's weight matrix under 4 GiB (and 512 rows of the GEMM's activation
+ *    operand under 4 GiB), every pointer 16-byte aligned.
  */
 #ifndef MOE_AMD_H
 #define MOE_AMD_H

@@ -12,7 +12,7 @@
 //    with unit scales for e4m3). A wave's M blocks are interleaved (wave wm takes
 //    blocks wm, wm+WM, ...) so the blocks past a group's last row, which are skipped,
 //    are spread over the waves.
-//  * K advances 128 bytes per stage (64 bf16 or 128 e4m3). Operands go from global
+//  * K advances 64 or 128 bytes per stage (32/64 bf16, 128 e4m3). Operands go from global
 //    memory straight into an LDS ring of STAGES buffers with 16-byte
 //    global_load_lds (no staging registers, no VALU copies); the loads for stage
 //    kt+STAGES-1 are in flight while stage kt is multiplied.
@@ -23,8 +23,9 @@
 //    k%4, read with ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one
 //    column (two reads form the 8-element MFMA operand). The swizzles are applied on
 //    the global side because global_load_lds places lane l's 16 bytes at base + 16*l.
-//  * Rows past a group's end and columns past N load from a zero block; the weight
-//    gradient's ragged reduction is zero-padded the same way.
+//  * Rows past a group's end and columns past N load the tile's first row or column:
+//    they only feed outputs that are never stored. The weight gradient's ragged
+//    reduction is zero-padded from a zero block.
 //  * Epilogue through LDS: accumulators (converted, or consumed by SwiGLU / SwiGLU
 //    backward) are staged row-major and written with 16-byte stores.
 //  * Tile schedule on the device: every block rebuilds the prefix of per-group M-tile
@@ -84,6 +85,12 @@ MOE_DEV void load_lds16(const void* g, uint8_t* lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
 }
 
+// The same from a wave-uniform base (SGPR pair) plus a 32-bit per-lane byte offset.
+MOE_DEV void load_lds16_s(const void* base, uint32_t off, uint8_t* lds) {
+  const unsigned m0 = (unsigned)(uintptr_t)((lds_u8_t*)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, int BKB_>
 struct Cfg {
   static constexpr int BKB = BKB_;      // K bytes per stage: 64 or 128
@@ -92,10 +99,13 @@ struct Cfg {
   static constexpr int NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int MB = TM / 32, NB = TN / 32;
-  static constexpr int A_BYTES = BM * BKB, B_BYTES = BN * BKB;
+  // A chunk-loads per wave: a whole number, so with BM * BKB not a multiple of NW KB the
+  // last rows of the A area are loaded (from the tile's first row) and never read
+  static constexpr int A_LOADS = (BM * BKB / 1024 + NW - 1) / NW;
+  static constexpr int A_BYTES = A_LOADS * NW * 1024, B_BYTES = BN * BKB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int SMEM = STAGE * STAGES;
-  static constexpr int A_LOADS = A_BYTES / 1024 / NW, B_LOADS = B_BYTES / 1024 / NW;  // per wave
+  static constexpr int B_LOADS = B_BYTES / 1024 / NW;  // per wave
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static_assert(BKB == 64 || BKB == 128, "stage depth");
   static_assert(MB >= 1 && NB >= 1, "wave tile");
@@ -332,9 +342,12 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       const int local = tile - s_pref[g] * ntn;
       const int ntile = local / mt, mtile = local % mt;
       const int gbeg = s_off[g], cnt = s_off[g + 1] - gbeg;
+      // the group's rows are spread evenly over its M tiles (in 32-row steps), so a group a
+      // little over BM rows takes two part tiles rather than a full one and a sliver
+      const int per = ((cnt + mt - 1) / mt + 31) & ~31;
       t.g = g;
-      t.m0 = gbeg + mtile * BM;
-      t.rows_valid = min(BM, cnt - mtile * BM);
+      t.m0 = gbeg + mtile * per;
+      t.rows_valid = min(per, cnt - mtile * per);
       t.n0 = ntile * (EPI == EPI_SWIGLU ? HB : BN);
       t.kcount = p.K;
       t.kbase = 0;
@@ -361,6 +374,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   const int esz = FP8 ? 1 : 2;
   const uint8_t* zero = g_zero_block;
   const size_t lda = (size_t)p.K * esz;
+  const uint32_t lda32 = (uint32_t)lda;
   const int nk_fixed = DW ? 0 : (int)(lda / BKB);
   size_t a_step, b_step;  // bytes per stage
   if constexpr (!DW) {
@@ -373,11 +387,14 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   auto stages_of = [&](const Tile& t) __attribute__((always_inline)) {
     return DW ? (t.kcount + KR - 1) / KR : nk_fixed;
   };
-  // NN/NT: a_src/b_src point at the cursor's next stage and advance by a_inc/b_inc per
-  // stage (0 for lanes that read the zero block). DW: base pointers plus the stage index.
-  const uint8_t* a_src[C::A_LOADS];
-  const uint8_t* b_src[C::B_LOADS];
-  uint32_t a_inc[C::A_LOADS], b_inc[C::B_LOADS];
+  // NN/NT: a wave-uniform base per operand (stage lk at base + lk * step) and a 32-bit byte
+  // offset per lane and chunk-load (the host keeps one expert's operands under 4 GiB).
+  // DW: full pointers plus the stage index.
+  const uint8_t* a_base = nullptr;
+  const uint8_t* b_base = nullptr;
+  uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
+  const uint8_t* a_src[DW ? C::A_LOADS : 1];
+  const uint8_t* b_src[DW ? C::B_LOADS : 1];
   int a_krow[C::A_LOADS], b_krow[C::B_LOADS];  // DW: k row of the chunk lane (zero past kcount)
   auto setup_loads = [&](const Tile& t) __attribute__((always_inline)) {
     if constexpr (!DW) {
@@ -386,13 +403,15 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
         const int chunk = wave + C::NW * i;
         const int row = kc_row<BKB>(chunk, lane);
         const bool ok = row < t.rows_valid;
-        a_src[i] = ok ? (const uint8_t*)p.A + (size_t)(t.m0 + row) * lda + kc_logical<BKB>(row, lane) * 16
-                      : zero;
-        a_inc[i] = ok ? (uint32_t)a_step : 0u;
+        // rows past the group's end read the tile's first row: they only feed output rows
+        // that are never stored
+        a_off[i] = (uint32_t)(ok ? row : 0) * lda32 + kc_logical<BKB>(row, lane) * 16;
         a_krow[i] = 0;
       }
+      a_base = (const uint8_t*)p.A + (size_t)t.m0 * lda;
       if constexpr (!B_MN) {  // NT: B_g is [N, K]
         const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.N * lda;
+        b_base = bg;
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i) {
           const int chunk = wave + C::NW * i;
@@ -407,12 +426,13 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
             col = t.n0 + row;
             ok = col < p.N;
           }
-          b_src[i] = ok ? bg + (size_t)col * lda + kc_logical<BKB>(row, lane) * 16 : zero;
-          b_inc[i] = ok ? (uint32_t)b_step : 0u;
+          // columns past the end read the tile's first column (outputs never stored)
+          b_off[i] = (uint32_t)(ok ? col : t.n0) * lda32 + kc_logical<BKB>(row, lane) * 16;
           b_krow[i] = 0;
         }
       } else {  // NN: B_g is [K, N]
         const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.K * p.N * 2;
+        b_base = bg;
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i) {
           const int chunk = wave + C::NW * i;
@@ -429,8 +449,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
             col = t.n0 + c;
             ok = col < p.N;
           }
-          b_src[i] = ok ? bg + ((size_t)k * p.N + col) * 2 : zero;
-          b_inc[i] = ok ? (uint32_t)b_step : 0u;
+          b_off[i] = ((uint32_t)k * p.N + (ok ? col : t.n0)) * 2u;
           b_krow[i] = 0;
         }
       }
@@ -493,8 +512,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       if constexpr (DW) {
         load_lds16((lk * KR + a_krow[i] < lt.kcount) ? a_src[i] + (size_t)lk * a_step : zero, dst);
       } else {
-        load_lds16(a_src[i], dst);
-        a_src[i] += a_inc[i];
+        load_lds16_s(a_base + (size_t)lk * a_step, a_off[i], dst);
       }
     } else {
       const int j = i - C::A_LOADS;
@@ -502,8 +520,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       if constexpr (DW) {
         load_lds16((lk * KR + b_krow[j] < lt.kcount) ? b_src[j] + (size_t)lk * b_step : zero, dst);
       } else {
-        load_lds16(b_src[j], dst);
-        b_src[j] += b_inc[j];
+        load_lds16_s(b_base + (size_t)lk * b_step, b_off[j], dst);
       }
     }
   };
@@ -533,77 +550,100 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   auto kc_frag = [&](const uint8_t* base, int row, int chunk) __attribute__((always_inline)) -> u32x4_t {
     return *(const u32x4_t*)(base + row * BKB + ((chunk ^ kc_swz<BKB>(row)) << 4));
   };
+  using frag_t = typename std::conditional<FP8, i32x8_t, bf16x8_t>::type;
+  // A fragment of M block i of this wave, k sub-step ks.
+  auto load_a = [&](const uint8_t* sa, int ks, int i) __attribute__((always_inline)) -> frag_t {
+    const int r0 = (wm + WM * i) * 32;
+    if constexpr (FP8) {
+      const u32x4_t x0 = kc_frag(sa, r0 + l32, ks * 4 + khalf * 2);
+      const u32x4_t x1 = kc_frag(sa, r0 + l32, ks * 4 + khalf * 2 + 1);
+      return i32x8_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                     (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    } else if constexpr (!DW) {
+      return __builtin_bit_cast(bf16x8_t, kc_frag(sa, r0 + l32, ks * 2 + khalf));
+    } else {
+      const int k = ks * 16 + tr_k;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(sa + mn_offset<BM>(k, r0 + tr_c)));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(sa + mn_offset<BM>(k + 4, r0 + tr_c)));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  // B fragments of this wave's N blocks, k sub-step ks.
+  auto load_b = [&](const uint8_t* sa, int ks, frag_t* bfr) __attribute__((always_inline)) {
+    const uint8_t* sb = sa + C::A_BYTES;
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j) {
+      const int c0 = bcol0(j);
+      if constexpr (FP8) {
+        const u32x4_t x0 = kc_frag(sb, c0 + l32, ks * 4 + khalf * 2);
+        const u32x4_t x1 = kc_frag(sb, c0 + l32, ks * 4 + khalf * 2 + 1);
+        bfr[j] = i32x8_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                         (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      } else if constexpr (!B_MN) {
+        bfr[j] = __builtin_bit_cast(bf16x8_t, kc_frag(sb, c0 + l32, ks * 2 + khalf));
+      } else {
+        const int k = ks * 16 + tr_k;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(sb + mn_offset<BN>(k, c0 + tr_c)));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(sb + mn_offset<BN>(k + 4, c0 + tr_c)));
+        bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+  };
   // Fragment loads of k sub-step ks into registers.
   auto load_frags = [&](auto MBL_c, const uint8_t* sa, int ks, auto& af, auto& bfr) __attribute__((always_inline)) {
     constexpr int MBL = decltype(MBL_c)::value;
-    const uint8_t* sb = sa + C::A_BYTES;
-    if constexpr (!FP8) {
 #pragma unroll
-      for (int i = 0; i < MBL; ++i) {
-        const int r0 = (wm + WM * i) * 32;
-        if constexpr (!DW) {
-          af[i] = __builtin_bit_cast(bf16x8_t, kc_frag(sa, r0 + l32, ks * 2 + khalf));
-        } else {
-          const int k = ks * 16 + tr_k;
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t*)(sa + mn_offset<BM>(k, r0 + tr_c)));
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t*)(sa + mn_offset<BM>(k + 4, r0 + tr_c)));
-          af[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < C::NB; ++j) {
-        const int c0 = bcol0(j);
-        if constexpr (!B_MN) {
-          bfr[j] = __builtin_bit_cast(bf16x8_t, kc_frag(sb, c0 + l32, ks * 2 + khalf));
-        } else {
-          const int k = ks * 16 + tr_k;
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t*)(sb + mn_offset<BN>(k, c0 + tr_c)));
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t*)(sb + mn_offset<BN>(k + 4, c0 + tr_c)));
-          bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < MBL; ++i) {
-        const int r = (wm + WM * i) * 32 + l32;
-        const u32x4_t x0 = kc_frag(sa, r, ks * 4 + khalf * 2);
-        const u32x4_t x1 = kc_frag(sa, r, ks * 4 + khalf * 2 + 1);
-        af[i] = i32x8_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                        (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-      }
-#pragma unroll
-      for (int j = 0; j < C::NB; ++j) {
-        const int r = bcol0(j) + l32;
-        const u32x4_t x0 = kc_frag(sb, r, ks * 4 + khalf * 2);
-        const u32x4_t x1 = kc_frag(sb, r, ks * 4 + khalf * 2 + 1);
-        bfr[j] = i32x8_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                         (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-      }
-    }
+    for (int i = 0; i < MBL; ++i) af[i] = load_a(sa, ks, i);
+    load_b(sa, ks, bfr);
+  };
+  auto mfma1 = [&](int i, int j, const frag_t& a, const frag_t& b) __attribute__((always_inline)) {
+    if constexpr (!FP8)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc[i][j], 0, 0, 0, 127, 0, 127);
   };
   auto mfmas = [&](auto MBL_c, const auto& af, const auto& bfr) __attribute__((always_inline)) {
     constexpr int MBL = decltype(MBL_c)::value;
 #pragma unroll
     for (int i = 0; i < MBL; ++i)
 #pragma unroll
-      for (int j = 0; j < C::NB; ++j) {
-        if constexpr (!FP8)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j],
-                                                                       0, 0, 0, 127, 0, 127);
-      }
+      for (int j = 0; j < C::NB; ++j) mfma1(i, j, af[i], bfr[j]);
   };
   // One ring stage: KS k sub-steps; while sub-step ks multiplies, the fragments of ks+1
   // are read and a slice of the cursor's next stage (into `nxt`) is issued.
+  // Five M blocks per wave leave no room for a whole sub-step of A fragments in flight:
+  // there A fragments are read one M block ahead of the multiply instead.
+  constexpr bool APIPE = C::MB >= 5;
   auto compute_stage = [&](auto MBL_c, const uint8_t* sa, bool iss, uint8_t* nxt) __attribute__((always_inline)) {
     constexpr int KS = FP8 ? BKB / 64 : BKB / 32;
     constexpr int PER = (C::LOADS + KS - 1) / KS;
-    using frag_t = typename std::conditional<FP8, i32x8_t, bf16x8_t>::type;
+    if constexpr (APIPE) {
+      constexpr int MBL = decltype(MBL_c)::value;
+      frag_t af[2], bfr[2][C::NB];
+      load_b(sa, 0, bfr[0]);
+      if constexpr (MBL > 0) af[0] = load_a(sa, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) load_b(sa, ks + 1, bfr[(ks + 1) & 1]);
+        if (iss) {
+#pragma unroll
+          for (int q = ks * PER; q < (ks + 1) * PER && q < C::LOADS; ++q) issue_one(nxt, q);
+        }
+#pragma unroll
+        for (int i = 0; i < MBL; ++i) {
+          const int f = ks * MBL + i;  // fragment f sits in af[f & 1]
+          if (i + 1 < MBL) af[(f + 1) & 1] = load_a(sa, ks, i + 1);
+          else if (ks + 1 < KS) af[(f + 1) & 1] = load_a(sa, ks + 1, 0);
+#pragma unroll
+          for (int j = 0; j < C::NB; ++j) mfma1(i, j, af[f & 1], bfr[ks & 1][j]);
+        }
+      }
+      return;
+    }
     frag_t af[2][C::MB], bfr[2][C::NB];
     load_frags(MBL_c, sa, 0, af[0], bfr[0]);
 #pragma unroll
@@ -875,7 +915,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       ++gs;
     }
   };
-  static_assert(C::MB <= 4, "live-block dispatch below covers up to four M blocks per wave");
+  static_assert(C::MB <= 5, "live-block dispatch below covers up to five M blocks per wave");
 
   cursor_advance();
   for (;; ++cj) {
@@ -909,7 +949,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       case 1: run_tile(std::integral_constant<int, 1>{}, cnk); break;
       case 2: if constexpr (C::MB >= 2) run_tile(std::integral_constant<int, 2>{}, cnk); break;
       case 3: if constexpr (C::MB >= 3) run_tile(std::integral_constant<int, 3>{}, cnk); break;
-      default: if constexpr (C::MB >= 4) run_tile(std::integral_constant<int, 4>{}, cnk); break;
+      case 4: if constexpr (C::MB >= 4) run_tile(std::integral_constant<int, 4>{}, cnk); break;
+      default: if constexpr (C::MB >= 5) run_tile(std::integral_constant<int, 5>{}, cnk); break;
     }
     epilogue(ct);
     epi2 = epi1;
@@ -1003,10 +1044,13 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 // three-stage ring of 128-byte steps. e4m3: 256x128 tiles with four waves and a three-stage
 // ring of 128-byte steps (its eight-wave build does not fit the register file).
 #ifndef MOE_GEMM_TILE_BF16
-#define MOE_GEMM_TILE_BF16 256, 256, 2, 4, 3, 64
+#define MOE_GEMM_TILE_BF16 320, 256, 2, 4, 3, 64
+#endif
+#ifndef MOE_GEMM_TILE_BF16_DW
+#define MOE_GEMM_TILE_BF16_DW 256, 256, 2, 4, 3, 64
 #endif
 #ifndef MOE_GEMM_TILE_BF16_SWIGLU
-#define MOE_GEMM_TILE_BF16_SWIGLU 256, 256, 4, 2, 3, 64
+#define MOE_GEMM_TILE_BF16_SWIGLU 320, 256, 2, 4, 3, 64
 #endif
 #ifndef MOE_GEMM_TILE_BF16_SWIGLU_BWD
 #define MOE_GEMM_TILE_BF16_SWIGLU_BWD 256, 128, 2, 2, 3, 128
@@ -1034,6 +1078,7 @@ hipError_t launch_sel(const GemmParams& p, hipStream_t s) {
     }
     if constexpr (EPI == EPI_SWIGLU_BWD) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU_BWD>(p, s);
     else if constexpr (EPI == EPI_SWIGLU) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU>(p, s);
+    else if constexpr (MODE == MOE_GEMM_TN_DW) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_DW>(p, s);
     else return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16>(p, s);
   }
 }

@@ -27,6 +27,12 @@ moe_status_t check_shape(int T, int H, int E, int k) {
   return MOE_OK;
 }
 
+// The grouped GEMM addresses one expert's weight matrix (N x K elements of esz bytes) and a
+// tile's rows of the activations with 32-bit offsets.
+bool gemm_offsets_fit(long long N, long long K, int esz) {
+  return N * K * esz < (1LL << 32) && 512LL * K * esz < (1LL << 32);
+}
+
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -79,6 +85,8 @@ moe_status_t check_problem(const moe_problem_t* p) {
   if (st != MOE_OK) return st;
   if (p->I <= 0 || p->shared_I < 0) return MOE_ERR_INVALID_ARG;
   if (p->I % 64 || p->shared_I % 64) return MOE_ERR_UNSUPPORTED;
+  if (!gemm_offsets_fit(2LL * p->I, p->H, 2) || !gemm_offsets_fit(2LL * p->shared_I, p->H, 2))
+    return MOE_ERR_UNSUPPORTED;
   if (p->score < MOE_SOFTMAX_PRE_RENORM || p->score > MOE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   if (p->dtype == MOE_FP8_E4M3) {
@@ -159,6 +167,7 @@ moe_status_t moe_grouped_gemm_swiglu(const void* xp, const float* xp_scale, cons
   if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   const bool fp8 = dtype == MOE_FP8_E4M3;
   if (fp8 && (H % 128)) return MOE_ERR_UNSUPPORTED;
+  if (!gemm_offsets_fit(2LL * I, H, fp8 ? 1 : 2)) return MOE_ERR_UNSUPPORTED;
   if (rows == 0) return MOE_OK;
   if (!ok_ptr(xp) || !ok_ptr(w_gu) || !ok_ptr(offsets) || !ok_ptr(h) || !opt_ptr(gu_saved))
     return MOE_ERR_INVALID_ARG;
@@ -200,6 +209,7 @@ moe_status_t moe_grouped_gemm(int mode, const void* A, const float* a_scale, con
   } else {
     if (K <= 0) return MOE_ERR_INVALID_ARG;
     if (K % (fp8 ? 128 : 64)) return MOE_ERR_UNSUPPORTED;
+    if (!gemm_offsets_fit(N, K, fp8 ? 1 : 2)) return MOE_ERR_UNSUPPORTED;
     if (rows == 0) return MOE_OK;
   }
   if (!ok_ptr(A) || !ok_ptr(B) || !ok_ptr(offsets) || !ok_ptr(C)) return MOE_ERR_INVALID_ARG;
@@ -228,6 +238,7 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const void* d_out, const void* w_down,
                                          int rows, int H, int I, void* dgu, void* stream) {
   if (G <= 0 || rows < 0 || H <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
   if (H % 64 || I % 64 || G > 256) return MOE_ERR_UNSUPPORTED;
+  if (!gemm_offsets_fit(I, H, 2)) return MOE_ERR_UNSUPPORTED;
   if (rows == 0) return MOE_OK;
   if (!ok_ptr(d_out) || !ok_ptr(w_down) || !ok_ptr(offsets) || !ok_ptr(gu_saved) || !ok_ptr(dgu))
     return MOE_ERR_INVALID_ARG;

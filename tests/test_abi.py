@@ -58,3 +58,21 @@ def test_host_only_entry_points(lib):
     assert lib.moe_set_gemm_max_blocks(0) == 0
     # argument validation answers before any device work
     assert lib.moe_router_topk(None, 4, 8, 2, 0, None, None, None, None, None, None) == 1
+
+
+def test_gemm_size_limits_answer_before_device_work(lib):
+    # one expert's weight matrix of 4 GiB or more is refused (the kernels address it with
+    # 32-bit offsets); sizes just under the limit pass the size checks and stop at the
+    # pointer checks
+    gg = lib.moe_grouped_gemm
+    gg.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    NN, NT, BF16 = 0, 1, 0
+    for mode in (NN, NT):
+        assert gg(mode, None, None, None, None, None, 8, 16, 0, 65536, 32768, BF16, None, BF16, None) == 2
+        assert gg(mode, None, None, None, None, None, 8, 16, 0, 65536, 32704, BF16, None, BF16, None) == 1
+    sw = lib.moe_grouped_gemm_swiglu
+    sw.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 3
+    assert sw(None, None, None, None, None, 8, 16, 32768, 32768, BF16, None, None, None) == 2
+    assert sw(None, None, None, None, None, 8, 16, 32704, 32768, BF16, None, None, None) == 1

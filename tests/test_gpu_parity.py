@@ -181,6 +181,8 @@ GROUP_CASES = {
     "ragged": [130, 0, 1, 255, 64, 300, 0, 17],
     "single": [513],
     "empty_heavy": [0, 0, 0, 200, 0, 0, 1, 0, 0, 0],
+    # around the largest M tile (320 rows) and its even splits
+    "tile_edges": [320, 321, 641, 32, 0, 319, 960],
 }
 
 
