@@ -960,8 +960,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
         // this wave's stores and the ticket requested one epilogue ago have landed
         wait_vmcnt<0>();
         if (lane == 0) {
-          if (pend_tk) s_tk[n_pub & 7] = tk;
-          if (sched_open) tk = 3 * ((int)gridDim.x / nx) + atomicAdd(ctr, 1);
+          // the counter value is kept as returned and offset only here, so nothing waits
+          // for the atomic before this point
+          if (pend_tk) s_tk[n_pub & 7] = 3 * ((int)gridDim.x / nx) + tk;
+          if (sched_open) tk = atomicAdd(ctr, 1);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the ticket is in LDS before the barrier
       }
