@@ -1006,6 +1006,17 @@ int persistent_blocks(K kern, int threads, int (&cache)[64]) {
   return cache[dev];
 }
 
+// Compute units of the current device (cached per device; 0 when the query fails).
+int device_cus() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0 &&
+      hipDeviceGetAttribute(&cache[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cache[dev];
+}
+
 int g_max_blocks = 0;  // grid cap set through moe_set_gemm_max_blocks (0: none)
 std::atomic<unsigned> g_launch_seq{0};  // picks the tile-counter slot of each launch
 
@@ -1039,12 +1050,14 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 }  // namespace
 
 // Tile configurations (BM, BN, WM, WN, STAGES, K bytes per stage), chosen by
-// measurement on the Qwen3- and Mixtral-shaped expert GEMMs. bf16: 256x256 tiles with eight
-// waves (two per SIMD, 128x64 each; the SwiGLU forward 64x128 each, so that a wave's h, g
-// and u rows are 64 columns wide) and a three-stage ring of 64-byte K steps; the SwiGLU
-// backward (whose epilogue reads the saved g,u) 256x128 tiles with four waves and a
-// three-stage ring of 128-byte steps. e4m3: 256x128 tiles with four waves and a three-stage
-// ring of 128-byte steps (its eight-wave build does not fit the register file).
+// measurement on the Qwen3- and Mixtral-shaped expert GEMMs. bf16 NN/NT and the SwiGLU
+// forward: 320x256 tiles with eight waves (two per SIMD, 160x64 each) and a three-stage
+// ring of 64-byte K steps; weight gradients the same with 256x256 tiles. SwiGLU backward
+// (whose epilogue reads the saved g,u): the same 320x256 tiles when they still give every
+// CU at least four tiles, else 320x128 tiles with four waves and a four-stage ring (fewer
+// tiles per CU leave too many CUs idle at the end). e4m3: 256x128 tiles with four waves and
+// a three-stage ring of 128-byte steps (its eight-wave build does not fit the register
+// file).
 #ifndef MOE_GEMM_TILE_BF16
 #define MOE_GEMM_TILE_BF16 320, 256, 2, 4, 3, 64
 #endif
@@ -1055,7 +1068,10 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 #define MOE_GEMM_TILE_BF16_SWIGLU 320, 256, 2, 4, 3, 64
 #endif
 #ifndef MOE_GEMM_TILE_BF16_SWIGLU_BWD
-#define MOE_GEMM_TILE_BF16_SWIGLU_BWD 256, 128, 2, 2, 3, 128
+#define MOE_GEMM_TILE_BF16_SWIGLU_BWD 320, 256, 2, 4, 3, 64
+#endif
+#ifndef MOE_GEMM_TILE_BF16_SWIGLU_BWD_NARROW
+#define MOE_GEMM_TILE_BF16_SWIGLU_BWD_NARROW 320, 128, 2, 2, 4, 64
 #endif
 #ifndef MOE_GEMM_TILE_FP8
 #define MOE_GEMM_TILE_FP8 256, 128, 2, 2, 3, 128
@@ -1078,7 +1094,15 @@ hipError_t launch_sel(const GemmParams& p, hipStream_t s) {
       if (p.rows <= 256 && p.rows <= 32 * p.G)
         return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_SMALL_M>(p, s);
     }
-    if constexpr (EPI == EPI_SWIGLU_BWD) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU_BWD>(p, s);
+    if constexpr (EPI == EPI_SWIGLU_BWD) {
+      // upper bound of the wide tiles (BM = 320, BN = 256), as the launcher counts them,
+      // against the blocks a launch can have
+      const long long wide = ((long long)(p.rows + 319) / 320 + p.G) * ((p.N + 255) / 256);
+      int blocks = device_cus();
+      if (g_max_blocks > 0 && g_max_blocks < blocks) blocks = g_max_blocks;
+      if (wide >= 4LL * blocks) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU_BWD>(p, s);
+      return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU_BWD_NARROW>(p, s);
+    }
     else if constexpr (EPI == EPI_SWIGLU) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU>(p, s);
     else if constexpr (MODE == MOE_GEMM_TN_DW) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_DW>(p, s);
     else return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16>(p, s);

@@ -248,11 +248,14 @@ def test_grouped_gemm_dw(case):
             assert not host_vals(c[g]).any()
 
 
-def test_grouped_gemm_swiglu_bwd():
+@pytest.mark.parametrize("I,cap", [(128, 0), (576, 4)])
+def test_grouped_gemm_swiglu_bwd(I, cap, grid_cap):
+    # a capped grid makes the launcher pick the wide (320x256) tiles: few blocks, many tiles
+    grid_cap(cap)
     counts = GROUP_CASES["ragged"]
     offs = _groups(counts)
     rows, G = int(offs[-1]), len(counts)
-    H, I = 256, 128
+    H = 256
     rng = np.random.default_rng(8)
     d_out = W.to_bf16_bits(rng.standard_normal((rows, H)).astype(np.float32))
     wd = W.to_bf16_bits(rng.standard_normal((G, I, H)).astype(np.float32) * 0.05)
