@@ -615,9 +615,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   };
   // One ring stage: KS k sub-steps; while sub-step ks multiplies, the fragments of ks+1
   // are read and a slice of the cursor's next stage (into `nxt`) is issued.
-  // Five M blocks per wave leave no room for a whole sub-step of A fragments in flight:
-  // there A fragments are read one M block ahead of the multiply instead.
-  constexpr bool APIPE = C::MB >= 5;
+  // Five M blocks per wave, or e4m3 fragments (8 registers each) with eight waves, leave no
+  // room for a whole sub-step of A fragments in flight: there A fragments are read one M
+  // block ahead of the multiply instead.
+  constexpr bool APIPE = C::MB >= 5 || (FP8 && C::NW == 8);
   auto compute_stage = [&](auto MBL_c, const uint8_t* sa, bool iss, uint8_t* nxt) __attribute__((always_inline)) {
     constexpr int KS = FP8 ? BKB / 64 : BKB / 32;
     constexpr int PER = (C::LOADS + KS - 1) / KS;
@@ -1055,9 +1056,9 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 // ring of 64-byte K steps; weight gradients the same with 256x256 tiles. SwiGLU backward
 // (whose epilogue reads the saved g,u): the same 320x256 tiles when they still give every
 // CU at least four tiles, else 320x128 tiles with four waves and a four-stage ring (fewer
-// tiles per CU leave too many CUs idle at the end). e4m3: 256x128 tiles with four waves and
-// a three-stage ring of 128-byte steps (its eight-wave build does not fit the register
-// file).
+// tiles per CU leave too many CUs idle at the end). e4m3: 256x256 tiles with eight waves
+// and a three-stage ring of 64-byte (64-element) K steps, A fragments read one M block
+// ahead of the multiply so that the 8-register e4m3 fragments fit.
 #ifndef MOE_GEMM_TILE_BF16
 #define MOE_GEMM_TILE_BF16 320, 256, 2, 4, 3, 64
 #endif
@@ -1074,7 +1075,7 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 #define MOE_GEMM_TILE_BF16_SWIGLU_BWD_NARROW 320, 128, 2, 2, 4, 64
 #endif
 #ifndef MOE_GEMM_TILE_FP8
-#define MOE_GEMM_TILE_FP8 256, 128, 2, 2, 3, 128
+#define MOE_GEMM_TILE_FP8 256, 256, 2, 4, 3, 64
 #endif
 // Small-M tiles (decode: a handful of rows per expert): 32-row tiles, 128 output columns
 // per block (two waves), a four-stage ring of 128-byte K steps: a decode step only streams
