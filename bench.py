@@ -156,6 +156,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--cpu-sample-tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=False,
+                    help="time replays of the step captured in a HIP graph instead of eager "
+                         "launches (measured no faster: the host stays ahead of the GPU)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch each stage once plus a 256 MiB calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -222,11 +225,24 @@ def main():
     torch.cuda.synchronize()
     _log(f"bench: warmup done ({args.warmup} steps)")
 
+    # With --graph the whole step (every launch reads its sizes from arguments and its row
+    # counts from device memory) is recorded once in a HIP graph and replayed.
+    run = step
+    graph = None
+    if args.graph and not args.pmc_pass:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
+        _log("bench: step captured in a HIP graph")
+
     # ---- timed region: whole layer --------------------------------------------------
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
@@ -378,7 +394,8 @@ def main():
         "config": {"workload": f"{w.name}-shaped MoE block " + ("forward+backward" if training else "forward"),
                    "T": w.T, "H": w.H, "E": w.E, "top_k": w.k, "I": w.I, "shared_I": w.shared_I,
                    "score": ["softmax_pre_renorm", "softmax_post", "sigmoid"][w.score],
-                   "parallelism": "single GPU", "active_experts": active},
+                   "parallelism": "single GPU", "active_experts": active,
+                   "launch": "hip_graph" if graph is not None else "eager"},
         "grouped_gemm_tflops": round(gemm_flops / gemm_time / 1e12, 1),
         "grouped_gemm_mfma_frac": round(gemm_flops / gemm_time / 1e12 / peak_tf, 4),
         "gemm": gemm,
