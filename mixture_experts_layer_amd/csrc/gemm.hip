@@ -12,13 +12,13 @@
 //    with unit scales for e4m3). A wave's M blocks are interleaved (wave wm takes
 //    blocks wm, wm+WM, ...) so the blocks past a group's last row, which are skipped,
 //    are spread over the waves.
-//  * K advances 64 or 128 bytes per stage (32/64 bf16, 128 e4m3). Operands go from global
-//    memory straight into an LDS ring of STAGES buffers with 16-byte
+//  * K advances 64 or 128 bytes per stage (32 or 64 bf16, 64 e4m3). Operands go from
+//    global memory straight into an LDS ring of STAGES buffers with 16-byte
 //    global_load_lds (no staging registers, no VALU copies); the loads for stage
 //    kt+STAGES-1 are in flight while stage kt is multiplied.
-//  * LDS layouts. K-contiguous operands: rows of 128 bytes, the 16-byte chunk index
-//    XORed with (row/2)%8, so the fragment reads of 16 consecutive rows hit distinct
-//    banks. M- or N-contiguous operands (the bf16 weight of the NN forward, both
+//  * LDS layouts. K-contiguous operands: rows of 64 or 128 bytes, the 16-byte chunk
+//    index XORed with (row/4)%4 or (row/2)%8, so the fragment reads of 16 consecutive
+//    rows hit distinct banks. M- or N-contiguous operands (the bf16 weight of the NN forward, both
 //    operands of the weight gradient): rows of k, the 64-byte segment index XORed with
 //    k%4, read with ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one
 //    column (two reads form the 8-element MFMA operand). The swizzles are applied on
@@ -30,10 +30,13 @@
 //    backward) are staged row-major and written with 16-byte stores.
 //  * Tile schedule on the device: every block rebuilds the prefix of per-group M-tile
 //    counts from offsets[] in LDS, so any row split works with no host sync and no
-//    padding. Tiles are ordered (group, N-tile, M-tile) so the M-tiles that share one
-//    weight panel are neighbours, and block ids are remapped so that neighbours land
-//    on the same XCD (blocks are dispatched round-robin over the 8 XCDs, each with
-//    its own L2).
+//    padding; a group's rows are spread evenly over its M tiles. Tiles are ordered
+//    (group, N-tile, M-tile) so the M-tiles that share one weight panel are neighbours.
+//    The grid is persistent (every resident block); XCD x (blocks are dispatched
+//    round-robin over the 8 XCDs, each with its own L2) serves the x-th eighth of the
+//    tile range, from a per-XCD ticket counter (ragged rows) or with a fixed stride
+//    (weight gradients), and the load of a block's next tile starts while the current
+//    one is still being multiplied.
 #include <atomic>
 #include <type_traits>
 
