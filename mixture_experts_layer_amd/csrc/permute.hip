@@ -366,13 +366,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict_
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const u32x4_t val = __builtin_nontemporal_load(&yp[(size_t)rows[j] * H8 + v]);
-      const float q = p[j];
+    // the k row pieces are requested 8 at a time before any is summed, so their latencies
+    // overlap; the sum still runs in slot order
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      u32x4_t val[8];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        acc[2 * d] = fmaf(q, bf16lo(val[d]), acc[2 * d]);
-        acc[2 * d + 1] = fmaf(q, bf16hi(val[d]), acc[2 * d + 1]);
+      for (int jj = 0; jj < 8; ++jj)
+        if (j0 + jj < k) val[jj] = __builtin_nontemporal_load(&yp[(size_t)rows[j0 + jj] * H8 + v]);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj >= k) break;
+        const float q = p[j0 + jj];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          acc[2 * d] = fmaf(q, bf16lo(val[jj][d]), acc[2 * d]);
+          acc[2 * d + 1] = fmaf(q, bf16hi(val[jj][d]), acc[2 * d + 1]);
+        }
       }
     }
     if (shared) {
