@@ -86,14 +86,24 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
     tot += x;
     if (q < part) before += x;
   }
-  if (part == 0) s[e] = e < E ? tot : 0;
-  __syncthreads();
-  for (int o = 1; o < EP; o <<= 1) {  // inclusive Hillis-Steele scan over the totals
-    const int add = (part == 0 && e >= o) ? s[e - o] : 0;
-    __syncthreads();
-    if (part == 0) s[e] += add;
-    __syncthreads();
+  // inclusive scan of the totals over e: within each wave by shuffles, then the wave
+  // totals (at most four waves: EP <= 256) added from LDS
+  __shared__ int wtot[4];
+  int incl = e < E ? tot : 0;
+  if (part == 0) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if ((e & 63) >= o) incl += y;
+    }
+    if ((e & 63) == 63) wtot[e >> 6] = incl;
   }
+  __syncthreads();
+  if (part == 0) {
+    for (int q = 0; q < (e >> 6); ++q) incl += wtot[q];
+    s[e] = incl;
+  }
+  __syncthreads();
   const int excl = s[e] - tot;
   if (part == 0 && e < E) {
     offsets[e] = excl;
