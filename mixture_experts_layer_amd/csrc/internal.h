@@ -16,7 +16,7 @@ hipError_t launch_router_hist(const float* logits, int T, int E, int k, int scor
                               int chunk_tokens, hipStream_t s);
 
 // permute.hip
-constexpr int kPermChunk = 1024;  // flattened (token, slot) entries per dispatch chunk
+constexpr int kPermChunk = 256;  // flattened (token, slot) entries per dispatch chunk
 size_t permute_scratch_bytes(int T, int E, int k);
 int router_chunk_tokens(int T);
 hipError_t launch_dispatch_from_hist(const int32_t* topk_idx, int T, int E, int k, int chunk_tokens,
