@@ -109,7 +109,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
     offsets[e] = excl;
     if (counts) counts[e] = tot;
   }
-  if (threadIdx.x == EP - 1) offsets[E] = s[EP - 1];
+  if ((int)threadIdx.x == EP - 1) offsets[E] = s[EP - 1];
   if (e < E) {
     int run = excl + before;
     if (c1 - c0 <= SCAN_BATCH) {  // the run is still in registers
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4_t* __rest
   __shared__ int rows[32];
   __shared__ float p[32];
   const int t = blockIdx.x;
-  if (threadIdx.x < k) {
+  if ((int)threadIdx.x < k) {
     rows[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
     p[threadIdx.x] = prob ? prob[(size_t)t * k + threadIdx.x] : 1.f;
   }
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void scatter_rows_fp8_kernel(const u32x4_t* __
   __shared__ int rows[32];
   __shared__ float red[8];
   const int t = blockIdx.x;
-  if (threadIdx.x < k) rows[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
+  if ((int)threadIdx.x < k) rows[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
   float a = 0.f;
   for (int v = threadIdx.x; v < H8; v += blockDim.x) a = fmaxf(a, amax8(x[(size_t)t * H8 + v]));
   a = block_max_256(a, red);
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) void scatter_rows_fp8_kernel(const u32x4_t* __
     const u32x2_t q = quant8(x[(size_t)t * H8 + v], sc);
     for (int j = 0; j < k; ++j) xq[(size_t)rows[j] * H8 + v] = q;
   }
-  if (threadIdx.x < k) xscale[rows[threadIdx.x]] = sc;
+  if ((int)threadIdx.x < k) xscale[rows[threadIdx.x]] = sc;
 }
 
 hipError_t launch_scatter_rows_fp8(const void* x, const int32_t* row_of, int T, int H, int k,
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict_
   __shared__ int rows[32];
   __shared__ float p[32];
   const int t = blockIdx.x;
-  if (threadIdx.x < k) {
+  if ((int)threadIdx.x < k) {
     rows[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
     p[threadIdx.x] = prob ? prob[(size_t)t * k + threadIdx.x] : 1.f;
   }
