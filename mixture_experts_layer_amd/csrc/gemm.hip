@@ -815,7 +815,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
             gv[x] = __builtin_amdgcn_raw_buffer_load_b64(gi, go[x], 0, 0);
             uv[x] = __builtin_amdgcn_raw_buffer_load_b64(gi, uo[x], 0, 0);
           }
-          block_f32(acc[i][j], [&](int x, int r, int c, u32x4_t dv) {
+          block_f32(acc[i][j], [&](int x, int, int, u32x4_t dv) {
             float dg[4], du[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1015,9 +1015,11 @@ int device_cus() {
   static int cache[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0 &&
-      hipDeviceGetAttribute(&cache[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = cus;
+  }
   return cache[dev];
 }
 
