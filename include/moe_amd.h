@@ -18,6 +18,12 @@
  *  - Token counts per expert stay on the device (Transformer Engine guide,
  *    "Grouped GEMM": device-side counts avoid a host synchronisation), so every
  *    call can be captured in a HIP graph.
+ *  - Concurrency: each grouped-GEMM launch (also those inside moe_forward /
+ *    moe_backward) takes one of 64 device-side tile-counter slots, in launch order,
+ *    and hands it back zeroed when it ends. Up to 64 launches may be in flight at
+ *    once on one device (different streams); a captured launch keeps the slot it
+ *    drew at capture, so a graph replay must not overlap an eager launch that drew
+ *    the same slot.
  *  - Routing is dropless: routed row buffers always hold T*k rows (guide, "Example:
  *    MoE layer on a single device": num_out_tokens = num_tokens * top_k).
  *  - Errors: host-side argument checks return MOE_ERR_INVALID_ARG (bad pointer,
