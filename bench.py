@@ -154,7 +154,10 @@ def main():
     ap.add_argument("--workload", default="qwen3",
                     help="qwen3 (default, forward+backward) | mixtral | llama4 | skewed_fp8 | tiny")
     ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    # the oracle's cost has a large fixed part (every expert's weights in float64), so a small
+    # token sample understates its rate; the default is the whole Qwen3-shaped workload
+    # (about 10 s on 16 host cores)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=False,
                     help="time replays of the step captured in a HIP graph instead of eager "
@@ -374,7 +377,8 @@ def main():
         threads = max([p.get("num_threads", 1) for p in threadpool_info()
                        if p.get("user_api") == "blas"] or [1])
         cpu = {"value": round(S / tc, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"first {S} of the {w.T} tokens, full weights, "
+               "sample": (f"the whole workload ({S} tokens)" if S == w.T else
+                          f"first {S} of the {w.T} tokens") + ", full weights, "
                          f"{'forward+backward' if training else 'forward'}; {tc:.1f} s"}
         _log(f"bench: oracle {S} tokens in {tc:.1f} s")
 
