@@ -40,27 +40,18 @@ MOE_DEV float sigmoid_fast(float x) {
 }
 
 // ---- OCP FP8 E4M3 ("fn": no infinities, max 448) ---------------------------
-// Round to nearest even, saturating to +-448. Works on the fp32 bit pattern:
-// normal range |v| >= 2^-6 keeps 3 mantissa bits, below that a fixed 2^-9 grid.
+// fp32 -> e4m3 code, round to nearest even: the gfx950 hardware convert
+// (v_cvt_pk_fp8_f32, OCP format). Every caller divides by a scale of amax/448, so
+// |v| <= 448 up to the division's rounding and nothing saturates; on every fp32 |v| < 464
+// the hardware codes equal a round-to-nearest-even, saturate-to-448 conversion written
+// out on the bit pattern (compared exhaustively on the device). NaN gives a NaN code.
 MOE_DEV uint32_t f32_to_e4m3(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  float a = fminf(fabsf(v), 448.0f);
-  uint32_t au = __float_as_uint(a);
-  uint32_t code;
-  if (a < 0.015625f) {                      // 2^-6: subnormal grid of 2^-9
-    // a * 2^9 is exact; rint rounds half to even
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    uint32_t exp = (au >> 23) - 127 + 7;    // biased e4m3 exponent, 1..15
-    uint32_t mant = au & 0x7fffffu;
-    uint32_t keep = mant >> 20;             // top 3 mantissa bits
-    uint32_t rest = mant & 0xfffffu;        // dropped 20 bits
-    uint32_t half = 0x80000u;
-    if (rest > half || (rest == half && (keep & 1u))) keep += 1;
-    code = (exp << 3) + keep;               // a carry out of the mantissa bumps the exponent
-  }
-  return sign | code;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false) & 0xffu;
+}
+// Four codes packed little-endian into one word: a | b << 8 | c << 16 | d << 24.
+MOE_DEV uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 MOE_DEV float e4m3_to_f32(uint32_t c) {

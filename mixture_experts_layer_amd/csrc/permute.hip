@@ -243,11 +243,8 @@ MOE_DEV u32x2_t quant8(const u32x4_t val, float s) {
   u32x2_t o;
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
-    uint32_t c0 = f32_to_e4m3(bf16lo(val[2 * d]) / s);
-    uint32_t c1 = f32_to_e4m3(bf16hi(val[2 * d]) / s);
-    uint32_t c2 = f32_to_e4m3(bf16lo(val[2 * d + 1]) / s);
-    uint32_t c3 = f32_to_e4m3(bf16hi(val[2 * d + 1]) / s);
-    o[d] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    o[d] = pack_e4m3x4(bf16lo(val[2 * d]) / s, bf16hi(val[2 * d]) / s, bf16lo(val[2 * d + 1]) / s,
+                       bf16hi(val[2 * d + 1]) / s);
   }
   return o;
 }
@@ -301,10 +298,59 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const u32x4_t* __res
   if (threadIdx.x == 0) scale[r] = sc;
 }
 
+// One wave per P rows (4P rows per block) for rows of at most 512 vectors of 8 values: the
+// rows are loaded once into registers (V vectors per lane and row, all requested before any
+// is used), each row's amax reduced within the wave, and the codes written from the
+// registers. Same scale and codes as the block kernel.
+template <int V, int P>
+__global__ __launch_bounds__(256) void quantize_rows_wave_kernel(const u32x4_t* __restrict__ x, int R,
+                                                                 int C8, u32x2_t* __restrict__ q,
+                                                                 float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * P;
+  if (r0 >= R) return;  // the whole wave
+  u32x4_t v[P][V];
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int c = lane + 64 * i;
+      if (r0 + j < R && c < C8) v[j][i] = x[(size_t)(r0 + j) * C8 + c];
+    }
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    if (r0 + j >= R) break;
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (lane + 64 * i < C8) a = fmaxf(a, amax8(v[j][i]));
+    a = wave_max(a);
+    const float sc = a == 0.f ? 1.f : a / 448.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int c = lane + 64 * i;
+      if (c < C8) q[(size_t)(r0 + j) * C8 + c] = quant8(v[j][i], sc);
+    }
+    if (lane == 0) scale[r0 + j] = sc;
+  }
+}
+
 hipError_t launch_quantize_rows(const void* x, int R, int C, uint8_t* q, float* scale,
                                 hipStream_t s) {
   if (R == 0) return hipSuccess;
-  quantize_rows_kernel<<<R, 256, 0, s>>>((const u32x4_t*)x, C / 8, (u32x2_t*)q, scale);
+  const int C8 = C / 8;
+#ifndef MOE_QROWS_P
+#define MOE_QROWS_P 2
+#endif
+  constexpr int P = MOE_QROWS_P;
+  const int blocks = (R + 4 * P - 1) / (4 * P);
+  const auto xx = (const u32x4_t*)x;
+  const auto qq = (u32x2_t*)q;
+  if (C8 <= 64) quantize_rows_wave_kernel<1, P><<<blocks, 256, 0, s>>>(xx, R, C8, qq, scale);
+  else if (C8 <= 128) quantize_rows_wave_kernel<2, P><<<blocks, 256, 0, s>>>(xx, R, C8, qq, scale);
+  else if (C8 <= 256) quantize_rows_wave_kernel<4, P><<<blocks, 256, 0, s>>>(xx, R, C8, qq, scale);
+  else if (C8 <= 512) quantize_rows_wave_kernel<8, P><<<blocks, 256, 0, s>>>(xx, R, C8, qq, scale);
+  else quantize_rows_kernel<<<R, 256, 0, s>>>((const u32x4_t*)x, C8, (u32x2_t*)q, scale);
   return hipGetLastError();
 }
 

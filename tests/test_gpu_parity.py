@@ -106,6 +106,26 @@ def test_permute_all_to_one_expert_and_empty_experts():
     assert np.array_equal(host_bits(xp), O.permute(x_bits, r_src))
 
 
+@pytest.mark.parametrize("C", [64, 512, 768, 2048, 4096, 8192])
+def test_quantize_rows_bit_exact(C):
+    # every register-resident width (1, 2, 4, 8 vectors per lane) and the wide-row path,
+    # a row count that is not a multiple of the four rows per block, an all-zero row and
+    # rows with widely different ranges
+    R = 37
+    rng = np.random.default_rng(C)
+    xv = rng.standard_normal((R, C)).astype(np.float32) * rng.uniform(1e-3, 300, (R, 1)).astype(np.float32)
+    xv[5] = 0.0
+    xv[11, C // 3] = 1e4
+    x_bits = W.to_bf16_bits(xv)
+    q = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((R,), dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8_rows(dev_bf16(x_bits), q, sc)
+    torch.cuda.synchronize()
+    rq, rs = O.quantize_rows_e4m3(O.bf16_bits_to_f64(x_bits))
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(sc.cpu().numpy(), rs)
+
+
 def test_permute_fp8_codes_and_scales_bit_exact():
     T, H, E, k = 300, 256, 16, 4
     rng = np.random.default_rng(2)
