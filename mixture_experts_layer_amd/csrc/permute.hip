@@ -339,10 +339,7 @@ hipError_t launch_quantize_rows(const void* x, int R, int C, uint8_t* q, float* 
                                 hipStream_t s) {
   if (R == 0) return hipSuccess;
   const int C8 = C / 8;
-#ifndef MOE_QROWS_P
-#define MOE_QROWS_P 2
-#endif
-  constexpr int P = MOE_QROWS_P;
+  constexpr int P = 1;  // rows per wave (2 and 4 measured no faster)
   const int blocks = (R + 4 * P - 1) / (4 * P);
   const auto xx = (const u32x4_t*)x;
   const auto qq = (u32x2_t*)q;
