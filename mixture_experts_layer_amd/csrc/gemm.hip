@@ -121,7 +121,7 @@ struct Tile {
   int n0;          // first output column (SWIGLU: first h column)
   int rows_valid;  // NN/NT: rows of this tile inside the group; DW: BM
   int kcount;      // DW: rows of the group (the reduction length)
-  int kbase;       // DW: first row of the group
+  int kbase;       // first row of the group
 };
 
 // K-contiguous operand tile: rows of BKB bytes, the 16-byte chunk index XORed with a
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       t.rows_valid = min(per, cnt - mtile * per);
       t.n0 = ntile * (EPI == EPI_SWIGLU ? HB : BN);
       t.kcount = p.K;
-      t.kbase = 0;
+      t.kbase = gbeg;
     } else {
       const int mtn = (p.M + BM - 1) / BM;
       const int g = tile / (mtn * ntn), rem = tile % (mtn * ntn);
@@ -371,6 +371,17 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
     t.kcount = __builtin_amdgcn_readfirstlane(t.kcount);
     t.kbase = __builtin_amdgcn_readfirstlane(t.kbase);
     return t;
+  };
+
+  // The last group's own A, weight and C tensors (a dense shared expert), when given.
+  auto last_group = [&](const Tile& t) __attribute__((always_inline)) {
+    return !DW && p.A_last != nullptr && t.g == p.G - 1;
+  };
+  auto c_base = [&](const Tile& t) __attribute__((always_inline)) -> const uint16_t* {
+    return (const uint16_t*)(last_group(t) ? p.C_last : p.C);
+  };
+  auto c_row = [&](const Tile& t) __attribute__((always_inline)) -> size_t {
+    return (size_t)(last_group(t) ? t.m0 - t.kbase : t.m0);
   };
 
   // ---- load descriptors: a global pointer per 1 KB chunk-load, advanced per stage ----
@@ -411,9 +422,11 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
         a_off[i] = (uint32_t)(ok ? row : 0) * lda32 + kc_logical<BKB>(row, lane) * 16;
         a_krow[i] = 0;
       }
-      a_base = (const uint8_t*)p.A + (size_t)t.m0 * lda;
+      const bool lastg = last_group(t);
+      a_base = lastg ? (const uint8_t*)p.A_last + (size_t)(t.m0 - t.kbase) * lda
+                     : (const uint8_t*)p.A + (size_t)t.m0 * lda;
       if constexpr (!B_MN) {  // NT: B_g is [N, K]
-        const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.N * lda;
+        const uint8_t* bg = lastg ? (const uint8_t*)p.B_last : (const uint8_t*)p.B + (size_t)t.g * p.N * lda;
         b_base = bg;
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i) {
@@ -434,7 +447,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
           b_krow[i] = 0;
         }
       } else {  // NN: B_g is [K, N]
-        const uint8_t* bg = (const uint8_t*)p.B + (size_t)t.g * p.K * p.N * 2;
+        const uint8_t* bg = lastg ? (const uint8_t*)p.B_last : (const uint8_t*)p.B + (size_t)t.g * p.K * p.N * 2;
         b_base = bg;
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i) {
@@ -729,7 +742,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
     if constexpr (EPI == EPI_SWIGLU) {
       constexpr int NH = C::NB / 2;
       const int twoI = 2 * p.I;
-      const auto hr = tile_rsrc((const uint16_t*)p.C + (size_t)t.m0 * p.I + t.n0);
+      const auto hr = tile_rsrc(c_base(t) + c_row(t) * p.I + t.n0);
       const auto gr = tile_rsrc(p.gu_out ? (const uint16_t*)p.gu_out + (size_t)t.m0 * twoI + t.n0
                                          : (const uint16_t*)p.C);
 #pragma unroll
@@ -837,7 +850,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
     } else {
       const int mlim = DW ? p.M - t.m0 : t.rows_valid;
       const size_t org = DW ? (size_t)t.g * p.M * p.N + (size_t)t.m0 * p.N + t.n0
-                            : (size_t)t.m0 * p.N + t.n0;
+                            : c_row(t) * p.N + t.n0;
 #pragma unroll
       for (int i = 0; i < C::MB; ++i) {
         const int r0 = (wm + WM * i) * 32;
@@ -874,7 +887,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
             });
           }
         } else {
-          const auto cr = tile_rsrc((const uint16_t*)p.C + org);
+          const auto cr = tile_rsrc(c_base(t) + org);
 #pragma unroll
           for (int j0 = 0; j0 < C::NB; j0 += PB) {
             const int c0 = bcol0(j0);

@@ -56,6 +56,12 @@ struct GemmParams {
   void* gu_out;          // EPI_SWIGLU: optional saved g,u [rows,2I]
   const void* gu_in;     // EPI_SWIGLU_BWD: saved g,u [rows,2I]
   int sched_slot;        // tile-counter slot of the launch (set by the launcher)
+  // NN/NT, bf16, no saved g,u: when A_last is set the last group (G-1) takes its A rows,
+  // its weight and its C rows from these tensors (row 0 = the group's first row) instead
+  // of from A, B and C. Used to run a dense shared expert as one more group.
+  const void* A_last;
+  const void* B_last;
+  void* C_last;
 };
 hipError_t launch_grouped_gemm(const GemmParams& p, hipStream_t s);
 // Grid cap of the persistent grouped-GEMM launches (0: every resident block).

@@ -57,7 +57,7 @@ Layout make_layout(const moe_problem_t& p) {
   L.topk_idx = take(N * 4);
   L.topk_prob = take(N * 4);
   L.counts = take((size_t)p.E * 4);
-  L.offsets = take(((size_t)p.E + 1) * 4);
+  L.offsets = take(((size_t)p.E + 2) * 4);  // one more end for a fused shared group
   L.row_of = take(N * 4);
   L.src_of = take(N * 4);
   L.shared_offsets = take(2 * 4);
@@ -365,7 +365,11 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
                                     v.counts, v.offsets, v.row_of, v.src_of, s));
   if (fp8) MOE_TRY(launch_scatter_rows_fp8(t->x, v.row_of, T, H, k, (uint8_t*)v.xp, v.xp_scale, s));
   else MOE_TRY(launch_scatter_rows(t->x, v.row_of, nullptr, T, H, k, v.xp, s));
-  // 3. grouped MLP
+  // 3. grouped MLP. A dense shared expert of the routed experts' width runs as one more
+  // group of T rows (offsets[E+1] = N + T) in the same two launches, reading x, its own
+  // weights and its own outputs; other widths, and training, launch it separately.
+  const bool fuse_shared = p->shared_I == I && !p->training && !fp8;
+  if (fuse_shared) MOE_TRY(launch_fill_i32(v.offsets + E + 1, 1, N + T, s));
   GemmParams g1{};
   g1.mode = fp8 ? MOE_GEMM_NT : MOE_GEMM_NN;
   g1.epi = EPI_SWIGLU;
@@ -382,6 +386,13 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   g1.C = v.h;
   g1.I = I;
   g1.gu_out = p->training ? v.gu : nullptr;
+  if (fuse_shared) {
+    g1.G = E + 1;
+    g1.rows = N + T;
+    g1.A_last = t->x;
+    g1.B_last = t->shared_gu;
+    g1.C_last = v.shared_h;
+  }
   MOE_TRY(launch_grouped_gemm(g1, s));
   GemmParams g2{};
   g2.mode = fp8 ? MOE_GEMM_NT : MOE_GEMM_NN;
@@ -402,9 +413,16 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   g2.N = H;
   g2.K = I;
   g2.C = v.out;
+  if (fuse_shared) {
+    g2.G = E + 1;
+    g2.rows = N + T;
+    g2.A_last = v.shared_h;
+    g2.B_last = t->shared_down;
+    g2.C_last = v.shared_out;
+  }
   MOE_TRY(launch_grouped_gemm(g2, s));
   // shared expert: one dense group over all T tokens, read straight from x
-  if (p->shared_I) {
+  if (p->shared_I && !fuse_shared) {
     MOE_TRY(launch_fill_i32(v.shared_offsets, 1, 0, s));
     MOE_TRY(launch_fill_i32(v.shared_offsets + 1, 1, T, s));
     GemmParams s1{};

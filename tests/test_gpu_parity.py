@@ -453,6 +453,12 @@ SMALL = {
     "small_post": W.custom("small_post", T=333, H=256, E=8, k=2, I=384, score=O.SOFTMAX_POST),
     "small_sig_shared": W.custom("small_sig_shared", T=8, H=320, E=16, k=1, I=256, score=O.SIGMOID,
                                  shared_I=192, hot_experts=(0, 1, 2), hot_bias=2.0),
+    # shared expert as wide as the routed ones: it runs as one more group of the routed
+    # launches (decode-sized tiles, then several 320-row tiles with a ragged last one)
+    "small_shared_eq": W.custom("small_shared_eq", T=8, H=320, E=16, k=1, I=256, score=O.SIGMOID,
+                                shared_I=256, hot_experts=(0, 1, 2), hot_bias=2.0),
+    "mid_shared_eq": W.custom("mid_shared_eq", T=700, H=384, E=8, k=2, I=320, score=O.SOFTMAX_POST,
+                              shared_I=320),
     "small_qwen": W.custom("small_qwen", T=257, H=256, E=32, k=8, I=192, training=True),
     "small_fp8": W.custom("small_fp8", T=300, H=256, E=32, k=8, I=256, fp8=True, zipf_s=1.2, n_empty=5),
     "t1": W.custom("t1", T=1, H=128, E=8, k=2, I=128, training=True),
