@@ -12,4 +12,5 @@ from .moe_oracle import (SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID, E4M3_MAX,  #
                          e4m3_decode, e4m3_encode, topk_select, topk_probs, router_topk,
                          dispatch_meta, permute, quantize_rows_e4m3, quantize_cols_e4m3,
                          silu, grouped_gemm, swiglu_from_gu, expert_mlp, dense_mlp, combine,
-                         moe_forward, swiglu_backward, grouped_gemm_dw, moe_backward)
+                         moe_forward, swiglu_backward, grouped_gemm_dw, moe_backward,
+                         gate_logits, router_backward, prob_grad)

@@ -122,6 +122,15 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
+def _logit_values(logits) -> np.ndarray:
+    """Logits as float64 values: float32 logits (the layer's input type) widen exactly;
+    float64 logits (the exact-arithmetic pins) are kept as they are."""
+    l = np.asarray(logits)
+    if l.dtype != np.float64:
+        l = l.astype(np.float32)
+    return l.astype(np.float64)
+
+
 def topk_select(logits: np.ndarray, k: int) -> np.ndarray:
     """Top-k expert ids per token, in descending order of the logit.
 
@@ -132,7 +141,7 @@ def topk_select(logits: np.ndarray, k: int) -> np.ndarray:
     Built as k rounds of arg-max (np.argmax returns the first, i.e. lowest, index of
     a tie), each round removing the chosen expert.
     """
-    l = np.asarray(logits, dtype=np.float32)
+    l = _logit_values(logits)
     assert np.isfinite(l).all(), "non-finite logits are not supported"
     T, E = l.shape
     assert 1 <= k <= E
@@ -140,7 +149,7 @@ def topk_select(logits: np.ndarray, k: int) -> np.ndarray:
     idx = np.empty((T, k), dtype=np.int32)
     rows = np.arange(T)
     for j in range(k):
-        cand = np.where(avail, l.astype(np.float64), -np.inf)
+        cand = np.where(avail, l, -np.inf)
         e = np.argmax(cand, axis=1)
         idx[:, j] = e
         avail[rows, e] = False
@@ -159,7 +168,7 @@ def topk_probs(logits: np.ndarray, idx: np.ndarray, score: int, exact=False) -> 
       are not one and must be applied]: q_j = 1 / (1 + exp(-l_idx_j)).
       READING: no renormalisation of sigmoid weights.
     """
-    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    l = _logit_values(logits)
     T = l.shape[0]
     sel = np.take_along_axis(l, idx.astype(np.int64), axis=1)
     if score == SOFTMAX_PRE_RENORM:
@@ -198,6 +207,66 @@ def router_topk(logits: np.ndarray, k: int, score: int, exact=False):
     dense[rows, idx] = q
     counts = rmap.sum(axis=0).astype(np.int32)
     return idx, q, counts, rmap, dense
+
+
+def gate_logits(x_vals, w_router_vals, exact=False):
+    """Router projection logits[t,e] = sum_h x[t,h] * W_r[e,h], summed in float64, one
+    rounding to fp32 [TE-MoE "Example: MoE layer on a single device": a bias-free linear
+    layer from the hidden size to the expert count produces the logits the router
+    scores; TE-MIX TEMixtralSparseMoeBlock: the gate is a bias-free Linear of shape
+    (experts, hidden) applied to the hidden states].
+    READING: W_r is [E, H] (the linear layer's weight layout); the logits keep the fp32
+    accumulator with no bf16 rounding, since the router's math runs in fp32 whatever
+    the logits' type [TE-MoE "Router"].
+    """
+    x = as_values(x_vals)
+    w = as_values(w_router_vals)
+    return to_f32(x @ w.T, exact)
+
+
+def router_backward(logits, idx, d_prob, score, exact=False):
+    """Gradient of the routing weights with respect to the logits [TE-MoE "Router": the
+    score function and the top-k run in one differentiable kernel with fp32 math].
+
+    The top-k choice is piecewise constant, so only the kept logits' influence through
+    the score function carries a gradient. Each score function is differentiated as
+    it is defined in topk_probs, in float64, then rounded once to fp32:
+      SOFTMAX_PRE_RENORM: p = softmax(l) over all experts, s = sum of the kept p,
+        q_j = p_idx_j / s. Through the renormalisation dp_i = (dq_i - sum_j q_j dq_j)/s
+        for a kept expert i (0 for the others), then through the softmax
+        dl_e = p_e (dp_e - sum_i p_i dp_i) for every expert e.
+      SOFTMAX_POST: q = softmax of the kept logits, dl_idx_j = q_j (dq_j - sum q dq);
+        0 elsewhere.
+      SIGMOID: q_j = sigmoid(l_idx_j), dl_idx_j = dq_j q_j (1 - q_j); 0 elsewhere.
+    Returns d_logits [T, E] (float64 values of fp32 results).
+    """
+    l = _logit_values(logits)
+    T, E = l.shape
+    ii = np.asarray(idx, dtype=np.int64)
+    dq = np.asarray(d_prob, dtype=np.float64)
+    rows = np.arange(T)[:, None]
+    dl = np.zeros((T, E), dtype=np.float64)
+    sel = np.take_along_axis(l, ii, axis=1)
+    if score == SOFTMAX_PRE_RENORM:
+        m = l.max(axis=1, keepdims=True)
+        p = np.exp(l - m)
+        p = p / p.sum(axis=1, keepdims=True)
+        ps = np.take_along_axis(p, ii, axis=1)
+        s_ = ps.sum(axis=1, keepdims=True)
+        q = ps / s_
+        dp = np.zeros((T, E), dtype=np.float64)
+        dp[rows, ii] = (dq - (q * dq).sum(axis=1, keepdims=True)) / s_
+        dl = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    elif score == SOFTMAX_POST:
+        z = np.exp(sel - sel.max(axis=1, keepdims=True))
+        q = z / z.sum(axis=1, keepdims=True)
+        dl[rows, ii] = q * (dq - (q * dq).sum(axis=1, keepdims=True))
+    elif score == SIGMOID:
+        q = 1.0 / (1.0 + np.exp(-sel))
+        dl[rows, ii] = dq * q * (1.0 - q)
+    else:
+        raise ValueError(f"unknown score function {score}")
+    return to_f32(dl, exact)
 
 
 # ---------------------------------------------------------------------------
@@ -360,7 +429,9 @@ def combine(out_vals, row_of, prob=None, shared_vals=None, exact=False):
     """y[t] = sum_j q[t,j] * out[row_of[t,j]] (+ shared[t]), summed in float64, one
     rounding to fp32 then bf16 [TE-MoE "Token combine": weighted sum of the per-expert
     contributions in the same pass; "Token probabilities": weights applied once].
-    prob=None: unweighted sum (the dispatch backward uses this form).
+    prob=None: unweighted sum (the dispatch backward uses this form). shared_vals is any
+    [T, H] term added before the rounding (the shared expert's output; in the backward,
+    the router's contribution to dx).
     """
     o = np.asarray(out_vals, dtype=np.float64)
     T, k = row_of.shape
@@ -373,6 +444,20 @@ def combine(out_vals, row_of, prob=None, shared_vals=None, exact=False):
     if shared_vals is not None:
         acc += np.asarray(shared_vals, dtype=np.float64)
     return to_bf16(acc, exact)
+
+
+def prob_grad(dy_vals, out_vals, row_of, exact=False):
+    """Gradient of y[t] = sum_j q[t,j] out[row_of[t,j]] (+ shared[t]) with respect to
+    the routing weights: d_prob[t,j] = sum_h dy[t,h] * out[row_of[t,j],h], summed in
+    float64, one rounding to fp32 [TE-MoE "Token combine": the merging weights are an
+    input of the differentiable combine]. out holds the stored (bf16) expert outputs."""
+    dy = as_values(dy_vals)
+    o = np.asarray(out_vals, dtype=np.float64)
+    T, k = row_of.shape
+    dq = np.zeros((T, k), dtype=np.float64)
+    for j in range(k):
+        dq[:, j] = (dy * o[np.asarray(row_of[:, j], dtype=np.int64)]).sum(axis=1)
+    return to_f32(dq, exact)
 
 
 # ---------------------------------------------------------------------------
@@ -398,7 +483,8 @@ def moe_forward(x_bits, logits, w_gu_bits, w_down_bits, k, score, I,
         shared = dense_mlp(x, shared_gu_bits, shared_down_bits, Is, exact)
     y = combine(mlp["out"], row_of, q, shared, exact)
     res = dict(topk_idx=idx, topk_prob=q, counts=counts, routing_map=rmap, probs_dense=dense,
-               offsets=offsets, row_of=row_of, src_of=src_of, xp=xp, shared=shared, y=y)
+               offsets=offsets, row_of=row_of, src_of=src_of, xp=xp, shared=shared, y=y,
+               x=x, logits=logits, score=score)
     res.update(mlp)
     return res
 
@@ -429,13 +515,19 @@ def grouped_gemm_dw(a_vals, b_vals, offsets, exact=False, out_bf16=False):
     return out
 
 
-def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False):
+def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False, w_router_bits=None):
     """Backward of the expert path for an upstream gradient dy [T, H]
     [TE-MoE "Example: MoE layer on a single device": all stages differentiable;
     HF-48201 "Numbers": the block is timed forward + backward].
 
-    READING: logits are an input, so no gradient flows to the router; dx goes
-    through the expert path only. dW are rounded to bf16.
+    READING: without a router weight the logits are an input, so no gradient flows to
+    the router and dx goes through the expert path only. dW are rounded to bf16.
+    With w_router_bits [E, H] (the logits were gate_logits(x, W_r)) the router is
+    differentiated too [TE-MoE "Router": one differentiable kernel]:
+      d_prob    = prob_grad(dy, out, row_of);  d_logits = router_backward(...)
+      dW_router = fp32(d_logits^T @ x)   (float64 sum of the fp32 d_logits values)
+      dx[t]     = bf16(sum_j dxp[row_of[t,j]] + sum_e d_logits[t,e] W_r[e])   (one
+                  rounding of the float64 sum of both paths)
       d_out[row_of[t,j]] = bf16(q[t,j] * dy[t])                 (combine backward)
       dh    = fp32(d_out_e @ W_down[e]^T);  dGU = SwiGLU'(dh; saved bf16 g, u)
       dW_down[e] = bf16(h_e^T @ d_out_e)
@@ -461,5 +553,13 @@ def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False):
     # GEMM1 backward
     dxp = to_bf16(grouped_gemm(dgu, np.swapaxes(w_gu, 1, 2), offsets, exact), exact)
     dw_gu = grouped_gemm_dw(fwd["xp"], dgu, offsets, exact, out_bf16=True)
-    dx = combine(dxp, row_of, None, None, exact)
-    return dict(d_out=d_out, dh=dh, dgu=dgu, dxp=dxp, dx=dx, dw_gu=dw_gu, dw_down=dw_down)
+    res = dict(d_out=d_out, dh=dh, dgu=dgu, dxp=dxp, dw_gu=dw_gu, dw_down=dw_down)
+    dx_router = None
+    if w_router_bits is not None:
+        d_prob = prob_grad(dy, fwd["out"], row_of, exact)
+        d_logits = router_backward(fwd["logits"], fwd["topk_idx"], d_prob, fwd["score"], exact)
+        dx_router = d_logits @ as_values(w_router_bits)
+        res.update(d_prob=d_prob, d_logits=d_logits, dx_router=dx_router,
+                   dw_router=to_f32(d_logits.T @ fwd["x"], exact))
+    res["dx"] = combine(dxp, row_of, None, dx_router, exact)
+    return res

@@ -20,6 +20,7 @@ import numpy as np
 # tensor ids of the seed sequence
 TID_X, TID_LOGITS, TID_WGATE, TID_WUP, TID_WDOWN = 0, 1, 2, 3, 4
 TID_SGATE, TID_SUP, TID_SDOWN, TID_DY, TID_PERM, TID_GUMBEL = 5, 6, 7, 8, 9, 10
+TID_WROUTER = 11
 
 SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID = 0, 1, 2
 
@@ -102,7 +103,8 @@ def make_inputs(name, seed: int = 0, T: int | None = None, with_weights: bool = 
 
     bf16 tensors are uint16 bit patterns: x [T,H], w_gu [E,H,2I] (gate columns
     [0,I), up columns [I,2I)), w_down [E,I,H], optional shared_gu [H,2Is],
-    shared_down [Is,H], optional dy [T,H]. logits [T,E] float32.
+    shared_down [Is,H], optional dy [T,H], w_router [E,H] (the router projection's
+    weight, N(0, 0.02) like the expert weights). logits [T,E] float32.
     ``T`` overrides the token count (same recipe, fewer or more rows).
     """
     w = WORKLOADS[name] if isinstance(name, str) else name
@@ -118,6 +120,7 @@ def make_inputs(name, seed: int = 0, T: int | None = None, with_weights: bool = 
         out["w_gu"] = to_bf16_bits(np.concatenate([g, u], axis=2))
         del g, u
         out["w_down"] = _bf16(seed, TID_WDOWN, (w.E, w.I, w.H), 0.02)
+        out["w_router"] = _bf16(seed, TID_WROUTER, (w.E, w.H), 0.02)
         if w.shared_I:
             sg = _normal_f32(seed, TID_SGATE, (w.H, w.shared_I), 0.02)
             su = _normal_f32(seed, TID_SUP, (w.H, w.shared_I), 0.02)
