@@ -172,6 +172,54 @@ moe_status_t moe_quantize_fp8_rows(const void* x, int R, int C, uint8_t* q, floa
 moe_status_t moe_quantize_fp8_weights(const void* w, int G, int K, int N, uint8_t* q,
                                       float* scale, void* stream);
 
+/* ---- router projection and router backward -------------------------------------- */
+
+/* Router projection (guide, "Example: MoE layer on a single device": the logits come
+ * from a bias-free linear layer of the hidden states; te_mixtral.py,
+ * TEMixtralSparseMoeBlock: gate of shape (experts, hidden)).
+ *  x [T,H] bf16, w_router [E,H] bf16 in; logits [T,E] float32 out:
+ *  logits[t,e] = sum_h x[t,h] w_router[e,h], fp32 accumulation, no bf16 rounding (the
+ *  router's math runs in fp32). */
+moe_status_t moe_router_logits(const void* x, const void* w_router, int T, int H, int E,
+                               float* logits, void* stream);
+
+/* Combine backward with the routing-weight gradient (guide, "Token combine": the merging
+ * weights are an input of the differentiable combine; "Router": the score function and
+ * top-k are differentiable with fp32 math).
+ *  dy [T,H] bf16, expert_out [T*k,H] bf16 (the forward's expert outputs before
+ *  weighting), row_of [T,k], topk_idx [T,k], topk_prob [T,k] float32, score as in
+ *  the forward.
+ *  d_out [T*k,H] bf16 out: d_out[row_of[t,j]] = bf16(p[t,j] * dy[t]).
+ *  d_prob [T,k] float32 out, nullable: <dy[t], expert_out[row_of[t,j]]> (fp32 sum).
+ *  d_logits [T,E] float32 out: at the kept experts, softmax (either order: the same
+ *  function of the kept logits) p_j (d_prob_j - sum_i p_i d_prob_i), sigmoid
+ *  d_prob_j p_j (1 - p_j); 0 at the other experts (the top-k choice is piecewise
+ *  constant). */
+moe_status_t moe_combine_backward_router(const void* dy, const void* expert_out,
+                                         const int32_t* row_of, const int32_t* topk_idx,
+                                         const float* topk_prob, int T, int H, int E, int k,
+                                         int score, void* d_out, float* d_prob, float* d_logits,
+                                         void* stream);
+
+/* Scratch bytes moe_router_weight_grad needs for (T, H, E). */
+size_t moe_router_weight_grad_workspace_bytes(int T, int H, int E);
+
+/* Router weight gradient dw_router [E,H] float32 = d_logits[T,E]^T . x[T,H]. Each d_logits
+ * value enters the bf16 matrix-core product as two bf16 halves (hi = bf16(d),
+ * lo = bf16(d - hi)), about 16 significant bits; the K = T reduction is split into
+ * ranges whose fp32 partial products are summed in a fixed order (deterministic).
+ *  ws: at least moe_router_weight_grad_workspace_bytes(T,H,E) bytes. T == 0 writes zeros. */
+moe_status_t moe_router_weight_grad(const void* x, const float* d_logits, int T, int H, int E,
+                                    float* dw_router, void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch backward of a layer that owns its router projection: dx[t] =
+ * bf16(sum_j dxp[row_of[t,j]] + sum_j d_logits[t,e_j] w_router[e_j]), e_j = topk_idx[t,j],
+ * summed in fp32 with one rounding (d_logits is 0 off the kept experts). */
+moe_status_t moe_dispatch_backward_router(const void* dxp, const int32_t* row_of,
+                                          const int32_t* topk_idx, const float* d_logits,
+                                          const void* w_router, int T, int H, int E, int k,
+                                          void* dx, void* stream);
+
 /* ---- whole layer ------------------------------------------------------------ */
 
 typedef struct {
@@ -182,6 +230,10 @@ typedef struct {
   int score;     /* moe_score_t */
   int dtype;     /* expert GEMMs: MOE_BF16 or MOE_FP8_E4M3 */
   int training;  /* 1: keep what moe_backward needs in the workspace */
+  int router;    /* 1: the layer owns its router projection: moe_forward computes the
+                    logits from x and w_router (into the workspace; t->logits is not
+                    read) and moe_backward also returns dw_router and adds the router's
+                    term to dx */
 } moe_problem_t;
 
 typedef struct {
@@ -194,6 +246,8 @@ typedef struct {
   const void* shared_gu;      /* bf16 [H,2*shared_I] or NULL */
   const void* shared_down;    /* bf16 [shared_I,H] or NULL */
   void* y;                    /* [T,H] bf16 out */
+  const void* w_router;       /* bf16 [E,H] (router = 1), else NULL */
+  float* dw_router;           /* [E,H] float32 out of moe_backward (router = 1), else NULL */
 } moe_tensors_t;
 
 /* Device pointers into a forward workspace (all inside ws). */
@@ -219,6 +273,10 @@ typedef struct {
   void* dxp;           /* [T*k,H] bf16 (training) */
   void* scratch;       /* moe_permute scratch */
   size_t scratch_bytes;
+  float* logits;       /* [T,E] (router = 1) */
+  float* d_logits;     /* [T,E] (router = 1, training) */
+  void* router_ws;     /* moe_router_weight_grad scratch (router = 1, training) */
+  size_t router_ws_bytes;
 } moe_views_t;
 
 /* Bytes of workspace moe_forward (and, when training, moe_backward) needs. */
@@ -234,9 +292,13 @@ moe_status_t moe_workspace_views(const moe_problem_t* p, void* ws, size_t ws_byt
 moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* ws,
                          size_t ws_bytes, void* stream);
 
-/* Backward of the expert path for upstream gradient dy [T,H] bf16 (bf16 MLP,
- * training=1 forward only): dx [T,H] bf16, dw_gu [E,H,2I] bf16, dw_down [E,I,H]
- * bf16. Logits are an input of the layer, so no gradient flows to the router. */
+/* Backward of the layer for upstream gradient dy [T,H] bf16 (bf16 MLP, training=1
+ * forward only): dx [T,H] bf16, dw_gu [E,H,2I] bf16, dw_down [E,I,H] bf16. With
+ * router = 0 the logits are an input of the layer and no gradient flows to the router.
+ * With router = 1 (t->x and t->w_router as in the forward) it also writes
+ * t->dw_router [E,H] float32 and d_logits into the workspace, and dx includes the
+ * router's term; the stages are moe_combine_backward_router, the GEMM backward,
+ * moe_router_weight_grad and moe_dispatch_backward_router. */
 moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const void* dy,
                           void* dx, void* dw_gu, void* dw_down, void* ws, size_t ws_bytes,
                           void* stream);

@@ -26,7 +26,9 @@ EXPORTS = [
     "moe_grouped_gemm_swiglu", "moe_grouped_gemm", "moe_grouped_gemm_swiglu_bwd",
     "moe_set_gemm_max_blocks", "moe_unpermute_combine", "moe_combine_backward", "moe_quantize_fp8_rows",
     "moe_quantize_fp8_weights", "moe_workspace_bytes", "moe_workspace_views", "moe_forward",
-    "moe_backward",
+    "moe_backward", "moe_router_logits", "moe_combine_backward_router",
+    "moe_router_weight_grad_workspace_bytes", "moe_router_weight_grad",
+    "moe_dispatch_backward_router",
 ]
 
 
@@ -39,13 +41,14 @@ class MoeError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int), ("H", ctypes.c_int), ("E", ctypes.c_int),
                 ("k", ctypes.c_int), ("I", ctypes.c_int), ("shared_I", ctypes.c_int),
-                ("score", ctypes.c_int), ("dtype", ctypes.c_int), ("training", ctypes.c_int)]
+                ("score", ctypes.c_int), ("dtype", ctypes.c_int), ("training", ctypes.c_int),
+                ("router", ctypes.c_int)]
 
 
 class Tensors(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("x", "logits", "w_gu", "w_gu_scale", "w_down", "w_down_scale",
-                 "shared_gu", "shared_down", "y")]
+                 "shared_gu", "shared_down", "y", "w_router", "dw_router")]
 
 
 class Views(ctypes.Structure):
@@ -53,7 +56,9 @@ class Views(ctypes.Structure):
                 ("topk_idx", "topk_prob", "counts", "offsets", "row_of", "src_of", "xp",
                  "xp_scale", "gu", "h", "hq", "h_scale", "out", "shared_h", "shared_out",
                  "shared_offsets", "d_out", "dgu", "dxp", "scratch")] + \
-               [("scratch_bytes", ctypes.c_size_t)]
+               [("scratch_bytes", ctypes.c_size_t)] + \
+               [(n, ctypes.c_void_p) for n in ("logits", "d_logits", "router_ws")] + \
+               [("router_ws_bytes", ctypes.c_size_t)]
 
 
 def _load():
@@ -80,6 +85,11 @@ def _load():
         "moe_forward": ([ctypes.POINTER(Problem), ctypes.POINTER(Tensors), vp, sz, vp], i),
         "moe_backward": ([ctypes.POINTER(Problem), ctypes.POINTER(Tensors), vp, vp, vp, vp, vp,
                           sz, vp], i),
+        "moe_router_logits": ([vp, vp, i, i, i, vp, vp], i),
+        "moe_combine_backward_router": ([vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp], i),
+        "moe_router_weight_grad_workspace_bytes": ([i, i, i], sz),
+        "moe_router_weight_grad": ([vp, vp, i, i, i, vp, vp, sz, vp], i),
+        "moe_dispatch_backward_router": ([vp, vp, vp, vp, vp, i, i, i, i, vp, vp], i),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -257,10 +267,66 @@ def moe_quantize_fp8_weights(w, q, scale, stream=None):
         _p(w), G, K, N, _p(q), _p(scale), _stream(stream)))
 
 
+def moe_router_logits(x, w_router, logits, stream=None):
+    T, H = x.shape
+    E = w_router.shape[0]
+    _want(x, torch.bfloat16, (T, H), "x")
+    _want(w_router, torch.bfloat16, (E, H), "w_router")
+    _want(logits, torch.float32, (T, E), "logits")
+    _check("moe_router_logits", _lib.moe_router_logits(
+        _p(x), _p(w_router), T, H, E, _p(logits), _stream(stream)))
+
+
+def moe_combine_backward_router(dy, expert_out, row_of, topk_idx, topk_prob, score, d_out,
+                                d_logits, d_prob=None, stream=None):
+    T, k = row_of.shape
+    H = dy.shape[1]
+    E = d_logits.shape[1]
+    _want(dy, torch.bfloat16, (T, H), "dy")
+    _want(expert_out, torch.bfloat16, (T * k, H), "expert_out")
+    _want(topk_idx, torch.int32, (T, k), "topk_idx")
+    _want(topk_prob, torch.float32, (T, k), "topk_prob")
+    _want(d_out, torch.bfloat16, (T * k, H), "d_out")
+    _want(d_logits, torch.float32, (T, E), "d_logits")
+    if d_prob is not None:
+        _want(d_prob, torch.float32, (T, k), "d_prob")
+    _check("moe_combine_backward_router", _lib.moe_combine_backward_router(
+        _p(dy), _p(expert_out), _p(row_of), _p(topk_idx), _p(topk_prob), T, H, E, k,
+        _score(score), _p(d_out), _p(d_prob), _p(d_logits), _stream(stream)))
+
+
+def moe_router_weight_grad_workspace_bytes(T, H, E):
+    return int(_lib.moe_router_weight_grad_workspace_bytes(T, H, E))
+
+
+def moe_router_weight_grad(x, d_logits, dw_router, ws, stream=None):
+    T, H = x.shape
+    E = d_logits.shape[1]
+    _want(x, torch.bfloat16, (T, H), "x")
+    _want(d_logits, torch.float32, (T, E), "d_logits")
+    _want(dw_router, torch.float32, (E, H), "dw_router")
+    _check("moe_router_weight_grad", _lib.moe_router_weight_grad(
+        _p(x), _p(d_logits), T, H, E, _p(dw_router), _p(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def moe_dispatch_backward_router(dxp, row_of, topk_idx, d_logits, w_router, dx, stream=None):
+    T, k = row_of.shape
+    E, H = w_router.shape
+    _want(dxp, torch.bfloat16, (T * k, H), "dxp")
+    _want(topk_idx, torch.int32, (T, k), "topk_idx")
+    _want(d_logits, torch.float32, (T, E), "d_logits")
+    _want(dx, torch.bfloat16, (T, H), "dx")
+    _check("moe_dispatch_backward_router", _lib.moe_dispatch_backward_router(
+        _p(dxp), _p(row_of), _p(topk_idx), _p(d_logits), _p(w_router), T, H, E, k, _p(dx),
+        _stream(stream)))
+
+
 # ---- whole layer -----------------------------------------------------------------------
 
-def problem(T, H, E, k, I, score, shared_I=0, dtype=MOE_BF16, training=False):
-    return Problem(T, H, E, k, I, shared_I, _score(score), dtype, int(bool(training)))
+def problem(T, H, E, k, I, score, shared_I=0, dtype=MOE_BF16, training=False, router=False):
+    return Problem(T, H, E, k, I, shared_I, _score(score), dtype, int(bool(training)),
+                   int(bool(router)))
 
 
 def moe_workspace_bytes(prob: Problem):
@@ -278,9 +344,9 @@ def moe_workspace_views(prob: Problem, ws):
 
 
 def tensors(x, logits, w_gu, w_down, y, w_gu_scale=None, w_down_scale=None, shared_gu=None,
-            shared_down=None):
+            shared_down=None, w_router=None, dw_router=None):
     return Tensors(_p(x), _p(logits), _p(w_gu), _p(w_gu_scale), _p(w_down), _p(w_down_scale),
-                   _p(shared_gu), _p(shared_down), _p(y))
+                   _p(shared_gu), _p(shared_down), _p(y), _p(w_router), _p(dw_router))
 
 
 def moe_forward(prob: Problem, tens: Tensors, ws, stream=None):

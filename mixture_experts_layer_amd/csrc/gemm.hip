@@ -230,7 +230,9 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   const int ntn = EPI == EPI_SWIGLU ? (p.I + HB - 1) / HB : (p.N + BN - 1) / BN;
 
   // ---- group offsets and tile count ----------------------------------------------
-  for (int g = tid; g <= p.G; g += C::NT) s_off[g] = p.offsets[g];
+  // no offsets: G groups split the rows evenly (split-K weight gradients)
+  for (int g = tid; g <= p.G; g += C::NT)
+    s_off[g] = p.offsets ? p.offsets[g] : (int)((long long)g * p.rows / p.G);
   __syncthreads();
   int total;
   if constexpr (!DW) {

@@ -35,6 +35,31 @@ hipError_t launch_quantize_rows(const void* x, int R, int C, uint8_t* q, float* 
 hipError_t launch_quantize_weights(const void* w, int G, int K, int N, uint8_t* q, float* scale,
                                    hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+// Dispatch backward with the router's dx term: dx[t] = sum_j dxp[row_of[t,j]] +
+// sum_j d_logits[t, topk_idx[t,j]] * w_router[topk_idx[t,j]], fp32 sum, one rounding.
+hipError_t launch_dispatch_bwd_router(const void* dxp, const int32_t* row_of,
+                                      const int32_t* topk_idx, const float* d_logits,
+                                      const void* w_router, int T, int H, int E, int k, void* dx,
+                                      hipStream_t s);
+
+// router_proj.hip
+hipError_t launch_router_logits(const void* x, const void* w_router, int T, int H, int E,
+                                float* logits, hipStream_t s);
+hipError_t launch_combine_bwd_router(const void* dy, const void* out, const int32_t* row_of,
+                                     const int32_t* topk_idx, const float* prob, int T, int H,
+                                     int E, int k, int score, void* d_out, float* d_prob,
+                                     float* d_logits, uint16_t* dls, int mp, hipStream_t s);
+hipError_t launch_router_wgrad_reduce(const float* part, int S, int E, int H, int mp, float* dw,
+                                      hipStream_t s);
+hipError_t launch_router_split(const float* d_logits, int T, int E, int mp, uint16_t* dls,
+                               hipStream_t s);
+// Columns of the split operand (hi and lo halves, padded to the GEMM's 64-column step)
+// and the number of K splits of the router weight-gradient GEMM.
+inline int router_split_cols(int E) { return (2 * E + 63) / 64 * 64; }
+inline int router_wgrad_splits(int T) {
+  const int s = T / 256;  // at least 256 rows per split
+  return s < 1 ? 1 : (s > 32 ? 32 : s);
+}
 
 // gemm.hip
 enum GemmEpi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2 };
@@ -47,7 +72,7 @@ struct GemmParams {
   const void* B;
   const float* a_scale;  // fp8: [rows]
   const float* b_scale;  // fp8: [G, Ncols]
-  const int32_t* offsets;
+  const int32_t* offsets;  // [G+1] device group boundaries; NULL: G even splits of rows
   int G, rows;
   int M, N, K;           // NN/NT: C[rows,N] = A[rows,K] B_g ; DW: C[g][M,N], K ragged
   void* C;

@@ -40,8 +40,17 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t topk_idx, topk_prob, counts, offsets, row_of, src_of, shared_offsets;
   size_t xp, xp_scale, gu, h, hq, h_scale, out, shared_h, shared_out;
-  size_t d_out, dgu, dxp, scratch, scratch_bytes, total;
+  size_t d_out, dgu, dxp, scratch, scratch_bytes;
+  size_t logits, d_logits, router_ws, router_ws_bytes, total;
 };
+
+// Scratch of the router weight gradient: the split d_logits operand [T, mp] bf16, then the
+// fp32 partial products [S, mp, H] of the K splits.
+size_t router_wgrad_dls_bytes(int T, int E) { return align_up((size_t)T * router_split_cols(E) * 2); }
+size_t router_wgrad_bytes(int T, int H, int E) {
+  return router_wgrad_dls_bytes(T, E) +
+         (size_t)router_wgrad_splits(T) * router_split_cols(E) * (size_t)H * 4;
+}
 
 Layout make_layout(const moe_problem_t& p) {
   Layout L{};
@@ -75,6 +84,10 @@ Layout make_layout(const moe_problem_t& p) {
   L.dxp = take(p.training ? N * p.H * 2 : 0);
   L.scratch_bytes = permute_scratch_bytes(p.T, p.E, p.k);
   L.scratch = take(L.scratch_bytes);
+  L.logits = take(p.router ? (size_t)p.T * p.E * 4 : 0);
+  L.d_logits = take(p.router && p.training ? (size_t)p.T * p.E * 4 : 0);
+  L.router_ws_bytes = p.router && p.training ? router_wgrad_bytes(p.T, p.H, p.E) : 0;
+  L.router_ws = take(L.router_ws_bytes);
   L.total = o;
   return L;
 }
@@ -89,11 +102,35 @@ moe_status_t check_problem(const moe_problem_t* p) {
     return MOE_ERR_UNSUPPORTED;
   if (p->score < MOE_SOFTMAX_PRE_RENORM || p->score > MOE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (p->router != 0 && p->router != 1) return MOE_ERR_INVALID_ARG;
   if (p->dtype == MOE_FP8_E4M3) {
     if (p->H % 128 || p->I % 128) return MOE_ERR_UNSUPPORTED;
     if (p->training || p->shared_I) return MOE_ERR_UNSUPPORTED;
   }
   return MOE_OK;
+}
+
+// dW_r = d_logits^T x from the split operand dls [T, mp] (hi | lo | 0): a ragged-K
+// weight-gradient GEMM over S even splits of the T rows into fp32 partials [S, mp, H],
+// then the fixed-order sum of the splits and of the two halves.
+hipError_t launch_router_wgrad(const void* x, const uint16_t* dls, int T, int H, int E,
+                               float* part, float* dw, hipStream_t s) {
+  const int mp = router_split_cols(E), S = router_wgrad_splits(T);
+  GemmParams r{};
+  r.mode = MOE_GEMM_TN_DW;
+  r.epi = EPI_STORE;
+  r.A = dls;
+  r.B = x;
+  r.offsets = nullptr;  // S even splits of the T rows
+  r.G = S;
+  r.rows = T;
+  r.M = mp;
+  r.N = H;
+  r.C = part;
+  r.c_fp32 = 1;
+  hipError_t e = launch_grouped_gemm(r, s);
+  if (e != hipSuccess) return e;
+  return launch_router_wgrad_reduce(part, S, E, H, mp, dw, s);
 }
 
 }  // namespace
@@ -282,6 +319,66 @@ moe_status_t moe_combine_backward(const void* dy, const int32_t* row_of, const f
   return hip_status(launch_scatter_rows(dy, row_of, topk_prob, T, H, k, d_out, S(stream)));
 }
 
+moe_status_t moe_router_logits(const void* x, const void* w_router, int T, int H, int E,
+                               float* logits, void* stream) {
+  moe_status_t st = check_shape(T, H, E, 1);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(w_router) || !ok_ptr(logits)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_router_logits(x, w_router, T, H, E, logits, S(stream)));
+}
+
+moe_status_t moe_combine_backward_router(const void* dy, const void* expert_out,
+                                         const int32_t* row_of, const int32_t* topk_idx,
+                                         const float* topk_prob, int T, int H, int E, int k,
+                                         int score, void* d_out, float* d_prob, float* d_logits,
+                                         void* stream) {
+  moe_status_t st = check_shape(T, H, E, k);
+  if (st != MOE_OK) return st;
+  if (score < MOE_SOFTMAX_PRE_RENORM || score > MOE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(dy) || !ok_ptr(expert_out) || !ok_ptr(row_of) || !ok_ptr(topk_idx) ||
+      !ok_ptr(topk_prob) || !ok_ptr(d_out) || !opt_ptr(d_prob) || !ok_ptr(d_logits))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine_bwd_router(dy, expert_out, row_of, topk_idx, topk_prob, T, H, E,
+                                              k, score, d_out, d_prob, d_logits, nullptr, 0,
+                                              S(stream)));
+}
+
+size_t moe_router_weight_grad_workspace_bytes(int T, int H, int E) {
+  if (check_shape(T, H, E, 1) != MOE_OK) return 0;
+  return router_wgrad_bytes(T, H, E);
+}
+
+moe_status_t moe_router_weight_grad(const void* x, const float* d_logits, int T, int H, int E,
+                                    float* dw_router, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_shape(T, H, E, 1);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(dw_router) || !ok_ptr(ws)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!ok_ptr(x) || !ok_ptr(d_logits))) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < router_wgrad_bytes(T, H, E)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = S(stream);
+  uint16_t* dls = (uint16_t*)ws;
+  MOE_TRY(launch_router_split(d_logits, T, E, router_split_cols(E), dls, s));
+  return hip_status(launch_router_wgrad(x, dls, T, H, E,
+                                        (float*)((uint8_t*)ws + router_wgrad_dls_bytes(T, E)),
+                                        dw_router, s));
+}
+
+moe_status_t moe_dispatch_backward_router(const void* dxp, const int32_t* row_of,
+                                          const int32_t* topk_idx, const float* d_logits,
+                                          const void* w_router, int T, int H, int E, int k,
+                                          void* dx, void* stream) {
+  moe_status_t st = check_shape(T, H, E, k);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(dxp) || !ok_ptr(row_of) || !ok_ptr(topk_idx) || !ok_ptr(d_logits) ||
+      !ok_ptr(w_router) || !ok_ptr(dx))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_dispatch_bwd_router(dxp, row_of, topk_idx, d_logits, w_router, T, H, E,
+                                               k, dx, S(stream)));
+}
+
 moe_status_t moe_quantize_fp8_rows(const void* x, int R, int C, uint8_t* q, float* scale,
                                    void* stream) {
   if (R < 0 || C <= 0) return MOE_ERR_INVALID_ARG;
@@ -333,6 +430,10 @@ moe_status_t moe_workspace_views(const moe_problem_t* p, void* ws, size_t ws_byt
   v->dxp = p->training ? b + L.dxp : nullptr;
   v->scratch = b + L.scratch;
   v->scratch_bytes = L.scratch_bytes;
+  v->logits = p->router ? (float*)(b + L.logits) : nullptr;
+  v->d_logits = p->router && p->training ? (float*)(b + L.d_logits) : nullptr;
+  v->router_ws = L.router_ws_bytes ? b + L.router_ws : nullptr;
+  v->router_ws_bytes = L.router_ws_bytes;
   return MOE_OK;
 }
 
@@ -343,9 +444,9 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   if (!t) return MOE_ERR_INVALID_ARG;
   if (p->T == 0) return MOE_OK;
   const bool fp8 = p->dtype == MOE_FP8_E4M3;
-  if (!ok_ptr(t->x) || !ok_ptr(t->logits) || !ok_ptr(t->w_gu) || !ok_ptr(t->w_down) ||
-      !ok_ptr(t->y))
+  if (!ok_ptr(t->x) || !ok_ptr(t->w_gu) || !ok_ptr(t->w_down) || !ok_ptr(t->y))
     return MOE_ERR_INVALID_ARG;
+  if (p->router ? !ok_ptr(t->w_router) : !ok_ptr(t->logits)) return MOE_ERR_INVALID_ARG;
   if (fp8 && (!ok_ptr(t->w_gu_scale) || !ok_ptr(t->w_down_scale))) return MOE_ERR_INVALID_ARG;
   if (p->shared_I && (!ok_ptr(t->shared_gu) || !ok_ptr(t->shared_down)))
     return MOE_ERR_INVALID_ARG;
@@ -356,9 +457,15 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   const int T = p->T, H = p->H, E = p->E, k = p->k, I = p->I;
   const int N = T * k;
 
-  // 1. router, writing per-chunk expert histograms (no atomics)
+  // 1. router (projection first when the layer owns it), writing per-chunk expert
+  //    histograms (no atomics)
+  const float* logits = t->logits;
+  if (p->router) {
+    MOE_TRY(launch_router_logits(t->x, t->w_router, T, H, E, v.logits, s));
+    logits = v.logits;
+  }
   const int chunk_tokens = router_chunk_tokens(T);
-  MOE_TRY(launch_router_hist(t->logits, T, E, k, p->score, v.topk_idx, v.topk_prob,
+  MOE_TRY(launch_router_hist(logits, T, E, k, p->score, v.topk_idx, v.topk_prob,
                              (int32_t*)v.scratch, chunk_tokens, s));
   // 2. dispatch: counts, offsets, row maps from the histograms, then the row copies
   MOE_TRY(launch_dispatch_from_hist(v.topk_idx, T, E, k, chunk_tokens, (int32_t*)v.scratch,
@@ -467,6 +574,8 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   if (!ok_ptr(t->w_gu) || !ok_ptr(t->w_down) || !ok_ptr(dw_gu) || !ok_ptr(dw_down))
     return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && (!ok_ptr(dy) || !ok_ptr(dx))) return MOE_ERR_INVALID_ARG;
+  if (p->router && (!ok_ptr(t->w_router) || !ok_ptr(t->dw_router) || !ok_ptr(t->x)))
+    return MOE_ERR_INVALID_ARG;
   moe_views_t v;
   st = moe_workspace_views(p, ws, ws_bytes, &v);
   if (st != MOE_OK) return st;
@@ -476,10 +585,20 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   if (T == 0) {
     // no routed rows: the weight gradients are zero (the dW GEMMs see empty groups)
     MOE_TRY(launch_fill_i32(v.offsets, E + 1, 0, s));
+  } else if (p->router) {
+    // combine backward with the routing-weight gradient: d_out, d_logits and the split
+    // operand of the router weight gradient
+    MOE_TRY(launch_combine_bwd_router(dy, v.out, v.row_of, v.topk_idx, v.topk_prob, T, H, E, k,
+                                      p->score, v.d_out, nullptr, v.d_logits,
+                                      (uint16_t*)v.router_ws, router_split_cols(E), s));
   } else {
     // combine backward: d_out[row_of[t,j]] = bf16(p[t,j] * dy[t])
     MOE_TRY(launch_scatter_rows(dy, v.row_of, v.topk_prob, T, H, k, v.d_out, s));
   }
+  if (p->router)
+    MOE_TRY(launch_router_wgrad(t->x, (const uint16_t*)v.router_ws, T, H, E,
+                                (float*)((uint8_t*)v.router_ws + router_wgrad_dls_bytes(T, E)),
+                                t->dw_router, s));
   // GEMM2 backward: dgu = SwiGLU'(d_out . W_down^T), dW_down = h^T . d_out
   GemmParams a{};
   a.mode = MOE_GEMM_NT;
@@ -532,8 +651,12 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   d.N = 2 * I;
   d.C = dw_gu;
   MOE_TRY(launch_grouped_gemm(d, s));
-  // dispatch backward: dx[t] = sum_j dxp[row_of[t,j]]
-  MOE_TRY(launch_combine(v.dxp, v.row_of, nullptr, nullptr, T, H, k, dx, s));
+  // dispatch backward: dx[t] = sum_j dxp[row_of[t,j]] (+ the router's term)
+  if (p->router)
+    MOE_TRY(launch_dispatch_bwd_router(v.dxp, v.row_of, v.topk_idx, v.d_logits, t->w_router, T, H,
+                                       E, k, dx, s));
+  else
+    MOE_TRY(launch_combine(v.dxp, v.row_of, nullptr, nullptr, T, H, k, dx, s));
   return MOE_OK;
 }
 

@@ -402,17 +402,30 @@ hipError_t launch_quantize_weights(const void* w, int G, int K, int N, uint8_t* 
 
 // y[t] = sum_j p[t,j] * y_perm[row_of[t,j]] (+ shared[t]); fp32 sum in slot order, one
 // rounding to bf16. prob == NULL gives the unweighted sum used by the dispatch backward.
+// ROUTER (dispatch backward of a layer that owns its router projection): the router's dx
+// term sum_j d_logits[t, e_j] * W_r[e_j] over the kept experts e_j is added after the k
+// rows, before the rounding (the other experts' d_logits are 0).
+template <bool ROUTER>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict__ yp,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ prob,
                                                       const u32x4_t* __restrict__ shared, int H8,
-                                                      int k, u32x4_t* __restrict__ y) {
-  __shared__ int rows[32];
-  __shared__ float p[32];
+                                                      int k, u32x4_t* __restrict__ y,
+                                                      const int32_t* __restrict__ topk_idx = nullptr,
+                                                      const float* __restrict__ d_logits = nullptr,
+                                                      const u32x4_t* __restrict__ w_router = nullptr,
+                                                      int E = 0) {
+  __shared__ int rows[32], ids[32];
+  __shared__ float p[32], dl[32];
   const int t = blockIdx.x;
   if ((int)threadIdx.x < k) {
     rows[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
     p[threadIdx.x] = prob ? prob[(size_t)t * k + threadIdx.x] : 1.f;
+    if constexpr (ROUTER) {
+      const int e = topk_idx[(size_t)t * k + threadIdx.x];
+      ids[threadIdx.x] = e;
+      dl[threadIdx.x] = d_logits[(size_t)t * E + e];
+    }
   }
   __syncthreads();
   for (int v = threadIdx.x; v < H8; v += blockDim.x) {
@@ -437,6 +450,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict_
         }
       }
     }
+    if constexpr (ROUTER) {
+      for (int j = 0; j < k; ++j) {
+        const u32x4_t wv = w_router[(size_t)ids[j] * H8 + v];
+        const float g = dl[j];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          acc[2 * d] = fmaf(g, bf16lo(wv[d]), acc[2 * d]);
+          acc[2 * d + 1] = fmaf(g, bf16hi(wv[d]), acc[2 * d + 1]);
+        }
+      }
+    }
     if (shared) {
       const u32x4_t sv = shared[(size_t)t * H8 + v];
 #pragma unroll
@@ -455,8 +479,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict_
 hipError_t launch_combine(const void* y_perm, const int32_t* row_of, const float* prob,
                           const void* shared, int T, int H, int k, void* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  combine_kernel<<<T, 256, 0, s>>>((const u32x4_t*)y_perm, row_of, prob, (const u32x4_t*)shared,
-                                   H / 8, k, (u32x4_t*)y);
+  combine_kernel<false><<<T, 256, 0, s>>>((const u32x4_t*)y_perm, row_of, prob,
+                                          (const u32x4_t*)shared, H / 8, k, (u32x4_t*)y);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_bwd_router(const void* dxp, const int32_t* row_of,
+                                      const int32_t* topk_idx, const float* d_logits,
+                                      const void* w_router, int T, int H, int E, int k, void* dx,
+                                      hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  combine_kernel<true><<<T, 256, 0, s>>>((const u32x4_t*)dxp, row_of, nullptr, nullptr, H / 8, k,
+                                         (u32x4_t*)dx, topk_idx, d_logits,
+                                         (const u32x4_t*)w_router, E);
   return hipGetLastError();
 }
 

@@ -84,13 +84,17 @@ def check_fp8(got, ref, name, rel_l2=5e-2):
 class GpuMoE:
     """Uploads one workload's inputs and runs moe_forward / moe_backward through the C ABI."""
 
-    def __init__(self, w, d, training=None, canary=True):
+    def __init__(self, w, d, training=None, canary=True, router=False):
         self.w, self.d = w, d
         T = d["T"]
         self.T = T
         self.training = w.training if training is None else training
+        self.router = router
         self.dtype = M.MOE_FP8_E4M3 if w.fp8 else M.MOE_BF16
-        self.prob = M.problem(T, w.H, w.E, w.k, w.I, w.score, w.shared_I, self.dtype, self.training)
+        self.prob = M.problem(T, w.H, w.E, w.k, w.I, w.score, w.shared_I, self.dtype, self.training,
+                              router)
+        self.w_router = dev_bf16(d["w_router"]) if router else None
+        self.dw_router = torch.full((w.E, w.H), float("nan"), device="cuda") if router else None
         self.x = dev_bf16(d["x"])
         self.logits = dev(d["logits"])
         self.w_gu = dev_bf16(d["w_gu"])
@@ -115,7 +119,8 @@ class GpuMoE:
         self.views = M.moe_workspace_views(self.prob, self.ws)
         self.tens = M.tensors(self.x, self.logits, self.w_gu_q if w.fp8 else self.w_gu,
                               self.w_down_q if w.fp8 else self.w_down, self.y,
-                              self.w_gu_scale, self.w_down_scale, self.shared_gu, self.shared_down)
+                              self.w_gu_scale, self.w_down_scale, self.shared_gu, self.shared_down,
+                              self.w_router, self.dw_router)
 
     def forward(self):
         M.moe_forward(self.prob, self.tens, self.ws)
@@ -146,3 +151,30 @@ class GpuMoE:
             row_of=self.view("row_of", (T, w.k), torch.int32).cpu().numpy(),
             src_of=self.view("src_of", (T * w.k,), torch.int32).cpu().numpy(),
         )
+
+
+def fp32_sum_bound(a_abs, b_abs_t, n):
+    """Bound on the error of fp32 sums of n exact products: n * 2^-24 * sum |a b| per
+    element (a_abs [R, n] @ b_abs_t [n, C]), the classic recursive-summation bound."""
+    return n * 2.0 ** -24 * (np.asarray(a_abs, np.float64) @ np.asarray(b_abs_t, np.float64))
+
+
+def check_close(got, ref, bound, name, floor=0.0):
+    """Elementwise |got - ref| <= bound (+ floor); prints the worst ratio."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    diff = np.abs(got - ref)
+    lim = np.asarray(bound, np.float64) + floor
+    ratio = (diff / np.maximum(lim, 1e-300)).max() if diff.size else 0.0
+    print(f"{name}: max_abs={diff.max() if diff.size else 0:.3e} worst diff/bound={ratio:.3e}")
+    assert (diff <= lim).all(), f"{name}: worst diff/bound {ratio:.3e}"
+
+
+def topk_gap(logits, k):
+    """Per token, the gap between the k-th and (k+1)-th largest logit (inf when k == E)."""
+    s = -np.sort(-np.asarray(logits, np.float64), axis=1)
+    if k >= s.shape[1]:
+        return np.full(s.shape[0], np.inf)
+    return s[:, k - 1] - s[:, k]

@@ -76,3 +76,15 @@ def test_gemm_size_limits_answer_before_device_work(lib):
     sw.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 3
     assert sw(None, None, None, None, None, 8, 16, 32768, 32768, BF16, None, None, None) == 2
     assert sw(None, None, None, None, None, 8, 16, 32704, 32768, BF16, None, None, None) == 1
+
+
+def test_router_entry_points_validate_on_the_host(lib):
+    lib.moe_router_weight_grad_workspace_bytes.restype = ctypes.c_size_t
+    # split operand [T, 2E padded to 64] bf16 plus 16 K splits of [2E.., H] fp32 partials
+    assert lib.moe_router_weight_grad_workspace_bytes(4096, 2048, 128) == 4096 * 256 * 2 + 16 * 256 * 2048 * 4
+    assert lib.moe_router_weight_grad_workspace_bytes(4096, 100, 128) == 0   # H % 64
+    assert lib.moe_router_weight_grad_workspace_bytes(64, 128, 300) == 0     # E > 256
+    # null pointers and unsupported sizes answer before any device work
+    assert lib.moe_router_logits(None, None, 8, 128, 4, None, None) == 1
+    assert lib.moe_router_logits(None, None, 8, 100, 4, None, None) == 2
+    assert lib.moe_dispatch_backward_router(None, None, None, None, None, 8, 128, 4, 2, None, None) == 1

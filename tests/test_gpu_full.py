@@ -15,7 +15,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_helpers import GpuMoE, check_bf16, check_fp8, combine_slack, host_vals
+from gpu_helpers import (GpuMoE, check_bf16, check_close, check_fp8, combine_slack,
+                         fp32_sum_bound, host_vals, topk_gap)
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +104,51 @@ def test_backward_full_size_qwen3():
         check_bf16(host_vals(g.dw_gu[e]), rb["dw_gu"][e], f"qwen3 dw_gu[{e}]")
     # no NaN canary survives anywhere in the weight gradients
     assert torch.isfinite(g.dw_gu).all().item() and torch.isfinite(g.dw_down).all().item()
+
+
+def test_router_full_size_qwen3():
+    """The Qwen3-shaped layer with its own router projection, forward + backward."""
+    w = W.WORKLOADS["qwen3"]
+    _say("full router qwen3")
+    d = _inputs("qwen3")
+    g = GpuMoE(w, d, router=True)
+    g.forward()
+    g.backward(d["dy"])
+    # whole logits against the oracle's, within the fp32 summation bound
+    ref_logits = O.gate_logits(d["x"], d["w_router"])
+    xa, wa = np.abs(O.as_values(d["x"])), np.abs(O.as_values(d["w_router"]))
+    bound = fp32_sum_bound(xa, wa.T, w.H) + 2.0 ** -24 * np.abs(ref_logits)
+    check_close(host_vals(g.view("logits", (w.T, w.E), torch.float32)), ref_logits, bound,
+                "qwen3 logits")
+    # every token whose top-k is decided by more than twice the bound must match
+    firm = topk_gap(ref_logits, w.k) > 2 * bound.max(axis=1)
+    idx = O.topk_select(ref_logits, w.k)
+    ints = g.ints()
+    _say("tokens with a near-tie:", int((~firm).sum()))
+    assert np.array_equal(ints["topk_idx"][firm], idx[firm])
+    # sampled tokens: dx and d_logits rows
+    S = _sample(w.T, seed=2, n=32)
+    S = S[firm[S]]
+    ref = O.moe_forward(d["x"][S], ref_logits[S], d["w_gu"], d["w_down"], w.k, w.score, w.I)
+    rb = O.moe_backward(ref, d["dy"][S], d["w_gu"], d["w_down"], w.I, w_router_bits=d["w_router"])
+    check_bf16(host_vals(g.dx)[S], rb["dx"], "qwen3 dx[sample] (router)",
+               slack=combine_slack(rb["dxp"], ref["row_of"]))
+    dl = host_vals(g.view("d_logits", (w.T, w.E), torch.float32))
+    rel = np.linalg.norm(dl[S] - rb["d_logits"]) / np.linalg.norm(rb["d_logits"])
+    _say(f"qwen3 d_logits[sample]: rel_l2={rel:.3e}")
+    assert rel <= 1e-2
+    # sampled experts: dW_r[e] sums over the tokens routed to e only
+    dwr = host_vals(g.dw_router)
+    assert np.isfinite(dwr).all()
+    for e in (5, 90):
+        toks = np.nonzero((idx == e).any(axis=1))[0]
+        if not firm[toks].all():
+            continue
+        _say("router expert", e, "tokens", toks.size)
+        ref = O.moe_forward(d["x"][toks], ref_logits[toks], d["w_gu"], d["w_down"], w.k, w.score, w.I)
+        rb = O.moe_backward(ref, d["dy"][toks], d["w_gu"], d["w_down"], w.I,
+                            w_router_bits=d["w_router"])
+        r = O.to_f32(rb["d_logits"][:, e] @ O.as_values(d["x"][toks]))
+        rel = np.linalg.norm(dwr[e] - r) / np.linalg.norm(r)
+        _say(f"qwen3 dw_router[{e}]: rel_l2={rel:.3e}")
+        assert rel <= 1e-2
