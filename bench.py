@@ -52,17 +52,31 @@ def stage_costs(w, training, active=None):
     return c
 
 
-def row_costs(w, training):
-    """Algorithmic bytes of the row-movement launches."""
-    T, N, H, k = w.T, w.T * w.k, w.H, w.k
+def row_costs(w, training, router=False):
+    """Algorithmic bytes of the row-movement launches (with the router projection, the
+    combine backward also reads the expert outputs and writes d_logits, and the dispatch
+    backward also reads d_logits and the router weight)."""
+    T, N, H, k, E = w.T, w.T * w.k, w.H, w.k, w.E
     act = 1 if w.fp8 else 2
     c = {
         "permute_scatter": T * H * 2 + N * H * act + T * k * 4,
         "combine": N * H * 2 + T * k * 8 + T * H * 2,
     }
-    if training:
+    if training and not router:
         c["combine_bwd"] = T * H * 2 + T * k * 8 + N * H * 2
         c["dispatch_bwd"] = N * H * 2 + T * k * 4 + T * H * 2
+    if training and router:
+        c["combine_bwd_router"] = T * H * 2 + 2 * N * H * 2 + T * k * 12 + T * E * 4
+        c["dispatch_bwd_router"] = N * H * 2 + T * k * 8 + E * H * 2 + T * H * 2
+    return c
+
+
+def router_costs(w, training):
+    """Algorithmic FLOPs and bytes of the router projection and its weight gradient."""
+    T, H, E = w.T, w.H, w.E
+    c = {"router_logits": (2.0 * T * H * E, T * H * 2 + E * H * 2 + T * E * 4)}
+    if training:
+        c["router_wgrad"] = (2.0 * T * H * E, T * E * 4 + T * H * 2 + E * H * 4)
     return c
 
 
@@ -162,6 +176,9 @@ def main():
     ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=False,
                     help="time replays of the step captured in a HIP graph instead of eager "
                          "launches (measured no faster: the host stays ahead of the GPU)")
+    ap.add_argument("--router", action="store_true",
+                    help="the layer owns its router projection: logits = x . W_r^T in the "
+                         "forward, d_logits, dW_r and the router's dx term in the backward")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch each stage once plus a 256 MiB calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -206,9 +223,13 @@ def main():
         M.moe_quantize_fp8_weights(w_down, dq, w_down_s)
         w_gu, w_down = wq, dq
     y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
-    prob = M.problem(w.T, w.H, w.E, w.k, w.I, w.score, w.shared_I, dtype, training)
+    router = args.router
+    w_router = bf(d["w_router"]) if router else None
+    dw_router = torch.empty((w.E, w.H), dtype=torch.float32, device=dev) if router else None
+    prob = M.problem(w.T, w.H, w.E, w.k, w.I, w.score, w.shared_I, dtype, training, router)
     ws = torch.zeros(M.moe_workspace_bytes(prob), dtype=torch.uint8, device=dev)
-    tens = M.tensors(x, logits, w_gu, w_down, y, w_gu_s, w_down_s, shared_gu, shared_down)
+    tens = M.tensors(x, None if router else logits, w_gu, w_down, y, w_gu_s, w_down_s, shared_gu,
+                     shared_down, w_router, dw_router)
     if training:
         dy = bf(d["dy"])
         dx = torch.empty_like(x)
@@ -292,13 +313,29 @@ def main():
         dgu = vt("dgu", (N, 2 * I), torch.bfloat16)
         dxp = vt("dxp", (N, H), torch.bfloat16)
         launches.update({
-            "combine_bwd": lambda: M.moe_combine_backward(dy, row_of, topk_prob, d_out),
+            **({} if router else {
+                "combine_bwd": lambda: M.moe_combine_backward(dy, row_of, topk_prob, d_out)}),
             "gemm2_bwd_swiglu": lambda: M.moe_grouped_gemm_swiglu_bwd(d_out, w_down, offs, gu, dgu),
             "dw_down": lambda: M.moe_grouped_gemm(M.MOE_GEMM_TN_DW, h, d_out, offs, dw_down),
             "gemm1_bwd_dx": lambda: M.moe_grouped_gemm(M.MOE_GEMM_NT, dgu, w_gu, offs, dxp),
             "dw_gu": lambda: M.moe_grouped_gemm(M.MOE_GEMM_TN_DW, xp, dgu, offs, dw_gu),
-            "dispatch_bwd": lambda: M.moe_unpermute_combine(dxp, row_of, None, dx),
+            **({} if router else {
+                "dispatch_bwd": lambda: M.moe_unpermute_combine(dxp, row_of, None, dx)}),
         })
+    if router:
+        r_logits = vt("logits", (T, E), torch.float32)
+        launches["router_logits"] = lambda: M.moe_router_logits(x, w_router, r_logits)
+        if training:
+            d_logits = vt("d_logits", (T, E), torch.float32)
+            rws = torch.empty(M.moe_router_weight_grad_workspace_bytes(T, H, E), dtype=torch.uint8,
+                              device=dev)
+            launches.update({
+                "combine_bwd_router": lambda: M.moe_combine_backward_router(
+                    dy, out, row_of, idx_t, topk_prob, w.score, d_out, d_logits),
+                "router_wgrad": lambda: M.moe_router_weight_grad(x, d_logits, dw_router, rws),
+                "dispatch_bwd_router": lambda: M.moe_dispatch_backward_router(
+                    dxp, row_of, idx_t, d_logits, w_router, dx),
+            })
     if args.pmc_pass:
         for name in GEMM_STAGES:
             if name in launches:
@@ -339,11 +376,18 @@ def main():
     gemm_flops = sum(fl for fl, _ in costs.values())
     gemm_time = sum(kernel_us[n] for n in costs) * 1e-6
     rows = {}
-    for name, by in row_costs(w, training).items():
+    for name, by in row_costs(w, training, router).items():
         key = "permute" if name == "permute_scatter" else name
         t = kernel_us[key] * 1e-6
         rows[name] = {"us": round(kernel_us[key], 2), "gbs": round(by / t / 1e9, 1),
                       "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+    rtr = {}
+    if router:
+        for name, (fl, by) in router_costs(w, training).items():
+            t = kernel_us[name] * 1e-6
+            rtr[name] = {"us": round(kernel_us[name], 2), "tflops": round(fl / t / 1e12, 1),
+                         "gbs": round(by / t / 1e9, 1), "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
 
     # dominant kernel: the GEMM launch with the longest duration
     dom = max(costs, key=lambda n: kernel_us[n])
@@ -369,10 +413,12 @@ def main():
         S = min(args.cpu_sample_tokens, w.T)
         _log(f"bench: timing the CPU oracle on {S} tokens")
         tc0 = time.perf_counter()
-        r = O.moe_forward(d["x"][:S], d["logits"][:S], d["w_gu"], d["w_down"], w.k, w.score,
+        lg = O.gate_logits(d["x"][:S], d["w_router"]) if router else d["logits"][:S]
+        r = O.moe_forward(d["x"][:S], lg, d["w_gu"], d["w_down"], w.k, w.score,
                           w.I, d.get("shared_gu"), d.get("shared_down"), fp8=w.fp8)
         if training:
-            O.moe_backward(r, d["dy"][:S], d["w_gu"], d["w_down"], w.I)
+            O.moe_backward(r, d["dy"][:S], d["w_gu"], d["w_down"], w.I,
+                           w_router_bits=d["w_router"] if router else None)
         tc = time.perf_counter() - tc0
         threads = max([p.get("num_threads", 1) for p in threadpool_info()
                        if p.get("user_api") == "blas"] or [1])
@@ -395,15 +441,17 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8" if w.fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}-shaped MoE block " + ("forward+backward" if training else "forward"),
+        "config": {"workload": f"{w.name}-shaped MoE block " + ("with its router projection " if router else "")
+                   + ("forward+backward" if training else "forward"),
                    "T": w.T, "H": w.H, "E": w.E, "top_k": w.k, "I": w.I, "shared_I": w.shared_I,
                    "score": ["softmax_pre_renorm", "softmax_post", "sigmoid"][w.score],
                    "parallelism": "single GPU", "active_experts": active,
-                   "launch": "hip_graph" if graph is not None else "eager"},
+                   "launch": "hip_graph" if graph is not None else "eager", "router": router},
         "grouped_gemm_tflops": round(gemm_flops / gemm_time / 1e12, 1),
         "grouped_gemm_mfma_frac": round(gemm_flops / gemm_time / 1e12 / peak_tf, 4),
         "gemm": gemm,
         "rows": rows,
+        **({"router": rtr} if router else {}),
         "kernel_us": {k_: round(v_, 2) for k_, v_ in kernel_us.items()},
         "roofline": roof,
         "cpu_baseline": cpu,

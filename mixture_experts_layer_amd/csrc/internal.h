@@ -56,8 +56,11 @@ hipError_t launch_router_split(const float* d_logits, int T, int E, int mp, uint
 // Columns of the split operand (hi and lo halves, padded to the GEMM's 64-column step)
 // and the number of K splits of the router weight-gradient GEMM.
 inline int router_split_cols(int E) { return (2 * E + 63) / 64 * 64; }
+#ifndef MOE_ROUTER_SPLIT_ROWS
+#define MOE_ROUTER_SPLIT_ROWS 256
+#endif
 inline int router_wgrad_splits(int T) {
-  const int s = T / 256;  // at least 256 rows per split
+  const int s = T / MOE_ROUTER_SPLIT_ROWS;  // at least that many rows per split
   return s < 1 ? 1 : (s > 32 ? 32 : s);
 }
 

@@ -19,61 +19,114 @@
 namespace moe {
 
 // ---- logits = x . W_r^T ------------------------------------------------------------
-// One block per 32 tokens, four waves; wave w owns the 32-expert blocks w and w+4
-// (E <= 256). Both operands are K-contiguous, so each lane loads its 16-byte MFMA
-// fragment (8 bf16 of one row) straight from memory: the token rows stream from HBM once
-// per block, the router weight (E*H*2 bytes) is served from L2.
-// v_mfma_f32_32x32x16_bf16 with the weight fragment as the first operand: lane l holds
-// token row l%32 and experts 8*(v/4) + 4*(l/32) + v%4 of its 32-expert block.
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ w, int T,
-                                                            int H, int E,
-                                                            float* __restrict__ logits) {
+// One block per 16 tokens and 16*NB experts (blockIdx.y picks the expert range; NB is the
+// power of two that covers E, at most 8), eight waves splitting K: wave w multiplies the
+// pairs of 32-wide K chunks w, w+8, ... for every 16-expert tile of the block, and the
+// eight partial tiles are summed in LDS in wave order (deterministic).
+// Both operands are K-contiguous and are loaded straight into registers: lane l reads 16
+// bytes of row l/4 (piece l%4 of the row's 64-byte K chunk), so every quad of lanes reads
+// one contiguous 64-byte segment, and one ds_bpermute per dword then moves piece p of row
+// r to lane r + 16p, the MFMA operand layout. The two chunks of a pair use two fragment
+// sets in turn, each reloaded with the next pair as soon as it has been multiplied, so one
+// set's loads are in flight while the other multiplies; every load is unconditional (the
+// prefetch past the last pair re-reads it), so the compiler waits for exactly the set in
+// use. The token rows stream from HBM once; the router weight (E*H*2 bytes) comes from L2,
+// once per 16 tokens (blocks of 32 or 64 tokens, which read it less often, measured
+// slower: half or a quarter of the blocks, and the same wave-serial load chain).
+// v_mfma_f32_16x16x32_bf16 with the weight fragment as the first operand: lane l holds
+// token l%16 and experts 4*(l/16) + q, q < 4, of its tile.
+constexpr int kLogitWaves = 8;
+template <int NB>
+__global__ __launch_bounds__(kLogitWaves * 64) void router_logits_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T, int H, int E,
+    float* __restrict__ logits) {
+  constexpr int MT = 1;  // 16-token tiles per block
+  __shared__ float red[kLogitWaves][16][16 * NB + 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 32;
-  const int r = lane & 31, kq = (lane >> 5) * 8;
-  const int tm = min(t0 + r, T - 1);  // rows past T read the last row; never stored
-  const bf16x8_t* xa = (const bf16x8_t*)(x + (size_t)tm * H + kq);
-  const bool live0 = wave * 32 < E, live1 = (wave + 4) * 32 < E;  // wave-uniform
-  const int n0 = min(wave * 32 + r, E - 1), n1 = min((wave + 4) * 32 + r, E - 1);
-  const bf16x8_t* wb0 = (const bf16x8_t*)(w + (size_t)n0 * H + kq);
-  const bf16x8_t* wb1 = (const bf16x8_t*)(w + (size_t)n1 * H + kq);
-  f32x16_t acc0 = {}, acc1 = {};
-  if (!live0) return;
-  // H % 64 == 0: four 16-wide K steps per iteration, loads issued before the multiplies
-  for (int k = 0; k < H; k += 64) {
-    bf16x8_t a[4], b0[4], b1[4];
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16 * NB;
+  // rows past T or E read the last row; their results are never stored
+  const int lr = lane >> 2, lp = (lane & 3) * 8;
+  const int src = (4 * (lane & 15) + (lane >> 4)) * 4;  // byte address of the source lane
+  const uint16_t* xa[MT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) a[s] = xa[(k + 16 * s) / 8];
+  for (int m = 0; m < MT; ++m) xa[m] = x + (size_t)min(t0 + 16 * m + lr, T - 1) * H + lp;
+  const uint16_t* wb[NB];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) b0[s] = wb0[(k + 16 * s) / 8];
-    if (live1) {
+  for (int j = 0; j < NB; ++j) wb[j] = w + (size_t)min(e0 + 16 * j + lr, E - 1) * H + lp;
+  auto perm = [&](const bf16x8_t& v) __attribute__((always_inline)) -> bf16x8_t {
+    typedef __attribute__((ext_vector_type(4))) int i4;
+    i4 u = __builtin_bit_cast(i4, v), o;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) b1[s] = wb1[(k + 16 * s) / 8];
+    for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_ds_bpermute(src, u[d]);
+    return __builtin_bit_cast(bf16x8_t, o);
+  };
+  f32x4_t acc[MT][NB];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bf16x8_t a0[MT], b0[NB], a1[MT], b1[NB];
+  auto load = [&](int c, bf16x8_t* a, bf16x8_t* b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) a[m] = *(const bf16x8_t*)(xa[m] + 32 * c);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) b[j] = *(const bf16x8_t*)(wb[j] + 32 * c);
+  };
+  auto mul = [&](const bf16x8_t* a, const bf16x8_t* b) __attribute__((always_inline)) {
+    bf16x8_t ap[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) ap[m] = perm(a[m]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const bf16x8_t bp = perm(b[j]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bp, ap[m], acc[m][j], 0, 0, 0);
     }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0[s], a[s], acc0, 0, 0, 0);
-    if (live1) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1[s], a[s], acc1, 0, 0, 0);
+  };
+  const int npair = H / 64;  // H % 64 == 0
+  if (wave < npair) {
+    load(2 * wave, a0, b0);
+    load(2 * wave + 1, a1, b1);
+    for (int p = wave; p < npair; p += kLogitWaves) {
+      const int pn = min(p + kLogitWaves, npair - 1);
+      // scheduling barriers keep each set's loads right after its multiplies (the
+      // scheduler would otherwise sink them next to their use, one latency per pair)
+      mul(a0, b0);
+      load(2 * pn, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(a1, b1);
+      load(2 * pn + 1, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if (t0 + r >= T) return;
-  float* row = logits + (size_t)(t0 + r) * E;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int e = 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
-    if (wave * 32 + e < E) row[wave * 32 + e] = acc0[v];
-    if (live1 && (wave + 4) * 32 + e < E) row[(wave + 4) * 32 + e] = acc1[v];
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[wave][lane & 15][16 * j + 4 * (lane >> 4) + q] = acc[0][j][q];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 16 * 16 * NB; i += kLogitWaves * 64) {
+    const int tr = i / (16 * NB), col = i % (16 * NB);
+    float v = red[0][tr][col];
+#pragma unroll
+    for (int ww = 1; ww < kLogitWaves; ++ww) v += red[ww][tr][col];
+    if (t0 + tr < T && e0 + col < E) logits[(size_t)(t0 + tr) * E + e0 + col] = v;
   }
 }
 
 hipError_t launch_router_logits(const void* x, const void* w_router, int T, int H, int E,
                                 float* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  router_logits_kernel<<<(T + 31) / 32, 256, 0, s>>>((const uint16_t*)x, (const uint16_t*)w_router,
-                                                     T, H, E, logits);
-  return hipGetLastError();
+  const unsigned bx = (T + 15) / 16;
+  auto go = [&](auto kern, int nb) {
+    kern<<<dim3(bx, (E + 16 * nb - 1) / (16 * nb)), kLogitWaves * 64, 0, s>>>(
+        (const uint16_t*)x, (const uint16_t*)w_router, T, H, E, logits);
+    return hipGetLastError();
+  };
+  if (E <= 16) return go(router_logits_kernel<1>, 1);
+  if (E <= 32) return go(router_logits_kernel<2>, 2);
+  if (E <= 64) return go(router_logits_kernel<4>, 4);
+  return go(router_logits_kernel<8>, 8);
 }
 
 // ---- combine backward with the routing-weight gradient --------------------------------
