@@ -7,10 +7,12 @@ no code. Everything here is float64 NumPy with explicit float32/bfloat16/e4m3
 rounding at the points where the GPU path stores narrower types.
 """
 from .moe_oracle import *  # noqa: F401,F403
-from .moe_oracle import (SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID, E4M3_MAX,  # noqa: F401
+from .moe_oracle import (SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID, SQRTSOFTPLUS,  # noqa: F401
+                         E4M3_MAX,
                          bf16_bits_to_f64, f32_to_bf16_bits, as_values, to_f32, to_bf16,
                          e4m3_decode, e4m3_encode, topk_select, topk_probs, router_topk,
                          dispatch_meta, permute, quantize_rows_e4m3, quantize_cols_e4m3,
                          silu, grouped_gemm, swiglu_from_gu, expert_mlp, dense_mlp, combine,
                          moe_forward, swiglu_backward, grouped_gemm_dw, moe_backward,
-                         gate_logits, router_backward, prob_grad)
+                         gate_logits, router_backward, prob_grad, softplus, score_values,
+                         selection_keys, topk_select_ext, pack_routing_map, expert_bias_update)

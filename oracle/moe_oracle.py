@@ -26,7 +26,7 @@ from __future__ import annotations
 
 import numpy as np
 
-SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID = 0, 1, 2
+SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID, SQRTSOFTPLUS = 0, 1, 2, 3
 E4M3_MAX = 448.0
 
 # ---------------------------------------------------------------------------
@@ -156,7 +156,26 @@ def topk_select(logits: np.ndarray, k: int) -> np.ndarray:
     return idx
 
 
-def topk_probs(logits: np.ndarray, idx: np.ndarray, score: int, exact=False) -> np.ndarray:
+def softplus(l):
+    """log(1 + e^l) in float64, as max(l, 0) + log1p(e^-|l|) (no overflow)."""
+    l = np.asarray(l, dtype=np.float64)
+    return np.maximum(l, 0.0) + np.log1p(np.exp(-np.abs(l)))
+
+
+def score_values(l, score):
+    """Per-expert score of the sigmoid and sqrtsoftplus functions, float64
+    [TE-MoE "Router": score functions softmax, sigmoid or sqrtsoftplus].
+    SQRTSOFTPLUS: sqrt(softplus(l)) = sqrt(log(1 + e^l))."""
+    l = np.asarray(l, dtype=np.float64)
+    if score == SIGMOID:
+        return 1.0 / (1.0 + np.exp(-l))
+    if score == SQRTSOFTPLUS:
+        return np.sqrt(softplus(l))
+    raise ValueError(f"no per-expert score for score function {score}")
+
+
+def topk_probs(logits: np.ndarray, idx: np.ndarray, score: int, exact=False,
+               scaling_factor=1.0) -> np.ndarray:
     """Routing weights of the selected experts, computed in float64, rounded once to fp32.
 
     SOFTMAX_PRE_RENORM [TE-MIX forward: softmax in fp32 over all experts, topk, then
@@ -167,6 +186,11 @@ def topk_probs(logits: np.ndarray, idx: np.ndarray, score: int, exact=False) -> 
     SIGMOID [TE-MoE "Router" score functions; "Token combine": sigmoid top-1 weights
       are not one and must be applied]: q_j = 1 / (1 + exp(-l_idx_j)).
       READING: no renormalisation of sigmoid weights.
+    SQRTSOFTPLUS [TE-MoE "Router" score functions; "Token combine": its weights are not
+      one either]: q_j = sqrt(log(1 + exp(l_idx_j))). READING: not renormalised, as
+      sigmoid.
+    scaling_factor [TE-MoE "Router": scaling rescales the returned weights]: multiplied
+      into q after the score function (and after the softmax renormalisation).
     """
     l = _logit_values(logits)
     T = l.shape[0]
@@ -181,16 +205,108 @@ def topk_probs(logits: np.ndarray, idx: np.ndarray, score: int, exact=False) -> 
         m = sel.max(axis=1, keepdims=True)
         z = np.exp(sel - m)
         q = z / z.sum(axis=1, keepdims=True)
-    elif score == SIGMOID:
-        q = 1.0 / (1.0 + np.exp(-sel))
+    elif score in (SIGMOID, SQRTSOFTPLUS):
+        q = score_values(sel, score)
     else:
         raise ValueError(f"unknown score function {score}")
     assert q.shape == (T, idx.shape[1])
-    return to_f32(q, exact)
+    return to_f32(q * float(scaling_factor), exact)
 
 
-def router_topk(logits: np.ndarray, k: int, score: int, exact=False):
-    """Fused score function + top-k [TE-MoE "Router"].
+def selection_keys(logits, score, expert_bias=None):
+    """The values the top-k ranks (key) and the values grouped routing sums (gval), as
+    float32 numbers (the router's math is fp32 [TE-MoE "Router"]; these values decide
+    integers, so both sides take the decision in fp32).
+      softmax (either order): key = the logit (R1: softmax is increasing); gval = the
+        softmax probability over all experts, fp32 (before the top-k) or the logit
+        (after the top-k: the kept logits are the scores the top-k sees).
+      sigmoid, sqrtsoftplus: s = fp32(score); without a bias key = the logit and
+        gval = s; with expert_bias [TE-MoE "Router" expert bias; "Load balancing": added
+        to the scores for the selection only] key = gval = fp32(s + bias).
+    """
+    l = _logit_values(logits)
+    if score in (SIGMOID, SQRTSOFTPLUS):
+        sv = to_f32(score_values(l, score))
+        if expert_bias is None:
+            return l, sv
+        kb = to_f32(sv + np.asarray(expert_bias, np.float32).astype(np.float64)[None, :])
+        return kb, kb
+    if expert_bias is not None:
+        raise ValueError("expert_bias applies to the sigmoid and sqrtsoftplus scores")
+    if score == SOFTMAX_PRE_RENORM:
+        m = l.max(axis=1, keepdims=True)
+        p = np.exp(l - m)
+        return l, to_f32(p / p.sum(axis=1, keepdims=True))
+    return l, l
+
+
+def topk_select_ext(logits, k, score, expert_bias=None, num_groups=0, group_topk=0):
+    """Top-k with the router's options [TE-MoE "Router": expert bias, grouped routing].
+
+    Grouped routing: the E experts form num_groups equal groups of consecutive ids; a
+    group's score is the fp32 sum, best first, of the gvals of its m best experts
+    (ranked by key, lower id first on a tie), READING m = k // group_topk (the pages say
+    "the sum of its best expert scores" without the count; with the top-k spread over
+    group_topk groups, each kept group contributes about k / group_topk experts); the
+    group_topk best groups are kept (lower group id first on a tie) and the top-k is
+    taken among their experts only. Without groups this is topk_select on the keys.
+    """
+    key, gval = selection_keys(logits, score, expert_bias)
+    T, E = key.shape
+    allowed = np.ones((T, E), dtype=bool)
+    if num_groups and num_groups > 1:
+        assert E % num_groups == 0 and 1 <= group_topk <= num_groups
+        gs = E // num_groups
+        m = k // group_topk
+        assert m >= 1 and k <= group_topk * gs
+        gscore = np.zeros((T, num_groups), dtype=np.float64)
+        for g in range(num_groups):
+            kg = key[:, g * gs:(g + 1) * gs]
+            vg = gval[:, g * gs:(g + 1) * gs]
+            best = topk_select(kg, m)          # best m by key, lower id first on a tie
+            acc = np.zeros(T, dtype=np.float64)
+            for j in range(m):                 # fp32 sum, best first
+                acc = to_f32(acc + np.take_along_axis(vg, best[:, j:j + 1].astype(np.int64), 1)[:, 0])
+            gscore[:, g] = acc
+        kept = topk_select(gscore, group_topk)
+        allowed[:] = False
+        for j in range(group_topk):
+            for g in range(num_groups):
+                sel = kept[:, j] == g
+                allowed[sel, g * gs:(g + 1) * gs] = True
+    masked = np.where(allowed, key, -np.inf)
+    idx = np.empty((T, k), dtype=np.int32)
+    rows = np.arange(T)
+    avail = allowed.copy()
+    for j in range(k):
+        e = np.argmax(np.where(avail, masked, -np.inf), axis=1)
+        idx[:, j] = e
+        avail[rows, e] = False
+    return idx
+
+
+def pack_routing_map(rmap):
+    """Bit-packed routing map [TE-MoE "Router": routing_map_format bitmap_u8]: bit e%8 of
+    byte e//8 of a token's row is routing_map[t,e] (least significant bit first).
+    READING: the bit order within a byte, which the pages do not state."""
+    return np.packbits(np.asarray(rmap, dtype=np.uint8), axis=1, bitorder="little")
+
+
+def expert_bias_update(bias, tokens_per_expert, coeff):
+    """Auxiliary-loss-free load balancing step [TT-1269 MoE._update_expert_bias; TE-MoE
+    "Load balancing": lower the bias of overloaded experts, raise it for under-used
+    ones]: delta = coeff * sign(mean(tokens) - tokens), minus its mean; bias + delta.
+    Computed in float64 from fp32 inputs, rounded once to fp32."""
+    c = np.asarray(tokens_per_expert, dtype=np.float64)
+    d = coeff * np.sign(c.mean() - c)
+    d = d - d.mean()
+    return to_f32(np.asarray(bias, np.float32).astype(np.float64) + d)
+
+
+def router_topk(logits: np.ndarray, k: int, score: int, exact=False, expert_bias=None,
+                num_groups=0, group_topk=0, scaling_factor=1.0):
+    """Fused score function + top-k [TE-MoE "Router"], with its options (expert bias,
+    grouped routing, scaling; see topk_select_ext and topk_probs).
 
     Returns topk_idx [T,k] int32, topk_prob [T,k], counts [E] int32,
     routing_map [T,E] uint8 (1 at the selected experts), probs_dense [T,E] (the
@@ -198,8 +314,11 @@ def router_topk(logits: np.ndarray, k: int, score: int, exact=False):
     counts = tokens routed to each expert [TE-MoE "Load balancing": routing_map.sum(0)].
     """
     T, E = logits.shape
-    idx = topk_select(logits, k)
-    q = topk_probs(logits, idx, score, exact)
+    if expert_bias is None and not (num_groups and num_groups > 1):
+        idx = topk_select(logits, k)
+    else:
+        idx = topk_select_ext(logits, k, score, expert_bias, num_groups, group_topk)
+    q = topk_probs(logits, idx, score, exact, scaling_factor)
     rmap = np.zeros((T, E), dtype=np.uint8)
     dense = np.zeros((T, E), dtype=np.float64)
     rows = np.arange(T)[:, None]
@@ -224,7 +343,7 @@ def gate_logits(x_vals, w_router_vals, exact=False):
     return to_f32(x @ w.T, exact)
 
 
-def router_backward(logits, idx, d_prob, score, exact=False):
+def router_backward(logits, idx, d_prob, score, exact=False, scaling_factor=1.0):
     """Gradient of the routing weights with respect to the logits [TE-MoE "Router": the
     score function and the top-k run in one differentiable kernel with fp32 math].
 
@@ -238,12 +357,15 @@ def router_backward(logits, idx, d_prob, score, exact=False):
       SOFTMAX_POST: q = softmax of the kept logits, dl_idx_j = q_j (dq_j - sum q dq);
         0 elsewhere.
       SIGMOID: q_j = sigmoid(l_idx_j), dl_idx_j = dq_j q_j (1 - q_j); 0 elsewhere.
+      SQRTSOFTPLUS: q_j = sqrt(softplus(l_idx_j)),
+        dl_idx_j = dq_j sigmoid(l_idx_j) / (2 q_j); 0 elsewhere.
+    A scaling factor c multiplies the weights, so the score function sees c * d_prob.
     Returns d_logits [T, E] (float64 values of fp32 results).
     """
     l = _logit_values(logits)
     T, E = l.shape
     ii = np.asarray(idx, dtype=np.int64)
-    dq = np.asarray(d_prob, dtype=np.float64)
+    dq = np.asarray(d_prob, dtype=np.float64) * float(scaling_factor)
     rows = np.arange(T)[:, None]
     dl = np.zeros((T, E), dtype=np.float64)
     sel = np.take_along_axis(l, ii, axis=1)
@@ -264,6 +386,8 @@ def router_backward(logits, idx, d_prob, score, exact=False):
     elif score == SIGMOID:
         q = 1.0 / (1.0 + np.exp(-sel))
         dl[rows, ii] = dq * q * (1.0 - q)
+    elif score == SQRTSOFTPLUS:
+        dl[rows, ii] = dq * (1.0 / (1.0 + np.exp(-sel))) / (2.0 * np.sqrt(softplus(sel)))
     else:
         raise ValueError(f"unknown score function {score}")
     return to_f32(dl, exact)
