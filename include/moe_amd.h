@@ -56,17 +56,21 @@ typedef enum {
 
 typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3 = 1, MOE_FP32 = 2 } moe_dtype_t;
 
-/* Score functions (guide, "Router": softmax before or after the top-k, sigmoid).
+/* Score functions (guide, "Router": softmax before or after the top-k, sigmoid,
+ * sqrtsoftplus).
  * MOE_SOFTMAX_PRE_RENORM: softmax over all experts, keep the top-k, divide by their
  *   sum (te_mixtral.py, TEMixtralSparseMoeBlock.forward).
  * MOE_SOFTMAX_POST: softmax over the k kept logits (guide, use_pre_softmax=False).
  * MOE_SIGMOID: sigmoid of each kept logit, not renormalised (guide, "Token
  *   combine": sigmoid top-1 weights are not one and must be applied).
- * Selection is on the logits, descending, ties to the lower expert index. */
+ * MOE_SQRTSOFTPLUS: sqrt(log(1 + e^l)) of each kept logit, not renormalised.
+ * Selection is on the logits, descending, ties to the lower expert index (with an
+ * expert bias: on fp32(score + bias); see moe_router_opts_t). */
 typedef enum {
   MOE_SOFTMAX_PRE_RENORM = 0,
   MOE_SOFTMAX_POST = 1,
-  MOE_SIGMOID = 2
+  MOE_SIGMOID = 2,
+  MOE_SQRTSOFTPLUS = 3
 } moe_score_t;
 
 /* Layouts of the grouped GEMM (guide, "Grouped GEMM": Y_i = X_i W_i per expert
@@ -90,6 +94,46 @@ const char* moe_status_str(moe_status_t s);
 moe_status_t moe_router_topk(const float* logits, int T, int E, int k, int score,
                              int32_t* topk_idx, float* topk_prob, int32_t* counts,
                              uint8_t* routing_map, float* probs_dense, void* stream);
+
+/* Router options (guide, "Router" options and "Load balancing").
+ *  expert_bias   [E] float32 or NULL: added to the sigmoid / sqrtsoftplus scores for the
+ *                selection only (the weights stay the unbiased scores); with a softmax
+ *                score function MOE_ERR_UNSUPPORTED.
+ *  num_groups    0 or 1: no grouped routing. Else the experts form num_groups equal
+ *                groups of consecutive ids (E % num_groups == 0, num_groups <= 64); a
+ *                group's score is the fp32 sum, best first, of the values of its
+ *                m = k / group_topk best experts (softmax before the top-k: the fp32
+ *                probabilities; after it: the logits; sigmoid / sqrtsoftplus: the fp32
+ *                scores, plus the bias when given); the group_topk best groups are kept
+ *                and the top-k is taken among their experts (ties to the lower id).
+ *  group_topk    groups kept: 1 <= group_topk <= num_groups, k >= group_topk,
+ *                k <= group_topk * (E / num_groups).
+ *  scaling_factor multiplies the returned weights (0 is taken as 1).
+ *  map_format    0: routing_map uint8 [T,E]; 1: bit-packed [T, ceil(E/8)] bytes, bit e%8
+ *                of byte e/8 (least significant first) set at the selected experts. */
+typedef struct {
+  const float* expert_bias;
+  int num_groups;
+  int group_topk;
+  float scaling_factor;
+  int map_format;
+} moe_router_opts_t;
+
+/* moe_router_topk with options (opts may be NULL: none). Arguments and outputs as
+ * moe_router_topk; routing_map in the opts->map_format layout. */
+moe_status_t moe_router_topk_ex(const float* logits, int T, int E, int k, int score,
+                                const moe_router_opts_t* opts, int32_t* topk_idx,
+                                float* topk_prob, int32_t* counts, uint8_t* routing_map,
+                                float* probs_dense, void* stream);
+
+/* Auxiliary-loss-free load balancing step (torchtitan pull request 1269,
+ * MoE._update_expert_bias; guide, "Load balancing": lower the bias of overloaded experts,
+ * raise it for under-used ones), in place on expert_bias [E] float32:
+ * bias += coeff * sign(mean(c) - c_e) - mean over experts of that term, c =
+ * tokens_per_expert [E] int32 (e.g. the counts of moe_router_topk). The signs are exact
+ * (integer comparison); the update is computed in fp64 and rounded once. E <= 256. */
+moe_status_t moe_expert_bias_update(float* expert_bias, const int32_t* tokens_per_expert,
+                                    int E, float coeff, void* stream);
 
 /* Scratch bytes moe_permute needs for (T, E, k). */
 size_t moe_permute_workspace_bytes(int T, int E, int k);
@@ -191,15 +235,16 @@ moe_status_t moe_router_logits(const void* x, const void* w_router, int T, int H
  *  the forward.
  *  d_out [T*k,H] bf16 out: d_out[row_of[t,j]] = bf16(p[t,j] * dy[t]).
  *  d_prob [T,k] float32 out, nullable: <dy[t], expert_out[row_of[t,j]]> (fp32 sum).
- *  d_logits [T,E] float32 out: at the kept experts, softmax (either order: the same
- *  function of the kept logits) p_j (d_prob_j - sum_i p_i d_prob_i), sigmoid
- *  d_prob_j p_j (1 - p_j); 0 at the other experts (the top-k choice is piecewise
- *  constant). */
+ *  d_logits [T,E] float32 out: with p = c s (c = scaling_factor, 0 taken as 1; s the
+ *  score-function output), at the kept experts softmax (either order: the same function
+ *  of the kept logits) c s_j (d_prob_j - sum_i s_i d_prob_i), sigmoid
+ *  c d_prob_j s_j (1 - s_j), sqrtsoftplus c d_prob_j sigmoid(l_j) / (2 s_j); 0 at the
+ *  other experts (the top-k choice is piecewise constant). */
 moe_status_t moe_combine_backward_router(const void* dy, const void* expert_out,
                                          const int32_t* row_of, const int32_t* topk_idx,
                                          const float* topk_prob, int T, int H, int E, int k,
-                                         int score, void* d_out, float* d_prob, float* d_logits,
-                                         void* stream);
+                                         int score, float scaling_factor, void* d_out,
+                                         float* d_prob, float* d_logits, void* stream);
 
 /* Scratch bytes moe_router_weight_grad needs for (T, H, E). */
 size_t moe_router_weight_grad_workspace_bytes(int T, int H, int E);
@@ -234,6 +279,9 @@ typedef struct {
                     logits from x and w_router (into the workspace; t->logits is not
                     read) and moe_backward also returns dw_router and adds the router's
                     term to dx */
+  int num_groups;        /* grouped routing, as moe_router_opts_t (0: none) */
+  int group_topk;
+  float scaling_factor;  /* multiplies the routing weights (0 is taken as 1) */
 } moe_problem_t;
 
 typedef struct {
@@ -248,6 +296,7 @@ typedef struct {
   void* y;                    /* [T,H] bf16 out */
   const void* w_router;       /* bf16 [E,H] (router = 1), else NULL */
   float* dw_router;           /* [E,H] float32 out of moe_backward (router = 1), else NULL */
+  const float* expert_bias;   /* [E] selection bias (sigmoid / sqrtsoftplus) or NULL */
 } moe_tensors_t;
 
 /* Device pointers into a forward workspace (all inside ws). */

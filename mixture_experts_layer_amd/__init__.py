@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_amd.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_BF16, MOE_FP8_E4M3, MOE_FP32 = 0, 1, 2
-MOE_SOFTMAX_PRE_RENORM, MOE_SOFTMAX_POST, MOE_SIGMOID = 0, 1, 2
+MOE_SOFTMAX_PRE_RENORM, MOE_SOFTMAX_POST, MOE_SIGMOID, MOE_SQRTSOFTPLUS = 0, 1, 2, 3
 MOE_GEMM_NN, MOE_GEMM_NT, MOE_GEMM_TN_DW = 0, 1, 2
 
 EXPORTS = [
@@ -28,7 +28,7 @@ EXPORTS = [
     "moe_quantize_fp8_weights", "moe_workspace_bytes", "moe_workspace_views", "moe_forward",
     "moe_backward", "moe_router_logits", "moe_combine_backward_router",
     "moe_router_weight_grad_workspace_bytes", "moe_router_weight_grad",
-    "moe_dispatch_backward_router",
+    "moe_dispatch_backward_router", "moe_router_topk_ex", "moe_expert_bias_update",
 ]
 
 
@@ -42,13 +42,20 @@ class Problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int), ("H", ctypes.c_int), ("E", ctypes.c_int),
                 ("k", ctypes.c_int), ("I", ctypes.c_int), ("shared_I", ctypes.c_int),
                 ("score", ctypes.c_int), ("dtype", ctypes.c_int), ("training", ctypes.c_int),
-                ("router", ctypes.c_int)]
+                ("router", ctypes.c_int), ("num_groups", ctypes.c_int), ("group_topk", ctypes.c_int),
+                ("scaling_factor", ctypes.c_float)]
 
 
 class Tensors(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("x", "logits", "w_gu", "w_gu_scale", "w_down", "w_down_scale",
-                 "shared_gu", "shared_down", "y", "w_router", "dw_router")]
+                 "shared_gu", "shared_down", "y", "w_router", "dw_router", "expert_bias")]
+
+
+class RouterOpts(ctypes.Structure):
+    _fields_ = [("expert_bias", ctypes.c_void_p), ("num_groups", ctypes.c_int),
+                ("group_topk", ctypes.c_int), ("scaling_factor", ctypes.c_float),
+                ("map_format", ctypes.c_int)]
 
 
 class Views(ctypes.Structure):
@@ -86,7 +93,10 @@ def _load():
         "moe_backward": ([ctypes.POINTER(Problem), ctypes.POINTER(Tensors), vp, vp, vp, vp, vp,
                           sz, vp], i),
         "moe_router_logits": ([vp, vp, i, i, i, vp, vp], i),
-        "moe_combine_backward_router": ([vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp], i),
+        "moe_combine_backward_router": ([vp, vp, vp, vp, vp, i, i, i, i, i, ctypes.c_float, vp, vp,
+                                         vp, vp], i),
+        "moe_router_topk_ex": ([vp, i, i, i, i, ctypes.POINTER(RouterOpts), vp, vp, vp, vp, vp, vp], i),
+        "moe_expert_bias_update": ([vp, vp, i, ctypes.c_float, vp], i),
         "moe_router_weight_grad_workspace_bytes": ([i, i, i], sz),
         "moe_router_weight_grad": ([vp, vp, i, i, i, vp, vp, sz, vp], i),
         "moe_dispatch_backward_router": ([vp, vp, vp, vp, vp, i, i, i, i, vp, vp], i),
@@ -135,7 +145,7 @@ def _want(t, dtype, shape, name):
 
 
 _SCORE = {"softmax_pre_renorm": MOE_SOFTMAX_PRE_RENORM, "softmax_post": MOE_SOFTMAX_POST,
-          "sigmoid": MOE_SIGMOID}
+          "sigmoid": MOE_SIGMOID, "sqrtsoftplus": MOE_SQRTSOFTPLUS}
 
 
 def _score(s):
@@ -163,6 +173,39 @@ def moe_router_topk(logits, k, score, topk_idx, topk_prob, counts, routing_map=N
     _check("moe_router_topk", _lib.moe_router_topk(
         _p(logits), T, E, k, _score(score), _p(topk_idx), _p(topk_prob), _p(counts),
         _p(routing_map), _p(probs_dense), _stream(stream)))
+
+
+def router_opts(expert_bias=None, num_groups=0, group_topk=0, scaling_factor=1.0, bitmap=False):
+    if expert_bias is not None:
+        _want(expert_bias, torch.float32, (expert_bias.numel(),), "expert_bias")
+    return RouterOpts(_p(expert_bias), int(num_groups), int(group_topk), float(scaling_factor),
+                      int(bool(bitmap)))
+
+
+def moe_router_topk_ex(logits, k, score, opts, topk_idx, topk_prob, counts, routing_map=None,
+                       probs_dense=None, stream=None):
+    T, E = logits.shape
+    _want(logits, torch.float32, (T, E), "logits")
+    _want(topk_idx, torch.int32, (T, k), "topk_idx")
+    _want(topk_prob, torch.float32, (T, k), "topk_prob")
+    _want(counts, torch.int32, (E,), "counts")
+    if routing_map is not None:
+        cols = (E + 7) // 8 if opts is not None and opts.map_format else E
+        _want(routing_map, torch.uint8, (T, cols), "routing_map")
+    if probs_dense is not None:
+        _want(probs_dense, torch.float32, (T, E), "probs_dense")
+    _check("moe_router_topk_ex", _lib.moe_router_topk_ex(
+        _p(logits), T, E, k, _score(score), None if opts is None else ctypes.byref(opts),
+        _p(topk_idx), _p(topk_prob), _p(counts), _p(routing_map), _p(probs_dense),
+        _stream(stream)))
+
+
+def moe_expert_bias_update(expert_bias, tokens_per_expert, coeff, stream=None):
+    E = expert_bias.numel()
+    _want(expert_bias, torch.float32, (E,), "expert_bias")
+    _want(tokens_per_expert, torch.int32, (E,), "tokens_per_expert")
+    _check("moe_expert_bias_update", _lib.moe_expert_bias_update(
+        _p(expert_bias), _p(tokens_per_expert), E, float(coeff), _stream(stream)))
 
 
 def moe_permute_workspace_bytes(T, E, k):
@@ -278,7 +321,7 @@ def moe_router_logits(x, w_router, logits, stream=None):
 
 
 def moe_combine_backward_router(dy, expert_out, row_of, topk_idx, topk_prob, score, d_out,
-                                d_logits, d_prob=None, stream=None):
+                                d_logits, d_prob=None, scaling_factor=1.0, stream=None):
     T, k = row_of.shape
     H = dy.shape[1]
     E = d_logits.shape[1]
@@ -292,7 +335,8 @@ def moe_combine_backward_router(dy, expert_out, row_of, topk_idx, topk_prob, sco
         _want(d_prob, torch.float32, (T, k), "d_prob")
     _check("moe_combine_backward_router", _lib.moe_combine_backward_router(
         _p(dy), _p(expert_out), _p(row_of), _p(topk_idx), _p(topk_prob), T, H, E, k,
-        _score(score), _p(d_out), _p(d_prob), _p(d_logits), _stream(stream)))
+        _score(score), float(scaling_factor), _p(d_out), _p(d_prob), _p(d_logits),
+        _stream(stream)))
 
 
 def moe_router_weight_grad_workspace_bytes(T, H, E):
@@ -324,9 +368,10 @@ def moe_dispatch_backward_router(dxp, row_of, topk_idx, d_logits, w_router, dx, 
 
 # ---- whole layer -----------------------------------------------------------------------
 
-def problem(T, H, E, k, I, score, shared_I=0, dtype=MOE_BF16, training=False, router=False):
+def problem(T, H, E, k, I, score, shared_I=0, dtype=MOE_BF16, training=False, router=False,
+            num_groups=0, group_topk=0, scaling_factor=1.0):
     return Problem(T, H, E, k, I, shared_I, _score(score), dtype, int(bool(training)),
-                   int(bool(router)))
+                   int(bool(router)), int(num_groups), int(group_topk), float(scaling_factor))
 
 
 def moe_workspace_bytes(prob: Problem):
@@ -344,9 +389,10 @@ def moe_workspace_views(prob: Problem, ws):
 
 
 def tensors(x, logits, w_gu, w_down, y, w_gu_scale=None, w_down_scale=None, shared_gu=None,
-            shared_down=None, w_router=None, dw_router=None):
+            shared_down=None, w_router=None, dw_router=None, expert_bias=None):
     return Tensors(_p(x), _p(logits), _p(w_gu), _p(w_gu_scale), _p(w_down), _p(w_down_scale),
-                   _p(shared_gu), _p(shared_down), _p(y), _p(w_router), _p(dw_router))
+                   _p(shared_gu), _p(shared_down), _p(y), _p(w_router), _p(dw_router),
+                   _p(expert_bias))
 
 
 def moe_forward(prob: Problem, tens: Tensors, ws, stream=None):

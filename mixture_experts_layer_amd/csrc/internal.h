@@ -5,6 +5,27 @@
 
 namespace moe {
 
+// Router options (router_opts.hip). Plain: none of them set.
+struct RouterOpts {
+  const float* expert_bias;  // [E] or null: added to sigmoid / sqrtsoftplus scores to select
+  int num_groups;            // <= 1: no grouped routing
+  int group_topk;            // groups kept
+  float scaling;             // multiplies the weights
+  int bitmap;                // routing_map bit-packed [T, ceil(E/8)]
+};
+inline bool router_opts_plain(const RouterOpts& o, int score) {
+  return o.expert_bias == nullptr && o.num_groups <= 1 && o.scaling == 1.0f && !o.bitmap &&
+         score != MOE_SQRTSOFTPLUS;
+}
+// chunk_tokens > 0: per-chunk histograms into counts[chunk][E] (as launch_router_hist);
+// 0: counts [E] zeroed then accumulated.
+hipError_t launch_router_ext(const float* logits, int T, int E, int k, int score,
+                             const RouterOpts& o, int32_t* topk_idx, float* topk_prob,
+                             int32_t* counts, uint8_t* routing_map, float* probs_dense,
+                             int chunk_tokens, hipStream_t s);
+hipError_t launch_expert_bias_update(float* bias, const int32_t* tokens_per_expert, int E,
+                                     float coeff, hipStream_t s);
+
 // router.hip
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int score,
                               int32_t* topk_idx, float* topk_prob, int32_t* counts,
@@ -47,8 +68,9 @@ hipError_t launch_router_logits(const void* x, const void* w_router, int T, int 
                                 float* logits, hipStream_t s);
 hipError_t launch_combine_bwd_router(const void* dy, const void* out, const int32_t* row_of,
                                      const int32_t* topk_idx, const float* prob, int T, int H,
-                                     int E, int k, int score, void* d_out, float* d_prob,
-                                     float* d_logits, uint16_t* dls, int mp, hipStream_t s);
+                                     int E, int k, int score, float scaling, void* d_out,
+                                     float* d_prob, float* d_logits, uint16_t* dls, int mp,
+                                     hipStream_t s);
 hipError_t launch_router_wgrad_reduce(const float* part, int S, int E, int H, int mp, float* dw,
                                       hipStream_t s);
 hipError_t launch_router_split(const float* d_logits, int T, int E, int mp, uint16_t* dls,

@@ -92,6 +92,29 @@ Layout make_layout(const moe_problem_t& p) {
   return L;
 }
 
+bool valid_score(int score) { return score >= MOE_SOFTMAX_PRE_RENORM && score <= MOE_SQRTSOFTPLUS; }
+
+// Router options against (E, k, score); fills `o` (scaling 0 is taken as 1).
+moe_status_t make_router_opts(int E, int k, int score, const float* expert_bias, int num_groups,
+                              int group_topk, float scaling, int map_format, RouterOpts* o) {
+  if (!opt_ptr(expert_bias) || num_groups < 0 || (map_format != 0 && map_format != 1))
+    return MOE_ERR_INVALID_ARG;
+  if (!(scaling == scaling) || scaling == INFINITY || scaling == -INFINITY) return MOE_ERR_INVALID_ARG;
+  if (expert_bias && score != MOE_SIGMOID && score != MOE_SQRTSOFTPLUS) return MOE_ERR_UNSUPPORTED;
+  if (num_groups > 1) {
+    if (num_groups > 64 || E % num_groups) return MOE_ERR_UNSUPPORTED;
+    if (group_topk < 1 || group_topk > num_groups || k < group_topk ||
+        k > group_topk * (E / num_groups))
+      return MOE_ERR_INVALID_ARG;
+  }
+  o->expert_bias = expert_bias;
+  o->num_groups = num_groups > 1 ? num_groups : 0;
+  o->group_topk = num_groups > 1 ? group_topk : 0;
+  o->scaling = scaling == 0.f ? 1.f : scaling;
+  o->bitmap = map_format;
+  return MOE_OK;
+}
+
 moe_status_t check_problem(const moe_problem_t* p) {
   if (!p) return MOE_ERR_INVALID_ARG;
   moe_status_t st = check_shape(p->T, p->H, p->E, p->k);
@@ -100,9 +123,13 @@ moe_status_t check_problem(const moe_problem_t* p) {
   if (p->I % 64 || p->shared_I % 64) return MOE_ERR_UNSUPPORTED;
   if (!gemm_offsets_fit(2LL * p->I, p->H, 2) || !gemm_offsets_fit(2LL * p->shared_I, p->H, 2))
     return MOE_ERR_UNSUPPORTED;
-  if (p->score < MOE_SOFTMAX_PRE_RENORM || p->score > MOE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (!valid_score(p->score)) return MOE_ERR_INVALID_ARG;
   if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   if (p->router != 0 && p->router != 1) return MOE_ERR_INVALID_ARG;
+  RouterOpts o;
+  moe_status_t so = make_router_opts(p->E, p->k, p->score, nullptr, p->num_groups, p->group_topk,
+                                     p->scaling_factor, 0, &o);
+  if (so != MOE_OK) return so;
   if (p->dtype == MOE_FP8_E4M3) {
     if (p->H % 128 || p->I % 128) return MOE_ERR_UNSUPPORTED;
     if (p->training || p->shared_I) return MOE_ERR_UNSUPPORTED;
@@ -157,15 +184,39 @@ moe_status_t moe_set_gemm_max_blocks(int max_blocks) {
 moe_status_t moe_router_topk(const float* logits, int T, int E, int k, int score,
                              int32_t* topk_idx, float* topk_prob, int32_t* counts,
                              uint8_t* routing_map, float* probs_dense, void* stream) {
+  return moe_router_topk_ex(logits, T, E, k, score, nullptr, topk_idx, topk_prob, counts,
+                            routing_map, probs_dense, stream);
+}
+
+moe_status_t moe_router_topk_ex(const float* logits, int T, int E, int k, int score,
+                                const moe_router_opts_t* opts, int32_t* topk_idx,
+                                float* topk_prob, int32_t* counts, uint8_t* routing_map,
+                                float* probs_dense, void* stream) {
   moe_status_t st = check_shape(T, 64, E, k);
   if (st != MOE_OK) return st;
-  if (score < MOE_SOFTMAX_PRE_RENORM || score > MOE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (!valid_score(score)) return MOE_ERR_INVALID_ARG;
+  RouterOpts o;
+  st = opts ? make_router_opts(E, k, score, opts->expert_bias, opts->num_groups, opts->group_topk,
+                               opts->scaling_factor, opts->map_format, &o)
+            : make_router_opts(E, k, score, nullptr, 0, 0, 1.f, 0, &o);
+  if (st != MOE_OK) return st;
   if (!ok_ptr(counts)) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!ok_ptr(logits) || !ok_ptr(topk_idx) || !ok_ptr(topk_prob)))
     return MOE_ERR_INVALID_ARG;
   if (!opt_ptr(routing_map) || !opt_ptr(probs_dense)) return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_router_topk(logits, T, E, k, score, topk_idx, topk_prob, counts,
-                                       routing_map, probs_dense, S(stream)));
+  if (router_opts_plain(o, score))
+    return hip_status(launch_router_topk(logits, T, E, k, score, topk_idx, topk_prob, counts,
+                                         routing_map, probs_dense, S(stream)));
+  return hip_status(launch_router_ext(logits, T, E, k, score, o, topk_idx, topk_prob, counts,
+                                      routing_map, probs_dense, 0, S(stream)));
+}
+
+moe_status_t moe_expert_bias_update(float* expert_bias, const int32_t* tokens_per_expert,
+                                    int E, float coeff, void* stream) {
+  if (E <= 0) return MOE_ERR_INVALID_ARG;
+  if (E > 256) return MOE_ERR_UNSUPPORTED;
+  if (!ok_ptr(expert_bias) || !ok_ptr(tokens_per_expert)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_expert_bias_update(expert_bias, tokens_per_expert, E, coeff, S(stream)));
 }
 
 size_t moe_permute_workspace_bytes(int T, int E, int k) {
@@ -331,18 +382,20 @@ moe_status_t moe_router_logits(const void* x, const void* w_router, int T, int H
 moe_status_t moe_combine_backward_router(const void* dy, const void* expert_out,
                                          const int32_t* row_of, const int32_t* topk_idx,
                                          const float* topk_prob, int T, int H, int E, int k,
-                                         int score, void* d_out, float* d_prob, float* d_logits,
-                                         void* stream) {
+                                         int score, float scaling_factor, void* d_out,
+                                         float* d_prob, float* d_logits, void* stream) {
   moe_status_t st = check_shape(T, H, E, k);
   if (st != MOE_OK) return st;
-  if (score < MOE_SOFTMAX_PRE_RENORM || score > MOE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (!valid_score(score)) return MOE_ERR_INVALID_ARG;
+  if (!(scaling_factor == scaling_factor) || scaling_factor == INFINITY || scaling_factor == -INFINITY)
+    return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(dy) || !ok_ptr(expert_out) || !ok_ptr(row_of) || !ok_ptr(topk_idx) ||
       !ok_ptr(topk_prob) || !ok_ptr(d_out) || !opt_ptr(d_prob) || !ok_ptr(d_logits))
     return MOE_ERR_INVALID_ARG;
   return hip_status(launch_combine_bwd_router(dy, expert_out, row_of, topk_idx, topk_prob, T, H, E,
-                                              k, score, d_out, d_prob, d_logits, nullptr, 0,
-                                              S(stream)));
+                                              k, score, scaling_factor == 0.f ? 1.f : scaling_factor,
+                                              d_out, d_prob, d_logits, nullptr, 0, S(stream)));
 }
 
 size_t moe_router_weight_grad_workspace_bytes(int T, int H, int E) {
@@ -447,6 +500,12 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   if (!ok_ptr(t->x) || !ok_ptr(t->w_gu) || !ok_ptr(t->w_down) || !ok_ptr(t->y))
     return MOE_ERR_INVALID_ARG;
   if (p->router ? !ok_ptr(t->w_router) : !ok_ptr(t->logits)) return MOE_ERR_INVALID_ARG;
+  {
+    RouterOpts chk;
+    moe_status_t so = make_router_opts(p->E, p->k, p->score, t->expert_bias, p->num_groups,
+                                       p->group_topk, p->scaling_factor, 0, &chk);
+    if (so != MOE_OK) return so;
+  }
   if (fp8 && (!ok_ptr(t->w_gu_scale) || !ok_ptr(t->w_down_scale))) return MOE_ERR_INVALID_ARG;
   if (p->shared_I && (!ok_ptr(t->shared_gu) || !ok_ptr(t->shared_down)))
     return MOE_ERR_INVALID_ARG;
@@ -465,8 +524,16 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
     logits = v.logits;
   }
   const int chunk_tokens = router_chunk_tokens(T);
-  MOE_TRY(launch_router_hist(logits, T, E, k, p->score, v.topk_idx, v.topk_prob,
-                             (int32_t*)v.scratch, chunk_tokens, s));
+  RouterOpts ro;
+  st = make_router_opts(E, k, p->score, t->expert_bias, p->num_groups, p->group_topk,
+                        p->scaling_factor, 0, &ro);
+  if (st != MOE_OK) return st;
+  if (router_opts_plain(ro, p->score))
+    MOE_TRY(launch_router_hist(logits, T, E, k, p->score, v.topk_idx, v.topk_prob,
+                               (int32_t*)v.scratch, chunk_tokens, s));
+  else
+    MOE_TRY(launch_router_ext(logits, T, E, k, p->score, ro, v.topk_idx, v.topk_prob,
+                              (int32_t*)v.scratch, nullptr, nullptr, chunk_tokens, s));
   // 2. dispatch: counts, offsets, row maps from the histograms, then the row copies
   MOE_TRY(launch_dispatch_from_hist(v.topk_idx, T, E, k, chunk_tokens, (int32_t*)v.scratch,
                                     v.counts, v.offsets, v.row_of, v.src_of, s));
@@ -589,8 +656,9 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
     // combine backward with the routing-weight gradient: d_out, d_logits and the split
     // operand of the router weight gradient
     MOE_TRY(launch_combine_bwd_router(dy, v.out, v.row_of, v.topk_idx, v.topk_prob, T, H, E, k,
-                                      p->score, v.d_out, nullptr, v.d_logits,
-                                      (uint16_t*)v.router_ws, router_split_cols(E), s));
+                                      p->score, p->scaling_factor == 0.f ? 1.f : p->scaling_factor,
+                                      v.d_out, nullptr, v.d_logits, (uint16_t*)v.router_ws,
+                                      router_split_cols(E), s));
   } else {
     // combine backward: d_out[row_of[t,j]] = bf16(p[t,j] * dy[t])
     MOE_TRY(launch_scatter_rows(dy, v.row_of, v.topk_prob, T, H, k, v.d_out, s));

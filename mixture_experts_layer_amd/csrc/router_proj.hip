@@ -9,9 +9,12 @@
 //
 //  logits    = x . W_r^T                    x [T,H] bf16, W_r [E,H] bf16, logits fp32
 //  d_prob    = <dy[t], out[row_of[t,j]]>    per routed pair, fp32
-//  d_logits  = score-function backward of d_prob at the kept experts, 0 elsewhere:
+//  d_logits  = score-function backward of d_prob at the kept experts, 0 elsewhere. With
+//              the weights q = c s (c the scaling factor, s the score-function output):
 //              softmax (before or after the top-k: the same function of the kept
-//              logits) q_j (d_prob_j - sum_i q_i d_prob_i); sigmoid d_prob_j q_j (1-q_j)
+//              logits) c s_j (d_prob_j - sum_i s_i d_prob_i); sigmoid c d_prob_j s_j (1-s_j);
+//              sqrtsoftplus c d_prob_j sigmoid(l_j) / (2 s_j), where s^2 = softplus(l)
+//              gives sigmoid(l) = 1 - e^(-s^2)
 //  dW_r      = d_logits^T . x               (split-K weight-gradient GEMM + reduce)
 //  dx       += d_logits . W_r               (folded into the dispatch backward)
 #include "internal.h"
@@ -142,7 +145,8 @@ template <int KM>  // a bound on k: 8 or 32
 __global__ __launch_bounds__(256) void combine_bwd_router_kernel(
     const u32x4_t* __restrict__ dy, const u32x4_t* __restrict__ out,
     const int32_t* __restrict__ row_of, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ prob, int H8, int E, int k, int score, u32x4_t* __restrict__ d_out,
+    const float* __restrict__ prob, int H8, int E, int k, int score, float scaling,
+    u32x4_t* __restrict__ d_out,
     float* __restrict__ d_prob, float* __restrict__ d_logits, uint16_t* __restrict__ dls, int mp) {
   __shared__ int rows[32], ids[32];
   __shared__ float p[32], red[4][32], dl_s[32];
@@ -197,14 +201,16 @@ __global__ __launch_bounds__(256) void combine_bwd_router_kernel(
   }
   __syncthreads();
   if (tid < k) {
-    const float q = p[tid], dq = red[0][tid];
+    const float sv = p[tid] / scaling, dq = red[0][tid];
     float dl;
     if (score == MOE_SIGMOID) {
-      dl = dq * q * (1.0f - q);
+      dl = scaling * dq * sv * (1.0f - sv);
+    } else if (score == MOE_SQRTSOFTPLUS) {
+      dl = scaling * dq * (-expm1f(-sv * sv)) / (2.0f * sv);
     } else {  // both softmax orders: the same function of the kept logits
       float sdot = 0.f;
-      for (int j = 0; j < k; ++j) sdot = fmaf(p[j], red[0][j], sdot);
-      dl = q * (dq - sdot);
+      for (int j = 0; j < k; ++j) sdot = fmaf(p[j] / scaling, red[0][j], sdot);
+      dl = scaling * sv * (dq - sdot);
     }
     dl_s[tid] = dl;
   }
@@ -225,16 +231,17 @@ __global__ __launch_bounds__(256) void combine_bwd_router_kernel(
 
 hipError_t launch_combine_bwd_router(const void* dy, const void* out, const int32_t* row_of,
                                      const int32_t* topk_idx, const float* prob, int T, int H,
-                                     int E, int k, int score, void* d_out, float* d_prob,
-                                     float* d_logits, uint16_t* dls, int mp, hipStream_t s) {
+                                     int E, int k, int score, float scaling, void* d_out,
+                                     float* d_prob, float* d_logits, uint16_t* dls, int mp,
+                                     hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (k <= 8)
     combine_bwd_router_kernel<8><<<T, 256, 0, s>>>((const u32x4_t*)dy, (const u32x4_t*)out, row_of,
-                                                   topk_idx, prob, H / 8, E, k, score,
+                                                   topk_idx, prob, H / 8, E, k, score, scaling,
                                                    (u32x4_t*)d_out, d_prob, d_logits, dls, mp);
   else
     combine_bwd_router_kernel<32><<<T, 256, 0, s>>>((const u32x4_t*)dy, (const u32x4_t*)out, row_of,
-                                                    topk_idx, prob, H / 8, E, k, score,
+                                                    topk_idx, prob, H / 8, E, k, score, scaling,
                                                     (u32x4_t*)d_out, d_prob, d_logits, dls, mp);
   return hipGetLastError();
 }
