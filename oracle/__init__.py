@@ -15,4 +15,5 @@ from .moe_oracle import (SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID, SQRTSOFTPLUS
                          silu, grouped_gemm, swiglu_from_gu, expert_mlp, dense_mlp, combine,
                          moe_forward, swiglu_backward, grouped_gemm_dw, moe_backward,
                          gate_logits, router_backward, prob_grad, softplus, score_values,
-                         selection_keys, topk_select_ext, pack_routing_map, expert_bias_update)
+                         selection_keys, topk_select_ext, pack_routing_map, expert_bias_update,
+                         PLACE_COMBINE, PLACE_INPUT)

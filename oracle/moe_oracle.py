@@ -570,17 +570,21 @@ def combine(out_vals, row_of, prob=None, shared_vals=None, exact=False):
     return to_bf16(acc, exact)
 
 
-def prob_grad(dy_vals, out_vals, row_of, exact=False):
+def prob_grad(dy_vals, out_vals, row_of, exact=False, rows_first=False):
     """Gradient of y[t] = sum_j q[t,j] out[row_of[t,j]] (+ shared[t]) with respect to
     the routing weights: d_prob[t,j] = sum_h dy[t,h] * out[row_of[t,j],h], summed in
     float64, one rounding to fp32 [TE-MoE "Token combine": the merging weights are an
-    input of the differentiable combine]. out holds the stored (bf16) expert outputs."""
-    dy = as_values(dy_vals)
-    o = np.asarray(out_vals, dtype=np.float64)
+    input of the differentiable combine]. out holds the stored (bf16) expert outputs.
+    rows_first: the first argument holds the routed rows and the second the token rows
+    (weights applied to the expert inputs: d_prob[t,j] = <dxp[row_of[t,j]], x[t]>)."""
+    a = np.asarray(as_values(dy_vals), dtype=np.float64)
+    b = np.asarray(as_values(out_vals), dtype=np.float64)
+    if rows_first:
+        a, b = b, a
     T, k = row_of.shape
     dq = np.zeros((T, k), dtype=np.float64)
     for j in range(k):
-        dq[:, j] = (dy * o[np.asarray(row_of[:, j], dtype=np.int64)]).sum(axis=1)
+        dq[:, j] = (a * b[np.asarray(row_of[:, j], dtype=np.int64)]).sum(axis=1)
     return to_f32(dq, exact)
 
 
@@ -589,26 +593,39 @@ def prob_grad(dy_vals, out_vals, row_of, exact=False):
 # ---------------------------------------------------------------------------
 
 
+PLACE_COMBINE, PLACE_INPUT = 0, 1
+
+
 def moe_forward(x_bits, logits, w_gu_bits, w_down_bits, k, score, I,
-                shared_gu_bits=None, shared_down_bits=None, fp8=False, exact=False):
+                shared_gu_bits=None, shared_down_bits=None, fp8=False, exact=False,
+                placement=PLACE_COMBINE):
     """Route -> dispatch -> grouped MLP -> combine [TE-MoE "Introduction", the four
     stages; "Example: MoE layer on a single device"]. x and the weights are bf16 bit
     patterns (or float64 values, for the exact-arithmetic pins); logits are float32.
+    placement PLACE_INPUT applies the routing weights to the expert inputs instead of
+    the outputs [TT-1269 MoE.forward, scoring_before_experts: the routed rows are
+    multiplied by their scores in fp32 and cast back to the activation type, and the
+    outputs are summed unweighted]: xp[r] = bf16(q[t,j] * x[t]), y = sum_j out[row_of].
     Returns a dict of every intermediate."""
     x = as_values(x_bits)
     E = logits.shape[1]
     idx, q, counts, rmap, dense = router_topk(logits, k, score, exact)
     offsets, row_of, src_of = dispatch_meta(idx, E)
     xp = x[src_of.astype(np.int64)]
+    if placement == PLACE_INPUT:
+        qr = np.zeros(len(src_of))
+        for j in range(k):
+            qr[row_of[:, j].astype(np.int64)] = q[:, j]
+        xp = to_bf16(xp * qr[:, None], exact)
     mlp = expert_mlp(xp, w_gu_bits, w_down_bits, offsets, I, exact, fp8)
     shared = None
     if shared_gu_bits is not None:
         Is = shared_down_bits.shape[0]
         shared = dense_mlp(x, shared_gu_bits, shared_down_bits, Is, exact)
-    y = combine(mlp["out"], row_of, q, shared, exact)
+    y = combine(mlp["out"], row_of, None if placement == PLACE_INPUT else q, shared, exact)
     res = dict(topk_idx=idx, topk_prob=q, counts=counts, routing_map=rmap, probs_dense=dense,
                offsets=offsets, row_of=row_of, src_of=src_of, xp=xp, shared=shared, y=y,
-               x=x, logits=logits, score=score)
+               x=x, logits=logits, score=score, placement=placement)
     res.update(mlp)
     return res
 
@@ -660,6 +677,7 @@ def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False, w_router_
     """
     dy = as_values(dy_bits)
     row_of, q, offsets = fwd["row_of"], fwd["topk_prob"], fwd["offsets"]
+    place = fwd.get("placement", PLACE_COMBINE)
     T, k = row_of.shape
     N = T * k
     H = dy.shape[1]
@@ -667,7 +685,8 @@ def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False, w_router_
     w_d = np.asarray(w_down_bits)
     d_out = np.zeros((N, H), dtype=np.float64)
     for j in range(k):
-        d_out[row_of[:, j].astype(np.int64)] = to_bf16(dy * q[:, j:j + 1], exact)
+        d_out[row_of[:, j].astype(np.int64)] = (dy if place == PLACE_INPUT else
+                                                to_bf16(dy * q[:, j:j + 1], exact))
     # GEMM2 backward: dh = d_out W_d^T (per expert), then the SwiGLU backward
     dh = grouped_gemm(d_out, np.swapaxes(w_d, 1, 2), offsets, exact)
     g_saved, u_saved = to_bf16(fwd["g"], exact), to_bf16(fwd["u"], exact)
@@ -680,10 +699,14 @@ def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False, w_router_
     res = dict(d_out=d_out, dh=dh, dgu=dgu, dxp=dxp, dw_gu=dw_gu, dw_down=dw_down)
     dx_router = None
     if w_router_bits is not None:
-        d_prob = prob_grad(dy, fwd["out"], row_of, exact)
-        d_logits = router_backward(fwd["logits"], fwd["topk_idx"], d_prob, fwd["score"], exact)
+        # the weights met the expert outputs (combine) or the expert inputs (input)
+        d_prob = (prob_grad(dxp, fwd["x"], row_of, exact, rows_first=True)
+                  if place == PLACE_INPUT else prob_grad(dy, fwd["out"], row_of, exact))
+        d_logits = router_backward(fwd["logits"], fwd["topk_idx"], d_prob, fwd["score"], exact,
+                                   fwd.get("scaling_factor", 1.0))
         dx_router = d_logits @ as_values(w_router_bits)
         res.update(d_prob=d_prob, d_logits=d_logits, dx_router=dx_router,
                    dw_router=to_f32(d_logits.T @ fwd["x"], exact))
-    res["dx"] = combine(dxp, row_of, None, dx_router, exact)
+    # input placement: xp = q x, so dx gets q * dxp
+    res["dx"] = combine(dxp, row_of, q if place == PLACE_INPUT else None, dx_router, exact)
     return res

@@ -80,10 +80,10 @@ def test_sigmoid_gradient_is_derivative_of_each_weight():
         assert np.allclose(got[rows[:, 0], idx[:, j]], fd, rtol=1e-7, atol=1e-10)
 
 
-def _layer(x, w_r, wgu, wd, dy, k, score, I, logits=None):
+def _layer(x, w_r, wgu, wd, dy, k, score, I, logits=None, placement=O.PLACE_COMBINE):
     if logits is None:
         logits = O.gate_logits(x, w_r, exact=True)
-    f = O.moe_forward(x, logits, wgu, wd, k, score, I, exact=True)
+    f = O.moe_forward(x, logits, wgu, wd, k, score, I, exact=True, placement=placement)
     return float((f["y"] * dy).sum()), f
 
 
@@ -92,8 +92,13 @@ def _margin(logits, k):
     return (s[:, k - 1] - s[:, k]).min()
 
 
-@pytest.mark.parametrize("score,k", [(O.SOFTMAX_PRE_RENORM, 3), (O.SOFTMAX_POST, 2), (O.SIGMOID, 2)])
-def test_layer_gradients_through_router_match_finite_differences(score, k):
+@pytest.mark.parametrize("score,k,placement", [(O.SOFTMAX_PRE_RENORM, 3, O.PLACE_COMBINE),
+                                               (O.SOFTMAX_POST, 2, O.PLACE_COMBINE),
+                                               (O.SIGMOID, 2, O.PLACE_COMBINE),
+                                               (O.SQRTSOFTPLUS, 2, O.PLACE_COMBINE),
+                                               (O.SOFTMAX_PRE_RENORM, 3, O.PLACE_INPUT),
+                                               (O.SIGMOID, 1, O.PLACE_INPUT)])
+def test_layer_gradients_through_router_match_finite_differences(score, k, placement):
     T, H, E, I = 6, 16, 7, 8
     rng = np.random.default_rng(30 + score)
     x = rng.standard_normal((T, H))
@@ -101,7 +106,7 @@ def test_layer_gradients_through_router_match_finite_differences(score, k):
     wgu = rng.standard_normal((E, H, 2 * I)) * 0.5
     wd = rng.standard_normal((E, I, H)) * 0.5
     dy = rng.standard_normal((T, H))
-    _, fwd = _layer(x, w_r, wgu, wd, dy, k, score, I)
+    _, fwd = _layer(x, w_r, wgu, wd, dy, k, score, I, placement=placement)
     # the top-k choice must not move under the perturbations below
     assert _margin(fwd["logits"], k) > 1e-3
     g = O.moe_backward(fwd, dy, wgu, wd, I, exact=True, w_router_bits=w_r)
@@ -121,10 +126,12 @@ def test_layer_gradients_through_router_match_finite_differences(score, k):
             fd = (lp - lm) / (2 * eps)
             assert abs(fd - gflat[i]) <= 1e-7 * scale + 1e-6 * abs(fd), (name, i, fd, gflat[i])
 
+    P = placement
     logits = fwd["logits"].copy()
-    check("logits", logits, g["d_logits"], lambda: _layer(x, w_r, wgu, wd, dy, k, score, I, logits)[0])
-    check("w_router", w_r, g["dw_router"], lambda: _layer(x, w_r, wgu, wd, dy, k, score, I)[0])
-    check("x", x, g["dx"], lambda: _layer(x, w_r, wgu, wd, dy, k, score, I)[0])
+    check("logits", logits, g["d_logits"], lambda: _layer(x, w_r, wgu, wd, dy, k, score, I, logits, P)[0])
+    check("w_router", w_r, g["dw_router"], lambda: _layer(x, w_r, wgu, wd, dy, k, score, I, None, P)[0])
+    check("x", x, g["dx"], lambda: _layer(x, w_r, wgu, wd, dy, k, score, I, None, P)[0])
+    check("w_gu", wgu, g["dw_gu"], lambda: _layer(x, w_r, wgu, wd, dy, k, score, I, None, P)[0])
 
 
 def test_backward_without_router_weight_is_unchanged():
@@ -142,3 +149,18 @@ def test_backward_without_router_weight_is_unchanged():
     b = O.moe_backward(f, dy, wgu, wd, I, exact=True, w_router_bits=np.zeros((E, H)))
     assert np.array_equal(a["dx"], b["dx"])
     assert np.array_equal(b["dw_router"], b["d_logits"].T @ x) and b["dw_router"].any()
+
+
+def test_input_placement_equals_combine_placement_for_unit_weights():
+    # top-1 with softmax after the top-k: every weight is exactly 1, so scaling the inputs
+    # or the outputs by it gives bit-identical layers (rounded mode)
+    rng = np.random.default_rng(50)
+    T, H, E, I = 12, 32, 4, 16
+    x = O.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    wgu = O.f32_to_bf16_bits((rng.standard_normal((E, H, 2 * I)) * 0.1).astype(np.float32))
+    wd = O.f32_to_bf16_bits((rng.standard_normal((E, I, H)) * 0.1).astype(np.float32))
+    a = O.moe_forward(x, lg, wgu, wd, 1, O.SOFTMAX_POST, I)
+    b = O.moe_forward(x, lg, wgu, wd, 1, O.SOFTMAX_POST, I, placement=O.PLACE_INPUT)
+    assert (a["topk_prob"] == 1.0).all()
+    assert np.array_equal(a["y"], b["y"])
