@@ -265,6 +265,23 @@ moe_status_t moe_dispatch_backward_router(const void* dxp, const int32_t* row_of
                                           const void* w_router, int T, int H, int E, int k,
                                           void* dx, void* stream);
 
+/* Dispatch backward of a layer whose routing weights scale the expert inputs and which
+ * owns its router projection (torchtitan pull request 1269, MoE.forward,
+ * scoring_before_experts; the weighted dispatch itself is moe_combine_backward applied to
+ * x, and without the router the dispatch backward is moe_unpermute_combine with the
+ * weights). dxp [T*k,H] bf16, x [T,H] bf16, row_of, topk_idx, topk_prob [T,k], w_router
+ * [E,H] bf16, score / scaling_factor as in the forward.
+ *  d_logits [T,E] float32 out: the score-function backward (see
+ *  moe_combine_backward_router) of d_prob_j = <dxp[row_of[t,j]], x[t]>.
+ *  dx [T,H] bf16 out: bf16(sum_j p_j dxp[row_of[t,j]] + sum_j d_logits[t,e_j] w_router[e_j]),
+ *  fp32 sum with one rounding. */
+moe_status_t moe_dispatch_backward_router_input(const void* dxp, const void* x,
+                                                const int32_t* row_of, const int32_t* topk_idx,
+                                                const float* topk_prob, const void* w_router,
+                                                int T, int H, int E, int k, int score,
+                                                float scaling_factor, void* dx, float* d_logits,
+                                                void* stream);
+
 /* ---- whole layer ------------------------------------------------------------ */
 
 typedef struct {
@@ -282,7 +299,14 @@ typedef struct {
   int num_groups;        /* grouped routing, as moe_router_opts_t (0: none) */
   int group_topk;
   float scaling_factor;  /* multiplies the routing weights (0 is taken as 1) */
+  int weight_placement;  /* MOE_PLACE_COMBINE (0): the weights scale the expert outputs in
+                            the combine; MOE_PLACE_INPUT (1, bf16 only): they scale the
+                            routed input rows, xp[r] = bf16(q x[t]), and the combine sums
+                            unweighted (torchtitan pull request 1269, MoE.forward,
+                            scoring_before_experts) */
 } moe_problem_t;
+
+enum { MOE_PLACE_COMBINE = 0, MOE_PLACE_INPUT = 1 };
 
 typedef struct {
   const void* x;              /* [T,H] bf16 */

@@ -20,6 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_BF16, MOE_FP8_E4M3, MOE_FP32 = 0, 1, 2
 MOE_SOFTMAX_PRE_RENORM, MOE_SOFTMAX_POST, MOE_SIGMOID, MOE_SQRTSOFTPLUS = 0, 1, 2, 3
 MOE_GEMM_NN, MOE_GEMM_NT, MOE_GEMM_TN_DW = 0, 1, 2
+MOE_PLACE_COMBINE, MOE_PLACE_INPUT = 0, 1
 
 EXPORTS = [
     "moe_status_str", "moe_router_topk", "moe_permute_workspace_bytes", "moe_permute",
@@ -29,6 +30,7 @@ EXPORTS = [
     "moe_backward", "moe_router_logits", "moe_combine_backward_router",
     "moe_router_weight_grad_workspace_bytes", "moe_router_weight_grad",
     "moe_dispatch_backward_router", "moe_router_topk_ex", "moe_expert_bias_update",
+    "moe_dispatch_backward_router_input",
 ]
 
 
@@ -43,7 +45,7 @@ class Problem(ctypes.Structure):
                 ("k", ctypes.c_int), ("I", ctypes.c_int), ("shared_I", ctypes.c_int),
                 ("score", ctypes.c_int), ("dtype", ctypes.c_int), ("training", ctypes.c_int),
                 ("router", ctypes.c_int), ("num_groups", ctypes.c_int), ("group_topk", ctypes.c_int),
-                ("scaling_factor", ctypes.c_float)]
+                ("scaling_factor", ctypes.c_float), ("weight_placement", ctypes.c_int)]
 
 
 class Tensors(ctypes.Structure):
@@ -97,6 +99,8 @@ def _load():
                                          vp, vp], i),
         "moe_router_topk_ex": ([vp, i, i, i, i, ctypes.POINTER(RouterOpts), vp, vp, vp, vp, vp, vp], i),
         "moe_expert_bias_update": ([vp, vp, i, ctypes.c_float, vp], i),
+        "moe_dispatch_backward_router_input": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, ctypes.c_float,
+                                                vp, vp, vp], i),
         "moe_router_weight_grad_workspace_bytes": ([i, i, i], sz),
         "moe_router_weight_grad": ([vp, vp, i, i, i, vp, vp, sz, vp], i),
         "moe_dispatch_backward_router": ([vp, vp, vp, vp, vp, i, i, i, i, vp, vp], i),
@@ -366,12 +370,27 @@ def moe_dispatch_backward_router(dxp, row_of, topk_idx, d_logits, w_router, dx, 
         _stream(stream)))
 
 
+def moe_dispatch_backward_router_input(dxp, x, row_of, topk_idx, topk_prob, w_router, score, dx,
+                                       d_logits, scaling_factor=1.0, stream=None):
+    T, k = row_of.shape
+    E, H = w_router.shape
+    _want(dxp, torch.bfloat16, (T * k, H), "dxp")
+    _want(x, torch.bfloat16, (T, H), "x")
+    _want(topk_prob, torch.float32, (T, k), "topk_prob")
+    _want(dx, torch.bfloat16, (T, H), "dx")
+    _want(d_logits, torch.float32, (T, E), "d_logits")
+    _check("moe_dispatch_backward_router_input", _lib.moe_dispatch_backward_router_input(
+        _p(dxp), _p(x), _p(row_of), _p(topk_idx), _p(topk_prob), _p(w_router), T, H, E, k,
+        _score(score), float(scaling_factor), _p(dx), _p(d_logits), _stream(stream)))
+
+
 # ---- whole layer -----------------------------------------------------------------------
 
 def problem(T, H, E, k, I, score, shared_I=0, dtype=MOE_BF16, training=False, router=False,
-            num_groups=0, group_topk=0, scaling_factor=1.0):
+            num_groups=0, group_topk=0, scaling_factor=1.0, weight_placement=MOE_PLACE_COMBINE):
     return Problem(T, H, E, k, I, shared_I, _score(score), dtype, int(bool(training)),
-                   int(bool(router)), int(num_groups), int(group_topk), float(scaling_factor))
+                   int(bool(router)), int(num_groups), int(group_topk), float(scaling_factor),
+                   int(weight_placement))
 
 
 def moe_workspace_bytes(prob: Problem):

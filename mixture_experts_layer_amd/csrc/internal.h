@@ -71,6 +71,13 @@ hipError_t launch_combine_bwd_router(const void* dy, const void* out, const int3
                                      int E, int k, int score, float scaling, void* d_out,
                                      float* d_prob, float* d_logits, uint16_t* dls, int mp,
                                      hipStream_t s);
+// Dispatch backward when the routing weights scale the expert inputs (with the router
+// projection): d_prob = <dxp, x>, d_logits (+ split halves), dx = sum q dxp + router term.
+hipError_t launch_dispatch_bwd_router_input(const void* dxp, const void* x, const int32_t* row_of,
+                                            const int32_t* topk_idx, const float* prob,
+                                            const void* w_router, int T, int H, int E, int k,
+                                            int score, float scaling, void* dx, float* d_logits,
+                                            uint16_t* dls, int mp, hipStream_t s);
 hipError_t launch_router_wgrad_reduce(const float* part, int S, int E, int H, int mp, float* dw,
                                       hipStream_t s);
 hipError_t launch_router_split(const float* d_logits, int T, int E, int mp, uint16_t* dls,

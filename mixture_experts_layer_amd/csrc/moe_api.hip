@@ -130,6 +130,9 @@ moe_status_t check_problem(const moe_problem_t* p) {
   moe_status_t so = make_router_opts(p->E, p->k, p->score, nullptr, p->num_groups, p->group_topk,
                                      p->scaling_factor, 0, &o);
   if (so != MOE_OK) return so;
+  if (p->weight_placement != MOE_PLACE_COMBINE && p->weight_placement != MOE_PLACE_INPUT)
+    return MOE_ERR_INVALID_ARG;
+  if (p->weight_placement == MOE_PLACE_INPUT && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (p->dtype == MOE_FP8_E4M3) {
     if (p->H % 128 || p->I % 128) return MOE_ERR_UNSUPPORTED;
     if (p->training || p->shared_I) return MOE_ERR_UNSUPPORTED;
@@ -432,6 +435,26 @@ moe_status_t moe_dispatch_backward_router(const void* dxp, const int32_t* row_of
                                                k, dx, S(stream)));
 }
 
+moe_status_t moe_dispatch_backward_router_input(const void* dxp, const void* x,
+                                                const int32_t* row_of, const int32_t* topk_idx,
+                                                const float* topk_prob, const void* w_router,
+                                                int T, int H, int E, int k, int score,
+                                                float scaling_factor, void* dx, float* d_logits,
+                                                void* stream) {
+  moe_status_t st = check_shape(T, H, E, k);
+  if (st != MOE_OK) return st;
+  if (!valid_score(score)) return MOE_ERR_INVALID_ARG;
+  if (!(scaling_factor == scaling_factor) || scaling_factor == INFINITY || scaling_factor == -INFINITY)
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(dxp) || !ok_ptr(x) || !ok_ptr(row_of) || !ok_ptr(topk_idx) || !ok_ptr(topk_prob) ||
+      !ok_ptr(w_router) || !ok_ptr(dx) || !ok_ptr(d_logits))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_dispatch_bwd_router_input(
+      dxp, x, row_of, topk_idx, topk_prob, w_router, T, H, E, k, score,
+      scaling_factor == 0.f ? 1.f : scaling_factor, dx, d_logits, nullptr, 0, S(stream)));
+}
+
 moe_status_t moe_quantize_fp8_rows(const void* x, int R, int C, uint8_t* q, float* scale,
                                    void* stream) {
   if (R < 0 || C <= 0) return MOE_ERR_INVALID_ARG;
@@ -537,8 +560,10 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   // 2. dispatch: counts, offsets, row maps from the histograms, then the row copies
   MOE_TRY(launch_dispatch_from_hist(v.topk_idx, T, E, k, chunk_tokens, (int32_t*)v.scratch,
                                     v.counts, v.offsets, v.row_of, v.src_of, s));
+  const bool at_input = p->weight_placement == MOE_PLACE_INPUT;
   if (fp8) MOE_TRY(launch_scatter_rows_fp8(t->x, v.row_of, T, H, k, (uint8_t*)v.xp, v.xp_scale, s));
-  else MOE_TRY(launch_scatter_rows(t->x, v.row_of, nullptr, T, H, k, v.xp, s));
+  else MOE_TRY(launch_scatter_rows(t->x, v.row_of, at_input ? v.topk_prob : nullptr, T, H, k,
+                                   v.xp, s));
   // 3. grouped MLP. A dense shared expert of the routed experts' width runs as one more
   // group of T rows (offsets[E+1] = N + T) in the same two launches, reading x, its own
   // weights and its own outputs; other widths, and training, launch it separately.
@@ -626,8 +651,8 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
     MOE_TRY(launch_grouped_gemm(s2, s));
   }
   // 4. combine
-  MOE_TRY(launch_combine(v.out, v.row_of, v.topk_prob, p->shared_I ? v.shared_out : nullptr, T, H,
-                         k, t->y, s));
+  MOE_TRY(launch_combine(v.out, v.row_of, at_input ? nullptr : v.topk_prob,
+                         p->shared_I ? v.shared_out : nullptr, T, H, k, t->y, s));
   return MOE_OK;
 }
 
@@ -649,9 +674,13 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   hipStream_t s = S(stream);
   const int T = p->T, H = p->H, E = p->E, k = p->k, I = p->I;
   const int N = T * k;
+  const bool at_input = p->weight_placement == MOE_PLACE_INPUT;
   if (T == 0) {
     // no routed rows: the weight gradients are zero (the dW GEMMs see empty groups)
     MOE_TRY(launch_fill_i32(v.offsets, E + 1, 0, s));
+  } else if (at_input) {
+    // the combine was unweighted: d_out[row_of[t,j]] = dy[t]
+    MOE_TRY(launch_scatter_rows(dy, v.row_of, nullptr, T, H, k, v.d_out, s));
   } else if (p->router) {
     // combine backward with the routing-weight gradient: d_out, d_logits and the split
     // operand of the router weight gradient
@@ -663,10 +692,11 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
     // combine backward: d_out[row_of[t,j]] = bf16(p[t,j] * dy[t])
     MOE_TRY(launch_scatter_rows(dy, v.row_of, v.topk_prob, T, H, k, v.d_out, s));
   }
-  if (p->router)
-    MOE_TRY(launch_router_wgrad(t->x, (const uint16_t*)v.router_ws, T, H, E,
-                                (float*)((uint8_t*)v.router_ws + router_wgrad_dls_bytes(T, E)),
-                                t->dw_router, s));
+  float* const r_part = p->router ? (float*)((uint8_t*)v.router_ws + router_wgrad_dls_bytes(T, E))
+                                   : nullptr;
+  const float r_scale = p->scaling_factor == 0.f ? 1.f : p->scaling_factor;
+  if (p->router && !at_input)
+    MOE_TRY(launch_router_wgrad(t->x, (const uint16_t*)v.router_ws, T, H, E, r_part, t->dw_router, s));
   // GEMM2 backward: dgu = SwiGLU'(d_out . W_down^T), dW_down = h^T . d_out
   GemmParams a{};
   a.mode = MOE_GEMM_NT;
@@ -719,12 +749,21 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   d.N = 2 * I;
   d.C = dw_gu;
   MOE_TRY(launch_grouped_gemm(d, s));
-  // dispatch backward: dx[t] = sum_j dxp[row_of[t,j]] (+ the router's term)
-  if (p->router)
+  // dispatch backward: dx[t] = sum_j dxp[row_of[t,j]] (weighted when the weights scaled the
+  // inputs; + the router's term)
+  if (p->router && at_input) {
+    MOE_TRY(launch_dispatch_bwd_router_input(v.dxp, t->x, v.row_of, v.topk_idx, v.topk_prob,
+                                             t->w_router, T, H, E, k, p->score, r_scale, dx,
+                                             v.d_logits, (uint16_t*)v.router_ws,
+                                             router_split_cols(E), s));
+    MOE_TRY(launch_router_wgrad(t->x, (const uint16_t*)v.router_ws, T, H, E, r_part, t->dw_router, s));
+  } else if (p->router) {
     MOE_TRY(launch_dispatch_bwd_router(v.dxp, v.row_of, v.topk_idx, v.d_logits, t->w_router, T, H,
                                        E, k, dx, s));
-  else
-    MOE_TRY(launch_combine(v.dxp, v.row_of, nullptr, nullptr, T, H, k, dx, s));
+  } else {
+    MOE_TRY(launch_combine(v.dxp, v.row_of, at_input ? v.topk_prob : nullptr, nullptr, T, H, k, dx,
+                           s));
+  }
   return MOE_OK;
 }
 

@@ -141,52 +141,15 @@ hipError_t launch_router_logits(const void* x, const void* w_router, int T, int 
 // values are also written as two bf16 halves, hi = bf16(d) at column e and
 // lo = bf16(d - hi) at column E + e of a row of `mp` columns (zero past 2E): the operand
 // of the router weight-gradient GEMM, which so keeps about 16 bits of each value.
-template <int KM>  // a bound on k: 8 or 32
-__global__ __launch_bounds__(256) void combine_bwd_router_kernel(
-    const u32x4_t* __restrict__ dy, const u32x4_t* __restrict__ out,
-    const int32_t* __restrict__ row_of, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ prob, int H8, int E, int k, int score, float scaling,
-    u32x4_t* __restrict__ d_out,
-    float* __restrict__ d_prob, float* __restrict__ d_logits, uint16_t* __restrict__ dls, int mp) {
-  __shared__ int rows[32], ids[32];
-  __shared__ float p[32], red[4][32], dl_s[32];
-  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < k) {
-    rows[tid] = row_of[(size_t)t * k + tid];
-    ids[tid] = topk_idx[(size_t)t * k + tid];
-    p[tid] = prob[(size_t)t * k + tid];
-  }
-  __syncthreads();
-  float dot[KM];
-#pragma unroll
-  for (int j = 0; j < KM; ++j) dot[j] = 0.f;
-  for (int v = tid; v < H8; v += 256) {
-    const u32x4_t g = dy[(size_t)t * H8 + v];
-#pragma unroll
-    for (int j0 = 0; j0 < KM; j0 += 8) {
-      if (j0 >= k) continue;  // (continue, not break: the loop stays unrolled)
-      u32x4_t o[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        if (j0 + jj < k) o[jj] = __builtin_nontemporal_load(&out[(size_t)rows[j0 + jj] * H8 + v]);
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        if (j0 + jj >= k) continue;
-        float s = dot[j0 + jj];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          s = fmaf(bf16lo(g[d]), bf16lo(o[jj][d]), s);
-          s = fmaf(bf16hi(g[d]), bf16hi(o[jj][d]), s);
-        }
-        dot[j0 + jj] = s;
-        const float q = p[j0 + jj];
-        u32x4_t w;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) w[d] = pack_bf16x2(q * bf16lo(g[d]), q * bf16hi(g[d]));
-        __builtin_nontemporal_store(w, &d_out[(size_t)rows[j0 + jj] * H8 + v]);
-      }
-    }
-  }
+
+// The block's k partial dot products -> d_prob (optional), the score-function backward
+// -> dl_s[k] in LDS, the token's d_logits row and its split halves. Every thread calls it.
+template <int KM>
+MOE_DEV void router_score_bwd(const float (&dot)[KM], int t, int E, int k, int score,
+                              float scaling, const float* p, const int* ids, float (*red)[32],
+                              float* dl_s, float* __restrict__ d_prob,
+                              float* __restrict__ d_logits, uint16_t* __restrict__ dls, int mp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
     if (j >= k) continue;
@@ -227,6 +190,150 @@ __global__ __launch_bounds__(256) void combine_bwd_router_kernel(
   }
   if (dls)
     for (int c = 2 * E + tid; c < mp; c += 256) dls[(size_t)t * mp + c] = 0;
+}
+
+template <int KM>  // a bound on k: 8 or 32
+__global__ __launch_bounds__(256) void combine_bwd_router_kernel(
+    const u32x4_t* __restrict__ dy, const u32x4_t* __restrict__ out,
+    const int32_t* __restrict__ row_of, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ prob, int H8, int E, int k, int score, float scaling,
+    u32x4_t* __restrict__ d_out,
+    float* __restrict__ d_prob, float* __restrict__ d_logits, uint16_t* __restrict__ dls, int mp) {
+  __shared__ int rows[32], ids[32];
+  __shared__ float p[32], red[4][32], dl_s[32];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < k) {
+    rows[tid] = row_of[(size_t)t * k + tid];
+    ids[tid] = topk_idx[(size_t)t * k + tid];
+    p[tid] = prob[(size_t)t * k + tid];
+  }
+  __syncthreads();
+  float dot[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) dot[j] = 0.f;
+  for (int v = tid; v < H8; v += 256) {
+    const u32x4_t g = dy[(size_t)t * H8 + v];
+#pragma unroll
+    for (int j0 = 0; j0 < KM; j0 += 8) {
+      if (j0 >= k) continue;  // (continue, not break: the loop stays unrolled)
+      u32x4_t o[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if (j0 + jj < k) o[jj] = __builtin_nontemporal_load(&out[(size_t)rows[j0 + jj] * H8 + v]);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj >= k) continue;
+        float s = dot[j0 + jj];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          s = fmaf(bf16lo(g[d]), bf16lo(o[jj][d]), s);
+          s = fmaf(bf16hi(g[d]), bf16hi(o[jj][d]), s);
+        }
+        dot[j0 + jj] = s;
+        const float q = p[j0 + jj];
+        u32x4_t w;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) w[d] = pack_bf16x2(q * bf16lo(g[d]), q * bf16hi(g[d]));
+        __builtin_nontemporal_store(w, &d_out[(size_t)rows[j0 + jj] * H8 + v]);
+      }
+    }
+  }
+  router_score_bwd<KM>(dot, t, E, k, score, scaling, p, ids, red, dl_s, d_prob, d_logits, dls, mp);
+}
+
+// ---- dispatch backward of a layer that weights the expert inputs ---------------------------
+// torchtitan pull request 1269, MoE.forward with scoring_before_experts: xp = q x, so
+// dx[t] = sum_j q_j dxp[row_j] and d_prob_j = <dxp[row_j], x[t]>. One block per token:
+// pass 1 reads x[t] and the k dxp rows and reduces the k dot products, the score-function
+// backward follows (router_score_bwd), and pass 2 writes dx[t] = bf16(sum_j q_j dxp[row_j]
+// + sum_j d_logits[t,e_j] W_r[e_j]) (fp32 sum, one rounding; the dxp rows were just read,
+// so the second read comes from cache).
+template <int KM>
+__global__ __launch_bounds__(256) void dispatch_bwd_router_input_kernel(
+    const u32x4_t* __restrict__ dxp, const u32x4_t* __restrict__ x,
+    const int32_t* __restrict__ row_of, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ prob, const u32x4_t* __restrict__ w_router, int H8, int E, int k,
+    int score, float scaling, u32x4_t* __restrict__ dx, float* __restrict__ d_logits,
+    uint16_t* __restrict__ dls, int mp) {
+  __shared__ int rows[32], ids[32];
+  __shared__ float p[32], red[4][32], dl_s[32];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < k) {
+    rows[tid] = row_of[(size_t)t * k + tid];
+    ids[tid] = topk_idx[(size_t)t * k + tid];
+    p[tid] = prob[(size_t)t * k + tid];
+  }
+  __syncthreads();
+  float dot[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) dot[j] = 0.f;
+  for (int v = tid; v < H8; v += 256) {
+    const u32x4_t xv = x[(size_t)t * H8 + v];
+#pragma unroll
+    for (int j0 = 0; j0 < KM; j0 += 8) {
+      if (j0 >= k) continue;
+      u32x4_t o[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if (j0 + jj < k) o[jj] = dxp[(size_t)rows[j0 + jj] * H8 + v];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj >= k) continue;
+        float s = dot[j0 + jj];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          s = fmaf(bf16lo(xv[d]), bf16lo(o[jj][d]), s);
+          s = fmaf(bf16hi(xv[d]), bf16hi(o[jj][d]), s);
+        }
+        dot[j0 + jj] = s;
+      }
+    }
+  }
+  router_score_bwd<KM>(dot, t, E, k, score, scaling, p, ids, red, dl_s, nullptr, d_logits, dls, mp);
+  for (int v = tid; v < H8; v += 256) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const u32x4_t o = dxp[(size_t)rows[j] * H8 + v];
+      const float q = p[j];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc[2 * d] = fmaf(q, bf16lo(o[d]), acc[2 * d]);
+        acc[2 * d + 1] = fmaf(q, bf16hi(o[d]), acc[2 * d + 1]);
+      }
+    }
+    for (int j = 0; j < k; ++j) {
+      const u32x4_t wv = w_router[(size_t)ids[j] * H8 + v];
+      const float g = dl_s[j];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc[2 * d] = fmaf(g, bf16lo(wv[d]), acc[2 * d]);
+        acc[2 * d + 1] = fmaf(g, bf16hi(wv[d]), acc[2 * d + 1]);
+      }
+    }
+    u32x4_t ov;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) ov[d] = pack_bf16x2(acc[2 * d], acc[2 * d + 1]);
+    dx[(size_t)t * H8 + v] = ov;
+  }
+}
+
+hipError_t launch_dispatch_bwd_router_input(const void* dxp, const void* x, const int32_t* row_of,
+                                            const int32_t* topk_idx, const float* prob,
+                                            const void* w_router, int T, int H, int E, int k,
+                                            int score, float scaling, void* dx, float* d_logits,
+                                            uint16_t* dls, int mp, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (k <= 8)
+    dispatch_bwd_router_input_kernel<8><<<T, 256, 0, s>>>(
+        (const u32x4_t*)dxp, (const u32x4_t*)x, row_of, topk_idx, prob, (const u32x4_t*)w_router,
+        H / 8, E, k, score, scaling, (u32x4_t*)dx, d_logits, dls, mp);
+  else
+    dispatch_bwd_router_input_kernel<32><<<T, 256, 0, s>>>(
+        (const u32x4_t*)dxp, (const u32x4_t*)x, row_of, topk_idx, prob, (const u32x4_t*)w_router,
+        H / 8, E, k, score, scaling, (u32x4_t*)dx, d_logits, dls, mp);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine_bwd_router(const void* dy, const void* out, const int32_t* row_of,

@@ -239,3 +239,82 @@ def test_layer_with_router(name):
         rel = np.linalg.norm(got - r) / max(np.linalg.norm(r), 1e-30)
         _say(f"{name} {key}: rel_l2={rel:.3e}")
         assert np.isfinite(got).all() and rel <= 1e-2, (key, rel)
+
+
+# ---- routing weights applied to the expert inputs ------------------------------------------
+
+@pytest.mark.parametrize("T,H,E,k,score", [(300, 256, 16, 4, O.SOFTMAX_PRE_RENORM),
+                                           (65, 512, 8, 1, O.SIGMOID)])
+def test_dispatch_backward_router_input(T, H, E, k, score):
+    _say("dispatch backward router (input placement)", T, H, E, k, score)
+    rng = np.random.default_rng(5 * T + k)
+    logits, idx, q, row_of = _routing(rng, T, E, k, score)
+    dxp, x, w = _bf(rng, (T * k, H)), _bf(rng, (T, H)), _bf(rng, (E, H), 0.02)
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    d_logits = torch.full((T, E), float("nan"), device="cuda")
+    M.moe_dispatch_backward_router_input(dev_bf16(dxp), dev_bf16(x), dev(row_of), dev(idx),
+                                         dev(q.astype(np.float32)), dev_bf16(w), score, dx, d_logits)
+    torch.cuda.synchronize()
+    dxpv, xv = O.as_values(dxp), O.as_values(x)
+    ref_dq = O.prob_grad(dxpv, xv, row_of, rows_first=True)
+    ref_dl = O.router_backward(logits, idx, ref_dq, score)
+    absdot = np.stack([(np.abs(xv) * np.abs(dxpv[row_of[:, j]])).sum(axis=1) for j in range(k)], 1)
+    b_dq = H * 2.0 ** -24 * absdot + 2.0 ** -24 * np.abs(ref_dq)
+    u = 2.0 ** -24
+    if score == O.SIGMOID:
+        b_sel = q * (1 - q) * b_dq + 8 * u * q * np.abs(ref_dq)
+    else:
+        s_b = (q * b_dq).sum(axis=1, keepdims=True)
+        s_abs = (q * np.abs(ref_dq)).sum(axis=1, keepdims=True)
+        b_sel = q * (b_dq + s_b) + (k + 8) * u * q * (np.abs(ref_dq) + s_abs)
+    bound = np.zeros((T, E))
+    bound[np.arange(T)[:, None], idx] = b_sel
+    got_dl = host_vals(d_logits)
+    check_close(got_dl, ref_dl, bound, "d_logits (input)", floor=1e-12 * np.abs(ref_dl).max())
+    # dx from the device's own d_logits would feed a device value into the reference;
+    # the oracle's d_logits differs from it by at most `bound`, far below a bf16 ulp of dx
+    ref_dx = O.combine(dxpv, row_of, q, ref_dl @ O.as_values(w))
+    check_bf16(host_vals(dx), ref_dx, "dx (input)", slack=combine_slack(dxpv, row_of, q))
+
+
+@pytest.mark.parametrize("router", [False, True])
+def test_layer_input_placement(router):
+    w = W.custom("inp", T=257, H=256, E=32, k=8, I=192, training=True)
+    _say("layer, weights on the inputs, router", router)
+    d = W.make_inputs(w)
+    g = GpuMoE(w, d, router=router)
+    g.prob.weight_placement = M.MOE_PLACE_INPUT
+    y = host_vals(g.forward())
+    if router:
+        ref_logits, same, clean = _router_choice(w, d, g)
+    else:
+        ref_logits, same, clean = d["logits"], np.ones(w.T, bool), np.ones(w.E, bool)
+    ref = O.moe_forward(d["x"], ref_logits, d["w_gu"], d["w_down"], w.k, w.score, w.I,
+                        placement=O.PLACE_INPUT)
+    if same.all():
+        ints = g.ints()
+        for key in ("topk_idx", "offsets", "row_of"):
+            assert np.array_equal(ints[key], ref[key]), key
+        # the scaled input rows: one fp32 product and one bf16 rounding, with the device's
+        # weight within 1e-6 of the oracle's, so at most one bf16 ulp apart
+        xp = host_vals(g.view("xp", (w.T * w.k, w.H), torch.bfloat16))
+        from gpu_helpers import bf16_ulp
+        assert (np.abs(xp - ref["xp"]) <= bf16_ulp(ref["xp"]) * (1 + 1e-9)).all()
+    S = np.nonzero(same)[0]
+    check_bf16(y[S], ref["y"][S], "input-placement y",
+               slack=combine_slack(ref["out"], ref["row_of"])[S])
+    g.backward(d["dy"])
+    rb = O.moe_backward(ref, d["dy"], d["w_gu"], d["w_down"], w.I,
+                        w_router_bits=d["w_router"] if router else None)
+    check_bf16(host_vals(g.dx)[S], rb["dx"][S], "input-placement dx",
+               slack=combine_slack(rb["dxp"], ref["row_of"], ref["topk_prob"])[S])
+    C = np.nonzero(clean)[0]
+    check_bf16(host_vals(g.dw_gu)[C], rb["dw_gu"][C], "input-placement dw_gu")
+    check_bf16(host_vals(g.dw_down)[C], rb["dw_down"][C], "input-placement dw_down")
+    if router:
+        dl = host_vals(g.view("d_logits", (w.T, w.E), torch.float32))
+        for key, got, r in (("d_logits", dl[S], rb["d_logits"][S]),
+                            ("dw_router", host_vals(g.dw_router)[C], rb["dw_router"][C])):
+            rel = np.linalg.norm(got - r) / max(np.linalg.norm(r), 1e-30)
+            _say(f"input placement {key}: rel_l2={rel:.3e}")
+            assert np.isfinite(got).all() and rel <= 1e-2, (key, rel)
