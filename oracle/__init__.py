@@ -16,4 +16,4 @@ from .moe_oracle import (SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID, SQRTSOFTPLUS
                          moe_forward, swiglu_backward, grouped_gemm_dw, moe_backward,
                          gate_logits, router_backward, prob_grad, softplus, score_values,
                          selection_keys, topk_select_ext, pack_routing_map, expert_bias_update,
-                         PLACE_COMBINE, PLACE_INPUT)
+                         PLACE_COMBINE, PLACE_INPUT, dispatch_meta_padded)

@@ -423,6 +423,29 @@ def dispatch_meta(idx: np.ndarray, E: int):
     return offsets.astype(np.int32), row_of.reshape(T, k).astype(np.int32), src_of.astype(np.int32)
 
 
+def dispatch_meta_padded(idx: np.ndarray, E: int, align: int):
+    """Padded dispatch layout [TE-MoE "Padding and alignment": each expert's block is
+    rounded up to a multiple of align_size rows, and the per-expert padding offsets let
+    combine drop the padding; "Receive buffer": counts 129 and 127 need 384 rows at
+    alignment 128].
+
+    Block e starts at offsets[e] = sum over e' < e of ceil(count_e' / align) * align; its
+    tokens keep the unpadded order (dispatch_meta) and are followed by its padding rows.
+    pad_offsets[e] = offsets[e] - (unpadded start of e). src_of is -1 on padding rows.
+    Returns offsets [E+1], pad_offsets [E], row_of [T,k], src_of [offsets[E]].
+    """
+    off_u, row_u, src_u = dispatch_meta(idx, E)
+    counts = np.diff(off_u)
+    padded = -(-counts // align) * align
+    offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+    pad_offsets = (offsets[:E] - off_u[:E]).astype(np.int32)
+    e_of = np.asarray(idx, dtype=np.int64)
+    row_of = (row_u + pad_offsets[e_of]).astype(np.int32)
+    src_of = np.full(int(offsets[E]), -1, dtype=np.int32)
+    src_of[row_of.reshape(-1)] = np.repeat(np.arange(idx.shape[0]), idx.shape[1])
+    return offsets, pad_offsets, row_of, src_of
+
+
 def permute(x_bits: np.ndarray, src_of: np.ndarray) -> np.ndarray:
     """Token dispatch gather: row r of the permuted buffer is token src_of[r]
     [TE-MoE "Token dispatch"]. A bit copy."""

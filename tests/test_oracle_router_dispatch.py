@@ -164,3 +164,29 @@ def test_weights_applied_once():
     # applying them twice is not the same thing
     c = O.combine(out * qp[:, None], row_of, q, exact=True)
     assert not np.allclose(a, c)
+
+
+def test_padded_dispatch_receive_buffer_example():
+    # the pages' example: counts of 129 and 127 need 384 rows at alignment 128
+    idx = np.array([[0]] * 129 + [[1]] * 127, dtype=np.int32)
+    offsets, pad, row_of, src_of = O.dispatch_meta_padded(idx, 2, 128)
+    assert offsets.tolist() == [0, 256, 384]
+    assert pad.tolist() == [0, 127]
+    assert row_of[128, 0] == 128 and row_of[129, 0] == 256 and row_of[-1, 0] == 382
+    assert (src_of[129:256] == -1).all() and src_of[383] == -1 and src_of[256] == 129
+
+
+def test_padded_dispatch_shifts_the_plain_layout():
+    rng = np.random.default_rng(9)
+    T, E, k = 97, 10, 3
+    idx = O.topk_select(rng.standard_normal((T, E)).astype(np.float32), k)
+    off_u, row_u, src_u = O.dispatch_meta(idx, E)
+    for align in (1, 8, 64):
+        offsets, pad, row_of, src_of = O.dispatch_meta_padded(idx, E, align)
+        assert (offsets % align == 0).all() and (np.diff(offsets) >= np.diff(off_u)).all()
+        assert (np.diff(offsets) - np.diff(off_u) < align).all()
+        assert np.array_equal(row_of - pad[idx], row_u)          # same order, shifted blocks
+        assert np.array_equal(src_of[src_of >= 0], src_u)        # token rows in plain order
+        assert (src_of >= 0).sum() == T * k
+    offsets1, pad1, row1, src1 = O.dispatch_meta_padded(idx, E, 1)
+    assert np.array_equal(offsets1, off_u) and not pad1.any() and np.array_equal(row1, row_u)
