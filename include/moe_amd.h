@@ -153,6 +153,24 @@ moe_status_t moe_permute(const void* x, const int32_t* topk_idx, int T, int H, i
                          int32_t* row_of, int32_t* src_of, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* Rows a padded dispatch needs at most: T*k + E*(align-1) (align > 1), else T*k (guide,
+ * "Receive buffer": counts of 129 and 127 need 384 rows at alignment 128). */
+size_t moe_padded_rows(int T, int E, int k, int align);
+
+/* Padded token dispatch (guide, "Padding and alignment"): moe_permute with every expert
+ * block rounded up to a multiple of `align` rows (1 <= align <= 4096).
+ *  xp [moe_padded_rows(T,E,k,align), H] (bf16, or e4m3 with xp_scale): token rows at
+ *  row_of, padding rows zero (fp8 scale 1); rows past offsets[E] are not written.
+ *  offsets [E+1] out: padded block starts (offsets[E] = the padded total).
+ *  pad_offsets [E] out: padding rows before block e (cumulative; 0 for e = 0).
+ *  src_of [moe_padded_rows] out: token of each row, -1 for padding rows.
+ *  ws: at least moe_permute_workspace_bytes(T,E,k) bytes. Combine needs nothing more:
+ *  row_of already points into the padded layout. */
+moe_status_t moe_permute_padded(const void* x, const int32_t* topk_idx, int T, int H, int E,
+                                int k, int align, int out_dtype, void* xp, float* xp_scale,
+                                int32_t* offsets, int32_t* pad_offsets, int32_t* row_of,
+                                int32_t* src_of, void* ws, size_t ws_bytes, void* stream);
+
 /* Grouped GEMM1 with the SwiGLU epilogue (guide, "Grouped MLP": FC1 with the
  * activation fused, FC2 separate; te_mixtral.py _expert_ffn: gate/up fused weight,
  * silu(gate) * up).
@@ -304,6 +322,10 @@ typedef struct {
                             routed input rows, xp[r] = bf16(q x[t]), and the combine sums
                             unweighted (torchtitan pull request 1269, MoE.forward,
                             scoring_before_experts) */
+  int align_size;        /* 0 or 1: no padding. Else a padded dispatch (guide, "Padding and
+                            alignment"): every expert block starts at a multiple of
+                            align_size rows (<= 4096), padding rows are zero; the row
+                            buffers hold T*k + E*(align_size-1) rows */
 } moe_problem_t;
 
 enum { MOE_PLACE_COMBINE = 0, MOE_PLACE_INPUT = 1 };
@@ -328,7 +350,7 @@ typedef struct {
   int32_t* topk_idx;   /* [T,k] */
   float* topk_prob;    /* [T,k] */
   int32_t* counts;     /* [E] */
-  int32_t* offsets;    /* [E+1] */
+  int32_t* offsets;    /* [E+1] (padded block starts when align_size > 1) */
   int32_t* row_of;     /* [T,k] */
   int32_t* src_of;     /* [T*k] */
   void* xp;            /* [T*k,H] bf16 (or e4m3) */
@@ -346,6 +368,8 @@ typedef struct {
   void* dxp;           /* [T*k,H] bf16 (training) */
   void* scratch;       /* moe_permute scratch */
   size_t scratch_bytes;
+  int32_t* pad_offsets; /* [E] padding before each expert block (align_size > 1) */
+  int rows;            /* rows of the expert-contiguous buffers below: T*k (+ padding) */
   float* logits;       /* [T,E] (router = 1) */
   float* d_logits;     /* [T,E] (router = 1, training) */
   void* router_ws;     /* moe_router_weight_grad scratch (router = 1, training) */

@@ -30,7 +30,7 @@ EXPORTS = [
     "moe_backward", "moe_router_logits", "moe_combine_backward_router",
     "moe_router_weight_grad_workspace_bytes", "moe_router_weight_grad",
     "moe_dispatch_backward_router", "moe_router_topk_ex", "moe_expert_bias_update",
-    "moe_dispatch_backward_router_input",
+    "moe_dispatch_backward_router_input", "moe_padded_rows", "moe_permute_padded",
 ]
 
 
@@ -45,7 +45,8 @@ class Problem(ctypes.Structure):
                 ("k", ctypes.c_int), ("I", ctypes.c_int), ("shared_I", ctypes.c_int),
                 ("score", ctypes.c_int), ("dtype", ctypes.c_int), ("training", ctypes.c_int),
                 ("router", ctypes.c_int), ("num_groups", ctypes.c_int), ("group_topk", ctypes.c_int),
-                ("scaling_factor", ctypes.c_float), ("weight_placement", ctypes.c_int)]
+                ("scaling_factor", ctypes.c_float), ("weight_placement", ctypes.c_int),
+                ("align_size", ctypes.c_int)]
 
 
 class Tensors(ctypes.Structure):
@@ -65,7 +66,8 @@ class Views(ctypes.Structure):
                 ("topk_idx", "topk_prob", "counts", "offsets", "row_of", "src_of", "xp",
                  "xp_scale", "gu", "h", "hq", "h_scale", "out", "shared_h", "shared_out",
                  "shared_offsets", "d_out", "dgu", "dxp", "scratch")] + \
-               [("scratch_bytes", ctypes.c_size_t)] + \
+               [("scratch_bytes", ctypes.c_size_t), ("pad_offsets", ctypes.c_void_p),
+                ("rows", ctypes.c_int)] + \
                [(n, ctypes.c_void_p) for n in ("logits", "d_logits", "router_ws")] + \
                [("router_ws_bytes", ctypes.c_size_t)]
 
@@ -101,6 +103,8 @@ def _load():
         "moe_expert_bias_update": ([vp, vp, i, ctypes.c_float, vp], i),
         "moe_dispatch_backward_router_input": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, ctypes.c_float,
                                                 vp, vp, vp], i),
+        "moe_padded_rows": ([i, i, i, i], sz),
+        "moe_permute_padded": ([vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp], i),
         "moe_router_weight_grad_workspace_bytes": ([i, i, i], sz),
         "moe_router_weight_grad": ([vp, vp, i, i, i, vp, vp, sz, vp], i),
         "moe_dispatch_backward_router": ([vp, vp, vp, vp, vp, i, i, i, i, vp, vp], i),
@@ -229,6 +233,28 @@ def moe_permute(x, topk_idx, E, xp, offsets, row_of, src_of, ws, out_dtype=MOE_B
     _check("moe_permute", _lib.moe_permute(
         _p(x), _p(topk_idx), T, H, E, k, out_dtype, _p(xp), _p(xp_scale), _p(offsets),
         _p(row_of), _p(src_of), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_padded_rows(T, E, k, align):
+    return int(_lib.moe_padded_rows(T, E, k, align))
+
+
+def moe_permute_padded(x, topk_idx, E, align, xp, offsets, pad_offsets, row_of, src_of, ws,
+                       out_dtype=MOE_BF16, xp_scale=None, stream=None):
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    R = moe_padded_rows(T, E, k, align)
+    _want(x, torch.bfloat16, (T, H), "x")
+    _want(topk_idx, torch.int32, (T, k), "topk_idx")
+    _want(xp, torch.bfloat16 if out_dtype == MOE_BF16 else torch.uint8, (R, H), "xp")
+    _want(offsets, torch.int32, (E + 1,), "offsets")
+    _want(pad_offsets, torch.int32, (E,), "pad_offsets")
+    _want(row_of, torch.int32, (T, k), "row_of")
+    _want(src_of, torch.int32, (R,), "src_of")
+    _check("moe_permute_padded", _lib.moe_permute_padded(
+        _p(x), _p(topk_idx), T, H, E, k, align, out_dtype, _p(xp), _p(xp_scale), _p(offsets),
+        _p(pad_offsets), _p(row_of), _p(src_of), _p(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
 
 
 def moe_grouped_gemm_swiglu(xp, w_gu, offsets, h, gu_saved=None, dtype=MOE_BF16, xp_scale=None,
@@ -387,10 +413,11 @@ def moe_dispatch_backward_router_input(dxp, x, row_of, topk_idx, topk_prob, w_ro
 # ---- whole layer -----------------------------------------------------------------------
 
 def problem(T, H, E, k, I, score, shared_I=0, dtype=MOE_BF16, training=False, router=False,
-            num_groups=0, group_topk=0, scaling_factor=1.0, weight_placement=MOE_PLACE_COMBINE):
+            num_groups=0, group_topk=0, scaling_factor=1.0, weight_placement=MOE_PLACE_COMBINE,
+            align_size=0):
     return Problem(T, H, E, k, I, shared_I, _score(score), dtype, int(bool(training)),
                    int(bool(router)), int(num_groups), int(group_topk), float(scaling_factor),
-                   int(weight_placement))
+                   int(weight_placement), int(align_size))
 
 
 def moe_workspace_bytes(prob: Problem):

@@ -40,11 +40,20 @@ hipError_t launch_router_hist(const float* logits, int T, int E, int k, int scor
 constexpr int kPermChunk = 256;  // flattened (token, slot) entries per dispatch chunk
 size_t permute_scratch_bytes(int T, int E, int k);
 int router_chunk_tokens(int T);
+// align > 1: padded dispatch (blocks rounded up to multiples of align; offsets padded,
+// pad_offsets [E] = padding before each block when given).
 hipError_t launch_dispatch_from_hist(const int32_t* topk_idx, int T, int E, int k, int chunk_tokens,
                                      int32_t* partial, int32_t* counts, int32_t* offsets,
-                                     int32_t* row_of, int32_t* src_of, hipStream_t s);
+                                     int32_t* row_of, int32_t* src_of, hipStream_t s,
+                                     int align = 1, int32_t* pad_offsets = nullptr);
 hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, int32_t* offsets,
-                                int32_t* row_of, int32_t* src_of, void* scratch, hipStream_t s);
+                                int32_t* row_of, int32_t* src_of, void* scratch, hipStream_t s,
+                                int align = 1, int32_t* pad_offsets = nullptr,
+                                int32_t* counts = nullptr);
+// zero the padding rows of a padded dispatch (and set their fp8 scale 1 and src_of -1)
+hipError_t launch_zero_pad_rows(const int32_t* offsets, const int32_t* counts, int E,
+                                int row_bytes, void* rows, float* scale, int32_t* src_of,
+                                hipStream_t s);
 hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, const float* prob, int T,
                                int H, int k, void* xp, hipStream_t s);
 hipError_t launch_scatter_rows_fp8(const void* x, const int32_t* row_of, int T, int H, int k,

@@ -38,10 +38,11 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace layout of moe_forward / moe_backward. Every region is 256-byte aligned.
 struct Layout {
-  size_t topk_idx, topk_prob, counts, offsets, row_of, src_of, shared_offsets;
+  size_t topk_idx, topk_prob, counts, offsets, pad_offsets, row_of, src_of, shared_offsets;
   size_t xp, xp_scale, gu, h, hq, h_scale, out, shared_h, shared_out;
   size_t d_out, dgu, dxp, scratch, scratch_bytes;
   size_t logits, d_logits, router_ws, router_ws_bytes, total;
+  size_t rows;  // rows of the expert-contiguous buffers
 };
 
 // Scratch of the router weight gradient: the split d_logits operand [T, mp] bf16, then the
@@ -54,7 +55,9 @@ size_t router_wgrad_bytes(int T, int H, int E) {
 
 Layout make_layout(const moe_problem_t& p) {
   Layout L{};
-  const size_t N = (size_t)p.T * p.k;
+  const size_t NT = (size_t)p.T * p.k;  // routed (token, choice) pairs
+  // rows of the expert-contiguous buffers: the pairs, plus the padding of a padded dispatch
+  const size_t N = NT + (p.align_size > 1 ? (size_t)p.E * (p.align_size - 1) : 0);
   const bool fp8 = p.dtype == MOE_FP8_E4M3;
   const size_t act = fp8 ? 1 : 2;
   size_t o = 0;
@@ -63,11 +66,12 @@ Layout make_layout(const moe_problem_t& p) {
     o += align_up(bytes);
     return at;
   };
-  L.topk_idx = take(N * 4);
-  L.topk_prob = take(N * 4);
+  L.topk_idx = take(NT * 4);
+  L.topk_prob = take(NT * 4);
   L.counts = take((size_t)p.E * 4);
   L.offsets = take(((size_t)p.E + 2) * 4);  // one more end for a fused shared group
-  L.row_of = take(N * 4);
+  L.pad_offsets = take((size_t)p.E * 4);
+  L.row_of = take(NT * 4);
   L.src_of = take(N * 4);
   L.shared_offsets = take(2 * 4);
   L.xp = take(N * p.H * act);
@@ -89,6 +93,7 @@ Layout make_layout(const moe_problem_t& p) {
   L.router_ws_bytes = p.router && p.training ? router_wgrad_bytes(p.T, p.H, p.E) : 0;
   L.router_ws = take(L.router_ws_bytes);
   L.total = o;
+  L.rows = N;
   return L;
 }
 
@@ -133,6 +138,8 @@ moe_status_t check_problem(const moe_problem_t* p) {
   if (p->weight_placement != MOE_PLACE_COMBINE && p->weight_placement != MOE_PLACE_INPUT)
     return MOE_ERR_INVALID_ARG;
   if (p->weight_placement == MOE_PLACE_INPUT && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (p->align_size < 0) return MOE_ERR_INVALID_ARG;
+  if (p->align_size > 4096) return MOE_ERR_UNSUPPORTED;
   if (p->dtype == MOE_FP8_E4M3) {
     if (p->H % 128 || p->I % 128) return MOE_ERR_UNSUPPORTED;
     if (p->training || p->shared_I) return MOE_ERR_UNSUPPORTED;
@@ -246,6 +253,42 @@ moe_status_t moe_permute(const void* x, const int32_t* topk_idx, int T, int H, i
   MOE_TRY(launch_dispatch_meta(topk_idx, T, E, k, offsets, row_of, src_of, ws, s));
   if (out_dtype == MOE_BF16) MOE_TRY(launch_scatter_rows(x, row_of, nullptr, T, H, k, xp, s));
   else MOE_TRY(launch_scatter_rows_fp8(x, row_of, T, H, k, (uint8_t*)xp, xp_scale, s));
+  return MOE_OK;
+}
+
+size_t moe_padded_rows(int T, int E, int k, int align) {
+  if (T < 0 || E <= 0 || k <= 0 || align < 0) return 0;
+  return (size_t)T * k + (align > 1 ? (size_t)E * (align - 1) : 0);
+}
+
+moe_status_t moe_permute_padded(const void* x, const int32_t* topk_idx, int T, int H, int E,
+                                int k, int align, int out_dtype, void* xp, float* xp_scale,
+                                int32_t* offsets, int32_t* pad_offsets, int32_t* row_of,
+                                int32_t* src_of, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_shape(T, H, E, k);
+  if (st != MOE_OK) return st;
+  if (align < 1) return MOE_ERR_INVALID_ARG;
+  if (align > 4096) return MOE_ERR_UNSUPPORTED;
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (out_dtype == MOE_FP8_E4M3 && H % 16) return MOE_ERR_UNSUPPORTED;
+  if (!ok_ptr(offsets) || !ok_ptr(pad_offsets) || !ok_ptr(ws)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < permute_scratch_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
+  if (T > 0) {
+    if (!ok_ptr(x) || !ok_ptr(topk_idx) || !ok_ptr(xp) || !ok_ptr(row_of) || !ok_ptr(src_of))
+      return MOE_ERR_INVALID_ARG;
+    if (out_dtype == MOE_FP8_E4M3 && !ok_ptr(xp_scale)) return MOE_ERR_INVALID_ARG;
+  }
+  hipStream_t s = S(stream);
+  const int nchunks = (T * k + kPermChunk - 1) / kPermChunk;
+  int32_t* counts = (int32_t*)ws + (size_t)2 * nchunks * E;  // after histograms and row bases
+  MOE_TRY(launch_dispatch_meta(topk_idx, T, E, k, offsets, row_of, src_of, ws, s, align,
+                               pad_offsets, counts));
+  if (T == 0) return MOE_OK;
+  const bool fp8 = out_dtype == MOE_FP8_E4M3;
+  if (!fp8) MOE_TRY(launch_scatter_rows(x, row_of, nullptr, T, H, k, xp, s));
+  else MOE_TRY(launch_scatter_rows_fp8(x, row_of, T, H, k, (uint8_t*)xp, xp_scale, s));
+  MOE_TRY(launch_zero_pad_rows(offsets, counts, E, fp8 ? H : 2 * H, xp, fp8 ? xp_scale : nullptr,
+                               src_of, s));
   return MOE_OK;
 }
 
@@ -489,6 +532,8 @@ moe_status_t moe_workspace_views(const moe_problem_t* p, void* ws, size_t ws_byt
   v->topk_prob = (float*)(b + L.topk_prob);
   v->counts = (int32_t*)(b + L.counts);
   v->offsets = (int32_t*)(b + L.offsets);
+  v->pad_offsets = (int32_t*)(b + L.pad_offsets);
+  v->rows = (int)(L.rows);
   v->row_of = (int32_t*)(b + L.row_of);
   v->src_of = (int32_t*)(b + L.src_of);
   v->xp = b + L.xp;
@@ -537,7 +582,8 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   if (st != MOE_OK) return st;
   hipStream_t s = S(stream);
   const int T = p->T, H = p->H, E = p->E, k = p->k, I = p->I;
-  const int N = T * k;
+  const int N = v.rows;  // T*k, plus the padding rows of a padded dispatch
+  const int align = p->align_size > 1 ? p->align_size : 1;
 
   // 1. router (projection first when the layer owns it), writing per-chunk expert
   //    histograms (no atomics)
@@ -559,7 +605,11 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
                               (int32_t*)v.scratch, nullptr, nullptr, chunk_tokens, s));
   // 2. dispatch: counts, offsets, row maps from the histograms, then the row copies
   MOE_TRY(launch_dispatch_from_hist(v.topk_idx, T, E, k, chunk_tokens, (int32_t*)v.scratch,
-                                    v.counts, v.offsets, v.row_of, v.src_of, s));
+                                    v.counts, v.offsets, v.row_of, v.src_of, s, align,
+                                    v.pad_offsets));
+  if (align > 1)  // zero padding rows (fp8: scale 1), src_of -1
+    MOE_TRY(launch_zero_pad_rows(v.offsets, v.counts, E, fp8 ? H : 2 * H, v.xp,
+                                 fp8 ? v.xp_scale : nullptr, v.src_of, s));
   const bool at_input = p->weight_placement == MOE_PLACE_INPUT;
   if (fp8) MOE_TRY(launch_scatter_rows_fp8(t->x, v.row_of, T, H, k, (uint8_t*)v.xp, v.xp_scale, s));
   else MOE_TRY(launch_scatter_rows(t->x, v.row_of, at_input ? v.topk_prob : nullptr, T, H, k,
@@ -567,7 +617,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   // 3. grouped MLP. A dense shared expert of the routed experts' width runs as one more
   // group of T rows (offsets[E+1] = N + T) in the same two launches, reading x, its own
   // weights and its own outputs; other widths, and training, launch it separately.
-  const bool fuse_shared = p->shared_I == I && !p->training && !fp8;
+  const bool fuse_shared = p->shared_I == I && !p->training && !fp8 && align == 1;
   if (fuse_shared) MOE_TRY(launch_fill_i32(v.offsets + E + 1, 1, N + T, s));
   GemmParams g1{};
   g1.mode = fp8 ? MOE_GEMM_NT : MOE_GEMM_NN;
@@ -673,7 +723,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   if (st != MOE_OK) return st;
   hipStream_t s = S(stream);
   const int T = p->T, H = p->H, E = p->E, k = p->k, I = p->I;
-  const int N = T * k;
+  const int N = v.rows;  // T*k, plus the padding rows of a padded dispatch
   const bool at_input = p->weight_placement == MOE_PLACE_INPUT;
   if (T == 0) {
     // no routed rows: the weight gradients are zero (the dW GEMMs see empty groups)
@@ -697,6 +747,8 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   const float r_scale = p->scaling_factor == 0.f ? 1.f : p->scaling_factor;
   if (p->router && !at_input)
     MOE_TRY(launch_router_wgrad(t->x, (const uint16_t*)v.router_ws, T, H, E, r_part, t->dw_router, s));
+  if (p->align_size > 1 && T > 0)  // the padding rows of d_out are zero
+    MOE_TRY(launch_zero_pad_rows(v.offsets, v.counts, E, 2 * H, v.d_out, nullptr, nullptr, s));
   // GEMM2 backward: dgu = SwiGLU'(d_out . W_down^T), dW_down = h^T . d_out
   GemmParams a{};
   a.mode = MOE_GEMM_NT;

@@ -33,7 +33,8 @@ size_t permute_scratch_bytes(int T, int E, int k) {
   const size_t a = (n + kPermChunk - 1) / kPermChunk;
   const int ct = router_chunk_tokens(T);
   const size_t b = ((size_t)T + ct - 1) / ct;
-  return 2 * (a > b ? a : b) * (size_t)E * sizeof(int32_t);
+  // per-chunk histograms and row bases, then the per-expert counts of a padded dispatch
+  return (2 * (a > b ? a : b) + 1) * (size_t)E * sizeof(int32_t);
 }
 
 __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ idx, int n,
@@ -56,11 +57,16 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
 // sums them; totals -> counts and offsets (exclusive scan over e); then each thread writes
 // the running row base of its chunks.
 constexpr int SCAN_BATCH = 64;
+// align > 1 (padded dispatch, guide "Padding and alignment"): every expert block is
+// rounded up to a multiple of align rows; offsets are the padded block starts and
+// pad_offsets[e] (when given) the padding before block e.
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ partial,
                                                              int nchunks, int E,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ chunk_base) {
+                                                             int32_t* __restrict__ chunk_base,
+                                                             int align,
+                                                             int32_t* __restrict__ pad_offsets) {
   __shared__ int psum[1024];
   __shared__ int s[256];
   const int EP = E <= 64 ? 64 : (E <= 128 ? 128 : 256);
@@ -86,25 +92,34 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
     tot += x;
     if (q < part) before += x;
   }
-  // inclusive scan of the totals over e: within each wave by shuffles, then the wave
-  // totals (at most four waves: EP <= 256) added from LDS
+  // inclusive scan over e of the (padded) block sizes: within each wave by shuffles, then
+  // the wave totals (at most four waves: EP <= 256) added from LDS
   __shared__ int wtot[4];
-  int incl = e < E ? tot : 0;
-  if (part == 0) {
+  const int ptot = align > 1 ? (tot + align - 1) / align * align : tot;
+  auto scan = [&](int val) -> int {  // returns the inclusive scan, s[] holds it for every e
+    int incl = e < E ? val : 0;
+    if (part == 0) {
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if ((e & 63) >= o) incl += y;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if ((e & 63) >= o) incl += y;
+      }
+      if ((e & 63) == 63) wtot[e >> 6] = incl;
     }
-    if ((e & 63) == 63) wtot[e >> 6] = incl;
+    __syncthreads();
+    if (part == 0) {
+      for (int q = 0; q < (e >> 6); ++q) incl += wtot[q];
+      s[e] = incl;
+    }
+    __syncthreads();
+    return s[e];
+  };
+  if (pad_offsets) {
+    const int pincl = scan(ptot - tot);
+    if (part == 0 && e < E) pad_offsets[e] = pincl - (ptot - tot);
+    __syncthreads();
   }
-  __syncthreads();
-  if (part == 0) {
-    for (int q = 0; q < (e >> 6); ++q) incl += wtot[q];
-    s[e] = incl;
-  }
-  __syncthreads();
-  const int excl = s[e] - tot;
+  const int excl = scan(ptot) - ptot;
   if (part == 0 && e < E) {
     offsets[e] = excl;
     if (counts) counts[e] = tot;
@@ -165,14 +180,20 @@ __global__ __launch_bounds__(64) void dispatch_rank_kernel(const int32_t* __rest
 }
 
 hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, int32_t* offsets,
-                                int32_t* row_of, int32_t* src_of, void* scratch, hipStream_t s) {
+                                int32_t* row_of, int32_t* src_of, void* scratch, hipStream_t s,
+                                int align, int32_t* pad_offsets, int32_t* counts) {
   const int n = T * k;
   const int nchunks = (n + kPermChunk - 1) / kPermChunk;
   int32_t* partial = (int32_t*)scratch;
   int32_t* chunk_base = partial + (size_t)nchunks * E;
-  if (n == 0) return launch_fill_i32(offsets, E + 1, 0, s);
+  if (n == 0) {
+    hipError_t e = pad_offsets ? launch_fill_i32(pad_offsets, E, 0, s) : hipSuccess;
+    if (e == hipSuccess && counts) e = launch_fill_i32(counts, E, 0, s);
+    return e == hipSuccess ? launch_fill_i32(offsets, E + 1, 0, s) : e;
+  }
   dispatch_hist_kernel<<<nchunks, 256, 0, s>>>(topk_idx, n, E, partial);
-  dispatch_scan_kernel<<<1, 1024, 0, s>>>(partial, nchunks, E, nullptr, offsets, chunk_base);
+  dispatch_scan_kernel<<<1, 1024, 0, s>>>(partial, nchunks, E, counts, offsets, chunk_base, align,
+                                          pad_offsets);
   dispatch_rank_kernel<<<nchunks, 64, 0, s>>>(topk_idx, n, k, E, kPermChunk, chunk_base, row_of,
                                               src_of);
   return hipGetLastError();
@@ -180,12 +201,17 @@ hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, in
 
 hipError_t launch_dispatch_from_hist(const int32_t* topk_idx, int T, int E, int k, int chunk_tokens,
                                      int32_t* partial, int32_t* counts, int32_t* offsets,
-                                     int32_t* row_of, int32_t* src_of, hipStream_t s) {
+                                     int32_t* row_of, int32_t* src_of, hipStream_t s, int align,
+                                     int32_t* pad_offsets) {
   const int n = T * k;
-  if (n == 0) return launch_fill_i32(offsets, E + 1, 0, s);
+  if (n == 0) {
+    hipError_t e = pad_offsets ? launch_fill_i32(pad_offsets, E, 0, s) : hipSuccess;
+    return e == hipSuccess ? launch_fill_i32(offsets, E + 1, 0, s) : e;
+  }
   const int nchunks = (T + chunk_tokens - 1) / chunk_tokens;
   int32_t* chunk_base = partial + (size_t)nchunks * E;
-  dispatch_scan_kernel<<<1, 1024, 0, s>>>(partial, nchunks, E, counts, offsets, chunk_base);
+  dispatch_scan_kernel<<<1, 1024, 0, s>>>(partial, nchunks, E, counts, offsets, chunk_base, align,
+                                          pad_offsets);
   dispatch_rank_kernel<<<nchunks, 64, 0, s>>>(topk_idx, n, k, E, chunk_tokens * k, chunk_base,
                                               row_of, src_of);
   return hipGetLastError();
@@ -224,6 +250,34 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, const float
                                int H, int k, void* xp, hipStream_t s) {
   if (T == 0) return hipSuccess;
   scatter_rows_kernel<<<T, 256, 0, s>>>((const u32x4_t*)x, row_of, prob, H / 8, k, (u32x4_t*)xp);
+  return hipGetLastError();
+}
+
+// Padding rows of a padded dispatch (guide, "Padding and alignment"): block e's rows
+// [offsets[e] + counts[e], offsets[e+1]) get zeros (row16 16-byte words each), scale 1
+// (fp8) and src_of -1. One block per expert.
+__global__ __launch_bounds__(256) void zero_pad_rows_kernel(const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ counts,
+                                                            int row16, u32x4_t* __restrict__ rows,
+                                                            float* __restrict__ scale,
+                                                            int32_t* __restrict__ src_of) {
+  const int e = blockIdx.x;
+  const int r0 = offsets[e] + counts[e], r1 = offsets[e + 1];
+  const size_t n = (size_t)(r1 - r0) * row16;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  if (rows)
+    for (size_t i = threadIdx.x; i < n; i += 256) rows[(size_t)r0 * row16 + i] = z;
+  for (int r = r0 + (int)threadIdx.x; r < r1; r += 256) {
+    if (scale) scale[r] = 1.f;
+    if (src_of) src_of[r] = -1;
+  }
+}
+
+hipError_t launch_zero_pad_rows(const int32_t* offsets, const int32_t* counts, int E,
+                                int row_bytes, void* rows, float* scale, int32_t* src_of,
+                                hipStream_t s) {
+  zero_pad_rows_kernel<<<E, 256, 0, s>>>(offsets, counts, row_bytes / 16, (u32x4_t*)rows, scale,
+                                         src_of);
   return hipGetLastError();
 }
 
