@@ -179,6 +179,17 @@ def main():
     ap.add_argument("--router", action="store_true",
                     help="the layer owns its router projection: logits = x . W_r^T in the "
                          "forward, d_logits, dW_r and the router's dx term in the backward")
+    ap.add_argument("--groups", type=int, nargs=2, metavar=("NUM_GROUPS", "GROUP_TOPK"),
+                    help="grouped routing: experts in NUM_GROUPS groups, top-k from GROUP_TOPK")
+    ap.add_argument("--expert-bias", action="store_true",
+                    help="an expert selection bias (sigmoid / sqrtsoftplus scores only)")
+    ap.add_argument("--score", choices=["softmax_pre_renorm", "softmax_post", "sigmoid",
+                                        "sqrtsoftplus"],
+                    help="override the workload's score function")
+    ap.add_argument("--scaling", type=float, default=1.0, help="routing-weight scaling factor")
+    ap.add_argument("--placement", choices=["combine", "input"], default="combine",
+                    help="apply the routing weights to the expert outputs (combine) or inputs")
+    ap.add_argument("--align", type=int, default=0, help="padded dispatch alignment (rows)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch each stage once plus a 256 MiB calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -226,10 +237,20 @@ def main():
     router = args.router
     w_router = bf(d["w_router"]) if router else None
     dw_router = torch.empty((w.E, w.H), dtype=torch.float32, device=dev) if router else None
-    prob = M.problem(w.T, w.H, w.E, w.k, w.I, w.score, w.shared_I, dtype, training, router)
+    score = M._score(args.score) if args.score else w.score
+    if score != w.score:
+        import dataclasses
+        w = dataclasses.replace(w, score=score)
+    groups = args.groups or (0, 0)
+    e_bias = (torch.randn(w.E, generator=torch.Generator().manual_seed(0)) * 0.1).to(dev) \
+        if args.expert_bias else None
+    placement = M.MOE_PLACE_INPUT if args.placement == "input" else M.MOE_PLACE_COMBINE
+    prob = M.problem(w.T, w.H, w.E, w.k, w.I, w.score, w.shared_I, dtype, training, router,
+                     groups[0], groups[1], args.scaling, placement, args.align)
     ws = torch.zeros(M.moe_workspace_bytes(prob), dtype=torch.uint8, device=dev)
     tens = M.tensors(x, None if router else logits, w_gu, w_down, y, w_gu_s, w_down_s, shared_gu,
-                     shared_down, w_router, dw_router)
+                     shared_down, w_router, dw_router, e_bias)
+    router_opts = M.router_opts(e_bias, groups[0], groups[1], args.scaling)
     if training:
         dy = bf(d["dy"])
         dx = torch.empty_like(x)
@@ -276,7 +297,7 @@ def main():
     # ---- per-kernel durations with HIP events on the launch stream -----------------
     stream = torch.cuda.current_stream()
     v = M.moe_workspace_views(prob, ws)
-    N, H, I, E, k, T = w.T * w.k, w.H, w.I, w.E, w.k, w.T
+    N, H, I, E, k, T = v.rows, w.H, w.I, w.E, w.k, w.T  # rows: T*k (+ padding capacity)
     vt = lambda name, shape, dt: M.view_tensor(getattr(v, name), shape, dt, ws)
     offs = vt("offsets", (E + 1,), torch.int32)
     row_of = vt("row_of", (T, k), torch.int32)
@@ -296,9 +317,13 @@ def main():
     counts = vt("counts", (E,), torch.int32)
 
     launches = {
-        "router": lambda: M.moe_router_topk(logits, k, w.score, idx_t, topk_prob, counts),
-        "permute": lambda: M.moe_permute(x, idx_t, E, xp, offs, row_of, src_of, scratch,
-                                         dtype, xp_scale),
+        "router": lambda: M.moe_router_topk_ex(logits, k, w.score, router_opts, idx_t, topk_prob,
+                                               counts),
+        "permute": (lambda: M.moe_permute_padded(
+            x, idx_t, E, args.align, xp, offs, vt("pad_offsets", (E,), torch.int32), row_of,
+            src_of, scratch, dtype, xp_scale)) if args.align > 1 else
+                   (lambda: M.moe_permute(x, idx_t, E, xp, offs, row_of, src_of, scratch,
+                                          dtype, xp_scale)),
         "gemm1_swiglu": lambda: M.moe_grouped_gemm_swiglu(xp, w_gu, offs, h, gu, dtype,
                                                           xp_scale, w_gu_s),
         "gemm2": (lambda: M.moe_grouped_gemm(M.MOE_GEMM_NT, hq, w_down, offs, out, dtype,
@@ -444,9 +469,14 @@ def main():
         "config": {"workload": f"{w.name}-shaped MoE block " + ("with its router projection " if router else "")
                    + ("forward+backward" if training else "forward"),
                    "T": w.T, "H": w.H, "E": w.E, "top_k": w.k, "I": w.I, "shared_I": w.shared_I,
-                   "score": ["softmax_pre_renorm", "softmax_post", "sigmoid"][w.score],
+                   "score": ["softmax_pre_renorm", "softmax_post", "sigmoid", "sqrtsoftplus"][w.score],
                    "parallelism": "single GPU", "active_experts": active,
-                   "launch": "hip_graph" if graph is not None else "eager", "router": router},
+                   "launch": "hip_graph" if graph is not None else "eager", "router": router,
+                   **({"groups": list(groups)} if groups[0] else {}),
+                   **({"expert_bias": True} if e_bias is not None else {}),
+                   **({"scaling": args.scaling} if args.scaling != 1.0 else {}),
+                   **({"placement": "input"} if placement == M.MOE_PLACE_INPUT else {}),
+                   **({"align": args.align} if args.align > 1 else {})},
         "grouped_gemm_tflops": round(gemm_flops / gemm_time / 1e12, 1),
         "grouped_gemm_mfma_frac": round(gemm_flops / gemm_time / 1e12 / peak_tf, 4),
         "gemm": gemm,

@@ -152,6 +152,13 @@ def _want(t, dtype, shape, name):
         raise ValueError(f"{name}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
 
 
+def _want_rows(t, dtype, min_rows, cols, name):
+    """A routed-row buffer: at least min_rows rows (a padded dispatch has more) of cols."""
+    if t.dtype != dtype or t.dim() != 2 or t.shape[0] < min_rows or t.shape[1] != cols:
+        raise ValueError(f"{name}: expected {dtype} [>= {min_rows}, {cols}], got {t.dtype} "
+                         f"{tuple(t.shape)}")
+
+
 _SCORE = {"softmax_pre_renorm": MOE_SOFTMAX_PRE_RENORM, "softmax_post": MOE_SOFTMAX_POST,
           "sigmoid": MOE_SIGMOID, "sqrtsoftplus": MOE_SQRTSOFTPLUS}
 
@@ -310,7 +317,7 @@ def moe_set_gemm_max_blocks(max_blocks):
 def moe_unpermute_combine(y_perm, row_of, topk_prob, y, shared_out=None, stream=None):
     T, k = row_of.shape
     H = y.shape[1]
-    _want(y_perm, torch.bfloat16, (y_perm.shape[0], H), "y_perm")
+    _want_rows(y_perm, torch.bfloat16, T * k, H, "y_perm")
     _want(y, torch.bfloat16, (T, H), "y")
     _check("moe_unpermute_combine", _lib.moe_unpermute_combine(
         _p(y_perm), _p(row_of), _p(topk_prob), _p(shared_out), T, H, k, _p(y), _stream(stream)))
@@ -319,7 +326,7 @@ def moe_unpermute_combine(y_perm, row_of, topk_prob, y, shared_out=None, stream=
 def moe_combine_backward(dy, row_of, topk_prob, d_out, stream=None):
     T, k = row_of.shape
     H = dy.shape[1]
-    _want(d_out, torch.bfloat16, (T * k, H), "d_out")
+    _want_rows(d_out, torch.bfloat16, T * k, H, "d_out")
     _check("moe_combine_backward", _lib.moe_combine_backward(
         _p(dy), _p(row_of), _p(topk_prob), T, H, k, _p(d_out), _stream(stream)))
 
@@ -356,10 +363,10 @@ def moe_combine_backward_router(dy, expert_out, row_of, topk_idx, topk_prob, sco
     H = dy.shape[1]
     E = d_logits.shape[1]
     _want(dy, torch.bfloat16, (T, H), "dy")
-    _want(expert_out, torch.bfloat16, (T * k, H), "expert_out")
+    _want_rows(expert_out, torch.bfloat16, T * k, H, "expert_out")
     _want(topk_idx, torch.int32, (T, k), "topk_idx")
     _want(topk_prob, torch.float32, (T, k), "topk_prob")
-    _want(d_out, torch.bfloat16, (T * k, H), "d_out")
+    _want_rows(d_out, torch.bfloat16, T * k, H, "d_out")
     _want(d_logits, torch.float32, (T, E), "d_logits")
     if d_prob is not None:
         _want(d_prob, torch.float32, (T, k), "d_prob")
@@ -387,7 +394,7 @@ def moe_router_weight_grad(x, d_logits, dw_router, ws, stream=None):
 def moe_dispatch_backward_router(dxp, row_of, topk_idx, d_logits, w_router, dx, stream=None):
     T, k = row_of.shape
     E, H = w_router.shape
-    _want(dxp, torch.bfloat16, (T * k, H), "dxp")
+    _want_rows(dxp, torch.bfloat16, T * k, H, "dxp")
     _want(topk_idx, torch.int32, (T, k), "topk_idx")
     _want(d_logits, torch.float32, (T, E), "d_logits")
     _want(dx, torch.bfloat16, (T, H), "dx")
@@ -400,7 +407,7 @@ def moe_dispatch_backward_router_input(dxp, x, row_of, topk_idx, topk_prob, w_ro
                                        d_logits, scaling_factor=1.0, stream=None):
     T, k = row_of.shape
     E, H = w_router.shape
-    _want(dxp, torch.bfloat16, (T * k, H), "dxp")
+    _want_rows(dxp, torch.bfloat16, T * k, H, "dxp")
     _want(x, torch.bfloat16, (T, H), "x")
     _want(topk_prob, torch.float32, (T, k), "topk_prob")
     _want(dx, torch.bfloat16, (T, H), "dx")

@@ -245,7 +245,9 @@ hipError_t launch_router_ext(const float* logits, int T, int E, int k, int score
     if (err != hipSuccess) return err;
   }
   if (T == 0) return hipSuccess;
-  int blocks = hist ? (T + chunk_tokens - 1) / chunk_tokens : (T + 3) / 4;
+  // without histograms: 16 tokens per block (four per wave), so the per-block count
+  // atomics at the end stay few
+  int blocks = hist ? (T + chunk_tokens - 1) / chunk_tokens : (T + 15) / 16;
   if (!hist && blocks > 2048) blocks = 2048;
 #define MOE_ROUTER_EXT(n)                                                                   \
   case n:                                                                                   \
