@@ -16,4 +16,5 @@ from .moe_oracle import (SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID, SQRTSOFTPLUS
                          moe_forward, swiglu_backward, grouped_gemm_dw, moe_backward,
                          gate_logits, router_backward, prob_grad, softplus, score_values,
                          selection_keys, topk_select_ext, pack_routing_map, expert_bias_update,
-                         PLACE_COMBINE, PLACE_INPUT, dispatch_meta_padded)
+                         PLACE_COMBINE, PLACE_INPUT, dispatch_meta_padded,
+                         MX_BLOCK, quantize_mx_e4m3, mx_decode, grouped_gemm_mx, expert_mlp_mx)

@@ -469,6 +469,55 @@ def quantize_rows_e4m3(vals: np.ndarray):
     return q, s
 
 
+MX_BLOCK = 32
+
+
+def quantize_mx_e4m3(vals: np.ndarray):
+    """MXFP8 quantisation along the last axis: e4m3 elements with one E8M0 (power-of-two)
+    scale per block of 32 consecutive values [TE-MIX: the mxfp8 recipe, te_mixtral_mxfp8
+    and FP8GlobalStateManager.get_fp8_recipe().mxfp8(); the pages name the recipe only].
+
+    READING, from the OCP Microscaling (MX) v1.0 conversion of a block: X = 2^(floor(
+    log2(amax)) - 8), 8 being the largest e4m3 exponent, clamped to [2^-127, 2^127]; the
+    codes are e4m3_encode(v / X) (an exact division by a power of two; nearest-even,
+    saturating to +-448, which values in [448, 512) * X reach); an all-zero block takes
+    X = 2^-127. Returns codes [.., C] uint8 and scale bytes [.., C/32] uint8 (the
+    exponent of X plus 127).
+    """
+    v = np.asarray(vals, dtype=np.float64).astype(np.float32).astype(np.float64)
+    C = v.shape[-1]
+    assert C % MX_BLOCK == 0
+    blk = v.reshape(v.shape[:-1] + (C // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(blk).max(axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))     # amax = m * 2^ex, m in [0.5, 1)
+    se = np.where(amax > 0, np.clip(ex - 1 - 8, -127, 127), -127)
+    codes = e4m3_encode((blk / np.exp2(se)[..., None]).astype(np.float32))
+    return codes.reshape(v.shape), (se + 127).astype(np.uint8)
+
+
+def mx_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """float64 values of MXFP8 codes with their block scale bytes (2^(byte - 127))."""
+    c = np.asarray(codes)
+    vals = e4m3_decode(c).reshape(c.shape[:-1] + (c.shape[-1] // MX_BLOCK, MX_BLOCK))
+    vals = vals * np.exp2(np.asarray(scales, np.float64) - 127.0)[..., None]
+    return vals.reshape(c.shape)
+
+
+def grouped_gemm_mx(qa, sa, qb, sb, offsets, exact=False):
+    """MXFP8 grouped GEMM, C = A_e B_e^T per expert block with the block scales of both
+    operands along K: C[r, n] = fp32( sum over blocks b of X_a[r,b] X_b[n,b] *
+    sum_{k in b} P_a[r,k] P_b[n,k] ), summed in float64 (every product is exact).
+    qa [N, K] codes, sa [N, K/32]; qb [E, Ncol, K] codes, sb [E, Ncol, K/32]."""
+    a = mx_decode(qa, sa)
+    E = qb.shape[0]
+    out = np.zeros((a.shape[0], qb.shape[1]), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            out[r0:r1] = to_f32(a[r0:r1] @ mx_decode(qb[e], sb[e]).T, exact)
+    return out
+
+
 def quantize_cols_e4m3(w_vals: np.ndarray):
     """Per-output-channel e4m3 quantisation of expert weights [.., K, N]: one scale per
     (expert, column) over the K (reduction) dimension. Same rounding rule as
@@ -528,6 +577,26 @@ def swiglu_from_gu(g, u, exact=False):
     """h = silu(g) * u from float32 g, u, then fp32 -> bf16 [TT-1269 GroupedExperts:
     silu(x w1) * (x w3); TE-MIX _expert_ffn: silu(gate) * up]."""
     return to_bf16(silu(g) * u, exact)
+
+
+def expert_mlp_mx(xp_vals, w_gu_vals, w_down_vals, offsets, I, exact=False):
+    """The grouped SwiGLU MLP in the MXFP8 recipe [TE-MIX mxfp8; TE-MoE "Grouped GEMM":
+    the expert GEMMs run in the recipe's precision]: x rows and (bf16) h rows are
+    quantised per 32-element block along K; each expert's weights per output channel and
+    32-element block along K (the GEMM's reduction axis), offline. g, u fp32, h bf16,
+    out bf16 as in the other recipes."""
+    qx, sx = quantize_mx_e4m3(xp_vals)
+    E = len(w_gu_vals)
+    qw = [quantize_mx_e4m3(as_values(w_gu_vals[e]).T) for e in range(E)]
+    gu = grouped_gemm_mx(qx, sx, np.stack([q for q, _ in qw]), np.stack([s_ for _, s_ in qw]),
+                         offsets, exact)
+    g, u = gu[:, :I], gu[:, I:]
+    h = swiglu_from_gu(g, u, exact)
+    qh, sh = quantize_mx_e4m3(h)
+    qd = [quantize_mx_e4m3(as_values(w_down_vals[e]).T) for e in range(E)]
+    out = grouped_gemm_mx(qh, sh, np.stack([q for q, _ in qd]), np.stack([s_ for _, s_ in qd]),
+                          offsets, exact)
+    return {"g": g, "u": u, "h": h, "out": to_bf16(out, exact)}
 
 
 def expert_mlp(xp_vals, w_gu_vals, w_down_vals, offsets, I, exact=False, fp8=False):
@@ -621,7 +690,7 @@ PLACE_COMBINE, PLACE_INPUT = 0, 1
 
 def moe_forward(x_bits, logits, w_gu_bits, w_down_bits, k, score, I,
                 shared_gu_bits=None, shared_down_bits=None, fp8=False, exact=False,
-                placement=PLACE_COMBINE):
+                placement=PLACE_COMBINE, mx=False):
     """Route -> dispatch -> grouped MLP -> combine [TE-MoE "Introduction", the four
     stages; "Example: MoE layer on a single device"]. x and the weights are bf16 bit
     patterns (or float64 values, for the exact-arithmetic pins); logits are float32.
@@ -640,7 +709,8 @@ def moe_forward(x_bits, logits, w_gu_bits, w_down_bits, k, score, I,
         for j in range(k):
             qr[row_of[:, j].astype(np.int64)] = q[:, j]
         xp = to_bf16(xp * qr[:, None], exact)
-    mlp = expert_mlp(xp, w_gu_bits, w_down_bits, offsets, I, exact, fp8)
+    mlp = (expert_mlp_mx(xp, w_gu_bits, w_down_bits, offsets, I, exact) if mx else
+           expert_mlp(xp, w_gu_bits, w_down_bits, offsets, I, exact, fp8))
     shared = None
     if shared_gu_bits is not None:
         Is = shared_down_bits.shape[0]
