@@ -54,7 +54,7 @@ typedef enum {
   MOE_ERR_HIP = 4
 } moe_status_t;
 
-typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3 = 1, MOE_FP32 = 2 } moe_dtype_t;
+typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3 = 1, MOE_FP32 = 2, MOE_MXFP8 = 3 } moe_dtype_t;
 
 /* Score functions (guide, "Router": softmax before or after the top-k, sigmoid,
  * sqrtsoftplus).
@@ -300,6 +300,31 @@ moe_status_t moe_dispatch_backward_router_input(const void* dxp, const void* x,
                                                 float scaling_factor, void* dx, float* d_logits,
                                                 void* stream);
 
+/* ---- MXFP8 (te_mixtral.py's mxfp8 recipe) ------------------------------------------
+ * e4m3 codes with one power-of-two scale per block of 32 consecutive values along K,
+ * stored as a byte (E8M0: log2(scale) + 127). Conversion of a block (OCP Microscaling
+ * v1.0): scale = 2^(floor(log2(amax)) - 8), clamped to [2^-127, 2^127], 2^-127 for an
+ * all-zero block; code = e4m3(v / scale), nearest-even, saturating to +-448. */
+
+/* x [R,C] bf16 (C % 32 == 0) -> q [R,C] codes, scale [R,C/32] bytes. */
+moe_status_t moe_quantize_mxfp8_rows(const void* x, int R, int C, uint8_t* q, uint8_t* scale,
+                                     void* stream);
+
+/* Offline weight preparation: w [G,K,N] bf16 (K % 32 == 0) -> q [G,N,K] codes (output
+ * channel major) and scale [G,N,K/32] bytes, blocks along K. */
+moe_status_t moe_quantize_mxfp8_weights(const void* w, int G, int K, int N, uint8_t* q,
+                                        uint8_t* scale, void* stream);
+
+/* Block-scaled grouped GEMM (layout NT): C[r,n] = sum over K blocks of
+ * scale_A[r,b] scale_B[g][n,b] sum_{k in b} A[r,k] B[g][n,k], fp32 accumulation, the scales
+ * applied by the matrix-core instruction. A [rows,K] codes + a_scale [rows,K/32]; B [G,N,K]
+ * codes + b_scale [G,N,K/32]; offsets [G+1] device. swiglu = 0: C bf16 [rows,N]
+ * (N % 64 == 0). swiglu = 1: N = 2I (gate columns [0,I), up [I,2I), I % 64 == 0) and
+ * C = h bf16 [rows,I] = silu(g) u. K % 64 == 0. */
+moe_status_t moe_grouped_gemm_mxfp8(const uint8_t* A, const uint8_t* a_scale, const uint8_t* B,
+                                    const uint8_t* b_scale, const int32_t* offsets, int G,
+                                    int rows, int N, int K, int swiglu, void* C, void* stream);
+
 /* ---- whole layer ------------------------------------------------------------ */
 
 typedef struct {
@@ -308,7 +333,9 @@ typedef struct {
                     unweighted, added in combine (torchtitan pull request 1269,
                     MoE.forward) */
   int score;     /* moe_score_t */
-  int dtype;     /* expert GEMMs: MOE_BF16 or MOE_FP8_E4M3 */
+  int dtype;     /* expert GEMMs: MOE_BF16, MOE_FP8_E4M3 or MOE_MXFP8 (forward only; the
+                    weight tensors then hold moe_quantize_mxfp8_weights codes, and the
+                    *_scale pointers their scale bytes, [E,2I,H/32] and [E,H,I/32]) */
   int training;  /* 1: keep what moe_backward needs in the workspace */
   int router;    /* 1: the layer owns its router projection: moe_forward computes the
                     logits from x and w_router (into the workspace; t->logits is not
@@ -360,6 +387,9 @@ typedef struct {
   uint8_t* hq;         /* [T*k,I] e4m3 (fp8) */
   float* h_scale;      /* [T*k] (fp8) */
   void* out;           /* [T*k,H] bf16 */
+  void* xq;            /* [rows,H] MXFP8 codes (MOE_MXFP8) */
+  uint8_t* xq_scale;   /* [rows,H/32] scale bytes (MOE_MXFP8) */
+  uint8_t* hq_scale;   /* [rows,I/32] scale bytes (MOE_MXFP8; codes in hq) */
   void* shared_h;      /* [T,shared_I] bf16 */
   void* shared_out;    /* [T,H] bf16 */
   int32_t* shared_offsets; /* [2] = {0, T} */

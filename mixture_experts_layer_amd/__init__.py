@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_amd.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_BF16, MOE_FP8_E4M3, MOE_FP32 = 0, 1, 2
+MOE_BF16, MOE_FP8_E4M3, MOE_FP32, MOE_MXFP8 = 0, 1, 2, 3
 MOE_SOFTMAX_PRE_RENORM, MOE_SOFTMAX_POST, MOE_SIGMOID, MOE_SQRTSOFTPLUS = 0, 1, 2, 3
 MOE_GEMM_NN, MOE_GEMM_NT, MOE_GEMM_TN_DW = 0, 1, 2
 MOE_PLACE_COMBINE, MOE_PLACE_INPUT = 0, 1
@@ -31,6 +31,7 @@ EXPORTS = [
     "moe_router_weight_grad_workspace_bytes", "moe_router_weight_grad",
     "moe_dispatch_backward_router", "moe_router_topk_ex", "moe_expert_bias_update",
     "moe_dispatch_backward_router_input", "moe_padded_rows", "moe_permute_padded",
+    "moe_quantize_mxfp8_rows", "moe_quantize_mxfp8_weights", "moe_grouped_gemm_mxfp8",
 ]
 
 
@@ -64,7 +65,8 @@ class RouterOpts(ctypes.Structure):
 class Views(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "topk_prob", "counts", "offsets", "row_of", "src_of", "xp",
-                 "xp_scale", "gu", "h", "hq", "h_scale", "out", "shared_h", "shared_out",
+                 "xp_scale", "gu", "h", "hq", "h_scale", "out", "xq", "xq_scale", "hq_scale",
+                 "shared_h", "shared_out",
                  "shared_offsets", "d_out", "dgu", "dxp", "scratch")] + \
                [("scratch_bytes", ctypes.c_size_t), ("pad_offsets", ctypes.c_void_p),
                 ("rows", ctypes.c_int)] + \
@@ -104,6 +106,9 @@ def _load():
         "moe_dispatch_backward_router_input": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, ctypes.c_float,
                                                 vp, vp, vp], i),
         "moe_padded_rows": ([i, i, i, i], sz),
+        "moe_quantize_mxfp8_rows": ([vp, i, i, vp, vp, vp], i),
+        "moe_quantize_mxfp8_weights": ([vp, i, i, i, vp, vp, vp], i),
+        "moe_grouped_gemm_mxfp8": ([vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp], i),
         "moe_permute_padded": ([vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp], i),
         "moe_router_weight_grad_workspace_bytes": ([i, i, i], sz),
         "moe_router_weight_grad": ([vp, vp, i, i, i, vp, vp, sz, vp], i),
@@ -329,6 +334,38 @@ def moe_combine_backward(dy, row_of, topk_prob, d_out, stream=None):
     _want_rows(d_out, torch.bfloat16, T * k, H, "d_out")
     _check("moe_combine_backward", _lib.moe_combine_backward(
         _p(dy), _p(row_of), _p(topk_prob), T, H, k, _p(d_out), _stream(stream)))
+
+
+def moe_quantize_mxfp8_rows(x, q, scale, stream=None):
+    R, C = x.shape
+    _want(x, torch.bfloat16, (R, C), "x")
+    _want(q, torch.uint8, (R, C), "q")
+    _want(scale, torch.uint8, (R, C // 32), "scale")
+    _check("moe_quantize_mxfp8_rows", _lib.moe_quantize_mxfp8_rows(
+        _p(x), R, C, _p(q), _p(scale), _stream(stream)))
+
+
+def moe_quantize_mxfp8_weights(w, q, scale, stream=None):
+    G, K, N = w.shape
+    _want(w, torch.bfloat16, (G, K, N), "w")
+    _want(q, torch.uint8, (G, N, K), "q")
+    _want(scale, torch.uint8, (G, N, K // 32), "scale")
+    _check("moe_quantize_mxfp8_weights", _lib.moe_quantize_mxfp8_weights(
+        _p(w), G, K, N, _p(q), _p(scale), _stream(stream)))
+
+
+def moe_grouped_gemm_mxfp8(A, a_scale, B, b_scale, offsets, C, swiglu=False, stream=None):
+    rows, K = A.shape
+    G, N, _ = B.shape
+    _want(A, torch.uint8, (rows, K), "A")
+    _want(a_scale, torch.uint8, (rows, K // 32), "a_scale")
+    _want(B, torch.uint8, (G, N, K), "B")
+    _want(b_scale, torch.uint8, (G, N, K // 32), "b_scale")
+    _want(offsets, torch.int32, (G + 1,), "offsets")
+    _want(C, torch.bfloat16, (rows, N // 2 if swiglu else N), "C")
+    _check("moe_grouped_gemm_mxfp8", _lib.moe_grouped_gemm_mxfp8(
+        _p(A), _p(a_scale), _p(B), _p(b_scale), _p(offsets), G, rows, N, K, int(bool(swiglu)),
+        _p(C), _stream(stream)))
 
 
 def moe_quantize_fp8_rows(x, q, scale, stream=None):

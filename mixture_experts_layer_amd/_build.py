@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_amd.so")
-SOURCES = ["router.hip", "router_opts.hip", "router_proj.hip", "permute.hip", "gemm.hip", "moe_api.hip"]
+SOURCES = ["router.hip", "router_opts.hip", "router_proj.hip", "permute.hip", "gemm.hip", "mx.hip", "moe_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -5,6 +5,16 @@
 
 namespace moe {
 
+// mx.hip: MXFP8 (e4m3 codes, one E8M0 scale byte per 32 along K)
+hipError_t launch_mx_quantize_rows(const void* x, int R, int C, uint8_t* q, uint8_t* scale,
+                                   hipStream_t s);
+hipError_t launch_mx_quantize_weights(const void* w, int G, int K, int N, uint8_t* q,
+                                      uint8_t* scale, hipStream_t s);
+// epi EPI_STORE: C bf16 [rows, N]; EPI_SWIGLU: N = 2I, C = h bf16 [rows, I]
+hipError_t launch_mx_gemm(int epi, const void* A, const uint8_t* sa, const void* B,
+                          const uint8_t* sb, const int32_t* offsets, int G, int rows, int N,
+                          int K, int I, void* C, hipStream_t s);
+
 // Router options (router_opts.hip). Plain: none of them set.
 struct RouterOpts {
   const float* expert_bias;  // [E] or null: added to sigmoid / sqrtsoftplus scores to select

@@ -39,7 +39,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Workspace layout of moe_forward / moe_backward. Every region is 256-byte aligned.
 struct Layout {
   size_t topk_idx, topk_prob, counts, offsets, pad_offsets, row_of, src_of, shared_offsets;
-  size_t xp, xp_scale, gu, h, hq, h_scale, out, shared_h, shared_out;
+  size_t xp, xp_scale, gu, h, hq, h_scale, out, shared_h, shared_out, xq, xq_scale, hq_scale;
   size_t d_out, dgu, dxp, scratch, scratch_bytes;
   size_t logits, d_logits, router_ws, router_ws_bytes, total;
   size_t rows;  // rows of the expert-contiguous buffers
@@ -59,6 +59,7 @@ Layout make_layout(const moe_problem_t& p) {
   // rows of the expert-contiguous buffers: the pairs, plus the padding of a padded dispatch
   const size_t N = NT + (p.align_size > 1 ? (size_t)p.E * (p.align_size - 1) : 0);
   const bool fp8 = p.dtype == MOE_FP8_E4M3;
+  const bool mx = p.dtype == MOE_MXFP8;
   const size_t act = fp8 ? 1 : 2;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -78,7 +79,10 @@ Layout make_layout(const moe_problem_t& p) {
   L.xp_scale = take(fp8 ? N * 4 : 0);
   L.gu = take(p.training ? N * 2 * p.I * 2 : 0);
   L.h = take(N * p.I * 2);
-  L.hq = take(fp8 ? N * p.I : 0);
+  L.hq = take(fp8 || mx ? N * p.I : 0);
+  L.xq = take(mx ? N * p.H : 0);
+  L.xq_scale = take(mx ? N * (p.H / 32) : 0);
+  L.hq_scale = take(mx ? N * (p.I / 32) : 0);
   L.h_scale = take(fp8 ? N * 4 : 0);
   L.out = take(N * p.H * 2);
   L.shared_h = take(p.shared_I ? (size_t)p.T * p.shared_I * 2 : 0);
@@ -129,7 +133,11 @@ moe_status_t check_problem(const moe_problem_t* p) {
   if (!gemm_offsets_fit(2LL * p->I, p->H, 2) || !gemm_offsets_fit(2LL * p->shared_I, p->H, 2))
     return MOE_ERR_UNSUPPORTED;
   if (!valid_score(p->score)) return MOE_ERR_INVALID_ARG;
-  if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3 && p->dtype != MOE_MXFP8)
+    return MOE_ERR_INVALID_ARG;
+  if (p->dtype == MOE_MXFP8 &&
+      (p->training || p->shared_I || p->weight_placement != MOE_PLACE_COMBINE))
+    return MOE_ERR_UNSUPPORTED;
   if (p->router != 0 && p->router != 1) return MOE_ERR_INVALID_ARG;
   RouterOpts o;
   moe_status_t so = make_router_opts(p->E, p->k, p->score, nullptr, p->num_groups, p->group_topk,
@@ -498,6 +506,37 @@ moe_status_t moe_dispatch_backward_router_input(const void* dxp, const void* x,
       scaling_factor == 0.f ? 1.f : scaling_factor, dx, d_logits, nullptr, 0, S(stream)));
 }
 
+moe_status_t moe_quantize_mxfp8_rows(const void* x, int R, int C, uint8_t* q, uint8_t* scale,
+                                     void* stream) {
+  if (R < 0 || C <= 0) return MOE_ERR_INVALID_ARG;
+  if (C % 32) return MOE_ERR_UNSUPPORTED;
+  if (R == 0) return MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(q) || scale == nullptr) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_mx_quantize_rows(x, R, C, q, scale, S(stream)));
+}
+
+moe_status_t moe_quantize_mxfp8_weights(const void* w, int G, int K, int N, uint8_t* q,
+                                        uint8_t* scale, void* stream) {
+  if (G <= 0 || K <= 0 || N <= 0) return MOE_ERR_INVALID_ARG;
+  if (K % 32) return MOE_ERR_UNSUPPORTED;
+  if (!ok_ptr(w) || !ok_ptr(q) || scale == nullptr) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_mx_quantize_weights(w, G, K, N, q, scale, S(stream)));
+}
+
+moe_status_t moe_grouped_gemm_mxfp8(const uint8_t* A, const uint8_t* a_scale, const uint8_t* B,
+                                    const uint8_t* b_scale, const int32_t* offsets, int G,
+                                    int rows, int N, int K, int swiglu, void* C, void* stream) {
+  if (G <= 0 || rows < 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
+  if (G > 256 || K % 64 || N % (swiglu ? 128 : 64)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)N * K >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!ok_ptr(A) || !ok_ptr(B) || !ok_ptr(offsets) || !ok_ptr(C) || a_scale == nullptr ||
+      b_scale == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_mx_gemm(swiglu ? EPI_SWIGLU : EPI_STORE, A, a_scale, B, b_scale,
+                                   offsets, G, rows, N, K, swiglu ? N / 2 : 0, C, S(stream)));
+}
+
 moe_status_t moe_quantize_fp8_rows(const void* x, int R, int C, uint8_t* q, float* scale,
                                    void* stream) {
   if (R < 0 || C <= 0) return MOE_ERR_INVALID_ARG;
@@ -540,7 +579,11 @@ moe_status_t moe_workspace_views(const moe_problem_t* p, void* ws, size_t ws_byt
   v->xp_scale = fp8 ? (float*)(b + L.xp_scale) : nullptr;
   v->gu = p->training ? b + L.gu : nullptr;
   v->h = b + L.h;
-  v->hq = fp8 ? b + L.hq : nullptr;
+  const bool mx = p->dtype == MOE_MXFP8;
+  v->hq = fp8 || mx ? b + L.hq : nullptr;
+  v->xq = mx ? b + L.xq : nullptr;
+  v->xq_scale = mx ? (uint8_t*)(b + L.xq_scale) : nullptr;
+  v->hq_scale = mx ? (uint8_t*)(b + L.hq_scale) : nullptr;
   v->h_scale = fp8 ? (float*)(b + L.h_scale) : nullptr;
   v->out = b + L.out;
   v->shared_h = p->shared_I ? b + L.shared_h : nullptr;
@@ -574,7 +617,9 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
                                        p->group_topk, p->scaling_factor, 0, &chk);
     if (so != MOE_OK) return so;
   }
-  if (fp8 && (!ok_ptr(t->w_gu_scale) || !ok_ptr(t->w_down_scale))) return MOE_ERR_INVALID_ARG;
+  const bool mx = p->dtype == MOE_MXFP8;
+  if ((fp8 || mx) && (!ok_ptr(t->w_gu_scale) || !ok_ptr(t->w_down_scale)))
+    return MOE_ERR_INVALID_ARG;
   if (p->shared_I && (!ok_ptr(t->shared_gu) || !ok_ptr(t->shared_down)))
     return MOE_ERR_INVALID_ARG;
   moe_views_t v;
@@ -614,6 +659,19 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   if (fp8) MOE_TRY(launch_scatter_rows_fp8(t->x, v.row_of, T, H, k, (uint8_t*)v.xp, v.xp_scale, s));
   else MOE_TRY(launch_scatter_rows(t->x, v.row_of, at_input ? v.topk_prob : nullptr, T, H, k,
                                    v.xp, s));
+  if (mx) {
+    // MXFP8 (te_mixtral's mxfp8 recipe): rows quantised per 32-element block, block-scaled
+    // GEMMs; the weight arguments hold codes and scale bytes (moe_quantize_mxfp8_weights)
+    MOE_TRY(launch_mx_quantize_rows(v.xp, N, H, (uint8_t*)v.xq, v.xq_scale, s));
+    MOE_TRY(launch_mx_gemm(EPI_SWIGLU, v.xq, v.xq_scale, t->w_gu, (const uint8_t*)t->w_gu_scale,
+                           v.offsets, E, N, 2 * I, H, I, v.h, s));
+    MOE_TRY(launch_mx_quantize_rows(v.h, N, I, (uint8_t*)v.hq, v.hq_scale, s));
+    MOE_TRY(launch_mx_gemm(EPI_STORE, v.hq, v.hq_scale, t->w_down,
+                           (const uint8_t*)t->w_down_scale, v.offsets, E, N, H, I, 0, v.out, s));
+    MOE_TRY(launch_combine(v.out, v.row_of, at_input ? nullptr : v.topk_prob, nullptr, T, H, k,
+                           t->y, s));
+    return MOE_OK;
+  }
   // 3. grouped MLP. A dense shared expert of the routed experts' width runs as one more
   // group of T rows (offsets[E+1] = N + T) in the same two launches, reading x, its own
   // weights and its own outputs; other widths, and training, launch it separately.

@@ -84,13 +84,13 @@ def check_fp8(got, ref, name, rel_l2=5e-2):
 class GpuMoE:
     """Uploads one workload's inputs and runs moe_forward / moe_backward through the C ABI."""
 
-    def __init__(self, w, d, training=None, canary=True, router=False):
+    def __init__(self, w, d, training=None, canary=True, router=False, mx=False):
         self.w, self.d = w, d
         T = d["T"]
         self.T = T
         self.training = w.training if training is None else training
         self.router = router
-        self.dtype = M.MOE_FP8_E4M3 if w.fp8 else M.MOE_BF16
+        self.dtype = M.MOE_MXFP8 if mx else (M.MOE_FP8_E4M3 if w.fp8 else M.MOE_BF16)
         self.prob = M.problem(T, w.H, w.E, w.k, w.I, w.score, w.shared_I, self.dtype, self.training,
                               router)
         self.w_router = dev_bf16(d["w_router"]) if router else None
@@ -102,7 +102,15 @@ class GpuMoE:
         self.shared_gu = dev_bf16(d["shared_gu"]) if w.shared_I else None
         self.shared_down = dev_bf16(d["shared_down"]) if w.shared_I else None
         self.w_gu_scale = self.w_down_scale = None
-        if w.fp8:
+        if mx:
+            E, H, I = w.E, w.H, w.I
+            self.w_gu_q = torch.empty((E, 2 * I, H), dtype=torch.uint8, device="cuda")
+            self.w_gu_scale = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device="cuda")
+            self.w_down_q = torch.empty((E, H, I), dtype=torch.uint8, device="cuda")
+            self.w_down_scale = torch.empty((E, H, I // 32), dtype=torch.uint8, device="cuda")
+            M.moe_quantize_mxfp8_weights(self.w_gu, self.w_gu_q, self.w_gu_scale)
+            M.moe_quantize_mxfp8_weights(self.w_down, self.w_down_q, self.w_down_scale)
+        elif w.fp8:
             E, H, I = w.E, w.H, w.I
             self.w_gu_q = torch.empty((E, 2 * I, H), dtype=torch.uint8, device="cuda")
             self.w_gu_scale = torch.empty((E, 2 * I), dtype=torch.float32, device="cuda")
@@ -117,8 +125,9 @@ class GpuMoE:
             self.ws.fill_(0xFF)
             self.y.view(torch.int16).fill_(0x7FC0)
         self.views = M.moe_workspace_views(self.prob, self.ws)
-        self.tens = M.tensors(self.x, self.logits, self.w_gu_q if w.fp8 else self.w_gu,
-                              self.w_down_q if w.fp8 else self.w_down, self.y,
+        q = w.fp8 or mx
+        self.tens = M.tensors(self.x, self.logits, self.w_gu_q if q else self.w_gu,
+                              self.w_down_q if q else self.w_down, self.y,
                               self.w_gu_scale, self.w_down_scale, self.shared_gu, self.shared_down,
                               self.w_router, self.dw_router)
 
