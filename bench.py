@@ -190,6 +190,9 @@ def main():
     ap.add_argument("--placement", choices=["combine", "input"], default="combine",
                     help="apply the routing weights to the expert outputs (combine) or inputs")
     ap.add_argument("--align", type=int, default=0, help="padded dispatch alignment (rows)")
+    ap.add_argument("--mx", action="store_true",
+                    help="the MXFP8 recipe (e4m3 with a power-of-two scale per 32 along K), "
+                         "forward only")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch each stage once plus a 256 MiB calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -223,7 +226,11 @@ def main():
     logits = torch.from_numpy(d["logits"]).to(dev)
     shared_gu = bf(d["shared_gu"]) if w.shared_I else None
     shared_down = bf(d["shared_down"]) if w.shared_I else None
-    dtype = M.MOE_FP8_E4M3 if w.fp8 else M.MOE_BF16
+    if args.mx:  # forward only; the cost model and peaks are the fp8 ones
+        import dataclasses
+        w = dataclasses.replace(w, fp8=False, training=False)
+        training = False
+    dtype = M.MOE_MXFP8 if args.mx else (M.MOE_FP8_E4M3 if w.fp8 else M.MOE_BF16)
     w_gu_s = w_down_s = None
     if w.fp8:  # offline weight preparation, outside the timed region
         wq = torch.empty((w.E, 2 * w.I, w.H), dtype=torch.uint8, device=dev)
@@ -232,6 +239,14 @@ def main():
         dq = torch.empty((w.E, w.H, w.I), dtype=torch.uint8, device=dev)
         w_down_s = torch.empty((w.E, w.H), dtype=torch.float32, device=dev)
         M.moe_quantize_fp8_weights(w_down, dq, w_down_s)
+        w_gu, w_down = wq, dq
+    if args.mx:  # offline weight preparation, outside the timed region
+        wq = torch.empty((w.E, 2 * w.I, w.H), dtype=torch.uint8, device=dev)
+        w_gu_s = torch.empty((w.E, 2 * w.I, w.H // 32), dtype=torch.uint8, device=dev)
+        M.moe_quantize_mxfp8_weights(w_gu, wq, w_gu_s)
+        dq = torch.empty((w.E, w.H, w.I), dtype=torch.uint8, device=dev)
+        w_down_s = torch.empty((w.E, w.H, w.I // 32), dtype=torch.uint8, device=dev)
+        M.moe_quantize_mxfp8_weights(w_down, dq, w_down_s)
         w_gu, w_down = wq, dq
     y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
     router = args.router
@@ -316,14 +331,15 @@ def main():
     src_of = vt("src_of", (N,), torch.int32)
     counts = vt("counts", (E,), torch.int32)
 
+    pdtype = M.MOE_BF16 if args.mx else dtype  # MXFP8 quantises after the bf16 dispatch
     launches = {
         "router": lambda: M.moe_router_topk_ex(logits, k, w.score, router_opts, idx_t, topk_prob,
                                                counts),
         "permute": (lambda: M.moe_permute_padded(
             x, idx_t, E, args.align, xp, offs, vt("pad_offsets", (E,), torch.int32), row_of,
-            src_of, scratch, dtype, xp_scale)) if args.align > 1 else
+            src_of, scratch, pdtype, xp_scale)) if args.align > 1 else
                    (lambda: M.moe_permute(x, idx_t, E, xp, offs, row_of, src_of, scratch,
-                                          dtype, xp_scale)),
+                                          pdtype, xp_scale)),
         "gemm1_swiglu": lambda: M.moe_grouped_gemm_swiglu(xp, w_gu, offs, h, gu, dtype,
                                                           xp_scale, w_gu_s),
         "gemm2": (lambda: M.moe_grouped_gemm(M.MOE_GEMM_NT, hq, w_down, offs, out, dtype,
@@ -333,6 +349,18 @@ def main():
     }
     if w.fp8:
         launches["quantize_h"] = lambda: M.moe_quantize_fp8_rows(h, hq, h_scale)
+    if args.mx:
+        xq = vt("xq", (N, H), torch.uint8)
+        xqs = vt("xq_scale", (N, H // 32), torch.uint8)
+        hq = vt("hq", (N, I), torch.uint8)
+        hqs = vt("hq_scale", (N, I // 32), torch.uint8)
+        launches.update({
+            "quantize_x": lambda: M.moe_quantize_mxfp8_rows(xp, xq, xqs),
+            "gemm1_swiglu": lambda: M.moe_grouped_gemm_mxfp8(xq, xqs, w_gu, w_gu_s, offs, h,
+                                                             swiglu=True),
+            "quantize_h": lambda: M.moe_quantize_mxfp8_rows(h, hq, hqs),
+            "gemm2": lambda: M.moe_grouped_gemm_mxfp8(hq, hqs, w_down, w_down_s, offs, out),
+        })
     if training:
         d_out = vt("d_out", (N, H), torch.bfloat16)
         dgu = vt("dgu", (N, 2 * I), torch.bfloat16)
@@ -390,6 +418,9 @@ def main():
     _log("bench: per-launch us " + json.dumps({k_: round(v_, 2) for k_, v_ in kernel_us.items()}))
 
     active = int((counts > 0).sum().item())  # experts that received rows in this step
+    if args.mx:
+        import dataclasses
+        w = dataclasses.replace(w, fp8=True)  # e4m3 operands (scale bytes are 1/32 more)
     costs = stage_costs(w, training, active)
     peak_tf = MFMA_PEAK_TFLOPS["fp8" if w.fp8 else "bf16"]
     gemm = {}
@@ -440,7 +471,8 @@ def main():
         tc0 = time.perf_counter()
         lg = O.gate_logits(d["x"][:S], d["w_router"]) if router else d["logits"][:S]
         r = O.moe_forward(d["x"][:S], lg, d["w_gu"], d["w_down"], w.k, w.score,
-                          w.I, d.get("shared_gu"), d.get("shared_down"), fp8=w.fp8)
+                          w.I, d.get("shared_gu"), d.get("shared_down"),
+                          fp8=w.fp8 and not args.mx, mx=args.mx)
         if training:
             O.moe_backward(r, d["dy"][:S], d["w_gu"], d["w_down"], w.I,
                            w_router_bits=d["w_router"] if router else None)
@@ -464,7 +496,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if w.fp8 else "bf16",
+        "dtype": "mxfp8" if args.mx else ("fp8" if w.fp8 else "bf16"),
         "data": "synthetic",
         "config": {"workload": f"{w.name}-shaped MoE block " + ("with its router projection " if router else "")
                    + ("forward+backward" if training else "forward"),

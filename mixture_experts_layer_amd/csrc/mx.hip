@@ -202,6 +202,9 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
   const uint8_t* psc;
   if (tid < kMxBM) psc = sa + (size_t)(m0 + (tid < rows_valid ? tid : 0)) * KB;
   else psc = sbg + (size_t)brow_of(tid - kMxBM) * KB;
+  // LDS rows of 64 bytes, the 16-byte chunk index XORed with (row/4)%4 so the fragment
+  // reads of 32 consecutive rows spread over the banks
+  auto chunk_at = [](int row, int c) { return row * kMxBK + ((c ^ ((row >> 2) & 3)) << 4); };
   u32x4_t ra[2], rb[2];
   uint16_t rs;
   auto gload = [&](int kt) {
@@ -215,8 +218,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      *(u32x4_t*)&s_a[buf][(lr + 64 * h) * kMxBK + lc] = ra[h];
-      *(u32x4_t*)&s_b[buf][(lr + 64 * h) * kMxBK + lc] = rb[h];
+      *(u32x4_t*)&s_a[buf][chunk_at(lr + 64 * h, lc >> 4)] = ra[h];
+      *(u32x4_t*)&s_b[buf][chunk_at(lr + 64 * h, lc >> 4)] = rb[h];
     }
     if (tid < kMxBM) s_sa[buf][tid] = rs;
     else s_sb[buf][tid - kMxBM] = rs;
@@ -241,8 +244,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = wm * 64 + 32 * i + l32;
-      const u32x4_t lo = *(const u32x4_t*)&s_a[buf][r * kMxBK + kh * 16];
-      const u32x4_t hi = *(const u32x4_t*)&s_a[buf][r * kMxBK + 32 + kh * 16];
+      const u32x4_t lo = *(const u32x4_t*)&s_a[buf][chunk_at(r, kh)];
+      const u32x4_t hi = *(const u32x4_t*)&s_a[buf][chunk_at(r, 2 + kh)];
       af[i] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       as[i] = mx_lane_scale(s_sa[buf][r], kh);
@@ -250,8 +253,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int r = EPI == EPI_SWIGLU ? 64 * j + 32 * wn + l32 : wn * 64 + 32 * j + l32;
-      const u32x4_t lo = *(const u32x4_t*)&s_b[buf][r * kMxBK + kh * 16];
-      const u32x4_t hi = *(const u32x4_t*)&s_b[buf][r * kMxBK + 32 + kh * 16];
+      const u32x4_t lo = *(const u32x4_t*)&s_b[buf][chunk_at(r, kh)];
+      const u32x4_t hi = *(const u32x4_t*)&s_b[buf][chunk_at(r, 2 + kh)];
       bf[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       bs[j] = mx_lane_scale(s_sb[buf][r], kh);
