@@ -17,4 +17,6 @@ from .moe_oracle import (SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID, SQRTSOFTPLUS
                          gate_logits, router_backward, prob_grad, softplus, score_values,
                          selection_keys, topk_select_ext, pack_routing_map, expert_bias_update,
                          PLACE_COMBINE, PLACE_INPUT, dispatch_meta_padded,
-                         MX_BLOCK, quantize_mx_e4m3, mx_decode, grouped_gemm_mx, expert_mlp_mx)
+                         MX_BLOCK, quantize_mx_e4m3, mx_decode, grouped_gemm_mx, expert_mlp_mx,
+                         MX_COL_ALIGN, mx_col_offsets, quantize_mx_cols,
+                         grouped_gemm_mx_wgrad, expert_mlp_mx_backward)

@@ -518,6 +518,52 @@ def grouped_gemm_mx(qa, sa, qb, sb, offsets, exact=False):
     return out
 
 
+MX_COL_ALIGN = 64
+
+
+def mx_col_offsets(offsets, align=MX_COL_ALIGN):
+    """Starts of the expert blocks along the token axis of the weight-gradient operands:
+    expert e takes its rows rounded up to a multiple of `align` (two MX blocks), so its
+    blocks start at its own first row and never hold another expert's rows [TE-MIX: the
+    mxfp8 recipe with pad_to_multiple=128, every expert's rows padded so that blocks never
+    straddle experts]. READING: the padding exists only in these operands (zero values),
+    not in the routed rows. Returns int64 [E+1]."""
+    n = np.diff(np.asarray(offsets, np.int64))
+    return np.concatenate([[0], np.cumsum((n + align - 1) // align * align)]).astype(np.int64)
+
+
+def quantize_mx_cols(vals: np.ndarray, offsets, align=MX_COL_ALIGN):
+    """MXFP8 quantisation along the token axis of expert-contiguous rows [R, C] (the
+    reduction axis of the weight-gradient GEMMs): per expert, blocks of 32 consecutive rows
+    starting at its first row, its last block completed with zero rows, the same block
+    conversion as ``quantize_mx_e4m3``. Returns the transposed codes [C, Kp], scale bytes
+    [C, Kp/32] and the expert starts along Kp (``mx_col_offsets``)."""
+    v = np.asarray(vals, dtype=np.float64)
+    co = mx_col_offsets(offsets, align)
+    padded = np.zeros((int(co[-1]), v.shape[1]), dtype=np.float64)
+    for e in range(len(co) - 1):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        padded[co[e]:co[e] + r1 - r0] = v[r0:r1]
+    q, s = quantize_mx_e4m3(padded.T)
+    return q, s, co
+
+
+def grouped_gemm_mx_wgrad(qa_t, sa_t, qb_t, sb_t, col_offsets, exact=False):
+    """MXFP8 weight-gradient GEMM: dW_e[m, n] = fp32( sum over expert e's token positions
+    k of A_t[m, k] B_t[n, k] ) with both operands' block scales along the token axis,
+    summed in float64 (every product is exact). qa_t [M, Kp], qb_t [N, Kp] codes with their
+    scale bytes; an expert with no rows gets zeros. Returns float32 values [E, M, N]."""
+    a = mx_decode(qa_t, sa_t)
+    b = mx_decode(qb_t, sb_t)
+    E = len(col_offsets) - 1
+    out = np.zeros((E, a.shape[0], b.shape[0]), dtype=np.float64)
+    for e in range(E):
+        c0, c1 = int(col_offsets[e]), int(col_offsets[e + 1])
+        if c1 > c0:
+            out[e] = to_f32(a[:, c0:c1] @ b[:, c0:c1].T, exact)
+    return out
+
+
 def quantize_cols_e4m3(w_vals: np.ndarray):
     """Per-output-channel e4m3 quantisation of expert weights [.., K, N]: one scale per
     (expert, column) over the K (reduction) dimension. Same rounding rule as
@@ -597,6 +643,41 @@ def expert_mlp_mx(xp_vals, w_gu_vals, w_down_vals, offsets, I, exact=False):
     out = grouped_gemm_mx(qh, sh, np.stack([q for q, _ in qd]), np.stack([s_ for _, s_ in qd]),
                           offsets, exact)
     return {"g": g, "u": u, "h": h, "out": to_bf16(out, exact)}
+
+
+def expert_mlp_mx_backward(mlp, xp_vals, d_out, w_gu_vals, w_down_vals, offsets, I,
+                           exact=False):
+    """Backward of the grouped SwiGLU MLP in the MXFP8 recipe [TE-MIX mxfp8: the recipe
+    covers the training step; TE-MoE "Grouped GEMM": every expert GEMM runs in the
+    recipe's precision]. READING (the pages give no per-tensor detail): e4m3 codes for
+    every operand, blocks of 32 along each GEMM's own reduction axis, so a tensor used by
+    two GEMMs along different axes is quantised twice:
+      dh   = fp32(MX_K(d_out) . MX_K(W_down[e])^T)      (blocks along H: d_out rows and
+                                                          W_down [I, H] as stored)
+      dGU  = SwiGLU'(dh; saved bf16 g, u)               (bf16)
+      dxp  = bf16(MX_K(dGU) . MX_K(W_gu[e])^T)          (blocks along 2I: dGU rows and
+                                                          W_gu [H, 2I] as stored)
+      dW_down[e] = bf16(MX_T(h_e)^T . MX_T(d_out_e))    (blocks along the expert's tokens,
+      dW_gu[e]   = bf16(MX_T(xp_e)^T . MX_T(dGU_e))      quantize_mx_cols)
+    `mlp` is the forward's dict (g, u fp32 values, h bf16 values); d_out bf16 values."""
+    E = len(w_gu_vals)
+    qd, sd = quantize_mx_e4m3(d_out)
+    wd = [quantize_mx_e4m3(as_values(w_down_vals[e])) for e in range(E)]
+    dh = grouped_gemm_mx(qd, sd, np.stack([q for q, _ in wd]), np.stack([s_ for _, s_ in wd]),
+                         offsets, exact)
+    dg, du = swiglu_backward(dh, to_bf16(mlp["g"], exact), to_bf16(mlp["u"], exact), exact)
+    dgu = np.concatenate([dg, du], axis=1)
+    qg, sg = quantize_mx_e4m3(dgu)
+    wg = [quantize_mx_e4m3(as_values(w_gu_vals[e])) for e in range(E)]
+    dxp = to_bf16(grouped_gemm_mx(qg, sg, np.stack([q for q, _ in wg]),
+                                  np.stack([s_ for _, s_ in wg]), offsets, exact), exact)
+    qh, sh, co = quantize_mx_cols(mlp["h"], offsets)
+    qo, so, _ = quantize_mx_cols(d_out, offsets)
+    dw_down = to_bf16(grouped_gemm_mx_wgrad(qh, sh, qo, so, co, exact), exact)
+    qx, sx, _ = quantize_mx_cols(xp_vals, offsets)
+    qt, st, _ = quantize_mx_cols(dgu, offsets)
+    dw_gu = to_bf16(grouped_gemm_mx_wgrad(qx, sx, qt, st, co, exact), exact)
+    return dict(dh=dh, dgu=dgu, dxp=dxp, dw_down=dw_down, dw_gu=dw_gu)
 
 
 def expert_mlp(xp_vals, w_gu_vals, w_down_vals, offsets, I, exact=False, fp8=False):
@@ -749,7 +830,8 @@ def grouped_gemm_dw(a_vals, b_vals, offsets, exact=False, out_bf16=False):
     return out
 
 
-def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False, w_router_bits=None):
+def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False, w_router_bits=None,
+                 mx=False):
     """Backward of the expert path for an upstream gradient dy [T, H]
     [TE-MoE "Example: MoE layer on a single device": all stages differentiable;
     HF-48201 "Numbers": the block is timed forward + backward].
@@ -767,6 +849,8 @@ def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False, w_router_
       dW_down[e] = bf16(h_e^T @ d_out_e)
       dxp   = bf16(dGU_e @ W_gu[e]^T);      dW_gu[e] = bf16(xp_e^T @ dGU_e)
       dx[t] = bf16(sum_j dxp[row_of[t,j]])                      (dispatch backward)
+    mx: the four expert GEMMs in the MXFP8 recipe (``expert_mlp_mx_backward``; the forward
+    ran with mx too).
     """
     dy = as_values(dy_bits)
     row_of, q, offsets = fwd["row_of"], fwd["topk_prob"], fwd["offsets"]
@@ -780,15 +864,19 @@ def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False, w_router_
     for j in range(k):
         d_out[row_of[:, j].astype(np.int64)] = (dy if place == PLACE_INPUT else
                                                 to_bf16(dy * q[:, j:j + 1], exact))
-    # GEMM2 backward: dh = d_out W_d^T (per expert), then the SwiGLU backward
-    dh = grouped_gemm(d_out, np.swapaxes(w_d, 1, 2), offsets, exact)
-    g_saved, u_saved = to_bf16(fwd["g"], exact), to_bf16(fwd["u"], exact)
-    dg, du = swiglu_backward(dh, g_saved, u_saved, exact)
-    dgu = np.concatenate([dg, du], axis=1)
-    dw_down = grouped_gemm_dw(fwd["h"], d_out, offsets, exact, out_bf16=True)
-    # GEMM1 backward
-    dxp = to_bf16(grouped_gemm(dgu, np.swapaxes(w_gu, 1, 2), offsets, exact), exact)
-    dw_gu = grouped_gemm_dw(fwd["xp"], dgu, offsets, exact, out_bf16=True)
+    if mx:
+        m = expert_mlp_mx_backward(fwd, fwd["xp"], d_out, w_gu, w_d, offsets, I, exact)
+        dh, dgu, dxp, dw_gu, dw_down = m["dh"], m["dgu"], m["dxp"], m["dw_gu"], m["dw_down"]
+    else:
+        # GEMM2 backward: dh = d_out W_d^T (per expert), then the SwiGLU backward
+        dh = grouped_gemm(d_out, np.swapaxes(w_d, 1, 2), offsets, exact)
+        g_saved, u_saved = to_bf16(fwd["g"], exact), to_bf16(fwd["u"], exact)
+        dg, du = swiglu_backward(dh, g_saved, u_saved, exact)
+        dgu = np.concatenate([dg, du], axis=1)
+        dw_down = grouped_gemm_dw(fwd["h"], d_out, offsets, exact, out_bf16=True)
+        # GEMM1 backward
+        dxp = to_bf16(grouped_gemm(dgu, np.swapaxes(w_gu, 1, 2), offsets, exact), exact)
+        dw_gu = grouped_gemm_dw(fwd["xp"], dgu, offsets, exact, out_bf16=True)
     res = dict(d_out=d_out, dh=dh, dgu=dgu, dxp=dxp, dw_gu=dw_gu, dw_down=dw_down)
     dx_router = None
     if w_router_bits is not None:
