@@ -325,6 +325,50 @@ moe_status_t moe_grouped_gemm_mxfp8(const uint8_t* A, const uint8_t* a_scale, co
                                     const uint8_t* b_scale, const int32_t* offsets, int G,
                                     int rows, int N, int K, int swiglu, void* C, void* stream);
 
+/* MXFP8 backward (the same recipe in the training step). The data-gradient GEMMs take
+ * operands quantised along their own K: d_out rows and dgu rows with
+ * moe_quantize_mxfp8_rows, and the weights as stored (w_down [E,I,H] as rows of H,
+ * w_gu [E,H,2I] as rows of 2I), also with moe_quantize_mxfp8_rows. The weight-gradient
+ * GEMMs reduce over each expert's rows, so their operands are quantised along the token
+ * axis, in blocks of 32 that start at every expert's first row: expert g's rows go to
+ * columns [co[g], co[g] + roundup(n_g, 64)) of a transposed operand [C, Kp], the columns
+ * past its rows holding zero codes (as if the expert's rows were padded with zero rows,
+ * te_mixtral.py's mxfp8 recipe padding every expert's split). */
+
+/* Columns a transposed operand needs: roundup(R + 63 G, 64) (-1 on bad arguments). */
+long long moe_mxfp8_cols_capacity(int R, int G);
+
+/* co [G+1] device out: co[0] = 0, co[g+1] = co[g] + roundup(offsets[g+1] - offsets[g], 64)
+ * from the row offsets [G+1] (device). */
+moe_status_t moe_mxfp8_col_offsets(const int32_t* offsets, int G, int32_t* col_offsets,
+                                   void* stream);
+
+/* x [R,C] bf16 expert-contiguous rows (C % 8 == 0), offsets [G+1] and col_offsets [G+1]
+ * (moe_mxfp8_col_offsets) device -> qt [C,Kp] codes and scale_t [C,Kp/32] bytes, the
+ * token axis blocked per expert as above. Kp % 64 == 0 and Kp >= moe_mxfp8_cols_capacity;
+ * columns at and past co[G] are not written. */
+moe_status_t moe_quantize_mxfp8_cols(const void* x, int R, int C, const int32_t* offsets,
+                                     const int32_t* col_offsets, int G, int Kp, uint8_t* qt,
+                                     uint8_t* scale_t, void* stream);
+
+/* Weight-gradient GEMM: C[g] [M,N] bf16 = sum over the columns k in [co[g], co[g+1]) of
+ * scale_A scale_B At[m,k] Bt[n,k] (fp32 accumulation, block scales in the instruction).
+ * At [M,Kp] + a_scale [M,Kp/32], Bt [N,Kp] + b_scale [N,Kp/32] (moe_quantize_mxfp8_cols);
+ * C [G,M,N]; an expert with no rows gets zeros. M % 64 == 0, N % 64 == 0. */
+moe_status_t moe_grouped_gemm_mxfp8_wgrad(const uint8_t* At, const uint8_t* a_scale,
+                                          const uint8_t* Bt, const uint8_t* b_scale,
+                                          const int32_t* col_offsets, int G, int M, int N, int Kp,
+                                          void* C, void* stream);
+
+/* GEMM2 data gradient with the SwiGLU backward: dh = A B^T per expert as in
+ * moe_grouped_gemm_mxfp8 (A = d_out codes [rows,K=H], B = w_down codes [G,I,H]), then from
+ * the saved gu [rows,2I] bf16 (gate columns first), s = sigmoid(g):
+ * dgu [rows,2I] bf16 = [dh u s (1 + g (1 - s)), dh g s]. I % 64 == 0, K % 64 == 0. */
+moe_status_t moe_grouped_gemm_mxfp8_swiglu_bwd(const uint8_t* A, const uint8_t* a_scale,
+                                               const uint8_t* B, const uint8_t* b_scale,
+                                               const int32_t* offsets, int G, int rows, int I,
+                                               int K, const void* gu, void* dgu, void* stream);
+
 /* ---- whole layer ------------------------------------------------------------ */
 
 typedef struct {
@@ -333,9 +377,10 @@ typedef struct {
                     unweighted, added in combine (torchtitan pull request 1269,
                     MoE.forward) */
   int score;     /* moe_score_t */
-  int dtype;     /* expert GEMMs: MOE_BF16, MOE_FP8_E4M3 or MOE_MXFP8 (forward only; the
+  int dtype;     /* expert GEMMs: MOE_BF16, MOE_FP8_E4M3 (forward only) or MOE_MXFP8 (the
                     weight tensors then hold moe_quantize_mxfp8_weights codes, and the
-                    *_scale pointers their scale bytes, [E,2I,H/32] and [E,H,I/32]) */
+                    *_scale pointers their scale bytes, [E,2I,H/32] and [E,H,I/32];
+                    training also takes the *_bwd copies) */
   int training;  /* 1: keep what moe_backward needs in the workspace */
   int router;    /* 1: the layer owns its router projection: moe_forward computes the
                     logits from x and w_router (into the workspace; t->logits is not
@@ -370,6 +415,13 @@ typedef struct {
   const void* w_router;       /* bf16 [E,H] (router = 1), else NULL */
   float* dw_router;           /* [E,H] float32 out of moe_backward (router = 1), else NULL */
   const float* expert_bias;   /* [E] selection bias (sigmoid / sqrtsoftplus) or NULL */
+  /* MOE_MXFP8 training: the weights' second MXFP8 copy, blocked along the stored last
+     axis, for the data gradients (moe_quantize_mxfp8_rows of w_gu as [E*H,2I] and of
+     w_down as [E*I,H]); NULL otherwise */
+  const void* w_gu_bwd;             /* [E,H,2I] codes */
+  const uint8_t* w_gu_bwd_scale;    /* [E,H,2I/32] */
+  const void* w_down_bwd;           /* [E,I,H] codes */
+  const uint8_t* w_down_bwd_scale;  /* [E,I,H/32] */
 } moe_tensors_t;
 
 /* Device pointers into a forward workspace (all inside ws). */
@@ -404,6 +456,15 @@ typedef struct {
   float* d_logits;     /* [T,E] (router = 1, training) */
   void* router_ws;     /* moe_router_weight_grad scratch (router = 1, training) */
   size_t router_ws_bytes;
+  /* MOE_MXFP8 training */
+  int32_t* mx_col_offsets;  /* [E+1] expert starts along the token axis (multiples of 64) */
+  uint8_t* dgq;             /* [rows,2I] dgu codes */
+  uint8_t* dgq_scale;       /* [rows,2I/32] */
+  uint8_t* mx_ta;           /* [max(H,I),mx_kp] token-axis codes: h, then xp */
+  uint8_t* mx_ta_scale;
+  uint8_t* mx_tb;           /* [max(H,2I),mx_kp] token-axis codes: d_out, then dgu */
+  uint8_t* mx_tb_scale;
+  int mx_kp;                /* moe_mxfp8_cols_capacity(rows, E) */
 } moe_views_t;
 
 /* Bytes of workspace moe_forward (and, when training, moe_backward) needs. */
@@ -419,8 +480,10 @@ moe_status_t moe_workspace_views(const moe_problem_t* p, void* ws, size_t ws_byt
 moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* ws,
                          size_t ws_bytes, void* stream);
 
-/* Backward of the layer for upstream gradient dy [T,H] bf16 (bf16 MLP, training=1
- * forward only): dx [T,H] bf16, dw_gu [E,H,2I] bf16, dw_down [E,I,H] bf16. With
+/* Backward of the layer for upstream gradient dy [T,H] bf16 (bf16 or MXFP8 MLP, training=1
+ * forward only): dx [T,H] bf16, dw_gu [E,H,2I] bf16, dw_down [E,I,H] bf16. MXFP8: the
+ * GEMMs of moe_grouped_gemm_mxfp8_swiglu_bwd, moe_grouped_gemm_mxfp8 and
+ * moe_grouped_gemm_mxfp8_wgrad on the operands described above them. With
  * router = 0 the logits are an input of the layer and no gradient flows to the router.
  * With router = 1 (t->x and t->w_router as in the forward) it also writes
  * t->dw_router [E,H] float32 and d_logits into the workspace, and dx includes the

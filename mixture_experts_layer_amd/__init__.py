@@ -32,6 +32,8 @@ EXPORTS = [
     "moe_dispatch_backward_router", "moe_router_topk_ex", "moe_expert_bias_update",
     "moe_dispatch_backward_router_input", "moe_padded_rows", "moe_permute_padded",
     "moe_quantize_mxfp8_rows", "moe_quantize_mxfp8_weights", "moe_grouped_gemm_mxfp8",
+    "moe_mxfp8_cols_capacity", "moe_mxfp8_col_offsets", "moe_quantize_mxfp8_cols",
+    "moe_grouped_gemm_mxfp8_wgrad", "moe_grouped_gemm_mxfp8_swiglu_bwd",
 ]
 
 
@@ -53,7 +55,8 @@ class Problem(ctypes.Structure):
 class Tensors(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("x", "logits", "w_gu", "w_gu_scale", "w_down", "w_down_scale",
-                 "shared_gu", "shared_down", "y", "w_router", "dw_router", "expert_bias")]
+                 "shared_gu", "shared_down", "y", "w_router", "dw_router", "expert_bias",
+                 "w_gu_bwd", "w_gu_bwd_scale", "w_down_bwd", "w_down_bwd_scale")]
 
 
 class RouterOpts(ctypes.Structure):
@@ -71,7 +74,10 @@ class Views(ctypes.Structure):
                [("scratch_bytes", ctypes.c_size_t), ("pad_offsets", ctypes.c_void_p),
                 ("rows", ctypes.c_int)] + \
                [(n, ctypes.c_void_p) for n in ("logits", "d_logits", "router_ws")] + \
-               [("router_ws_bytes", ctypes.c_size_t)]
+               [("router_ws_bytes", ctypes.c_size_t)] + \
+               [(n, ctypes.c_void_p) for n in ("mx_col_offsets", "dgq", "dgq_scale", "mx_ta",
+                                               "mx_ta_scale", "mx_tb", "mx_tb_scale")] + \
+               [("mx_kp", ctypes.c_int)]
 
 
 def _load():
@@ -109,6 +115,11 @@ def _load():
         "moe_quantize_mxfp8_rows": ([vp, i, i, vp, vp, vp], i),
         "moe_quantize_mxfp8_weights": ([vp, i, i, i, vp, vp, vp], i),
         "moe_grouped_gemm_mxfp8": ([vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp], i),
+        "moe_mxfp8_cols_capacity": ([i, i], ctypes.c_longlong),
+        "moe_mxfp8_col_offsets": ([vp, i, vp, vp], i),
+        "moe_quantize_mxfp8_cols": ([vp, i, i, vp, vp, i, i, vp, vp, vp], i),
+        "moe_grouped_gemm_mxfp8_wgrad": ([vp, vp, vp, vp, vp, i, i, i, i, vp, vp], i),
+        "moe_grouped_gemm_mxfp8_swiglu_bwd": ([vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp], i),
         "moe_permute_padded": ([vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp], i),
         "moe_router_weight_grad_workspace_bytes": ([i, i, i], sz),
         "moe_router_weight_grad": ([vp, vp, i, i, i, vp, vp, sz, vp], i),
@@ -368,6 +379,64 @@ def moe_grouped_gemm_mxfp8(A, a_scale, B, b_scale, offsets, C, swiglu=False, str
         _p(C), _stream(stream)))
 
 
+def moe_mxfp8_cols_capacity(R, G):
+    n = _lib.moe_mxfp8_cols_capacity(int(R), int(G))
+    if n < 0:
+        raise MoeError("moe_mxfp8_cols_capacity", 1)
+    return n
+
+
+def moe_mxfp8_col_offsets(offsets, col_offsets, stream=None):
+    G = offsets.numel() - 1
+    _want(offsets, torch.int32, (G + 1,), "offsets")
+    _want(col_offsets, torch.int32, (G + 1,), "col_offsets")
+    _check("moe_mxfp8_col_offsets", _lib.moe_mxfp8_col_offsets(
+        _p(offsets), G, _p(col_offsets), _stream(stream)))
+
+
+def moe_quantize_mxfp8_cols(x, offsets, col_offsets, qt, scale_t, stream=None):
+    R, C = x.shape
+    G = offsets.numel() - 1
+    Kp = qt.shape[1]
+    _want(x, torch.bfloat16, (R, C), "x")
+    _want(offsets, torch.int32, (G + 1,), "offsets")
+    _want(col_offsets, torch.int32, (G + 1,), "col_offsets")
+    _want(qt, torch.uint8, (C, Kp), "qt")
+    _want(scale_t, torch.uint8, (C, Kp // 32), "scale_t")
+    _check("moe_quantize_mxfp8_cols", _lib.moe_quantize_mxfp8_cols(
+        _p(x), R, C, _p(offsets), _p(col_offsets), G, Kp, _p(qt), _p(scale_t), _stream(stream)))
+
+
+def moe_grouped_gemm_mxfp8_wgrad(At, a_scale, Bt, b_scale, col_offsets, C, stream=None):
+    M, Kp = At.shape
+    N = Bt.shape[0]
+    G = col_offsets.numel() - 1
+    _want(At, torch.uint8, (M, Kp), "At")
+    _want(a_scale, torch.uint8, (M, Kp // 32), "a_scale")
+    _want(Bt, torch.uint8, (N, Kp), "Bt")
+    _want(b_scale, torch.uint8, (N, Kp // 32), "b_scale")
+    _want(col_offsets, torch.int32, (G + 1,), "col_offsets")
+    _want(C, torch.bfloat16, (G, M, N), "C")
+    _check("moe_grouped_gemm_mxfp8_wgrad", _lib.moe_grouped_gemm_mxfp8_wgrad(
+        _p(At), _p(a_scale), _p(Bt), _p(b_scale), _p(col_offsets), G, M, N, Kp, _p(C),
+        _stream(stream)))
+
+
+def moe_grouped_gemm_mxfp8_swiglu_bwd(A, a_scale, B, b_scale, offsets, gu, dgu, stream=None):
+    rows, K = A.shape
+    G, I, _ = B.shape
+    _want(A, torch.uint8, (rows, K), "A")
+    _want(a_scale, torch.uint8, (rows, K // 32), "a_scale")
+    _want(B, torch.uint8, (G, I, K), "B")
+    _want(b_scale, torch.uint8, (G, I, K // 32), "b_scale")
+    _want(offsets, torch.int32, (G + 1,), "offsets")
+    _want(gu, torch.bfloat16, (rows, 2 * I), "gu")
+    _want(dgu, torch.bfloat16, (rows, 2 * I), "dgu")
+    _check("moe_grouped_gemm_mxfp8_swiglu_bwd", _lib.moe_grouped_gemm_mxfp8_swiglu_bwd(
+        _p(A), _p(a_scale), _p(B), _p(b_scale), _p(offsets), G, rows, I, K, _p(gu), _p(dgu),
+        _stream(stream)))
+
+
 def moe_quantize_fp8_rows(x, q, scale, stream=None):
     R, C = x.shape
     _want(q, torch.uint8, (R, C), "q")
@@ -479,10 +548,12 @@ def moe_workspace_views(prob: Problem, ws):
 
 
 def tensors(x, logits, w_gu, w_down, y, w_gu_scale=None, w_down_scale=None, shared_gu=None,
-            shared_down=None, w_router=None, dw_router=None, expert_bias=None):
+            shared_down=None, w_router=None, dw_router=None, expert_bias=None, w_gu_bwd=None,
+            w_gu_bwd_scale=None, w_down_bwd=None, w_down_bwd_scale=None):
     return Tensors(_p(x), _p(logits), _p(w_gu), _p(w_gu_scale), _p(w_down), _p(w_down_scale),
                    _p(shared_gu), _p(shared_down), _p(y), _p(w_router), _p(dw_router),
-                   _p(expert_bias))
+                   _p(expert_bias), _p(w_gu_bwd), _p(w_gu_bwd_scale), _p(w_down_bwd),
+                   _p(w_down_bwd_scale))
 
 
 def moe_forward(prob: Problem, tens: Tensors, ws, stream=None):

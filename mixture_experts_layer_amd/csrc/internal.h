@@ -10,10 +10,28 @@ hipError_t launch_mx_quantize_rows(const void* x, int R, int C, uint8_t* q, uint
                                    hipStream_t s);
 hipError_t launch_mx_quantize_weights(const void* w, int G, int K, int N, uint8_t* q,
                                       uint8_t* scale, hipStream_t s);
-// epi EPI_STORE: C bf16 [rows, N]; EPI_SWIGLU: N = 2I, C = h bf16 [rows, I]
+// epi EPI_STORE: C bf16 [rows, N]; EPI_SWIGLU: N = 2I, C = h bf16 [rows, I] (and g,u into
+// gu_out [rows, 2I] when not null); EPI_SWIGLU_BWD: N = I, C = dgu bf16 [rows, 2I] from
+// dh = A B^T and the saved g,u in gu_in [rows, 2I]
 hipError_t launch_mx_gemm(int epi, const void* A, const uint8_t* sa, const void* B,
                           const uint8_t* sb, const int32_t* offsets, int G, int rows, int N,
-                          int K, int I, void* C, hipStream_t s);
+                          int K, int I, void* C, hipStream_t s, const void* gu_in = nullptr,
+                          void* gu_out = nullptr);
+// Weight-gradient layout: expert ranges along the token axis padded to multiples of 64.
+constexpr int kMxColAlign = 64;
+inline long long mx_cols_capacity(long long R, long long G) {
+  return (R + (kMxColAlign - 1) * G + kMxColAlign - 1) / kMxColAlign * kMxColAlign;
+}
+hipError_t launch_mx_col_offsets(const int32_t* offsets, int G, int32_t* col_offsets,
+                                 hipStream_t s);
+// x [R, C] bf16 expert-contiguous rows -> qt [C, Kp] codes, st [C, Kp/32] scale bytes
+hipError_t launch_mx_quantize_cols(const void* x, int R, int C, const int32_t* offsets,
+                                   const int32_t* col_offsets, int G, int Kp, uint8_t* qt,
+                                   uint8_t* st, hipStream_t s);
+// C[g] [M, N] bf16 = At[:, co[g]:co[g+1]] Bt[:, co[g]:co[g+1]]^T with block scales
+hipError_t launch_mx_gemm_wgrad(const void* At, const uint8_t* sa, const void* Bt,
+                                const uint8_t* sb, const int32_t* col_offsets, int G, int M,
+                                int N, int Kp, void* C, hipStream_t s);
 
 // Router options (router_opts.hip). Plain: none of them set.
 struct RouterOpts {

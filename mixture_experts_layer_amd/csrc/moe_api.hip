@@ -42,6 +42,7 @@ struct Layout {
   size_t xp, xp_scale, gu, h, hq, h_scale, out, shared_h, shared_out, xq, xq_scale, hq_scale;
   size_t d_out, dgu, dxp, scratch, scratch_bytes;
   size_t logits, d_logits, router_ws, router_ws_bytes, total;
+  size_t mx_col_offsets, dgq, dgq_scale, mx_ta, mx_ta_scale, mx_tb, mx_tb_scale, mx_kp;
   size_t rows;  // rows of the expert-contiguous buffers
 };
 
@@ -96,6 +97,18 @@ Layout make_layout(const moe_problem_t& p) {
   L.d_logits = take(p.router && p.training ? (size_t)p.T * p.E * 4 : 0);
   L.router_ws_bytes = p.router && p.training ? router_wgrad_bytes(p.T, p.H, p.E) : 0;
   L.router_ws = take(L.router_ws_bytes);
+  // MXFP8 training: dgu codes (rows), and the token-axis (transposed) operands of the weight
+  // gradients, [C, Kp] codes for C up to max(H, I) (A side) and max(H, 2I) (B side)
+  const bool mxt = mx && p.training;
+  L.mx_kp = mxt ? (size_t)mx_cols_capacity((long long)N, p.E) : 0;
+  const size_t ca = (size_t)(p.H > p.I ? p.H : p.I), cb = (size_t)(p.H > 2 * p.I ? p.H : 2 * p.I);
+  L.mx_col_offsets = take(mxt ? ((size_t)p.E + 1) * 4 : 0);
+  L.dgq = take(mxt ? N * 2 * p.I : 0);
+  L.dgq_scale = take(mxt ? N * 2 * p.I / 32 : 0);
+  L.mx_ta = take(ca * L.mx_kp);
+  L.mx_ta_scale = take(ca * L.mx_kp / 32);
+  L.mx_tb = take(cb * L.mx_kp);
+  L.mx_tb_scale = take(cb * L.mx_kp / 32);
   L.total = o;
   L.rows = N;
   return L;
@@ -135,8 +148,7 @@ moe_status_t check_problem(const moe_problem_t* p) {
   if (!valid_score(p->score)) return MOE_ERR_INVALID_ARG;
   if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3 && p->dtype != MOE_MXFP8)
     return MOE_ERR_INVALID_ARG;
-  if (p->dtype == MOE_MXFP8 &&
-      (p->training || p->shared_I || p->weight_placement != MOE_PLACE_COMBINE))
+  if (p->dtype == MOE_MXFP8 && (p->shared_I || p->weight_placement != MOE_PLACE_COMBINE))
     return MOE_ERR_UNSUPPORTED;
   if (p->router != 0 && p->router != 1) return MOE_ERR_INVALID_ARG;
   RouterOpts o;
@@ -537,6 +549,59 @@ moe_status_t moe_grouped_gemm_mxfp8(const uint8_t* A, const uint8_t* a_scale, co
                                    offsets, G, rows, N, K, swiglu ? N / 2 : 0, C, S(stream)));
 }
 
+long long moe_mxfp8_cols_capacity(int R, int G) {
+  if (R < 0 || G <= 0) return -1;
+  return mx_cols_capacity(R, G);
+}
+
+moe_status_t moe_mxfp8_col_offsets(const int32_t* offsets, int G, int32_t* col_offsets,
+                                   void* stream) {
+  if (G <= 0 || !ok_ptr(offsets) || !ok_ptr(col_offsets)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_mx_col_offsets(offsets, G, col_offsets, S(stream)));
+}
+
+moe_status_t moe_quantize_mxfp8_cols(const void* x, int R, int C, const int32_t* offsets,
+                                     const int32_t* col_offsets, int G, int Kp, uint8_t* qt,
+                                     uint8_t* scale_t, void* stream) {
+  if (R < 0 || C <= 0 || G <= 0 || Kp < 0) return MOE_ERR_INVALID_ARG;
+  if (C % 8 || Kp % kMxColAlign) return MOE_ERR_UNSUPPORTED;
+  if (Kp < mx_cols_capacity(R, G)) return MOE_ERR_INVALID_ARG;
+  if (Kp == 0) return MOE_OK;
+  if ((R > 0 && !ok_ptr(x)) || !ok_ptr(offsets) || !ok_ptr(col_offsets) || !ok_ptr(qt) ||
+      scale_t == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(
+      launch_mx_quantize_cols(x, R, C, offsets, col_offsets, G, Kp, qt, scale_t, S(stream)));
+}
+
+moe_status_t moe_grouped_gemm_mxfp8_wgrad(const uint8_t* At, const uint8_t* a_scale,
+                                          const uint8_t* Bt, const uint8_t* b_scale,
+                                          const int32_t* col_offsets, int G, int M, int N, int Kp,
+                                          void* C, void* stream) {
+  if (G <= 0 || M <= 0 || N <= 0 || Kp < 0) return MOE_ERR_INVALID_ARG;
+  if (M % 64 || N % 64 || Kp % kMxColAlign) return MOE_ERR_UNSUPPORTED;
+  if (!ok_ptr(At) || !ok_ptr(Bt) || !ok_ptr(col_offsets) || !ok_ptr(C) || a_scale == nullptr ||
+      b_scale == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_mx_gemm_wgrad(At, a_scale, Bt, b_scale, col_offsets, G, M, N, Kp, C,
+                                         S(stream)));
+}
+
+moe_status_t moe_grouped_gemm_mxfp8_swiglu_bwd(const uint8_t* A, const uint8_t* a_scale,
+                                               const uint8_t* B, const uint8_t* b_scale,
+                                               const int32_t* offsets, int G, int rows, int I,
+                                               int K, const void* gu, void* dgu, void* stream) {
+  if (G <= 0 || rows < 0 || I <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
+  if (G > 256 || K % 64 || I % 64) return MOE_ERR_UNSUPPORTED;
+  if ((long long)I * K >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!ok_ptr(A) || !ok_ptr(B) || !ok_ptr(offsets) || !ok_ptr(gu) || !ok_ptr(dgu) ||
+      a_scale == nullptr || b_scale == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_mx_gemm(EPI_SWIGLU_BWD, A, a_scale, B, b_scale, offsets, G, rows, I, K,
+                                   I, dgu, S(stream), gu, nullptr));
+}
+
 moe_status_t moe_quantize_fp8_rows(const void* x, int R, int C, uint8_t* q, float* scale,
                                    void* stream) {
   if (R < 0 || C <= 0) return MOE_ERR_INVALID_ARG;
@@ -598,6 +663,15 @@ moe_status_t moe_workspace_views(const moe_problem_t* p, void* ws, size_t ws_byt
   v->d_logits = p->router && p->training ? (float*)(b + L.d_logits) : nullptr;
   v->router_ws = L.router_ws_bytes ? b + L.router_ws : nullptr;
   v->router_ws_bytes = L.router_ws_bytes;
+  const bool mxt = mx && p->training;
+  v->mx_col_offsets = mxt ? (int32_t*)(b + L.mx_col_offsets) : nullptr;
+  v->dgq = mxt ? b + L.dgq : nullptr;
+  v->dgq_scale = mxt ? b + L.dgq_scale : nullptr;
+  v->mx_ta = mxt ? b + L.mx_ta : nullptr;
+  v->mx_ta_scale = mxt ? b + L.mx_ta_scale : nullptr;
+  v->mx_tb = mxt ? b + L.mx_tb : nullptr;
+  v->mx_tb_scale = mxt ? b + L.mx_tb_scale : nullptr;
+  v->mx_kp = (int)L.mx_kp;
   return MOE_OK;
 }
 
@@ -664,7 +738,8 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
     // GEMMs; the weight arguments hold codes and scale bytes (moe_quantize_mxfp8_weights)
     MOE_TRY(launch_mx_quantize_rows(v.xp, N, H, (uint8_t*)v.xq, v.xq_scale, s));
     MOE_TRY(launch_mx_gemm(EPI_SWIGLU, v.xq, v.xq_scale, t->w_gu, (const uint8_t*)t->w_gu_scale,
-                           v.offsets, E, N, 2 * I, H, I, v.h, s));
+                           v.offsets, E, N, 2 * I, H, I, v.h, s, nullptr,
+                           p->training ? v.gu : nullptr));
     MOE_TRY(launch_mx_quantize_rows(v.h, N, I, (uint8_t*)v.hq, v.hq_scale, s));
     MOE_TRY(launch_mx_gemm(EPI_STORE, v.hq, v.hq_scale, t->w_down,
                            (const uint8_t*)t->w_down_scale, v.offsets, E, N, H, I, 0, v.out, s));
@@ -769,7 +844,11 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
                           void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  if (!t || !p->training || p->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!t || !p->training || p->dtype == MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  const bool mx = p->dtype == MOE_MXFP8;
+  if (mx && (!ok_ptr(t->w_gu_bwd) || !ok_ptr(t->w_down_bwd) || t->w_gu_bwd_scale == nullptr ||
+             t->w_down_bwd_scale == nullptr))
+    return MOE_ERR_INVALID_ARG;
   if (p->shared_I) return MOE_ERR_UNSUPPORTED;
   if (!ok_ptr(t->w_gu) || !ok_ptr(t->w_down) || !ok_ptr(dw_gu) || !ok_ptr(dw_down))
     return MOE_ERR_INVALID_ARG;
@@ -807,6 +886,33 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
     MOE_TRY(launch_router_wgrad(t->x, (const uint16_t*)v.router_ws, T, H, E, r_part, t->dw_router, s));
   if (p->align_size > 1 && T > 0)  // the padding rows of d_out are zero
     MOE_TRY(launch_zero_pad_rows(v.offsets, v.counts, E, 2 * H, v.d_out, nullptr, nullptr, s));
+  if (mx) {
+    // MXFP8: data gradients with operands blocked along their K (d_out and dgu rows; the
+    // weights' second copy, blocked along the stored last axis), weight gradients with
+    // operands blocked along each expert's tokens
+    const int Kp = v.mx_kp;
+    if (N > 0) {
+      MOE_TRY(launch_mx_quantize_rows(v.d_out, N, H, (uint8_t*)v.xq, v.xq_scale, s));
+      MOE_TRY(launch_mx_gemm(EPI_SWIGLU_BWD, v.xq, v.xq_scale, t->w_down_bwd, t->w_down_bwd_scale,
+                             v.offsets, E, N, I, H, I, v.dgu, s, v.gu, nullptr));
+      MOE_TRY(launch_mx_quantize_rows(v.dgu, N, 2 * I, v.dgq, v.dgq_scale, s));
+      MOE_TRY(launch_mx_gemm(EPI_STORE, v.dgq, v.dgq_scale, t->w_gu_bwd, t->w_gu_bwd_scale,
+                             v.offsets, E, N, H, 2 * I, 0, v.dxp, s));
+    }
+    MOE_TRY(launch_mx_col_offsets(v.offsets, E, v.mx_col_offsets, s));
+    MOE_TRY(launch_mx_quantize_cols(v.h, N, I, v.offsets, v.mx_col_offsets, E, Kp, v.mx_ta,
+                                    v.mx_ta_scale, s));
+    MOE_TRY(launch_mx_quantize_cols(v.d_out, N, H, v.offsets, v.mx_col_offsets, E, Kp, v.mx_tb,
+                                    v.mx_tb_scale, s));
+    MOE_TRY(launch_mx_gemm_wgrad(v.mx_ta, v.mx_ta_scale, v.mx_tb, v.mx_tb_scale, v.mx_col_offsets,
+                                 E, I, H, Kp, dw_down, s));
+    MOE_TRY(launch_mx_quantize_cols(v.xp, N, H, v.offsets, v.mx_col_offsets, E, Kp, v.mx_ta,
+                                    v.mx_ta_scale, s));
+    MOE_TRY(launch_mx_quantize_cols(v.dgu, N, 2 * I, v.offsets, v.mx_col_offsets, E, Kp, v.mx_tb,
+                                    v.mx_tb_scale, s));
+    MOE_TRY(launch_mx_gemm_wgrad(v.mx_ta, v.mx_ta_scale, v.mx_tb, v.mx_tb_scale, v.mx_col_offsets,
+                                 E, H, 2 * I, Kp, dw_gu, s));
+  } else {
   // GEMM2 backward: dgu = SwiGLU'(d_out . W_down^T), dW_down = h^T . d_out
   GemmParams a{};
   a.mode = MOE_GEMM_NT;
@@ -859,6 +965,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   d.N = 2 * I;
   d.C = dw_gu;
   MOE_TRY(launch_grouped_gemm(d, s));
+  }
   // dispatch backward: dx[t] = sum_j dxp[row_of[t,j]] (weighted when the weights scaled the
   // inputs; + the router's term)
   if (p->router && at_input) {

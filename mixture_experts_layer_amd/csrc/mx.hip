@@ -134,6 +134,98 @@ hipError_t launch_mx_quantize_weights(const void* w, int G, int K, int N, uint8_
   return hipGetLastError();
 }
 
+// ---- token-axis (transposed) quantisation for the weight gradients ---------------------------
+// Expert e's rows [off[e], off[e+1]) go to columns [co[e], co[e] + roundup(n_e, 64)) of the
+// transposed codes qt [C, Kp]: blocks of 32 start at the expert's first row and the rows past
+// its end read as zero, so no block holds two experts' rows.
+__global__ void mx_col_offsets_kernel(const int32_t* __restrict__ off, int G,
+                                      int32_t* __restrict__ co) {
+  if (threadIdx.x != 0) return;
+  int acc = 0;
+  co[0] = 0;
+  for (int g = 0; g < G; ++g) {
+    acc += (off[g + 1] - off[g] + kMxColAlign - 1) / kMxColAlign * kMxColAlign;
+    co[g + 1] = acc;
+  }
+}
+
+hipError_t launch_mx_col_offsets(const int32_t* offsets, int G, int32_t* col_offsets,
+                                 hipStream_t s) {
+  mx_col_offsets_kernel<<<1, 64, 0, s>>>(offsets, G, col_offsets);
+  return hipGetLastError();
+}
+
+// One block per (64 token columns, 64 channels): a 64-column span lies inside one expert's
+// range (every range is a multiple of 64 long). The bf16 rows are staged in LDS (rows of 66
+// values, so the column reads below fall in distinct banks); thread t then takes channel
+// t/4 and rows 16*(t%4) .. +16 (half a block: the block amax by one shuffle) and writes
+// 16 code bytes, four threads covering one channel's 64 contiguous bytes.
+constexpr int kColTile = 64, kColLd = 66;
+__global__ __launch_bounds__(256) void mx_quantize_cols_kernel(
+    const uint16_t* __restrict__ x, int R, int C, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ co, int G, int Kp, uint8_t* __restrict__ qt,
+    uint8_t* __restrict__ st) {
+  __shared__ uint16_t s_x[kColTile * kColLd];
+  const int tid = threadIdx.x;
+  const int p0 = blockIdx.x * kColTile, c0 = blockIdx.y * kColTile;
+  if (p0 >= co[G]) return;  // past the last expert's range (uniform per block)
+  int lo = 0, hi = G - 1;   // the expert whose range holds p0: co[e] <= p0 < co[e+1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (co[mid] <= p0) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int n_e = off[e + 1] - off[e];
+  const int local0 = p0 - co[e];
+  // stage: 64 rows x 64 channels, thread t loads 8 channels of rows t/8 and t/8 + 32
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = (tid >> 3) + 32 * h, c = (tid & 7) * 8;
+    const int li = local0 + r;
+    const long long src = (long long)off[e] + li;
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (li < n_e && src < R && c0 + c < C) v = *(const u32x4_t*)(x + (size_t)src * C + c0 + c);
+    uint32_t* d = (uint32_t*)&s_x[r * kColLd + c];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) d[w] = v[w];
+  }
+  __syncthreads();
+  const int ch = tid >> 2, q = tid & 3;
+  if (c0 + ch >= C) return;  // no barrier follows
+  float f[16];
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    f[i] = bf16_to_f32(s_x[(16 * q + i) * kColLd + ch]);
+    m = fmaxf(m, fabsf(f[i]));
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, 64));  // the other half of the 32-row block
+  const int se = mx_scale_exp(m);
+  const float inv = exp2i(-se);
+  u32x4_t o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    float t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = fminf(fmaxf(f[4 * d + i] * inv, -448.f), 448.f);
+    o[d] = pack_e4m3x4(t[0], t[1], t[2], t[3]);
+  }
+  const size_t row = (size_t)(c0 + ch);
+  *(u32x4_t*)(qt + row * Kp + p0 + 16 * q) = o;
+  if ((q & 1) == 0) st[row * (Kp / 32) + p0 / 32 + q / 2] = (uint8_t)(se + 127);
+}
+
+hipError_t launch_mx_quantize_cols(const void* x, int R, int C, const int32_t* offsets,
+                                   const int32_t* col_offsets, int G, int Kp, uint8_t* qt,
+                                   uint8_t* st, hipStream_t s) {
+  if (Kp == 0 || C == 0) return hipSuccess;
+  const dim3 grid((unsigned)(Kp / kColTile), (unsigned)((C + kColTile - 1) / kColTile));
+  mx_quantize_cols_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, R, C, offsets, col_offsets,
+                                               G, Kp, qt, st);
+  return hipGetLastError();
+}
+
 // ---- grouped GEMM ---------------------------------------------------------------------------
 constexpr int kMxBM = 128, kMxBN = 128, kMxBK = 64;
 // Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3), read off the hardware with a
@@ -142,40 +234,70 @@ constexpr int kMxBM = 128, kMxBN = 128, kMxBK = 64;
 // comes from lane r + 32*b (byte 0 of its scale register).
 MOE_DEV int mx_lane_scale(uint16_t two_blocks, int kh) { return (two_blocks >> (8 * kh)) & 0xff; }
 
-template <int EPI>  // EPI_STORE (C bf16 [rows, N]) or EPI_SWIGLU (h bf16 [rows, I])
-__global__ __launch_bounds__(256) void mx_gemm_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ sb, const int32_t* __restrict__ offsets, int G, int N, int K,
-    int I, uint16_t* __restrict__ C) {
+// Two ways of grouping: by rows (the forward and the data gradients: group g owns rows
+// [off[g], off[g+1]) of A and its own B [N, K]) or by K (the weight gradients: A [M, K] and
+// B [N, K] are shared, group g owns K columns [off[g], off[g+1]), a multiple of 64, and
+// writes C[g] [M, N]).
+struct MxArgs {
+  const uint8_t* A;
+  const uint8_t* sa;
+  const uint8_t* B;
+  const uint8_t* sb;
+  const int32_t* offsets;
+  int G, M, N, K, I;  // by rows: M unused; by K: K is the row length of A and B (Kp)
+  uint16_t* C;
+  const uint16_t* gu_in;  // SwiGLU backward: the saved g,u [rows, 2I]
+  uint16_t* gu_out;       // SwiGLU forward: g,u [rows, 2I] (training) or null
+};
+
+template <int EPI, bool KGRP>  // EPI_STORE, EPI_SWIGLU (h [rows, I]) or EPI_SWIGLU_BWD
+__global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kMxBM * kMxBK];
   __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kMxBN * kMxBK];
   __shared__ uint16_t s_sa[2][kMxBM], s_sb[2][kMxBN];  // two block scales per row per stage
   __shared__ int s_off[264], s_pref[264];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  // ---- tile decode: groups' M-tile prefix, then (group, n-tile, m-tile) ----
-  const int ntn = EPI == EPI_SWIGLU ? I / 64 : (N + kMxBN - 1) / kMxBN;
-  for (int g = tid; g <= G; g += 256) s_off[g] = offsets[g];
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    s_pref[0] = 0;
-    for (int g = 0; g < G; ++g) {
-      acc += (s_off[g + 1] - s_off[g] + kMxBM - 1) / kMxBM;
-      s_pref[g + 1] = acc;
-    }
-  }
-  __syncthreads();
-  const int tile = blockIdx.x;
-  if (tile >= s_pref[G] * ntn) return;
-  int g = 0;
-  while (s_pref[g + 1] * ntn <= tile) ++g;
-  const int local = tile - s_pref[g] * ntn;
-  const int mt = s_pref[g + 1] - s_pref[g];
-  const int ntile = local / mt, mtile = local % mt;
-  const int m0 = s_off[g] + mtile * kMxBM;
-  const int rows_valid = min(kMxBM, s_off[g + 1] - m0);
+  const int K = p.K, I = p.I, N = p.N;
   const int KB = K / 32;
+  // ---- tile decode ----
+  int g, ntile, m0, rows_valid, k0, nk;
+  if constexpr (KGRP) {
+    const int mt = (p.M + kMxBM - 1) / kMxBM, ntn = (N + kMxBN - 1) / kMxBN;
+    const int tile = blockIdx.x;
+    g = tile / (mt * ntn);
+    const int local = tile - g * (mt * ntn);
+    ntile = local / mt;
+    m0 = (local % mt) * kMxBM;
+    rows_valid = min(kMxBM, p.M - m0);
+    k0 = min(p.offsets[g], K);  // clamped to the operands' row length
+    nk = max(0, min(p.offsets[g + 1], K) - k0) / kMxBK;
+  } else {
+    // groups' M-tile prefix, then (group, n-tile, m-tile)
+    const int ntn = EPI == EPI_SWIGLU ? I / 64 : (N + kMxBN - 1) / kMxBN;
+    for (int x = tid; x <= p.G; x += 256) s_off[x] = p.offsets[x];
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      s_pref[0] = 0;
+      for (int x = 0; x < p.G; ++x) {
+        acc += (s_off[x + 1] - s_off[x] + kMxBM - 1) / kMxBM;
+        s_pref[x + 1] = acc;
+      }
+    }
+    __syncthreads();
+    const int tile = blockIdx.x;
+    if (tile >= s_pref[p.G] * ntn) return;
+    g = 0;
+    while (s_pref[g + 1] * ntn <= tile) ++g;
+    const int local = tile - s_pref[g] * ntn;
+    const int mt = s_pref[g + 1] - s_pref[g];
+    ntile = local / mt;
+    m0 = s_off[g] + (local % mt) * kMxBM;
+    rows_valid = min(kMxBM, s_off[g + 1] - m0);
+    k0 = 0;
+    nk = K / kMxBK;
+  }
   // ---- loaders: thread t loads 16 bytes of two A rows and two B rows per stage ----
   // A row r = t / 4 (+64), 16-byte chunk t % 4; B rows likewise; scales: t < 128 -> A row
   // t, else B row t - 128 (two bytes: the stage's two 32-element blocks).
@@ -188,20 +310,20 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
       return c < N ? c : ntile * kMxBN;
     }
   };
-  const uint8_t* bg = B + (size_t)g * N * K;
-  const uint8_t* sbg = sb + (size_t)g * N * KB;
+  const uint8_t* bg = KGRP ? p.B : p.B + (size_t)g * N * K;
+  const uint8_t* sbg = KGRP ? p.sb : p.sb + (size_t)g * N * KB;
   const int lr = tid >> 2, lc = (tid & 3) * 16;
   const uint8_t* pa[2];
   const uint8_t* pb[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r = lr + 64 * h;
-    pa[h] = A + (size_t)(m0 + (r < rows_valid ? r : 0)) * K + lc;  // dead rows: the first
-    pb[h] = bg + (size_t)brow_of(r) * K + lc;
+    pa[h] = p.A + (size_t)(m0 + (r < rows_valid ? r : 0)) * K + k0 + lc;  // dead rows: the first
+    pb[h] = bg + (size_t)brow_of(r) * K + k0 + lc;
   }
   const uint8_t* psc;
-  if (tid < kMxBM) psc = sa + (size_t)(m0 + (tid < rows_valid ? tid : 0)) * KB;
-  else psc = sbg + (size_t)brow_of(tid - kMxBM) * KB;
+  if (tid < kMxBM) psc = p.sa + (size_t)(m0 + (tid < rows_valid ? tid : 0)) * KB + k0 / 32;
+  else psc = sbg + (size_t)brow_of(tid - kMxBM) * KB + k0 / 32;
   // LDS rows of 64 bytes, the 16-byte chunk index XORed with (row/4)%4 so the fragment
   // reads of 32 consecutive rows spread over the banks
   auto chunk_at = [](int row, int c) { return row * kMxBK + ((c ^ ((row >> 2) & 3)) << 4); };
@@ -232,10 +354,11 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   const int l32 = lane & 31, kh = lane >> 5;
-  const int nk = K / kMxBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  if (nk > 0) {  // uniform per block
+    gload(0);
+    lstore(0);
+    __syncthreads();
+  }
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
@@ -279,7 +402,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
     if (rloc >= rows_valid) continue;
     const size_t row = (size_t)m0 + rloc;
     if constexpr (EPI == EPI_SWIGLU) {
-      uint16_t* hr = C + row * I + ntile * 64 + 32 * wn;
+      const int hc = ntile * 64 + 32 * wn;
+      uint16_t* hr = p.C + row * I + hc;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         float hv[4];
@@ -289,8 +413,45 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
           hv[r] = gg * sigmoid_fast(gg) * uu;
         }
         *(u32x2_t*)(hr + 8 * q4 + 4 * kh) = u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+        if (p.gu_out) {
+          uint16_t* gr = p.gu_out + row * 2 * I + hc + 8 * q4 + 4 * kh;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const f32x16_t& a = acc[i][j];
+            *(u32x2_t*)(gr + j * I) = u32x2_t{pack_bf16x2(a[4 * q4], a[4 * q4 + 1]),
+                                              pack_bf16x2(a[4 * q4 + 2], a[4 * q4 + 3])};
+          }
+        }
+      }
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+      // acc = dh[row, c] (fp32), c < I; with s = sigmoid(g), from the saved bf16 g,u:
+      // dgu[row] = [dh u s (1 + g (1 - s)), dh g s]
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c0 = ntile * kMxBN + wn * 64 + 32 * j;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int c = c0 + 8 * q4 + 4 * kh;
+          if (c >= N) continue;
+          const size_t o = row * 2 * I + c;
+          const u32x2_t gw = *(const u32x2_t*)(p.gu_in + o);
+          const u32x2_t uw = *(const u32x2_t*)(p.gu_in + o + I);
+          float dg[4], du[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float gg = (e & 1) ? bf16hi(gw[e >> 1]) : bf16lo(gw[e >> 1]);
+            const float uu = (e & 1) ? bf16hi(uw[e >> 1]) : bf16lo(uw[e >> 1]);
+            const float dh = acc[i][j][4 * q4 + e];
+            const float sg = sigmoid_fast(gg);
+            dg[e] = dh * uu * sg * (1.0f + gg * (1.0f - sg));
+            du[e] = dh * gg * sg;
+          }
+          *(u32x2_t*)(p.C + o) = u32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+          *(u32x2_t*)(p.C + o + I) = u32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+        }
       }
     } else {
+      uint16_t* cg = KGRP ? p.C + (size_t)g * p.M * N : p.C;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int c0 = ntile * kMxBN + wn * 64 + 32 * j;
@@ -299,7 +460,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
           const int c = c0 + 8 * q4 + 4 * kh;
           if (c >= N) continue;
           const f32x16_t& a = acc[i][j];
-          *(u32x2_t*)(C + row * N + c) =
+          *(u32x2_t*)(cg + row * N + c) =
               u32x2_t{pack_bf16x2(a[4 * q4], a[4 * q4 + 1]), pack_bf16x2(a[4 * q4 + 2], a[4 * q4 + 3])};
         }
       }
@@ -309,17 +470,33 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
 
 hipError_t launch_mx_gemm(int epi, const void* A, const uint8_t* sa, const void* B,
                           const uint8_t* sb, const int32_t* offsets, int G, int rows, int N,
-                          int K, int I, void* C, hipStream_t s) {
+                          int K, int I, void* C, hipStream_t s, const void* gu_in,
+                          void* gu_out) {
   const int ntn = epi == EPI_SWIGLU ? I / 64 : (N + kMxBN - 1) / kMxBN;
   const long long tiles = ((long long)rows / kMxBM + G) * ntn;  // upper bound
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  MxArgs a{(const uint8_t*)A, sa, (const uint8_t*)B, sb, offsets, G, 0, N, K, I, (uint16_t*)C,
+           (const uint16_t*)gu_in, (uint16_t*)gu_out};
   if (epi == EPI_SWIGLU)
-    mx_gemm_kernel<EPI_SWIGLU><<<(unsigned)tiles, 256, 0, s>>>(
-        (const uint8_t*)A, sa, (const uint8_t*)B, sb, offsets, G, N, K, I, (uint16_t*)C);
+    mx_gemm_kernel<EPI_SWIGLU, false><<<(unsigned)tiles, 256, 0, s>>>(a);
+  else if (epi == EPI_SWIGLU_BWD)
+    mx_gemm_kernel<EPI_SWIGLU_BWD, false><<<(unsigned)tiles, 256, 0, s>>>(a);
   else
-    mx_gemm_kernel<EPI_STORE><<<(unsigned)tiles, 256, 0, s>>>(
-        (const uint8_t*)A, sa, (const uint8_t*)B, sb, offsets, G, N, K, I, (uint16_t*)C);
+    mx_gemm_kernel<EPI_STORE, false><<<(unsigned)tiles, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm_wgrad(const void* At, const uint8_t* sa, const void* Bt,
+                                const uint8_t* sb, const int32_t* col_offsets, int G, int M,
+                                int N, int Kp, void* C, hipStream_t s) {
+  const long long tiles =
+      (long long)G * ((M + kMxBM - 1) / kMxBM) * ((N + kMxBN - 1) / kMxBN);
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  MxArgs a{(const uint8_t*)At, sa, (const uint8_t*)Bt, sb, col_offsets, G, M, N, Kp, 0,
+           (uint16_t*)C, nullptr, nullptr};
+  mx_gemm_kernel<EPI_STORE, true><<<(unsigned)tiles, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

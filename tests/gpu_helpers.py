@@ -110,6 +110,15 @@ class GpuMoE:
             self.w_down_scale = torch.empty((E, H, I // 32), dtype=torch.uint8, device="cuda")
             M.moe_quantize_mxfp8_weights(self.w_gu, self.w_gu_q, self.w_gu_scale)
             M.moe_quantize_mxfp8_weights(self.w_down, self.w_down_q, self.w_down_scale)
+            if self.training:  # the second copy, blocked along the stored last axis
+                self.w_gu_b = torch.empty((E, H, 2 * I), dtype=torch.uint8, device="cuda")
+                self.w_gu_bs = torch.empty((E, H, 2 * I // 32), dtype=torch.uint8, device="cuda")
+                self.w_down_b = torch.empty((E, I, H), dtype=torch.uint8, device="cuda")
+                self.w_down_bs = torch.empty((E, I, H // 32), dtype=torch.uint8, device="cuda")
+                M.moe_quantize_mxfp8_rows(self.w_gu.view(E * H, 2 * I), self.w_gu_b.view(E * H, 2 * I),
+                                          self.w_gu_bs.view(E * H, 2 * I // 32))
+                M.moe_quantize_mxfp8_rows(self.w_down.view(E * I, H), self.w_down_b.view(E * I, H),
+                                          self.w_down_bs.view(E * I, H // 32))
         elif w.fp8:
             E, H, I = w.E, w.H, w.I
             self.w_gu_q = torch.empty((E, 2 * I, H), dtype=torch.uint8, device="cuda")
@@ -129,7 +138,10 @@ class GpuMoE:
         self.tens = M.tensors(self.x, self.logits, self.w_gu_q if q else self.w_gu,
                               self.w_down_q if q else self.w_down, self.y,
                               self.w_gu_scale, self.w_down_scale, self.shared_gu, self.shared_down,
-                              self.w_router, self.dw_router)
+                              self.w_router, self.dw_router,
+                              **({} if not (mx and self.training) else dict(
+                                  w_gu_bwd=self.w_gu_b, w_gu_bwd_scale=self.w_gu_bs,
+                                  w_down_bwd=self.w_down_b, w_down_bwd_scale=self.w_down_bs)))
 
     def forward(self):
         M.moe_forward(self.prob, self.tens, self.ws)
@@ -160,6 +172,26 @@ class GpuMoE:
             row_of=self.view("row_of", (T, w.k), torch.int32).cpu().numpy(),
             src_of=self.view("src_of", (T * w.k,), torch.int32).cpu().numpy(),
         )
+
+
+def mx_gemm_slack(a_abs, b_abs):
+    """Accumulation slack of the block-scaled e4m3 GEMM for C = A B^T over K (a_abs [R, K],
+    b_abs [N, K]: decoded magnitudes): K 2^-24 sum|ab| for the fp32 accumulation across
+    K steps, plus, per 64-wide K step, 2^-10 of that step's largest product. The matrix
+    instruction sums one step's 64 products with an error up to about 2^-12 of the largest
+    of them (measured: at most 2^-11.9 over 4 M outputs at K = 64 .. 512 with random
+    signs), not to fp32 precision; the 2^-10 keeps a 4x margin."""
+    a_abs = np.asarray(a_abs, np.float64)
+    b_abs = np.asarray(b_abs, np.float64)
+    K = a_abs.shape[1]
+    out = K * 2.0 ** -24 * (a_abs @ b_abs.T)
+    rows = max(1, (1 << 22) // max(1, b_abs.shape[0] * 64))
+    for r0 in range(0, a_abs.shape[0], rows):
+        sl = slice(r0, r0 + rows)
+        for k0 in range(0, K, 64):
+            p = a_abs[sl, None, k0:k0 + 64] * b_abs[None, :, k0:k0 + 64]
+            out[sl] += 2.0 ** -10 * p.max(axis=2)
+    return out
 
 
 def fp32_sum_bound(a_abs, b_abs_t, n):

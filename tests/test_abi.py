@@ -16,7 +16,7 @@ LIB = os.path.join(ROOT, "mixture_experts_layer_amd", "libmoe_amd.so")
 def declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:long\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
