@@ -13,13 +13,13 @@
 // Layout: A [rows, K] codes with scales [rows, K/32]; B [G, N, K] codes (output-channel
 // major) with scales [G, N, K/32].
 //
-// Tiles: 128 rows x 128 B rows per block, four waves of 64 x 64 (2 x 2 blocks of 32x32),
-// K in steps of 64 bytes through a double-buffered LDS stage loaded by all threads (16-byte
-// loads into registers, then LDS), the next stage's loads in flight during the multiply.
-// SwiGLU: a block's 128 B rows are 64 gate columns and the 64 matching up columns, and a
-// wave's two B blocks are a gate block and its up block, so h = silu(g) u is formed in
-// registers. One block per tile; the grid covers an upper bound of the tile count and the
-// extra blocks exit.
+// Tiles: BM rows x BN B rows per block (256 x 256, eight waves of 128 x 64 as 4 x 2 blocks
+// of 32x32), K in steps of 64 bytes through a double-buffered LDS stage loaded by all
+// threads (16-byte loads into registers, then LDS), the next stage's loads in flight during
+// the multiply. SwiGLU: a block's first BN/2 B rows are gate columns and the last BN/2 the
+// matching up columns, and a wave's B blocks pair a gate block with its up block, so
+// h = silu(g) u is formed in registers. One block per tile; the grid covers an upper bound
+// of the tile count and the extra blocks exit.
 #include "internal.h"
 
 namespace moe {
@@ -138,20 +138,37 @@ hipError_t launch_mx_quantize_weights(const void* w, int G, int K, int N, uint8_
 // Expert e's rows [off[e], off[e+1]) go to columns [co[e], co[e] + roundup(n_e, 64)) of the
 // transposed codes qt [C, Kp]: blocks of 32 start at the expert's first row and the rows past
 // its end read as zero, so no block holds two experts' rows.
-__global__ void mx_col_offsets_kernel(const int32_t* __restrict__ off, int G,
-                                      int32_t* __restrict__ co) {
-  if (threadIdx.x != 0) return;
-  int acc = 0;
-  co[0] = 0;
-  for (int g = 0; g < G; ++g) {
-    acc += (off[g + 1] - off[g] + kMxColAlign - 1) / kMxColAlign * kMxColAlign;
-    co[g + 1] = acc;
+// One block of 256 threads: thread t sums the padded sizes of experts [t*per, (t+1)*per),
+// a block-wide exclusive scan of those sums, then each thread writes its experts' starts.
+__global__ __launch_bounds__(256) void mx_col_offsets_kernel(const int32_t* __restrict__ off,
+                                                             int G, int32_t* __restrict__ co) {
+  __shared__ int s_sum[256];
+  const int t = threadIdx.x, per = (G + 255) / 256;
+  const int g0 = min(G, t * per), g1 = min(G, g0 + per);
+  auto padded = [&](int g) {
+    return (off[g + 1] - off[g] + kMxColAlign - 1) / kMxColAlign * kMxColAlign;
+  };
+  int mine = 0;
+  for (int g = g0; g < g1; ++g) mine += padded(g);
+  s_sum[t] = mine;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {  // inclusive scan (Hillis-Steele)
+    const int v = t >= d ? s_sum[t - d] : 0;
+    __syncthreads();
+    s_sum[t] += v;
+    __syncthreads();
   }
+  int acc = s_sum[t] - mine;
+  for (int g = g0; g < g1; ++g) {
+    co[g] = acc;
+    acc += padded(g);
+  }
+  if (t == 255) co[G] = s_sum[255];
 }
 
 hipError_t launch_mx_col_offsets(const int32_t* offsets, int G, int32_t* col_offsets,
                                  hipStream_t s) {
-  mx_col_offsets_kernel<<<1, 64, 0, s>>>(offsets, G, col_offsets);
+  mx_col_offsets_kernel<<<1, 256, 0, s>>>(offsets, G, col_offsets);
   return hipGetLastError();
 }
 
@@ -227,7 +244,7 @@ hipError_t launch_mx_quantize_cols(const void* x, int R, int C, const int32_t* o
 }
 
 // ---- grouped GEMM ---------------------------------------------------------------------------
-constexpr int kMxBM = 128, kMxBN = 128, kMxBK = 64;
+constexpr int kMxBK = 64;  // K bytes (e4m3 values) per stage: two scale blocks
 // Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3), read off the hardware with a
 // one-hot probe: lane l holds row l%32; its bytes 0-15 are k 16*(l/32) .. +16 (K block 0)
 // and bytes 16-31 are k 32 + 16*(l/32) .. +16 (K block 1); the scale of block b of row r
@@ -250,38 +267,49 @@ struct MxArgs {
   uint16_t* gu_out;       // SwiGLU forward: g,u [rows, 2I] (training) or null
 };
 
-template <int EPI, bool KGRP>  // EPI_STORE, EPI_SWIGLU (h [rows, I]) or EPI_SWIGLU_BWD
-__global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kMxBM * kMxBK];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kMxBN * kMxBK];
-  __shared__ uint16_t s_sa[2][kMxBM], s_sb[2][kMxBN];  // two block scales per row per stage
+// Tile BM x BN, WM x WN waves, each wave (BM/WM) x (BN/WN) outputs as 32x32 blocks. The LDS
+// traffic per matrix instruction falls as the wave tile grows (a 128x64 wave tile reads six
+// 2 KB fragments per eight instructions, a 64x64 one four per four), so the wide tiles run
+// the long launches. SwiGLU: the tile's first BN/2 B rows are gate columns, the last BN/2
+// the matching up columns, and a wave's N blocks are NB/2 gate blocks then their up blocks.
+template <int EPI, bool KGRP, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int MB = BM / WM / 32, NB = BN / WN / 32, NH = NB / 2, HB = BN / 2;
+  constexpr int A_PER = BM * 4 / NT, B_PER = BN * 4 / NT;  // 16-byte chunks per thread
+  static_assert(A_PER >= 1 && B_PER >= 1 && BM * 4 % NT == 0 && BN * 4 % NT == 0, "load split");
+  static_assert(EPI != EPI_SWIGLU || NB % 2 == 0, "SwiGLU pairs gate and up blocks");
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][BM * kMxBK];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][BN * kMxBK];
+  __shared__ uint16_t s_sa[2][BM], s_sb[2][BN];  // two block scales per row per stage
   __shared__ int s_off[264], s_pref[264];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
   const int K = p.K, I = p.I, N = p.N;
   const int KB = K / 32;
   // ---- tile decode ----
   int g, ntile, m0, rows_valid, k0, nk;
   if constexpr (KGRP) {
-    const int mt = (p.M + kMxBM - 1) / kMxBM, ntn = (N + kMxBN - 1) / kMxBN;
+    const int mt = (p.M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
     const int tile = blockIdx.x;
     g = tile / (mt * ntn);
     const int local = tile - g * (mt * ntn);
     ntile = local / mt;
-    m0 = (local % mt) * kMxBM;
-    rows_valid = min(kMxBM, p.M - m0);
+    m0 = (local % mt) * BM;
+    rows_valid = min(BM, p.M - m0);
     k0 = min(p.offsets[g], K);  // clamped to the operands' row length
     nk = max(0, min(p.offsets[g + 1], K) - k0) / kMxBK;
   } else {
     // groups' M-tile prefix, then (group, n-tile, m-tile)
-    const int ntn = EPI == EPI_SWIGLU ? I / 64 : (N + kMxBN - 1) / kMxBN;
-    for (int x = tid; x <= p.G; x += 256) s_off[x] = p.offsets[x];
+    const int ntn = EPI == EPI_SWIGLU ? (I + HB - 1) / HB : (N + BN - 1) / BN;
+    for (int x = tid; x <= p.G; x += NT) s_off[x] = p.offsets[x];
     __syncthreads();
     if (tid == 0) {
       int acc = 0;
       s_pref[0] = 0;
       for (int x = 0; x < p.G; ++x) {
-        acc += (s_off[x + 1] - s_off[x] + kMxBM - 1) / kMxBM;
+        acc += (s_off[x + 1] - s_off[x] + BM - 1) / BM;
         s_pref[x + 1] = acc;
       }
     }
@@ -293,67 +321,94 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     const int local = tile - s_pref[g] * ntn;
     const int mt = s_pref[g + 1] - s_pref[g];
     ntile = local / mt;
-    m0 = s_off[g] + (local % mt) * kMxBM;
-    rows_valid = min(kMxBM, s_off[g + 1] - m0);
+    m0 = s_off[g] + (local % mt) * BM;
+    rows_valid = min(BM, s_off[g + 1] - m0);
     k0 = 0;
     nk = K / kMxBK;
   }
-  // ---- loaders: thread t loads 16 bytes of two A rows and two B rows per stage ----
-  // A row r = t / 4 (+64), 16-byte chunk t % 4; B rows likewise; scales: t < 128 -> A row
-  // t, else B row t - 128 (two bytes: the stage's two 32-element blocks).
+  // ---- loaders: chunk c (of BM*4 for A, BN*4 for B) = row c/4, 16-byte piece c%4; thread t
+  // takes chunks t, t + NT, ...; scales: thread t < BM takes A row t, then B rows ----
   auto brow_of = [&](int r) -> int {  // B row (output channel) of LDS B row r
     if constexpr (EPI == EPI_SWIGLU) {
-      const int hcol = ntile * 64 + (r & 63);
-      return r < 64 ? hcol : I + hcol;
+      int hcol = ntile * HB + (r < HB ? r : r - HB);
+      hcol = hcol < I ? hcol : ntile * HB;  // past I: outputs never stored
+      return r < HB ? hcol : I + hcol;
     } else {
-      const int c = ntile * kMxBN + r;
-      return c < N ? c : ntile * kMxBN;
+      const int c = ntile * BN + r;
+      return c < N ? c : ntile * BN;
     }
   };
   const uint8_t* bg = KGRP ? p.B : p.B + (size_t)g * N * K;
   const uint8_t* sbg = KGRP ? p.sb : p.sb + (size_t)g * N * KB;
-  const int lr = tid >> 2, lc = (tid & 3) * 16;
-  const uint8_t* pa[2];
-  const uint8_t* pb[2];
+  const uint8_t* pa[A_PER];
+  const uint8_t* pb[B_PER];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = lr + 64 * h;
-    pa[h] = p.A + (size_t)(m0 + (r < rows_valid ? r : 0)) * K + k0 + lc;  // dead rows: the first
-    pb[h] = bg + (size_t)brow_of(r) * K + k0 + lc;
+  for (int h = 0; h < A_PER; ++h) {
+    const int c = tid + NT * h, r = c >> 2;
+    pa[h] = p.A + (size_t)(m0 + (r < rows_valid ? r : 0)) * K + k0 + (c & 3) * 16;  // dead rows: the first
   }
-  const uint8_t* psc;
-  if (tid < kMxBM) psc = p.sa + (size_t)(m0 + (tid < rows_valid ? tid : 0)) * KB + k0 / 32;
-  else psc = sbg + (size_t)brow_of(tid - kMxBM) * KB + k0 / 32;
+#pragma unroll
+  for (int h = 0; h < B_PER; ++h) {
+    const int c = tid + NT * h;
+    pb[h] = bg + (size_t)brow_of(c >> 2) * K + k0 + (c & 3) * 16;
+  }
+  constexpr int SC_PER = (BM + BN + NT - 1) / NT;
+  const uint8_t* psc[SC_PER];
+#pragma unroll
+  for (int h = 0; h < SC_PER; ++h) {
+    const int r = tid + NT * h;
+    if (r < BM) psc[h] = p.sa + (size_t)(m0 + (r < rows_valid ? r : 0)) * KB + k0 / 32;
+    else if (r < BM + BN) psc[h] = sbg + (size_t)brow_of(r - BM) * KB + k0 / 32;
+    else psc[h] = nullptr;
+  }
   // LDS rows of 64 bytes, the 16-byte chunk index XORed with (row/4)%4 so the fragment
   // reads of 32 consecutive rows spread over the banks
   auto chunk_at = [](int row, int c) { return row * kMxBK + ((c ^ ((row >> 2) & 3)) << 4); };
-  u32x4_t ra[2], rb[2];
-  uint16_t rs;
+  u32x4_t ra[A_PER], rb[B_PER];
+  uint16_t rs[SC_PER];
   auto gload = [&](int kt) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      ra[h] = *(const u32x4_t*)(pa[h] + (size_t)kt * kMxBK);
-      rb[h] = *(const u32x4_t*)(pb[h] + (size_t)kt * kMxBK);
-    }
-    rs = (uint16_t)(psc[2 * kt] | (psc[2 * kt + 1] << 8));
+    for (int h = 0; h < A_PER; ++h) ra[h] = *(const u32x4_t*)(pa[h] + (size_t)kt * kMxBK);
+#pragma unroll
+    for (int h = 0; h < B_PER; ++h) rb[h] = *(const u32x4_t*)(pb[h] + (size_t)kt * kMxBK);
+#pragma unroll
+    for (int h = 0; h < SC_PER; ++h)
+      if (psc[h]) rs[h] = (uint16_t)(psc[h][2 * kt] | (psc[h][2 * kt + 1] << 8));
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      *(u32x4_t*)&s_a[buf][chunk_at(lr + 64 * h, lc >> 4)] = ra[h];
-      *(u32x4_t*)&s_b[buf][chunk_at(lr + 64 * h, lc >> 4)] = rb[h];
+    for (int h = 0; h < A_PER; ++h) {
+      const int c = tid + NT * h;
+      *(u32x4_t*)&s_a[buf][chunk_at(c >> 2, c & 3)] = ra[h];
     }
-    if (tid < kMxBM) s_sa[buf][tid] = rs;
-    else s_sb[buf][tid - kMxBM] = rs;
+#pragma unroll
+    for (int h = 0; h < B_PER; ++h) {
+      const int c = tid + NT * h;
+      *(u32x4_t*)&s_b[buf][chunk_at(c >> 2, c & 3)] = rb[h];
+    }
+#pragma unroll
+    for (int h = 0; h < SC_PER; ++h) {
+      const int r = tid + NT * h;
+      if (r < BM) s_sa[buf][r] = rs[h];
+      else if (r < BM + BN) s_sb[buf][r - BM] = rs[h];
+    }
   };
-  f32x16_t acc[2][2];
+  // B row (within the tile) of N block j of this wave
+  auto bcol0 = [&](int j) {
+    if constexpr (EPI == EPI_SWIGLU) return j < NH ? (wn * NH + j) * 32 : HB + (wn * NH + j - NH) * 32;
+    return (wn * NB + j) * 32;
+  };
+  f32x16_t acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   const int l32 = lane & 31, kh = lane >> 5;
+  // M blocks of this wave holding a valid row (wave-uniform): the others skip the multiply
+  const int mlive = __builtin_amdgcn_readfirstlane(
+      min(MB, max(0, (rows_valid - wm * (BM / WM) + 31) / 32)));
   if (nk > 0) {  // uniform per block
     gload(0);
     lstore(0);
@@ -362,20 +417,11 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
-    i32x8_t af[2], bf[2];
-    int as[2], bs[2];
+    i32x8_t bf[NB];
+    int bs[NB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = wm * 64 + 32 * i + l32;
-      const u32x4_t lo = *(const u32x4_t*)&s_a[buf][chunk_at(r, kh)];
-      const u32x4_t hi = *(const u32x4_t*)&s_a[buf][chunk_at(r, 2 + kh)];
-      af[i] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      as[i] = mx_lane_scale(s_sa[buf][r], kh);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = EPI == EPI_SWIGLU ? 64 * j + 32 * wn + l32 : wn * 64 + 32 * j + l32;
+    for (int j = 0; j < NB; ++j) {
+      const int r = bcol0(j) + l32;
       const u32x4_t lo = *(const u32x4_t*)&s_b[buf][chunk_at(r, kh)];
       const u32x4_t hi = *(const u32x4_t*)&s_b[buf][chunk_at(r, 2 + kh)];
       bf[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
@@ -383,11 +429,20 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
       bs[j] = mx_lane_scale(s_sb[buf][r], kh);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MB; ++i) {
+      if (i < mlive) {
+        const int r = wm * (BM / WM) + 32 * i + l32;
+        const u32x4_t lo = *(const u32x4_t*)&s_a[buf][chunk_at(r, kh)];
+        const u32x4_t hi = *(const u32x4_t*)&s_a[buf][chunk_at(r, 2 + kh)];
+        const i32x8_t af = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const int as = mx_lane_scale(s_sa[buf][r], kh);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], 0, 0,
-                                                                    0, bs[j], 0, as[i]);
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af, acc[i][j], 0, 0,
+                                                                      0, bs[j], 0, as);
+      }
+    }
     if (kt + 1 < nk) {
       __syncthreads();  // every wave is done with the other buffer (read two steps ago)
       lstore(buf ^ 1);
@@ -397,29 +452,33 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   // ---- epilogue: lane l holds row l%32 of its M block and, per j, columns
   // 8*(v/4) + 4*(l/32) + v%4 of its 32-column B block ----
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rloc = wm * 64 + 32 * i + l32;
+  for (int i = 0; i < MB; ++i) {
+    const int rloc = wm * (BM / WM) + 32 * i + l32;
     if (rloc >= rows_valid) continue;
     const size_t row = (size_t)m0 + rloc;
     if constexpr (EPI == EPI_SWIGLU) {
-      const int hc = ntile * 64 + 32 * wn;
-      uint16_t* hr = p.C + row * I + hc;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float hv[4];
+      for (int jj = 0; jj < NH; ++jj) {
+        const int hc = ntile * HB + (wn * NH + jj) * 32;
+        if (hc >= I) continue;  // I % 64 == 0: a 32-column block is wholly in or out
+        uint16_t* hr = p.C + row * I + hc;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float gg = acc[i][0][4 * q4 + r], uu = acc[i][1][4 * q4 + r];
-          hv[r] = gg * sigmoid_fast(gg) * uu;
-        }
-        *(u32x2_t*)(hr + 8 * q4 + 4 * kh) = u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-        if (p.gu_out) {
-          uint16_t* gr = p.gu_out + row * 2 * I + hc + 8 * q4 + 4 * kh;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float hv[4];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const f32x16_t& a = acc[i][j];
-            *(u32x2_t*)(gr + j * I) = u32x2_t{pack_bf16x2(a[4 * q4], a[4 * q4 + 1]),
-                                              pack_bf16x2(a[4 * q4 + 2], a[4 * q4 + 3])};
+          for (int r = 0; r < 4; ++r) {
+            const float gg = acc[i][jj][4 * q4 + r], uu = acc[i][jj + NH][4 * q4 + r];
+            hv[r] = gg * sigmoid_fast(gg) * uu;
+          }
+          *(u32x2_t*)(hr + 8 * q4 + 4 * kh) = u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+          if (p.gu_out) {
+            uint16_t* gr = p.gu_out + row * 2 * I + hc + 8 * q4 + 4 * kh;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const f32x16_t& a = acc[i][jj + u * NH];
+              *(u32x2_t*)(gr + u * I) = u32x2_t{pack_bf16x2(a[4 * q4], a[4 * q4 + 1]),
+                                                pack_bf16x2(a[4 * q4 + 2], a[4 * q4 + 3])};
+            }
           }
         }
       }
@@ -427,8 +486,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
       // acc = dh[row, c] (fp32), c < I; with s = sigmoid(g), from the saved bf16 g,u:
       // dgu[row] = [dh u s (1 + g (1 - s)), dh g s]
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c0 = ntile * kMxBN + wn * 64 + 32 * j;
+      for (int j = 0; j < NB; ++j) {
+        const int c0 = ntile * BN + bcol0(j);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int c = c0 + 8 * q4 + 4 * kh;
@@ -453,8 +512,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     } else {
       uint16_t* cg = KGRP ? p.C + (size_t)g * p.M * N : p.C;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c0 = ntile * kMxBN + wn * 64 + 32 * j;
+      for (int j = 0; j < NB; ++j) {
+        const int c0 = ntile * BN + bcol0(j);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int c = c0 + 8 * q4 + 4 * kh;
@@ -468,36 +527,55 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   }
 }
 
+// Tile configurations (BM, BN, WM, WN): the SwiGLU forward and backward and the plain
+// store by rows, and the weight gradients by K. 256x256 tiles with eight waves of 128x64
+// (measured on the Qwen3-shaped stages, one process per build: 1.59 ms for the six
+// against 1.80 with 128x128 tiles of four 64x64 waves and 2.19 with 256x128 or 128x256
+// tiles of four waves; 4x2 waves of 64x128 the same as 2x4).
+#ifndef MOE_MX_TILE_ROWS
+#define MOE_MX_TILE_ROWS 256, 256, 2, 4
+#endif
+#ifndef MOE_MX_TILE_SWIGLU
+#define MOE_MX_TILE_SWIGLU 256, 256, 2, 4
+#endif
+#ifndef MOE_MX_TILE_SWIGLU_BWD
+#define MOE_MX_TILE_SWIGLU_BWD 256, 256, 2, 4
+#endif
+#ifndef MOE_MX_TILE_WGRAD
+#define MOE_MX_TILE_WGRAD 256, 256, 2, 4
+#endif
+
+namespace {
+template <int EPI, bool KGRP, int BM, int BN, int WM, int WN>
+hipError_t mx_launch(const MxArgs& a, int rows, hipStream_t s) {
+  long long tiles;
+  if (KGRP) tiles = (long long)a.G * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  else tiles = ((long long)rows / BM + a.G) *
+               (EPI == EPI_SWIGLU ? (a.I + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN);
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  mx_gemm_kernel<EPI, KGRP, BM, BN, WM, WN><<<(unsigned)tiles, WM * WN * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_mx_gemm(int epi, const void* A, const uint8_t* sa, const void* B,
                           const uint8_t* sb, const int32_t* offsets, int G, int rows, int N,
                           int K, int I, void* C, hipStream_t s, const void* gu_in,
                           void* gu_out) {
-  const int ntn = epi == EPI_SWIGLU ? I / 64 : (N + kMxBN - 1) / kMxBN;
-  const long long tiles = ((long long)rows / kMxBM + G) * ntn;  // upper bound
-  if (tiles <= 0) return hipSuccess;
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   MxArgs a{(const uint8_t*)A, sa, (const uint8_t*)B, sb, offsets, G, 0, N, K, I, (uint16_t*)C,
            (const uint16_t*)gu_in, (uint16_t*)gu_out};
-  if (epi == EPI_SWIGLU)
-    mx_gemm_kernel<EPI_SWIGLU, false><<<(unsigned)tiles, 256, 0, s>>>(a);
-  else if (epi == EPI_SWIGLU_BWD)
-    mx_gemm_kernel<EPI_SWIGLU_BWD, false><<<(unsigned)tiles, 256, 0, s>>>(a);
-  else
-    mx_gemm_kernel<EPI_STORE, false><<<(unsigned)tiles, 256, 0, s>>>(a);
-  return hipGetLastError();
+  if (epi == EPI_SWIGLU) return mx_launch<EPI_SWIGLU, false, MOE_MX_TILE_SWIGLU>(a, rows, s);
+  if (epi == EPI_SWIGLU_BWD) return mx_launch<EPI_SWIGLU_BWD, false, MOE_MX_TILE_SWIGLU_BWD>(a, rows, s);
+  return mx_launch<EPI_STORE, false, MOE_MX_TILE_ROWS>(a, rows, s);
 }
 
 hipError_t launch_mx_gemm_wgrad(const void* At, const uint8_t* sa, const void* Bt,
                                 const uint8_t* sb, const int32_t* col_offsets, int G, int M,
                                 int N, int Kp, void* C, hipStream_t s) {
-  const long long tiles =
-      (long long)G * ((M + kMxBM - 1) / kMxBM) * ((N + kMxBN - 1) / kMxBN);
-  if (tiles <= 0) return hipSuccess;
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   MxArgs a{(const uint8_t*)At, sa, (const uint8_t*)Bt, sb, col_offsets, G, M, N, Kp, 0,
            (uint16_t*)C, nullptr, nullptr};
-  mx_gemm_kernel<EPI_STORE, true><<<(unsigned)tiles, 256, 0, s>>>(a);
-  return hipGetLastError();
+  return mx_launch<EPI_STORE, true, MOE_MX_TILE_WGRAD>(a, 0, s);
 }
 
 }  // namespace moe

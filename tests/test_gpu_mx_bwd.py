@@ -38,7 +38,8 @@ def _rows(rng, R, C):
 
 
 @pytest.mark.parametrize("counts,C", [([130, 0, 1, 255, 64, 33], 64), ([7], 200),
-                                      ([300, 129, 0, 128], 768)])
+                                      ([300, 129, 0, 128], 768),
+                                      ([(i * 37) % 70 for i in range(600)], 64)])
 def test_quantize_mxfp8_cols_bit_exact(counts, C):
     _say("mx cols", counts, C)
     rng = np.random.default_rng(C + len(counts))
