@@ -13,10 +13,10 @@
 // Layout: A [rows, K] codes with scales [rows, K/32]; B [G, N, K] codes (output-channel
 // major) with scales [G, N, K/32].
 //
-// Tiles: BM rows x BN B rows per block (256 x 256, eight waves of 128 x 64 as 4 x 2 blocks
-// of 32x32), K in steps of 64 bytes through a double-buffered LDS stage loaded by all
-// threads (16-byte loads into registers, then LDS), the next stage's loads in flight during
-// the multiply. SwiGLU: a block's first BN/2 B rows are gate columns and the last BN/2 the
+// Tiles: BM rows x BN B rows per block (320 or 256 x 256, eight waves of 160 or 128 x 64 as
+// 5 or 4 x 2 blocks of 32x32), K in steps of 64 bytes through a double-buffered LDS stage
+// loaded by all threads (16-byte loads into registers, then LDS), the next stage's loads in
+// flight during the multiply. SwiGLU: a block's first BN/2 B rows are gate columns and the last BN/2 the
 // matching up columns, and a wave's B blocks pair a gate block with its up block, so
 // h = silu(g) u is formed in registers. One block per tile; the grid covers an upper bound
 // of the tile count and the extra blocks exit.
@@ -276,8 +276,9 @@ template <int EPI, bool KGRP, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
   constexpr int NT = WM * WN * 64;
   constexpr int MB = BM / WM / 32, NB = BN / WN / 32, NH = NB / 2, HB = BN / 2;
-  constexpr int A_PER = BM * 4 / NT, B_PER = BN * 4 / NT;  // 16-byte chunks per thread
-  static_assert(A_PER >= 1 && B_PER >= 1 && BM * 4 % NT == 0 && BN * 4 % NT == 0, "load split");
+  // 16-byte chunks per thread (the last round partial when BM * 4 is not a multiple of NT)
+  constexpr int A_PER = (BM * 4 + NT - 1) / NT, B_PER = (BN * 4 + NT - 1) / NT;
+  static_assert(BN * 4 % NT == 0 && BM % 32 == 0, "load split");
   static_assert(EPI != EPI_SWIGLU || NB % 2 == 0, "SwiGLU pairs gate and up blocks");
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][BM * kMxBK];
   __shared__ __attribute__((aligned(16))) uint8_t s_b[2][BN * kMxBK];
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
   const uint8_t* pb[B_PER];
 #pragma unroll
   for (int h = 0; h < A_PER; ++h) {
-    const int c = tid + NT * h, r = c >> 2;
+    const int c = tid + NT * h, r = c >> 2;  // c >= BM * 4: no chunk (pa unused)
     pa[h] = p.A + (size_t)(m0 + (r < rows_valid ? r : 0)) * K + k0 + (c & 3) * 16;  // dead rows: the first
   }
 #pragma unroll
@@ -368,7 +369,8 @@ __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
   uint16_t rs[SC_PER];
   auto gload = [&](int kt) {
 #pragma unroll
-    for (int h = 0; h < A_PER; ++h) ra[h] = *(const u32x4_t*)(pa[h] + (size_t)kt * kMxBK);
+    for (int h = 0; h < A_PER; ++h)
+      if (BM * 4 % NT == 0 || tid + NT * h < BM * 4) ra[h] = *(const u32x4_t*)(pa[h] + (size_t)kt * kMxBK);
 #pragma unroll
     for (int h = 0; h < B_PER; ++h) rb[h] = *(const u32x4_t*)(pb[h] + (size_t)kt * kMxBK);
 #pragma unroll
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
 #pragma unroll
     for (int h = 0; h < A_PER; ++h) {
       const int c = tid + NT * h;
-      *(u32x4_t*)&s_a[buf][chunk_at(c >> 2, c & 3)] = ra[h];
+      if (BM * 4 % NT == 0 || c < BM * 4) *(u32x4_t*)&s_a[buf][chunk_at(c >> 2, c & 3)] = ra[h];
     }
 #pragma unroll
     for (int h = 0; h < B_PER; ++h) {
@@ -528,18 +530,20 @@ __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
 }
 
 // Tile configurations (BM, BN, WM, WN): the SwiGLU forward and backward and the plain
-// store by rows, and the weight gradients by K. 256x256 tiles with eight waves of 128x64
-// (measured on the Qwen3-shaped stages, one process per build: 1.59 ms for the six
-// against 1.80 with 128x128 tiles of four 64x64 waves and 2.19 with 256x128 or 128x256
-// tiles of four waves; 4x2 waves of 64x128 the same as 2x4).
+// store by rows, and the weight gradients by K. Eight waves of 128x64 or 160x64 (measured on
+// the Qwen3-shaped stages, one process per build: with exactly 256 rows per expert 1.59 ms
+// for the six at 256x256 against 1.80 with 128x128 tiles of four 64x64 waves and 2.19 with
+// 256x128 or 128x256 tiles of four waves; 4x2 waves the same as 2x4). With the routed
+// (ragged) rows, 320-row tiles keep most experts to one M tile: the four row-grouped
+// launches 0.89 ms against 1.12 with 256 rows.
 #ifndef MOE_MX_TILE_ROWS
-#define MOE_MX_TILE_ROWS 256, 256, 2, 4
+#define MOE_MX_TILE_ROWS 320, 256, 2, 4
 #endif
 #ifndef MOE_MX_TILE_SWIGLU
-#define MOE_MX_TILE_SWIGLU 256, 256, 2, 4
+#define MOE_MX_TILE_SWIGLU 320, 256, 2, 4
 #endif
 #ifndef MOE_MX_TILE_SWIGLU_BWD
-#define MOE_MX_TILE_SWIGLU_BWD 256, 256, 2, 4
+#define MOE_MX_TILE_SWIGLU_BWD 320, 256, 2, 4
 #endif
 #ifndef MOE_MX_TILE_WGRAD
 #define MOE_MX_TILE_WGRAD 256, 256, 2, 4
