@@ -511,20 +511,45 @@ __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
           *(u32x2_t*)(p.C + o + I) = u32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
         }
       }
-    } else {
-      uint16_t* cg = KGRP ? p.C + (size_t)g * p.M * N : p.C;
+    }
+  }
+  if constexpr (EPI == EPI_STORE) {
+    // Through LDS, so that every store covers whole 128-byte lines: per M block, the wave
+    // writes its 32 rows x 64 columns (bf16) into a 4 KB area of its own, the 16-byte chunk
+    // index XORed with row%8, and reads them back as 16 consecutive bytes of one row per
+    // lane. The areas lie in the stage buffer the last K step did not use: every wave
+    // finished reading it before the barrier that preceded the last stage's LDS writes
+    // (with a single K step it was never written).
+    static_assert(BM * kMxBK >= 4 * 4096 && BN * kMxBK >= 4 * 4096 && NB == 2 && WM * WN == 8,
+                  "staging areas: eight waves of 32 x 64 bf16");
+    const int sb_ = nk & 1;
+    uint8_t* stg = (wave < 4 ? s_a[sb_] : s_b[sb_]) + (wave & 3) * 4096;
+    uint16_t* cg = KGRP ? p.C + (size_t)g * p.M * N : p.C;
+    const int c0 = ntile * BN + bcol0(0);  // this wave's 64 columns (N % 64 == 0: all or none)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int c0 = ntile * BN + bcol0(j);
+    for (int i = 0; i < MB; ++i) {
+      const int r0 = wm * (BM / WM) + 32 * i;
+      if (r0 >= rows_valid || c0 >= N) continue;  // wave-uniform
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int c = c0 + 8 * q4 + 4 * kh;
-          if (c >= N) continue;
           const f32x16_t& a = acc[i][j];
-          *(u32x2_t*)(cg + row * N + c) =
+          const int chunk = 4 * j + q4;  // columns 32 j + 8 q4 .. +8: 16-byte chunk 4 j + q4
+          *(u32x2_t*)(stg + l32 * 128 + ((chunk ^ (l32 & 7)) << 4) + 8 * kh) =
               u32x2_t{pack_bf16x2(a[4 * q4], a[4 * q4 + 1]), pack_bf16x2(a[4 * q4 + 2], a[4 * q4 + 3])};
         }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        const int r = pass * 8 + (lane >> 3), piece = lane & 7;
+        const u32x4_t v = *(const u32x4_t*)(stg + r * 128 + ((piece ^ (r & 7)) << 4));
+        if (r0 + r < rows_valid)
+          *(u32x4_t*)(cg + ((size_t)m0 + r0 + r) * N + c0 + piece * 8) = v;
       }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
     }
   }
 }
