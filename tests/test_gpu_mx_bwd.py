@@ -173,3 +173,46 @@ def test_layer_mxfp8_training(name, T, E, k, H, I):
     empty = np.flatnonzero(np.diff(fwd["offsets"]) == 0)
     assert not host_vals(g.dw_gu)[empty].any() and not host_vals(g.dw_down)[empty].any()
     _say(name, {k_: f"{v:.2e}" for k_, v in rels.items()})
+
+
+def test_layer_mxfp8_training_full_size_qwen3():
+    """The Qwen3-shaped block (T=4096, H=2048, E=128, top-8, I=768) in the launch
+    configuration the benchmark times with --mx. Routing and offsets whole (bit-exact); an
+    expert's output rows, dgu and dxp rows and weight gradients depend only on the rows
+    routed to it, so the oracle runs that expert's MXFP8 MLP forward and backward alone,
+    on sampled experts (the most and the least loaded, and one more)."""
+    w = W.WORKLOADS["qwen3"]
+    _say("layer mxfp8 training full size qwen3")
+    d = W.make_inputs("qwen3")
+    g = GpuMoE(w, d, training=True, mx=True)
+    g.forward()
+    g.backward(d["dy"])
+    idx, q, counts, _, _ = O.router_topk(d["logits"], w.k, w.score)
+    offs, row_of, src_of = O.dispatch_meta(idx, w.E)
+    ints = g.ints()
+    assert np.array_equal(ints["offsets"], offs) and np.array_equal(ints["row_of"], row_of)
+    N, H, I = w.T * w.k, w.H, w.I
+    out = g.view("out", (N, H), torch.bfloat16)
+    dgu = g.view("dgu", (N, 2 * I), torch.bfloat16)
+    dxp = g.view("dxp", (N, H), torch.bfloat16)
+    dy = O.as_values(d["dy"])
+    x = O.as_values(d["x"])
+    qr = np.zeros(N)
+    for j in range(w.k):
+        qr[row_of[:, j]] = q[:, j]
+    n = np.diff(offs)
+    for e in (int(np.argmax(n)), int(np.argmin(np.where(n > 0, n, N))), 77):
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        _say("expert", e, "rows", r1 - r0)
+        eo = np.array([0, r1 - r0])
+        xp = x[src_of[r0:r1]]
+        mlp = O.expert_mlp_mx(xp, d["w_gu"][e:e + 1], d["w_down"][e:e + 1], eo, I)
+        d_out = O.to_bf16(dy[src_of[r0:r1]] * qr[r0:r1, None])
+        rb = O.expert_mlp_mx_backward(mlp, xp, d_out, d["w_gu"][e:e + 1], d["w_down"][e:e + 1], eo, I)
+        check_fp8(host_vals(out[r0:r1]), mlp["out"], f"out[{e}]", rel_l2=1e-2)
+        check_fp8(host_vals(dgu[r0:r1]), rb["dgu"], f"dgu[{e}]", rel_l2=1e-2)
+        check_fp8(host_vals(dxp[r0:r1]), rb["dxp"], f"dxp[{e}]", rel_l2=1e-2)
+        check_fp8(host_vals(g.dw_down[e]), rb["dw_down"][0], f"dw_down[{e}]", rel_l2=1e-2)
+        check_fp8(host_vals(g.dw_gu[e]), rb["dw_gu"][0], f"dw_gu[{e}]", rel_l2=1e-2)
+    assert torch.isfinite(g.dx).all().item()
+    assert torch.isfinite(g.dw_gu).all().item() and torch.isfinite(g.dw_down).all().item()
