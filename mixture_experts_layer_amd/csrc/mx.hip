@@ -484,19 +484,50 @@ __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
           }
         }
       }
-    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-      // acc = dh[row, c] (fp32), c < I; with s = sigmoid(g), from the saved bf16 g,u:
-      // dgu[row] = [dh u s (1 + g (1 - s)), dh g s]
+    }
+  }
+  if constexpr (EPI == EPI_SWIGLU_BWD) {
+    // acc = dh[row, c] (fp32), c < I; with s = sigmoid(g), from the saved bf16 g,u:
+    // dgu[row] = [dh u s (1 + g (1 - s)), dh g s]. Per M block and 32-column N block, the
+    // wave moves g,u in and dg,du out as 64-byte row segments through two 2 KB areas of
+    // its own in LDS (the staging buffer of the store epilogue below), converting between
+    // them and the accumulator layout there; 16-byte chunks XORed with (row/4)%4.
+    static_assert(BM * kMxBK >= 4 * 4096 && BN * kMxBK >= 4 * 4096 && WM * WN == 8,
+                  "staging areas: eight waves of 4 KB");
+    const int sb_ = nk & 1;
+    uint8_t* const sgv = (wave < 4 ? s_a[sb_] : s_b[sb_]) + (wave & 3) * 4096;
+    uint8_t* const suv = sgv + 2048;
+    auto at = [](int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); };
+    const size_t twoI = 2 * (size_t)I;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int r0 = wm * (BM / WM) + 32 * i;
+      if (r0 >= rows_valid) continue;  // wave-uniform
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int c0 = ntile * BN + bcol0(j);
+        const int cb = ntile * BN + bcol0(j);  // 32 dh columns (I % 64 == 0: all or none)
+        if (cb >= N) continue;
+        // g, u in: piece p = lane + 64 h is row p/4, 16-byte chunk p%4
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int pc = lane + 64 * h, rr = pc >> 2, ch = pc & 3;
+          u32x4_t gv = u32x4_t{0u, 0u, 0u, 0u}, uv = gv;
+          if (r0 + rr < rows_valid) {
+            const uint16_t* src = p.gu_in + ((size_t)m0 + r0 + rr) * twoI + cb + ch * 8;
+            gv = *(const u32x4_t*)src;
+            uv = *(const u32x4_t*)(src + I);
+          }
+          *(u32x4_t*)(sgv + at(rr, ch)) = gv;
+          *(u32x4_t*)(suv + at(rr, ch)) = uv;
+        }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+        // accumulator layout: row l32, columns 8 q4 + 4 kh .. +4 (chunk q4, byte 8 kh)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int c = c0 + 8 * q4 + 4 * kh;
-          if (c >= N) continue;
-          const size_t o = row * 2 * I + c;
-          const u32x2_t gw = *(const u32x2_t*)(p.gu_in + o);
-          const u32x2_t uw = *(const u32x2_t*)(p.gu_in + o + I);
+          u32x2_t* gp = (u32x2_t*)(sgv + at(l32, q4) + 8 * kh);
+          u32x2_t* up = (u32x2_t*)(suv + at(l32, q4) + 8 * kh);
+          const u32x2_t gw = *gp, uw = *up;
           float dg[4], du[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -507,9 +538,25 @@ __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
             dg[e] = dh * uu * sg * (1.0f + gg * (1.0f - sg));
             du[e] = dh * gg * sg;
           }
-          *(u32x2_t*)(p.C + o) = u32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-          *(u32x2_t*)(p.C + o + I) = u32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+          *gp = u32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+          *up = u32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
         }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+        // dg, du out
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int pc = lane + 64 * h, rr = pc >> 2, ch = pc & 3;
+          const u32x4_t gv = *(const u32x4_t*)(sgv + at(rr, ch));
+          const u32x4_t uv = *(const u32x4_t*)(suv + at(rr, ch));
+          if (r0 + rr < rows_valid) {
+            uint16_t* dst = p.C + ((size_t)m0 + r0 + rr) * twoI + cb + ch * 8;
+            *(u32x4_t*)dst = gv;
+            *(u32x4_t*)(dst + I) = uv;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
       }
     }
   }
