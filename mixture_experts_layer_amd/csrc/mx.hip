@@ -451,37 +451,68 @@ __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
       __syncthreads();
     }
   }
-  // ---- epilogue: lane l holds row l%32 of its M block and, per j, columns
-  // 8*(v/4) + 4*(l/32) + v%4 of its 32-column B block ----
+  // ---- epilogues: lane l holds row l%32 of its M block and, per j, columns
+  // 8*(v/4) + 4*(l/32) + v%4 of its 32-column B block. Each goes through LDS areas of the
+  // wave's own in the stage buffer the last K step did not use (every wave finished reading
+  // it before the barrier that preceded the last stage's LDS writes; with a single K step it
+  // was never written), so that global memory sees row segments of 64 or 128 bytes ----
+  static_assert(BM * kMxBK >= 4 * 4096 && BN * kMxBK >= 4 * 4096 && WM * WN == 8,
+                "staging areas: eight waves of 4 KB");
+  const int sb_ = nk & 1;
+  uint8_t* const stg = (wave < 4 ? s_a[sb_] : s_b[sb_]) + (wave & 3) * 4096;
+  // 32 rows of 64 bytes, 16-byte chunks XORed with (row/4)%4
+  auto at = [](int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); };
+  if constexpr (EPI == EPI_SWIGLU) {
+    // per M block and gate block: h = silu(g) u (and, training, g and u) as bf16 32 x 32
+    // tiles, written in the accumulator layout and read back as 16-byte row pieces
+    uint8_t* const s0 = stg;
+    uint8_t* const s1 = stg + 2048;
+    auto put = [&](uint8_t* area, int q4, float a0, float a1, float a2, float a3) {
+      *(u32x2_t*)(area + at(l32, q4) + 8 * kh) = u32x2_t{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+    };
+    auto sync_wave = [&]() {
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+    };
+    auto out = [&](const uint8_t* area, uint16_t* base, size_t ld, int r0, int col) {
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int rloc = wm * (BM / WM) + 32 * i + l32;
-    if (rloc >= rows_valid) continue;
-    const size_t row = (size_t)m0 + rloc;
-    if constexpr (EPI == EPI_SWIGLU) {
+      for (int h = 0; h < 2; ++h) {
+        const int pc = lane + 64 * h, rr = pc >> 2, ch = pc & 3;
+        const u32x4_t v = *(const u32x4_t*)(area + at(rr, ch));
+        if (r0 + rr < rows_valid) *(u32x4_t*)(base + ((size_t)m0 + r0 + rr) * ld + col + ch * 8) = v;
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int r0 = wm * (BM / WM) + 32 * i;
+      if (r0 >= rows_valid) continue;  // wave-uniform
 #pragma unroll
       for (int jj = 0; jj < NH; ++jj) {
         const int hc = ntile * HB + (wn * NH + jj) * 32;
         if (hc >= I) continue;  // I % 64 == 0: a 32-column block is wholly in or out
-        uint16_t* hr = p.C + row * I + hc;
+        const f32x16_t& ga = acc[i][jj];
+        const f32x16_t& ua = acc[i][jj + NH];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           float hv[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float gg = acc[i][jj][4 * q4 + r], uu = acc[i][jj + NH][4 * q4 + r];
+            const float gg = ga[4 * q4 + r], uu = ua[4 * q4 + r];
             hv[r] = gg * sigmoid_fast(gg) * uu;
           }
-          *(u32x2_t*)(hr + 8 * q4 + 4 * kh) = u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-          if (p.gu_out) {
-            uint16_t* gr = p.gu_out + row * 2 * I + hc + 8 * q4 + 4 * kh;
+          put(s0, q4, hv[0], hv[1], hv[2], hv[3]);
+          if (p.gu_out) put(s1, q4, ga[4 * q4], ga[4 * q4 + 1], ga[4 * q4 + 2], ga[4 * q4 + 3]);
+        }
+        sync_wave();
+        out(s0, p.C, (size_t)I, r0, hc);
+        if (p.gu_out) out(s1, p.gu_out, 2 * (size_t)I, r0, hc);
+        sync_wave();
+        if (p.gu_out) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const f32x16_t& a = acc[i][jj + u * NH];
-              *(u32x2_t*)(gr + u * I) = u32x2_t{pack_bf16x2(a[4 * q4], a[4 * q4 + 1]),
-                                                pack_bf16x2(a[4 * q4 + 2], a[4 * q4 + 3])};
-            }
-          }
+          for (int q4 = 0; q4 < 4; ++q4) put(s0, q4, ua[4 * q4], ua[4 * q4 + 1], ua[4 * q4 + 2], ua[4 * q4 + 3]);
+          sync_wave();
+          out(s0, p.gu_out, 2 * (size_t)I, r0, I + hc);
+          sync_wave();
         }
       }
     }
@@ -489,15 +520,10 @@ __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
   if constexpr (EPI == EPI_SWIGLU_BWD) {
     // acc = dh[row, c] (fp32), c < I; with s = sigmoid(g), from the saved bf16 g,u:
     // dgu[row] = [dh u s (1 + g (1 - s)), dh g s]. Per M block and 32-column N block, the
-    // wave moves g,u in and dg,du out as 64-byte row segments through two 2 KB areas of
-    // its own in LDS (the staging buffer of the store epilogue below), converting between
-    // them and the accumulator layout there; 16-byte chunks XORed with (row/4)%4.
-    static_assert(BM * kMxBK >= 4 * 4096 && BN * kMxBK >= 4 * 4096 && WM * WN == 8,
-                  "staging areas: eight waves of 4 KB");
-    const int sb_ = nk & 1;
-    uint8_t* const sgv = (wave < 4 ? s_a[sb_] : s_b[sb_]) + (wave & 3) * 4096;
-    uint8_t* const suv = sgv + 2048;
-    auto at = [](int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); };
+    // wave moves g,u in and dg,du out as 64-byte row segments through the two 2 KB halves
+    // of its area, converting between them and the accumulator layout there.
+    uint8_t* const sgv = stg;
+    uint8_t* const suv = stg + 2048;
     const size_t twoI = 2 * (size_t)I;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
@@ -561,16 +587,10 @@ __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
     }
   }
   if constexpr (EPI == EPI_STORE) {
-    // Through LDS, so that every store covers whole 128-byte lines: per M block, the wave
-    // writes its 32 rows x 64 columns (bf16) into a 4 KB area of its own, the 16-byte chunk
-    // index XORed with row%8, and reads them back as 16 consecutive bytes of one row per
-    // lane. The areas lie in the stage buffer the last K step did not use: every wave
-    // finished reading it before the barrier that preceded the last stage's LDS writes
-    // (with a single K step it was never written).
-    static_assert(BM * kMxBK >= 4 * 4096 && BN * kMxBK >= 4 * 4096 && NB == 2 && WM * WN == 8,
-                  "staging areas: eight waves of 32 x 64 bf16");
-    const int sb_ = nk & 1;
-    uint8_t* stg = (wave < 4 ? s_a[sb_] : s_b[sb_]) + (wave & 3) * 4096;
+    // Whole 128-byte lines: per M block, the wave writes its 32 rows x 64 columns (bf16)
+    // into its 4 KB area, the 16-byte chunk index XORed with row%8, and reads them back as
+    // 16 consecutive bytes of one row per lane.
+    static_assert(NB == 2, "a wave's 64 output columns");
     uint16_t* cg = KGRP ? p.C + (size_t)g * p.M * N : p.C;
     const int c0 = ntile * BN + bcol0(0);  // this wave's 64 columns (N % 64 == 0: all or none)
 #pragma unroll
