@@ -273,7 +273,7 @@ struct MxArgs {
 // the long launches. SwiGLU: the tile's first BN/2 B rows are gate columns, the last BN/2
 // the matching up columns, and a wave's N blocks are NB/2 gate blocks then their up blocks.
 template <int EPI, bool KGRP, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
+__global__ __launch_bounds__(WM* WN * 64, 2) void mx_gemm_kernel(MxArgs p) {
   constexpr int NT = WM * WN * 64;
   constexpr int MB = BM / WM / 32, NB = BN / WN / 32, NH = NB / 2, HB = BN / 2;
   // 16-byte chunks per thread (the last round partial when BM * 4 is not a multiple of NT)
@@ -289,7 +289,8 @@ __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
   const int wm = wave / WN, wn = wave % WN;
   const int K = p.K, I = p.I, N = p.N;
   const int KB = K / 32;
-  // ---- tile decode ----
+  // ---- tile decode (blocks in tile order: an XCD-contiguous remapping of the tiles measured
+  // no faster, dW_down 7 % faster and dW_gu 5 % slower) ----
   int g, ntile, m0, rows_valid, k0, nk;
   if constexpr (KGRP) {
     const int mt = (p.M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
@@ -456,10 +457,10 @@ __global__ __launch_bounds__(WM* WN * 64) void mx_gemm_kernel(MxArgs p) {
   // wave's own in the stage buffer the last K step did not use (every wave finished reading
   // it before the barrier that preceded the last stage's LDS writes; with a single K step it
   // was never written), so that global memory sees row segments of 64 or 128 bytes ----
-  static_assert(BM * kMxBK >= 4 * 4096 && BN * kMxBK >= 4 * 4096 && WM * WN == 8,
-                "staging areas: eight waves of 4 KB");
+  constexpr int NA = BM * kMxBK / 4096;  // 4 KB areas in the A half of a stage buffer
+  static_assert(NA + BN * kMxBK / 4096 >= WM * WN, "staging areas: one of 4 KB per wave");
   const int sb_ = nk & 1;
-  uint8_t* const stg = (wave < 4 ? s_a[sb_] : s_b[sb_]) + (wave & 3) * 4096;
+  uint8_t* const stg = wave < NA ? s_a[sb_] + wave * 4096 : s_b[sb_] + (wave - NA) * 4096;
   // 32 rows of 64 bytes, 16-byte chunks XORed with (row/4)%4
   auto at = [](int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); };
   if constexpr (EPI == EPI_SWIGLU) {
