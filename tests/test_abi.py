@@ -88,3 +88,33 @@ def test_router_entry_points_validate_on_the_host(lib):
     assert lib.moe_router_logits(None, None, 8, 128, 4, None, None) == 1
     assert lib.moe_router_logits(None, None, 8, 100, 4, None, None) == 2
     assert lib.moe_dispatch_backward_router(None, None, None, None, None, 8, 128, 4, 2, None, None) == 1
+
+
+def test_mxfp8_backward_entry_points_validate_on_the_host(lib):
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    cap = lib.moe_mxfp8_cols_capacity
+    cap.argtypes, cap.restype = [i, i], ctypes.c_longlong
+    # every expert's range rounded up to 64 columns: at most R + 63 G, rounded to 64
+    assert cap(0, 1) == 64 and cap(1, 1) == 64 and cap(64, 1) == 128 and cap(32768, 128) == 40832
+    assert cap(-1, 4) == -1 and cap(10, 0) == -1
+    fake = vp(0x1000)
+    co = lib.moe_mxfp8_col_offsets
+    co.argtypes = [vp, i, vp, vp]
+    assert co(None, 4, fake, None) == 1 and co(fake, 0, fake, None) == 1
+    qc = lib.moe_quantize_mxfp8_cols
+    qc.argtypes = [vp, i, i, vp, vp, i, i, vp, vp, vp]
+    assert qc(fake, 100, 64, fake, fake, 4, 64, fake, fake, None) == 1     # Kp below capacity
+    assert qc(fake, 100, 64, fake, fake, 4, 448 + 32, fake, fake, None) == 2  # Kp % 64
+    assert qc(fake, 100, 60, fake, fake, 4, 448, fake, fake, None) == 2    # C % 8
+    assert qc(fake, 100, 64, None, fake, 4, 448, fake, fake, None) == 1    # no offsets
+    wg = lib.moe_grouped_gemm_mxfp8_wgrad
+    wg.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp, vp]
+    assert wg(fake, fake, fake, fake, fake, 4, 96, 64, 448, fake, None) == 2   # M % 64
+    assert wg(fake, fake, fake, fake, fake, 4, 64, 64, 480, fake, None) == 2   # Kp % 64
+    assert wg(fake, None, fake, fake, fake, 4, 64, 64, 448, fake, None) == 1   # no scales
+    sb = lib.moe_grouped_gemm_mxfp8_swiglu_bwd
+    sb.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp]
+    assert sb(fake, fake, fake, fake, fake, 4, 100, 96, 256, fake, fake, None) == 2  # I % 64
+    assert sb(fake, fake, fake, fake, fake, 4, 100, 64, 200, fake, fake, None) == 2  # K % 64
+    assert sb(fake, fake, fake, fake, fake, 4, 100, 64, 256, None, fake, None) == 1  # no g,u
+    assert sb(fake, fake, fake, fake, fake, 4, 0, 64, 256, fake, fake, None) == 0    # no rows
