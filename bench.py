@@ -30,13 +30,15 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def stage_costs(w, training, active=None):
+def stage_costs(w, training, active=None, mx=False):
     """Algorithmic FLOPs and HBM bytes of each GEMM launch (read every input once,
     write every output once). Weights are counted for the `active` experts (those that
-    received rows; all E by default): an expert with no rows has no tiles."""
+    received rows; all E by default): an expert with no rows has no tiles. mx: every GEMM
+    operand is e4m3 (the scale bytes, 1/32 more, are not counted); outputs stay bf16."""
     N, H, I = w.T * w.k, w.H, w.I
     E = w.E if active is None else active
-    act = 1 if w.fp8 else 2
+    act = 1 if (w.fp8 or mx) else 2
+    q = 1 if mx else 2  # backward GEMM operands
     c = {
         "gemm1_swiglu": (2.0 * N * H * 2 * I,
                          N * H * act + E * H * 2 * I * act + N * I * 2 + (N * 2 * I * 2 if training else 0)),
@@ -44,10 +46,10 @@ def stage_costs(w, training, active=None):
     }
     if training:
         c.update({
-            "gemm2_bwd_swiglu": (2.0 * N * H * I, N * H * 2 + E * I * H * 2 + 2 * N * 2 * I * 2),
-            "dw_down": (2.0 * N * I * H, N * I * 2 + N * H * 2 + E * I * H * 2),
-            "gemm1_bwd_dx": (2.0 * N * 2 * I * H, N * 2 * I * 2 + E * H * 2 * I * 2 + N * H * 2),
-            "dw_gu": (2.0 * N * H * 2 * I, N * H * 2 + N * 2 * I * 2 + E * H * 2 * I * 2),
+            "gemm2_bwd_swiglu": (2.0 * N * H * I, N * H * q + E * I * H * q + 2 * N * 2 * I * 2),
+            "dw_down": (2.0 * N * I * H, N * I * q + N * H * q + E * I * H * 2),
+            "gemm1_bwd_dx": (2.0 * N * 2 * I * H, N * 2 * I * q + E * H * 2 * I * q + N * H * 2),
+            "dw_gu": (2.0 * N * H * 2 * I, N * H * q + N * 2 * I * q + E * H * 2 * I * 2),
         })
     return c
 
@@ -146,16 +148,17 @@ def pmc_summary(fetch_dir, write_dir, workload):
     return "\n".join(lines)
 
 
-def measured_traffic(stage):
+def measured_traffic(stage, workload):
     """HBM bytes per launch of `stage` from the committed counter summary, or None when the
-    summary is missing or the GEMM source changed since the counters were taken."""
+    summary is missing, was taken on another workload, or the GEMM source changed since the
+    counters were taken."""
     try:
         text = open(TRAFFIC_FILE).read()
         blob = text.split("```json", 1)[1].split("```", 1)[0]
         data = json.loads(blob)
     except (OSError, IndexError, ValueError):
         return None
-    if data.get("gemm_source_sha256_16") != _source_hash():
+    if data.get("gemm_source_sha256_16") != _source_hash() or data.get("workload") != workload:
         return None
     return data["bytes_per_launch"].get(stage)
 
@@ -191,8 +194,8 @@ def main():
                     help="apply the routing weights to the expert outputs (combine) or inputs")
     ap.add_argument("--align", type=int, default=0, help="padded dispatch alignment (rows)")
     ap.add_argument("--mx", action="store_true",
-                    help="the MXFP8 recipe (e4m3 with a power-of-two scale per 32 along K), "
-                         "forward only")
+                    help="the MXFP8 recipe (e4m3 with a power-of-two scale per 32 along K) in "
+                         "every expert GEMM, forward and (training workloads) backward")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch each stage once plus a 256 MiB calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -226,10 +229,9 @@ def main():
     logits = torch.from_numpy(d["logits"]).to(dev)
     shared_gu = bf(d["shared_gu"]) if w.shared_I else None
     shared_down = bf(d["shared_down"]) if w.shared_I else None
-    if args.mx:  # forward only; the cost model and peaks are the fp8 ones
+    if args.mx:  # the per-row fp8 recipe is replaced, not combined
         import dataclasses
-        w = dataclasses.replace(w, fp8=False, training=False)
-        training = False
+        w = dataclasses.replace(w, fp8=False)
     dtype = M.MOE_MXFP8 if args.mx else (M.MOE_FP8_E4M3 if w.fp8 else M.MOE_BF16)
     w_gu_s = w_down_s = None
     if w.fp8:  # offline weight preparation, outside the timed region
@@ -240,13 +242,32 @@ def main():
         w_down_s = torch.empty((w.E, w.H), dtype=torch.float32, device=dev)
         M.moe_quantize_fp8_weights(w_down, dq, w_down_s)
         w_gu, w_down = wq, dq
-    if args.mx:  # offline weight preparation, outside the timed region
-        wq = torch.empty((w.E, 2 * w.I, w.H), dtype=torch.uint8, device=dev)
-        w_gu_s = torch.empty((w.E, 2 * w.I, w.H // 32), dtype=torch.uint8, device=dev)
-        M.moe_quantize_mxfp8_weights(w_gu, wq, w_gu_s)
-        dq = torch.empty((w.E, w.H, w.I), dtype=torch.uint8, device=dev)
-        w_down_s = torch.empty((w.E, w.H, w.I // 32), dtype=torch.uint8, device=dev)
-        M.moe_quantize_mxfp8_weights(w_down, dq, w_down_s)
+    mx_bwd = {}
+    if args.mx:
+        # weight preparation, once per optimizer update (outside the timed region; timed
+        # below as its own launches): codes blocked along the forward K, and for training a
+        # second copy blocked along the stored last axis for the data gradients
+        E_, H_, I_ = w.E, w.H, w.I
+        w_gu_bf, w_down_bf = w_gu, w_down
+        wq = torch.empty((E_, 2 * I_, H_), dtype=torch.uint8, device=dev)
+        w_gu_s = torch.empty((E_, 2 * I_, H_ // 32), dtype=torch.uint8, device=dev)
+        dq = torch.empty((E_, H_, I_), dtype=torch.uint8, device=dev)
+        w_down_s = torch.empty((E_, H_, I_ // 32), dtype=torch.uint8, device=dev)
+        mx_prep = {"quantize_w_fwd": lambda: (M.moe_quantize_mxfp8_weights(w_gu_bf, wq, w_gu_s),
+                                              M.moe_quantize_mxfp8_weights(w_down_bf, dq, w_down_s))}
+        if training:
+            gb = torch.empty((E_, H_, 2 * I_), dtype=torch.uint8, device=dev)
+            gbs = torch.empty((E_, H_, 2 * I_ // 32), dtype=torch.uint8, device=dev)
+            db = torch.empty((E_, I_, H_), dtype=torch.uint8, device=dev)
+            dbs = torch.empty((E_, I_, H_ // 32), dtype=torch.uint8, device=dev)
+            mx_prep["quantize_w_bwd"] = lambda: (
+                M.moe_quantize_mxfp8_rows(w_gu_bf.view(E_ * H_, 2 * I_), gb.view(E_ * H_, 2 * I_),
+                                          gbs.view(E_ * H_, 2 * I_ // 32)),
+                M.moe_quantize_mxfp8_rows(w_down_bf.view(E_ * I_, H_), db.view(E_ * I_, H_),
+                                          dbs.view(E_ * I_, H_ // 32)))
+            mx_bwd = dict(w_gu_bwd=gb, w_gu_bwd_scale=gbs, w_down_bwd=db, w_down_bwd_scale=dbs)
+        for fn in mx_prep.values():
+            fn()
         w_gu, w_down = wq, dq
     y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
     router = args.router
@@ -264,7 +285,7 @@ def main():
                      groups[0], groups[1], args.scaling, placement, args.align)
     ws = torch.zeros(M.moe_workspace_bytes(prob), dtype=torch.uint8, device=dev)
     tens = M.tensors(x, None if router else logits, w_gu, w_down, y, w_gu_s, w_down_s, shared_gu,
-                     shared_down, w_router, dw_router, e_bias)
+                     shared_down, w_router, dw_router, e_bias, **mx_bwd)
     router_opts = M.router_opts(e_bias, groups[0], groups[1], args.scaling)
     if training:
         dy = bf(d["dy"])
@@ -361,6 +382,7 @@ def main():
             "quantize_h": lambda: M.moe_quantize_mxfp8_rows(h, hq, hqs),
             "gemm2": lambda: M.moe_grouped_gemm_mxfp8(hq, hqs, w_down, w_down_s, offs, out),
         })
+        launches.update(mx_prep)
     if training:
         d_out = vt("d_out", (N, H), torch.bfloat16)
         dgu = vt("dgu", (N, 2 * I), torch.bfloat16)
@@ -374,6 +396,27 @@ def main():
             "dw_gu": lambda: M.moe_grouped_gemm(M.MOE_GEMM_TN_DW, xp, dgu, offs, dw_gu),
             **({} if router else {
                 "dispatch_bwd": lambda: M.moe_unpermute_combine(dxp, row_of, None, dx)}),
+        })
+    if training and args.mx:
+        Kp = v.mx_kp
+        co = vt("mx_col_offsets", (E + 1,), torch.int32)
+        dgq, dgqs = vt("dgq", (N, 2 * I), torch.uint8), vt("dgq_scale", (N, 2 * I // 32), torch.uint8)
+        ta = lambda C: (vt("mx_ta", (C, Kp), torch.uint8), vt("mx_ta_scale", (C, Kp // 32), torch.uint8))
+        tb = lambda C: (vt("mx_tb", (C, Kp), torch.uint8), vt("mx_tb_scale", (C, Kp // 32), torch.uint8))
+        launches.update({
+            "quantize_dout": lambda: M.moe_quantize_mxfp8_rows(d_out, xq, xqs),
+            "gemm2_bwd_swiglu": lambda: M.moe_grouped_gemm_mxfp8_swiglu_bwd(
+                xq, xqs, mx_bwd["w_down_bwd"], mx_bwd["w_down_bwd_scale"], offs, gu, dgu),
+            "quantize_dgu": lambda: M.moe_quantize_mxfp8_rows(dgu, dgq, dgqs),
+            "gemm1_bwd_dx": lambda: M.moe_grouped_gemm_mxfp8(
+                dgq, dgqs, mx_bwd["w_gu_bwd"], mx_bwd["w_gu_bwd_scale"], offs, dxp),
+            "col_offsets": lambda: M.moe_mxfp8_col_offsets(offs, co),
+            "quantize_cols_h": lambda: M.moe_quantize_mxfp8_cols(h, offs, co, *ta(I)),
+            "quantize_cols_dout": lambda: M.moe_quantize_mxfp8_cols(d_out, offs, co, *tb(H)),
+            "dw_down": lambda: M.moe_grouped_gemm_mxfp8_wgrad(*ta(I), *tb(H), co, dw_down),
+            "quantize_cols_x": lambda: M.moe_quantize_mxfp8_cols(xp, offs, co, *ta(H)),
+            "quantize_cols_dgu": lambda: M.moe_quantize_mxfp8_cols(dgu, offs, co, *tb(2 * I)),
+            "dw_gu": lambda: M.moe_grouped_gemm_mxfp8_wgrad(*ta(H), *tb(2 * I), co, dw_gu),
         })
     if router:
         r_logits = vt("logits", (T, E), torch.float32)
@@ -418,11 +461,8 @@ def main():
     _log("bench: per-launch us " + json.dumps({k_: round(v_, 2) for k_, v_ in kernel_us.items()}))
 
     active = int((counts > 0).sum().item())  # experts that received rows in this step
-    if args.mx:
-        import dataclasses
-        w = dataclasses.replace(w, fp8=True)  # e4m3 operands (scale bytes are 1/32 more)
-    costs = stage_costs(w, training, active)
-    peak_tf = MFMA_PEAK_TFLOPS["fp8" if w.fp8 else "bf16"]
+    costs = stage_costs(w, training, active, mx=args.mx)
+    peak_tf = MFMA_PEAK_TFLOPS["fp8" if (w.fp8 or args.mx) else "bf16"]
     gemm = {}
     for name, (fl, by) in costs.items():
         t = kernel_us[name] * 1e-6
@@ -457,7 +497,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(by / t_dom / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(dom)
+    plain = not (args.mx or w.fp8 or router or args.align > 1 or args.groups or args.expert_bias
+                 or args.score or args.scaling != 1.0 or placement != M.MOE_PLACE_COMBINE)
+    roof["traffic"] = measured_traffic(dom, args.workload) if plain else None
     roof["kernel"] = dom
     roof["launch_us"] = round(kernel_us[dom], 2)
 
@@ -475,7 +517,7 @@ def main():
                           fp8=w.fp8 and not args.mx, mx=args.mx)
         if training:
             O.moe_backward(r, d["dy"][:S], d["w_gu"], d["w_down"], w.I,
-                           w_router_bits=d["w_router"] if router else None)
+                           w_router_bits=d["w_router"] if router else None, mx=args.mx)
         tc = time.perf_counter() - tc0
         threads = max([p.get("num_threads", 1) for p in threadpool_info()
                        if p.get("user_api") == "blas"] or [1])
