@@ -216,3 +216,31 @@ def test_layer_mxfp8_training_full_size_qwen3():
         check_fp8(host_vals(g.dw_gu[e]), rb["dw_gu"][0], f"dw_gu[{e}]", rel_l2=1e-2)
     assert torch.isfinite(g.dx).all().item()
     assert torch.isfinite(g.dw_gu).all().item() and torch.isfinite(g.dw_down).all().item()
+
+
+@pytest.mark.parametrize("align", [64, 128])
+def test_layer_mxfp8_training_padded(align):
+    """MXFP8 training on a padded dispatch: the padding rows are zero, which changes no
+    block maximum and no sum (the token-axis blocks start at every expert's first row
+    either way), so the results are those of the unpadded MXFP8 oracle."""
+    w = W.custom("mxpad", T=300, H=256, E=16, k=4, I=192, zipf_s=1.2, n_empty=3)
+    _say("layer mxfp8 training padded", align)
+    d = W.make_inputs(w)
+    rng = np.random.default_rng(align)
+    dy = W.to_bf16_bits(rng.standard_normal((w.T, w.H)).astype(np.float32))
+    g = GpuMoE(w, d, training=True, mx=True)
+    g.prob.align_size = align
+    g.ws = torch.empty(M.moe_workspace_bytes(g.prob), dtype=torch.uint8, device="cuda")
+    g.ws.fill_(0xFF)
+    g.views = M.moe_workspace_views(g.prob, g.ws)
+    y = host_vals(g.forward())
+    g.backward(dy)
+    fwd = O.moe_forward(d["x"], d["logits"], d["w_gu"], d["w_down"], w.k, w.score, w.I, mx=True)
+    ref = O.moe_backward(fwd, dy, d["w_gu"], d["w_down"], w.I, mx=True)
+    r_off, _, r_row, _ = O.dispatch_meta_padded(fwd["topk_idx"], w.E, align)
+    assert np.array_equal(g.view("offsets", (w.E + 1,), torch.int32).cpu().numpy(), r_off)
+    assert np.array_equal(g.view("row_of", (w.T, w.k), torch.int32).cpu().numpy(), r_row)
+    check_fp8(y, fwd["y"], f"mx padded{align} y", rel_l2=1e-2)
+    check_fp8(host_vals(g.dx), ref["dx"], f"mx padded{align} dx", rel_l2=1e-2)
+    check_fp8(host_vals(g.dw_gu), ref["dw_gu"], f"mx padded{align} dw_gu", rel_l2=1e-2)
+    check_fp8(host_vals(g.dw_down), ref["dw_down"], f"mx padded{align} dw_down", rel_l2=1e-2)
