@@ -132,9 +132,9 @@ def pmc_summary(fetch_dir, write_dir, workload):
             "write_bytes_per_launch": {n: round(out["WRITE_SIZE"]["stages"][n]) for n in GEMM_STAGES}}
     lines = ["# HBM traffic of the grouped-GEMM launches: Qwen3-30B-A3B-shaped block", "",
              "Commands (repository root; rocprofv3 run from /tmp):", "", "```",
-             "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --pmc-pass --no-cpu-baseline",
-             "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o run -- python3 bench.py --pmc-pass --no-cpu-baseline",
-             "python3 bench.py --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write", "```", "",
+             "rocprofv3 --pmc FETCH_SIZE -f csv -d out/pmc_fetch -o run -- python3 bench.py --pmc-pass --no-cpu-baseline",
+             "rocprofv3 --pmc WRITE_SIZE -f csv -d out/pmc_write -o run -- python3 bench.py --pmc-pass --no-cpu-baseline",
+             "python3 bench.py --pmc-summary out/pmc_fetch out/pmc_write", "```", "",
              f"Calibration: a plain copy of {CALIB_BYTES >> 20} MiB reads FETCH_SIZE x {data['fetch_factor']} "
              f"and WRITE_SIZE x {data['write_factor']} of its true byte counts; the factors scale the "
              "GEMM readings below. The data block is read by bench.py while the GEMM source hash matches.", "",
