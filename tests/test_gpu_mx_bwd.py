@@ -244,3 +244,34 @@ def test_layer_mxfp8_training_padded(align):
     check_fp8(host_vals(g.dx), ref["dx"], f"mx padded{align} dx", rel_l2=1e-2)
     check_fp8(host_vals(g.dw_gu), ref["dw_gu"], f"mx padded{align} dw_gu", rel_l2=1e-2)
     check_fp8(host_vals(g.dw_down), ref["dw_down"], f"mx padded{align} dw_down", rel_l2=1e-2)
+
+
+def test_layer_mxfp8_training_with_router():
+    """MXFP8 training with the layer's own router projection: the routing comes from
+    device-computed logits, so near-tie tokens may choose differently from the oracle; as
+    in the bf16 router test, outputs are compared on the tokens whose choice matches and
+    weight gradients on the experts no differing token chose."""
+    from test_gpu_router import _router_choice, _valid_dispatch
+    w = W.custom("mxrouter", T=300, H=256, E=16, k=4, I=192, training=True)
+    _say("layer mxfp8 training with router")
+    d = W.make_inputs(w)
+    g = GpuMoE(w, d, training=True, mx=True, router=True)
+    y = host_vals(g.forward())
+    ref_logits, same, clean = _router_choice(w, d, g)
+    fwd = O.moe_forward(d["x"], ref_logits, d["w_gu"], d["w_down"], w.k, w.score, w.I, mx=True)
+    ints = g.ints()
+    if same.all():
+        for key in ("topk_idx", "counts", "offsets", "row_of", "src_of"):
+            assert np.array_equal(ints[key], fwd[key]), key
+    else:
+        _valid_dispatch(ints, w.E)
+    S, C = np.nonzero(same)[0], np.nonzero(clean)[0]
+    check_fp8(y[S], fwd["y"][S], "mx router y", rel_l2=1e-2)
+    g.backward(d["dy"])
+    rb = O.moe_backward(fwd, d["dy"], d["w_gu"], d["w_down"], w.I, w_router_bits=d["w_router"], mx=True)
+    check_fp8(host_vals(g.dx)[S], rb["dx"][S], "mx router dx", rel_l2=1e-2)
+    check_fp8(host_vals(g.dw_gu)[C], rb["dw_gu"][C], "mx router dw_gu", rel_l2=1e-2)
+    check_fp8(host_vals(g.dw_down)[C], rb["dw_down"][C], "mx router dw_down", rel_l2=1e-2)
+    dl = host_vals(g.view("d_logits", (w.T, w.E), torch.float32))
+    check_fp8(dl[S], rb["d_logits"][S], "mx router d_logits", rel_l2=1e-2)
+    check_fp8(host_vals(g.dw_router)[C], rb["dw_router"][C], "mx router dw_router", rel_l2=1e-2)
