@@ -280,9 +280,14 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void mx_gemm_kernel(MxArgs p) {
   constexpr int A_PER = (BM * 4 + NT - 1) / NT, B_PER = (BN * 4 + NT - 1) / NT;
   static_assert(BN * 4 % NT == 0 && BM % 32 == 0, "load split");
   static_assert(EPI != EPI_SWIGLU || NB % 2 == 0, "SwiGLU pairs gate and up blocks");
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][BM * kMxBK];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][BN * kMxBK];
-  __shared__ uint16_t s_sa[2][BM], s_sb[2][BN];  // two block scales per row per stage
+  // Row-grouped: a ring of three stage buffers, stage kt+2 written while stage kt is
+  // multiplied, into the buffer of stage kt-1, which every wave finished reading before the
+  // last barrier (one barrier per K step). By K (4-5 K steps per tile): two buffers, the
+  // next stage written between two barriers (measured faster there).
+  constexpr int NSTG = KGRP ? 2 : 3;
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[NSTG][BM * kMxBK];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[NSTG][BN * kMxBK];
+  __shared__ uint16_t s_sa[NSTG][BM], s_sb[NSTG][BN];  // two block scales per row per stage
   __shared__ int s_off[264], s_pref[264];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -415,11 +420,15 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void mx_gemm_kernel(MxArgs p) {
   if (nk > 0) {  // uniform per block
     gload(0);
     lstore(0);
+    if (NSTG == 3 && nk > 1) {
+      gload(1);
+      lstore(1);
+    }
     __syncthreads();
   }
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    const int buf = kt % NSTG;
+    if (kt + NSTG - 1 < nk) gload(kt + NSTG - 1);
     i32x8_t bf[NB];
     int bs[NB];
 #pragma unroll
@@ -446,20 +455,27 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void mx_gemm_kernel(MxArgs p) {
                                                                       0, bs[j], 0, as);
       }
     }
-    if (kt + 1 < nk) {
-      __syncthreads();  // every wave is done with the other buffer (read two steps ago)
-      lstore(buf ^ 1);
-      __syncthreads();
+    if constexpr (NSTG == 3) {
+      if (kt + 2 < nk) lstore((kt + 2) % 3);  // stage kt-1's buffer: read before the last barrier
+      __syncthreads();  // stage kt+1 (written one step ago) is visible; stage kt is read
+    } else {
+      if (kt + 1 < nk) {
+        __syncthreads();  // every wave is done with the other buffer (read two steps ago)
+        lstore(buf ^ 1);
+        __syncthreads();
+      }
     }
   }
   // ---- epilogues: lane l holds row l%32 of its M block and, per j, columns
   // 8*(v/4) + 4*(l/32) + v%4 of its 32-column B block. Each goes through LDS areas of the
-  // wave's own in the stage buffer the last K step did not use (every wave finished reading
-  // it before the barrier that preceded the last stage's LDS writes; with a single K step it
-  // was never written), so that global memory sees row segments of 64 or 128 bytes ----
+  // wave's own in a stage buffer no wave reads any more (three buffers: every K step ends
+  // with a barrier, so buffer 0; two: the one the last K step did not use, which every wave
+  // finished reading before the barrier that preceded the last stage's LDS writes, or never
+  // written with a single K step), so that global memory sees row segments of 64 or 128
+  // bytes ----
   constexpr int NA = BM * kMxBK / 4096;  // 4 KB areas in the A half of a stage buffer
   static_assert(NA + BN * kMxBK / 4096 >= WM * WN, "staging areas: one of 4 KB per wave");
-  const int sb_ = nk & 1;
+  const int sb_ = NSTG == 3 ? 0 : (nk & 1);
   uint8_t* const stg = wave < NA ? s_a[sb_] + wave * 4096 : s_b[sb_] + (wave - NA) * 4096;
   // 32 rows of 64 bytes, 16-byte chunks XORed with (row/4)%4
   auto at = [](int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); };
