@@ -128,3 +128,43 @@ def test_router_backward_with_scaling_matches_finite_differences(score):
             fm = (O.topk_probs(lm, idx, score, exact=True, scaling_factor=c) * dq).sum()
             fd = (fp - fm) / (2 * eps)
             assert abs(fd - got[t, e]) <= 1e-7 * np.abs(got).max() + 1e-6 * abs(fd), (t, e, fd, got[t, e])
+
+
+def test_grouping_softmax_before_topk_sums_probabilities():
+    # 4 experts in 2 groups of 2, k = 2 from one group (m = 2), softmax before the top-k:
+    # a group's value is the sum of its experts' softmax probabilities.
+    # Groups [2, 2] and [3, -10]: on probabilities the second wins (e^3 + e^-10 > 2 e^2)
+    # while summed logits would keep the first (4 > -7).
+    lg = np.array([[2.0, 2.0, 3.0, -10.0]], np.float32)
+    assert O.topk_select_ext(lg, 2, O.SOFTMAX_PRE_RENORM, None, 2, 1).tolist() == [[2, 3]]
+    assert O.topk_select_ext(lg, 2, O.SOFTMAX_POST, None, 2, 1).tolist() == [[0, 1]]
+    # groups [2, 2] and [2.5, -10]: the sum keeps the first (2 e^2 > e^2.5), the best single
+    # probability would keep the second
+    lg = np.array([[2.0, 2.0, 2.5, -10.0]], np.float32)
+    assert O.topk_select_ext(lg, 2, O.SOFTMAX_PRE_RENORM, None, 2, 1).tolist() == [[0, 1]]
+
+
+def test_grouping_softmax_before_topk_brute_force():
+    # plain Python with math.exp: every group scored by the sum of the softmax
+    # probabilities of its m best experts, every set of group_topk groups enumerated
+    import math
+    rng = np.random.default_rng(6)
+    T, E, G, gt, k = 25, 12, 4, 2, 4
+    m = k // gt
+    lg = (rng.standard_normal((T, E)) * 2.0).astype(np.float32)
+    idx = O.topk_select_ext(lg, k, O.SOFTMAX_PRE_RENORM, None, G, gt)
+    gs = E // G
+    for t in range(T):
+        row = [float(v) for v in lg[t]]
+        mx = max(row)
+        z = sum(math.exp(v - mx) for v in row)
+        prob = [math.exp(v - mx) / z for v in row]
+        gscore = [sum(sorted(prob[g * gs:(g + 1) * gs], reverse=True)[:m]) for g in range(G)]
+        best = max(sum(gscore[g] for g in c) for c in itertools.combinations(range(G), gt))
+        groups = {int(e) // gs for e in idx[t]}
+        chosen = sorted(groups)
+        while len(chosen) < gt:
+            chosen.append(max((g for g in range(G) if g not in chosen), key=lambda g: gscore[g]))
+        assert abs(sum(gscore[g] for g in chosen) - best) < 1e-6
+        pool = sorted((row[e], -e) for g in chosen for e in range(g * gs, (g + 1) * gs))[::-1]
+        assert [int(e) for e in idx[t]] == [-p[1] for p in pool[:k]]
