@@ -8,6 +8,7 @@ rounding at the points where the GPU path stores narrower types.
 """
 from .moe_oracle import *  # noqa: F401,F403
 from .moe_oracle import (SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID, SQRTSOFTPLUS,  # noqa: F401
+                         SOFTMAX_PRE, SOFTMAX_KINDS, aux_scores, aux_loss, aux_loss_backward,
                          E4M3_MAX,
                          bf16_bits_to_f64, f32_to_bf16_bits, as_values, to_f32, to_bf16,
                          e4m3_decode, e4m3_encode, topk_select, topk_probs, router_topk,

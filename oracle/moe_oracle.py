@@ -26,7 +26,8 @@ from __future__ import annotations
 
 import numpy as np
 
-SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID, SQRTSOFTPLUS = 0, 1, 2, 3
+SOFTMAX_PRE_RENORM, SOFTMAX_POST, SIGMOID, SQRTSOFTPLUS, SOFTMAX_PRE = 0, 1, 2, 3, 4
+SOFTMAX_KINDS = (SOFTMAX_PRE_RENORM, SOFTMAX_POST, SOFTMAX_PRE)
 E4M3_MAX = 448.0
 
 # ---------------------------------------------------------------------------
@@ -124,11 +125,22 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
 
 def _logit_values(logits) -> np.ndarray:
     """Logits as float64 values: float32 logits (the layer's input type) widen exactly;
-    float64 logits (the exact-arithmetic pins) are kept as they are."""
+    float64 logits (the exact-arithmetic pins) are kept as they are.
+    READING (the pages do not treat non-finite logits): -inf marks an expert that can only
+    be chosen when too few others are left, and a NaN logit counts as -inf everywhere
+    (selection and weights), so every token always gets k distinct valid expert ids."""
     l = np.asarray(logits)
     if l.dtype != np.float64:
         l = l.astype(np.float32)
-    return l.astype(np.float64)
+    l = l.astype(np.float64)
+    return np.where(np.isnan(l), -np.inf, l)
+
+
+def _best_available(key: np.ndarray, avail: np.ndarray) -> np.ndarray:
+    """Per row, the lowest index among the available entries holding the largest key
+    (-inf keys included: an available -inf entry still beats every unavailable one)."""
+    top = np.where(avail, key, -np.inf).max(axis=1, keepdims=True)
+    return np.argmax(avail & (key == top), axis=1)
 
 
 def topk_select(logits: np.ndarray, k: int) -> np.ndarray:
@@ -138,19 +150,16 @@ def topk_select(logits: np.ndarray, k: int) -> np.ndarray:
     READING: selection is on the logits themselves (softmax and sigmoid are strictly
     increasing, so the chosen set is the same real-number choice), ties go to the
     lower expert index, and the ids are listed best first.
-    Built as k rounds of arg-max (np.argmax returns the first, i.e. lowest, index of
-    a tie), each round removing the chosen expert.
+    Built as k rounds of arg-max, each round removing the chosen expert.
     """
     l = _logit_values(logits)
-    assert np.isfinite(l).all(), "non-finite logits are not supported"
     T, E = l.shape
     assert 1 <= k <= E
     avail = np.ones((T, E), dtype=bool)
     idx = np.empty((T, k), dtype=np.int32)
     rows = np.arange(T)
     for j in range(k):
-        cand = np.where(avail, l, -np.inf)
-        e = np.argmax(cand, axis=1)
+        e = _best_available(l, avail)
         idx[:, j] = e
         avail[rows, e] = False
     return idx
@@ -189,18 +198,21 @@ def topk_probs(logits: np.ndarray, idx: np.ndarray, score: int, exact=False,
     SQRTSOFTPLUS [TE-MoE "Router" score functions; "Token combine": its weights are not
       one either]: q_j = sqrt(log(1 + exp(l_idx_j))). READING: not renormalised, as
       sigmoid.
+    SOFTMAX_PRE [TE-MoE "Router": use_pre_softmax=True applies the softmax before the
+      top-k; "Token combine": pre-softmax top-1 weights are not one]: q_j = p_idx_j, the
+      softmax over all experts, not renormalised over the kept ones.
     scaling_factor [TE-MoE "Router": scaling rescales the returned weights]: multiplied
       into q after the score function (and after the softmax renormalisation).
     """
     l = _logit_values(logits)
     T = l.shape[0]
     sel = np.take_along_axis(l, idx.astype(np.int64), axis=1)
-    if score == SOFTMAX_PRE_RENORM:
+    if score in (SOFTMAX_PRE_RENORM, SOFTMAX_PRE):
         m = l.max(axis=1, keepdims=True)
         p = np.exp(l - m)
         p = p / p.sum(axis=1, keepdims=True)
         ps = np.take_along_axis(p, idx.astype(np.int64), axis=1)
-        q = ps / ps.sum(axis=1, keepdims=True)
+        q = ps / ps.sum(axis=1, keepdims=True) if score == SOFTMAX_PRE_RENORM else ps
     elif score == SOFTMAX_POST:
         m = sel.max(axis=1, keepdims=True)
         z = np.exp(sel - m)
@@ -217,9 +229,9 @@ def selection_keys(logits, score, expert_bias=None):
     """The values the top-k ranks (key) and the values grouped routing sums (gval), as
     float32 numbers (the router's math is fp32 [TE-MoE "Router"]; these values decide
     integers, so both sides take the decision in fp32).
-      softmax (either order): key = the logit (R1: softmax is increasing); gval = the
-        softmax probability over all experts, fp32 (before the top-k) or the logit
-        (after the top-k: the kept logits are the scores the top-k sees).
+      softmax (any order): key = the logit (softmax is increasing); gval = the softmax
+        probability over all experts, fp32 (before the top-k, renormalised or not) or the
+        logit (after the top-k: the kept logits are the scores the top-k sees).
       sigmoid, sqrtsoftplus: s = fp32(score); without a bias key = the logit and
         gval = s; with expert_bias [TE-MoE "Router" expert bias; "Load balancing": added
         to the scores for the selection only] key = gval = fp32(s + bias).
@@ -233,7 +245,7 @@ def selection_keys(logits, score, expert_bias=None):
         return kb, kb
     if expert_bias is not None:
         raise ValueError("expert_bias applies to the sigmoid and sqrtsoftplus scores")
-    if score == SOFTMAX_PRE_RENORM:
+    if score in (SOFTMAX_PRE_RENORM, SOFTMAX_PRE):
         m = l.max(axis=1, keepdims=True)
         p = np.exp(l - m)
         return l, to_f32(p / p.sum(axis=1, keepdims=True))
@@ -274,12 +286,11 @@ def topk_select_ext(logits, k, score, expert_bias=None, num_groups=0, group_topk
             for g in range(num_groups):
                 sel = kept[:, j] == g
                 allowed[sel, g * gs:(g + 1) * gs] = True
-    masked = np.where(allowed, key, -np.inf)
     idx = np.empty((T, k), dtype=np.int32)
     rows = np.arange(T)
     avail = allowed.copy()
     for j in range(k):
-        e = np.argmax(np.where(avail, masked, -np.inf), axis=1)
+        e = _best_available(key, avail)
         idx[:, j] = e
         avail[rows, e] = False
     return idx
@@ -301,6 +312,69 @@ def expert_bias_update(bias, tokens_per_expert, coeff):
     d = coeff * np.sign(c.mean() - c)
     d = d - d.mean()
     return to_f32(np.asarray(bias, np.float32).astype(np.float64) + d)
+
+
+def aux_scores(logits, score, exact=False):
+    """Dense routing scores for the auxiliary load-balancing loss [TE-MoE "Load balancing":
+    fused_compute_score_for_moe_aux_loss returns one score per expert, not only the kept
+    top-k, and ignores expert bias and grouped routing].
+    READING (the pages give no formula): every token's scores form a distribution over
+    the experts, as the router probabilities of the Switch Transformer balance loss (Fedus,
+    Zoph and Shazeer 2021, section 2.2) do: softmax (any order) -> the softmax over all
+    experts; sigmoid and sqrtsoftplus -> the per-expert scores divided by their sum.
+    float64, one rounding to fp32. Returns [T, E]."""
+    l = _logit_values(logits)
+    if score in SOFTMAX_KINDS:
+        z = np.exp(l - l.max(axis=1, keepdims=True))
+    else:
+        z = score_values(l, score)
+    return to_f32(z / z.sum(axis=1, keepdims=True), exact)
+
+
+def aux_loss(scores, tokens_per_expert, total_num_tokens, topk, coeff, exact=False):
+    """Auxiliary load-balancing loss [TE-MoE "Load balancing": fused_moe_aux_loss(scores,
+    tokens_per_expert, total_num_tokens, num_experts, topk, coeff) penalises uneven token
+    counts and has a gradient with respect to every expert's logit].
+    READING: the Switch Transformer balance loss, coeff * E * sum_e f_e P_e, with f_e the
+    fraction of the routed (token, choice) pairs that went to expert e, c_e / (k T), and
+    P_e the mean score of expert e over the tokens, sum_t s_te / T:
+        loss = coeff * E / (k T^2) * sum_e c_e sum_t s_te,
+    T = total_num_tokens, E the number of score columns; k = 1 is the published form.
+    float64 from the fp32 scores and the integer counts, one rounding to fp32."""
+    s = np.asarray(scores, dtype=np.float64)
+    c = np.asarray(tokens_per_expert, dtype=np.float64)
+    E = s.shape[1]
+    T = float(total_num_tokens)
+    val = coeff * E / (topk * T * T) * float((c * s.sum(axis=0)).sum())
+    return float(to_f32(val, exact))
+
+
+def aux_loss_backward(logits, tokens_per_expert, total_num_tokens, topk, coeff, score,
+                      d_loss=1.0, exact=False):
+    """Gradient of aux_loss(aux_scores(logits)) with respect to the logits, for an upstream
+    gradient d_loss. With C = d_loss * coeff * E / (k T^2), the loss gradient with respect to
+    s_te is g_e = C c_e for every token, then through the normalised scores:
+      softmax: dl_te = s_te (g_e - sum_i s_ti g_i);
+      sigmoid / sqrtsoftplus, s_te = r_te / sum_i r_ti:
+        dl_te = r'(l_te) (g_e - sum_i s_ti g_i) / sum_i r_ti,
+        r' = r (1 - r) (sigmoid) or sigmoid(l) / (2 r) (sqrtsoftplus).
+    float64, one rounding to fp32. Returns [T, E]."""
+    l = _logit_values(logits)
+    T_, E = l.shape
+    c = np.asarray(tokens_per_expert, dtype=np.float64)
+    T = float(total_num_tokens)
+    g = d_loss * coeff * E / (topk * T * T) * c[None, :]
+    if score in SOFTMAX_KINDS:
+        z = np.exp(l - l.max(axis=1, keepdims=True))
+        s = z / z.sum(axis=1, keepdims=True)
+        dl = s * (g - (s * g).sum(axis=1, keepdims=True))
+    else:
+        r = score_values(l, score)
+        tot = r.sum(axis=1, keepdims=True)
+        s = r / tot
+        dr = r * (1.0 - r) if score == SIGMOID else (1.0 / (1.0 + np.exp(-l))) / (2.0 * r)
+        dl = dr * (g - (s * g).sum(axis=1, keepdims=True)) / tot
+    return to_f32(dl, exact)
 
 
 def router_topk(logits: np.ndarray, k: int, score: int, exact=False, expert_bias=None,
@@ -347,13 +421,16 @@ def router_backward(logits, idx, d_prob, score, exact=False, scaling_factor=1.0)
     """Gradient of the routing weights with respect to the logits [TE-MoE "Router": the
     score function and the top-k run in one differentiable kernel with fp32 math].
 
-    The top-k choice is piecewise constant, so only the kept logits' influence through
-    the score function carries a gradient. Each score function is differentiated as
-    it is defined in topk_probs, in float64, then rounded once to fp32:
+    The top-k choice is piecewise constant, so only the weights' dependence on the logits
+    through the score function carries a gradient. Each score function is differentiated
+    as it is defined in topk_probs, in float64, then rounded once to fp32:
       SOFTMAX_PRE_RENORM: p = softmax(l) over all experts, s = sum of the kept p,
         q_j = p_idx_j / s. Through the renormalisation dp_i = (dq_i - sum_j q_j dq_j)/s
         for a kept expert i (0 for the others), then through the softmax
         dl_e = p_e (dp_e - sum_i p_i dp_i) for every expert e.
+      SOFTMAX_PRE: q_j = p_idx_j with p = softmax(l) over all experts; dp = dq at the
+        kept experts (0 elsewhere), dl_e = p_e (dp_e - sum_i p_i dp_i) for every expert e
+        (the experts not kept get -p_e sum_j q_j dq_j).
       SOFTMAX_POST: q = softmax of the kept logits, dl_idx_j = q_j (dq_j - sum q dq);
         0 elsewhere.
       SIGMOID: q_j = sigmoid(l_idx_j), dl_idx_j = dq_j q_j (1 - q_j); 0 elsewhere.
@@ -378,6 +455,13 @@ def router_backward(logits, idx, d_prob, score, exact=False, scaling_factor=1.0)
         q = ps / s_
         dp = np.zeros((T, E), dtype=np.float64)
         dp[rows, ii] = (dq - (q * dq).sum(axis=1, keepdims=True)) / s_
+        dl = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    elif score == SOFTMAX_PRE:
+        m = l.max(axis=1, keepdims=True)
+        p = np.exp(l - m)
+        p = p / p.sum(axis=1, keepdims=True)
+        dp = np.zeros((T, E), dtype=np.float64)
+        dp[rows, ii] = dq
         dl = p * (dp - (p * dp).sum(axis=1, keepdims=True))
     elif score == SOFTMAX_POST:
         z = np.exp(sel - sel.max(axis=1, keepdims=True))
