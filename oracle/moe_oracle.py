@@ -764,7 +764,8 @@ def expert_mlp_mx_backward(mlp, xp_vals, d_out, w_gu_vals, w_down_vals, offsets,
     return dict(dh=dh, dgu=dgu, dxp=dxp, dw_down=dw_down, dw_gu=dw_gu)
 
 
-def expert_mlp(xp_vals, w_gu_vals, w_down_vals, offsets, I, exact=False, fp8=False):
+def expert_mlp(xp_vals, w_gu_vals, w_down_vals, offsets, I, exact=False, fp8=False,
+               row_scale=None):
     """Grouped expert SwiGLU MLP on expert-contiguous rows.
 
     [TE-MIX __init__ / _expert_ffn]: fused gate/up weight with 2I outputs split in
@@ -774,6 +775,9 @@ def expert_mlp(xp_vals, w_gu_vals, w_down_vals, offsets, I, exact=False, fp8=Fal
     intermediate h.
     fp8 [TE-MoE "Grouped GEMM" low precision; AO-2600 fp8dq]: x rows quantised per
     row, weights per output column; h is re-quantised per row from its bf16 value.
+    row_scale [N] (ScaledSwiGLU, [TE-MoE "Grouped MLP"]: the activation output is
+    multiplied by the routing weight of its row before FC2): h = bf16(silu(g) u p_r),
+    READING: the product taken on the fp32 g, u with one rounding, as the unscaled h.
     Returns dict with g, u (fp32 values), h (bf16 values), out (bf16 values).
     """
     if fp8:
@@ -782,7 +786,10 @@ def expert_mlp(xp_vals, w_gu_vals, w_down_vals, offsets, I, exact=False, fp8=Fal
     else:
         gu = grouped_gemm(xp_vals, w_gu_vals, offsets, exact)
     g, u = gu[:, :I], gu[:, I:]
-    h = swiglu_from_gu(g, u, exact)
+    if row_scale is None:
+        h = swiglu_from_gu(g, u, exact)
+    else:
+        h = to_bf16(silu(g) * u * np.asarray(row_scale, np.float64)[:, None], exact)
     if fp8:
         qh, sh = quantize_rows_e4m3(h)
         out = grouped_gemm(e4m3_decode(qh), w_down_vals, offsets, exact, sh, quantize_b=True)
@@ -850,7 +857,15 @@ def prob_grad(dy_vals, out_vals, row_of, exact=False, rows_first=False):
 # ---------------------------------------------------------------------------
 
 
-PLACE_COMBINE, PLACE_INPUT = 0, 1
+PLACE_COMBINE, PLACE_INPUT, PLACE_ACTIVATION = 0, 1, 2
+
+
+def row_weights(q, row_of, n_rows):
+    """The routing weight of every routed row: w[row_of[t, j]] = q[t, j]."""
+    w = np.zeros(n_rows)
+    for j in range(row_of.shape[1]):
+        w[np.asarray(row_of[:, j], np.int64)] = np.asarray(q, np.float64)[:, j]
+    return w
 
 
 def moe_forward(x_bits, logits, w_gu_bits, w_down_bits, k, score, I,
@@ -863,6 +878,10 @@ def moe_forward(x_bits, logits, w_gu_bits, w_down_bits, k, score, I,
     the outputs [TT-1269 MoE.forward, scoring_before_experts: the routed rows are
     multiplied by their scores in fp32 and cast back to the activation type, and the
     outputs are summed unweighted]: xp[r] = bf16(q[t,j] * x[t]), y = sum_j out[row_of].
+    placement PLACE_ACTIVATION applies them to the SwiGLU output before FC2 [TE-MoE
+    "Grouped MLP": ScaledSwiGLU; with a bias-free FC2 the expert output is then already
+    weighted and the combine must not weight it again]: h = bf16(silu(g) u q), y = sum_j
+    out[row_of].
     Returns a dict of every intermediate."""
     x = as_values(x_bits)
     E = logits.shape[1]
@@ -874,13 +893,14 @@ def moe_forward(x_bits, logits, w_gu_bits, w_down_bits, k, score, I,
         for j in range(k):
             qr[row_of[:, j].astype(np.int64)] = q[:, j]
         xp = to_bf16(xp * qr[:, None], exact)
+    rscale = row_weights(q, row_of, len(src_of)) if placement == PLACE_ACTIVATION else None
     mlp = (expert_mlp_mx(xp, w_gu_bits, w_down_bits, offsets, I, exact) if mx else
-           expert_mlp(xp, w_gu_bits, w_down_bits, offsets, I, exact, fp8))
+           expert_mlp(xp, w_gu_bits, w_down_bits, offsets, I, exact, fp8, rscale))
     shared = None
     if shared_gu_bits is not None:
         Is = shared_down_bits.shape[0]
         shared = dense_mlp(x, shared_gu_bits, shared_down_bits, Is, exact)
-    y = combine(mlp["out"], row_of, None if placement == PLACE_INPUT else q, shared, exact)
+    y = combine(mlp["out"], row_of, q if placement == PLACE_COMBINE else None, shared, exact)
     res = dict(topk_idx=idx, topk_prob=q, counts=counts, routing_map=rmap, probs_dense=dense,
                offsets=offsets, row_of=row_of, src_of=src_of, xp=xp, shared=shared, y=y,
                x=x, logits=logits, score=score, placement=placement)
@@ -935,6 +955,11 @@ def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False, w_router_
       dx[t] = bf16(sum_j dxp[row_of[t,j]])                      (dispatch backward)
     mx: the four expert GEMMs in the MXFP8 recipe (``expert_mlp_mx_backward``; the forward
     ran with mx too).
+    Weights on the SwiGLU output (PLACE_ACTIVATION, ScaledSwiGLU): the combine was
+    unweighted, so d_out[row_of[t,j]] = dy[t]; dh = fp32(d_out W_down^T) is the gradient
+    of the scaled h, the SwiGLU backward takes p dh, and
+      d_prob[t, j] = sum_i dh[r, i] silu(g[r, i]) u[r, i],  r = row_of[t, j]
+    (fp32, from the saved bf16 g, u); dx = bf16(sum_j dxp[row_of[t,j]] (+ router term)).
     """
     dy = as_values(dy_bits)
     row_of, q, offsets = fwd["row_of"], fwd["topk_prob"], fwd["offsets"]
@@ -946,8 +971,8 @@ def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False, w_router_
     w_d = np.asarray(w_down_bits)
     d_out = np.zeros((N, H), dtype=np.float64)
     for j in range(k):
-        d_out[row_of[:, j].astype(np.int64)] = (dy if place == PLACE_INPUT else
-                                                to_bf16(dy * q[:, j:j + 1], exact))
+        d_out[row_of[:, j].astype(np.int64)] = (to_bf16(dy * q[:, j:j + 1], exact)
+                                                if place == PLACE_COMBINE else dy)
     if mx:
         m = expert_mlp_mx_backward(fwd, fwd["xp"], d_out, w_gu, w_d, offsets, I, exact)
         dh, dgu, dxp, dw_gu, dw_down = m["dh"], m["dgu"], m["dxp"], m["dw_gu"], m["dw_down"]
@@ -955,7 +980,11 @@ def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False, w_router_
         # GEMM2 backward: dh = d_out W_d^T (per expert), then the SwiGLU backward
         dh = grouped_gemm(d_out, np.swapaxes(w_d, 1, 2), offsets, exact)
         g_saved, u_saved = to_bf16(fwd["g"], exact), to_bf16(fwd["u"], exact)
-        dg, du = swiglu_backward(dh, g_saved, u_saved, exact)
+        if place == PLACE_ACTIVATION:
+            rw = row_weights(q, row_of, N)
+            dg, du = swiglu_backward(dh * rw[:, None], g_saved, u_saved, exact)
+        else:
+            dg, du = swiglu_backward(dh, g_saved, u_saved, exact)
         dgu = np.concatenate([dg, du], axis=1)
         dw_down = grouped_gemm_dw(fwd["h"], d_out, offsets, exact, out_bf16=True)
         # GEMM1 backward
@@ -965,8 +994,15 @@ def moe_backward(fwd, dy_bits, w_gu_bits, w_down_bits, I, exact=False, w_router_
     dx_router = None
     if w_router_bits is not None:
         # the weights met the expert outputs (combine) or the expert inputs (input)
-        d_prob = (prob_grad(dxp, fwd["x"], row_of, exact, rows_first=True)
-                  if place == PLACE_INPUT else prob_grad(dy, fwd["out"], row_of, exact))
+        if place == PLACE_INPUT:
+            d_prob = prob_grad(dxp, fwd["x"], row_of, exact, rows_first=True)
+        elif place == PLACE_ACTIVATION:
+            hu = silu(to_bf16(fwd["g"], exact)) * to_bf16(fwd["u"], exact)
+            per_row = (dh * hu).sum(axis=1)
+            d_prob = to_f32(np.stack([per_row[np.asarray(row_of[:, j], np.int64)]
+                                      for j in range(k)], axis=1), exact)
+        else:
+            d_prob = prob_grad(dy, fwd["out"], row_of, exact)
         d_logits = router_backward(fwd["logits"], fwd["topk_idx"], d_prob, fwd["score"], exact,
                                    fwd.get("scaling_factor", 1.0))
         dx_router = d_logits @ as_values(w_router_bits)

@@ -97,7 +97,10 @@ def _margin(logits, k):
                                                (O.SIGMOID, 2, O.PLACE_COMBINE),
                                                (O.SQRTSOFTPLUS, 2, O.PLACE_COMBINE),
                                                (O.SOFTMAX_PRE_RENORM, 3, O.PLACE_INPUT),
-                                               (O.SIGMOID, 1, O.PLACE_INPUT)])
+                                               (O.SIGMOID, 1, O.PLACE_INPUT),
+                                               (O.SOFTMAX_PRE_RENORM, 3, O.PLACE_ACTIVATION),
+                                               (O.SIGMOID, 1, O.PLACE_ACTIVATION),
+                                               (O.SOFTMAX_PRE, 2, O.PLACE_ACTIVATION)])
 def test_layer_gradients_through_router_match_finite_differences(score, k, placement):
     T, H, E, I = 6, 16, 7, 8
     rng = np.random.default_rng(30 + score)
@@ -132,6 +135,7 @@ def test_layer_gradients_through_router_match_finite_differences(score, k, place
     check("w_router", w_r, g["dw_router"], lambda: _layer(x, w_r, wgu, wd, dy, k, score, I, None, P)[0])
     check("x", x, g["dx"], lambda: _layer(x, w_r, wgu, wd, dy, k, score, I, None, P)[0])
     check("w_gu", wgu, g["dw_gu"], lambda: _layer(x, w_r, wgu, wd, dy, k, score, I, None, P)[0])
+    check("w_down", wd, g["dw_down"], lambda: _layer(x, w_r, wgu, wd, dy, k, score, I, None, P)[0])
 
 
 def test_backward_without_router_weight_is_unchanged():
@@ -164,3 +168,44 @@ def test_input_placement_equals_combine_placement_for_unit_weights():
     b = O.moe_forward(x, lg, wgu, wd, 1, O.SOFTMAX_POST, I, placement=O.PLACE_INPUT)
     assert (a["topk_prob"] == 1.0).all()
     assert np.array_equal(a["y"], b["y"])
+
+
+def test_activation_placement_equals_combine_placement():
+    # ScaledSwiGLU with a bias-free FC2: (p h) W = p (h W), so in exact arithmetic the
+    # weights on the SwiGLU output give the layer of weights in the combine; with unit
+    # weights (top-1, softmax after the top-k) the rounded layers are bit-identical too,
+    # forward and backward
+    rng = np.random.default_rng(51)
+    T, H, E, I, k = 10, 16, 5, 8, 3
+    x = rng.standard_normal((T, H))
+    lg = rng.standard_normal((T, E))
+    wgu = rng.standard_normal((E, H, 2 * I)) * 0.5
+    wd = rng.standard_normal((E, I, H)) * 0.5
+    dy = rng.standard_normal((T, H))
+    a = O.moe_forward(x, lg, wgu, wd, k, O.SOFTMAX_PRE_RENORM, I, exact=True)
+    b = O.moe_forward(x, lg, wgu, wd, k, O.SOFTMAX_PRE_RENORM, I, exact=True,
+                      placement=O.PLACE_ACTIVATION)
+    assert np.allclose(a["y"], b["y"], rtol=1e-12, atol=1e-14)
+    # the expert outputs differ by exactly the weight factor
+    rw = O.row_weights(a["topk_prob"], a["row_of"], T * k)
+    assert np.allclose(b["out"], a["out"] * rw[:, None], rtol=1e-12, atol=1e-14)
+    ga = O.moe_backward(a, dy, wgu, wd, I, exact=True)
+    gb = O.moe_backward(b, dy, wgu, wd, I, exact=True)
+    for key in ("dx", "dw_gu"):
+        assert np.allclose(ga[key], gb[key], rtol=1e-10, atol=1e-12), key
+    # dW_down differs: it pairs the scaled h with the unweighted d_out, which is the same
+    # product in exact arithmetic
+    assert np.allclose(ga["dw_down"], gb["dw_down"], rtol=1e-10, atol=1e-12)
+    xb = O.f32_to_bf16_bits(x.astype(np.float32))
+    lg32 = lg.astype(np.float32)
+    wgub = O.f32_to_bf16_bits((wgu * 0.2).astype(np.float32))
+    wdb = O.f32_to_bf16_bits((wd * 0.2).astype(np.float32))
+    dyb = O.f32_to_bf16_bits(dy.astype(np.float32))
+    a = O.moe_forward(xb, lg32, wgub, wdb, 1, O.SOFTMAX_POST, I)
+    b = O.moe_forward(xb, lg32, wgub, wdb, 1, O.SOFTMAX_POST, I, placement=O.PLACE_ACTIVATION)
+    assert (a["topk_prob"] == 1.0).all()
+    assert np.array_equal(a["h"], b["h"]) and np.array_equal(a["y"], b["y"])
+    ga = O.moe_backward(a, dyb, wgub, wdb, I)
+    gb = O.moe_backward(b, dyb, wgub, wdb, I)
+    for key in ("dx", "dw_gu", "dw_down", "dgu"):
+        assert np.array_equal(ga[key], gb[key]), key
