@@ -64,13 +64,19 @@ typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3 = 1, MOE_FP32 = 2, MOE_MXFP8 = 3 } moe
  * MOE_SIGMOID: sigmoid of each kept logit, not renormalised (guide, "Token
  *   combine": sigmoid top-1 weights are not one and must be applied).
  * MOE_SQRTSOFTPLUS: sqrt(log(1 + e^l)) of each kept logit, not renormalised.
+ * MOE_SOFTMAX_PRE: softmax over all experts, the kept experts' probabilities as they are,
+ *   not renormalised (guide, use_pre_softmax=True; "Token combine": pre-softmax top-1
+ *   weights are not one).
  * Selection is on the logits, descending, ties to the lower expert index (with an
- * expert bias: on fp32(score + bias); see moe_router_opts_t). */
+ * expert bias: on fp32(score + bias); see moe_router_opts_t). A NaN logit counts as -inf;
+ * an expert at -inf is still taken when too few others are left (lowest id first), so
+ * the ids are always k distinct experts of [0, E). */
 typedef enum {
   MOE_SOFTMAX_PRE_RENORM = 0,
   MOE_SOFTMAX_POST = 1,
   MOE_SIGMOID = 2,
-  MOE_SQRTSOFTPLUS = 3
+  MOE_SQRTSOFTPLUS = 3,
+  MOE_SOFTMAX_PRE = 4
 } moe_score_t;
 
 /* Layouts of the grouped GEMM (guide, "Grouped GEMM": Y_i = X_i W_i per expert
@@ -102,9 +108,10 @@ moe_status_t moe_router_topk(const float* logits, int T, int E, int k, int score
  *  num_groups    0 or 1: no grouped routing. Else the experts form num_groups equal
  *                groups of consecutive ids (E % num_groups == 0, num_groups <= 64); a
  *                group's score is the fp32 sum, best first, of the values of its
- *                m = k / group_topk best experts (softmax before the top-k: the fp32
- *                probabilities; after it: the logits; sigmoid / sqrtsoftplus: the fp32
- *                scores, plus the bias when given); the group_topk best groups are kept
+ *                m = k / group_topk best experts (softmax before the top-k, either
+ *                form: the fp32 probabilities; after it: the logits; sigmoid /
+ *                sqrtsoftplus: the fp32 scores, plus the bias when given); the
+ *                group_topk best groups are kept
  *                and the top-k is taken among their experts (ties to the lower id).
  *  group_topk    groups kept: 1 <= group_topk <= num_groups, k >= group_topk,
  *                k <= group_topk * (E / num_groups).
@@ -134,6 +141,43 @@ moe_status_t moe_router_topk_ex(const float* logits, int T, int E, int k, int sc
  * (integer comparison); the update is computed in fp64 and rounded once. E <= 256. */
 moe_status_t moe_expert_bias_update(float* expert_bias, const int32_t* tokens_per_expert,
                                     int E, float coeff, void* stream);
+
+/* ---- auxiliary load-balancing loss (guide, "Load balancing") --------------------------
+ * The loss is the Switch Transformer balance loss (Fedus, Zoph and Shazeer 2021, section
+ * 2.2) for top-k routing: coeff * E * sum_e f_e P_e, f_e = c_e / (k T) the fraction of the
+ * routed (token, choice) pairs sent to expert e, P_e = sum_t s_te / T the mean dense score:
+ *   loss = coeff * E / (k T^2) * sum_e c_e sum_t s_te,  T = total_num_tokens. */
+
+/* Dense scores for the loss (guide: fused_compute_score_for_moe_aux_loss; no expert bias, no
+ * grouped routing). logits [T,E] float32 in (a NaN counts as -inf); scores [T,E] float32
+ * out, a distribution over the experts per token: the softmax over all experts (any
+ * softmax score function), or the sigmoid / sqrtsoftplus scores divided by their sum.
+ * routing_map [T,E] uint8 out, nullable: the plain top-k of the logits (as moe_router_topk),
+ * which can differ from the real router's when that one uses a bias or groups. */
+moe_status_t moe_aux_loss_scores(const float* logits, int T, int E, int k, int score,
+                                 float* scores, uint8_t* routing_map, void* stream);
+
+/* Scratch bytes moe_aux_loss needs for (T, E). */
+size_t moe_aux_loss_workspace_bytes(int T, int E);
+
+/* The loss (guide: fused_moe_aux_loss). scores [T,E] float32 (moe_aux_loss_scores),
+ * tokens_per_expert [E] int32 (the real router's counts), total_num_tokens > 0, coeff the
+ * loss weight. loss [1] float32 device out. fp32 column sums over fixed token chunks,
+ * added in a fixed order (deterministic). ws: moe_aux_loss_workspace_bytes(T, E). */
+moe_status_t moe_aux_loss(const float* scores, const int32_t* tokens_per_expert, int T, int E,
+                          int k, int total_num_tokens, float coeff, float* loss, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Gradient of the loss with respect to every logit, for an upstream gradient d_loss [1]
+ * float32 device (NULL: 1). With C = d_loss coeff E / (k T^2), g_e = C c_e and
+ * D = sum_i s_i g_i: softmax d_logits[t,e] = s_e (g_e - D); sigmoid / sqrtsoftplus, with r
+ * the unnormalised scores, r'(l_e) (g_e - D) / sum_i r_i (r' = r (1 - r), or
+ * sigmoid(l) / (2 r)). accumulate = 1 adds to d_logits (e.g. the router backward's), 0
+ * overwrites it. */
+moe_status_t moe_aux_loss_backward(const float* logits, const int32_t* tokens_per_expert, int T,
+                                   int E, int k, int total_num_tokens, float coeff, int score,
+                                   const float* d_loss, float* d_logits, int accumulate,
+                                   void* stream);
 
 /* Scratch bytes moe_permute needs for (T, E, k). */
 size_t moe_permute_workspace_bytes(int T, int E, int k);
@@ -250,19 +294,21 @@ moe_status_t moe_router_logits(const void* x, const void* w_router, int T, int H
  * top-k are differentiable with fp32 math).
  *  dy [T,H] bf16, expert_out [T*k,H] bf16 (the forward's expert outputs before
  *  weighting), row_of [T,k], topk_idx [T,k], topk_prob [T,k] float32, score as in
- *  the forward.
+ *  the forward. logits [T,E] float32: read for MOE_SOFTMAX_PRE only (else may be NULL).
  *  d_out [T*k,H] bf16 out: d_out[row_of[t,j]] = bf16(p[t,j] * dy[t]).
  *  d_prob [T,k] float32 out, nullable: <dy[t], expert_out[row_of[t,j]]> (fp32 sum).
  *  d_logits [T,E] float32 out: with p = c s (c = scaling_factor, 0 taken as 1; s the
- *  score-function output), at the kept experts softmax (either order: the same function
- *  of the kept logits) c s_j (d_prob_j - sum_i s_i d_prob_i), sigmoid
- *  c d_prob_j s_j (1 - s_j), sqrtsoftplus c d_prob_j sigmoid(l_j) / (2 s_j); 0 at the
- *  other experts (the top-k choice is piecewise constant). */
+ *  score-function output), at the kept experts softmax (every form) c s_j (d_prob_j -
+ *  sum_i s_i d_prob_i), sigmoid c d_prob_j s_j (1 - s_j), sqrtsoftplus
+ *  c d_prob_j sigmoid(l_j) / (2 s_j). At the other experts 0 (the top-k choice is
+ *  piecewise constant), except for MOE_SOFTMAX_PRE, whose weights are probabilities of
+ *  a softmax over every expert: -c p_e sum_i s_i d_prob_i, p_e the softmax of logits. */
 moe_status_t moe_combine_backward_router(const void* dy, const void* expert_out,
                                          const int32_t* row_of, const int32_t* topk_idx,
-                                         const float* topk_prob, int T, int H, int E, int k,
-                                         int score, float scaling_factor, void* d_out,
-                                         float* d_prob, float* d_logits, void* stream);
+                                         const float* topk_prob, const float* logits, int T,
+                                         int H, int E, int k, int score, float scaling_factor,
+                                         void* d_out, float* d_prob, float* d_logits,
+                                         void* stream);
 
 /* Scratch bytes moe_router_weight_grad needs for (T, H, E). */
 size_t moe_router_weight_grad_workspace_bytes(int T, int H, int E);
@@ -276,8 +322,10 @@ moe_status_t moe_router_weight_grad(const void* x, const float* d_logits, int T,
                                     float* dw_router, void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatch backward of a layer that owns its router projection: dx[t] =
- * bf16(sum_j dxp[row_of[t,j]] + sum_j d_logits[t,e_j] w_router[e_j]), e_j = topk_idx[t,j],
- * summed in fp32 with one rounding (d_logits is 0 off the kept experts). */
+ * bf16(sum_j dxp[row_of[t,j]] + sum_e d_logits[t,e] w_router[e]), summed in fp32 with one
+ * rounding; the router's term runs over the experts whose d_logits is nonzero, in
+ * ascending id (the kept ones, topk_idx, for every score function but MOE_SOFTMAX_PRE,
+ * whose d_logits reaches every expert). topk_idx is checked but not read. */
 moe_status_t moe_dispatch_backward_router(const void* dxp, const int32_t* row_of,
                                           const int32_t* topk_idx, const float* d_logits,
                                           const void* w_router, int T, int H, int E, int k,
@@ -287,18 +335,19 @@ moe_status_t moe_dispatch_backward_router(const void* dxp, const int32_t* row_of
  * owns its router projection (torchtitan pull request 1269, MoE.forward,
  * scoring_before_experts; the weighted dispatch itself is moe_combine_backward applied to
  * x, and without the router the dispatch backward is moe_unpermute_combine with the
- * weights). dxp [T*k,H] bf16, x [T,H] bf16, row_of, topk_idx, topk_prob [T,k], w_router
- * [E,H] bf16, score / scaling_factor as in the forward.
+ * weights). dxp [T*k,H] bf16, x [T,H] bf16, row_of, topk_idx, topk_prob [T,k], logits
+ * [T,E] float32 (read for MOE_SOFTMAX_PRE only), w_router [E,H] bf16, score /
+ * scaling_factor as in the forward.
  *  d_logits [T,E] float32 out: the score-function backward (see
  *  moe_combine_backward_router) of d_prob_j = <dxp[row_of[t,j]], x[t]>.
- *  dx [T,H] bf16 out: bf16(sum_j p_j dxp[row_of[t,j]] + sum_j d_logits[t,e_j] w_router[e_j]),
+ *  dx [T,H] bf16 out: bf16(sum_j p_j dxp[row_of[t,j]] + sum_e d_logits[t,e] w_router[e]),
  *  fp32 sum with one rounding. */
 moe_status_t moe_dispatch_backward_router_input(const void* dxp, const void* x,
                                                 const int32_t* row_of, const int32_t* topk_idx,
-                                                const float* topk_prob, const void* w_router,
-                                                int T, int H, int E, int k, int score,
-                                                float scaling_factor, void* dx, float* d_logits,
-                                                void* stream);
+                                                const float* topk_prob, const float* logits,
+                                                const void* w_router, int T, int H, int E, int k,
+                                                int score, float scaling_factor, void* dx,
+                                                float* d_logits, void* stream);
 
 /* ---- MXFP8 (te_mixtral.py's mxfp8 recipe) ------------------------------------------
  * e4m3 codes with one power-of-two scale per block of 32 consecutive values along K,

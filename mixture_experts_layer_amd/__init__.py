@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_amd.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_BF16, MOE_FP8_E4M3, MOE_FP32, MOE_MXFP8 = 0, 1, 2, 3
-MOE_SOFTMAX_PRE_RENORM, MOE_SOFTMAX_POST, MOE_SIGMOID, MOE_SQRTSOFTPLUS = 0, 1, 2, 3
+MOE_SOFTMAX_PRE_RENORM, MOE_SOFTMAX_POST, MOE_SIGMOID, MOE_SQRTSOFTPLUS, MOE_SOFTMAX_PRE = range(5)
 MOE_GEMM_NN, MOE_GEMM_NT, MOE_GEMM_TN_DW = 0, 1, 2
 MOE_PLACE_COMBINE, MOE_PLACE_INPUT = 0, 1
 
@@ -34,6 +34,8 @@ EXPORTS = [
     "moe_quantize_mxfp8_rows", "moe_quantize_mxfp8_weights", "moe_grouped_gemm_mxfp8",
     "moe_mxfp8_cols_capacity", "moe_mxfp8_col_offsets", "moe_quantize_mxfp8_cols",
     "moe_grouped_gemm_mxfp8_wgrad", "moe_grouped_gemm_mxfp8_swiglu_bwd",
+    "moe_aux_loss_scores", "moe_aux_loss_workspace_bytes", "moe_aux_loss",
+    "moe_aux_loss_backward",
 ]
 
 
@@ -105,12 +107,12 @@ def _load():
         "moe_backward": ([ctypes.POINTER(Problem), ctypes.POINTER(Tensors), vp, vp, vp, vp, vp,
                           sz, vp], i),
         "moe_router_logits": ([vp, vp, i, i, i, vp, vp], i),
-        "moe_combine_backward_router": ([vp, vp, vp, vp, vp, i, i, i, i, i, ctypes.c_float, vp, vp,
-                                         vp, vp], i),
+        "moe_combine_backward_router": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, ctypes.c_float, vp,
+                                         vp, vp, vp], i),
         "moe_router_topk_ex": ([vp, i, i, i, i, ctypes.POINTER(RouterOpts), vp, vp, vp, vp, vp, vp], i),
         "moe_expert_bias_update": ([vp, vp, i, ctypes.c_float, vp], i),
-        "moe_dispatch_backward_router_input": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, ctypes.c_float,
-                                                vp, vp, vp], i),
+        "moe_dispatch_backward_router_input": ([vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
+                                                ctypes.c_float, vp, vp, vp], i),
         "moe_padded_rows": ([i, i, i, i], sz),
         "moe_quantize_mxfp8_rows": ([vp, i, i, vp, vp, vp], i),
         "moe_quantize_mxfp8_weights": ([vp, i, i, i, vp, vp, vp], i),
@@ -124,6 +126,10 @@ def _load():
         "moe_router_weight_grad_workspace_bytes": ([i, i, i], sz),
         "moe_router_weight_grad": ([vp, vp, i, i, i, vp, vp, sz, vp], i),
         "moe_dispatch_backward_router": ([vp, vp, vp, vp, vp, i, i, i, i, vp, vp], i),
+        "moe_aux_loss_scores": ([vp, i, i, i, i, vp, vp, vp], i),
+        "moe_aux_loss_workspace_bytes": ([i, i], sz),
+        "moe_aux_loss": ([vp, vp, i, i, i, i, ctypes.c_float, vp, vp, sz, vp], i),
+        "moe_aux_loss_backward": ([vp, vp, i, i, i, i, ctypes.c_float, i, vp, vp, i, vp], i),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -176,7 +182,8 @@ def _want_rows(t, dtype, min_rows, cols, name):
 
 
 _SCORE = {"softmax_pre_renorm": MOE_SOFTMAX_PRE_RENORM, "softmax_post": MOE_SOFTMAX_POST,
-          "sigmoid": MOE_SIGMOID, "sqrtsoftplus": MOE_SQRTSOFTPLUS}
+          "sigmoid": MOE_SIGMOID, "sqrtsoftplus": MOE_SQRTSOFTPLUS,
+          "softmax_pre": MOE_SOFTMAX_PRE}
 
 
 def _score(s):
@@ -464,7 +471,8 @@ def moe_router_logits(x, w_router, logits, stream=None):
 
 
 def moe_combine_backward_router(dy, expert_out, row_of, topk_idx, topk_prob, score, d_out,
-                                d_logits, d_prob=None, scaling_factor=1.0, stream=None):
+                                d_logits, d_prob=None, scaling_factor=1.0, logits=None,
+                                stream=None):
     T, k = row_of.shape
     H = dy.shape[1]
     E = d_logits.shape[1]
@@ -476,8 +484,10 @@ def moe_combine_backward_router(dy, expert_out, row_of, topk_idx, topk_prob, sco
     _want(d_logits, torch.float32, (T, E), "d_logits")
     if d_prob is not None:
         _want(d_prob, torch.float32, (T, k), "d_prob")
+    if logits is not None:
+        _want(logits, torch.float32, (T, E), "logits")
     _check("moe_combine_backward_router", _lib.moe_combine_backward_router(
-        _p(dy), _p(expert_out), _p(row_of), _p(topk_idx), _p(topk_prob), T, H, E, k,
+        _p(dy), _p(expert_out), _p(row_of), _p(topk_idx), _p(topk_prob), _p(logits), T, H, E, k,
         _score(score), float(scaling_factor), _p(d_out), _p(d_prob), _p(d_logits),
         _stream(stream)))
 
@@ -510,7 +520,7 @@ def moe_dispatch_backward_router(dxp, row_of, topk_idx, d_logits, w_router, dx, 
 
 
 def moe_dispatch_backward_router_input(dxp, x, row_of, topk_idx, topk_prob, w_router, score, dx,
-                                       d_logits, scaling_factor=1.0, stream=None):
+                                       d_logits, scaling_factor=1.0, logits=None, stream=None):
     T, k = row_of.shape
     E, H = w_router.shape
     _want_rows(dxp, torch.bfloat16, T * k, H, "dxp")
@@ -518,9 +528,51 @@ def moe_dispatch_backward_router_input(dxp, x, row_of, topk_idx, topk_prob, w_ro
     _want(topk_prob, torch.float32, (T, k), "topk_prob")
     _want(dx, torch.bfloat16, (T, H), "dx")
     _want(d_logits, torch.float32, (T, E), "d_logits")
+    if logits is not None:
+        _want(logits, torch.float32, (T, E), "logits")
     _check("moe_dispatch_backward_router_input", _lib.moe_dispatch_backward_router_input(
-        _p(dxp), _p(x), _p(row_of), _p(topk_idx), _p(topk_prob), _p(w_router), T, H, E, k,
+        _p(dxp), _p(x), _p(row_of), _p(topk_idx), _p(topk_prob), _p(logits), _p(w_router), T, H,
+        E, k,
         _score(score), float(scaling_factor), _p(dx), _p(d_logits), _stream(stream)))
+
+
+# ---- auxiliary load-balancing loss ----------------------------------------------------------
+
+def moe_aux_loss_scores(logits, k, score, scores, routing_map=None, stream=None):
+    T, E = logits.shape
+    _want(logits, torch.float32, (T, E), "logits")
+    _want(scores, torch.float32, (T, E), "scores")
+    if routing_map is not None:
+        _want(routing_map, torch.uint8, (T, E), "routing_map")
+    _check("moe_aux_loss_scores", _lib.moe_aux_loss_scores(
+        _p(logits), T, E, k, _score(score), _p(scores), _p(routing_map), _stream(stream)))
+
+
+def moe_aux_loss_workspace_bytes(T, E):
+    return int(_lib.moe_aux_loss_workspace_bytes(T, E))
+
+
+def moe_aux_loss(scores, tokens_per_expert, k, total_num_tokens, coeff, loss, ws, stream=None):
+    T, E = scores.shape
+    _want(scores, torch.float32, (T, E), "scores")
+    _want(tokens_per_expert, torch.int32, (E,), "tokens_per_expert")
+    _want(loss, torch.float32, (1,), "loss")
+    _check("moe_aux_loss", _lib.moe_aux_loss(
+        _p(scores) if T else None, _p(tokens_per_expert), T, E, k, int(total_num_tokens),
+        float(coeff), _p(loss), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_aux_loss_backward(logits, tokens_per_expert, k, total_num_tokens, coeff, score, d_logits,
+                          d_loss=None, accumulate=False, stream=None):
+    T, E = logits.shape
+    _want(logits, torch.float32, (T, E), "logits")
+    _want(tokens_per_expert, torch.int32, (E,), "tokens_per_expert")
+    _want(d_logits, torch.float32, (T, E), "d_logits")
+    if d_loss is not None:
+        _want(d_loss, torch.float32, (1,), "d_loss")
+    _check("moe_aux_loss_backward", _lib.moe_aux_loss_backward(
+        _p(logits), _p(tokens_per_expert), T, E, k, int(total_num_tokens), float(coeff),
+        _score(score), _p(d_loss), _p(d_logits), int(bool(accumulate)), _stream(stream)))
 
 
 # ---- whole layer -----------------------------------------------------------------------

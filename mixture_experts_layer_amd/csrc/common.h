@@ -60,6 +60,9 @@ MOE_DEV float e4m3_to_f32(uint32_t c) {
   return (c & 0x80u) ? -v : v;
 }
 
+// A NaN logit counts as -inf (the router's reading of non-finite logits).
+MOE_DEV float nan_to_ninf(float v) { return v != v ? -__builtin_inff() : v; }
+
 // ---- wave reductions -------------------------------------------------------
 MOE_DEV float wave_max(float v) {
 #pragma unroll

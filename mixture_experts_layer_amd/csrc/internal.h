@@ -54,6 +54,16 @@ hipError_t launch_router_ext(const float* logits, int T, int E, int k, int score
 hipError_t launch_expert_bias_update(float* bias, const int32_t* tokens_per_expert, int E,
                                      float coeff, hipStream_t s);
 
+// aux_loss.hip: the auxiliary load-balancing loss (C = coeff E / (k T^2), host-computed)
+hipError_t launch_aux_scores(const float* logits, int T, int E, int k, int score, float* scores,
+                             uint8_t* routing_map, hipStream_t s);
+size_t aux_loss_scratch_bytes(int T, int E);
+hipError_t launch_aux_loss(const float* scores, const int32_t* counts, int T, int E, float C,
+                           float* loss, float* part, hipStream_t s);
+hipError_t launch_aux_loss_bwd(const float* logits, int T, int E, int score, const int32_t* counts,
+                               float C, const float* d_loss, float* d_logits, int accumulate,
+                               hipStream_t s);
+
 // router.hip
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int score,
                               int32_t* topk_idx, float* topk_prob, int32_t* counts,
@@ -94,7 +104,7 @@ hipError_t launch_quantize_weights(const void* w, int G, int K, int N, uint8_t* 
                                    hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 // Dispatch backward with the router's dx term: dx[t] = sum_j dxp[row_of[t,j]] +
-// sum_j d_logits[t, topk_idx[t,j]] * w_router[topk_idx[t,j]], fp32 sum, one rounding.
+// sum_e d_logits[t, e] * w_router[e] (over the nonzero d_logits), fp32 sum, one rounding.
 hipError_t launch_dispatch_bwd_router(const void* dxp, const int32_t* row_of,
                                       const int32_t* topk_idx, const float* d_logits,
                                       const void* w_router, int T, int H, int E, int k, void* dx,
@@ -103,18 +113,20 @@ hipError_t launch_dispatch_bwd_router(const void* dxp, const int32_t* row_of,
 // router_proj.hip
 hipError_t launch_router_logits(const void* x, const void* w_router, int T, int H, int E,
                                 float* logits, hipStream_t s);
+// logits [T,E] are read for MOE_SOFTMAX_PRE only (the experts not kept get a gradient).
 hipError_t launch_combine_bwd_router(const void* dy, const void* out, const int32_t* row_of,
-                                     const int32_t* topk_idx, const float* prob, int T, int H,
-                                     int E, int k, int score, float scaling, void* d_out,
-                                     float* d_prob, float* d_logits, uint16_t* dls, int mp,
-                                     hipStream_t s);
+                                     const int32_t* topk_idx, const float* prob,
+                                     const float* logits, int T, int H, int E, int k, int score,
+                                     float scaling, void* d_out, float* d_prob, float* d_logits,
+                                     uint16_t* dls, int mp, hipStream_t s);
 // Dispatch backward when the routing weights scale the expert inputs (with the router
 // projection): d_prob = <dxp, x>, d_logits (+ split halves), dx = sum q dxp + router term.
 hipError_t launch_dispatch_bwd_router_input(const void* dxp, const void* x, const int32_t* row_of,
                                             const int32_t* topk_idx, const float* prob,
-                                            const void* w_router, int T, int H, int E, int k,
-                                            int score, float scaling, void* dx, float* d_logits,
-                                            uint16_t* dls, int mp, hipStream_t s);
+                                            const float* logits, const void* w_router, int T,
+                                            int H, int E, int k, int score, float scaling,
+                                            void* dx, float* d_logits, uint16_t* dls, int mp,
+                                            hipStream_t s);
 hipError_t launch_router_wgrad_reduce(const float* part, int S, int E, int H, int mp, float* dw,
                                       hipStream_t s);
 hipError_t launch_router_split(const float* d_logits, int T, int E, int mp, uint16_t* dls,

@@ -114,7 +114,7 @@ Layout make_layout(const moe_problem_t& p) {
   return L;
 }
 
-bool valid_score(int score) { return score >= MOE_SOFTMAX_PRE_RENORM && score <= MOE_SQRTSOFTPLUS; }
+bool valid_score(int score) { return score >= MOE_SOFTMAX_PRE_RENORM && score <= MOE_SOFTMAX_PRE; }
 
 // Router options against (E, k, score); fills `o` (scaling 0 is taken as 1).
 moe_status_t make_router_opts(int E, int k, int score, const float* expert_bias, int num_groups,
@@ -447,9 +447,10 @@ moe_status_t moe_router_logits(const void* x, const void* w_router, int T, int H
 
 moe_status_t moe_combine_backward_router(const void* dy, const void* expert_out,
                                          const int32_t* row_of, const int32_t* topk_idx,
-                                         const float* topk_prob, int T, int H, int E, int k,
-                                         int score, float scaling_factor, void* d_out,
-                                         float* d_prob, float* d_logits, void* stream) {
+                                         const float* topk_prob, const float* logits, int T,
+                                         int H, int E, int k, int score, float scaling_factor,
+                                         void* d_out, float* d_prob, float* d_logits,
+                                         void* stream) {
   moe_status_t st = check_shape(T, H, E, k);
   if (st != MOE_OK) return st;
   if (!valid_score(score)) return MOE_ERR_INVALID_ARG;
@@ -457,11 +458,13 @@ moe_status_t moe_combine_backward_router(const void* dy, const void* expert_out,
     return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(dy) || !ok_ptr(expert_out) || !ok_ptr(row_of) || !ok_ptr(topk_idx) ||
-      !ok_ptr(topk_prob) || !ok_ptr(d_out) || !opt_ptr(d_prob) || !ok_ptr(d_logits))
+      !ok_ptr(topk_prob) || !ok_ptr(d_out) || !opt_ptr(d_prob) || !ok_ptr(d_logits) ||
+      (score == MOE_SOFTMAX_PRE && !ok_ptr(logits)))
     return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_combine_bwd_router(dy, expert_out, row_of, topk_idx, topk_prob, T, H, E,
-                                              k, score, scaling_factor == 0.f ? 1.f : scaling_factor,
-                                              d_out, d_prob, d_logits, nullptr, 0, S(stream)));
+  return hip_status(launch_combine_bwd_router(dy, expert_out, row_of, topk_idx, topk_prob, logits,
+                                              T, H, E, k, score,
+                                              scaling_factor == 0.f ? 1.f : scaling_factor, d_out,
+                                              d_prob, d_logits, nullptr, 0, S(stream)));
 }
 
 size_t moe_router_weight_grad_workspace_bytes(int T, int H, int E) {
@@ -500,10 +503,10 @@ moe_status_t moe_dispatch_backward_router(const void* dxp, const int32_t* row_of
 
 moe_status_t moe_dispatch_backward_router_input(const void* dxp, const void* x,
                                                 const int32_t* row_of, const int32_t* topk_idx,
-                                                const float* topk_prob, const void* w_router,
-                                                int T, int H, int E, int k, int score,
-                                                float scaling_factor, void* dx, float* d_logits,
-                                                void* stream) {
+                                                const float* topk_prob, const float* logits,
+                                                const void* w_router, int T, int H, int E, int k,
+                                                int score, float scaling_factor, void* dx,
+                                                float* d_logits, void* stream) {
   moe_status_t st = check_shape(T, H, E, k);
   if (st != MOE_OK) return st;
   if (!valid_score(score)) return MOE_ERR_INVALID_ARG;
@@ -511,11 +514,69 @@ moe_status_t moe_dispatch_backward_router_input(const void* dxp, const void* x,
     return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(dxp) || !ok_ptr(x) || !ok_ptr(row_of) || !ok_ptr(topk_idx) || !ok_ptr(topk_prob) ||
-      !ok_ptr(w_router) || !ok_ptr(dx) || !ok_ptr(d_logits))
+      !ok_ptr(w_router) || !ok_ptr(dx) || !ok_ptr(d_logits) ||
+      (score == MOE_SOFTMAX_PRE && !ok_ptr(logits)))
     return MOE_ERR_INVALID_ARG;
   return hip_status(launch_dispatch_bwd_router_input(
-      dxp, x, row_of, topk_idx, topk_prob, w_router, T, H, E, k, score,
+      dxp, x, row_of, topk_idx, topk_prob, logits, w_router, T, H, E, k, score,
       scaling_factor == 0.f ? 1.f : scaling_factor, dx, d_logits, nullptr, 0, S(stream)));
+}
+
+// ---- auxiliary load-balancing loss -------------------------------------------------------
+
+moe_status_t moe_aux_loss_scores(const float* logits, int T, int E, int k, int score,
+                                 float* scores, uint8_t* routing_map, void* stream) {
+  moe_status_t st = check_shape(T, 64, E, k);
+  if (st != MOE_OK) return st;
+  if (!valid_score(score)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(logits) || !ok_ptr(scores) || !opt_ptr(routing_map)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_aux_scores(logits, T, E, k, score, scores, routing_map, S(stream)));
+}
+
+size_t moe_aux_loss_workspace_bytes(int T, int E) {
+  if (T < 0 || E <= 0 || E > 256) return 0;
+  return aux_loss_scratch_bytes(T, E);
+}
+
+namespace {
+// coeff * E / (k * total^2), in double, rounded once
+bool aux_constant(int E, int k, int total, float coeff, float* C) {
+  if (total <= 0 || k <= 0 || !(coeff == coeff) || coeff == INFINITY || coeff == -INFINITY)
+    return false;
+  *C = (float)((double)coeff * E / ((double)k * (double)total * (double)total));
+  return true;
+}
+}  // namespace
+
+moe_status_t moe_aux_loss(const float* scores, const int32_t* tokens_per_expert, int T, int E,
+                          int k, int total_num_tokens, float coeff, float* loss, void* ws,
+                          size_t ws_bytes, void* stream) {
+  moe_status_t st = check_shape(T, 64, E, k);
+  if (st != MOE_OK) return st;
+  float C;
+  if (!aux_constant(E, k, total_num_tokens, coeff, &C)) return MOE_ERR_INVALID_ARG;
+  if ((T > 0 && !ok_ptr(scores)) || !ok_ptr(tokens_per_expert) || !ok_ptr(loss) || !ok_ptr(ws))
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < aux_loss_scratch_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_aux_loss(scores, tokens_per_expert, T, E, C, loss, (float*)ws,
+                                    S(stream)));
+}
+
+moe_status_t moe_aux_loss_backward(const float* logits, const int32_t* tokens_per_expert, int T,
+                                   int E, int k, int total_num_tokens, float coeff, int score,
+                                   const float* d_loss, float* d_logits, int accumulate,
+                                   void* stream) {
+  moe_status_t st = check_shape(T, 64, E, k);
+  if (st != MOE_OK) return st;
+  if (!valid_score(score) || (accumulate != 0 && accumulate != 1)) return MOE_ERR_INVALID_ARG;
+  float C;
+  if (!aux_constant(E, k, total_num_tokens, coeff, &C)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(logits) || !ok_ptr(tokens_per_expert) || !opt_ptr(d_loss) || !ok_ptr(d_logits))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_aux_loss_bwd(logits, T, E, score, tokens_per_expert, C, d_loss,
+                                        d_logits, accumulate, S(stream)));
 }
 
 moe_status_t moe_quantize_mxfp8_rows(const void* x, int R, int C, uint8_t* q, uint8_t* scale,
@@ -871,7 +932,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   } else if (p->router) {
     // combine backward with the routing-weight gradient: d_out, d_logits and the split
     // operand of the router weight gradient
-    MOE_TRY(launch_combine_bwd_router(dy, v.out, v.row_of, v.topk_idx, v.topk_prob, T, H, E, k,
+    MOE_TRY(launch_combine_bwd_router(dy, v.out, v.row_of, v.topk_idx, v.topk_prob, v.logits, T, H, E, k,
                                       p->score, p->scaling_factor == 0.f ? 1.f : p->scaling_factor,
                                       v.d_out, nullptr, v.d_logits, (uint16_t*)v.router_ws,
                                       router_split_cols(E), s));
@@ -969,7 +1030,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   // dispatch backward: dx[t] = sum_j dxp[row_of[t,j]] (weighted when the weights scaled the
   // inputs; + the router's term)
   if (p->router && at_input) {
-    MOE_TRY(launch_dispatch_bwd_router_input(v.dxp, t->x, v.row_of, v.topk_idx, v.topk_prob,
+    MOE_TRY(launch_dispatch_bwd_router_input(v.dxp, t->x, v.row_of, v.topk_idx, v.topk_prob, v.logits,
                                              t->w_router, T, H, E, k, p->score, r_scale, dx,
                                              v.d_logits, (uint16_t*)v.router_ws,
                                              router_split_cols(E), s));

@@ -457,28 +457,42 @@ hipError_t launch_quantize_weights(const void* w, int G, int K, int N, uint8_t* 
 // y[t] = sum_j p[t,j] * y_perm[row_of[t,j]] (+ shared[t]); fp32 sum in slot order, one
 // rounding to bf16. prob == NULL gives the unweighted sum used by the dispatch backward.
 // ROUTER (dispatch backward of a layer that owns its router projection): the router's dx
-// term sum_j d_logits[t, e_j] * W_r[e_j] over the kept experts e_j is added after the k
-// rows, before the rounding (the other experts' d_logits are 0).
+// term sum_e d_logits[t, e] * W_r[e] is added after the k rows, before the rounding, over
+// the experts whose d_logits is nonzero (ascending id): the kept experts, or every expert
+// for softmax before the top-k without renormalisation.
 template <bool ROUTER>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict__ yp,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ prob,
                                                       const u32x4_t* __restrict__ shared, int H8,
                                                       int k, u32x4_t* __restrict__ y,
-                                                      const int32_t* __restrict__ topk_idx = nullptr,
                                                       const float* __restrict__ d_logits = nullptr,
                                                       const u32x4_t* __restrict__ w_router = nullptr,
                                                       int E = 0) {
-  __shared__ int rows[32], ids[32];
-  __shared__ float p[32], dl[32];
+  __shared__ int rows[32], ids[256], wcount[4];
+  __shared__ float p[32], dl[256];
   const int t = blockIdx.x;
   if ((int)threadIdx.x < k) {
     rows[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
     p[threadIdx.x] = prob ? prob[(size_t)t * k + threadIdx.x] : 1.f;
-    if constexpr (ROUTER) {
-      const int e = topk_idx[(size_t)t * k + threadIdx.x];
-      ids[threadIdx.x] = e;
-      dl[threadIdx.x] = d_logits[(size_t)t * E + e];
+  }
+  int nnz = 0;
+  if constexpr (ROUTER) {  // compact the nonzero d_logits of the token (E <= 256 threads)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float v = tid < E ? d_logits[(size_t)t * E + tid] : 0.f;
+    const bool nz = v != 0.f;
+    const uint64_t b = __ballot(nz);
+    if (lane == 0) wcount[wave] = __popcll(b);
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < 4; ++w) {
+      before += w < wave ? wcount[w] : 0;
+      nnz += wcount[w];
+    }
+    if (nz) {
+      const int at = before + __popcll(b & lanemask_lt());
+      ids[at] = tid;
+      dl[at] = v;
     }
   }
   __syncthreads();
@@ -505,7 +519,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict_
       }
     }
     if constexpr (ROUTER) {
-      for (int j = 0; j < k; ++j) {
+      for (int j = 0; j < nnz; ++j) {
         const u32x4_t wv = w_router[(size_t)ids[j] * H8 + v];
         const float g = dl[j];
 #pragma unroll
@@ -544,8 +558,7 @@ hipError_t launch_dispatch_bwd_router(const void* dxp, const int32_t* row_of,
                                       hipStream_t s) {
   if (T == 0) return hipSuccess;
   combine_kernel<true><<<T, 256, 0, s>>>((const u32x4_t*)dxp, row_of, nullptr, nullptr, H / 8, k,
-                                         (u32x4_t*)dx, topk_idx, d_logits,
-                                         (const u32x4_t*)w_router, E);
+                                         (u32x4_t*)dx, d_logits, (const u32x4_t*)w_router, E);
   return hipGetLastError();
 }
 

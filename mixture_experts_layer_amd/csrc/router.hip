@@ -6,10 +6,14 @@
 //
 // Selection works on the logits (softmax and sigmoid are strictly increasing, so they
 // select the same experts): k rounds of a wave-wide arg-max with the lower expert id
-// winning a tie, each lane holding up to four experts (E <= 256) in registers.
-// Weights: for softmax (before or after the top-k) q_j = exp(l_j - l_max) / sum over
-// the k kept logits -- the full-softmax denominator cancels in the renormalisation --
-// and sigmoid(l_j) without renormalisation for the sigmoid score.
+// winning a tie, each lane holding up to four experts (E <= 256) in registers. A NaN logit
+// counts as -inf, and each round takes the best available expert even when every one
+// left is at -inf, so the ids are always k distinct experts of [0, E).
+// Weights: for softmax before the top-k with renormalisation, or after the top-k,
+// q_j = exp(l_j - l_max) / sum over the k kept logits -- the full-softmax denominator
+// cancels in the renormalisation; for softmax before the top-k without renormalisation
+// q_j = exp(l_j - l_max) / sum over all E logits; sigmoid(l_j) without renormalisation
+// for the sigmoid score.
 #include "internal.h"
 
 namespace moe {
@@ -58,7 +62,19 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     for (int i = 0; i < EPL; ++i) {
       int e = lane + 64 * i;
       taken[i] = e >= E;
-      v[i] = taken[i] ? 0.f : row[e];
+      v[i] = taken[i] ? 0.f : nan_to_ninf(row[e]);
+    }
+    // softmax before the top-k without renormalisation: every expert's exp(l - l_max)
+    float zall = 0.f, vmax = -__builtin_inff();
+    if (score == MOE_SOFTMAX_PRE) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (!taken[i]) vmax = fmaxf(vmax, v[i]);
+      vmax = wave_max(vmax);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (!taken[i]) zall += expf(v[i] - vmax);
+      zall = wave_sum(zall);
     }
     int my_e = 0;
     float my_v = 0.f;
@@ -94,6 +110,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     float q;
     if (score == MOE_SIGMOID) {
       q = 1.0f / (1.0f + expf(-my_v));
+    } else if (score == MOE_SOFTMAX_PRE) {
+      q = expf(my_v - vmax) / zall;
     } else {
       float m = __shfl(my_v, 0, 64);  // the best logit is the first choice
       float z = lane < k ? expf(my_v - m) : 0.f;
@@ -169,19 +187,21 @@ __global__ __launch_bounds__(512) void router_row_kernel(
 #pragma unroll
     for (int i = 0; i < EPR; ++i) {
       const int e = r + 16 * i;
-      v[i] = e < E ? lrow[e] : 0.f;
+      v[i] = e < E ? nan_to_ninf(lrow[e]) : 0.f;
       if (e < E) avail |= 1 << i;
     }
+    const int exists = avail;
     int my_e = 0;
     float my_v = 0.f, top_v = 0.f;
     for (int j = 0; j < k; ++j) {
-      // branch-free: a lane with no candidate holds (-inf, INT_MAX), which every finite
-      // logit beats and which keeps ties among empty lanes harmless
+      // branch-free: a lane with no candidate holds (-inf, INT_MAX), which every available
+      // expert beats (an available one at -inf by its lower id), so the winner is always a
+      // real expert; the lane's first available expert is taken whatever its value
       float bv = -__builtin_inff();
       int be = 0x7fffffff;
 #pragma unroll
       for (int i = 0; i < EPR; ++i) {  // ascending id: strict > keeps the lower id on a tie
-        const bool take = ((avail >> i) & 1) & (v[i] > bv);
+        const bool take = ((avail >> i) & 1) & ((be == 0x7fffffff) | (v[i] > bv));
         bv = take ? v[i] : bv;
         be = take ? r + 16 * i : be;
       }
@@ -203,6 +223,15 @@ __global__ __launch_bounds__(512) void router_row_kernel(
     float q;
     if (score == MOE_SIGMOID) {
       q = 1.0f / (1.0f + expf(-my_v));
+    } else if (score == MOE_SOFTMAX_PRE) {
+      // the full softmax: every expert's exp(l - l_max) summed over the row's 16 lanes
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPR; ++i)
+        if ((exists >> i) & 1) sum += expf(v[i] - top_v);
+#pragma unroll
+      for (int sh = 8; sh > 0; sh >>= 1) sum += __int_as_float(dpp_ror(__float_as_int(sum), sh));
+      q = expf(my_v - top_v) / sum;
     } else {
       const float z = r < k ? expf(my_v - top_v) : 0.f;  // the best logit is the first choice
       float sum = z;

@@ -12,7 +12,8 @@
 // One wavefront per token. Each lane holds experts lane, lane+64, ... (EPL of them). The
 // selection key is the logit, except with an expert bias, where it is fp32(score + bias);
 // grouped routing sums, per group, the values of its m = k / group_topk best experts
-// (softmax before the top-k: the fp32 probabilities; after it: the logits; sigmoid and
+// (softmax before the top-k, renormalised or not: the fp32 probabilities; after it: the
+// logits; sigmoid and
 // sqrtsoftplus: the fp32 scores, plus the bias when there is one), best first, in fp32.
 // The wave writes the keys and values of its token to LDS, lane g < num_groups scores
 // group g, group_topk rounds of a wave arg-max keep the groups, and the experts of the
@@ -76,10 +77,24 @@ __global__ __launch_bounds__(256) void router_ext_kernel(
       const int e = lane + 64 * i;
       taken[i] = e >= E;
       chosen[i] = false;
-      key[i] = taken[i] ? 0.f : row[e];
+      key[i] = taken[i] ? 0.f : nan_to_ninf(row[e]);
       gv[i] = key[i];
     }
-    if (score == MOE_SOFTMAX_PRE_RENORM && o.num_groups > 1) {
+    const bool pre = score == MOE_SOFTMAX_PRE_RENORM || score == MOE_SOFTMAX_PRE;
+    // softmax before the top-k without renormalisation: the weights divide by every
+    // expert's exp(l - l_max)
+    float zall = 0.f, vmax = -INFINITY;
+    if (score == MOE_SOFTMAX_PRE) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (!taken[i]) vmax = fmaxf(vmax, key[i]);
+      vmax = wave_max(vmax);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (!taken[i]) zall += expf(key[i] - vmax);
+      zall = wave_sum(zall);
+    }
+    if (pre && o.num_groups > 1) {
       float m = -INFINITY;
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
@@ -138,7 +153,7 @@ __global__ __launch_bounds__(256) void router_ext_kernel(
           pk = bk;
           pi = bi;
         }
-        gscore = acc;
+        gscore = nan_to_ninf(acc);  // a row of -inf logits: every group ties, lowest id first
       }
       uint64_t kept = 0;
       bool gdone = lane >= o.num_groups;
@@ -180,12 +195,14 @@ __global__ __launch_bounds__(256) void router_ext_kernel(
         }
     }
     // weights from the chosen experts' logits
-    const float lsel = lane < k ? row[my_e] : 0.f;
+    const float lsel = lane < k ? nan_to_ninf(row[my_e]) : 0.f;
     float q;
     if (score == MOE_SIGMOID) {
       q = 1.0f / (1.0f + expf(-lsel));
     } else if (score == MOE_SQRTSOFTPLUS) {
       q = sqrtf(softplus_f(lsel));
+    } else if (score == MOE_SOFTMAX_PRE) {
+      q = expf(lsel - vmax) / zall;
     } else {
       // the largest kept logit: with grouping the first choice need not be the largest
       float mx = lane < k ? lsel : -INFINITY;

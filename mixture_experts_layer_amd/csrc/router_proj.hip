@@ -143,13 +143,34 @@ hipError_t launch_router_logits(const void* x, const void* w_router, int T, int 
 // of the router weight-gradient GEMM, which so keeps about 16 bits of each value.
 
 // The block's k partial dot products -> d_prob (optional), the score-function backward
-// -> dl_s[k] in LDS, the token's d_logits row and its split halves. Every thread calls it.
+// -> dl_s[k] in LDS, the token's d_logits row (also kept in LDS, dl_row[E]) and its split
+// halves. Every thread calls it. Softmax before the top-k without renormalisation also
+// moves the logits of the experts not kept: with u_j the kept probabilities and
+// S = sum_j u_j d_prob_j, expert e gets -c p_e S, p_e = exp(l_e - l_max) / sum over the
+// token's logits (read from `logits`, block max and sum).
 template <int KM>
 MOE_DEV void router_score_bwd(const float (&dot)[KM], int t, int E, int k, int score,
                               float scaling, const float* p, const int* ids, float (*red)[32],
-                              float* dl_s, float* __restrict__ d_prob,
-                              float* __restrict__ d_logits, uint16_t* __restrict__ dls, int mp) {
+                              float* dl_s, float* dl_row, const float* __restrict__ logits,
+                              float* __restrict__ d_prob, float* __restrict__ d_logits,
+                              uint16_t* __restrict__ dls, int mp) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // softmax before the top-k: this token's logit, the block max and the block sum
+  float pe = 0.f;
+  if (score == MOE_SOFTMAX_PRE) {
+    const float l = tid < E ? nan_to_ninf(logits[(size_t)t * E + tid]) : -__builtin_inff();
+    const float wm = wave_max(l);
+    if (lane == 0) red[wave][31] = wm;
+    __syncthreads();
+    const float m = fmaxf(fmaxf(red[0][31], red[1][31]), fmaxf(red[2][31], red[3][31]));
+    const float z = tid < E ? expf(l - m) : 0.f;
+    __syncthreads();
+    const float ws = wave_sum(z);
+    if (lane == 0) red[wave][31] = ws;
+    __syncthreads();
+    pe = z / ((red[0][31] + red[1][31]) + (red[2][31] + red[3][31]));
+    __syncthreads();
+  }
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
     if (j >= k) continue;
@@ -170,18 +191,22 @@ MOE_DEV void router_score_bwd(const float (&dot)[KM], int t, int E, int k, int s
       dl = scaling * dq * sv * (1.0f - sv);
     } else if (score == MOE_SQRTSOFTPLUS) {
       dl = scaling * dq * (-expm1f(-sv * sv)) / (2.0f * sv);
-    } else {  // both softmax orders: the same function of the kept logits
+    } else {  // softmax: both renormalised orders are the same function of the kept
+              // logits; without renormalisation the same form with the full probabilities
       float sdot = 0.f;
       for (int j = 0; j < k; ++j) sdot = fmaf(p[j] / scaling, red[0][j], sdot);
       dl = scaling * sv * (dq - sdot);
+      if (tid == 0) red[1][31] = sdot;  // S, for the experts not kept
     }
     dl_s[tid] = dl;
   }
   __syncthreads();
+  const float off = score == MOE_SOFTMAX_PRE ? -scaling * red[1][31] : 0.f;
   for (int e = tid; e < E; e += 256) {
-    float v = 0.f;
+    float v = off * pe;  // e < 256: thread e holds p_e
     for (int j = 0; j < k; ++j) v = ids[j] == e ? dl_s[j] : v;
     d_logits[(size_t)t * E + e] = v;
+    dl_row[e] = v;
     if (dls) {
       const uint32_t hi = f32_to_bf16(v);
       dls[(size_t)t * mp + e] = (uint16_t)hi;
@@ -190,17 +215,41 @@ MOE_DEV void router_score_bwd(const float (&dot)[KM], int t, int E, int k, int s
   }
   if (dls)
     for (int c = 2 * E + tid; c < mp; c += 256) dls[(size_t)t * mp + c] = 0;
+  __syncthreads();  // dl_row complete
+}
+
+// The nonzero entries of the token's d_logits row, ascending expert id, compacted into
+// nz_e / nz_v (LDS); returns their number. Every thread calls it (E <= 256 = blockDim).
+MOE_DEV int compact_nonzero(const float* dl_row, int E, int* nz_e, float* nz_v, int* wcount) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float v = tid < E ? dl_row[tid] : 0.f;
+  const bool nz = v != 0.f;
+  const uint64_t b = __ballot(nz);
+  if (lane == 0) wcount[wave] = __popcll(b);
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < 4; ++w) {
+    before += w < wave ? wcount[w] : 0;
+    total += wcount[w];
+  }
+  if (nz) {
+    const int at = before + __popcll(b & lanemask_lt());
+    nz_e[at] = tid;
+    nz_v[at] = v;
+  }
+  __syncthreads();
+  return total;
 }
 
 template <int KM>  // a bound on k: 8 or 32
 __global__ __launch_bounds__(256) void combine_bwd_router_kernel(
     const u32x4_t* __restrict__ dy, const u32x4_t* __restrict__ out,
     const int32_t* __restrict__ row_of, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ prob, int H8, int E, int k, int score, float scaling,
-    u32x4_t* __restrict__ d_out,
+    const float* __restrict__ prob, const float* __restrict__ logits, int H8, int E, int k,
+    int score, float scaling, u32x4_t* __restrict__ d_out,
     float* __restrict__ d_prob, float* __restrict__ d_logits, uint16_t* __restrict__ dls, int mp) {
   __shared__ int rows[32], ids[32];
-  __shared__ float p[32], red[4][32], dl_s[32];
+  __shared__ float p[32], red[4][32], dl_s[32], dl_row[256];
   const int t = blockIdx.x, tid = threadIdx.x;
   if (tid < k) {
     rows[tid] = row_of[(size_t)t * k + tid];
@@ -238,7 +287,8 @@ __global__ __launch_bounds__(256) void combine_bwd_router_kernel(
       }
     }
   }
-  router_score_bwd<KM>(dot, t, E, k, score, scaling, p, ids, red, dl_s, d_prob, d_logits, dls, mp);
+  router_score_bwd<KM>(dot, t, E, k, score, scaling, p, ids, red, dl_s, dl_row, logits, d_prob,
+                       d_logits, dls, mp);
 }
 
 // ---- dispatch backward of a layer that weights the expert inputs ---------------------------
@@ -252,11 +302,11 @@ template <int KM>
 __global__ __launch_bounds__(256) void dispatch_bwd_router_input_kernel(
     const u32x4_t* __restrict__ dxp, const u32x4_t* __restrict__ x,
     const int32_t* __restrict__ row_of, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ prob, const u32x4_t* __restrict__ w_router, int H8, int E, int k,
-    int score, float scaling, u32x4_t* __restrict__ dx, float* __restrict__ d_logits,
-    uint16_t* __restrict__ dls, int mp) {
-  __shared__ int rows[32], ids[32];
-  __shared__ float p[32], red[4][32], dl_s[32];
+    const float* __restrict__ prob, const float* __restrict__ logits,
+    const u32x4_t* __restrict__ w_router, int H8, int E, int k, int score, float scaling,
+    u32x4_t* __restrict__ dx, float* __restrict__ d_logits, uint16_t* __restrict__ dls, int mp) {
+  __shared__ int rows[32], ids[32], nz_e[256], wcount[4];
+  __shared__ float p[32], red[4][32], dl_s[32], dl_row[256], nz_v[256];
   const int t = blockIdx.x, tid = threadIdx.x;
   if (tid < k) {
     rows[tid] = row_of[(size_t)t * k + tid];
@@ -289,7 +339,11 @@ __global__ __launch_bounds__(256) void dispatch_bwd_router_input_kernel(
       }
     }
   }
-  router_score_bwd<KM>(dot, t, E, k, score, scaling, p, ids, red, dl_s, nullptr, d_logits, dls, mp);
+  router_score_bwd<KM>(dot, t, E, k, score, scaling, p, ids, red, dl_s, dl_row, logits, nullptr,
+                       d_logits, dls, mp);
+  // the router's dx term over the experts with a nonzero d_logits (the kept ones, or every
+  // expert for softmax before the top-k without renormalisation)
+  const int nnz = compact_nonzero(dl_row, E, nz_e, nz_v, wcount);
   for (int v = tid; v < H8; v += 256) {
     float acc[8];
 #pragma unroll
@@ -303,9 +357,9 @@ __global__ __launch_bounds__(256) void dispatch_bwd_router_input_kernel(
         acc[2 * d + 1] = fmaf(q, bf16hi(o[d]), acc[2 * d + 1]);
       }
     }
-    for (int j = 0; j < k; ++j) {
-      const u32x4_t wv = w_router[(size_t)ids[j] * H8 + v];
-      const float g = dl_s[j];
+    for (int j = 0; j < nnz; ++j) {
+      const u32x4_t wv = w_router[(size_t)nz_e[j] * H8 + v];
+      const float g = nz_v[j];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         acc[2 * d] = fmaf(g, bf16lo(wv[d]), acc[2 * d]);
@@ -321,35 +375,38 @@ __global__ __launch_bounds__(256) void dispatch_bwd_router_input_kernel(
 
 hipError_t launch_dispatch_bwd_router_input(const void* dxp, const void* x, const int32_t* row_of,
                                             const int32_t* topk_idx, const float* prob,
-                                            const void* w_router, int T, int H, int E, int k,
-                                            int score, float scaling, void* dx, float* d_logits,
-                                            uint16_t* dls, int mp, hipStream_t s) {
+                                            const float* logits, const void* w_router, int T,
+                                            int H, int E, int k, int score, float scaling,
+                                            void* dx, float* d_logits, uint16_t* dls, int mp,
+                                            hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (k <= 8)
     dispatch_bwd_router_input_kernel<8><<<T, 256, 0, s>>>(
-        (const u32x4_t*)dxp, (const u32x4_t*)x, row_of, topk_idx, prob, (const u32x4_t*)w_router,
-        H / 8, E, k, score, scaling, (u32x4_t*)dx, d_logits, dls, mp);
+        (const u32x4_t*)dxp, (const u32x4_t*)x, row_of, topk_idx, prob, logits,
+        (const u32x4_t*)w_router, H / 8, E, k, score, scaling, (u32x4_t*)dx, d_logits, dls, mp);
   else
     dispatch_bwd_router_input_kernel<32><<<T, 256, 0, s>>>(
-        (const u32x4_t*)dxp, (const u32x4_t*)x, row_of, topk_idx, prob, (const u32x4_t*)w_router,
-        H / 8, E, k, score, scaling, (u32x4_t*)dx, d_logits, dls, mp);
+        (const u32x4_t*)dxp, (const u32x4_t*)x, row_of, topk_idx, prob, logits,
+        (const u32x4_t*)w_router, H / 8, E, k, score, scaling, (u32x4_t*)dx, d_logits, dls, mp);
   return hipGetLastError();
 }
 
 hipError_t launch_combine_bwd_router(const void* dy, const void* out, const int32_t* row_of,
-                                     const int32_t* topk_idx, const float* prob, int T, int H,
-                                     int E, int k, int score, float scaling, void* d_out,
-                                     float* d_prob, float* d_logits, uint16_t* dls, int mp,
-                                     hipStream_t s) {
+                                     const int32_t* topk_idx, const float* prob,
+                                     const float* logits, int T, int H, int E, int k, int score,
+                                     float scaling, void* d_out, float* d_prob, float* d_logits,
+                                     uint16_t* dls, int mp, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (k <= 8)
     combine_bwd_router_kernel<8><<<T, 256, 0, s>>>((const u32x4_t*)dy, (const u32x4_t*)out, row_of,
-                                                   topk_idx, prob, H / 8, E, k, score, scaling,
-                                                   (u32x4_t*)d_out, d_prob, d_logits, dls, mp);
+                                                   topk_idx, prob, logits, H / 8, E, k, score,
+                                                   scaling, (u32x4_t*)d_out, d_prob, d_logits,
+                                                   dls, mp);
   else
     combine_bwd_router_kernel<32><<<T, 256, 0, s>>>((const u32x4_t*)dy, (const u32x4_t*)out, row_of,
-                                                    topk_idx, prob, H / 8, E, k, score, scaling,
-                                                    (u32x4_t*)d_out, d_prob, d_logits, dls, mp);
+                                                    topk_idx, prob, logits, H / 8, E, k, score,
+                                                    scaling, (u32x4_t*)d_out, d_prob, d_logits,
+                                                    dls, mp);
   return hipGetLastError();
 }
 

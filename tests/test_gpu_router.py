@@ -158,6 +158,7 @@ LAYER = {
     "post": W.custom("r_post", T=300, H=384, E=8, k=2, I=256, score=O.SOFTMAX_POST, training=True),
     "sigmoid": W.custom("r_sig", T=96, H=256, E=16, k=2, I=128, score=O.SIGMOID, training=True),
     "t1": W.custom("r_t1", T=1, H=128, E=8, k=2, I=128, training=True),
+    "pre": W.custom("r_pre", T=200, H=256, E=16, k=4, I=128, score=O.SOFTMAX_PRE, training=True),
 }
 
 
