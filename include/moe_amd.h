@@ -247,6 +247,32 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const void* d_out, const void* w_down,
                                          const int32_t* offsets, const void* gu_saved, int G,
                                          int rows, int H, int I, void* dgu, void* stream);
 
+/* ScaledSwiGLU (guide, "Grouped MLP": the activation output is multiplied by the routing
+ * weights before FC2; with a bias-free FC2 the expert output is then already weighted and
+ * the combine sums unweighted). bf16 only. As moe_grouped_gemm_swiglu, with
+ * h[r] = bf16(silu(g) u row_scale[r]) (one fp32 product of g, u, weight, one rounding).
+ *  row_scale [rows] float32: the routing weight of each routed row (moe_permute_probs). */
+moe_status_t moe_grouped_gemm_swiglu_scaled(const void* xp, const void* w_gu,
+                                            const int32_t* offsets, const float* row_scale, int G,
+                                            int rows, int H, int I, void* h, void* gu_saved,
+                                            void* stream);
+
+/* Backward of FC2 + ScaledSwiGLU: dh = d_out . W_down[g]^T (the gradient of the scaled h),
+ * then as moe_grouped_gemm_swiglu_bwd with dh * row_scale[r]. d_scale_part [rows, I/64]
+ * float32 out, nullable: per row and block of 64 h columns, sum_c dh[r,c] silu(g) u from the
+ * saved bf16 g, u (fp32); the weight gradient of row r is the sum of its I/64 values. */
+moe_status_t moe_grouped_gemm_swiglu_scaled_bwd(const void* d_out, const void* w_down,
+                                                const int32_t* offsets, const void* gu_saved,
+                                                const float* row_scale, int G, int rows, int H,
+                                                int I, void* dgu, float* d_scale_part,
+                                                void* stream);
+
+/* The routing weight of every routed row (guide, "Token dispatch": the permuted
+ * probabilities): row_prob[row_of[t,j]] = topk_prob[t,j]. row_of, topk_prob [T,k];
+ * row_prob [T*k] float32 out (rows of a padded dispatch's padding are not written). */
+moe_status_t moe_permute_probs(const int32_t* row_of, const float* topk_prob, int T, int k,
+                               float* row_prob, void* stream);
+
 /* Cap on the persistent grid of every grouped-GEMM launch (the entry points above and
  * the ones inside moe_forward / moe_backward). Each launch runs min(tiles, resident)
  * blocks, resident = compute units x blocks per unit, and every block walks its share of
@@ -349,6 +375,18 @@ moe_status_t moe_dispatch_backward_router_input(const void* dxp, const void* x,
                                                 int score, float scaling_factor, void* dx,
                                                 float* d_logits, void* stream);
 
+/* Dispatch backward of a ScaledSwiGLU layer that owns its router projection: d_prob[t,j] =
+ * the sum, in a fixed order, of the I/64 partials d_scale_part [rows, I/64] of row
+ * row_of[t,j] (moe_grouped_gemm_swiglu_scaled_bwd); d_logits [T,E] out, its score-function
+ * backward (see moe_combine_backward_router; logits read for MOE_SOFTMAX_PRE only);
+ * dx [T,H] bf16 out: bf16(sum_j dxp[row_of[t,j]] + sum_e d_logits[t,e] w_router[e]). */
+moe_status_t moe_dispatch_backward_router_scaled(const void* dxp, const float* d_scale_part,
+                                                 const int32_t* row_of, const int32_t* topk_idx,
+                                                 const float* topk_prob, const float* logits,
+                                                 const void* w_router, int T, int H, int E, int k,
+                                                 int I, int score, float scaling_factor, void* dx,
+                                                 float* d_logits, void* stream);
+
 /* ---- MXFP8 (te_mixtral.py's mxfp8 recipe) ------------------------------------------
  * e4m3 codes with one power-of-two scale per block of 32 consecutive values along K,
  * stored as a byte (E8M0: log2(scale) + 127). Conversion of a block (OCP Microscaling
@@ -442,14 +480,16 @@ typedef struct {
                             the combine; MOE_PLACE_INPUT (1, bf16 only): they scale the
                             routed input rows, xp[r] = bf16(q x[t]), and the combine sums
                             unweighted (torchtitan pull request 1269, MoE.forward,
-                            scoring_before_experts) */
+                            scoring_before_experts); MOE_PLACE_ACTIVATION (2, bf16 only):
+                            they scale the SwiGLU output, h = bf16(silu(g) u q), and the
+                            combine sums unweighted (guide, "Grouped MLP", ScaledSwiGLU) */
   int align_size;        /* 0 or 1: no padding. Else a padded dispatch (guide, "Padding and
                             alignment"): every expert block starts at a multiple of
                             align_size rows (<= 4096), padding rows are zero; the row
                             buffers hold T*k + E*(align_size-1) rows */
 } moe_problem_t;
 
-enum { MOE_PLACE_COMBINE = 0, MOE_PLACE_INPUT = 1 };
+enum { MOE_PLACE_COMBINE = 0, MOE_PLACE_INPUT = 1, MOE_PLACE_ACTIVATION = 2 };
 
 typedef struct {
   const void* x;              /* [T,H] bf16 */

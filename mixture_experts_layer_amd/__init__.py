@@ -20,7 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_BF16, MOE_FP8_E4M3, MOE_FP32, MOE_MXFP8 = 0, 1, 2, 3
 MOE_SOFTMAX_PRE_RENORM, MOE_SOFTMAX_POST, MOE_SIGMOID, MOE_SQRTSOFTPLUS, MOE_SOFTMAX_PRE = range(5)
 MOE_GEMM_NN, MOE_GEMM_NT, MOE_GEMM_TN_DW = 0, 1, 2
-MOE_PLACE_COMBINE, MOE_PLACE_INPUT = 0, 1
+MOE_PLACE_COMBINE, MOE_PLACE_INPUT, MOE_PLACE_ACTIVATION = 0, 1, 2
 
 EXPORTS = [
     "moe_status_str", "moe_router_topk", "moe_permute_workspace_bytes", "moe_permute",
@@ -35,7 +35,8 @@ EXPORTS = [
     "moe_mxfp8_cols_capacity", "moe_mxfp8_col_offsets", "moe_quantize_mxfp8_cols",
     "moe_grouped_gemm_mxfp8_wgrad", "moe_grouped_gemm_mxfp8_swiglu_bwd",
     "moe_aux_loss_scores", "moe_aux_loss_workspace_bytes", "moe_aux_loss",
-    "moe_aux_loss_backward",
+    "moe_aux_loss_backward", "moe_grouped_gemm_swiglu_scaled",
+    "moe_grouped_gemm_swiglu_scaled_bwd", "moe_permute_probs", "moe_dispatch_backward_router_scaled",
 ]
 
 
@@ -130,6 +131,11 @@ def _load():
         "moe_aux_loss_workspace_bytes": ([i, i], sz),
         "moe_aux_loss": ([vp, vp, i, i, i, i, ctypes.c_float, vp, vp, sz, vp], i),
         "moe_aux_loss_backward": ([vp, vp, i, i, i, i, ctypes.c_float, i, vp, vp, i, vp], i),
+        "moe_grouped_gemm_swiglu_scaled": ([vp, vp, vp, vp, i, i, i, i, vp, vp, vp], i),
+        "moe_grouped_gemm_swiglu_scaled_bwd": ([vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp], i),
+        "moe_permute_probs": ([vp, vp, i, i, vp, vp], i),
+        "moe_dispatch_backward_router_scaled": ([vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                                                 ctypes.c_float, vp, vp, vp], i),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -534,6 +540,67 @@ def moe_dispatch_backward_router_input(dxp, x, row_of, topk_idx, topk_prob, w_ro
         _p(dxp), _p(x), _p(row_of), _p(topk_idx), _p(topk_prob), _p(logits), _p(w_router), T, H,
         E, k,
         _score(score), float(scaling_factor), _p(dx), _p(d_logits), _stream(stream)))
+
+
+# ---- ScaledSwiGLU ------------------------------------------------------------------------------
+
+def moe_permute_probs(row_of, topk_prob, row_prob, stream=None):
+    T, k = row_of.shape
+    _want(topk_prob, torch.float32, (T, k), "topk_prob")
+    if row_prob.dtype != torch.float32 or row_prob.dim() != 1 or row_prob.shape[0] < T * k:
+        raise ValueError("row_prob: expected float32 [>= T*k]")
+    _check("moe_permute_probs", _lib.moe_permute_probs(
+        _p(row_of), _p(topk_prob), T, k, _p(row_prob), _stream(stream)))
+
+
+def moe_grouped_gemm_swiglu_scaled(xp, w_gu, offsets, row_scale, h, gu_saved=None, stream=None):
+    rows, H = xp.shape
+    G, _, I2 = w_gu.shape
+    I = I2 // 2
+    _want(xp, torch.bfloat16, (rows, H), "xp")
+    _want(w_gu, torch.bfloat16, (G, H, 2 * I), "w_gu")
+    _want(offsets, torch.int32, (G + 1,), "offsets")
+    _want(row_scale, torch.float32, (rows,), "row_scale")
+    _want(h, torch.bfloat16, (rows, I), "h")
+    if gu_saved is not None:
+        _want(gu_saved, torch.bfloat16, (rows, 2 * I), "gu_saved")
+    _check("moe_grouped_gemm_swiglu_scaled", _lib.moe_grouped_gemm_swiglu_scaled(
+        _p(xp), _p(w_gu), _p(offsets), _p(row_scale), G, rows, H, I, _p(h), _p(gu_saved),
+        _stream(stream)))
+
+
+def moe_grouped_gemm_swiglu_scaled_bwd(d_out, w_down, offsets, gu_saved, row_scale, dgu,
+                                       d_scale_part=None, stream=None):
+    rows, H = d_out.shape
+    G, I, _ = w_down.shape
+    _want(d_out, torch.bfloat16, (rows, H), "d_out")
+    _want(w_down, torch.bfloat16, (G, I, H), "w_down")
+    _want(offsets, torch.int32, (G + 1,), "offsets")
+    _want(gu_saved, torch.bfloat16, (rows, 2 * I), "gu_saved")
+    _want(row_scale, torch.float32, (rows,), "row_scale")
+    _want(dgu, torch.bfloat16, (rows, 2 * I), "dgu")
+    if d_scale_part is not None:
+        _want(d_scale_part, torch.float32, (rows, I // 64), "d_scale_part")
+    _check("moe_grouped_gemm_swiglu_scaled_bwd", _lib.moe_grouped_gemm_swiglu_scaled_bwd(
+        _p(d_out), _p(w_down), _p(offsets), _p(gu_saved), _p(row_scale), G, rows, H, I, _p(dgu),
+        _p(d_scale_part), _stream(stream)))
+
+
+def moe_dispatch_backward_router_scaled(dxp, d_scale_part, row_of, topk_idx, topk_prob, w_router,
+                                        I, score, dx, d_logits, scaling_factor=1.0, logits=None,
+                                        stream=None):
+    T, k = row_of.shape
+    E, H = w_router.shape
+    _want_rows(dxp, torch.bfloat16, T * k, H, "dxp")
+    _want_rows(d_scale_part, torch.float32, T * k, I // 64, "d_scale_part")
+    _want(topk_idx, torch.int32, (T, k), "topk_idx")
+    _want(topk_prob, torch.float32, (T, k), "topk_prob")
+    _want(dx, torch.bfloat16, (T, H), "dx")
+    _want(d_logits, torch.float32, (T, E), "d_logits")
+    _check("moe_dispatch_backward_router_scaled", _lib.moe_dispatch_backward_router_scaled(
+        _p(dxp), _p(d_scale_part), _p(row_of), _p(topk_idx), _p(topk_prob), _p(logits),
+        _p(w_router), T, H, E, k, I, _score(score), float(scaling_factor), _p(dx), _p(d_logits),
+        _stream(stream)))
 
 
 # ---- auxiliary load-balancing loss ----------------------------------------------------------

@@ -747,11 +747,15 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       const auto hr = tile_rsrc(c_base(t) + c_row(t) * p.I + t.n0);
       const auto gr = tile_rsrc(p.gu_out ? (const uint16_t*)p.gu_out + (size_t)t.m0 * twoI + t.n0
                                          : (const uint16_t*)p.C);
+      const bool scaled = !FP8 && p.row_scale != nullptr && !last_group(t);
 #pragma unroll
       for (int i = 0; i < C::MB; ++i) {
         const int r0 = (wm + WM * i) * 32;
         float sa = 1.f;
         if (FP8) sa = p.a_scale[t.m0 + (r0 + l32 < t.rows_valid ? r0 + l32 : 0)];
+        // ScaledSwiGLU: the routing weight of this lane's row (lane l holds row l % 32)
+        float rs = 1.f;
+        if (scaled) rs = p.row_scale[t.m0 + (r0 + l32 < t.rows_valid ? r0 + l32 : 0)];
         auto row_ok = [&](int r) { return r0 + r < t.rows_valid; };
 #pragma unroll
         for (int jg0 = 0; jg0 < NH; jg0 += PB) {
@@ -786,6 +790,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
                        for (int r = 0; r < 4; ++r) {
                          const float gg = g[b][4 * q + r];
                          hv[r] = gg * sigmoid_fast(gg) * u[b][4 * q + r];
+                         if (scaled) hv[r] *= rs;
                        }
                        return u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
                      },
@@ -810,9 +815,22 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       const size_t org = (size_t)t.m0 * twoI + t.n0;
       const auto dr = tile_rsrc((const uint16_t*)p.C + org);
       const auto gi = tile_rsrc((const uint16_t*)p.gu_in + org);
+      // ScaledSwiGLU: dh of the scaled h is multiplied by the row's weight before the SwiGLU
+      // backward, and the weight's gradient sum_c dh silu(g) u is accumulated per row over
+      // this wave's 64 columns (one partial per row and 64-column block)
+      const bool scaled = p.row_scale != nullptr;
+      const bool parts = p.row_part != nullptr;
+      static_assert(C::TN == 64, "one 64-column block of partials per wave");
 #pragma unroll
       for (int i = 0; i < C::MB; ++i) {
         const int r0 = (wm + WM * i) * 32;
+        float rsv[NRI], part[NRI];
+#pragma unroll
+        for (int h = 0; h < NRI; ++h) {
+          const int r = rr + RPI * h;
+          rsv[h] = scaled ? p.row_scale[t.m0 + (r0 + r < t.rows_valid ? r0 + r : 0)] : 1.f;
+          part[h] = 0.f;
+        }
 #pragma unroll
         for (int j = 0; j < C::NB; ++j) {
           const int c0 = bcol0(j);
@@ -837,8 +855,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
               const uint32_t gw = gv[x][e >> 1], uw = uv[x][e >> 1];
               const float gg = (e & 1) ? bf16hi(gw) : bf16lo(gw);
               const float uu = (e & 1) ? bf16hi(uw) : bf16lo(uw);
-              const float dh = __uint_as_float(dv[e]);
+              const float dhs = __uint_as_float(dv[e]);
               const float sg = sigmoid_fast(gg);
+              if (parts) part[x % NRI] = fmaf(dhs, gg * sg * uu, part[x % NRI]);
+              const float dh = scaled ? dhs * rsv[x % NRI] : dhs;
               dg[e] = dh * uu * sg * (1.0f + gg * (1.0f - sg));
               du[e] = dh * gg * sg;
             }
@@ -847,6 +867,20 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
             __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])},
                                                   dr, uo[x], 0, 0);
           });
+        }
+        if (parts) {
+          // the LPR lanes of a row group hold its row's pieces: sum them (fixed xor order),
+          // then the group's first lane stores the row's partial of this 64-column block
+          const int slot = (t.n0 + wn * C::TN) / 64, P = p.I / 64;
+#pragma unroll
+          for (int h = 0; h < NRI; ++h) {
+            float v = part[h];
+#pragma unroll
+            for (int o = 1; o < LPR; o <<= 1) v += __shfl_xor(v, o, 64);
+            const int r = rr + RPI * h;
+            if (cc == 0 && r0 + r < t.rows_valid && t.n0 + wn * C::TN < p.I)
+              p.row_part[(size_t)(t.m0 + r0 + r) * P + slot] = v;
+          }
         }
       }
     } else {
@@ -913,7 +947,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   // it (epilogues that read global memory, fp32 output) each tile starts with its own
   // prologue after the previous epilogue.
   constexpr bool CROSS = !FP8 && EPI != EPI_SWIGLU_BWD;
-  const bool cross = CROSS && !p.c_fp32;
+  const bool cross = CROSS && !p.c_fp32 && !(EPI == EPI_SWIGLU && p.row_scale);
   const int s_allow = (EPI == EPI_SWIGLU && p.gu_out) ? 2 : 1;
   auto buf = [&](int s) __attribute__((always_inline)) { return smem + (s % STAGES) * C::STAGE; };
   int gs = 0, gl = 0;

@@ -92,8 +92,12 @@ hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, in
 hipError_t launch_zero_pad_rows(const int32_t* offsets, const int32_t* counts, int E,
                                 int row_bytes, void* rows, float* scale, int32_t* src_of,
                                 hipStream_t s);
+// with row_w: also row_w[row_of[t,j]] = w[t,j] (the routing weight of each routed row)
 hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, const float* prob, int T,
-                               int H, int k, void* xp, hipStream_t s);
+                               int H, int k, void* xp, hipStream_t s, const float* w = nullptr,
+                               float* row_w = nullptr);
+hipError_t launch_row_weights(const int32_t* row_of, const float* w, int T, int k, float* row_w,
+                              hipStream_t s);
 hipError_t launch_scatter_rows_fp8(const void* x, const int32_t* row_of, int T, int H, int k,
                                    uint8_t* xq, float* xscale, hipStream_t s);
 hipError_t launch_combine(const void* y_perm, const int32_t* row_of, const float* prob,
@@ -127,6 +131,16 @@ hipError_t launch_dispatch_bwd_router_input(const void* dxp, const void* x, cons
                                             int H, int E, int k, int score, float scaling,
                                             void* dx, float* d_logits, uint16_t* dls, int mp,
                                             hipStream_t s);
+// Dispatch backward of a layer whose routing weights scale the SwiGLU output (ScaledSwiGLU)
+// and which owns its router projection: d_prob[t,j] = sum over the P = I/64 partials of
+// row row_of[t,j] (row_part [rows, P], fixed order), d_logits (+ split halves), dx =
+// sum_j dxp[row_of[t,j]] + router term.
+hipError_t launch_dispatch_bwd_router_act(const void* dxp, const float* row_part, int P,
+                                          const int32_t* row_of, const int32_t* topk_idx,
+                                          const float* prob, const float* logits,
+                                          const void* w_router, int T, int H, int E, int k,
+                                          int score, float scaling, void* dx, float* d_logits,
+                                          uint16_t* dls, int mp, hipStream_t s);
 hipError_t launch_router_wgrad_reduce(const float* part, int S, int E, int H, int mp, float* dw,
                                       hipStream_t s);
 hipError_t launch_router_split(const float* d_logits, int T, int E, int mp, uint16_t* dls,
@@ -168,6 +182,11 @@ struct GemmParams {
   const void* A_last;
   const void* B_last;
   void* C_last;
+  // ScaledSwiGLU (bf16 only): EPI_SWIGLU multiplies h by row_scale[row] (not the A_last
+  // group's rows); EPI_SWIGLU_BWD multiplies dh by it, and with row_part [rows, I/64]
+  // writes per row and 64-column block sum_c dh[row,c] silu(g) u (dh before the scaling).
+  const float* row_scale;
+  float* row_part;
 };
 hipError_t launch_grouped_gemm(const GemmParams& p, hipStream_t s);
 // Grid cap of the persistent grouped-GEMM launches (0: every resident block).

@@ -43,6 +43,7 @@ struct Layout {
   size_t d_out, dgu, dxp, scratch, scratch_bytes;
   size_t logits, d_logits, router_ws, router_ws_bytes, total;
   size_t mx_col_offsets, dgq, dgq_scale, mx_ta, mx_ta_scale, mx_tb, mx_tb_scale, mx_kp;
+  size_t row_prob, row_part;  // ScaledSwiGLU: weight of each routed row; d_prob partials
   size_t rows;  // rows of the expert-contiguous buffers
 };
 
@@ -97,6 +98,9 @@ Layout make_layout(const moe_problem_t& p) {
   L.d_logits = take(p.router && p.training ? (size_t)p.T * p.E * 4 : 0);
   L.router_ws_bytes = p.router && p.training ? router_wgrad_bytes(p.T, p.H, p.E) : 0;
   L.router_ws = take(L.router_ws_bytes);
+  const bool at_act = p.weight_placement == MOE_PLACE_ACTIVATION;
+  L.row_prob = take(at_act ? N * 4 : 0);
+  L.row_part = take(at_act && p.router && p.training ? N * (size_t)(p.I / 64) * 4 : 0);
   // MXFP8 training: dgu codes (rows), and the token-axis (transposed) operands of the weight
   // gradients, [C, Kp] codes for C up to max(H, I) (A side) and max(H, 2I) (B side)
   const bool mxt = mx && p.training;
@@ -155,9 +159,10 @@ moe_status_t check_problem(const moe_problem_t* p) {
   moe_status_t so = make_router_opts(p->E, p->k, p->score, nullptr, p->num_groups, p->group_topk,
                                      p->scaling_factor, 0, &o);
   if (so != MOE_OK) return so;
-  if (p->weight_placement != MOE_PLACE_COMBINE && p->weight_placement != MOE_PLACE_INPUT)
+  if (p->weight_placement != MOE_PLACE_COMBINE && p->weight_placement != MOE_PLACE_INPUT &&
+      p->weight_placement != MOE_PLACE_ACTIVATION)
     return MOE_ERR_INVALID_ARG;
-  if (p->weight_placement == MOE_PLACE_INPUT && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (p->weight_placement != MOE_PLACE_COMBINE && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (p->align_size < 0) return MOE_ERR_INVALID_ARG;
   if (p->align_size > 4096) return MOE_ERR_UNSUPPORTED;
   if (p->dtype == MOE_FP8_E4M3) {
@@ -412,6 +417,73 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const void* d_out, const void* w_down,
   return hip_status(launch_grouped_gemm(p, S(stream)));
 }
 
+moe_status_t moe_grouped_gemm_swiglu_scaled(const void* xp, const void* w_gu,
+                                            const int32_t* offsets, const float* row_scale, int G,
+                                            int rows, int H, int I, void* h, void* gu_saved,
+                                            void* stream) {
+  if (G <= 0 || rows < 0 || H <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 64 || I % 64 || G > 256) return MOE_ERR_UNSUPPORTED;
+  if (!gemm_offsets_fit(2LL * I, H, 2)) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!ok_ptr(xp) || !ok_ptr(w_gu) || !ok_ptr(offsets) || !ok_ptr(row_scale) || !ok_ptr(h) ||
+      !opt_ptr(gu_saved))
+    return MOE_ERR_INVALID_ARG;
+  GemmParams p{};
+  p.mode = MOE_GEMM_NN;
+  p.epi = EPI_SWIGLU;
+  p.A = xp;
+  p.B = w_gu;
+  p.offsets = offsets;
+  p.G = G;
+  p.rows = rows;
+  p.N = 2 * I;
+  p.K = H;
+  p.C = h;
+  p.I = I;
+  p.gu_out = gu_saved;
+  p.row_scale = row_scale;
+  return hip_status(launch_grouped_gemm(p, S(stream)));
+}
+
+moe_status_t moe_grouped_gemm_swiglu_scaled_bwd(const void* d_out, const void* w_down,
+                                                const int32_t* offsets, const void* gu_saved,
+                                                const float* row_scale, int G, int rows, int H,
+                                                int I, void* dgu, float* d_scale_part,
+                                                void* stream) {
+  if (G <= 0 || rows < 0 || H <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 64 || I % 64 || G > 256) return MOE_ERR_UNSUPPORTED;
+  if (!gemm_offsets_fit(I, H, 2)) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!ok_ptr(d_out) || !ok_ptr(w_down) || !ok_ptr(offsets) || !ok_ptr(gu_saved) ||
+      !ok_ptr(row_scale) || !ok_ptr(dgu) || !opt_ptr(d_scale_part))
+    return MOE_ERR_INVALID_ARG;
+  GemmParams p{};
+  p.mode = MOE_GEMM_NT;
+  p.epi = EPI_SWIGLU_BWD;
+  p.A = d_out;
+  p.B = w_down;
+  p.offsets = offsets;
+  p.G = G;
+  p.rows = rows;
+  p.N = I;
+  p.K = H;
+  p.C = dgu;
+  p.I = I;
+  p.gu_in = gu_saved;
+  p.row_scale = row_scale;
+  p.row_part = d_scale_part;
+  return hip_status(launch_grouped_gemm(p, S(stream)));
+}
+
+moe_status_t moe_permute_probs(const int32_t* row_of, const float* topk_prob, int T, int k,
+                               float* row_prob, void* stream) {
+  if (T < 0 || k <= 0) return MOE_ERR_INVALID_ARG;
+  if (k > 32) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(row_of) || !ok_ptr(topk_prob) || !ok_ptr(row_prob)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_row_weights(row_of, topk_prob, T, k, row_prob, S(stream)));
+}
+
 moe_status_t moe_unpermute_combine(const void* y_perm, const int32_t* row_of,
                                    const float* topk_prob, const void* shared_out, int T,
                                    int H, int k, void* y, void* stream) {
@@ -577,6 +649,28 @@ moe_status_t moe_aux_loss_backward(const float* logits, const int32_t* tokens_pe
     return MOE_ERR_INVALID_ARG;
   return hip_status(launch_aux_loss_bwd(logits, T, E, score, tokens_per_expert, C, d_loss,
                                         d_logits, accumulate, S(stream)));
+}
+
+moe_status_t moe_dispatch_backward_router_scaled(const void* dxp, const float* d_scale_part,
+                                                 const int32_t* row_of, const int32_t* topk_idx,
+                                                 const float* topk_prob, const float* logits,
+                                                 const void* w_router, int T, int H, int E, int k,
+                                                 int I, int score, float scaling_factor, void* dx,
+                                                 float* d_logits, void* stream) {
+  moe_status_t st = check_shape(T, H, E, k);
+  if (st != MOE_OK) return st;
+  if (!valid_score(score) || I <= 0) return MOE_ERR_INVALID_ARG;
+  if (I % 64) return MOE_ERR_UNSUPPORTED;
+  if (!(scaling_factor == scaling_factor) || scaling_factor == INFINITY || scaling_factor == -INFINITY)
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(dxp) || !ok_ptr(d_scale_part) || !ok_ptr(row_of) || !ok_ptr(topk_idx) ||
+      !ok_ptr(topk_prob) || !ok_ptr(w_router) || !ok_ptr(dx) || !ok_ptr(d_logits) ||
+      (score == MOE_SOFTMAX_PRE && !ok_ptr(logits)))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_dispatch_bwd_router_act(
+      dxp, d_scale_part, I / 64, row_of, topk_idx, topk_prob, logits, w_router, T, H, E, k, score,
+      scaling_factor == 0.f ? 1.f : scaling_factor, dx, d_logits, nullptr, 0, S(stream)));
 }
 
 moe_status_t moe_quantize_mxfp8_rows(const void* x, int R, int C, uint8_t* q, uint8_t* scale,
@@ -787,13 +881,15 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   MOE_TRY(launch_dispatch_from_hist(v.topk_idx, T, E, k, chunk_tokens, (int32_t*)v.scratch,
                                     v.counts, v.offsets, v.row_of, v.src_of, s, align,
                                     v.pad_offsets));
-  if (align > 1)  // zero padding rows (fp8: scale 1), src_of -1
-    MOE_TRY(launch_zero_pad_rows(v.offsets, v.counts, E, fp8 ? H : 2 * H, v.xp,
-                                 fp8 ? v.xp_scale : nullptr, v.src_of, s));
   const bool at_input = p->weight_placement == MOE_PLACE_INPUT;
+  const bool at_act = p->weight_placement == MOE_PLACE_ACTIVATION;
+  float* row_prob = at_act ? (float*)((uint8_t*)ws + make_layout(*p).row_prob) : nullptr;
+  if (align > 1)  // zero padding rows (fp8 scale / ScaledSwiGLU weight 1), src_of -1
+    MOE_TRY(launch_zero_pad_rows(v.offsets, v.counts, E, fp8 ? H : 2 * H, v.xp,
+                                 fp8 ? v.xp_scale : row_prob, v.src_of, s));
   if (fp8) MOE_TRY(launch_scatter_rows_fp8(t->x, v.row_of, T, H, k, (uint8_t*)v.xp, v.xp_scale, s));
   else MOE_TRY(launch_scatter_rows(t->x, v.row_of, at_input ? v.topk_prob : nullptr, T, H, k,
-                                   v.xp, s));
+                                   v.xp, s, v.topk_prob, row_prob));
   if (mx) {
     // MXFP8 (te_mixtral's mxfp8 recipe): rows quantised per 32-element block, block-scaled
     // GEMMs; the weight arguments hold codes and scale bytes (moe_quantize_mxfp8_weights)
@@ -804,8 +900,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
     MOE_TRY(launch_mx_quantize_rows(v.h, N, I, (uint8_t*)v.hq, v.hq_scale, s));
     MOE_TRY(launch_mx_gemm(EPI_STORE, v.hq, v.hq_scale, t->w_down,
                            (const uint8_t*)t->w_down_scale, v.offsets, E, N, H, I, 0, v.out, s));
-    MOE_TRY(launch_combine(v.out, v.row_of, at_input ? nullptr : v.topk_prob, nullptr, T, H, k,
-                           t->y, s));
+    MOE_TRY(launch_combine(v.out, v.row_of, v.topk_prob, nullptr, T, H, k, t->y, s));
     return MOE_OK;
   }
   // 3. grouped MLP. A dense shared expert of the routed experts' width runs as one more
@@ -829,6 +924,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   g1.C = v.h;
   g1.I = I;
   g1.gu_out = p->training ? v.gu : nullptr;
+  g1.row_scale = row_prob;  // ScaledSwiGLU: h of routed rows times their weight
   if (fuse_shared) {
     g1.G = E + 1;
     g1.rows = N + T;
@@ -894,8 +990,8 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
     s2.C = v.shared_out;
     MOE_TRY(launch_grouped_gemm(s2, s));
   }
-  // 4. combine
-  MOE_TRY(launch_combine(v.out, v.row_of, at_input ? nullptr : v.topk_prob,
+  // 4. combine (unweighted when the weights already scaled the inputs or the SwiGLU output)
+  MOE_TRY(launch_combine(v.out, v.row_of, at_input || at_act ? nullptr : v.topk_prob,
                          p->shared_I ? v.shared_out : nullptr, T, H, k, t->y, s));
   return MOE_OK;
 }
@@ -923,10 +1019,14 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   const int T = p->T, H = p->H, E = p->E, k = p->k, I = p->I;
   const int N = v.rows;  // T*k, plus the padding rows of a padded dispatch
   const bool at_input = p->weight_placement == MOE_PLACE_INPUT;
+  const bool at_act = p->weight_placement == MOE_PLACE_ACTIVATION;
+  const Layout L = make_layout(*p);
+  float* const row_prob = at_act ? (float*)((uint8_t*)ws + L.row_prob) : nullptr;
+  float* const row_part = at_act && p->router ? (float*)((uint8_t*)ws + L.row_part) : nullptr;
   if (T == 0) {
     // no routed rows: the weight gradients are zero (the dW GEMMs see empty groups)
     MOE_TRY(launch_fill_i32(v.offsets, E + 1, 0, s));
-  } else if (at_input) {
+  } else if (at_input || at_act) {
     // the combine was unweighted: d_out[row_of[t,j]] = dy[t]
     MOE_TRY(launch_scatter_rows(dy, v.row_of, nullptr, T, H, k, v.d_out, s));
   } else if (p->router) {
@@ -943,7 +1043,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   float* const r_part = p->router ? (float*)((uint8_t*)v.router_ws + router_wgrad_dls_bytes(T, E))
                                    : nullptr;
   const float r_scale = p->scaling_factor == 0.f ? 1.f : p->scaling_factor;
-  if (p->router && !at_input)
+  if (p->router && !at_input && !at_act)
     MOE_TRY(launch_router_wgrad(t->x, (const uint16_t*)v.router_ws, T, H, E, r_part, t->dw_router, s));
   if (p->align_size > 1 && T > 0)  // the padding rows of d_out are zero
     MOE_TRY(launch_zero_pad_rows(v.offsets, v.counts, E, 2 * H, v.d_out, nullptr, nullptr, s));
@@ -988,6 +1088,8 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   a.C = v.dgu;
   a.I = I;
   a.gu_in = v.gu;
+  a.row_scale = row_prob;  // ScaledSwiGLU: dh times the row's weight
+  a.row_part = row_part;   // and the weight gradient's partials (router projection)
   if (N > 0) MOE_TRY(launch_grouped_gemm(a, s));
   GemmParams b{};
   b.mode = MOE_GEMM_TN_DW;
@@ -1034,6 +1136,12 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
                                              t->w_router, T, H, E, k, p->score, r_scale, dx,
                                              v.d_logits, (uint16_t*)v.router_ws,
                                              router_split_cols(E), s));
+    MOE_TRY(launch_router_wgrad(t->x, (const uint16_t*)v.router_ws, T, H, E, r_part, t->dw_router, s));
+  } else if (p->router && at_act) {
+    MOE_TRY(launch_dispatch_bwd_router_act(v.dxp, row_part, I / 64, v.row_of, v.topk_idx,
+                                           v.topk_prob, v.logits, t->w_router, T, H, E, k,
+                                           p->score, r_scale, dx, v.d_logits,
+                                           (uint16_t*)v.router_ws, router_split_cols(E), s));
     MOE_TRY(launch_router_wgrad(t->x, (const uint16_t*)v.router_ws, T, H, E, r_part, t->dw_router, s));
   } else if (p->router) {
     MOE_TRY(launch_dispatch_bwd_router(v.dxp, v.row_of, v.topk_idx, v.d_logits, t->w_router, T, H,

@@ -220,16 +220,21 @@ hipError_t launch_dispatch_from_hist(const int32_t* topk_idx, int T, int E, int 
 // ---- row movement ----------------------------------------------------------
 
 // xp[row_of[t,j]] = x[t] (prob == NULL), or bf16(prob[t,j] * x[t]) (combine backward).
+// row_w (nullable): row_w[row_of[t,j]] = w[t,j], the routing weight of every routed row.
 __global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4_t* __restrict__ x,
                                                            const int32_t* __restrict__ row_of,
                                                            const float* __restrict__ prob, int H8,
-                                                           int k, u32x4_t* __restrict__ xp) {
+                                                           int k, u32x4_t* __restrict__ xp,
+                                                           const float* __restrict__ w,
+                                                           float* __restrict__ row_w) {
   __shared__ int rows[32];
   __shared__ float p[32];
   const int t = blockIdx.x;
   if ((int)threadIdx.x < k) {
-    rows[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
+    const int r = row_of[(size_t)t * k + threadIdx.x];
+    rows[threadIdx.x] = r;
     p[threadIdx.x] = prob ? prob[(size_t)t * k + threadIdx.x] : 1.f;
+    if (row_w) row_w[r] = w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
   for (int v = threadIdx.x; v < H8; v += blockDim.x) {
@@ -247,9 +252,27 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4_t* __rest
 }
 
 hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, const float* prob, int T,
-                               int H, int k, void* xp, hipStream_t s) {
+                               int H, int k, void* xp, hipStream_t s, const float* w,
+                               float* row_w) {
   if (T == 0) return hipSuccess;
-  scatter_rows_kernel<<<T, 256, 0, s>>>((const u32x4_t*)x, row_of, prob, H / 8, k, (u32x4_t*)xp);
+  scatter_rows_kernel<<<T, 256, 0, s>>>((const u32x4_t*)x, row_of, prob, H / 8, k, (u32x4_t*)xp,
+                                        w, row_w);
+  return hipGetLastError();
+}
+
+// row_w[row_of[t,j]] = w[t,j] alone (the permuted routing weights).
+__global__ __launch_bounds__(256) void row_weights_kernel(const int32_t* __restrict__ row_of,
+                                                          const float* __restrict__ w, int n,
+                                                          float* __restrict__ row_w) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) row_w[row_of[i]] = w[i];
+}
+
+hipError_t launch_row_weights(const int32_t* row_of, const float* w, int T, int k, float* row_w,
+                              hipStream_t s) {
+  const int n = T * k;
+  if (n == 0) return hipSuccess;
+  row_weights_kernel<<<(n + 255) / 256, 256, 0, s>>>(row_of, w, n, row_w);
   return hipGetLastError();
 }
 

@@ -298,9 +298,14 @@ __global__ __launch_bounds__(256) void combine_bwd_router_kernel(
 // backward follows (router_score_bwd), and pass 2 writes dx[t] = bf16(sum_j q_j dxp[row_j]
 // + sum_j d_logits[t,e_j] W_r[e_j]) (fp32 sum, one rounding; the dxp rows were just read,
 // so the second read comes from cache).
-template <int KM>
+// ACT (ScaledSwiGLU: the weights scaled the SwiGLU output): d_prob_j is the sum of the P
+// per-64-column partials of row row_of[t,j] written by the SwiGLU-backward epilogue
+// (threads take slots tid, tid + 256, ...; the block reduction adds them in a fixed
+// order), and dx[t] = bf16(sum_j dxp[row_j] + router term), unweighted.
+template <int KM, bool ACT>
 __global__ __launch_bounds__(256) void dispatch_bwd_router_input_kernel(
     const u32x4_t* __restrict__ dxp, const u32x4_t* __restrict__ x,
+    const float* __restrict__ row_part, int P,
     const int32_t* __restrict__ row_of, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ prob, const float* __restrict__ logits,
     const u32x4_t* __restrict__ w_router, int H8, int E, int k, int score, float scaling,
@@ -317,7 +322,16 @@ __global__ __launch_bounds__(256) void dispatch_bwd_router_input_kernel(
   float dot[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) dot[j] = 0.f;
-  for (int v = tid; v < H8; v += 256) {
+  if constexpr (ACT) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j >= k) continue;
+      float a = 0.f;
+      for (int q = tid; q < P; q += 256) a += row_part[(size_t)rows[j] * P + q];
+      dot[j] = a;
+    }
+  }
+  for (int v = tid; v < (ACT ? 0 : H8); v += 256) {
     const u32x4_t xv = x[(size_t)t * H8 + v];
 #pragma unroll
     for (int j0 = 0; j0 < KM; j0 += 8) {
@@ -350,7 +364,7 @@ __global__ __launch_bounds__(256) void dispatch_bwd_router_input_kernel(
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     for (int j = 0; j < k; ++j) {
       const u32x4_t o = dxp[(size_t)rows[j] * H8 + v];
-      const float q = p[j];
+      const float q = ACT ? 1.f : p[j];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         acc[2 * d] = fmaf(q, bf16lo(o[d]), acc[2 * d]);
@@ -381,12 +395,30 @@ hipError_t launch_dispatch_bwd_router_input(const void* dxp, const void* x, cons
                                             hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (k <= 8)
-    dispatch_bwd_router_input_kernel<8><<<T, 256, 0, s>>>(
-        (const u32x4_t*)dxp, (const u32x4_t*)x, row_of, topk_idx, prob, logits,
+    dispatch_bwd_router_input_kernel<8, false><<<T, 256, 0, s>>>(
+        (const u32x4_t*)dxp, (const u32x4_t*)x, nullptr, 0, row_of, topk_idx, prob, logits,
         (const u32x4_t*)w_router, H / 8, E, k, score, scaling, (u32x4_t*)dx, d_logits, dls, mp);
   else
-    dispatch_bwd_router_input_kernel<32><<<T, 256, 0, s>>>(
-        (const u32x4_t*)dxp, (const u32x4_t*)x, row_of, topk_idx, prob, logits,
+    dispatch_bwd_router_input_kernel<32, false><<<T, 256, 0, s>>>(
+        (const u32x4_t*)dxp, (const u32x4_t*)x, nullptr, 0, row_of, topk_idx, prob, logits,
+        (const u32x4_t*)w_router, H / 8, E, k, score, scaling, (u32x4_t*)dx, d_logits, dls, mp);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_bwd_router_act(const void* dxp, const float* row_part, int P,
+                                          const int32_t* row_of, const int32_t* topk_idx,
+                                          const float* prob, const float* logits,
+                                          const void* w_router, int T, int H, int E, int k,
+                                          int score, float scaling, void* dx, float* d_logits,
+                                          uint16_t* dls, int mp, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (k <= 8)
+    dispatch_bwd_router_input_kernel<8, true><<<T, 256, 0, s>>>(
+        (const u32x4_t*)dxp, nullptr, row_part, P, row_of, topk_idx, prob, logits,
+        (const u32x4_t*)w_router, H / 8, E, k, score, scaling, (u32x4_t*)dx, d_logits, dls, mp);
+  else
+    dispatch_bwd_router_input_kernel<32, true><<<T, 256, 0, s>>>(
+        (const u32x4_t*)dxp, nullptr, row_part, P, row_of, topk_idx, prob, logits,
         (const u32x4_t*)w_router, H / 8, E, k, score, scaling, (u32x4_t*)dx, d_logits, dls, mp);
   return hipGetLastError();
 }

@@ -84,7 +84,8 @@ def check_fp8(got, ref, name, rel_l2=5e-2):
 class GpuMoE:
     """Uploads one workload's inputs and runs moe_forward / moe_backward through the C ABI."""
 
-    def __init__(self, w, d, training=None, canary=True, router=False, mx=False):
+    def __init__(self, w, d, training=None, canary=True, router=False, mx=False,
+                 placement=M.MOE_PLACE_COMBINE):
         self.w, self.d = w, d
         T = d["T"]
         self.T = T
@@ -92,7 +93,7 @@ class GpuMoE:
         self.router = router
         self.dtype = M.MOE_MXFP8 if mx else (M.MOE_FP8_E4M3 if w.fp8 else M.MOE_BF16)
         self.prob = M.problem(T, w.H, w.E, w.k, w.I, w.score, w.shared_I, self.dtype, self.training,
-                              router)
+                              router, weight_placement=placement)
         self.w_router = dev_bf16(d["w_router"]) if router else None
         self.dw_router = torch.full((w.E, w.H), float("nan"), device="cuda") if router else None
         self.x = dev_bf16(d["x"])
