@@ -197,6 +197,22 @@ moe_status_t moe_permute(const void* x, const int32_t* topk_idx, int T, int H, i
                          int32_t* row_of, int32_t* src_of, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* moe_permute for callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops or harnesses that forbid hipMalloc): the same arguments and results minus
+ * the workspace. The dispatch scratch lives in a device array of the library of
+ * moe_permute_noalloc_limit() bytes (4 MiB) that each GPU holds until the process ends; the
+ * call allocates nothing. Sizes whose scratch, moe_permute_workspace_bytes(T, E, k), exceeds
+ * the limit return MOE_ERR_UNSUPPORTED (e.g. E = 256 allows T*k up to 524032). Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (several streams, or a
+ * graph replay during an eager call) race and must be serialised by the caller. */
+moe_status_t moe_permute_noalloc(const void* x, const int32_t* topk_idx, int T, int H, int E,
+                                 int k, int out_dtype, void* xp, float* xp_scale,
+                                 int32_t* offsets, int32_t* row_of, int32_t* src_of,
+                                 void* stream);
+
+/* Bytes of the device scratch array moe_permute_noalloc uses. */
+size_t moe_permute_noalloc_limit(void);
+
 /* Rows a padded dispatch needs at most: T*k + E*(align-1) (align > 1), else T*k (guide,
  * "Receive buffer": counts of 129 and 127 need 384 rows at alignment 128). */
 size_t moe_padded_rows(int T, int E, int k, int align);

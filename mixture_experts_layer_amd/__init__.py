@@ -37,6 +37,7 @@ EXPORTS = [
     "moe_aux_loss_scores", "moe_aux_loss_workspace_bytes", "moe_aux_loss",
     "moe_aux_loss_backward", "moe_grouped_gemm_swiglu_scaled",
     "moe_grouped_gemm_swiglu_scaled_bwd", "moe_permute_probs", "moe_dispatch_backward_router_scaled",
+    "moe_permute_noalloc", "moe_permute_noalloc_limit",
 ]
 
 
@@ -134,6 +135,8 @@ def _load():
         "moe_grouped_gemm_swiglu_scaled": ([vp, vp, vp, vp, i, i, i, i, vp, vp, vp], i),
         "moe_grouped_gemm_swiglu_scaled_bwd": ([vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp], i),
         "moe_permute_probs": ([vp, vp, i, i, vp, vp], i),
+        "moe_permute_noalloc": ([vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp], i),
+        "moe_permute_noalloc_limit": ([], sz),
         "moe_dispatch_backward_router_scaled": ([vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
                                                  ctypes.c_float, vp, vp, vp], i),
     }
@@ -269,6 +272,26 @@ def moe_permute(x, topk_idx, E, xp, offsets, row_of, src_of, ws, out_dtype=MOE_B
     _check("moe_permute", _lib.moe_permute(
         _p(x), _p(topk_idx), T, H, E, k, out_dtype, _p(xp), _p(xp_scale), _p(offsets),
         _p(row_of), _p(src_of), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_permute_noalloc(x, topk_idx, E, xp, offsets, row_of, src_of, out_dtype=MOE_BF16,
+                        xp_scale=None, stream=None):
+    """moe_permute without a workspace: the scratch is the library's own device array."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    _want(x, torch.bfloat16, (T, H), "x")
+    _want(topk_idx, torch.int32, (T, k), "topk_idx")
+    _want(xp, torch.bfloat16 if out_dtype == MOE_BF16 else torch.uint8, (T * k, H), "xp")
+    _want(offsets, torch.int32, (E + 1,), "offsets")
+    _want(row_of, torch.int32, (T, k), "row_of")
+    _want(src_of, torch.int32, (T * k,), "src_of")
+    _check("moe_permute_noalloc", _lib.moe_permute_noalloc(
+        _p(x), _p(topk_idx), T, H, E, k, out_dtype, _p(xp), _p(xp_scale), _p(offsets),
+        _p(row_of), _p(src_of), _stream(stream)))
+
+
+def moe_permute_noalloc_limit():
+    return int(_lib.moe_permute_noalloc_limit())
 
 
 def moe_padded_rows(T, E, k, align):

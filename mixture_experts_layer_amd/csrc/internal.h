@@ -64,6 +64,13 @@ hipError_t launch_aux_loss_bwd(const float* logits, int T, int E, int score, con
                                float C, const float* d_loss, float* d_logits, int accumulate,
                                hipStream_t s);
 
+// noalloc.hip: moe_permute with its scratch in the library's device array
+size_t permute_noalloc_scratch_limit();
+hipError_t launch_permute_noalloc(const void* x, const int32_t* topk_idx, int T, int H, int E,
+                                  int k, int out_dtype, void* xp, float* xp_scale,
+                                  int32_t* offsets, int32_t* row_of, int32_t* src_of,
+                                  hipStream_t s);
+
 // router.hip
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int score,
                               int32_t* topk_idx, float* topk_prob, int32_t* counts,

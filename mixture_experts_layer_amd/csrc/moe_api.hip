@@ -281,6 +281,27 @@ moe_status_t moe_permute(const void* x, const int32_t* topk_idx, int T, int H, i
   return MOE_OK;
 }
 
+moe_status_t moe_permute_noalloc(const void* x, const int32_t* topk_idx, int T, int H, int E,
+                                 int k, int out_dtype, void* xp, float* xp_scale,
+                                 int32_t* offsets, int32_t* row_of, int32_t* src_of,
+                                 void* stream) {
+  moe_status_t st = check_shape(T, H, E, k);
+  if (st != MOE_OK) return st;
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (!ok_ptr(offsets)) return MOE_ERR_INVALID_ARG;
+  if (permute_scratch_bytes(T, E, k) > permute_noalloc_scratch_limit())
+    return MOE_ERR_UNSUPPORTED;
+  if (T > 0) {
+    if (!ok_ptr(x) || !ok_ptr(topk_idx) || !ok_ptr(xp) || !ok_ptr(row_of) || !ok_ptr(src_of))
+      return MOE_ERR_INVALID_ARG;
+    if (out_dtype == MOE_FP8_E4M3 && !ok_ptr(xp_scale)) return MOE_ERR_INVALID_ARG;
+  }
+  return hip_status(launch_permute_noalloc(x, topk_idx, T, H, E, k, out_dtype, xp, xp_scale,
+                                           offsets, row_of, src_of, S(stream)));
+}
+
+size_t moe_permute_noalloc_limit(void) { return permute_noalloc_scratch_limit(); }
+
 size_t moe_padded_rows(int T, int E, int k, int align) {
   if (T < 0 || E <= 0 || k <= 0 || align < 0) return 0;
   return (size_t)T * k + (align > 1 ? (size_t)E * (align - 1) : 0);
