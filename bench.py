@@ -187,10 +187,10 @@ def main():
     ap.add_argument("--expert-bias", action="store_true",
                     help="an expert selection bias (sigmoid / sqrtsoftplus scores only)")
     ap.add_argument("--score", choices=["softmax_pre_renorm", "softmax_post", "sigmoid",
-                                        "sqrtsoftplus"],
+                                        "sqrtsoftplus", "softmax_pre"],
                     help="override the workload's score function")
     ap.add_argument("--scaling", type=float, default=1.0, help="routing-weight scaling factor")
-    ap.add_argument("--placement", choices=["combine", "input"], default="combine",
+    ap.add_argument("--placement", choices=["combine", "input", "activation"], default="combine",
                     help="apply the routing weights to the expert outputs (combine) or inputs")
     ap.add_argument("--align", type=int, default=0, help="padded dispatch alignment (rows)")
     ap.add_argument("--mx", action="store_true",
@@ -280,7 +280,8 @@ def main():
     groups = args.groups or (0, 0)
     e_bias = (torch.randn(w.E, generator=torch.Generator().manual_seed(0)) * 0.1).to(dev) \
         if args.expert_bias else None
-    placement = M.MOE_PLACE_INPUT if args.placement == "input" else M.MOE_PLACE_COMBINE
+    placement = {"combine": M.MOE_PLACE_COMBINE, "input": M.MOE_PLACE_INPUT,
+                 "activation": M.MOE_PLACE_ACTIVATION}[args.placement]
     prob = M.problem(w.T, w.H, w.E, w.k, w.I, w.score, w.shared_I, dtype, training, router,
                      groups[0], groups[1], args.scaling, placement, args.align)
     ws = torch.zeros(M.moe_workspace_bytes(prob), dtype=torch.uint8, device=dev)
@@ -521,7 +522,17 @@ def main():
         tc = time.perf_counter() - tc0
         threads = max([p.get("num_threads", 1) for p in threadpool_info()
                        if p.get("user_api") == "blas"] or [1])
-        cpu = {"value": round(S / tc, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), model)
+        except OSError:
+            pass
+        # cores: the BLAS threads the oracle's float64 products ran on (its only parallel
+        # part); host_cpus: every logical CPU the box shows
+        cpu = {"value": round(S / tc, 2), "unit": "tokens/s", "cores": threads,
+               "host_cpus": os.cpu_count(), "cpu_model": model, "kind": "oracle",
                "sample": (f"the whole workload ({S} tokens)" if S == w.T else
                           f"first {S} of the {w.T} tokens") + ", full weights, "
                          f"{'forward+backward' if training else 'forward'}; {tc:.1f} s"}
@@ -543,13 +554,14 @@ def main():
         "config": {"workload": f"{w.name}-shaped MoE block " + ("with its router projection " if router else "")
                    + ("forward+backward" if training else "forward"),
                    "T": w.T, "H": w.H, "E": w.E, "top_k": w.k, "I": w.I, "shared_I": w.shared_I,
-                   "score": ["softmax_pre_renorm", "softmax_post", "sigmoid", "sqrtsoftplus"][w.score],
+                   "score": ["softmax_pre_renorm", "softmax_post", "sigmoid", "sqrtsoftplus",
+                             "softmax_pre"][w.score],
                    "parallelism": "single GPU", "active_experts": active,
                    "launch": "hip_graph" if graph is not None else "eager", "router": router,
                    **({"groups": list(groups)} if groups[0] else {}),
                    **({"expert_bias": True} if e_bias is not None else {}),
                    **({"scaling": args.scaling} if args.scaling != 1.0 else {}),
-                   **({"placement": "input"} if placement == M.MOE_PLACE_INPUT else {}),
+                   **({"placement": args.placement} if placement != M.MOE_PLACE_COMBINE else {}),
                    **({"align": args.align} if args.align > 1 else {})},
         "grouped_gemm_tflops": round(gemm_flops / gemm_time / 1e12, 1),
         "grouped_gemm_mfma_frac": round(gemm_flops / gemm_time / 1e12 / peak_tf, 4),
