@@ -202,7 +202,7 @@ moe_status_t moe_permute(const void* x, const int32_t* topk_idx, int T, int H, i
  * the workspace. The dispatch scratch lives in a device array of the library of
  * moe_permute_noalloc_limit() bytes (4 MiB) that each GPU holds until the process ends; the
  * call allocates nothing. Sizes whose scratch, moe_permute_workspace_bytes(T, E, k), exceeds
- * the limit return MOE_ERR_UNSUPPORTED (e.g. E = 256 allows T*k up to 524032). Every call
+ * the limit return MOE_ERR_UNSUPPORTED (e.g. E = 256 allows T*k up to 1048320). Every call
  * on one GPU shares that GPU's array: calls that overlap on one GPU (several streams, or a
  * graph replay during an eager call) race and must be serialised by the caller. */
 moe_status_t moe_permute_noalloc(const void* x, const int32_t* topk_idx, int T, int H, int E,

@@ -326,7 +326,7 @@ moe_status_t moe_permute_padded(const void* x, const int32_t* topk_idx, int T, i
   }
   hipStream_t s = S(stream);
   const int nchunks = (T * k + kPermChunk - 1) / kPermChunk;
-  int32_t* counts = (int32_t*)ws + (size_t)2 * nchunks * E;  // after histograms and row bases
+  int32_t* counts = (int32_t*)ws + (size_t)nchunks * E;  // after the histograms
   MOE_TRY(launch_dispatch_meta(topk_idx, T, E, k, offsets, row_of, src_of, ws, s, align,
                                pad_offsets, counts));
   if (T == 0) return MOE_OK;

@@ -6,14 +6,15 @@
 // contributions with the routing weights in the same pass.
 //
 // Dispatch metadata is a stable counting sort of the flattened [T,k] choices by expert:
-//   1. per-chunk histograms over experts: dispatch_hist (chunks of 1024 entries, LDS
+//   1. per-chunk histograms over experts: dispatch_hist (chunks of 256 entries, LDS
 //      atomics) for a given topk_idx, or written by the router itself inside the layer
 //      (chunks of whole tokens, see router.hip);
-//   2. dispatch_scan  : one block; per-expert totals (the counts), offsets[e] = their
-//                       exclusive scan, and each chunk's starting row per expert;
-//   3. dispatch_rank  : one wave per chunk walks its entries in order; lanes that chose
-//                       the same expert find each other with 9 ballots (one per bit of the
-//                       id), so a row is chunk_base + rank among the earlier lanes.
+//   2. dispatch_rank_scan: one block per chunk reads every chunk's histogram and forms the
+//      per-expert totals (the counts), offsets[e] = their exclusive scan and the chunk's
+//      starting row per expert itself (no serial scan launch); one wave then walks the
+//      chunk's entries in order, and lanes that chose the same expert find each other with
+//      9 ballots (one per bit of the id), so a row is the chunk's base + rank among the
+//      earlier lanes.
 // No atomics decide any order, so the layout is deterministic and matches a stable sort.
 // Row copies read each token row once and write its k destination rows with 16-byte
 // vector accesses (scatter form: x is read exactly once).
@@ -33,8 +34,8 @@ size_t permute_scratch_bytes(int T, int E, int k) {
   const size_t a = (n + kPermChunk - 1) / kPermChunk;
   const int ct = router_chunk_tokens(T);
   const size_t b = ((size_t)T + ct - 1) / ct;
-  // per-chunk histograms and row bases, then the per-expert counts of a padded dispatch
-  return (2 * (a > b ? a : b) + 1) * (size_t)E * sizeof(int32_t);
+  // per-chunk histograms, then the per-expert counts of a padded dispatch
+  return ((a > b ? a : b) + 1) * (size_t)E * sizeof(int32_t);
 }
 
 __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ idx, int n,
@@ -51,115 +52,106 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
   for (int e = threadIdx.x; e < E; e += 256) partial[(size_t)blockIdx.x * E + e] = h[e];
 }
 
-// One block of 1024 threads: thread (part, e), e < EP (E rounded up to 64, 128 or 256),
-// part < 1024/EP, owns a contiguous run of the chunks of expert e. It loads its run in
-// batches of SCAN_BATCH independent loads (kept in registers when the run fits one batch),
-// sums them; totals -> counts and offsets (exclusive scan over e); then each thread writes
-// the running row base of its chunks.
-constexpr int SCAN_BATCH = 64;
-// align > 1 (padded dispatch, guide "Padding and alignment"): every expert block is
-// rounded up to a multiple of align rows; offsets are the padded block starts and
-// pad_offsets[e] (when given) the padding before block e.
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ partial,
-                                                             int nchunks, int E,
-                                                             int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ chunk_base,
-                                                             int align,
-                                                             int32_t* __restrict__ pad_offsets) {
-  __shared__ int psum[1024];
-  __shared__ int s[256];
-  const int EP = E <= 64 ? 64 : (E <= 128 ? 128 : 256);
-  const int P = 1024 / EP;
-  const int e = threadIdx.x % EP, part = threadIdx.x / EP;
-  const int L = (nchunks + P - 1) / P;
-  const int c0 = part * L, c1 = min(nchunks, c0 + L);
-  int v[SCAN_BATCH];
-  int sum = 0;
-  if (e < E) {
-    for (int b = c0; b < c1; b += SCAN_BATCH) {
-#pragma unroll
-      for (int i = 0; i < SCAN_BATCH; ++i) v[i] = b + i < c1 ? partial[(size_t)(b + i) * E + e] : 0;
-#pragma unroll
-      for (int i = 0; i < SCAN_BATCH; ++i) sum += v[i];
-    }
-  }
-  psum[threadIdx.x] = sum;
-  __syncthreads();
-  int tot = 0, before = 0;
-  for (int q = 0; q < P; ++q) {
-    const int x = psum[q * EP + e];
-    tot += x;
-    if (q < part) before += x;
-  }
-  // inclusive scan over e of the (padded) block sizes: within each wave by shuffles, then
-  // the wave totals (at most four waves: EP <= 256) added from LDS
-  __shared__ int wtot[4];
-  const int ptot = align > 1 ? (tot + align - 1) / align * align : tot;
-  auto scan = [&](int val) -> int {  // returns the inclusive scan, s[] holds it for every e
-    int incl = e < E ? val : 0;
-    if (part == 0) {
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if ((e & 63) >= o) incl += y;
-      }
-      if ((e & 63) == 63) wtot[e >> 6] = incl;
-    }
-    __syncthreads();
-    if (part == 0) {
-      for (int q = 0; q < (e >> 6); ++q) incl += wtot[q];
-      s[e] = incl;
-    }
-    __syncthreads();
-    return s[e];
-  };
-  if (pad_offsets) {
-    const int pincl = scan(ptot - tot);
-    if (part == 0 && e < E) pad_offsets[e] = pincl - (ptot - tot);
-    __syncthreads();
-  }
-  const int excl = scan(ptot) - ptot;
-  if (part == 0 && e < E) {
-    offsets[e] = excl;
-    if (counts) counts[e] = tot;
-  }
-  if ((int)threadIdx.x == EP - 1) offsets[E] = s[EP - 1];
-  if (e < E) {
-    int run = excl + before;
-    if (c1 - c0 <= SCAN_BATCH) {  // the run is still in registers
-#pragma unroll
-      for (int i = 0; i < SCAN_BATCH; ++i)
-        if (c0 + i < c1) {
-          chunk_base[(size_t)(c0 + i) * E + e] = run;
-          run += v[i];
-        }
-    } else {
-      for (int c = c0; c < c1; ++c) {
-        chunk_base[(size_t)c * E + e] = run;
-        run += partial[(size_t)c * E + e];
-      }
-    }
-  }
-}
-
-__global__ __launch_bounds__(64) void dispatch_rank_kernel(const int32_t* __restrict__ idx, int n,
-                                                           int k, int E, int chunk_entries,
-                                                           const int32_t* __restrict__ chunk_base,
-                                                           int32_t* __restrict__ row_of,
-                                                           int32_t* __restrict__ src_of) {
-  __shared__ int base[256];
-  const int lane = threadIdx.x;
+// One block of 256 threads per chunk of the flattened [T,k] choices. The chunk's row base
+// per expert, offsets[e] + (entries of e in earlier chunks), is computed here from every
+// chunk's histogram (partial [nchunks][E]; each block reads them all from L2), so no
+// separate scan launch orders the blocks. Units of W experts (16-byte loads when E % 4 == 0)
+// are spread over the threads, the threads of a unit splitting the chunks; their sums meet
+// in LDS and are added in a fixed order, then the (padded) totals are scanned over the
+// experts. Block 0 writes counts, offsets (and pad_offsets). The chunk's entries are then
+// ranked 256 at a time, one per thread: lanes of a wave that chose the same expert find each
+// other with 9 ballots (one per bit of the id), the waves' per-expert counts meet in LDS, and
+// an entry's row is the base + the entries of its expert in earlier waves + earlier lanes of
+// its wave (a stable counting sort: no atomics decide the order).
+template <int W>
+__global__ __launch_bounds__(256) void dispatch_rank_scan_kernel(
+    const int32_t* __restrict__ idx, int n, int k, int E, int nchunks, int chunk_entries,
+    const int32_t* __restrict__ partial, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_of, int32_t* __restrict__ src_of,
+    int align, int32_t* __restrict__ pad_offsets) {
+  __shared__ int s_tot[1024], s_bef[1024];  // [group][expert], NG * E <= 256 * W
+  __shared__ int base[256], wsum[4], cnt[4][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x;
-  for (int e = lane; e < E; e += 64) base[e] = chunk_base[(size_t)c * E + e];
+  // the first 256 entries of the chunk, requested before the histogram reads
+  const int f0 = c * chunk_entries + tid;
+  int e_next = (tid < chunk_entries && f0 < n) ? idx[f0] : 0x1ff;
+  const int NU = (E + W - 1) / W;  // units of W experts
+  const int NG = 256 / NU;          // thread groups splitting the chunks
+  const int u = tid % NU, gr = tid / NU;
+  if (gr < NG) {
+    int tot[W], bef[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) tot[w] = bef[w] = 0;
+    for (int cc = gr; cc < nchunks; cc += NG) {
+      int v[W];
+      if constexpr (W == 4) {
+        const int4 q = *(const int4*)(partial + (size_t)cc * E + 4 * u);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+      } else {
+        v[0] = partial[(size_t)cc * E + u];
+      }
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        tot[w] += v[w];
+        bef[w] += cc < c ? v[w] : 0;
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      s_tot[gr * E + W * u + w] = tot[w];
+      s_bef[gr * E + W * u + w] = bef[w];
+    }
+  }
   __syncthreads();
+  // per expert (thread e): the group sums in order, then the padded size
+  int tot = 0, bef = 0;
+  if (tid < E)
+    for (int q = 0; q < NG; ++q) {
+      tot += s_tot[q * E + tid];
+      bef += s_bef[q * E + tid];
+    }
+  const int ptot = tid < E ? (align > 1 ? (tot + align - 1) / align * align : tot) : 0;
+  // exclusive scan over the experts of the padded sizes (and of the padding)
+  int incl = ptot, pincl = ptot - (tid < E ? tot : 0);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64), z = __shfl_up(pincl, o, 64);
+    if (lane >= o) {
+      incl += y;
+      pincl += z;
+    }
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  for (int q = 0; q < wave; ++q) incl += wsum[q];
+  const int excl = incl - ptot;
+  if (tid < E) base[tid] = excl + bef;
+  if (c == 0) {
+    if (tid < E) {
+      offsets[tid] = excl;
+      if (counts) counts[tid] = tot;
+    }
+    if (tid == 255) offsets[E] = incl;  // threads past E add nothing: incl is the total
+    if (pad_offsets) {
+      __syncthreads();
+      if (lane == 63) wsum[wave] = pincl;
+      __syncthreads();
+      for (int q = 0; q < wave; ++q) pincl += wsum[q];
+      if (tid < E) pad_offsets[tid] = pincl - (ptot - tot);
+    }
+  }
   const uint64_t lt = lanemask_lt();
-  const int iters = (chunk_entries + 63) / 64;
-  for (int it = 0; it < iters; ++it) {
-    const int off = it * 64 + lane;
+  for (int g0 = 0; g0 < chunk_entries; g0 += 256) {
+    const int off = g0 + tid;
     const int f = c * chunk_entries + off;
     const bool valid = off < chunk_entries && f < n;
-    const int e = valid ? idx[f] : 0x1ff;  // 9-bit sentinel never equals a real id (< 256)
+    const int e = e_next;  // 9-bit sentinel 0x1ff for no entry: never a real id (< 256)
+    if (g0 + 256 < chunk_entries) {  // the next 256 entries, requested early
+      const int fn = f + 256;
+      e_next = (off + 256 < chunk_entries && fn < n) ? idx[fn] : 0x1ff;
+    }
+    cnt[0][tid] = cnt[1][tid] = cnt[2][tid] = cnt[3][tid] = 0;
     uint64_t peers = ~0ull;
 #pragma unroll
     for (int b = 0; b < 9; ++b) {
@@ -167,16 +159,34 @@ __global__ __launch_bounds__(64) void dispatch_rank_kernel(const int32_t* __rest
       const uint64_t bal = __ballot(bit);
       peers &= bit ? bal : ~bal;
     }
-    const int rank = __popcll(peers & lt);
+    __syncthreads();  // counters cleared, base updated by the previous round
+    // the last lane of each group of equal ids stores the wave's count of that id
+    if (valid && (peers >> lane) == 1ull) cnt[wave][e] = __popcll(peers);
+    __syncthreads();
     if (valid) {
-      const int r = base[e] + rank;
+      int r = base[e] + __popcll(peers & lt);
+      for (int w = 0; w < wave; ++w) r += cnt[w][e];
       row_of[f] = r;
       src_of[r] = f / k;
     }
     __syncthreads();
-    if (valid && (peers >> lane) == 1ull) base[e] += __popcll(peers);  // last lane of the group
-    __syncthreads();
+    if (tid < E) base[tid] += (cnt[0][tid] + cnt[1][tid]) + (cnt[2][tid] + cnt[3][tid]);
   }
+}
+
+hipError_t launch_rank_scan(const int32_t* idx, int n, int k, int E, int nchunks,
+                            int chunk_entries, const int32_t* partial, int32_t* counts,
+                            int32_t* offsets, int32_t* row_of, int32_t* src_of, int align,
+                            int32_t* pad_offsets, hipStream_t s) {
+  if (E % 4 == 0)
+    dispatch_rank_scan_kernel<4><<<nchunks, 256, 0, s>>>(idx, n, k, E, nchunks, chunk_entries,
+                                                         partial, counts, offsets, row_of, src_of,
+                                                         align, pad_offsets);
+  else
+    dispatch_rank_scan_kernel<1><<<nchunks, 256, 0, s>>>(idx, n, k, E, nchunks, chunk_entries,
+                                                         partial, counts, offsets, row_of, src_of,
+                                                         align, pad_offsets);
+  return hipGetLastError();
 }
 
 hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, int32_t* offsets,
@@ -185,18 +195,14 @@ hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, in
   const int n = T * k;
   const int nchunks = (n + kPermChunk - 1) / kPermChunk;
   int32_t* partial = (int32_t*)scratch;
-  int32_t* chunk_base = partial + (size_t)nchunks * E;
   if (n == 0) {
     hipError_t e = pad_offsets ? launch_fill_i32(pad_offsets, E, 0, s) : hipSuccess;
     if (e == hipSuccess && counts) e = launch_fill_i32(counts, E, 0, s);
     return e == hipSuccess ? launch_fill_i32(offsets, E + 1, 0, s) : e;
   }
   dispatch_hist_kernel<<<nchunks, 256, 0, s>>>(topk_idx, n, E, partial);
-  dispatch_scan_kernel<<<1, 1024, 0, s>>>(partial, nchunks, E, counts, offsets, chunk_base, align,
-                                          pad_offsets);
-  dispatch_rank_kernel<<<nchunks, 64, 0, s>>>(topk_idx, n, k, E, kPermChunk, chunk_base, row_of,
-                                              src_of);
-  return hipGetLastError();
+  return launch_rank_scan(topk_idx, n, k, E, nchunks, kPermChunk, partial, counts, offsets, row_of,
+                          src_of, align, pad_offsets, s);
 }
 
 hipError_t launch_dispatch_from_hist(const int32_t* topk_idx, int T, int E, int k, int chunk_tokens,
@@ -209,12 +215,8 @@ hipError_t launch_dispatch_from_hist(const int32_t* topk_idx, int T, int E, int 
     return e == hipSuccess ? launch_fill_i32(offsets, E + 1, 0, s) : e;
   }
   const int nchunks = (T + chunk_tokens - 1) / chunk_tokens;
-  int32_t* chunk_base = partial + (size_t)nchunks * E;
-  dispatch_scan_kernel<<<1, 1024, 0, s>>>(partial, nchunks, E, counts, offsets, chunk_base, align,
-                                          pad_offsets);
-  dispatch_rank_kernel<<<nchunks, 64, 0, s>>>(topk_idx, n, k, E, chunk_tokens * k, chunk_base,
-                                              row_of, src_of);
-  return hipGetLastError();
+  return launch_rank_scan(topk_idx, n, k, E, nchunks, chunk_tokens * k, partial, counts, offsets,
+                          row_of, src_of, align, pad_offsets, s);
 }
 
 // ---- row movement ----------------------------------------------------------
