@@ -163,6 +163,26 @@ def measured_traffic(stage, workload):
     return data["bytes_per_launch"].get(stage)
 
 
+def step_order(training, mx, fp8, router):
+    """Stage names in the order moe_forward / moe_backward enqueue their kernels."""
+    fwd = (["router_logits"] if router else []) + ["router", "permute"]
+    if mx:
+        fwd += ["quantize_x", "gemm1_swiglu", "quantize_h", "gemm2", "combine"]
+    else:
+        fwd += ["gemm1_swiglu"] + (["quantize_h"] if fp8 else []) + ["gemm2", "combine"]
+    if not training:
+        return fwd
+    bwd = ["combine_bwd_router", "router_wgrad"] if router else ["combine_bwd"]
+    if mx:
+        bwd += ["quantize_dout", "gemm2_bwd_swiglu", "quantize_dgu", "gemm1_bwd_dx", "col_offsets",
+                "quantize_cols_h", "quantize_cols_dout", "dw_down", "quantize_cols_x",
+                "quantize_cols_dgu", "dw_gu"]
+    else:
+        bwd += ["gemm2_bwd_swiglu", "dw_down", "gemm1_bwd_dx", "dw_gu"]
+    bwd += ["dispatch_bwd_router"] if router else ["dispatch_bwd"]
+    return fwd + bwd
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -457,9 +477,30 @@ def main():
         ev1.record(stream)
         ev1.synchronize()
         kernel_us[name] = ev0.elapsed_time(ev1) * 1e3 / args.kernel_reps
+    kernel_us_warm = kernel_us
+    # The same stages inside steps: the layer's launch sequence, stage by stage through the
+    # entry points (the kernels moe_forward / moe_backward enqueue, in their order, on the same
+    # inputs), with HIP events on the launch stream between the stages, for args.steps steps.
+    # Each stage then runs on the cache state the stages before it leave, as in the timed
+    # steps, rather than on its own warm inputs; these durations feed the roofline entry.
+    order = [n for n in step_order(training, args.mx, w.fp8, router) if n in launches]
+    in_step = {n: 0.0 for n in order}
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i, n in enumerate(order):
+            launches[n]()
+            evs[i + 1].record(stream)
+        evs[-1].synchronize()
+        for i, n in enumerate(order):
+            in_step[n] += evs[i].elapsed_time(evs[i + 1]) * 1e3 / args.steps
+    kernel_us = {**kernel_us_warm, **in_step}
     step()  # leave the workspace as one full step wrote it
     torch.cuda.synchronize()
-    _log("bench: per-launch us " + json.dumps({k_: round(v_, 2) for k_, v_ in kernel_us.items()}))
+    _log("bench: per-launch us, warm repetitions " +
+         json.dumps({k_: round(v_, 2) for k_, v_ in kernel_us_warm.items()}))
+    _log("bench: per-launch us, inside steps " + json.dumps({k_: round(v_, 2) for k_, v_ in in_step.items()}))
 
     active = int((counts > 0).sum().item())  # experts that received rows in this step
     costs = stage_costs(w, training, active, mx=args.mx)
@@ -502,7 +543,8 @@ def main():
                  or args.score or args.scaling != 1.0 or placement != M.MOE_PLACE_COMBINE)
     roof["traffic"] = measured_traffic(dom, args.workload) if plain else None
     roof["kernel"] = dom
-    roof["launch_us"] = round(kernel_us[dom], 2)
+    roof["launch_us"] = round(kernel_us[dom], 2)       # inside steps (events between stages)
+    roof["launch_us_warm"] = round(kernel_us_warm[dom], 2)  # back-to-back repetitions
 
     # ---- CPU oracle on a bounded sample -----------------------------------------------
     cpu = None
@@ -569,6 +611,7 @@ def main():
         "rows": rows,
         **({"router": rtr} if router else {}),
         "kernel_us": {k_: round(v_, 2) for k_, v_ in kernel_us.items()},
+        "kernel_us_warm": {k_: round(v_, 2) for k_, v_ in kernel_us_warm.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
