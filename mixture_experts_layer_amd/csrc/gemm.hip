@@ -657,8 +657,13 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
           const int f = ks * MBL + i;  // fragment f sits in af[f & 1]
           if (i + 1 < MBL) af[(f + 1) & 1] = load_a(sa, ks, i + 1);
           else if (ks + 1 < KS) af[(f + 1) & 1] = load_a(sa, ks + 1, 0);
+          // keep the read of the next fragment ahead of this block's multiplies: left
+          // alone, the scheduler sinks it below them into the same registers, and every
+          // pair of multiplies then waits for a read issued just before it
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int j = 0; j < C::NB; ++j) mfma1(i, j, af[f & 1], bfr[ks & 1][j]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       return;
