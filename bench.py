@@ -83,7 +83,22 @@ def router_costs(w, training):
 
 
 GEMM_STAGES = ["gemm1_swiglu", "gemm2", "gemm2_bwd_swiglu", "dw_down", "gemm1_bwd_dx", "dw_gu"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_hbm_traffic_qwen3.md")
+TITLES = {"qwen3": "Qwen3-30B-A3B-shaped block, forward + backward",
+          "mixtral": "Mixtral-shaped block, forward",
+          "llama4": "Llama4-shaped decode step, forward",
+          "skewed_fp8": "skewed-routing block in e4m3, forward"}
+
+
+def traffic_file(workload):
+    """The committed HBM-traffic summary of one workload's grouped-GEMM launches."""
+    return os.path.join(ROOT, "profiles", f"grouped_gemm_hbm_traffic_{workload}.md")
+
+
+def gemm_stages(workload):
+    """GEMM stages a --pmc-pass run launches, in order: the forward pair, plus the four
+    backward launches when the workload trains."""
+    import workloads as W
+    return GEMM_STAGES if W.WORKLOADS[workload].training else GEMM_STAGES[:2]
 GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_amd", "csrc", "gemm.hip")
 CALIB_BYTES = 256 << 20
 
@@ -111,35 +126,37 @@ def pmc_summary(fetch_dir, write_dir, workload):
     WRITE_SIZE (KiB per dispatch) scaled by what each counter reads for a plain copy of
     CALIB_BYTES (read CALIB_BYTES, write CALIB_BYTES)."""
     out = {}
+    stages = gemm_stages(workload)
     for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _pmc_rows(folder, counter)
         gemm = [r for r in rows if "grouped_gemm_kernel" in r[1]]
-        assert len(gemm) >= len(GEMM_STAGES), f"{counter}: {len(gemm)} GEMM dispatches"
+        assert len(gemm) >= len(stages), f"{counter}: {len(gemm)} GEMM dispatches"
         # the calibration copy (an fp32 negation, CALIB_BYTES in and out) is the last dispatch
         assert "elementwise" in rows[-1][1], rows[-1][1]
         factor = CALIB_BYTES / (rows[-1][2] * 1024.0)
         # the pass launches each stage once, in GEMM_STAGES order, after one warm step
-        stage_rows = gemm[-len(GEMM_STAGES):]
+        stage_rows = gemm[-len(stages):]
         out[counter] = {"factor": factor, "stages": {n: r[2] * 1024.0 * factor
-                                                     for n, r in zip(GEMM_STAGES, stage_rows)},
-                        "kernels": {n: r[1] for n, r in zip(GEMM_STAGES, stage_rows)}}
+                                                     for n, r in zip(stages, stage_rows)},
+                        "kernels": {n: r[1] for n, r in zip(stages, stage_rows)}}
     data = {"workload": workload, "gemm_source_sha256_16": _source_hash(),
             "fetch_factor": round(out["FETCH_SIZE"]["factor"], 4),
             "write_factor": round(out["WRITE_SIZE"]["factor"], 4),
             "bytes_per_launch": {n: round(out["FETCH_SIZE"]["stages"][n] + out["WRITE_SIZE"]["stages"][n])
-                                 for n in GEMM_STAGES},
-            "fetch_bytes_per_launch": {n: round(out["FETCH_SIZE"]["stages"][n]) for n in GEMM_STAGES},
-            "write_bytes_per_launch": {n: round(out["WRITE_SIZE"]["stages"][n]) for n in GEMM_STAGES}}
-    lines = ["# HBM traffic of the grouped-GEMM launches: Qwen3-30B-A3B-shaped block", "",
+                                 for n in stages},
+            "fetch_bytes_per_launch": {n: round(out["FETCH_SIZE"]["stages"][n]) for n in stages},
+            "write_bytes_per_launch": {n: round(out["WRITE_SIZE"]["stages"][n]) for n in stages}}
+    wl = f" --workload {workload}"
+    lines = [f"# HBM traffic of the grouped-GEMM launches: {TITLES.get(workload, workload)}", "",
              "Commands (repository root; rocprofv3 run from /tmp):", "", "```",
-             "rocprofv3 --pmc FETCH_SIZE -f csv -d out/pmc_fetch -o run -- python3 bench.py --pmc-pass --no-cpu-baseline",
-             "rocprofv3 --pmc WRITE_SIZE -f csv -d out/pmc_write -o run -- python3 bench.py --pmc-pass --no-cpu-baseline",
-             "python3 bench.py --pmc-summary out/pmc_fetch out/pmc_write", "```", "",
+             f"rocprofv3 --pmc FETCH_SIZE -f csv -d out/pmc_fetch -o run -- python3 bench.py{wl} --pmc-pass --no-cpu-baseline",
+             f"rocprofv3 --pmc WRITE_SIZE -f csv -d out/pmc_write -o run -- python3 bench.py{wl} --pmc-pass --no-cpu-baseline",
+             f"python3 bench.py{wl} --pmc-summary out/pmc_fetch out/pmc_write", "```", "",
              f"Calibration: a plain copy of {CALIB_BYTES >> 20} MiB reads FETCH_SIZE x {data['fetch_factor']} "
              f"and WRITE_SIZE x {data['write_factor']} of its true byte counts; the factors scale the "
              "GEMM readings below. The data block is read by bench.py while the GEMM source hash matches.", "",
              "| stage | kernel | HBM read MB | HBM write MB | total MB |", "|---|---|---:|---:|---:|"]
-    for n in GEMM_STAGES:
+    for n in stages:
         k = out["FETCH_SIZE"]["kernels"][n]
         k = k[k.find("grouped_gemm_kernel"):][:60]
         lines.append(f"| {n} | `{k}` | {data['fetch_bytes_per_launch'][n] / 1e6:.1f} | "
@@ -153,7 +170,7 @@ def measured_traffic(stage, workload):
     summary is missing, was taken on another workload, or the GEMM source changed since the
     counters were taken."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(traffic_file(workload)).read()
         blob = text.split("```json", 1)[1].split("```", 1)[0]
         data = json.loads(blob)
     except (OSError, IndexError, ValueError):
