@@ -86,11 +86,13 @@ constexpr int kPermChunk = 256;  // flattened (token, slot) entries per dispatch
 size_t permute_scratch_bytes(int T, int E, int k);
 int router_chunk_tokens(int T);
 // align > 1: padded dispatch (blocks rounded up to multiples of align; offsets padded,
-// pad_offsets [E] = padding before each block when given).
+// pad_offsets [E] = padding before each block when given). extra_end >= 0: also write
+// offsets[E + 1] = extra_end (the end of one more group after the experts).
 hipError_t launch_dispatch_from_hist(const int32_t* topk_idx, int T, int E, int k, int chunk_tokens,
                                      int32_t* partial, int32_t* counts, int32_t* offsets,
                                      int32_t* row_of, int32_t* src_of, hipStream_t s,
-                                     int align = 1, int32_t* pad_offsets = nullptr);
+                                     int align = 1, int32_t* pad_offsets = nullptr,
+                                     int extra_end = -1);
 hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, int32_t* offsets,
                                 int32_t* row_of, int32_t* src_of, void* scratch, hipStream_t s,
                                 int align = 1, int32_t* pad_offsets = nullptr,

@@ -898,10 +898,15 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   else
     MOE_TRY(launch_router_ext(logits, T, E, k, p->score, ro, v.topk_idx, v.topk_prob,
                               (int32_t*)v.scratch, nullptr, nullptr, chunk_tokens, s));
-  // 2. dispatch: counts, offsets, row maps from the histograms, then the row copies
+  // A dense shared expert of the routed experts' width runs as one more group of T rows
+  // (offsets[E+1] = N + T) in the expert GEMM launches, reading x, its own weights and its
+  // own outputs; other widths, and training, launch it separately.
+  const bool fuse_shared = p->shared_I == I && !p->training && !fp8 && !mx && align == 1;
+  // 2. dispatch: counts, offsets (and the shared group's end), row maps from the
+  //    histograms, then the row copies
   MOE_TRY(launch_dispatch_from_hist(v.topk_idx, T, E, k, chunk_tokens, (int32_t*)v.scratch,
                                     v.counts, v.offsets, v.row_of, v.src_of, s, align,
-                                    v.pad_offsets));
+                                    v.pad_offsets, fuse_shared ? N + T : -1));
   const bool at_input = p->weight_placement == MOE_PLACE_INPUT;
   const bool at_act = p->weight_placement == MOE_PLACE_ACTIVATION;
   float* row_prob = at_act ? (float*)((uint8_t*)ws + make_layout(*p).row_prob) : nullptr;
@@ -924,11 +929,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
     MOE_TRY(launch_combine(v.out, v.row_of, v.topk_prob, nullptr, T, H, k, t->y, s));
     return MOE_OK;
   }
-  // 3. grouped MLP. A dense shared expert of the routed experts' width runs as one more
-  // group of T rows (offsets[E+1] = N + T) in the same two launches, reading x, its own
-  // weights and its own outputs; other widths, and training, launch it separately.
-  const bool fuse_shared = p->shared_I == I && !p->training && !fp8 && align == 1;
-  if (fuse_shared) MOE_TRY(launch_fill_i32(v.offsets + E + 1, 1, N + T, s));
+  // 3. grouped MLP (with the fused shared group when there is one)
   GemmParams g1{};
   g1.mode = fp8 ? MOE_GEMM_NT : MOE_GEMM_NN;
   g1.epi = EPI_SWIGLU;
