@@ -165,6 +165,77 @@ def pmc_summary(fetch_dir, write_dir, workload):
     return "\n".join(lines)
 
 
+def trace_summary(folder, steps):
+    """Markdown tables from a rocprofv3 --kernel-trace run of this script with --steps
+    `steps`: every kernel (calls and durations); the layer steps' launches in order (the
+    first, cold step left out; the steps end where the per-stage region begins, at the
+    first launch of the plain router entry point, since the layer's own router launch also
+    writes chunk histograms); and the stages timed inside steps, the region whose HIP events
+    give the bench line's per-launch times and roofline: `steps` passes over the entry
+    points, each opened by one plain router launch (and the fill of its counts), up to the
+    closing layer step."""
+    import csv
+    import glob
+    import re
+
+    def short(name):
+        name = name.replace("moe::", "").replace("(anonymous namespace)::", "").replace("void ", "")
+        m = re.match(r"(grouped_gemm_kernel<[^>]*>|mx_gemm_kernel<[^>]*>)", name)
+        return m.group(1) if m else re.sub(r"\(.*$", "", name)[:70]
+
+    ev = []
+    for path in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            ev.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short(r["Kernel_Name"])))
+    ev.sort()
+    lines = ["| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    per = {}
+    for t0, t1, n in ev:
+        per.setdefault(n, []).append((t1 - t0) / 1e3)
+    for n, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{n}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+
+    def plain_router(n):
+        return n.startswith(("router_row_kernel<", "router_topk_kernel<")) and n.endswith(", false>")
+
+    def layer_router(n):
+        return (n.startswith(("router_row_kernel<", "router_topk_kernel<")) and n.endswith(", true>")) \
+            or n.startswith(("router_logits", "router_ext"))
+
+    end = next((i for i, e in enumerate(ev) if plain_router(e[2])), len(ev))
+    start = next((i for i, e in enumerate(ev[:end]) if layer_router(e[2])), 0)
+    layer = ev[start:end]
+    names = [n for _, _, n in layer]
+    firsts = [i for i, n in enumerate(names) if n == names[0]] if names else []
+    period = firsts[1] - firsts[0] if len(firsts) > 1 else len(names)
+    nstep = len(names) // period if period else 0
+    if nstep > 1:
+        lines += ["", f"Layer steps: {nstep} steps of {period} launches; per launch over steps 2..{nstep}:", "",
+                  "| # | kernel | avg us | min us | max us |", "|---:|---|---:|---:|---:|"]
+        for j in range(period):
+            v = [(layer[s * period + j][1] - layer[s * period + j][0]) / 1e3 for s in range(1, nstep)]
+            lines.append(f"| {j} | `{names[j]}` | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        spans = [(layer[s * period + period - 1][1] - layer[s * period][0]) / 1e3 for s in range(1, nstep)]
+        lines += ["", f"Step span (first launch start to last launch end), steps 2..{nstep}: "
+                      f"avg {sum(spans) / len(spans):.1f} us, min {min(spans):.1f} us"]
+    plain = [i for i, e in enumerate(ev) if plain_router(e[2])]
+    closing = [i for i, e in enumerate(ev) if layer_router(e[2])]
+    if len(plain) >= steps and closing and closing[-1] > plain[-1]:
+        s0 = plain[-steps]
+        if s0 > 0 and ev[s0 - 1][2] == "fill_i32_kernel":
+            s0 -= 1
+        region = ev[s0:closing[-1]]
+        per_step = len(region) // steps
+        if per_step and per_step * steps == len(region):
+            lines += ["", f"Stages timed inside steps by the bench (its HIP events): {steps} passes of "
+                          f"{per_step} launches; per launch over all passes:", "",
+                      "| # | kernel | avg us | min us | max us |", "|---:|---|---:|---:|---:|"]
+            for j in range(per_step):
+                v = [(region[s * per_step + j][1] - region[s * per_step + j][0]) / 1e3 for s in range(steps)]
+                lines.append(f"| {j} | `{region[j][2]}` | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def measured_traffic(stage, workload):
     """HBM bytes per launch of `stage` from the committed counter summary, or None when the
     summary is missing, was taken on another workload, or the GEMM source changed since the
@@ -237,9 +308,14 @@ def main():
                     help="launch each stage once plus a 256 MiB calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the HBM-traffic summary from two rocprofv3 --pmc output folders")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="print kernel tables from a rocprofv3 --kernel-trace output folder")
     args = ap.parse_args()
     if args.pmc_summary:
         print(pmc_summary(*args.pmc_summary, args.workload))
+        return
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.steps), end="")
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -488,6 +564,7 @@ def main():
         fn()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        torch.cuda._sleep(1_000_000)  # untimed: the repetitions are enqueued before they run
         ev0.record(stream)
         for _ in range(args.kernel_reps):
             fn()
@@ -505,6 +582,9 @@ def main():
     for _ in range(args.steps):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
         torch.cuda.synchronize()
+        # hold the stream (untimed) while the host enqueues the pass, so that no stage's
+        # interval includes the GPU waiting for the host's next launch
+        torch.cuda._sleep(1_000_000)
         evs[0].record(stream)
         for i, n in enumerate(order):
             launches[n]()
