@@ -234,6 +234,11 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4_t* __rest
   __shared__ int rows[32];
   __shared__ float p[32];
   const int t = blockIdx.x;
+  // the thread's first piece of the row is requested before the row map, so that the two
+  // loads' latencies overlap instead of adding up
+  const int v0 = threadIdx.x;
+  u32x4_t first = {0u, 0u, 0u, 0u};
+  if (v0 < H8) first = x[(size_t)t * H8 + v0];
   if ((int)threadIdx.x < k) {
     const int r = row_of[(size_t)t * k + threadIdx.x];
     rows[threadIdx.x] = r;
@@ -241,8 +246,8 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4_t* __rest
     if (row_w) row_w[r] = w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
-  for (int v = threadIdx.x; v < H8; v += blockDim.x) {
-    const u32x4_t val = x[(size_t)t * H8 + v];
+  for (int v = v0; v < H8; v += blockDim.x) {
+    const u32x4_t val = v == v0 ? first : x[(size_t)t * H8 + v];
     for (int j = 0; j < k; ++j) {
       u32x4_t o = val;
       if (prob) {
