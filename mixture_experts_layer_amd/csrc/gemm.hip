@@ -635,8 +635,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   // are read and a slice of the cursor's next stage (into `nxt`) is issued.
   // Five M blocks per wave, or e4m3 fragments (8 registers each) with eight waves, leave no
   // room for a whole sub-step of A fragments in flight: there A fragments are read one M
-  // block ahead of the multiply instead.
-  constexpr bool APIPE = C::MB >= 5 || (FP8 && C::NW == 8);
+  // block ahead of the multiply instead. The weight gradients take the same order (measured
+  // 3 % faster than reading the whole next sub-step ahead; their fragments come from
+  // transposing LDS reads).
+  constexpr bool APIPE = C::MB >= 5 || (FP8 && C::NW == 8) || DW;
   auto compute_stage = [&](auto MBL_c, const uint8_t* sa, bool iss, uint8_t* nxt) __attribute__((always_inline)) {
     constexpr int KS = FP8 ? BKB / 64 : BKB / 32;
     constexpr int PER = (C::LOADS + KS - 1) / KS;
