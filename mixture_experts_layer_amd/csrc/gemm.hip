@@ -48,11 +48,12 @@ namespace {
 
 __device__ __attribute__((aligned(256))) uint8_t g_zero_block[4096];  // stays zero
 
-// Tile counters of the persistent launches: slot s holds one counter per XCD ([0..8)) and
-// the count of finished blocks ([8]). The last block of a launch to finish puts the slot
-// back to zero, so the next launch that takes the slot starts from zero. Launches take the
-// slots in turn (kSchedSlots of them), so launches in flight at the same time on one device
-// use different slots as long as fewer than kSchedSlots overlap.
+// Tile counters of the persistent launches: one counter per XCD ([0..8)) and the count of
+// finished blocks ([8]). The last block of a launch to finish puts them back to zero, so the
+// next launch that uses them starts from zero. The layer's launches bring their own (in
+// the layer workspace, zeroed by its dispatch); the stand-alone entry points take the
+// library's slots in turn (kSchedSlots of them), so launches in flight at the same time
+// on one device use different slots as long as fewer than kSchedSlots overlap.
 constexpr int kSchedSlots = 64;
 __device__ int g_sched[kSchedSlots][16];
 
@@ -288,7 +289,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
     r_end = r_start + base + (xcd < rem ? 1 : 0);
   }
   const int seq_first = r_start + (int)(blockIdx.x / nx), seq_stride = (int)gridDim.x / nx;
-  int* const ctr = &g_sched[p.sched_slot][xcd];
+  int* const sched = p.sched ? p.sched : g_sched[p.sched_slot];
+  int* const ctr = &sched[xcd];
   int n_pub = 0x40000000;     // tickets published in s_tk (a ring of 8); unbounded when static
   bool sched_open = false;    // later tickets may still hold tiles
   int pend_tk = 0;            // wave 0 holds a requested, unpublished ticket
@@ -1039,10 +1041,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
     if (tid == 0) {
       wait_vmcnt<0>();
       __threadfence();
-      if (atomicAdd(&g_sched[p.sched_slot][8], 1) == (int)gridDim.x - 1) {
+      if (atomicAdd(&sched[8], 1) == (int)gridDim.x - 1) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) g_sched[p.sched_slot][i] = 0;
-        g_sched[p.sched_slot][8] = 0;
+        for (int i = 0; i < 8; ++i) sched[i] = 0;
+        sched[8] = 0;
         __threadfence();
       }
     }

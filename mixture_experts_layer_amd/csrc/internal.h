@@ -87,12 +87,13 @@ size_t permute_scratch_bytes(int T, int E, int k);
 int router_chunk_tokens(int T);
 // align > 1: padded dispatch (blocks rounded up to multiples of align; offsets padded,
 // pad_offsets [E] = padding before each block when given). extra_end >= 0: also write
-// offsets[E + 1] = extra_end (the end of one more group after the experts).
+// offsets[E + 1] = extra_end (the end of one more group after the experts). zero16: 16 ints
+// set to zero (the layer's GEMM tile counters).
 hipError_t launch_dispatch_from_hist(const int32_t* topk_idx, int T, int E, int k, int chunk_tokens,
                                      int32_t* partial, int32_t* counts, int32_t* offsets,
                                      int32_t* row_of, int32_t* src_of, hipStream_t s,
                                      int align = 1, int32_t* pad_offsets = nullptr,
-                                     int extra_end = -1);
+                                     int extra_end = -1, int32_t* zero16 = nullptr);
 hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, int32_t* offsets,
                                 int32_t* row_of, int32_t* src_of, void* scratch, hipStream_t s,
                                 int align = 1, int32_t* pad_offsets = nullptr,
@@ -185,6 +186,8 @@ struct GemmParams {
   void* gu_out;          // EPI_SWIGLU: optional saved g,u [rows,2I]
   const void* gu_in;     // EPI_SWIGLU_BWD: saved g,u [rows,2I]
   int sched_slot;        // tile-counter slot of the launch (set by the launcher)
+  int* sched;            // optional: the launch's own tile counters (16 ints, zero when the
+                         // launch starts, left zero when it ends); NULL: a library slot
   // NN/NT, bf16, no saved g,u: when A_last is set the last group (G-1) takes its A rows,
   // its weight and its C rows from these tensors (row 0 = the group's first row) instead
   // of from A, B and C. Used to run a dense shared expert as one more group.

@@ -44,6 +44,7 @@ struct Layout {
   size_t logits, d_logits, router_ws, router_ws_bytes, total;
   size_t mx_col_offsets, dgq, dgq_scale, mx_ta, mx_ta_scale, mx_tb, mx_tb_scale, mx_kp;
   size_t row_prob, row_part;  // ScaledSwiGLU: weight of each routed row; d_prob partials
+  size_t sched;  // tile counters of the layer's grouped-GEMM launches (16 ints)
   size_t rows;  // rows of the expert-contiguous buffers
 };
 
@@ -101,6 +102,7 @@ Layout make_layout(const moe_problem_t& p) {
   const bool at_act = p.weight_placement == MOE_PLACE_ACTIVATION;
   L.row_prob = take(at_act ? N * 4 : 0);
   L.row_part = take(at_act && p.router && p.training ? N * (size_t)(p.I / 64) * 4 : 0);
+  L.sched = take(16 * 4);
   // MXFP8 training: dgu codes (rows), and the token-axis (transposed) operands of the weight
   // gradients, [C, Kp] codes for C up to max(H, I) (A side) and max(H, 2I) (B side)
   const bool mxt = mx && p.training;
@@ -904,9 +906,12 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   const bool fuse_shared = p->shared_I == I && !p->training && !fp8 && !mx && align == 1;
   // 2. dispatch: counts, offsets (and the shared group's end), row maps from the
   //    histograms, then the row copies
+  // The layer's grouped-GEMM launches (forward and backward) keep their tile counters in
+  // the workspace: the dispatch zeroes them, each launch leaves them zero.
+  int32_t* const sched = (int32_t*)((uint8_t*)ws + make_layout(*p).sched);
   MOE_TRY(launch_dispatch_from_hist(v.topk_idx, T, E, k, chunk_tokens, (int32_t*)v.scratch,
                                     v.counts, v.offsets, v.row_of, v.src_of, s, align,
-                                    v.pad_offsets, fuse_shared ? N + T : -1));
+                                    v.pad_offsets, fuse_shared ? N + T : -1, sched));
   const bool at_input = p->weight_placement == MOE_PLACE_INPUT;
   const bool at_act = p->weight_placement == MOE_PLACE_ACTIVATION;
   float* row_prob = at_act ? (float*)((uint8_t*)ws + make_layout(*p).row_prob) : nullptr;
@@ -931,6 +936,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   }
   // 3. grouped MLP (with the fused shared group when there is one)
   GemmParams g1{};
+  g1.sched = sched;
   g1.mode = fp8 ? MOE_GEMM_NT : MOE_GEMM_NN;
   g1.epi = EPI_SWIGLU;
   g1.fp8 = fp8;
@@ -956,6 +962,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   }
   MOE_TRY(launch_grouped_gemm(g1, s));
   GemmParams g2{};
+  g2.sched = sched;
   g2.mode = fp8 ? MOE_GEMM_NT : MOE_GEMM_NN;
   g2.epi = EPI_STORE;
   g2.fp8 = fp8;
@@ -987,6 +994,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
     MOE_TRY(launch_fill_i32(v.shared_offsets, 1, 0, s));
     MOE_TRY(launch_fill_i32(v.shared_offsets + 1, 1, T, s));
     GemmParams s1{};
+  s1.sched = sched;
     s1.mode = MOE_GEMM_NN;
     s1.epi = EPI_SWIGLU;
     s1.A = t->x;
@@ -1000,6 +1008,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
     s1.I = p->shared_I;
     MOE_TRY(launch_grouped_gemm(s1, s));
     GemmParams s2{};
+  s2.sched = sched;
     s2.mode = MOE_GEMM_NN;
     s2.epi = EPI_STORE;
     s2.A = v.shared_h;
@@ -1045,6 +1054,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   const Layout L = make_layout(*p);
   float* const row_prob = at_act ? (float*)((uint8_t*)ws + L.row_prob) : nullptr;
   float* const row_part = at_act && p->router ? (float*)((uint8_t*)ws + L.row_part) : nullptr;
+  int32_t* const gsched = (int32_t*)((uint8_t*)ws + L.sched);  // zero since the forward
   if (T == 0) {
     // no routed rows: the weight gradients are zero (the dW GEMMs see empty groups)
     MOE_TRY(launch_fill_i32(v.offsets, E + 1, 0, s));
@@ -1098,6 +1108,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   } else {
   // GEMM2 backward: dgu = SwiGLU'(d_out . W_down^T), dW_down = h^T . d_out
   GemmParams a{};
+  a.sched = gsched;
   a.mode = MOE_GEMM_NT;
   a.epi = EPI_SWIGLU_BWD;
   a.A = v.d_out;
@@ -1114,6 +1125,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   a.row_part = row_part;   // and the weight gradient's partials (router projection)
   if (N > 0) MOE_TRY(launch_grouped_gemm(a, s));
   GemmParams b{};
+  b.sched = gsched;
   b.mode = MOE_GEMM_TN_DW;
   b.epi = EPI_STORE;
   b.A = v.h;
@@ -1127,6 +1139,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   MOE_TRY(launch_grouped_gemm(b, s));
   // GEMM1 backward: dxp = dgu . W_gu^T, dW_gu = xp^T . dgu
   GemmParams c{};
+  c.sched = gsched;
   c.mode = MOE_GEMM_NT;
   c.epi = EPI_STORE;
   c.A = v.dgu;
@@ -1139,6 +1152,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   c.C = v.dxp;
   if (N > 0) MOE_TRY(launch_grouped_gemm(c, s));
   GemmParams d{};
+  d.sched = gsched;
   d.mode = MOE_GEMM_TN_DW;
   d.epi = EPI_STORE;
   d.A = v.xp;

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void dispatch_rank_scan_kernel(
     const int32_t* __restrict__ idx, int n, int k, int E, int nchunks, int chunk_entries,
     const int32_t* __restrict__ partial, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_of, int32_t* __restrict__ src_of,
-    int align, int32_t* __restrict__ pad_offsets, int extra_end) {
+    int align, int32_t* __restrict__ pad_offsets, int extra_end, int32_t* __restrict__ zero16) {
   __shared__ int s_tot[1024], s_bef[1024];  // [group][expert], NG * E <= 256 * W
   __shared__ int base[256], wsum[4], cnt[4][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -134,6 +134,7 @@ __global__ __launch_bounds__(256) void dispatch_rank_scan_kernel(
     }
     if (tid == 255) offsets[E] = incl;  // threads past E add nothing: incl is the total
     if (tid == 0 && extra_end >= 0) offsets[E + 1] = extra_end;  // one more group's end
+    if (zero16 && tid < 16) zero16[tid] = 0;
     if (pad_offsets) {
       __syncthreads();
       if (lane == 63) wsum[wave] = pincl;
@@ -178,15 +179,16 @@ __global__ __launch_bounds__(256) void dispatch_rank_scan_kernel(
 hipError_t launch_rank_scan(const int32_t* idx, int n, int k, int E, int nchunks,
                             int chunk_entries, const int32_t* partial, int32_t* counts,
                             int32_t* offsets, int32_t* row_of, int32_t* src_of, int align,
-                            int32_t* pad_offsets, hipStream_t s, int extra_end = -1) {
+                            int32_t* pad_offsets, hipStream_t s, int extra_end = -1,
+                            int32_t* zero16 = nullptr) {
   if (E % 4 == 0)
     dispatch_rank_scan_kernel<4><<<nchunks, 256, 0, s>>>(idx, n, k, E, nchunks, chunk_entries,
                                                          partial, counts, offsets, row_of, src_of,
-                                                         align, pad_offsets, extra_end);
+                                                         align, pad_offsets, extra_end, zero16);
   else
     dispatch_rank_scan_kernel<1><<<nchunks, 256, 0, s>>>(idx, n, k, E, nchunks, chunk_entries,
                                                          partial, counts, offsets, row_of, src_of,
-                                                         align, pad_offsets, extra_end);
+                                                         align, pad_offsets, extra_end, zero16);
   return hipGetLastError();
 }
 
@@ -209,16 +211,17 @@ hipError_t launch_dispatch_meta(const int32_t* topk_idx, int T, int E, int k, in
 hipError_t launch_dispatch_from_hist(const int32_t* topk_idx, int T, int E, int k, int chunk_tokens,
                                      int32_t* partial, int32_t* counts, int32_t* offsets,
                                      int32_t* row_of, int32_t* src_of, hipStream_t s, int align,
-                                     int32_t* pad_offsets, int extra_end) {
+                                     int32_t* pad_offsets, int extra_end, int32_t* zero16) {
   const int n = T * k;
   if (n == 0) {
     hipError_t e = pad_offsets ? launch_fill_i32(pad_offsets, E, 0, s) : hipSuccess;
     if (e == hipSuccess && extra_end >= 0) e = launch_fill_i32(offsets + E + 1, 1, extra_end, s);
+    if (e == hipSuccess && zero16) e = launch_fill_i32(zero16, 16, 0, s);
     return e == hipSuccess ? launch_fill_i32(offsets, E + 1, 0, s) : e;
   }
   const int nchunks = (T + chunk_tokens - 1) / chunk_tokens;
   return launch_rank_scan(topk_idx, n, k, E, nchunks, chunk_tokens * k, partial, counts, offsets,
-                          row_of, src_of, align, pad_offsets, s, extra_end);
+                          row_of, src_of, align, pad_offsets, s, extra_end, zero16);
 }
 
 // ---- row movement ----------------------------------------------------------
