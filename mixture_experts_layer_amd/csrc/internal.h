@@ -77,6 +77,17 @@ hipError_t launch_router_topk(const float* logits, int T, int E, int k, int scor
                               uint8_t* routing_map, float* probs_dense, hipStream_t s);
 // Router that also writes the per-expert histogram of each chunk of `chunk_tokens`
 // tokens to partial[chunk][E] (input of launch_dispatch_from_hist).
+// Routing, dispatch metadata and row copies of a step of at most 32 tokens and 256
+// choices (k <= 16, E <= 256, H % 8 == 0) in one launch, for the plain router options:
+// the same topk_idx, topk_prob, counts, offsets (offsets[E + 1] = extra_end when >= 0),
+// row_of, src_of and xp as launch_router_hist + launch_dispatch_from_hist +
+// launch_scatter_rows; zero16 (nullable): 16 ints set to zero.
+bool route_dispatch_small_fits(int T, int E, int k);
+hipError_t launch_route_dispatch_small(const float* logits, int T, int E, int k, int score,
+                                       int32_t* topk_idx, float* topk_prob, int32_t* counts,
+                                       int32_t* offsets, int32_t* row_of, int32_t* src_of,
+                                       const void* x, int H, void* xp, int extra_end,
+                                       int32_t* zero16, hipStream_t s);
 hipError_t launch_router_hist(const float* logits, int T, int E, int k, int score,
                               int32_t* topk_idx, float* topk_prob, int32_t* partial,
                               int chunk_tokens, hipStream_t s);

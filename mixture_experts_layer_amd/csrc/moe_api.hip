@@ -894,33 +894,41 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   st = make_router_opts(E, k, p->score, t->expert_bias, p->num_groups, p->group_topk,
                         p->scaling_factor, 0, &ro);
   if (st != MOE_OK) return st;
-  if (router_opts_plain(ro, p->score))
-    MOE_TRY(launch_router_hist(logits, T, E, k, p->score, v.topk_idx, v.topk_prob,
-                               (int32_t*)v.scratch, chunk_tokens, s));
-  else
-    MOE_TRY(launch_router_ext(logits, T, E, k, p->score, ro, v.topk_idx, v.topk_prob,
-                              (int32_t*)v.scratch, nullptr, nullptr, chunk_tokens, s));
   // A dense shared expert of the routed experts' width runs as one more group of T rows
   // (offsets[E+1] = N + T) in the expert GEMM launches, reading x, its own weights and its
   // own outputs; other widths, and training, launch it separately.
   const bool fuse_shared = p->shared_I == I && !p->training && !fp8 && !mx && align == 1;
-  // 2. dispatch: counts, offsets (and the shared group's end), row maps from the
-  //    histograms, then the row copies
   // The layer's grouped-GEMM launches (forward and backward) keep their tile counters in
   // the workspace: the dispatch zeroes them, each launch leaves them zero.
   int32_t* const sched = (int32_t*)((uint8_t*)ws + make_layout(*p).sched);
-  MOE_TRY(launch_dispatch_from_hist(v.topk_idx, T, E, k, chunk_tokens, (int32_t*)v.scratch,
-                                    v.counts, v.offsets, v.row_of, v.src_of, s, align,
-                                    v.pad_offsets, fuse_shared ? N + T : -1, sched));
   const bool at_input = p->weight_placement == MOE_PLACE_INPUT;
   const bool at_act = p->weight_placement == MOE_PLACE_ACTIVATION;
   float* row_prob = at_act ? (float*)((uint8_t*)ws + make_layout(*p).row_prob) : nullptr;
-  if (align > 1)  // zero padding rows (fp8 scale / ScaledSwiGLU weight 1), src_of -1
-    MOE_TRY(launch_zero_pad_rows(v.offsets, v.counts, E, fp8 ? H : 2 * H, v.xp,
-                                 fp8 ? v.xp_scale : row_prob, v.src_of, s));
-  if (fp8) MOE_TRY(launch_scatter_rows_fp8(t->x, v.row_of, T, H, k, (uint8_t*)v.xp, v.xp_scale, s));
-  else MOE_TRY(launch_scatter_rows(t->x, v.row_of, at_input ? v.topk_prob : nullptr, T, H, k,
-                                   v.xp, s, v.topk_prob, row_prob));
+  const bool plain = router_opts_plain(ro, p->score);
+  if (plain && route_dispatch_small_fits(T, E, k) && align == 1 && !fp8 && !at_input && !at_act) {
+    // a decode-sized step: routing, dispatch and row copies in one launch
+    MOE_TRY(launch_route_dispatch_small(logits, T, E, k, p->score, v.topk_idx, v.topk_prob,
+                                        v.counts, v.offsets, v.row_of, v.src_of, t->x, H, v.xp,
+                                        fuse_shared ? N + T : -1, sched, s));
+  } else {
+    if (plain)
+      MOE_TRY(launch_router_hist(logits, T, E, k, p->score, v.topk_idx, v.topk_prob,
+                                 (int32_t*)v.scratch, chunk_tokens, s));
+    else
+      MOE_TRY(launch_router_ext(logits, T, E, k, p->score, ro, v.topk_idx, v.topk_prob,
+                                (int32_t*)v.scratch, nullptr, nullptr, chunk_tokens, s));
+    // 2. dispatch: counts, offsets (and the shared group's end), row maps from the
+    //    histograms, then the row copies
+    MOE_TRY(launch_dispatch_from_hist(v.topk_idx, T, E, k, chunk_tokens, (int32_t*)v.scratch,
+                                      v.counts, v.offsets, v.row_of, v.src_of, s, align,
+                                      v.pad_offsets, fuse_shared ? N + T : -1, sched));
+    if (align > 1)  // zero padding rows (fp8 scale / ScaledSwiGLU weight 1), src_of -1
+      MOE_TRY(launch_zero_pad_rows(v.offsets, v.counts, E, fp8 ? H : 2 * H, v.xp,
+                                   fp8 ? v.xp_scale : row_prob, v.src_of, s));
+    if (fp8) MOE_TRY(launch_scatter_rows_fp8(t->x, v.row_of, T, H, k, (uint8_t*)v.xp, v.xp_scale, s));
+    else MOE_TRY(launch_scatter_rows(t->x, v.row_of, at_input ? v.topk_prob : nullptr, T, H, k,
+                                     v.xp, s, v.topk_prob, row_prob));
+  }
   if (mx) {
     // MXFP8 (te_mixtral's mxfp8 recipe): rows quantised per 32-element block, block-scaled
     // GEMMs; the weight arguments hold codes and scale bytes (moe_quantize_mxfp8_weights)

@@ -158,6 +158,70 @@ MOE_DEV int dpp_ror(int v, int ctrl_sel) {
   }
 }
 
+// One token's routing on its 16-lane row (lane r holds experts r, r+16, ...): k rounds of
+// arg-max, then the weight of the lane's choice (lanes r < k: choice r). `avail` ends with
+// bit i clear where expert r + 16 i was taken.
+template <int EPR>
+MOE_DEV void route_row(const float* __restrict__ lrow, int E, int k, int score, int r, int& my_e,
+                       float& q, int& avail) {
+  float v[EPR];
+  avail = 0;  // bit i: expert r + 16 i exists and is not taken
+#pragma unroll
+  for (int i = 0; i < EPR; ++i) {
+    const int e = r + 16 * i;
+    v[i] = e < E ? nan_to_ninf(lrow[e]) : 0.f;
+    if (e < E) avail |= 1 << i;
+  }
+  const int exists = avail;
+  my_e = 0;
+  float my_v = 0.f, top_v = 0.f;
+  for (int j = 0; j < k; ++j) {
+    // branch-free: a lane with no candidate holds (-inf, INT_MAX), which every available
+    // expert beats (an available one at -inf by its lower id), so the winner is always a
+    // real expert; the lane's first available expert is taken whatever its value
+    float bv = -__builtin_inff();
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < EPR; ++i) {  // ascending id: strict > keeps the lower id on a tie
+      const bool take = ((avail >> i) & 1) & ((be == 0x7fffffff) | (v[i] > bv));
+      bv = take ? v[i] : bv;
+      be = take ? r + 16 * i : be;
+    }
+#pragma unroll
+    for (int sh = 8; sh > 0; sh >>= 1) {
+      const float ov = __int_as_float(dpp_ror(__float_as_int(bv), sh));
+      const int oe = dpp_ror(be, sh);
+      const bool other = (ov > bv) | ((ov == bv) & (oe < be));
+      bv = other ? ov : bv;
+      be = other ? oe : be;
+    }
+    if (j == 0) top_v = bv;
+    if (r == j) {
+      my_e = be;
+      my_v = bv;
+    }
+    if ((be & 15) == r) avail &= ~(1 << (be >> 4));
+  }
+  if (score == MOE_SIGMOID) {
+    q = 1.0f / (1.0f + expf(-my_v));
+  } else if (score == MOE_SOFTMAX_PRE) {
+    // the full softmax: every expert's exp(l - l_max) summed over the row's 16 lanes
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPR; ++i)
+      if ((exists >> i) & 1) sum += expf(v[i] - top_v);
+#pragma unroll
+    for (int sh = 8; sh > 0; sh >>= 1) sum += __int_as_float(dpp_ror(__float_as_int(sum), sh));
+    q = expf(my_v - top_v) / sum;
+  } else {
+    const float z = r < k ? expf(my_v - top_v) : 0.f;  // the best logit is the first choice
+    float sum = z;
+#pragma unroll
+    for (int sh = 8; sh > 0; sh >>= 1) sum += __int_as_float(dpp_ror(__float_as_int(sum), sh));
+    q = z / sum;
+  }
+}
+
 template <int EPR, bool HIST>  // experts per lane: ceil(E / 16)
 __global__ __launch_bounds__(512) void router_row_kernel(
     const float* __restrict__ logits, int T, int E, int k, int score, int32_t* __restrict__ topk_idx,
@@ -182,63 +246,9 @@ __global__ __launch_bounds__(512) void router_row_kernel(
     const int t = t0 + row;
     const bool live = t < t_end;
     const float* lrow = logits + (size_t)(live ? t : t0) * E;
-    float v[EPR];
-    int avail = 0;  // bit i: expert r + 16 i exists and is not taken
-#pragma unroll
-    for (int i = 0; i < EPR; ++i) {
-      const int e = r + 16 * i;
-      v[i] = e < E ? nan_to_ninf(lrow[e]) : 0.f;
-      if (e < E) avail |= 1 << i;
-    }
-    const int exists = avail;
-    int my_e = 0;
-    float my_v = 0.f, top_v = 0.f;
-    for (int j = 0; j < k; ++j) {
-      // branch-free: a lane with no candidate holds (-inf, INT_MAX), which every available
-      // expert beats (an available one at -inf by its lower id), so the winner is always a
-      // real expert; the lane's first available expert is taken whatever its value
-      float bv = -__builtin_inff();
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < EPR; ++i) {  // ascending id: strict > keeps the lower id on a tie
-        const bool take = ((avail >> i) & 1) & ((be == 0x7fffffff) | (v[i] > bv));
-        bv = take ? v[i] : bv;
-        be = take ? r + 16 * i : be;
-      }
-#pragma unroll
-      for (int sh = 8; sh > 0; sh >>= 1) {
-        const float ov = __int_as_float(dpp_ror(__float_as_int(bv), sh));
-        const int oe = dpp_ror(be, sh);
-        const bool other = (ov > bv) | ((ov == bv) & (oe < be));
-        bv = other ? ov : bv;
-        be = other ? oe : be;
-      }
-      if (j == 0) top_v = bv;
-      if (r == j) {
-        my_e = be;
-        my_v = bv;
-      }
-      if ((be & 15) == r) avail &= ~(1 << (be >> 4));
-    }
+    int my_e, avail;
     float q;
-    if (score == MOE_SIGMOID) {
-      q = 1.0f / (1.0f + expf(-my_v));
-    } else if (score == MOE_SOFTMAX_PRE) {
-      // the full softmax: every expert's exp(l - l_max) summed over the row's 16 lanes
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < EPR; ++i)
-        if ((exists >> i) & 1) sum += expf(v[i] - top_v);
-#pragma unroll
-      for (int sh = 8; sh > 0; sh >>= 1) sum += __int_as_float(dpp_ror(__float_as_int(sum), sh));
-      q = expf(my_v - top_v) / sum;
-    } else {
-      const float z = r < k ? expf(my_v - top_v) : 0.f;  // the best logit is the first choice
-      float sum = z;
-#pragma unroll
-      for (int sh = 8; sh > 0; sh >>= 1) sum += __int_as_float(dpp_ror(__float_as_int(sum), sh));
-      q = z / sum;
-    }
+    route_row<EPR>(lrow, E, k, score, r, my_e, q, avail);
     if (live) {
       if (r < k) {
         topk_idx[(size_t)t * k + r] = my_e;
@@ -313,6 +323,105 @@ hipError_t launch_router_topk(const float* logits, int T, int E, int k, int scor
       return hipErrorInvalidValue;
   }
 #undef MOE_ROUTER_CASE
+  return hipGetLastError();
+}
+
+// A step of at most 32 tokens and 256 choices (decode) in one block: the routing above
+// (one token per 16-lane row), then the dispatch metadata -- counts, offsets (and the end
+// of one more group after the experts), each choice's row in expert-contiguous order, the
+// stable counting sort of the flattened choices, with a choice's rank the number of
+// earlier choices of the same expert -- and the row copies xp[row_of[f]] = x[f / k]. The
+// results are those of the router, dispatch and scatter launches of larger steps.
+template <int EPR>
+__global__ __launch_bounds__(512) void route_dispatch_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int score, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_prob, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ src_of, const u32x4_t* __restrict__ x,
+    int H8, u32x4_t* __restrict__ xp, int extra_end, int32_t* __restrict__ zero16) {
+  __shared__ int hist[256], base[256], s_idx[256], s_row[256], wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int r = tid & 15, t = tid >> 4;
+  if (t < T) {  // whole 16-lane rows: the row's rotations stay among live lanes
+    int my_e, avail;
+    float q;
+    route_row<EPR>(logits + (size_t)t * E, E, k, score, r, my_e, q, avail);
+    if (r < k) {
+      topk_idx[(size_t)t * k + r] = my_e;
+      topk_prob[(size_t)t * k + r] = q;
+      s_idx[t * k + r] = my_e;
+      atomicAdd(&hist[my_e], 1);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the counts over the experts (E <= 256: the first four waves)
+  int cnt = tid < E ? hist[tid] : 0, incl = cnt;
+  if (wave < 4) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+  }
+  __syncthreads();
+  if (wave < 4) {
+    for (int w = 0; w < wave; ++w) incl += wsum[w];
+    if (tid < E) {
+      base[tid] = incl - cnt;
+      offsets[tid] = incl - cnt;
+      counts[tid] = cnt;
+    }
+    if (tid == 255) offsets[E] = incl;  // threads past E add nothing: incl is the total
+    if (tid == 0 && extra_end >= 0) offsets[E + 1] = extra_end;
+    if (zero16 && tid < 16) zero16[tid] = 0;
+  }
+  __syncthreads();
+  const int n = T * k;
+  if (tid < n) {
+    const int e = s_idx[tid];
+    int rank = 0;
+    for (int f = 0; f < tid; ++f) rank += s_idx[f] == e ? 1 : 0;
+    const int row = base[e] + rank;
+    s_row[tid] = row;
+    row_of[tid] = row;
+    src_of[row] = tid / k;
+  }
+  __syncthreads();
+  for (int i = tid; i < n * H8; i += blockDim.x) {
+    const int f = i / H8, v = i - f * H8;
+    __builtin_nontemporal_store(x[(size_t)(f / k) * H8 + v], &xp[(size_t)s_row[f] * H8 + v]);
+  }
+}
+
+bool route_dispatch_small_fits(int T, int E, int k) {
+  return T >= 1 && T <= 32 && k >= 1 && k <= 16 && T * k <= 256 && E >= 1 && E <= 256;
+}
+
+hipError_t launch_route_dispatch_small(const float* logits, int T, int E, int k, int score,
+                                       int32_t* topk_idx, float* topk_prob, int32_t* counts,
+                                       int32_t* offsets, int32_t* row_of, int32_t* src_of,
+                                       const void* x, int H, void* xp, int extra_end,
+                                       int32_t* zero16, hipStream_t s) {
+  if (!route_dispatch_small_fits(T, E, k) || H % 8) return hipErrorInvalidValue;
+  const int epr = (E + 15) / 16;
+#define MOE_ROUTE_SMALL(n)                                                                      \
+  case n:                                                                                      \
+    route_dispatch_small_kernel<n><<<1, 512, 0, s>>>(logits, T, E, k, score, topk_idx, topk_prob, \
+                                                     counts, offsets, row_of, src_of,          \
+                                                     (const u32x4_t*)x, H / 8, (u32x4_t*)xp,    \
+                                                     extra_end, zero16);                       \
+    break;
+  switch ((epr + 3) / 4 * 4) {
+    MOE_ROUTE_SMALL(4)
+    MOE_ROUTE_SMALL(8)
+    MOE_ROUTE_SMALL(12)
+    MOE_ROUTE_SMALL(16)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MOE_ROUTE_SMALL
   return hipGetLastError();
 }
 

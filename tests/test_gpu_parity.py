@@ -462,6 +462,12 @@ SMALL = {
     "small_qwen": W.custom("small_qwen", T=257, H=256, E=32, k=8, I=192, training=True),
     "small_fp8": W.custom("small_fp8", T=300, H=256, E=32, k=8, I=256, fp8=True, zipf_s=1.2, n_empty=5),
     "t1": W.custom("t1", T=1, H=128, E=8, k=2, I=128, training=True),
+    # decode-sized steps (at most 32 tokens and 256 choices, k <= 16) route, dispatch and
+    # copy rows in one launch: its limits, E not a multiple of 16, each plain score
+    "dec_256": W.custom("dec_256", T=32, H=128, E=256, k=8, I=128, score=O.SOFTMAX_POST),
+    "dec_k16": W.custom("dec_k16", T=16, H=256, E=64, k=16, I=128, score=O.SOFTMAX_PRE),
+    "dec_e100": W.custom("dec_e100", T=5, H=192, E=100, k=3, I=128, score=O.SIGMOID),
+    "dec_renorm": W.custom("dec_renorm", T=31, H=128, E=40, k=6, I=128, training=True),
 }
 
 
@@ -487,7 +493,21 @@ def test_forward_parity_small(name):
         check_bf16(host_vals(g.view("h", (N, w.I), torch.bfloat16)), ref["h"], f"{name} h")
 
 
-@pytest.mark.parametrize("name", ["small_qwen", "t1"])
+@pytest.mark.parametrize("name", ["dec_256", "dec_k16", "dec_e100", "dec_renorm", "small_shared_eq"])
+def test_decode_step_rows_copied(name):
+    # the expert-contiguous rows of a decode-sized step: xp[r] = x[src_of[r]] bit for bit
+    w = SMALL[name]
+    _say("decode rows", name)
+    d = W.make_inputs(w)
+    g = GpuMoE(w, d)
+    g.forward()
+    src = g.ints()["src_of"]
+    xp = g.view("xp", (w.T * w.k, w.H), torch.bfloat16).view(torch.int16).cpu().numpy()
+    x = np.asarray(d["x"]).view(np.int16).reshape(w.T, w.H)
+    assert np.array_equal(xp, x[src])
+
+
+@pytest.mark.parametrize("name", ["small_qwen", "t1", "dec_renorm"])
 def test_backward_parity_small(name):
     w = SMALL[name]
     _say("backward", name)
