@@ -202,7 +202,7 @@ def trace_summary(folder, steps):
 
     def layer_router(n):
         return (n.startswith(("router_row_kernel<", "router_topk_kernel<")) and n.endswith(", true>")) \
-            or n.startswith(("router_logits", "router_ext"))
+            or n.startswith(("router_logits", "router_ext", "route_dispatch_small_kernel"))
 
     end = next((i for i, e in enumerate(ev) if plain_router(e[2])), len(ev))
     start = next((i for i, e in enumerate(ev[:end]) if layer_router(e[2])), 0)
