@@ -186,7 +186,8 @@ moe_status_t moe_aux_loss_backward(const float* logits, const int32_t* tokens_pe
 size_t moe_permute_workspace_bytes(int T, int E, int k);
 
 /* Token dispatch (guide, "Token dispatch"): expert-contiguous copy of the tokens.
- *  x        [T,H] bf16 in.       topk_idx [T,k] int32 in (ids in [0,E)).
+ *  x        [T,H] bf16 in.       topk_idx [T,k] int32 in (ids in [0,E); not checked on the
+ *           device: another id makes the kernels write outside the buffers).
  *  out_dtype MOE_BF16: xp [T*k,H] bf16 is a bit copy of the token rows.
  *            MOE_FP8_E4M3: xp [T*k,H] e4m3 codes, xp_scale [T*k] float32: each token
  *            quantised per row, scale = amax/448 (1 for an all-zero row).
