@@ -114,7 +114,15 @@ __global__ __launch_bounds__(256) void aux_colsum_kernel(const float* __restrict
   if (e >= E) return;
   const int t0 = b * chunk, t1 = min(T, t0 + chunk);
   float acc = 0.f;
-  for (int t = t0; t < t1; ++t) acc += scores[(size_t)t * E + e];
+  // rows 8 at a time, requested before any is added; the sum still runs in row order
+  for (int ta = t0; ta < t1; ta += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = ta + j < t1 ? scores[(size_t)(ta + j) * E + e] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (ta + j < t1) acc += v[j];
+  }
   part[(size_t)b * E + e] = acc;
 }
 

@@ -83,18 +83,30 @@ __global__ __launch_bounds__(256) void dispatch_rank_scan_kernel(
     int tot[W], bef[W];
 #pragma unroll
     for (int w = 0; w < W; ++w) tot[w] = bef[w] = 0;
-    for (int cc = gr; cc < nchunks; cc += NG) {
-      int v[W];
-      if constexpr (W == 4) {
-        const int4 q = *(const int4*)(partial + (size_t)cc * E + 4 * u);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-      } else {
-        v[0] = partial[(size_t)cc * E + u];
+    // eight of the thread's chunk rows are requested before any is added, so their
+    // latencies overlap (one at a time, each row cost a full L2 round trip)
+    constexpr int U = 8;
+    for (int cc0 = gr; cc0 < nchunks; cc0 += U * NG) {
+      int v[U][W];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int cc = cc0 + j * NG;
+        if constexpr (W == 4) {
+          int4 q = make_int4(0, 0, 0, 0);
+          if (cc < nchunks) q = *(const int4*)(partial + (size_t)cc * E + 4 * u);
+          v[j][0] = q.x; v[j][1] = q.y; v[j][2] = q.z; v[j][3] = q.w;
+        } else {
+          v[j][0] = cc < nchunks ? partial[(size_t)cc * E + u] : 0;
+        }
       }
 #pragma unroll
-      for (int w = 0; w < W; ++w) {
-        tot[w] += v[w];
-        bef[w] += cc < c ? v[w] : 0;
+      for (int j = 0; j < U; ++j) {
+        const int cc = cc0 + j * NG;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          tot[w] += v[j][w];
+          bef[w] += cc < c ? v[j][w] : 0;
+        }
       }
     }
 #pragma unroll
@@ -571,13 +583,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict_
       }
     }
     if constexpr (ROUTER) {
-      for (int j = 0; j < nnz; ++j) {
-        const u32x4_t wv = w_router[(size_t)ids[j] * H8 + v];
-        const float g = dl[j];
+      // router weight rows 8 at a time, requested before any is added (ascending id order)
+      for (int j0 = 0; j0 < nnz; j0 += 8) {
+        u32x4_t wv[8];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          acc[2 * d] = fmaf(g, bf16lo(wv[d]), acc[2 * d]);
-          acc[2 * d + 1] = fmaf(g, bf16hi(wv[d]), acc[2 * d + 1]);
+        for (int jj = 0; jj < 8; ++jj)
+          if (j0 + jj < nnz) wv[jj] = w_router[(size_t)ids[j0 + jj] * H8 + v];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          if (j0 + jj >= nnz) break;
+          const float g = dl[j0 + jj];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            acc[2 * d] = fmaf(g, bf16lo(wv[jj][d]), acc[2 * d]);
+            acc[2 * d + 1] = fmaf(g, bf16hi(wv[jj][d]), acc[2 * d + 1]);
+          }
         }
       }
     }

@@ -362,22 +362,38 @@ __global__ __launch_bounds__(256) void dispatch_bwd_router_input_kernel(
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const u32x4_t o = dxp[(size_t)rows[j] * H8 + v];
-      const float q = ACT ? 1.f : p[j];
+    // rows 8 at a time, requested before any is added; the sums keep slot order, then
+    // ascending expert id
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      u32x4_t o[8];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        acc[2 * d] = fmaf(q, bf16lo(o[d]), acc[2 * d]);
-        acc[2 * d + 1] = fmaf(q, bf16hi(o[d]), acc[2 * d + 1]);
+      for (int jj = 0; jj < 8; ++jj)
+        if (j0 + jj < k) o[jj] = dxp[(size_t)rows[j0 + jj] * H8 + v];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj >= k) break;
+        const float q = ACT ? 1.f : p[j0 + jj];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          acc[2 * d] = fmaf(q, bf16lo(o[jj][d]), acc[2 * d]);
+          acc[2 * d + 1] = fmaf(q, bf16hi(o[jj][d]), acc[2 * d + 1]);
+        }
       }
     }
-    for (int j = 0; j < nnz; ++j) {
-      const u32x4_t wv = w_router[(size_t)nz_e[j] * H8 + v];
-      const float g = nz_v[j];
+    for (int j0 = 0; j0 < nnz; j0 += 8) {
+      u32x4_t wv[8];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        acc[2 * d] = fmaf(g, bf16lo(wv[d]), acc[2 * d]);
-        acc[2 * d + 1] = fmaf(g, bf16hi(wv[d]), acc[2 * d + 1]);
+      for (int jj = 0; jj < 8; ++jj)
+        if (j0 + jj < nnz) wv[jj] = w_router[(size_t)nz_e[j0 + jj] * H8 + v];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj >= nnz) break;
+        const float g = nz_v[j0 + jj];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          acc[2 * d] = fmaf(g, bf16lo(wv[jj][d]), acc[2 * d]);
+          acc[2 * d + 1] = fmaf(g, bf16hi(wv[jj][d]), acc[2 * d + 1]);
+        }
       }
     }
     u32x4_t ov;
