@@ -312,19 +312,43 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void mx_gemm_kernel(MxArgs p) {
     const int ntn = EPI == EPI_SWIGLU ? (I + HB - 1) / HB : (N + BN - 1) / BN;
     for (int x = tid; x <= p.G; x += NT) s_off[x] = p.offsets[x];
     __syncthreads();
-    if (tid == 0) {
-      int acc = 0;
-      s_pref[0] = 0;
-      for (int x = 0; x < p.G; ++x) {
-        acc += (s_off[x + 1] - s_off[x] + BM - 1) / BM;
-        s_pref[x + 1] = acc;
+    if (wave == 0) {  // the prefix by one wave: up to five groups per lane, then a lane scan
+      const int per = (p.G + 63) / 64;
+      int loc[5];
+      int sum = 0;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int x = lane * per + i;
+        int mtx = 0;
+        if (i < per && x < p.G) mtx = (s_off[x + 1] - s_off[x] + BM - 1) / BM;
+        sum += mtx;
+        loc[i] = sum;
+      }
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      if (lane == 0) s_pref[0] = 0;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int x = lane * per + i;
+        if (i < per && x < p.G) s_pref[x + 1] = incl - sum + loc[i];
       }
     }
     __syncthreads();
     const int tile = blockIdx.x;
     if (tile >= s_pref[p.G] * ntn) return;
-    g = 0;
-    while (s_pref[g + 1] * ntn <= tile) ++g;
+    {  // the tile's group: the last g with s_pref[g] * ntn <= tile (binary search)
+      int lo = 0, hi = p.G;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pref[mid] * ntn <= tile) lo = mid;
+        else hi = mid - 1;
+      }
+      g = lo;
+    }
     const int local = tile - s_pref[g] * ntn;
     const int mt = s_pref[g + 1] - s_pref[g];
     ntile = local / mt;

@@ -494,10 +494,18 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const f32x4_t*
   if (i >= E * H4) return;
   const int e = i / H4, c = i % H4;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const f32x4_t a = part[((size_t)s * mp + e) * H4 + c];
-    const f32x4_t b = part[((size_t)s * mp + E + e) * H4 + c];
-    acc += a + b;
+  // eight splits' partials requested before any is added; the sum keeps split order
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    f32x4_t a[8], b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < S) {
+        a[j] = part[((size_t)(s0 + j) * mp + e) * H4 + c];
+        b[j] = part[((size_t)(s0 + j) * mp + E + e) * H4 + c];
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < S) acc += a[j] + b[j];
   }
   dw[i] = acc;
 }
