@@ -90,6 +90,11 @@ MOE_DEV void load_lds16(const void* g, uint8_t* lds) {
 }
 
 // The same from a wave-uniform base (SGPR pair) plus a 32-bit per-lane byte offset.
+// One 4-byte LDS-DMA per lane: lane l fills lds + 4 l.
+MOE_DEV void load_lds4(const void* g, uint8_t* lds) {
+  const unsigned m0 = (unsigned)(uintptr_t)((lds_u8_t*)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
 MOE_DEV void load_lds16_s(const void* base, uint32_t off, uint8_t* lds) {
   const unsigned m0 = (unsigned)(uintptr_t)((lds_u8_t*)lds);
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
@@ -219,6 +224,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
                          ? 128 : 64;
   __shared__ __attribute__((aligned(16))) uint8_t s_epi[C::NW * 32 * SB];
   __shared__ int s_tk[8];      // published tile tickets
+  // e4m3: each tile's row and column scales, DMA'd when the load cursor reaches the tile
+  // (so they land before its first stage is read), one slot per tile the cursor can be ahead
+  constexpr int SC_SLOTS = LEAD + 1;
+  __shared__ __attribute__((aligned(16))) float s_fsc[FP8 ? SC_SLOTS : 1][FP8 ? BM + BN : 1];
   static_assert(EPI != EPI_SWIGLU || C::NB % 2 == 0, "SwiGLU wave tile: gate blocks + as many up blocks");
 
   const int tid = threadIdx.x;
@@ -495,6 +504,35 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
     }
   };
 
+  // e4m3: the tile's BM row scales and BN column scales (in B-tile row order: for SwiGLU
+  // the gate columns, then the up columns) into slot j % SC_SLOTS, 64 values per
+  // wave-uniform DMA; rows and columns past the tile's valid ones read the zero block (their
+  // outputs are never stored).
+  auto issue_scales = [&](const Tile& t, int j) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+      static_assert((BM + BN) % 64 == 0, "whole 64-value scale DMAs");
+      constexpr int PARTS = (BM + BN) / 64;
+      float* slot = s_fsc[j % SC_SLOTS];
+      for (int part = wave; part < PARTS; part += C::NW) {
+        const int idx = part * 64 + lane;
+        const void* src = zero;
+        if (idx < BM) {
+          if (idx < t.rows_valid) src = p.a_scale + t.m0 + idx;
+        } else {
+          const int r = idx - BM;
+          if (EPI == EPI_SWIGLU) {
+            const int hcol = t.n0 + (r < HB ? r : r - HB);
+            if (hcol < p.I) src = p.b_scale + (size_t)t.g * (2 * p.I) + (r < HB ? hcol : p.I + hcol);
+          } else {
+            const int col = t.n0 + r;
+            if (col < p.N) src = p.b_scale + (size_t)t.g * p.N + col;
+          }
+        }
+        load_lds4(src, (uint8_t*)(slot + part * 64));
+      }
+    }
+  };
+
   // ---- load cursor: walks this block's tiles ahead of the multiply ---------------------
   Tile lt;              // tile whose stages are being loaded
   int lj = -1;          // its index in this block's sequence
@@ -519,6 +557,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       lk = 0;
       if (lnk > 0) {
         setup_loads(lt);
+        issue_scales(lt, lj);
         st = L_LIVE;
         break;
       }
@@ -708,7 +747,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   constexpr int S1 = EPI == EPI_SWIGLU ? S_SWIGLU : S_STORE;
   constexpr int S2 = EPI == EPI_SWIGLU ? S_SWIGLU_GU : S_STORE;
   static_assert((EPI == EPI_SWIGLU ? NH_ : C::NB) % PB == 0, "staging groups");
-  auto epilogue = [&](const Tile& t) __attribute__((always_inline)) {
+  auto epilogue = [&](const Tile& t, int sc) __attribute__((always_inline)) {  // sc: scale slot
     // Lane-derived row and column parts, made opaque so the address arithmetic below is
     // not hoisted out of the tile loop (where it would sit in registers the whole time).
     int l32 = lane & 31, kh = lane >> 5, rr = lane / LPR, cc = lane % LPR;
@@ -761,7 +800,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       for (int i = 0; i < C::MB; ++i) {
         const int r0 = (wm + WM * i) * 32;
         float sa = 1.f;
-        if (FP8) sa = p.a_scale[t.m0 + (r0 + l32 < t.rows_valid ? r0 + l32 : 0)];
+        if (FP8) sa = s_fsc[sc][r0 + l32];
         // ScaledSwiGLU: the routing weight of this lane's row (lane l holds row l % 32)
         float rs = 1.f;
         if (scaled) rs = p.row_scale[t.m0 + (r0 + l32 < t.rows_valid ? r0 + l32 : 0)];
@@ -779,17 +818,16 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
               u[b][v] = acc[i][jg0 + b + NH][v];
             }
           if (FP8) {
-            const float* bs = p.b_scale + (size_t)t.g * twoI;
+            const float* bs = &s_fsc[sc][BM];  // gate columns, then HB up columns
 #pragma unroll
             for (int b = 0; b < PB; ++b)
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const int c = t.n0 + hb + 32 * b + 8 * q + 4 * kh;
-                const int cs = c < p.I ? c : 0;
+                const int c = hb + 32 * b + 8 * q + 4 * kh;  // h column within the tile
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                  g[b][4 * q + r] *= sa * bs[cs + r];
-                  u[b][4 * q + r] *= sa * bs[p.I + cs + r];
+                  g[b][4 * q + r] *= sa * bs[c + r];
+                  u[b][4 * q + r] *= sa * bs[HB + c + r];
                 }
               }
           }
@@ -900,7 +938,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       for (int i = 0; i < C::MB; ++i) {
         const int r0 = (wm + WM * i) * 32;
         float sa = 1.f;
-        if (FP8) sa = p.a_scale[t.m0 + (r0 + l32 < mlim ? r0 + l32 : 0)];
+        if (FP8) sa = s_fsc[sc][r0 + l32];
         auto row_ok = [&](int r) { return r0 + r < mlim; };
         float v[C::NB][16];
 #pragma unroll
@@ -911,8 +949,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
             const int c0 = bcol0(j);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int c = t.n0 + c0 + 8 * q + 4 * kh;
-              const float* bs = p.b_scale + (size_t)t.g * p.N + (c < p.N ? c : 0);
+              const float* bs = &s_fsc[sc][BM + c0 + 8 * q + 4 * kh];
 #pragma unroll
               for (int r = 0; r < 4; ++r) v[j][4 * q + r] *= sa * bs[r];
             }
@@ -952,10 +989,11 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   // Stream stages are numbered over all of this block's tiles: gs is the next stage to
   // multiply, gl the next to load, gl - gs <= LEAD. With `cross`, the cursor runs into the
   // next tile while the current one finishes, so the next tile's first stages are in flight
-  // during the epilogue (whose stores then sit between those loads and their wait). Without
-  // it (epilogues that read global memory, fp32 output) each tile starts with its own
-  // prologue after the previous epilogue.
-  constexpr bool CROSS = !FP8 && EPI != EPI_SWIGLU_BWD;
+  // during the epilogue (whose stores then sit between those loads and their wait). The e4m3
+  // scales of a tile are staged into LDS when the cursor reaches it, so those epilogues read
+  // no global memory either. Without it (the SwiGLU backward, which reads h and the routing
+  // weights) each tile starts with its own prologue after the previous epilogue.
+  constexpr bool CROSS = EPI != EPI_SWIGLU_BWD;
   const bool cross = CROSS && !p.c_fp32 && !(EPI == EPI_SWIGLU && p.row_scale);
   const int s_allow = (EPI == EPI_SWIGLU && p.gu_out) ? 2 : 1;
   auto buf = [&](int s) __attribute__((always_inline)) { return smem + (s % STAGES) * C::STAGE; };
@@ -1014,7 +1052,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       case 4: if constexpr (C::MB >= 4) run_tile(std::integral_constant<int, 4>{}, cnk); break;
       default: if constexpr (C::MB >= 5) run_tile(std::integral_constant<int, 5>{}, cnk); break;
     }
-    epilogue(ct);
+    epilogue(ct, cj % SC_SLOTS);
     epi2 = epi1;
     epi1 = gl;
     if constexpr (DYN) {
