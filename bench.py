@@ -469,6 +469,10 @@ def main():
     counts = vt("counts", (E,), torch.int32)
 
     pdtype = M.MOE_BF16 if args.mx else dtype  # MXFP8 quantises after the bf16 dispatch
+    # split-K space of the decode-sized bf16 GEMMs (the layer keeps its own in ws)
+    sk_bytes = max(M.moe_grouped_gemm_splitk_workspace_bytes(N, E, 2 * I),
+                   M.moe_grouped_gemm_splitk_workspace_bytes(N, E, H)) if dtype == M.MOE_BF16 else 0
+    skws = torch.empty(sk_bytes, dtype=torch.uint8, device=dev) if sk_bytes else None
     launches = {
         "router": lambda: M.moe_router_topk_ex(logits, k, w.score, router_opts, idx_t, topk_prob,
                                                counts),
@@ -478,10 +482,10 @@ def main():
                    (lambda: M.moe_permute(x, idx_t, E, xp, offs, row_of, src_of, scratch,
                                           pdtype, xp_scale)),
         "gemm1_swiglu": lambda: M.moe_grouped_gemm_swiglu(xp, w_gu, offs, h, gu, dtype,
-                                                          xp_scale, w_gu_s),
+                                                          xp_scale, w_gu_s, ws=skws),
         "gemm2": (lambda: M.moe_grouped_gemm(M.MOE_GEMM_NT, hq, w_down, offs, out, dtype,
                                              h_scale, w_down_s)) if w.fp8 else
-                 (lambda: M.moe_grouped_gemm(M.MOE_GEMM_NN, h, w_down, offs, out)),
+                 (lambda: M.moe_grouped_gemm(M.MOE_GEMM_NN, h, w_down, offs, out, ws=skws)),
         "combine": lambda: M.moe_unpermute_combine(out, row_of, topk_prob, y, shared_out),
     }
     if w.fp8:

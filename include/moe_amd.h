@@ -245,20 +245,36 @@ moe_status_t moe_permute_padded(const void* x, const int32_t* topk_idx, int T, i
  *                moe_quantize_fp8_weights), w_scale [G,2I] float32.
  *  offsets [G+1] int32 device group boundaries.
  *  h       [rows,I] bf16 out: silu(g) * u, g and u held in fp32.
- *  gu_saved [rows,2I] bf16 out, nullable: g and u rounded to bf16 (for backward). */
+ *  gu_saved [rows,2I] bf16 out, nullable: g and u rounded to bf16 (for backward).
+ *  ws, ws_bytes: nullable split-K space (see moe_grouped_gemm_splitk_workspace_bytes with
+ *          ncols = 2I); ignored by shapes that never split. */
 moe_status_t moe_grouped_gemm_swiglu(const void* xp, const float* xp_scale, const void* w_gu,
                                      const float* w_scale, const int32_t* offsets, int G,
                                      int rows, int H, int I, int dtype, void* h, void* gu_saved,
-                                     void* stream);
+                                     void* ws, size_t ws_bytes, void* stream);
 
 /* Grouped GEMM (guide, "Grouped GEMM"); see moe_gemm_mode_t for the layouts.
  *  dtype MOE_BF16: A, B bf16.  MOE_FP8_E4M3 (mode NT only): A e4m3 [rows,K] with
  *  a_scale [rows], B e4m3 [G][N,K] with b_scale [G,N]; C = acc * a_scale * b_scale.
  *  c_dtype MOE_BF16 or MOE_FP32 (fp32 accumulation in every case). M is used by
- *  MOE_GEMM_TN_DW only, K by NN/NT only. */
+ *  MOE_GEMM_TN_DW only, K by NN/NT only.
+ *  ws, ws_bytes: nullable split-K space (moe_grouped_gemm_splitk_workspace_bytes with
+ *  ncols = N); ignored by shapes that never split. */
 moe_status_t moe_grouped_gemm(int mode, const void* A, const float* a_scale, const void* B,
                               const float* b_scale, const int32_t* offsets, int G, int rows,
-                              int M, int N, int K, int dtype, void* C, int c_dtype, void* stream);
+                              int M, int N, int K, int dtype, void* C, int c_dtype, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Split-K space of a bf16 NN/NT grouped GEMM (moe_grouped_gemm_swiglu: ncols = 2I;
+ * moe_grouped_gemm: ncols = N) over `rows` rows in G groups; 0 for shapes that never split.
+ * Only decode-sized launches split (at most 256 rows and at most 32 rows per group on
+ * average: one 32-row tile per expert, so a few wide tiles per expert would leave compute
+ * units idle): each tile's reduction over K is cut into up to 8 parts, chosen on the device
+ * from the exact tile count; the parts' fp32 sums go to this space and a second launch adds
+ * them in part order and applies the epilogue. Results equal the unsplit launch's up to the
+ * order of the fp32 additions. The caller owns the space; concurrent launches need their
+ * own. The layer's forward (moe_forward) keeps its own in the layer workspace. */
+size_t moe_grouped_gemm_splitk_workspace_bytes(int rows, int G, int ncols);
 
 /* Backward of GEMM2 + SwiGLU: dh = d_out[rows,H] . W_down[g][I,H]^T (layout NT), then
  *  with the saved bf16 g,u and s = sigmoid(g): dg = dh*u*s*(1+g*(1-s)), du = dh*g*s,

@@ -37,7 +37,7 @@ EXPORTS = [
     "moe_aux_loss_scores", "moe_aux_loss_workspace_bytes", "moe_aux_loss",
     "moe_aux_loss_backward", "moe_grouped_gemm_swiglu_scaled",
     "moe_grouped_gemm_swiglu_scaled_bwd", "moe_permute_probs", "moe_dispatch_backward_router_scaled",
-    "moe_permute_noalloc", "moe_permute_noalloc_limit",
+    "moe_permute_noalloc", "moe_permute_noalloc_limit", "moe_grouped_gemm_splitk_workspace_bytes",
 ]
 
 
@@ -95,8 +95,9 @@ def _load():
         "moe_router_topk": ([vp, i, i, i, i, vp, vp, vp, vp, vp, vp], i),
         "moe_permute_workspace_bytes": ([i, i, i], sz),
         "moe_permute": ([vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp, sz, vp], i),
-        "moe_grouped_gemm_swiglu": ([vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp], i),
-        "moe_grouped_gemm": ([i, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp], i),
+        "moe_grouped_gemm_swiglu": ([vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, sz, vp], i),
+        "moe_grouped_gemm": ([i, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, sz, vp], i),
+        "moe_grouped_gemm_splitk_workspace_bytes": ([i, i, i], sz),
         "moe_grouped_gemm_swiglu_bwd": ([vp, vp, vp, vp, i, i, i, i, vp, vp], i),
         "moe_set_gemm_max_blocks": ([i], i),
         "moe_unpermute_combine": ([vp, vp, vp, vp, i, i, i, vp, vp], i),
@@ -316,8 +317,21 @@ def moe_permute_padded(x, topk_idx, E, align, xp, offsets, pad_offsets, row_of, 
         _stream(stream)))
 
 
+def moe_grouped_gemm_splitk_workspace_bytes(rows, G, ncols):
+    return int(_lib.moe_grouped_gemm_splitk_workspace_bytes(rows, G, ncols))
+
+
+def _ws(ws):
+    """(pointer, bytes) of an optional uint8 device workspace."""
+    if ws is None:
+        return None, 0
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("ws: a contiguous uint8 tensor")
+    return ws.data_ptr(), ws.numel()
+
+
 def moe_grouped_gemm_swiglu(xp, w_gu, offsets, h, gu_saved=None, dtype=MOE_BF16, xp_scale=None,
-                            w_scale=None, stream=None):
+                            w_scale=None, stream=None, ws=None):
     rows, H = xp.shape
     G = offsets.numel() - 1
     I = h.shape[1]
@@ -328,13 +342,14 @@ def moe_grouped_gemm_swiglu(xp, w_gu, offsets, h, gu_saved=None, dtype=MOE_BF16,
         _want(w_gu, torch.uint8, (G, 2 * I, H), "w_gu")
     if gu_saved is not None:
         _want(gu_saved, torch.bfloat16, (rows, 2 * I), "gu_saved")
+    wp, wb = _ws(ws)
     _check("moe_grouped_gemm_swiglu", _lib.moe_grouped_gemm_swiglu(
         _p(xp), _p(xp_scale), _p(w_gu), _p(w_scale), _p(offsets), G, rows, H, I, dtype, _p(h),
-        _p(gu_saved), _stream(stream)))
+        _p(gu_saved), wp, wb, _stream(stream)))
 
 
 def moe_grouped_gemm(mode, A, B, offsets, C, dtype=MOE_BF16, a_scale=None, b_scale=None,
-                     stream=None):
+                     stream=None, ws=None):
     G = offsets.numel() - 1
     rows = A.shape[0]
     c_dtype = MOE_FP32 if C.dtype == torch.float32 else MOE_BF16
@@ -346,9 +361,10 @@ def moe_grouped_gemm(mode, A, B, offsets, C, dtype=MOE_BF16, a_scale=None, b_sca
         N = B.shape[2] if mode == MOE_GEMM_NN else B.shape[1]
         M = 0
         _want(C, C.dtype, (rows, N), "C")
+    wp, wb = _ws(ws)
     _check("moe_grouped_gemm", _lib.moe_grouped_gemm(
         mode, _p(A), _p(a_scale), _p(B), _p(b_scale), _p(offsets), G, rows, M, N, K, dtype,
-        _p(C), c_dtype, _stream(stream)))
+        _p(C), c_dtype, wp, wb, _stream(stream)))
 
 
 def moe_grouped_gemm_swiglu_bwd(d_out, w_down, offsets, gu_saved, dgu, stream=None):

@@ -210,7 +210,20 @@ struct GemmParams {
   // writes per row and 64-column block sum_c dh[row,c] silu(g) u (dh before the scaling).
   const float* row_scale;
   float* row_part;
+  // Split-K (bf16 NN/NT launches on 32-row tiles, the decode case, where a few wide tiles
+  // per expert leave compute units idle): with `part` set, each tile's K range may be cut
+  // into S <= kSplitKMax parts, chosen on the device from the exact tile count. Every part
+  // writes its fp32 sums to part[S][rows][ncols] (ncols = 2I for SwiGLU, else N), S goes
+  // to *part_s, and a second kernel adds the parts in order and applies the epilogue.
+  // NULL: no split. Space: splitk_workspace_bytes.
+  float* part;
+  int* part_s;
 };
+constexpr int kSplitKMax = 8;
+// Bytes of the split-K space of a bf16 NN/NT grouped GEMM over `rows` rows in G groups with
+// ncols output columns before the epilogue (0: the shape never splits). The space holds
+// part_s at offset 0 and part at offset 256.
+size_t splitk_workspace_bytes(long long rows, int G, long long ncols);
 hipError_t launch_grouped_gemm(const GemmParams& p, hipStream_t s);
 // Grid cap of the persistent grouped-GEMM launches (0: every resident block).
 void set_gemm_max_blocks(int n);

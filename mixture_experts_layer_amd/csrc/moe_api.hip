@@ -45,6 +45,7 @@ struct Layout {
   size_t mx_col_offsets, dgq, dgq_scale, mx_ta, mx_ta_scale, mx_tb, mx_tb_scale, mx_kp;
   size_t row_prob, row_part;  // ScaledSwiGLU: weight of each routed row; d_prob partials
   size_t sched;  // tile counters of the layer's grouped-GEMM launches (16 ints)
+  size_t splitk, splitk_bytes;  // split-K partial sums of the forward's decode-sized GEMMs
   size_t rows;  // rows of the expert-contiguous buffers
 };
 
@@ -54,6 +55,13 @@ size_t router_wgrad_dls_bytes(int T, int E) { return align_up((size_t)T * router
 size_t router_wgrad_bytes(int T, int H, int E) {
   return router_wgrad_dls_bytes(T, E) +
          (size_t)router_wgrad_splits(T) * router_split_cols(E) * (size_t)H * 4;
+}
+
+// A dense shared expert of the routed experts' width runs as one more group of T rows
+// (offsets[E+1] = N + T) in the forward's expert GEMM launches, reading x, its own weights
+// and its own outputs; other widths, and training, launch it separately.
+bool fuses_shared(const moe_problem_t& p) {
+  return p.shared_I == p.I && !p.training && p.dtype == MOE_BF16 && p.align_size <= 1;
 }
 
 Layout make_layout(const moe_problem_t& p) {
@@ -103,6 +111,15 @@ Layout make_layout(const moe_problem_t& p) {
   L.row_prob = take(at_act ? N * 4 : 0);
   L.row_part = take(at_act && p.router && p.training ? N * (size_t)(p.I / 64) * 4 : 0);
   L.sched = take(16 * 4);
+  // split-K space of the bf16 forward GEMMs (one after the other, so they share it)
+  if (p.dtype == MOE_BF16) {
+    const long long rows = (long long)N + (fuses_shared(p) ? p.T : 0);
+    const int G = p.E + (fuses_shared(p) ? 1 : 0);
+    const size_t b1 = splitk_workspace_bytes(rows, G, 2LL * p.I);
+    const size_t b2 = splitk_workspace_bytes(rows, G, p.H);
+    L.splitk_bytes = b1 > b2 ? b1 : b2;
+  }
+  L.splitk = take(L.splitk_bytes);
   // MXFP8 training: dgu codes (rows), and the token-axis (transposed) operands of the weight
   // gradients, [C, Kp] codes for C up to max(H, I) (A side) and max(H, 2I) (B side)
   const bool mxt = mx && p.training;
@@ -340,10 +357,26 @@ moe_status_t moe_permute_padded(const void* x, const int32_t* topk_idx, int T, i
   return MOE_OK;
 }
 
+size_t moe_grouped_gemm_splitk_workspace_bytes(int rows, int G, int ncols) {
+  return splitk_workspace_bytes(rows, G, ncols);
+}
+
+// Optional split-K space of a stand-alone grouped GEMM: NULL, or at least the bytes above.
+static moe_status_t take_splitk(GemmParams& p, long long ncols, void* ws, size_t ws_bytes) {
+  if (ws == nullptr) return MOE_OK;
+  if (!ok_ptr(ws)) return MOE_ERR_INVALID_ARG;
+  const size_t need = splitk_workspace_bytes(p.rows, p.G, ncols);
+  if (need == 0 || p.fp8 || p.mode == MOE_GEMM_TN_DW) return MOE_OK;  // never splits
+  if (ws_bytes < need) return MOE_ERR_INVALID_ARG;
+  p.part_s = (int*)ws;
+  p.part = (float*)((uint8_t*)ws + 256);
+  return MOE_OK;
+}
+
 moe_status_t moe_grouped_gemm_swiglu(const void* xp, const float* xp_scale, const void* w_gu,
                                      const float* w_scale, const int32_t* offsets, int G,
                                      int rows, int H, int I, int dtype, void* h, void* gu_saved,
-                                     void* stream) {
+                                     void* ws, size_t ws_bytes, void* stream) {
   if (G <= 0 || rows < 0 || H <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
   if (H % 64 || I % 64 || G > 256) return MOE_ERR_UNSUPPORTED;
   if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
@@ -370,12 +403,15 @@ moe_status_t moe_grouped_gemm_swiglu(const void* xp, const float* xp_scale, cons
   p.C = h;
   p.I = I;
   p.gu_out = gu_saved;
+  const moe_status_t st = take_splitk(p, 2LL * I, ws, ws_bytes);
+  if (st != MOE_OK) return st;
   return hip_status(launch_grouped_gemm(p, S(stream)));
 }
 
 moe_status_t moe_grouped_gemm(int mode, const void* A, const float* a_scale, const void* B,
                               const float* b_scale, const int32_t* offsets, int G, int rows,
-                              int M, int N, int K, int dtype, void* C, int c_dtype, void* stream) {
+                              int M, int N, int K, int dtype, void* C, int c_dtype, void* ws,
+                              size_t ws_bytes, void* stream) {
   if (G <= 0 || rows < 0 || N <= 0) return MOE_ERR_INVALID_ARG;
   if (G > 256) return MOE_ERR_UNSUPPORTED;
   if (mode != MOE_GEMM_NN && mode != MOE_GEMM_NT && mode != MOE_GEMM_TN_DW)
@@ -412,6 +448,8 @@ moe_status_t moe_grouped_gemm(int mode, const void* A, const float* a_scale, con
   p.K = K;
   p.C = C;
   p.c_fp32 = c_dtype == MOE_FP32;
+  const moe_status_t st = take_splitk(p, N, ws, ws_bytes);
+  if (st != MOE_OK) return st;
   return hip_status(launch_grouped_gemm(p, S(stream)));
 }
 
@@ -894,10 +932,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   st = make_router_opts(E, k, p->score, t->expert_bias, p->num_groups, p->group_topk,
                         p->scaling_factor, 0, &ro);
   if (st != MOE_OK) return st;
-  // A dense shared expert of the routed experts' width runs as one more group of T rows
-  // (offsets[E+1] = N + T) in the expert GEMM launches, reading x, its own weights and its
-  // own outputs; other widths, and training, launch it separately.
-  const bool fuse_shared = p->shared_I == I && !p->training && !fp8 && !mx && align == 1;
+  const bool fuse_shared = fuses_shared(*p);
   // The layer's grouped-GEMM launches (forward and backward) keep their tile counters in
   // the workspace: the dispatch zeroes them, each launch leaves them zero.
   int32_t* const sched = (int32_t*)((uint8_t*)ws + make_layout(*p).sched);
@@ -968,6 +1003,14 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
     g1.B_last = t->shared_gu;
     g1.C_last = v.shared_h;
   }
+  // decode-sized launches may split K (partial sums in the workspace)
+  const Layout L = make_layout(*p);
+  float* const part = L.splitk_bytes ? (float*)((uint8_t*)ws + L.splitk + 256) : nullptr;
+  int32_t* const part_s = (int32_t*)((uint8_t*)ws + L.splitk);
+  if (!fp8 && part && splitk_workspace_bytes(g1.rows, g1.G, 2LL * I) != 0) {
+    g1.part = part;
+    g1.part_s = part_s;
+  }
   MOE_TRY(launch_grouped_gemm(g1, s));
   GemmParams g2{};
   g2.sched = sched;
@@ -995,6 +1038,10 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
     g2.A_last = v.shared_h;
     g2.B_last = t->shared_down;
     g2.C_last = v.shared_out;
+  }
+  if (!fp8 && part && splitk_workspace_bytes(g2.rows, g2.G, H) != 0) {
+    g2.part = part;
+    g2.part_s = part_s;
   }
   MOE_TRY(launch_grouped_gemm(g2, s));
   // shared expert: one dense group over all T tokens, read straight from x

@@ -67,15 +67,26 @@ def test_gemm_size_limits_answer_before_device_work(lib):
     gg = lib.moe_grouped_gemm
     gg.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                    ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.c_size_t, ctypes.c_void_p]
     NN, NT, BF16 = 0, 1, 0
     for mode in (NN, NT):
-        assert gg(mode, None, None, None, None, None, 8, 16, 0, 65536, 32768, BF16, None, BF16, None) == 2
-        assert gg(mode, None, None, None, None, None, 8, 16, 0, 65536, 32704, BF16, None, BF16, None) == 1
+        assert gg(mode, None, None, None, None, None, 8, 16, 0, 65536, 32768, BF16, None, BF16, None, 0, None) == 2
+        assert gg(mode, None, None, None, None, None, 8, 16, 0, 65536, 32704, BF16, None, BF16, None, 0, None) == 1
     sw = lib.moe_grouped_gemm_swiglu
-    sw.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 3
-    assert sw(None, None, None, None, None, 8, 16, 32768, 32768, BF16, None, None, None) == 2
-    assert sw(None, None, None, None, None, 8, 16, 32704, 32768, BF16, None, None, None) == 1
+    sw.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert sw(None, None, None, None, None, 8, 16, 32768, 32768, BF16, None, None, None, 0, None) == 2
+    assert sw(None, None, None, None, None, 8, 16, 32704, 32768, BF16, None, None, None, 0, None) == 1
+
+
+def test_splitk_space_only_for_decode_shapes(lib):
+    # split-K space: part count at offset 0, then 8 parts of [rows, ncols] fp32; only shapes
+    # of at most 256 rows and 32 rows per group on average split
+    f = lib.moe_grouped_gemm_splitk_workspace_bytes
+    f.argtypes, f.restype = [ctypes.c_int] * 3, ctypes.c_size_t
+    assert f(48, 16, 640) == 256 + 8 * 48 * 640 * 4
+    assert f(256, 8, 128) == 256 + 8 * 256 * 128 * 4
+    assert f(257, 16, 640) == 0 and f(200, 4, 640) == 0 and f(0, 4, 640) == 0 and f(8, 0, 64) == 0
 
 
 def test_router_entry_points_validate_on_the_host(lib):
