@@ -742,6 +742,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
   auto compute_stage = [&](auto MBL_c, const uint8_t* sa, bool iss, uint8_t* nxt) __attribute__((always_inline)) {
     constexpr int KS = FP8 ? BKB / 64 : BKB / 32;
     constexpr int PER = (C::LOADS + KS - 1) / KS;
+    // e4m3 (one sub-step per stage): the next stage's loads go out between the M blocks'
+    // multiplies rather than together (measured 1.5-2.5 % faster there, 1-3 % slower on the
+    // bf16 tiles)
+    constexpr bool SPREAD = FP8;
     if constexpr (APIPE) {
       constexpr int MBL = decltype(MBL_c)::value;
       frag_t af[2], bfr[2][C::NB];
@@ -750,12 +754,17 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + 1 < KS) load_b(sa, ks + 1, bfr[(ks + 1) & 1]);
-        if (iss) {
+        if (iss && !(SPREAD && MBL > 0)) {
 #pragma unroll
           for (int q = ks * PER; q < (ks + 1) * PER && q < C::LOADS; ++q) issue_one(nxt, q);
         }
 #pragma unroll
         for (int i = 0; i < MBL; ++i) {
+          if (SPREAD && iss) {
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+              if (j * MBL / PER == i && ks * PER + j < C::LOADS) issue_one(nxt, ks * PER + j);
+          }
           const int f = ks * MBL + i;  // fragment f sits in af[f & 1]
           if (i + 1 < MBL) af[(f + 1) & 1] = load_a(sa, ks, i + 1);
           else if (ks + 1 < KS) af[(f + 1) & 1] = load_a(sa, ks + 1, 0);
