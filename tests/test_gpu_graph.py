@@ -29,11 +29,20 @@ def _bits(t):
     return t.view(torch.int16).cpu().numpy().copy()
 
 
-@pytest.mark.parametrize("name", ["qwen3", "llama4"])
+# decode steps of one or two tokens, whose expert GEMMs split over K (partial sums in the
+# workspace, then a second launch): inference with a shared expert, and a training step
+SPLIT = {
+    "dec_split_shared": W.custom("dec_split_shared", T=2, H=1024, E=16, k=1, I=512, score=W.SIGMOID,
+                                 shared_I=512),
+    "dec_split_train": W.custom("dec_split_train", T=2, H=768, E=16, k=2, I=256, training=True),
+}
+
+
+@pytest.mark.parametrize("name", ["qwen3", "llama4", "dec_split_shared", "dec_split_train"])
 def test_graph_replay_matches_eager(name):
-    w = W.WORKLOADS[name]
+    w = SPLIT[name] if name in SPLIT else W.WORKLOADS[name]
     _say("graph", name)
-    d = W.make_inputs(name)
+    d = W.make_inputs(w)
     g = GpuMoE(w, d)
     g.forward()
     outs = [g.y]
