@@ -6,6 +6,10 @@
 namespace moe {
 
 // mx.hip: MXFP8 (e4m3 codes, one E8M0 scale byte per 32 along K)
+// The dispatch copy (times prob[t,j] when given) fused with the MXFP8 row quantisation of
+// its copies: xp rows (bf16, H values) plus their e4m3 codes q and block scales (H % 32 == 0).
+hipError_t launch_scatter_rows_mx(const void* x, const int32_t* row_of, const float* prob, int T,
+                                  int H, int k, void* xp, uint8_t* q, uint8_t* scale, hipStream_t s);
 hipError_t launch_mx_quantize_rows(const void* x, int R, int C, uint8_t* q, uint8_t* scale,
                                    hipStream_t s);
 hipError_t launch_mx_quantize_weights(const void* w, int G, int K, int N, uint8_t* q,

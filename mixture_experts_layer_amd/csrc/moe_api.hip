@@ -940,6 +940,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
   const bool at_act = p->weight_placement == MOE_PLACE_ACTIVATION;
   float* row_prob = at_act ? (float*)((uint8_t*)ws + make_layout(*p).row_prob) : nullptr;
   const bool plain = router_opts_plain(ro, p->score);
+  bool xq_done = false;  // MXFP8: the row copies were quantised as they were written
   if (plain && route_dispatch_small_fits(T, E, k) && align == 1 && !fp8 && !at_input && !at_act) {
     // a decode-sized step: routing, dispatch and row copies in one launch
     MOE_TRY(launch_route_dispatch_small(logits, T, E, k, p->score, v.topk_idx, v.topk_prob,
@@ -960,14 +961,21 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_tensors_t* t, void* w
     if (align > 1)  // zero padding rows (fp8 scale / ScaledSwiGLU weight 1), src_of -1
       MOE_TRY(launch_zero_pad_rows(v.offsets, v.counts, E, fp8 ? H : 2 * H, v.xp,
                                    fp8 ? v.xp_scale : row_prob, v.src_of, s));
-    if (fp8) MOE_TRY(launch_scatter_rows_fp8(t->x, v.row_of, T, H, k, (uint8_t*)v.xp, v.xp_scale, s));
-    else MOE_TRY(launch_scatter_rows(t->x, v.row_of, at_input ? v.topk_prob : nullptr, T, H, k,
-                                     v.xp, s, v.topk_prob, row_prob));
+    if (fp8) {
+      MOE_TRY(launch_scatter_rows_fp8(t->x, v.row_of, T, H, k, (uint8_t*)v.xp, v.xp_scale, s));
+    } else if (mx && align == 1 && !at_act) {
+      MOE_TRY(launch_scatter_rows_mx(t->x, v.row_of, at_input ? v.topk_prob : nullptr, T, H, k, v.xp,
+                                     (uint8_t*)v.xq, v.xq_scale, s));
+      xq_done = true;
+    } else {
+      MOE_TRY(launch_scatter_rows(t->x, v.row_of, at_input ? v.topk_prob : nullptr, T, H, k, v.xp, s,
+                                  v.topk_prob, row_prob));
+    }
   }
   if (mx) {
     // MXFP8 (te_mixtral's mxfp8 recipe): rows quantised per 32-element block, block-scaled
     // GEMMs; the weight arguments hold codes and scale bytes (moe_quantize_mxfp8_weights)
-    MOE_TRY(launch_mx_quantize_rows(v.xp, N, H, (uint8_t*)v.xq, v.xq_scale, s));
+    if (!xq_done) MOE_TRY(launch_mx_quantize_rows(v.xp, N, H, (uint8_t*)v.xq, v.xq_scale, s));
     MOE_TRY(launch_mx_gemm(EPI_SWIGLU, v.xq, v.xq_scale, t->w_gu, (const uint8_t*)t->w_gu_scale,
                            v.offsets, E, N, 2 * I, H, I, v.h, s, nullptr,
                            p->training ? v.gu : nullptr));
@@ -1110,12 +1118,19 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
   float* const row_prob = at_act ? (float*)((uint8_t*)ws + L.row_prob) : nullptr;
   float* const row_part = at_act && p->router ? (float*)((uint8_t*)ws + L.row_part) : nullptr;
   int32_t* const gsched = (int32_t*)((uint8_t*)ws + L.sched);  // zero since the forward
+  // MXFP8 without padding: the d_out copies are quantised as they are written
+  const bool dq_fused = mx && p->align_size <= 1;
+  bool dq_done = false;
   if (T == 0) {
     // no routed rows: the weight gradients are zero (the dW GEMMs see empty groups)
     MOE_TRY(launch_fill_i32(v.offsets, E + 1, 0, s));
   } else if (at_input || at_act) {
     // the combine was unweighted: d_out[row_of[t,j]] = dy[t]
-    MOE_TRY(launch_scatter_rows(dy, v.row_of, nullptr, T, H, k, v.d_out, s));
+    if (dq_fused)
+      MOE_TRY(launch_scatter_rows_mx(dy, v.row_of, nullptr, T, H, k, v.d_out, (uint8_t*)v.xq,
+                                     v.xq_scale, s));
+    else MOE_TRY(launch_scatter_rows(dy, v.row_of, nullptr, T, H, k, v.d_out, s));
+    dq_done = dq_fused;
   } else if (p->router) {
     // combine backward with the routing-weight gradient: d_out, d_logits and the split
     // operand of the router weight gradient
@@ -1125,7 +1140,11 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
                                       router_split_cols(E), s));
   } else {
     // combine backward: d_out[row_of[t,j]] = bf16(p[t,j] * dy[t])
-    MOE_TRY(launch_scatter_rows(dy, v.row_of, v.topk_prob, T, H, k, v.d_out, s));
+    if (dq_fused)
+      MOE_TRY(launch_scatter_rows_mx(dy, v.row_of, v.topk_prob, T, H, k, v.d_out, (uint8_t*)v.xq,
+                                     v.xq_scale, s));
+    else MOE_TRY(launch_scatter_rows(dy, v.row_of, v.topk_prob, T, H, k, v.d_out, s));
+    dq_done = dq_fused;
   }
   float* const r_part = p->router ? (float*)((uint8_t*)v.router_ws + router_wgrad_dls_bytes(T, E))
                                    : nullptr;
@@ -1140,7 +1159,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const moe_tensors_t* t, const 
     // operands blocked along each expert's tokens
     const int Kp = v.mx_kp;
     if (N > 0) {
-      MOE_TRY(launch_mx_quantize_rows(v.d_out, N, H, (uint8_t*)v.xq, v.xq_scale, s));
+      if (!dq_done) MOE_TRY(launch_mx_quantize_rows(v.d_out, N, H, (uint8_t*)v.xq, v.xq_scale, s));
       MOE_TRY(launch_mx_gemm(EPI_SWIGLU_BWD, v.xq, v.xq_scale, t->w_down_bwd, t->w_down_bwd_scale,
                              v.offsets, E, N, I, H, I, v.dgu, s, v.gu, nullptr));
       MOE_TRY(launch_mx_quantize_rows(v.dgu, N, 2 * I, v.dgq, v.dgq_scale, s));

@@ -77,6 +77,92 @@ __global__ __launch_bounds__(256) void mx_quantize_rows_kernel(const u32x4_t* __
   }
 }
 
+namespace {
+// One 16-byte piece (8 bf16) of a 32-value block whose four pieces sit in four neighbouring
+// lanes (all four lanes call this together): the block scale exponent and the 8 codes, as
+// mx_quantize_rows_kernel forms them.
+MOE_DEV void mx_quant8(const u32x4_t v, uint32_t (&w)[2], int& se) {
+  float f[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    f[2 * d] = bf16lo(v[d]);
+    f[2 * d + 1] = bf16hi(v[d]);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(f[e]));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  se = mx_scale_exp(m);
+  const float inv = exp2i(-se);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float t[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = fminf(fmaxf(f[4 * h + e] * inv, -448.f), 448.f);
+    w[h] = pack_e4m3x4(t[0], t[1], t[2], t[3]);
+  }
+}
+}  // namespace
+
+// The dispatch copy fused with the MXFP8 row quantisation of its copies: each token's row
+// is read once; each of its k copies (times prob[t,j] and rounded to bf16 when prob is
+// given) goes to xp[row_of[t,j]] as bf16 and to q / scale as e4m3 codes and block scales,
+// equal to what mx_quantize_rows_kernel makes of that xp row. TPB tokens per block.
+template <int TPB>
+__global__ __launch_bounds__(256) void scatter_rows_mx_kernel(const u32x4_t* __restrict__ x,
+                                                              const int32_t* __restrict__ row_of,
+                                                              const float* __restrict__ prob, int T,
+                                                              int H8, int k, u32x4_t* __restrict__ xp,
+                                                              uint32_t* __restrict__ q,
+                                                              uint8_t* __restrict__ scale) {
+  __shared__ int rows[TPB][32];
+  __shared__ float pw[TPB][32];
+  const int t0 = blockIdx.x * TPB;
+  if ((int)threadIdx.x < TPB * k) {
+    const int b = threadIdx.x / k, j = threadIdx.x - b * k, t = t0 + b;
+    if (t < T) {
+      rows[b][j] = row_of[(size_t)t * k + j];
+      pw[b][j] = prob ? prob[(size_t)t * k + j] : 1.f;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < TPB; ++b) {
+    const int t = t0 + b;
+    if (t >= T) break;
+    // every lane of a 32-value block (four neighbouring lanes) runs the same iterations
+    for (int v = threadIdx.x; v < H8; v += blockDim.x) {
+      const u32x4_t val = x[(size_t)t * H8 + v];
+      uint32_t w[2];
+      int se = 0;
+      if (!prob) mx_quant8(val, w, se);
+      for (int j = 0; j < k; ++j) {
+        const size_t r = (size_t)rows[b][j];
+        u32x4_t o = val;
+        if (prob) {
+          const float g = pw[b][j];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(g * bf16lo(val[d]), g * bf16hi(val[d]));
+          mx_quant8(o, w, se);
+        }
+        __builtin_nontemporal_store(o, &xp[r * H8 + v]);
+        *(u32x2_t*)&q[(r * H8 + v) * 2] = u32x2_t{w[0], w[1]};
+        if ((v & 3) == 0) scale[r * (H8 / 4) + v / 4] = (uint8_t)(se + 127);
+      }
+    }
+  }
+}
+
+hipError_t launch_scatter_rows_mx(const void* x, const int32_t* row_of, const float* prob, int T,
+                                  int H, int k, void* xp, uint8_t* q, uint8_t* scale, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  constexpr int TPB = 2;
+  scatter_rows_mx_kernel<TPB><<<(T + TPB - 1) / TPB, 256, 0, s>>>(
+      (const u32x4_t*)x, row_of, prob, T, H / 8, k, (u32x4_t*)xp, (uint32_t*)q, scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx_quantize_rows(const void* x, int R, int C, uint8_t* q, uint8_t* scale,
                                    hipStream_t s) {
   const size_t n8 = (size_t)R * C / 8;
