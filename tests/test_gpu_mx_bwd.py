@@ -277,27 +277,31 @@ def test_layer_mxfp8_training_with_router():
     check_fp8(host_vals(g.dw_router)[C], rb["dw_router"][C], "mx router dw_router", rel_l2=1e-2)
 
 
-def test_layer_mxfp8_dispatch_codes_bit_exact():
-    # the dispatch writes each row copy and its MXFP8 codes in one pass (forward: the x
-    # rows; backward: the combine-backward rows d_out = bf16(p dy), one quantisation per
-    # weighted copy): codes and scale bytes equal the oracle's quantisation of the bf16
-    # rows the layer kept
-    w = W.custom("mx_codes", T=300, H=256, E=16, k=4, I=192)
-    _say("layer mxfp8 dispatch codes")
+def test_layer_mxfp8_fused_codes_bit_exact():
+    # the MXFP8 row codes of every row-blocked GEMM operand of the layer: written by the
+    # dispatch copies as they go (forward: the x rows; backward: the combine-backward rows
+    # d_out = bf16(p dy), one quantisation per weighted copy) or by the row quantiser (h,
+    # dgu). Codes and scale bytes equal the oracle's quantisation of the bf16 rows the layer
+    # kept (I = 192: the second 128-column h tile half full; skewed routing with empty
+    # experts)
+    w = W.custom("mx_codes", T=300, H=256, E=16, k=4, I=192, zipf_s=1.2, n_empty=3)
+    _say("layer mxfp8 fused codes")
     d = W.make_inputs(w)
     dy = W.to_bf16_bits(np.random.default_rng(2).standard_normal((w.T, w.H)).astype(np.float32))
     g = GpuMoE(w, d, training=True, mx=True)
     g.forward()
-    N, H = w.T * w.k, w.H
+    N, H, I = w.T * w.k, w.H, w.I
 
-    def codes_match(rows_name, label):
-        rows = g.view(rows_name, (N, H), torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16)
-        q = g.view("xq", (N, H), torch.uint8).cpu().numpy()
-        s = g.view("xq_scale", (N, H // 32), torch.uint8).cpu().numpy()
+    def codes_match(rows_name, C, q_name, s_name, label):
+        rows = g.view(rows_name, (N, C), torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16)
+        q = g.view(q_name, (N, C), torch.uint8).cpu().numpy()
+        s = g.view(s_name, (N, C // 32), torch.uint8).cpu().numpy()
         rq, rs = O.quantize_mx_e4m3(O.as_values(rows))
         assert np.array_equal(s, rs), f"{label}: scale bytes"
         assert np.array_equal(q, rq), f"{label}: codes"
 
-    codes_match("xp", "forward xp")
+    codes_match("xp", H, "xq", "xq_scale", "forward xp")
+    codes_match("h", I, "hq", "hq_scale", "forward h")
     g.backward(dy)
-    codes_match("d_out", "backward d_out")
+    codes_match("d_out", H, "xq", "xq_scale", "backward d_out")
+    codes_match("dgu", 2 * I, "dgq", "dgq_scale", "backward dgu")
