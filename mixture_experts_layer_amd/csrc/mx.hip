@@ -270,7 +270,9 @@ __global__ __launch_bounds__(256) void mx_quantize_cols_kernel(
     uint8_t* __restrict__ st) {
   __shared__ uint16_t s_x[kColTile * kColLd];
   const int tid = threadIdx.x;
-  const int p0 = blockIdx.x * kColTile, c0 = blockIdx.y * kColTile;
+  // channel tiles vary fastest over the grid, so blocks that run together read neighbouring
+  // 128-byte pieces of the same rows (measured 8-17 % faster than token tiles fastest)
+  const int p0 = blockIdx.y * kColTile, c0 = blockIdx.x * kColTile;
   if (p0 >= co[G]) return;  // past the last expert's range (uniform per block)
   int lo = 0, hi = G - 1;   // the expert whose range holds p0: co[e] <= p0 < co[e+1]
   while (lo < hi) {
@@ -323,7 +325,7 @@ hipError_t launch_mx_quantize_cols(const void* x, int R, int C, const int32_t* o
                                    const int32_t* col_offsets, int G, int Kp, uint8_t* qt,
                                    uint8_t* st, hipStream_t s) {
   if (Kp == 0 || C == 0) return hipSuccess;
-  const dim3 grid((unsigned)(Kp / kColTile), (unsigned)((C + kColTile - 1) / kColTile));
+  const dim3 grid((unsigned)((C + kColTile - 1) / kColTile), (unsigned)(Kp / kColTile));
   mx_quantize_cols_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, R, C, offsets, col_offsets,
                                                G, Kp, qt, st);
   return hipGetLastError();
