@@ -1363,8 +1363,9 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 // (whose epilogue reads the saved g,u): the same 320x256 tiles when they still give every
 // CU at least four tiles, else 320x128 tiles with four waves and a four-stage ring (fewer
 // tiles per CU leave too many CUs idle at the end). e4m3: 256x256 tiles with eight waves
-// and a three-stage ring of 64-byte (64-element) K steps, A fragments read one M block
-// ahead of the multiply so that the 8-register e4m3 fragments fit.
+// and a four-stage ring of 64-byte (64-element) K steps (1-2 % faster than three), A
+// fragments read one M block ahead of the multiply so that the 8-register e4m3 fragments
+// fit.
 #ifndef MOE_GEMM_TILE_BF16
 #define MOE_GEMM_TILE_BF16 320, 256, 2, 4, 3, 64
 #endif
@@ -1381,7 +1382,7 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 #define MOE_GEMM_TILE_BF16_SWIGLU_BWD_NARROW 320, 128, 2, 2, 4, 64
 #endif
 #ifndef MOE_GEMM_TILE_FP8
-#define MOE_GEMM_TILE_FP8 256, 256, 2, 4, 3, 64
+#define MOE_GEMM_TILE_FP8 256, 256, 2, 4, 4, 64
 #endif
 // Small-M tiles (decode: a handful of rows per expert): 32-row tiles, since a decode step
 // only streams weights. The store GEMM: 128 output columns per block (two waves) and four
