@@ -247,7 +247,8 @@ moe_status_t moe_permute_padded(const void* x, const int32_t* topk_idx, int T, i
  *  h       [rows,I] bf16 out: silu(g) * u, g and u held in fp32.
  *  gu_saved [rows,2I] bf16 out, nullable: g and u rounded to bf16 (for backward).
  *  ws, ws_bytes: nullable split-K space (see moe_grouped_gemm_splitk_workspace_bytes with
- *          ncols = 2I); ignored by shapes that never split. */
+ *          ncols = 2I); ignored by shapes that never split; a space smaller than that size
+ *          returns MOE_ERR_INVALID_ARG before any launch. */
 moe_status_t moe_grouped_gemm_swiglu(const void* xp, const float* xp_scale, const void* w_gu,
                                      const float* w_scale, const int32_t* offsets, int G,
                                      int rows, int H, int I, int dtype, void* h, void* gu_saved,
@@ -259,7 +260,8 @@ moe_status_t moe_grouped_gemm_swiglu(const void* xp, const float* xp_scale, cons
  *  c_dtype MOE_BF16 or MOE_FP32 (fp32 accumulation in every case). M is used by
  *  MOE_GEMM_TN_DW only, K by NN/NT only.
  *  ws, ws_bytes: nullable split-K space (moe_grouped_gemm_splitk_workspace_bytes with
- *  ncols = N); ignored by shapes that never split. */
+ *  ncols = N); ignored by shapes that never split; a space smaller than that size returns
+ *  MOE_ERR_INVALID_ARG before any launch. */
 moe_status_t moe_grouped_gemm(int mode, const void* A, const float* a_scale, const void* B,
                               const float* b_scale, const int32_t* offsets, int G, int rows,
                               int M, int N, int K, int dtype, void* C, int c_dtype, void* ws,
