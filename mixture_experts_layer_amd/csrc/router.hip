@@ -389,9 +389,27 @@ __global__ __launch_bounds__(512) void route_dispatch_small_kernel(
     src_of[row] = tid / k;
   }
   __syncthreads();
-  for (int i = tid; i < n * H8; i += blockDim.x) {
-    const int f = i / H8, v = i - f * H8;
-    __builtin_nontemporal_store(x[(size_t)(f / k) * H8 + v], &xp[(size_t)s_row[f] * H8 + v]);
+  // the row copies, eight 16-byte pieces per thread requested before any is stored (one
+  // load latency per batch instead of one per piece)
+  const int total = n * H8;
+  for (int i0 = tid; i0 < total; i0 += 8 * blockDim.x) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * (int)blockDim.x;
+      if (i < total) {
+        const int f = i / H8, c = i - f * H8;
+        v[u] = x[(size_t)(f / k) * H8 + c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * (int)blockDim.x;
+      if (i < total) {
+        const int f = i / H8, c = i - f * H8;
+        __builtin_nontemporal_store(v[u], &xp[(size_t)s_row[f] * H8 + c]);
+      }
+    }
   }
 }
 
