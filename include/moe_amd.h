@@ -316,7 +316,9 @@ moe_status_t moe_permute_probs(const int32_t* row_of, const float* topk_prob, in
  * blocks, resident = compute units x blocks per unit, and every block walks its share of
  * the tiles. max_blocks > 0 lowers the cap to that many blocks (leaving compute units to
  * concurrent work, or forcing many tiles per block); 0 restores the default. Process-wide
- * host setting, read at launch time. MOE_ERR_INVALID_ARG for max_blocks < 0. */
+ * host setting, read once by each launch as it is enqueued (an atomic: any host thread may
+ * set it; launches already enqueued keep the grid they were given). MOE_ERR_INVALID_ARG for
+ * max_blocks < 0. */
 moe_status_t moe_set_gemm_max_blocks(int max_blocks);
 
 /* Token combine (guide, "Token combine"): y[t] = sum_j p[t,j] * y_perm[row_of[t,j]]

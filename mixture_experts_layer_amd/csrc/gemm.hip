@@ -1297,7 +1297,9 @@ int device_cus() {
   return cache[dev];
 }
 
-int g_max_blocks = 0;  // grid cap set through moe_set_gemm_max_blocks (0: none)
+// grid cap set through moe_set_gemm_max_blocks (0: none); atomic so that a launch on one
+// host thread may read it while another thread sets it (each launch reads it once)
+std::atomic<int> g_max_blocks{0};
 std::atomic<unsigned> g_launch_seq{0};  // picks the tile-counter slot of each launch
 
 template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int BKB>
@@ -1318,6 +1320,7 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   if ((long long)BM * row_bytes >= kOutOfRange) return hipErrorInvalidValue;
   static int resident_cache[64];  // one per instantiation of launch_cfg
   const int resident = persistent_blocks(kern, C::NT, resident_cache);
+  const int max_blocks = g_max_blocks.load(std::memory_order_relaxed);
   if (resident <= 0) return hipErrorInvalidValue;
   // split-K (32-row bf16 tiles): up to kSplitKMax parts per tile, fp32 partial rows of
   // 2I (SwiGLU) or N columns. Offered to the device only when even the most tiles the rows
@@ -1332,12 +1335,12 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
     const long long mt = (long long)(p.rows + BM - 1) / BM + p.G;
     const long long most = (mt < p.rows ? mt : (long long)p.rows) * ntn;
     int blocks = resident;
-    if (g_max_blocks > 0 && g_max_blocks < blocks) blocks = g_max_blocks;
+    if (max_blocks > 0 && max_blocks < blocks) blocks = max_blocks;
     split = most < blocks;
     if (split) tiles *= kSplitKMax;
   }
   long long grid = tiles < resident ? tiles : resident;
-  if (g_max_blocks > 0 && grid > g_max_blocks) grid = g_max_blocks;
+  if (max_blocks > 0 && grid > max_blocks) grid = max_blocks;
   GemmParams q = p;
   if (!split) q.part = nullptr;
   q.sched_slot = (int)(g_launch_seq.fetch_add(1, std::memory_order_relaxed) % kSchedSlots);
@@ -1418,7 +1421,8 @@ hipError_t launch_sel(const GemmParams& p, hipStream_t s) {
       // against the blocks a launch can have
       const long long wide = ((long long)(p.rows + 319) / 320 + p.G) * ((p.N + 255) / 256);
       int blocks = device_cus();
-      if (g_max_blocks > 0 && g_max_blocks < blocks) blocks = g_max_blocks;
+      const int max_blocks = g_max_blocks.load(std::memory_order_relaxed);
+      if (max_blocks > 0 && max_blocks < blocks) blocks = max_blocks;
       if (wide >= 4LL * blocks) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU_BWD>(p, s);
       return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU_BWD_NARROW>(p, s);
     }
@@ -1429,7 +1433,7 @@ hipError_t launch_sel(const GemmParams& p, hipStream_t s) {
 }
 }  // namespace
 
-void set_gemm_max_blocks(int n) { g_max_blocks = n; }
+void set_gemm_max_blocks(int n) { g_max_blocks.store(n, std::memory_order_relaxed); }
 
 size_t splitk_workspace_bytes(long long rows, int G, long long ncols) {
   if (rows <= 0 || G <= 0 || ncols <= 0 || !small_m_rows(rows, G)) return 0;
