@@ -24,9 +24,10 @@ namespace moe {
 
 int router_chunk_tokens(int T) {
   // whole-token chunks for the fused router histogram: at most 512 chunks, a multiple of
-  // 32 tokens (one router block step)
+  // 32 tokens (one router block step), never zero (T == 0 still sizes a workspace)
   int c = (T + 511) / 512;
-  return (c + 31) / 32 * 32;
+  c = (c + 31) / 32 * 32;
+  return c > 0 ? c : 32;
 }
 
 size_t permute_scratch_bytes(int T, int E, int k) {

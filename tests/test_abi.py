@@ -129,3 +129,40 @@ def test_mxfp8_backward_entry_points_validate_on_the_host(lib):
     assert sb(fake, fake, fake, fake, fake, 4, 100, 64, 200, fake, fake, None) == 2  # K % 64
     assert sb(fake, fake, fake, fake, fake, 4, 100, 64, 256, None, fake, None) == 1  # no g,u
     assert sb(fake, fake, fake, fake, fake, 4, 0, 64, 256, fake, fake, None) == 0    # no rows
+
+
+_SIZE_SWEEP = r"""
+import itertools, sys
+import mixture_experts_layer_amd as M
+Ts = (0, 1, 2, 31, 32, 33, 257, 4096, 8193, 65536)
+variants = []
+for training, router, placement, align, dtype, shared in itertools.product(
+        (False, True), (False, True), (M.MOE_PLACE_COMBINE, M.MOE_PLACE_INPUT, M.MOE_PLACE_ACTIVATION),
+        (0, 128), (M.MOE_BF16, M.MOE_FP8_E4M3, M.MOE_MXFP8), (0, 192)):
+    if dtype == M.MOE_FP8_E4M3 and training:
+        continue
+    variants.append(dict(training=training, router=router, weight_placement=placement,
+                         align_size=align, dtype=dtype, shared_I=shared))
+for v in variants:
+    sizes = []
+    for T in Ts:
+        print(T, v, flush=True)
+        sizes.append(int(M.lib().moe_workspace_bytes(M.ctypes.byref(M.problem(T, 256, 16, 4, 192, 0, **v)))))
+    # a combination the layer does not take gets 0 for every T; any other, a size for every T
+    assert all(n == 0 for n in sizes) or all(n > 0 for n in sizes), (v, sizes)
+for T in Ts:
+    for E, k in ((8, 2), (128, 8), (256, 32)):
+        assert M.moe_permute_workspace_bytes(T, E, k) > 0
+        assert M.moe_aux_loss_workspace_bytes(T, E) > 0
+        assert M.moe_grouped_gemm_splitk_workspace_bytes(T, E, 256) >= 0
+print("sizes ok", flush=True)
+"""
+
+
+def test_workspace_sizes_for_every_token_count():
+    # host-only size queries answer for every token count, T = 0 included (no division by
+    # a zero chunk size)
+    r = subprocess.run([sys.executable, "-c", _SIZE_SWEEP], cwd=ROOT, capture_output=True,
+                       text=True, timeout=300)
+    tail = "\n".join((r.stdout + r.stderr).splitlines()[-5:])
+    assert r.returncode == 0 and "sizes ok" in r.stdout, tail

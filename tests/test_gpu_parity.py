@@ -547,3 +547,41 @@ def test_invalid_arguments_return_status():
                            None, 0, None) == M.MOE_ERR_INVALID_ARG
     with pytest.raises(M.MoeError):
         M.moe_forward(M.problem(8, 128, 4, 2, 128, 0), M.tensors(x, None, x, x, x), x.view(torch.uint8))
+
+
+def test_zero_tokens_is_a_no_op():
+    # T = 0: the stand-alone calls write only what has a size (the router's counts, the
+    # dispatch offsets: all zero), the layer forward does nothing, and the layer backward
+    # writes zero weight gradients (every expert is empty)
+    _say("zero tokens")
+    H, E, k, I = 128, 8, 2, 128
+    cuda = dict(device="cuda")
+    logits = torch.empty((0, E), **cuda)
+    idx = torch.empty((0, k), dtype=torch.int32, **cuda)
+    prob = torch.empty((0, k), **cuda)
+    counts = torch.full((E,), -1, dtype=torch.int32, **cuda)
+    M.moe_router_topk(logits, k, O.SOFTMAX_PRE_RENORM, idx, prob, counts)
+    x = torch.empty((0, H), dtype=torch.bfloat16, **cuda)
+    xp = torch.empty((0, H), dtype=torch.bfloat16, **cuda)
+    offs = torch.full((E + 1,), -1, dtype=torch.int32, **cuda)
+    row_of = torch.empty((0, k), dtype=torch.int32, **cuda)
+    src_of = torch.empty((0,), dtype=torch.int32, **cuda)
+    ws = torch.empty(M.moe_permute_workspace_bytes(0, E, k), dtype=torch.uint8, **cuda)
+    M.moe_permute(x, idx, E, xp, offs, row_of, src_of, ws)
+    y = torch.empty((0, H), dtype=torch.bfloat16, **cuda)
+    M.moe_unpermute_combine(xp, row_of, prob, y)
+    torch.cuda.synchronize()
+    assert (counts == 0).all() and (offs == 0).all()
+
+    rng = np.random.default_rng(0)
+    wgu = dev_bf16(O.f32_to_bf16_bits(0.02 * rng.standard_normal((E, H, 2 * I)).astype(np.float32)))
+    wd = dev_bf16(O.f32_to_bf16_bits(0.02 * rng.standard_normal((E, I, H)).astype(np.float32)))
+    prob_l = M.problem(0, H, E, k, I, O.SOFTMAX_PRE_RENORM, training=True)
+    lws = torch.zeros(M.moe_workspace_bytes(prob_l), dtype=torch.uint8, **cuda)
+    tens = M.tensors(x, logits, wgu, wd, y)
+    M.moe_forward(prob_l, tens, lws)
+    dwgu = torch.full_like(wgu, float("nan"))
+    dwd = torch.full_like(wd, float("nan"))
+    M.moe_backward(prob_l, tens, y, torch.empty_like(x), dwgu, dwd, lws)
+    torch.cuda.synchronize()
+    assert (dwgu == 0).all() and (dwd == 0).all()
