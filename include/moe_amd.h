@@ -37,7 +37,9 @@
  *    caller's error and are not checked on the device.
  *  - Supported sizes: 1 <= k <= min(E, 32), E <= 256, H % 64 == 0, I % 64 == 0,
  *    one expert's weight matrix under 4 GiB (and 512 rows of the GEMM's activation
- *    operand under 4 GiB), every pointer 16-byte aligned.
+ *    operand under 4 GiB), T*(k+1) + 256*4095 routed rows within int32 (row ids and
+ *    offsets are int32), T*k*H <= 2^40, every pointer 16-byte aligned; larger sizes
+ *    return MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_AMD_H
 #define MOE_AMD_H

@@ -24,6 +24,9 @@ moe_status_t check_shape(int T, int H, int E, int k) {
   if (k > 32 || E > 256) return MOE_ERR_UNSUPPORTED;
   if (H % 64) return MOE_ERR_UNSUPPORTED;
   if ((long long)T * k * (long long)(H > 0 ? H : 1) > (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  // routed rows (T k, plus T of a shared expert, plus at most 256 x 4095 of padding) are
+  // int32 row ids and offsets
+  if ((long long)T * (k + 1) + 256LL * 4095 > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -539,7 +542,7 @@ moe_status_t moe_grouped_gemm_swiglu_scaled_bwd(const void* d_out, const void* w
 moe_status_t moe_permute_probs(const int32_t* row_of, const float* topk_prob, int T, int k,
                                float* row_prob, void* stream) {
   if (T < 0 || k <= 0) return MOE_ERR_INVALID_ARG;
-  if (k > 32) return MOE_ERR_UNSUPPORTED;
+  if (k > 32 || (long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;  // int32 row ids
   if (T == 0) return MOE_OK;
   if (!ok_ptr(row_of) || !ok_ptr(topk_prob) || !ok_ptr(row_prob)) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_row_weights(row_of, topk_prob, T, k, row_prob, S(stream)));
@@ -549,7 +552,7 @@ moe_status_t moe_unpermute_combine(const void* y_perm, const int32_t* row_of,
                                    const float* topk_prob, const void* shared_out, int T,
                                    int H, int k, void* y, void* stream) {
   if (T < 0 || H <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
-  if (k > 32) return MOE_ERR_UNSUPPORTED;
+  if (k > 32 || (long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;  // int32 row ids
   if (H % 64) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(y_perm) || !ok_ptr(row_of) || !ok_ptr(y) || !opt_ptr(topk_prob) ||
@@ -561,7 +564,7 @@ moe_status_t moe_unpermute_combine(const void* y_perm, const int32_t* row_of,
 moe_status_t moe_combine_backward(const void* dy, const int32_t* row_of, const float* topk_prob,
                                   int T, int H, int k, void* d_out, void* stream) {
   if (T < 0 || H <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
-  if (k > 32) return MOE_ERR_UNSUPPORTED;
+  if (k > 32 || (long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;  // int32 row ids
   if (H % 64) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(dy) || !ok_ptr(row_of) || !ok_ptr(topk_prob) || !ok_ptr(d_out))

@@ -166,3 +166,23 @@ def test_workspace_sizes_for_every_token_count():
                        text=True, timeout=300)
     tail = "\n".join((r.stdout + r.stderr).splitlines()[-5:])
     assert r.returncode == 0 and "sizes ok" in r.stdout, tail
+
+
+def test_routed_rows_beyond_int32_are_refused(lib):
+    # row ids and offsets are int32: with a narrow hidden size the routed rows T*k can pass
+    # the T*k*H bound and still overflow them; every shape check refuses such a T before
+    # touching a pointer (MOE_ERR_UNSUPPORTED = 2)
+    import mixture_experts_layer_amd as M
+    T, H, E, k = 1 << 26, 64, 256, 32          # T*k = 2^31 rows, T*k*H = 2^37
+    assert lib.moe_router_topk(None, T, E, k, 0, None, None, None, None, None, None) == 2
+    assert lib.moe_permute(None, None, T, H, E, k, 0, None, None, None, None, None, None, 0,
+                           None) == 2
+    assert lib.moe_unpermute_combine(None, None, None, None, T, H, k, None, None) == 2
+    assert lib.moe_combine_backward(None, None, None, T, H, k, None, None) == 2
+    assert lib.moe_permute_probs(None, None, T, k, None, None) == 2
+    lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.moe_workspace_bytes(ctypes.byref(M.problem(T, H, E, k, 64, 0))) == 0
+    # just inside the bound the size query answers
+    T_ok = (0x7fffffff - 256 * 4095) // (k + 1)
+    assert lib.moe_workspace_bytes(ctypes.byref(M.problem(T_ok, H, E, k, 64, 0))) > 0
+    assert lib.moe_workspace_bytes(ctypes.byref(M.problem(T_ok + 1, H, E, k, 64, 0))) == 0
