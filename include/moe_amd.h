@@ -34,7 +34,8 @@
  *    not handle); a failed kernel launch returns MOE_ERR_HIP; a workspace smaller
  *    than required returns MOE_ERR_WORKSPACE. Nothing is enqueued when a check
  *    fails. T == 0 is a valid no-op. Out-of-range expert ids in topk_idx are the
- *    caller's error and are not checked on the device.
+ *    caller's error and are not checked on the device; so are device group offsets
+ *    passed to the grouped GEMMs that are not non-decreasing within [0, rows].
  *  - Supported sizes: 1 <= k <= min(E, 32), E <= 256, H % 64 == 0, I % 64 == 0,
  *    one expert's weight matrix under 4 GiB (and 512 rows of the GEMM's activation
  *    operand under 4 GiB), T*(k+1) + 256*4095 routed rows within int32 (row ids and
