@@ -105,6 +105,11 @@ MOE_DEV void load_lds16_s(const void* base, uint32_t off, uint8_t* lds) {
   const unsigned m0 = (unsigned)(uintptr_t)((lds_u8_t*)lds);
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
 }
+// The same with the non-temporal cache policy, for data streamed once.
+MOE_DEV void load_lds16_s_nt(const void* base, uint32_t off, uint8_t* lds) {
+  const unsigned m0 = (unsigned)(uintptr_t)((lds_u8_t*)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
 
 template <int BM, int BN, int WM, int WN, int STAGES, int BKB_>
 struct Cfg {
@@ -234,9 +239,16 @@ MOE_DEV void wait_stage(int pend, int allow) {
 
 }  // namespace
 
-template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int BKB_>
+// BNT (NN only): the launch streams each weight panel once (its groups average at most one
+// M tile), so the weight tiles are loaded with the non-temporal policy and leave the caches
+// to the activation rows that several N tiles re-read. An NN weight tile is read as whole
+// runs of its columns per stage (256 or 512 contiguous bytes: every line used once); an NT
+// operand's 64-byte pieces share lines with the next stage, so NT keeps the default policy.
+template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int BKB_,
+          bool BNT = false>
 __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const GemmParams p) {
   using C = Cfg<BM, BN, WM, WN, STAGES, BKB_>;
+  static_assert(!BNT || MODE == MOE_GEMM_NN, "non-temporal weight loads: NN only");
   constexpr int BKB = C::BKB, KR = C::KR;
   constexpr int LEAD = STAGES - 1;  // stages in flight ahead of the one being multiplied
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
@@ -638,7 +650,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void grouped_gemm_kernel(const Gemm
       if constexpr (DW) {
         load_lds16((lk * KR + b_krow[j] < lt.kcount) ? b_src[j] + (size_t)lk * b_step : zero, dst);
       } else {
-        load_lds16_s(b_base + (size_t)lk * b_step, b_off[j], dst);
+        if constexpr (BNT) load_lds16_s_nt(b_base + (size_t)lk * b_step, b_off[j], dst);
+        else load_lds16_s(b_base + (size_t)lk * b_step, b_off[j], dst);
       }
     }
   };
@@ -1302,10 +1315,11 @@ int device_cus() {
 std::atomic<int> g_max_blocks{0};
 std::atomic<unsigned> g_launch_seq{0};  // picks the tile-counter slot of each launch
 
-template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int BKB>
+template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int BKB,
+          bool BNT = false>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   using C = Cfg<BM, BN, WM, WN, STAGES, BKB>;
-  auto kern = grouped_gemm_kernel<MODE, EPI, FP8, BM, BN, WM, WN, STAGES, BKB>;
+  auto kern = grouped_gemm_kernel<MODE, EPI, FP8, BM, BN, WM, WN, STAGES, BKB, BNT>;
   static_assert(C::SMEM + 2 * 264 * 4 + 64 + C::NW * 2048 <= 160 * 1024, "LDS budget");
   const int ntn = EPI == EPI_SWIGLU ? (p.I + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   // upper bound of the tile count (the exact count depends on offsets[], read on the device)
@@ -1405,15 +1419,21 @@ namespace {
 // average and at most 256 rows: the decode case
 bool small_m_rows(long long rows, int G) { return rows <= 256 && rows <= 32LL * G; }
 
+// The M-tile height of a tile configuration.
+constexpr int tile_rows(int bm, int, int, int, int, int) { return bm; }
+
 template <int MODE, int EPI, bool F8>
 hipError_t launch_sel(const GemmParams& p, hipStream_t s) {
+  // NN launches whose groups average at most one M tile stream each weight panel once
+  const auto nn_once = [&](int bm) { return (long long)p.rows <= (long long)p.G * bm; };
   if constexpr (F8) {
     return launch_cfg<MODE, EPI, true, MOE_GEMM_TILE_FP8>(p, s);
   } else {
     if constexpr (MODE != MOE_GEMM_TN_DW) {
-      if (small_m_rows(p.rows, p.G)) {
-        if constexpr (EPI == EPI_SWIGLU) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_SMALL_M_SWIGLU>(p, s);
-        else return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_SMALL_M>(p, s);
+      if (small_m_rows(p.rows, p.G)) {  // (at most 32 rows per group on average)
+        constexpr bool NT_W = MODE == MOE_GEMM_NN;
+        if constexpr (EPI == EPI_SWIGLU) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_SMALL_M_SWIGLU, NT_W>(p, s);
+        else return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_SMALL_M, NT_W>(p, s);
       }
     }
     if constexpr (EPI == EPI_SWIGLU_BWD) {
@@ -1426,9 +1446,18 @@ hipError_t launch_sel(const GemmParams& p, hipStream_t s) {
       if (wide >= 4LL * blocks) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU_BWD>(p, s);
       return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU_BWD_NARROW>(p, s);
     }
-    else if constexpr (EPI == EPI_SWIGLU) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU>(p, s);
+    else if constexpr (EPI == EPI_SWIGLU) {
+      if constexpr (MODE == MOE_GEMM_NN)
+        if (nn_once(tile_rows(MOE_GEMM_TILE_BF16_SWIGLU)))
+          return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU, true>(p, s);
+      return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_SWIGLU>(p, s);
+    }
     else if constexpr (MODE == MOE_GEMM_TN_DW) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16_DW>(p, s);
-    else return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16>(p, s);
+    else {
+      if constexpr (MODE == MOE_GEMM_NN)
+        if (nn_once(tile_rows(MOE_GEMM_TILE_BF16))) return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16, true>(p, s);
+      return launch_cfg<MODE, EPI, false, MOE_GEMM_TILE_BF16>(p, s);
+    }
   }
 }
 }  // namespace
