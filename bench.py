@@ -675,7 +675,7 @@ def main():
         except OSError:
             pass
         # cores: the BLAS threads the oracle's float64 products ran on (its only parallel
-        # part); host_cpus: every logical CPU the box shows
+        # part); host_cpus: every logical CPU of the host
         cpu = {"value": round(S / tc, 2), "unit": "tokens/s", "cores": threads,
                "host_cpus": os.cpu_count(), "cpu_model": model, "kind": "oracle",
                "sample": (f"the whole workload ({S} tokens)" if S == w.T else
