@@ -1283,31 +1283,35 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const GemmParams p) 
 namespace {
 
 // Resident blocks of one kernel on the current device (compute units x blocks per CU),
-// queried once per device and kernel: `cache` belongs to the caller's instantiation.
+// queried once per device and kernel: `cache` belongs to the caller's instantiation. The
+// entries are atomics so that launches from several host threads may fill them (every
+// thread computes the same value).
 template <typename K>
-int persistent_blocks(K kern, int threads, int (&cache)[64]) {
+int persistent_blocks(K kern, int threads, std::atomic<int> (&cache)[64]) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int cus = 0, occ = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0) != hipSuccess) return 0;
-    cache[dev] = cus * (occ > 0 ? occ : 1);
+    v = cus * (occ > 0 ? occ : 1);
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
 }
 
 // Compute units of the current device (cached per device; 0 when the query fails).
 int device_cus() {
-  static int cache[64] = {};
+  static std::atomic<int> cache[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = cus;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
 }
 
 // grid cap set through moe_set_gemm_max_blocks (0: none); atomic so that a launch on one
@@ -1332,7 +1336,7 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   const long long row_bytes = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD) ? 4LL * p.I
                                                                           : (long long)p.N * (p.c_fp32 ? 4 : 2);
   if ((long long)BM * row_bytes >= kOutOfRange) return hipErrorInvalidValue;
-  static int resident_cache[64];  // one per instantiation of launch_cfg
+  static std::atomic<int> resident_cache[64];  // one per instantiation of launch_cfg
   const int resident = persistent_blocks(kern, C::NT, resident_cache);
   const int max_blocks = g_max_blocks.load(std::memory_order_relaxed);
   if (resident <= 0) return hipErrorInvalidValue;
