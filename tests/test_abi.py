@@ -186,3 +186,38 @@ def test_routed_rows_beyond_int32_are_refused(lib):
     T_ok = (0x7fffffff - 256 * 4095) // (k + 1)
     assert lib.moe_workspace_bytes(ctypes.byref(M.problem(T_ok, H, E, k, 64, 0))) > 0
     assert lib.moe_workspace_bytes(ctypes.byref(M.problem(T_ok + 1, H, E, k, 64, 0))) == 0
+
+
+def test_workspace_views_inside_an_exact_size(lib):
+    # random mostly-valid layer problems (host-only calls): the workspace size is exact (one
+    # byte less is MOE_ERR_WORKSPACE = 3) and every view the layer uses lies inside it
+    import random
+    import mixture_experts_layer_amd as M
+    lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    rng = random.Random(7)
+    base, accepted = 1 << 40, 0
+    for _ in range(3000):
+        E = rng.choice([1, 2, 4, 8, 16, 40, 64, 128, 256])
+        k = rng.randint(1, min(E, 32))
+        dtype = rng.choice([0, 0, 1, 3])
+        ng = rng.choice([0, 0, 1, 2, 4, 8])
+        p = M.Problem(rng.choice([0, 1, 2, 7, 31, 32, 33, 256, 257, 4096, 8193, 65536]),
+                      64 * rng.randint(1, 80), E, k, 64 * rng.randint(1, 40),
+                      rng.choice([0, 0, 64, 128]), rng.choice([0, 1, 2, 3, 4]), dtype,
+                      0 if dtype == 1 else rng.choice([0, 1]), rng.choice([0, 1]), ng,
+                      rng.randint(1, ng) if ng > 1 else 0, rng.choice([0.0, 1.0, 2.5]),
+                      rng.choice([0, 1, 2]), rng.choice([0, 0, 1, 8, 64, 128]))
+        b = lib.moe_workspace_bytes(ctypes.byref(p))
+        if not b:
+            continue
+        accepted += 1
+        v = M.Views()
+        assert lib.moe_workspace_views(ctypes.byref(p), ctypes.c_void_p(base), ctypes.c_size_t(b),
+                                       ctypes.byref(v)) == 0
+        assert lib.moe_workspace_views(ctypes.byref(p), ctypes.c_void_p(base),
+                                       ctypes.c_size_t(b - 1), ctypes.byref(v)) == 3
+        for name, ftype in M.Views._fields_:
+            ptr = getattr(v, name)
+            if ftype is ctypes.c_void_p and ptr:
+                assert base <= ptr < base + b, (name, hex(ptr), b)
+    assert accepted > 500
